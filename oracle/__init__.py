@@ -1,0 +1,239 @@
+"""CPU oracle for FP8 tensor quantization (test infrastructure).
+
+A plain, slow C implementation (``qf8_oracle.c``) of what the quantization path computes,
+wrapped with ctypes. Only the test suite, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` may import this package; the product path never does. It shares no code
+with the GPU library (``mx_block_scaled_amax_amd``), and neither imports the other.
+
+Arrays: BF16 tensors are ``numpy.uint16`` arrays of raw bit patterns, FP32 tensors are
+``numpy.float32`` arrays. Formats: 0 = E4M3, 1 = E5M2, 2 = E8M0 (decode only).
+MX rounding: 0 = OCP round-down, 1 = round-up.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+E4M3, E5M2, E8M0 = 0, 1, 2
+ROUND_DOWN, ROUND_UP = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qf8_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libqf8_oracle.so")
+_lib = None
+
+_c_void_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+
+def build():
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    tmp = _LIB_PATH + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+                           "-Wall", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"])
+    os.replace(tmp, _LIB_PATH)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.qf8o_decode.restype = ctypes.c_double
+    lib.qf8o_decode.argtypes = [ctypes.c_int, ctypes.c_uint]
+    lib.qf8o_encode.restype = ctypes.c_uint
+    lib.qf8o_encode.argtypes = [ctypes.c_int, ctypes.c_double]
+    lib.qf8o_num_finite_nonneg.restype = ctypes.c_int
+    lib.qf8o_num_finite_nonneg.argtypes = [ctypes.c_int]
+    lib.qf8o_max_finite.restype = ctypes.c_double
+    lib.qf8o_max_finite.argtypes = [ctypes.c_int]
+    lib.qf8o_amax.restype = ctypes.c_double
+    lib.qf8o_amax.argtypes = [_c_void_p, ctypes.c_int, _i64]
+    lib.qf8o_scale_from_amax.restype = ctypes.c_float
+    lib.qf8o_scale_from_amax.argtypes = [ctypes.c_int, ctypes.c_double]
+    lib.qf8o_cast_one.restype = ctypes.c_uint
+    lib.qf8o_cast_one.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_float]
+    lib.qf8o_cast.restype = None
+    lib.qf8o_cast.argtypes = [_c_void_p, ctypes.c_int, _i64, ctypes.c_int, ctypes.c_float, _c_void_p]
+    lib.qf8o_encode_f32.restype = None
+    lib.qf8o_encode_f32.argtypes = [ctypes.c_int, _c_void_p, _i64, _c_void_p]
+    lib.qf8o_quantize_per_tensor.restype = None
+    lib.qf8o_quantize_per_tensor.argtypes = [_c_void_p, ctypes.c_int, _i64, _i64, ctypes.c_int,
+                                             _c_void_p, _c_void_p, _c_void_p, _c_void_p]
+    lib.qf8o_delayed_sizeof.restype = ctypes.c_size_t
+    lib.qf8o_delayed_init.restype = ctypes.c_int
+    lib.qf8o_delayed_init.argtypes = [_c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.qf8o_delayed_reset.restype = None
+    lib.qf8o_delayed_reset.argtypes = [_c_void_p]
+    lib.qf8o_delayed_estimate.restype = ctypes.c_float
+    lib.qf8o_delayed_estimate.argtypes = [_c_void_p]
+    lib.qf8o_delayed_scale.restype = ctypes.c_float
+    lib.qf8o_delayed_scale.argtypes = [_c_void_p]
+    lib.qf8o_delayed_step.restype = None
+    lib.qf8o_delayed_step.argtypes = [_c_void_p, _c_void_p, ctypes.c_int, _i64, _i64,
+                                      _c_void_p, _c_void_p, _c_void_p, _c_void_p]
+    lib.qf8o_delayed_get.restype = None
+    lib.qf8o_delayed_get.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p]
+    lib.qf8o_quantize_block.restype = None
+    lib.qf8o_quantize_block.argtypes = [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                        _c_void_p, _c_void_p, _c_void_p, _c_void_p]
+    lib.qf8o_emax.restype = ctypes.c_int
+    lib.qf8o_emax.argtypes = [ctypes.c_int]
+    lib.qf8o_mx_exponent.restype = ctypes.c_int
+    lib.qf8o_mx_exponent.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double]
+    lib.qf8o_quantize_mx.restype = None
+    lib.qf8o_quantize_mx.argtypes = [_c_void_p, ctypes.c_int, _i64, _i64, ctypes.c_int, ctypes.c_int,
+                                     _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_c_void_p)
+
+
+def _dtype_code(x):
+    if x.dtype == np.uint16:
+        return 0
+    if x.dtype == np.float32:
+        return 1
+    raise TypeError("oracle inputs are uint16 (bf16 bits) or float32 arrays")
+
+
+def _contig(x):
+    return np.ascontiguousarray(x)
+
+
+def decode(fmt, code):
+    return _load().qf8o_decode(fmt, int(code))
+
+
+def encode(fmt, y):
+    return _load().qf8o_encode(fmt, float(y))
+
+
+def encode_f32(fmt, y):
+    y = _contig(np.asarray(y, dtype=np.float32))
+    q = np.empty(y.shape, np.uint8)
+    _load().qf8o_encode_f32(fmt, _ptr(y), y.size, _ptr(q))
+    return q
+
+
+def num_finite_nonneg(fmt):
+    return _load().qf8o_num_finite_nonneg(fmt)
+
+
+def max_finite(fmt):
+    return _load().qf8o_max_finite(fmt)
+
+
+def emax(fmt):
+    return _load().qf8o_emax(fmt)
+
+
+def amax(x):
+    x = _contig(x)
+    return _load().qf8o_amax(_ptr(x), _dtype_code(x), x.size)
+
+
+def scale_from_amax(fmt, a):
+    return _load().qf8o_scale_from_amax(fmt, float(a))
+
+
+def cast_one(fmt, x, scale):
+    return _load().qf8o_cast_one(fmt, float(x), float(np.float32(scale)))
+
+
+def cast(x, fmt, scale):
+    """q = sat_rne8(fl32(x * scale)) elementwise."""
+    x = _contig(x)
+    q = np.empty(x.shape, np.uint8)
+    _load().qf8o_cast(_ptr(x), _dtype_code(x), x.size, fmt, float(np.float32(scale)), _ptr(q))
+    return q
+
+
+def quantize_per_tensor(x, fmt):
+    """Returns (q, amax, scale, nonfinite)."""
+    x = _contig(x)
+    rows, cols = (x.shape[0], int(np.prod(x.shape[1:]))) if x.ndim >= 2 else (1, x.size)
+    q = np.empty(x.shape, np.uint8)
+    am = np.zeros(1, np.float32)
+    sc = np.zeros(1, np.float32)
+    nf = np.zeros(1, np.int32)
+    _load().qf8o_quantize_per_tensor(_ptr(x), _dtype_code(x), rows, cols, fmt, _ptr(q), _ptr(am), _ptr(sc), _ptr(nf))
+    return q, am[0], sc[0], int(nf[0])
+
+
+class Delayed:
+    """Delayed-scaling state machine (amax history FIFO, Interval, 2^-N margin)."""
+
+    def __init__(self, hist_len, interval, n_guard, fmt):
+        lib = _load()
+        self._buf = np.zeros(lib.qf8o_delayed_sizeof(), np.uint8)
+        if lib.qf8o_delayed_init(_ptr(self._buf), hist_len, interval, n_guard, fmt) != 0:
+            raise ValueError("bad delayed-scaling configuration")
+        self.hist_len = hist_len
+        self.fmt = fmt
+
+    def reset(self):
+        _load().qf8o_delayed_reset(_ptr(self._buf))
+
+    def estimate(self):
+        return _load().qf8o_delayed_estimate(_ptr(self._buf))
+
+    def next_scale(self):
+        return _load().qf8o_delayed_scale(_ptr(self._buf))
+
+    def step(self, x):
+        """One iteration. Returns (q, scale_used, amax, nonfinite)."""
+        x = _contig(x)
+        rows, cols = (x.shape[0], int(np.prod(x.shape[1:]))) if x.ndim >= 2 else (1, x.size)
+        q = np.empty(x.shape, np.uint8)
+        s = np.zeros(1, np.float32)
+        a = np.zeros(1, np.float32)
+        nf = np.zeros(1, np.int32)
+        _load().qf8o_delayed_step(_ptr(self._buf), _ptr(x), _dtype_code(x), rows, cols, _ptr(q), _ptr(s), _ptr(a), _ptr(nf))
+        return q, s[0], a[0], int(nf[0])
+
+    def state(self):
+        """Returns (history oldest-first as float32 array, count, step)."""
+        h = np.zeros(self.hist_len, np.float32)
+        c = np.zeros(1, np.int32)
+        st = np.zeros(1, np.int64)
+        _load().qf8o_delayed_get(_ptr(self._buf), _ptr(h), _ptr(c), _ptr(st))
+        return h[:c[0]].copy(), int(c[0]), int(st[0])
+
+
+def quantize_block(x, br, bc, fmt):
+    """Returns (q, scales, amax, nonfinite); scales/amax are [ceil(R/br)][ceil(C/bc)]."""
+    x = _contig(x)
+    rows, cols = x.shape
+    gr, gc = -(-rows // br), -(-cols // bc)
+    q = np.empty(x.shape, np.uint8)
+    sc = np.zeros((gr, gc), np.float32)
+    am = np.zeros((gr, gc), np.float32)
+    nf = np.zeros(1, np.int32)
+    _load().qf8o_quantize_block(_ptr(x), _dtype_code(x), rows, cols, br, bc, fmt, _ptr(q), _ptr(sc), _ptr(am), _ptr(nf))
+    return q, sc, am, int(nf[0])
+
+
+def mx_exponent(fmt, rnd, a):
+    return _load().qf8o_mx_exponent(fmt, rnd, float(a))
+
+
+def quantize_mx(x, fmt, rnd, row=True, col=True):
+    """Returns (q_row, s_row, q_colT, s_colT, nonfinite); a direction not asked for is None."""
+    x = _contig(x)
+    rows, cols = x.shape
+    q_row = np.empty((rows, cols), np.uint8) if row else None
+    s_row = np.empty((rows, cols // 32), np.uint8) if row else None
+    q_colT = np.empty((cols, rows), np.uint8) if col else None
+    s_colT = np.empty((cols, rows // 32), np.uint8) if col else None
+    nf = np.zeros(1, np.int32)
+    _load().qf8o_quantize_mx(_ptr(x), _dtype_code(x), rows, cols, fmt, rnd, _ptr(q_row), _ptr(s_row),
+                             _ptr(q_colT), _ptr(s_colT), _ptr(nf))
+    return q_row, s_row, q_colT, s_colT, int(nf[0])

@@ -1,0 +1,422 @@
+/*
+ * qf8_oracle.c -- plain, slow CPU definition of FP8 tensor quantization.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the CPU-baseline leg of the
+ * benchmark load this library. It shares no code, header, table or helper with the GPU library,
+ * and the GPU library never calls it.
+ *
+ * Everything here is written for a reader to check by eye against the pages:
+ *   [HiF8-train]   "HiFloat8：高性能训练之路" (hifloat.gccorg.com blog):
+ *                  section 1.2 (current scaling, Eq.(1)-(2); delayed scaling, Eq.(3)-(4),
+ *                  amax history, Interval) and section 5.2 (first step / restart is current).
+ *   [MP-FP8]       "混合精度与 FP8 训练" (hs-black.github.io, posts/scaling-mixed-precision):
+ *                  sections 2.1-2.3 (field layout, E4M3/E5M2, the 0.1 example), 3 (binades),
+ *                  4.1 (round to nearest, ties to even), 8.1 (S = F8max/amax, saturation),
+ *                  8.2 (delayed scaling, margin), 10.2 (1x128 and 128x128 groups),
+ *                  13.1 (MX blocks of 32, E8M0 scale, shared exponent, the 5.3 example).
+ *   [MXFP8-recipe] "NVIDIA：Blackwell GPU MXFP8 预训练最佳实践" (51cto.com):
+ *                  section 4.1 (amax = 0 gives X = -127, OCP round-down exponent, the
+ *                  round-up exponent of Algorithm 1, saturating RNE cast of V/2^X).
+ *
+ * Arithmetic: fp64 throughout. A value is rounded to fp32 exactly where the method keeps an
+ * fp32 value (the scale factor S and the scaled product x*S). Both roundings are done by a cast
+ * of an fp64 result to float: a product of two fp32 (or bf16 and fp32) values is exact in fp64,
+ * and for a quotient of two fp32 values fp64 then fp32 rounding equals one correct fp32
+ * rounding, because 53 >= 2*24 + 2 (double rounding is innocuous for +,-,*,/ under that bound).
+ *
+ * Readings where the pages are silent or garbled (each is listed with its reason in the design
+ * notes of the repository):
+ *   R1 the MX element step divides by 2^X (X = -6 multiplies by 64 in the 5.3 example);
+ *   R2 the scaled value is rounded to fp32 before the fp8 rounding (Eq.(2)/(4) bodies are lost);
+ *   R3 IEEE signed zero, except that an all-zero MX block writes 0x00 everywhere;
+ *   R4 amax = 0 (tensor, group or delayed estimate) gives the base ratio 1; an fp32 overflow of
+ *      F8max/amax gives FLT_MAX;
+ *   R5 E8M0 byte = X + 127, 0xFF is NaN;
+ *   R6 Inf/NaN input is outside the bit-exact contract: it sets the non-finite flag, a NaN
+ *      element encodes to an fp8 NaN code, a non-finite amax gives S = 1 (tensor, group) or
+ *      E8M0 byte 0xFF (MX block), and a delayed step never pushes a non-finite amax;
+ *   R7 delayed: step 0 (after init or reset) is current scaling without the 2^-N margin; later
+ *      steps scale with the history as it stood before the step, then append; the update
+ *      steps are step % Interval == 0; an empty history estimate counts as amax = 0;
+ *   R8 the OCP round-down exponent is floor(log2 amax) - emax (a difference, not a quotient).
+ */
+#include <stdint.h>
+#include <stddef.h>
+#include <string.h>
+#include <math.h>
+#include <float.h>
+
+#define QF8O_E4M3 0
+#define QF8O_E5M2 1
+#define QF8O_E8M0 2
+
+#define QF8O_BF16 0
+#define QF8O_FP32 1
+
+#define QF8O_ROUND_DOWN 0
+#define QF8O_ROUND_UP 1
+
+/* ---------------------------------------------------------------------------------------------
+ * Number formats, from their definitions.
+ * [MP-FP8 2.1]: sign, biased exponent, trailing mantissa; exponent field 0 = subnormal with the
+ * minimum exponent; [MP-FP8 2.2]: E5M2 follows IEEE (all-ones exponent = Inf/NaN); E4M3 has no
+ * Inf and one NaN pattern S.1111.111, so the all-ones exponent also holds finite values up to 448.
+ * Bias is 2^(e-1) - 1.
+ * ------------------------------------------------------------------------------------------- */
+static int fmt_mbits(int fmt) { return fmt == QF8O_E4M3 ? 3 : 2; }
+static int fmt_ebits(int fmt) { return fmt == QF8O_E4M3 ? 4 : 5; }
+static int fmt_bias(int fmt) { return (1 << (fmt_ebits(fmt) - 1)) - 1; }
+
+double qf8o_decode(int fmt, unsigned code)
+{
+    code &= 0xFFu;
+    if (fmt == QF8O_E8M0) {                   /* [MP-FP8 13.1]: a power of two, 8 exponent bits */
+        if (code == 0xFFu) return NAN;        /* R5 */
+        return ldexp(1.0, (int)code - 127);
+    }
+    int mb = fmt_mbits(fmt), eb = fmt_ebits(fmt), bias = fmt_bias(fmt);
+    int s = (int)(code >> 7);
+    int e = (int)(code >> mb) & ((1 << eb) - 1);
+    int m = (int)code & ((1 << mb) - 1);
+    int eall = (1 << eb) - 1;
+    double v;
+    if (fmt == QF8O_E4M3 && e == eall && m == (1 << mb) - 1) return NAN;
+    if (fmt == QF8O_E5M2 && e == eall) {
+        if (m != 0) return NAN;
+        return s ? -INFINITY : INFINITY;
+    }
+    if (e == 0)                                /* subnormal: 0.m * 2^(1-bias) */
+        v = ldexp((double)m, 1 - bias - mb);
+    else                                       /* normal: 1.m * 2^(e-bias) */
+        v = ldexp((double)((1 << mb) + m), e - bias - mb);
+    return s ? -v : v;
+}
+
+/* Ascending list of the non-negative finite values. Codes 0, 1, 2, ... decode in increasing
+ * order, so the index in the list is the code itself (checked by the test suite). */
+static double g_vals[2][128];
+static int g_nvals[2] = {0, 0};
+
+static void build_table(int fmt)
+{
+    if (g_nvals[fmt]) return;
+    int n = 0;
+    for (unsigned c = 0; c < 128; ++c) {
+        double v = qf8o_decode(fmt, c);
+        if (!isfinite(v)) break;
+        g_vals[fmt][n++] = v;
+    }
+    g_nvals[fmt] = n;
+}
+
+int qf8o_num_finite_nonneg(int fmt) { build_table(fmt); return g_nvals[fmt]; }
+double qf8o_max_finite(int fmt) { build_table(fmt); return g_vals[fmt][g_nvals[fmt] - 1]; }
+
+/* sat_rne8(y): nearest fp8 value, ties to the even code, with magnitudes at or above the largest
+ * finite value clamped to it ([MP-FP8 4.1] RNE; [MP-FP8 8.1] overflow saturates, it is not
+ * skipped; [MXFP8-recipe 4.1] the cast saturates). Sign kept, so -0 and negative values that
+ * round to zero give 0x80 (R3). NaN gives the positive NaN code (R6). */
+unsigned qf8o_encode(int fmt, double y)
+{
+    build_table(fmt);
+    const double *v = g_vals[fmt];
+    int n = g_nvals[fmt];
+    if (isnan(y)) return 0x7Fu;
+    unsigned sign = signbit(y) ? 0x80u : 0u;
+    double a = fabs(y);
+    int i;
+    if (a >= v[n - 1]) {
+        i = n - 1;
+    } else {
+        int lo = 0, hi = n - 1;                /* invariant: v[lo] <= a < v[hi] */
+        while (hi - lo > 1) {
+            int mid = (lo + hi) / 2;
+            if (v[mid] <= a) lo = mid; else hi = mid;
+        }
+        i = lo;
+        if (v[i] != a) {
+            double midpoint = 0.5 * (v[i] + v[i + 1]);   /* exact: short dyadic rationals */
+            if (a > midpoint) i = i + 1;
+            else if (a == midpoint && (i & 1)) i = i + 1; /* tie: the even code */
+        }
+    }
+    return sign | (unsigned)i;
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Inputs. BF16 is the upper half of an fp32 ([MP-FP8 2.2]); widening is exact.
+ * ------------------------------------------------------------------------------------------- */
+static double load_elem(const void *x, int dtype, int64_t i)
+{
+    uint32_t u;
+    float f;
+    if (dtype == QF8O_BF16) u = (uint32_t)((const uint16_t *)x)[i] << 16;
+    else u = ((const uint32_t *)x)[i];
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* amax = max |x| over a set of elements ([HiF8-train 1.2]: ComputeAmax, e.g. torch.max of |x|;
+ * [MXFP8-recipe 4.1]: amax = max |V_i| over the block). NaN anywhere gives NaN. */
+typedef struct { double amax; int has_nan; } amax_acc;
+static void acc_init(amax_acc *a) { a->amax = 0.0; a->has_nan = 0; }
+static void acc_add(amax_acc *a, double v)
+{
+    if (isnan(v)) { a->has_nan = 1; return; }
+    if (fabs(v) > a->amax) a->amax = fabs(v);
+}
+static double acc_value(const amax_acc *a) { return a->has_nan ? NAN : a->amax; }
+
+double qf8o_amax(const void *x, int dtype, int64_t n)
+{
+    amax_acc a;
+    acc_init(&a);
+    for (int64_t i = 0; i < n; ++i) acc_add(&a, load_elem(x, dtype, i));
+    return acc_value(&a);
+}
+
+/* Eq.(1) of [HiF8-train 1.2] / [MP-FP8 8.1]: S = F8max / amax, kept as fp32 (R4, R6). */
+float qf8o_scale_from_amax(int fmt, double amax)
+{
+    if (!isfinite(amax)) return 1.0f;
+    if (amax == 0.0) return 1.0f;
+    float s = (float)(qf8o_max_finite(fmt) / amax);
+    if (isinf(s)) s = FLT_MAX;
+    return s;
+}
+
+/* Eq.(2)/(4): q = sat_rne8(fl32(x * S)) (R2). */
+unsigned qf8o_cast_one(int fmt, double x, float scale)
+{
+    float p = (float)(x * (double)scale);
+    return qf8o_encode(fmt, (double)p);
+}
+
+void qf8o_cast(const void *x, int dtype, int64_t n, int fmt, float scale, uint8_t *q)
+{
+    for (int64_t i = 0; i < n; ++i) q[i] = (uint8_t)qf8o_cast_one(fmt, load_elem(x, dtype, i), scale);
+}
+
+void qf8o_encode_f32(int fmt, const float *y, int64_t n, uint8_t *q)
+{
+    for (int64_t i = 0; i < n; ++i) q[i] = (uint8_t)qf8o_encode(fmt, (double)y[i]);
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Per-tensor current scaling ([HiF8-train 1.2] Eq.(1)-(2)). Outputs q, amax and S.
+ * ------------------------------------------------------------------------------------------- */
+void qf8o_quantize_per_tensor(const void *x, int dtype, int64_t rows, int64_t cols, int fmt,
+                              uint8_t *q, float *amax_out, float *scale_out, int32_t *nonfinite)
+{
+    int64_t n = rows * cols;
+    double amax = qf8o_amax(x, dtype, n);
+    float s = qf8o_scale_from_amax(fmt, amax);
+    qf8o_cast(x, dtype, n, fmt, s, q);
+    if (amax_out) *amax_out = (float)amax;
+    if (scale_out) *scale_out = s;
+    if (nonfinite) *nonfinite = isfinite(amax) ? 0 : 1;
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Per-tensor delayed scaling ([HiF8-train 1.2] Eq.(3)-(4); [MP-FP8 8.2]).
+ * A fixed-capacity FIFO of past amax values; the estimate is its maximum; the true amax is
+ * appended every Interval steps and the oldest entry drops out when the buffer is full.
+ * S = F8max/estimate * 2^-N_guard. Step 0 (or the first step after a reset) has no history and
+ * runs current scaling once ([HiF8-train 5.2]).
+ * ------------------------------------------------------------------------------------------- */
+#define QF8O_MAX_HIST 4096
+typedef struct {
+    int32_t hist_len, interval, n_guard, fmt;
+    int32_t count, head;        /* head = slot of the oldest entry */
+    int64_t step;
+    float hist[QF8O_MAX_HIST];
+} qf8o_delayed;
+
+size_t qf8o_delayed_sizeof(void) { return sizeof(qf8o_delayed); }
+
+int qf8o_delayed_init(qf8o_delayed *st, int hist_len, int interval, int n_guard, int fmt)
+{
+    if (hist_len < 1 || hist_len > QF8O_MAX_HIST || interval < 1 || n_guard < 0) return -1;
+    memset(st, 0, sizeof(*st));
+    st->hist_len = hist_len;
+    st->interval = interval;
+    st->n_guard = n_guard;
+    st->fmt = fmt;
+    return 0;
+}
+
+void qf8o_delayed_reset(qf8o_delayed *st)
+{
+    st->count = 0;
+    st->head = 0;
+    st->step = 0;
+    memset(st->hist, 0, sizeof(st->hist));
+}
+
+static void delayed_push(qf8o_delayed *st, float v)
+{
+    if (st->count < st->hist_len) {
+        st->hist[(st->head + st->count) % st->hist_len] = v;
+        st->count++;
+    } else {
+        st->hist[st->head] = v;                        /* overwrite the oldest */
+        st->head = (st->head + 1) % st->hist_len;
+    }
+}
+
+float qf8o_delayed_estimate(const qf8o_delayed *st)
+{
+    float e = 0.0f;                                    /* R7: empty history counts as 0 */
+    for (int i = 0; i < st->count; ++i)
+        if (st->hist[(st->head + i) % st->hist_len] > e) e = st->hist[(st->head + i) % st->hist_len];
+    return e;
+}
+
+/* The scale a step uses, from the state before the step. */
+float qf8o_delayed_scale(const qf8o_delayed *st)
+{
+    float base = qf8o_scale_from_amax(st->fmt, (double)qf8o_delayed_estimate(st));
+    return (float)((double)base * ldexp(1.0, -st->n_guard));
+}
+
+void qf8o_delayed_step(qf8o_delayed *st, const void *x, int dtype, int64_t rows, int64_t cols,
+                       uint8_t *q, float *scale_used, float *amax_out, int32_t *nonfinite)
+{
+    int64_t n = rows * cols;
+    double amax = qf8o_amax(x, dtype, n);
+    float s;
+    int update;
+    if (st->step == 0) {                               /* current scaling, no margin (R7) */
+        s = qf8o_scale_from_amax(st->fmt, amax);
+        update = 1;
+    } else {                                           /* scale from the history, then maybe append */
+        s = qf8o_delayed_scale(st);
+        update = (st->step % st->interval) == 0;
+    }
+    qf8o_cast(x, dtype, n, st->fmt, s, q);
+    if (update && isfinite(amax)) delayed_push(st, (float)amax);
+    st->step++;
+    if (scale_used) *scale_used = s;
+    if (amax_out) *amax_out = (float)amax;
+    if (nonfinite) *nonfinite = isfinite(amax) ? 0 : 1;
+}
+
+void qf8o_delayed_get(const qf8o_delayed *st, float *hist_oldest_first, int32_t *count, int64_t *step)
+{
+    for (int i = 0; i < st->count; ++i) hist_oldest_first[i] = st->hist[(st->head + i) % st->hist_len];
+    *count = st->count;
+    *step = st->step;
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Fine-grained groups ([MP-FP8 10.2]; online, current-scaled per group [MP-FP8 10.3]):
+ * rule Eq.(1)-(2) applied to every br x bc group on its own. Groups at the right and bottom
+ * edges may be partial. Scales and amax are [ceil(rows/br)][ceil(cols/bc)] fp32.
+ * ------------------------------------------------------------------------------------------- */
+void qf8o_quantize_block(const void *x, int dtype, int64_t rows, int64_t cols, int64_t br, int64_t bc,
+                         int fmt, uint8_t *q, float *scales, float *amax_out, int32_t *nonfinite)
+{
+    int64_t gr = (rows + br - 1) / br, gc = (cols + bc - 1) / bc;
+    int bad = 0;
+    for (int64_t bi = 0; bi < gr; ++bi) {
+        for (int64_t bj = 0; bj < gc; ++bj) {
+            int64_t r0 = bi * br, r1 = r0 + br < rows ? r0 + br : rows;
+            int64_t c0 = bj * bc, c1 = c0 + bc < cols ? c0 + bc : cols;
+            amax_acc a;
+            acc_init(&a);
+            for (int64_t r = r0; r < r1; ++r)
+                for (int64_t c = c0; c < c1; ++c) acc_add(&a, load_elem(x, dtype, r * cols + c));
+            double amax = acc_value(&a);
+            float s = qf8o_scale_from_amax(fmt, amax);
+            if (!isfinite(amax)) bad = 1;
+            for (int64_t r = r0; r < r1; ++r)
+                for (int64_t c = c0; c < c1; ++c)
+                    q[r * cols + c] = (uint8_t)qf8o_cast_one(fmt, load_elem(x, dtype, r * cols + c), s);
+            if (scales) scales[bi * gc + bj] = s;
+            if (amax_out) amax_out[bi * gc + bj] = (float)amax;
+        }
+    }
+    if (nonfinite) *nonfinite = bad;
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * MX blocks of 32 with an E8M0 shared scale 2^X ([MP-FP8 13.1]; [MXFP8-recipe 4.1]).
+ * emax is the exponent of the largest normal of the element format (E4M3: 8, E5M2: 15) and
+ * destmax its largest finite value.
+ * ------------------------------------------------------------------------------------------- */
+int qf8o_emax(int fmt)
+{
+    int e;
+    frexp(qf8o_max_finite(fmt), &e);
+    return e - 1;
+}
+
+/* Returns X (before the +127 bias); amax must be finite and >= 0. */
+int qf8o_mx_exponent(int fmt, int rnd, double amax)
+{
+    if (amax == 0.0) return -127;                        /* [MXFP8-recipe 4.1] */
+    int e;
+    frexp(amax, &e);                                     /* amax = m * 2^e, m in [0.5, 1) */
+    int floor_log2 = e - 1;
+    int X;
+    if (rnd == QF8O_ROUND_DOWN) {
+        X = floor_log2 - qf8o_emax(fmt);                 /* OCP: floor(log2 amax) - emax (R8) */
+    } else {
+        /* Algorithm 1: the exponent of amax/destmax rounded toward +inf, i.e. the smallest
+         * integer X with amax / 2^X <= destmax. */
+        double destmax = qf8o_max_finite(fmt);
+        X = floor_log2 - qf8o_emax(fmt) - 1;
+        while (amax > ldexp(destmax, X)) X++;
+    }
+    if (X < -127) X = -127;                              /* saturate to the E8M0 bounds */
+    if (X > 127) X = 127;
+    return X;
+}
+
+static void mx_group(const void *x, int dtype, int fmt, int rnd, const int64_t *idx,
+                     uint8_t *qout, int64_t qstride, uint8_t *sbyte, int *bad)
+{
+    amax_acc a;
+    acc_init(&a);
+    for (int k = 0; k < 32; ++k) acc_add(&a, load_elem(x, dtype, idx[k]));
+    double amax = acc_value(&a);
+    if (!isfinite(amax)) {                               /* R6: outside the bit-exact contract */
+        *bad = 1;
+        *sbyte = 0xFF;
+        for (int k = 0; k < 32; ++k) qout[k * qstride] = (uint8_t)qf8o_encode(fmt, load_elem(x, dtype, idx[k]));
+        return;
+    }
+    int X = qf8o_mx_exponent(fmt, rnd, amax);
+    *sbyte = (uint8_t)(X + 127);
+    for (int k = 0; k < 32; ++k) {
+        if (amax == 0.0) { qout[k * qstride] = 0x00; continue; }   /* zero block: every byte 0 */
+        double v = load_elem(x, dtype, idx[k]) * ldexp(1.0, -X);  /* V_i / 2^X, exact (R1) */
+        qout[k * qstride] = (uint8_t)qf8o_encode(fmt, v);
+    }
+}
+
+/* Rowwise: groups of 32 along a row, q_row [rows][cols], s_row [rows][cols/32].
+ * Columnwise: groups of 32 down a column, stored transposed: q_colT [cols][rows],
+ * s_colT [cols][rows/32]. Either pair may be NULL. Both come from the same high-precision
+ * input ([MP-FP8 13.1]: a tensor and its transpose are each quantized from the original). */
+void qf8o_quantize_mx(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int rnd,
+                      uint8_t *q_row, uint8_t *s_row, uint8_t *q_colT, uint8_t *s_colT, int32_t *nonfinite)
+{
+    int bad = 0;
+    int64_t idx[32];
+    if (q_row) {
+        for (int64_t r = 0; r < rows; ++r)
+            for (int64_t g = 0; g < cols / 32; ++g) {
+                for (int k = 0; k < 32; ++k) idx[k] = r * cols + g * 32 + k;
+                mx_group(x, dtype, fmt, rnd, idx, q_row + r * cols + g * 32, 1, s_row + r * (cols / 32) + g, &bad);
+            }
+    }
+    if (q_colT) {
+        for (int64_t c = 0; c < cols; ++c)
+            for (int64_t g = 0; g < rows / 32; ++g) {
+                for (int k = 0; k < 32; ++k) idx[k] = (g * 32 + k) * cols + c;
+                mx_group(x, dtype, fmt, rnd, idx, q_colT + c * rows + g * 32, 1, s_colT + c * (rows / 32) + g, &bad);
+            }
+    }
+    if (nonfinite) *nonfinite = bad;
+}
