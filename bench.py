@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 quantization library on one MI355X.
+
+Headline (one JSON line on stdout): MXFP8 dual quantization of a 16384x4096 BF16 gradient tensor
+(Laplace(0, 1e-3) with 0.01% outliers x1e4), rowwise and columnwise 1x32 blocks with E8M0
+scales. One step = the four variants the workload names: {E4M3, E5M2} x {OCP round-down,
+round-up}, each on its own device-resident copy of the input and its own outputs, so that no
+variant finds the previous variant's data in the 256 MB last-level cache.
+
+  effective GB/s = algorithmic bytes (2N read + N + N written + 2 * N/32 scale bytes per
+                   variant = 272,629,760 B) * 4 variants * steps / wall time of the timed steps
+  roofline.achieved = 272,629,760 B / average duration of one dual-quantization kernel launch,
+                   measured with HIP events on the launch stream over the timed region;
+                   peak = 8000 GB/s (MI355X HBM3E).
+  roofline.traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE counters (in
+                   profiles/), scaled by the same counters' reading for a plain copy of known
+                   size; null when the kernel sources changed since the counters were taken.
+  cpu_baseline   = the CPU oracle (single-threaded C) on the first 4096 rows, all four variants.
+
+--suite also times every other operation on its workload (per-tensor, delayed, 1x128, 128x128,
+MX rowwise on the small tensor, a plain copy) and writes gpurun_out/bench_suite.json.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective GB/s (bytes in+out) & % of HBM peak, MXFP8 dual quantize 16384x4096"
+PEAK_GBPS = 8000.0
+ROWS, COLS = 16384, 4096
+DUAL_BYTES = 2 * ROWS * COLS + 2 * ROWS * COLS + 2 * (ROWS * COLS // 32)   # 272,629,760
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mx_dual_16384x4096_traffic.json")
+KERNEL_SOURCES = ["mx_block_scaled_amax_amd/csrc/qf8_mx.hip", "mx_block_scaled_amax_amd/csrc/qf8_device.h"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per dual launch from the committed counter summary, if it matches the sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sources_sha256_16") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--suite", action="store_true", help="also time every other operation")
+    ap.add_argument("--only-dual", action="store_true",
+                    help="launch only the dual kernel (E4M3 round-up) --steps times, for counter runs")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="launch only a plain 256 MiB device copy --steps times, for counter runs")
+    return ap.parse_args()
+
+
+def to_dev(bits):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class DualCall:
+    """Pre-marshalled quantize_mx_dual call (keeps Python overhead out of the timed loop)."""
+
+    def __init__(self, qf8, x, fmt, rnd, stream):
+        import torch
+        self.out = [torch.empty((ROWS, COLS), dtype=torch.uint8, device="cuda"),
+                    torch.empty((ROWS, COLS // 32), dtype=torch.uint8, device="cuda"),
+                    torch.empty((COLS, ROWS), dtype=torch.uint8, device="cuda"),
+                    torch.empty((COLS, ROWS // 32), dtype=torch.uint8, device="cuda")]
+        self.x = x
+        vp = ctypes.c_void_p
+        self.fn = qf8._load().quantize_mx_dual
+        self.args = (vp(x.data_ptr()), 0, ROWS, COLS, fmt, rnd) + tuple(vp(t.data_ptr()) for t in self.out) + \
+                    (None, vp(stream.cuda_stream))
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError(f"quantize_mx_dual failed with status {st}")
+
+
+def cpu_baseline(xb):
+    import oracle as O
+    sample = xb[:4096]
+    t0 = time.perf_counter()
+    for fmt in (O.E4M3, O.E5M2):
+        for rnd in (O.ROUND_DOWN, O.ROUND_UP):
+            O.quantize_mx(sample, fmt, rnd)
+    dt = time.perf_counter() - t0
+    nbytes = 4 * (4 * sample.size + 2 * (sample.size // 32))
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"rows 0..4095 of the 16384x4096 input (1/4 of it), all four variants, "
+                      f"single-threaded C oracle, {dt:.2f} s on {platform.processor() or platform.machine()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this quantization path has no multi-GPU leg here "
+              "(see DESIGN.md on sharding); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mx_block_scaled_amax_amd as qf8
+    from synthetic import mx_gradient
+
+    torch.cuda.init()
+    stream = torch.cuda.current_stream()
+
+    if args.copy_calibration:
+        n = 256 << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty(n, dtype=torch.uint8, device="cuda")
+        a.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": args.steps}))
+        return
+
+    xb = mx_gradient(ROWS, COLS, seed=4)
+    variants = [(f, r) for f in (qf8.E4M3, qf8.E5M2) for r in (qf8.ROUND_DOWN, qf8.ROUND_UP)]
+
+    if args.only_dual:
+        call = DualCall(qf8, to_dev(xb), qf8.E4M3, qf8.ROUND_UP, stream)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            call()
+        torch.cuda.synchronize()
+        print(json.dumps({"dual_launches": args.steps, "bytes_per_launch": DUAL_BYTES}))
+        return
+
+    calls = [DualCall(qf8, to_dev(xb), f, r, stream) for f, r in variants]
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+
+    starts = [[torch.cuda.Event(enable_timing=True) for _ in calls] for _ in range(args.steps)]
+    ends = [[torch.cuda.Event(enable_timing=True) for _ in calls] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        for j, c in enumerate(calls):
+            starts[k][j].record(stream)
+            c()
+            ends[k][j].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    kms = np.array([[starts[k][j].elapsed_time(ends[k][j]) for j in range(len(calls))] for k in range(args.steps)])
+    avg_launch_s = float(kms.mean()) / 1e3
+    achieved = DUAL_BYTES / avg_launch_s / 1e9
+    value = len(calls) * DUAL_BYTES * args.steps / wall / 1e9
+    traffic = stored_traffic()
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mxfp8_dual_16384x4096", "rows": ROWS, "cols": COLS, "input": "bf16",
+                   "values": "Laplace(0, 1e-3), 0.01% entries x1e4, seed 4",
+                   "variants": ["e4m3-round_down", "e4m3-round_up", "e5m2-round_down", "e5m2-round_up"],
+                   "bytes_per_variant": DUAL_BYTES, "pct_of_hbm_peak": round(100 * value / PEAK_GBPS, 2),
+                   "kernel_ms_per_variant": {v: round(float(kms[:, j].mean()), 5) for j, v in enumerate(
+                       ["e4m3-round_down", "e4m3-round_up", "e5m2-round_down", "e5m2-round_up"])}},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(xb)
+    print(json.dumps(line), flush=True)
+
+    if args.suite:
+        from bench_suite import run_suite
+        run_suite(args)
+
+
+if __name__ == "__main__":
+    main()

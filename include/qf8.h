@@ -1,0 +1,152 @@
+/*
+ * qf8.h -- C ABI of libqf8.so: FP8 tensor quantization (amax -> scale -> saturating RNE cast)
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Pages the operations follow (title, section):
+ *   [HiF8-train]   "HiFloat8：高性能训练之路" (hifloat.gccorg.com blog)
+ *   [MP-FP8]       "混合精度与 FP8 训练" (hs-black.github.io, posts/scaling-mixed-precision)
+ *   [MXFP8-recipe] "NVIDIA：Blackwell GPU MXFP8 预训练最佳实践" (51cto.com)
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are row-major and contiguous: element (r, c) of a [rows][cols] tensor is at
+ *     r*cols + c. Input elements are BF16 (QF8_IN_BF16, raw 16-bit patterns) or FP32.
+ *   - All tensor and scalar arguments named x, q, s_*, scale*, amax*, nonfinite, ws, history,
+ *     meta are DEVICE pointers on the current HIP device. The caller owns every buffer; the
+ *     library allocates nothing and keeps no pointer after a call returns, except through work
+ *     already queued on the stream.
+ *   - stream is a hipStream_t passed as void*; NULL is the null stream. Every call only
+ *     enqueues work on that stream and returns; results are valid once the stream has
+ *     synchronized. No call synchronizes the host.
+ *   - Arithmetic: amax is an exact maximum of |x|; a scale F8max/amax is one IEEE fp32
+ *     division rounded to nearest even; x*S is one fp32 multiplication; the cast to fp8 is
+ *     round-to-nearest-even with saturation to +-F8max (F8max = 448 for E4M3, 57344 for E5M2).
+ *     A scale is 1 when the amax it comes from is 0 or not finite, and FLT_MAX when F8max/amax
+ *     overflows fp32.
+ *   - nonfinite (nullable, device int32): set to 1 when the input holds Inf or NaN, never
+ *     cleared by the library (the caller zeroes it). Outputs computed from non-finite input
+ *     are outside the bit-exact contract except where stated.
+ *   - Return value: QF8_OK or a negative qf8_status. Argument errors are detected on the host
+ *     before anything is enqueued; QF8_ERR_HIP reports a failed kernel launch.
+ *   - Calls are thread-safe (no global mutable state). Calls on the same output buffers or the
+ *     same delayed state must be ordered by the caller (same stream or events).
+ */
+#ifndef QF8_H
+#define QF8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qf8_fmt { QF8_E4M3 = 0, QF8_E5M2 = 1 } qf8_fmt;
+typedef enum qf8_dtype { QF8_IN_BF16 = 0, QF8_IN_FP32 = 1 } qf8_dtype;
+/* MX shared-exponent rounding ([MXFP8-recipe 4.1]): OCP round-down X = floor(log2 amax) - emax,
+ * or the round-up X = ceil(log2(amax / F8max)) of the recipe's Algorithm 1. */
+typedef enum qf8_mx_round { QF8_MX_ROUND_DOWN = 0, QF8_MX_ROUND_UP = 1 } qf8_mx_round;
+
+typedef enum qf8_status {
+    QF8_OK = 0,
+    QF8_ERR_NULL = -1,       /* a required pointer is NULL */
+    QF8_ERR_ENUM = -2,       /* fmt, dtype or rounding mode out of range */
+    QF8_ERR_SHAPE = -3,      /* negative size, or a size the operation's grouping cannot take */
+    QF8_ERR_ALIGN = -4,      /* a tensor pointer is not 16-byte aligned (scalars: 4-byte) */
+    QF8_ERR_WORKSPACE = -5,  /* ws is NULL or smaller than qf8_workspace_bytes() */
+    QF8_ERR_STATE = -6,      /* delayed-scaling state invalid or not initialised */
+    QF8_ERR_HIP = -7         /* a HIP launch failed */
+} qf8_status;
+
+/* Human-readable name of a status code. Never NULL. */
+const char *qf8_status_string(int status);
+
+/* Bytes of device workspace quantize_per_tensor and quantize_delayed need for a tensor of
+ * rows x cols elements of dtype: per-workgroup partial maxima. The contents need no
+ * initialisation and are scratch between calls. */
+size_t qf8_workspace_bytes(int64_t rows, int64_t cols, int dtype);
+
+/* Scaled saturating cast (Eq.(2) of [HiF8-train 1.2], [MP-FP8 8.1]):
+ *   q[i] = sat_rne8(fl32(x[i] * scale[0])),  i in [0, n).
+ * x: n elements of dtype, 16-byte aligned. scale: one device fp32 value. q: n bytes, 16-byte
+ * aligned. n >= 0 (n = 0 enqueues nothing). */
+int qf8_cast_scaled(const void *x, int dtype, int64_t n, int fmt, const float *scale,
+                    uint8_t *q, void *stream);
+
+/* Per-tensor current scaling ([HiF8-train 1.2] Eq.(1)-(2); [MP-FP8 8.1]):
+ *   amax = max |x|;  S = fl32(F8max / amax);  q = sat_rne8(fl32(x * S)).
+ * x: rows*cols elements (any rows, cols >= 0), 16-byte aligned. q: rows*cols bytes, 16-byte
+ * aligned. amax, scale: one device fp32 each (amax of an empty tensor is 0, its scale 1).
+ * ws: qf8_workspace_bytes(rows, cols, dtype) bytes of device scratch.
+ * Two kernels: a grid-wide partial max, then the cast (each workgroup finishes the
+ * reduction of the partials itself). */
+int quantize_per_tensor(const void *x, int dtype, int64_t rows, int64_t cols, int fmt,
+                        uint8_t *q, float *amax, float *scale, int32_t *nonfinite,
+                        void *ws, size_t ws_bytes, void *stream);
+
+/* Per-tensor delayed scaling ([HiF8-train 1.2] Eq.(3)-(4) and section 5.2; [MP-FP8 8.2]).
+ * State: a FIFO of the last hist_len amax values kept on the device; the estimate is the
+ * maximum over it; the scale a step uses is S = fl32(F8max / estimate) * 2^-n_guard.
+ * Step 0 after init or reset has no history and runs current scaling (no margin). Every step
+ * t >= 1 casts with the scale the history gave before the step; when t % interval == 0 (and
+ * at step 0) the step's own amax is appended afterwards, dropping the oldest entry when the
+ * FIFO is full. A non-finite amax is never appended (it sets nonfinite instead).
+ * history (hist_len fp32), meta (4 int32) and scale (1 fp32) are caller-owned device buffers
+ * that must outlive every queued step; step is a host counter the library advances.
+ * Checkpoint = copy history, meta, scale and step; resume = copy them back. */
+typedef struct qf8_delayed_state {
+    float *history;      /* device: hist_len fp32 slots */
+    int32_t *meta;       /* device: [0] count, [1] head (oldest slot), [2..3] reserved */
+    float *scale;        /* device: the scale the next delayed step uses */
+    int32_t hist_len;    /* 1 .. 4096 */
+    int32_t interval;    /* >= 1 */
+    int32_t n_guard;     /* 0 .. 64 */
+    int32_t fmt;         /* qf8_fmt */
+    int64_t step;        /* host: number of steps since init or reset */
+    int32_t magic;       /* set by qf8_delayed_init */
+    int32_t reserved;
+} qf8_delayed_state;
+
+/* Fills the host fields, clears history/meta/scale on the device, step = 0. */
+int qf8_delayed_init(qf8_delayed_state *st, float *history, int32_t *meta, float *scale,
+                     int hist_len, int interval, int n_guard, int fmt, void *stream);
+/* Empties the history and sets step = 0, so the next step is current scaling again (the
+ * restart after an anomaly, [HiF8-train 5.2]). */
+int qf8_delayed_reset(qf8_delayed_state *st, void *stream);
+/* One iteration on x (rows*cols elements, 16-byte aligned) -> q (16-byte aligned).
+ * scale_used (nullable): the scale this step cast with. amax_out (nullable): this step's true
+ * amax (computed in the same pass as the cast; only update steps append it to the history).
+ * ws: qf8_workspace_bytes(rows, cols, dtype) bytes. */
+int quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, qf8_delayed_state *st,
+                     uint8_t *q, float *scale_used, float *amax_out, int32_t *nonfinite,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/* Fine-grained current scaling ([MP-FP8 10.2] and 10.3): Eq.(1)-(2) applied to each group of
+ * block_rows x block_cols elements on its own; (block_rows, block_cols) is (1, 128) (per-token
+ * groups) or (128, 128) (weight blocks). Groups at the right and bottom edges may be partial.
+ * x: [rows][cols] with cols % 8 == 0 (BF16) or cols % 4 == 0 (FP32), 16-byte aligned.
+ * q: [rows][cols] bytes, 16-byte aligned.
+ * scales: [ceil(rows/block_rows)][ceil(cols/block_cols)] fp32, the S_g of each group.
+ * amax (nullable): same shape, each group's amax. */
+int quantize_block(const void *x, int dtype, int64_t rows, int64_t cols, int block_rows,
+                   int block_cols, int fmt, uint8_t *q, float *scales, float *amax,
+                   int32_t *nonfinite, void *stream);
+
+/* MX quantization with 1x32 blocks and E8M0 shared scales ([MP-FP8 13.1]; [MXFP8-recipe 4.1]),
+ * rowwise and/or columnwise from the same high-precision input in one pass.
+ * Per block of 32: amax = 0 gives X = -127 and 32 zero bytes; otherwise X from the rounding
+ * mode, clamped to [-127, 127]; scale byte = X + 127; element = sat_rne8(x / 2^X).
+ *   rowwise   (q_row non-NULL): blocks run along a row. q_row [rows][cols],
+ *             s_row [rows][cols/32]; needs cols % 32 == 0.
+ *   columnwise (q_colT non-NULL): blocks run down a column and are stored transposed:
+ *             q_colT [cols][rows], s_colT [cols][rows/32]; needs rows % 32 == 0.
+ * At least one direction; s_row / s_colT are required with their q. x, q_row, q_colT 16-byte
+ * aligned. A block holding Inf or NaN gets scale byte 0xFF and sets nonfinite. */
+int quantize_mx_dual(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int rnd,
+                     uint8_t *q_row, uint8_t *s_row, uint8_t *q_colT, uint8_t *s_colT,
+                     int32_t *nonfinite, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QF8_H */

@@ -1,0 +1,250 @@
+"""FP8 tensor quantization on AMD Instinct MI355X (gfx950).
+
+Thin Python binding of ``libqf8.so`` (C ABI in ``include/qf8.h``): the functions below carry the
+C names, marshal torch tensors into device pointers and the current HIP stream, allocate output
+tensors when none are given, and raise ``QF8Error`` on a non-zero status. Every step of the
+quantization runs in the library's HIP kernels; there is no CPU path. torch supplies device
+memory and streams only.
+
+Formats: ``E4M3`` (max 448) and ``E5M2`` (max 57344), OCP encodings. Inputs: ``torch.bfloat16``
+or ``torch.float32`` CUDA tensors, contiguous, 2-D ``[rows, cols]`` (1-D tensors count as one
+row). Outputs are ``torch.uint8`` tensors of raw fp8 / E8M0 bytes.
+"""
+import ctypes
+import os
+
+import torch  # loaded first: the library binds to the HIP runtime torch has already loaded
+
+__all__ = [
+    "E4M3", "E5M2", "ROUND_DOWN", "ROUND_UP", "QF8Error", "library_path",
+    "qf8_status_string", "qf8_workspace_bytes", "qf8_cast_scaled", "quantize_per_tensor",
+    "DelayedState", "qf8_delayed_init", "qf8_delayed_reset", "quantize_delayed",
+    "quantize_block", "quantize_mx_dual",
+]
+
+E4M3, E5M2 = 0, 1
+ROUND_DOWN, ROUND_UP = 0, 1
+_BF16, _FP32 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libqf8.so")
+_lib = None
+
+
+class QF8Error(RuntimeError):
+    def __init__(self, status, what=""):
+        self.status = status
+        super().__init__(f"{what}: {qf8_status_string(status)} ({status})")
+
+
+class _DelayedStruct(ctypes.Structure):
+    _fields_ = [("history", ctypes.c_void_p), ("meta", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("hist_len", ctypes.c_int32), ("interval", ctypes.c_int32), ("n_guard", ctypes.c_int32),
+                ("fmt", ctypes.c_int32), ("step", ctypes.c_int64), ("magic", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built: run `python -m mx_block_scaled_amax_amd.build` "
+                          "(hipcc, gfx950). There is no CPU fallback.")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    sigs = {
+        "qf8_status_string": (ctypes.c_char_p, [i32]),
+        "qf8_workspace_bytes": (sz, [i64, i64, i32]),
+        "qf8_cast_scaled": (i32, [vp, i32, i64, i32, vp, vp, vp]),
+        "quantize_per_tensor": (i32, [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, sz, vp]),
+        "qf8_delayed_init": (i32, [ctypes.POINTER(_DelayedStruct), vp, vp, vp, i32, i32, i32, i32, vp]),
+        "qf8_delayed_reset": (i32, [ctypes.POINTER(_DelayedStruct), vp]),
+        "quantize_delayed": (i32, [vp, i32, i64, i64, ctypes.POINTER(_DelayedStruct), vp, vp, vp, vp, vp, sz, vp]),
+        "quantize_block": (i32, [vp, i32, i64, i64, i32, i32, i32, vp, vp, vp, vp, vp]),
+        "quantize_mx_dual": (i32, [vp, i32, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp]),
+    }
+    for name, (res, args) in sigs.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def qf8_status_string(status):
+    return _load().qf8_status_string(int(status)).decode()
+
+
+def _check(status, what):
+    if status != 0:
+        raise QF8Error(status, what)
+
+
+def _dtype_code(x):
+    if x.dtype == torch.bfloat16:
+        return _BF16
+    if x.dtype == torch.float32:
+        return _FP32
+    raise TypeError(f"input must be torch.bfloat16 or torch.float32, got {x.dtype}")
+
+
+def _dev_tensor(x, name):
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor; the library has no CPU path")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return x
+
+
+def _rows_cols(x):
+    if x.dim() == 1:
+        return 1, x.shape[0]
+    if x.dim() != 2:
+        raise ValueError("expected a 1-D or 2-D tensor")
+    return x.shape[0], x.shape[1]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _out(t, shape, dtype, device, name):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _dev_tensor(t, name)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}")
+    return t
+
+
+def qf8_workspace_bytes(rows, cols, dtype=torch.bfloat16):
+    return _load().qf8_workspace_bytes(rows, cols, _BF16 if dtype == torch.bfloat16 else _FP32)
+
+
+def workspace(x):
+    """A device workspace tensor large enough for quantize_per_tensor / quantize_delayed on x."""
+    rows, cols = _rows_cols(x)
+    return torch.empty(qf8_workspace_bytes(rows, cols, x.dtype), dtype=torch.uint8, device=x.device)
+
+
+def qf8_cast_scaled(x, fmt, scale, q=None, stream=None):
+    """q = sat_rne8(fl32(x * scale)); scale is a 1-element float32 device tensor."""
+    _dev_tensor(x, "x")
+    _dev_tensor(scale, "scale")
+    q = _out(q, tuple(x.shape), torch.uint8, x.device, "q")
+    _check(_load().qf8_cast_scaled(_ptr(x), _dtype_code(x), x.numel(), fmt, _ptr(scale), _ptr(q),
+                                   _stream(stream, x.device)), "qf8_cast_scaled")
+    return q
+
+
+def quantize_per_tensor(x, fmt, q=None, amax=None, scale=None, nonfinite=None, ws=None, stream=None):
+    """Per-tensor current scaling. Returns (q, amax, scale) as device tensors."""
+    _dev_tensor(x, "x")
+    rows, cols = _rows_cols(x)
+    dev = x.device
+    q = _out(q, tuple(x.shape), torch.uint8, dev, "q")
+    amax = _out(amax, (1,), torch.float32, dev, "amax")
+    scale = _out(scale, (1,), torch.float32, dev, "scale")
+    ws = workspace(x) if ws is None else _dev_tensor(ws, "ws")
+    _check(_load().quantize_per_tensor(_ptr(x), _dtype_code(x), rows, cols, fmt, _ptr(q), _ptr(amax), _ptr(scale),
+                                       _ptr(nonfinite), _ptr(ws), ws.numel() * ws.element_size(),
+                                       _stream(stream, dev)), "quantize_per_tensor")
+    return q, amax, scale
+
+
+class DelayedState:
+    """Device state of per-tensor delayed scaling: history FIFO, meta (count, head), next scale."""
+
+    def __init__(self, hist_len, interval, n_guard, fmt, device="cuda", stream=None):
+        self.history = torch.zeros(hist_len, dtype=torch.float32, device=device)
+        self.meta = torch.zeros(4, dtype=torch.int32, device=device)
+        self.scale = torch.ones(1, dtype=torch.float32, device=device)
+        self.struct = _DelayedStruct()
+        self.device = self.history.device
+        qf8_delayed_init(self, hist_len, interval, n_guard, fmt, stream)
+
+    @property
+    def step(self):
+        return self.struct.step
+
+    @step.setter
+    def step(self, v):
+        self.struct.step = int(v)
+
+    def history_list(self):
+        """History oldest-first (synchronizes)."""
+        count, head = (int(v) for v in self.meta[:2].cpu())
+        h = self.history.cpu().tolist()
+        n = self.struct.hist_len
+        return [h[(head + i) % n] for i in range(count)]
+
+
+def qf8_delayed_init(state, hist_len, interval, n_guard, fmt, stream=None):
+    _check(_load().qf8_delayed_init(ctypes.byref(state.struct), _ptr(state.history), _ptr(state.meta),
+                                    _ptr(state.scale), hist_len, interval, n_guard, fmt,
+                                    _stream(stream, state.device)), "qf8_delayed_init")
+
+
+def qf8_delayed_reset(state, stream=None):
+    _check(_load().qf8_delayed_reset(ctypes.byref(state.struct), _stream(stream, state.device)), "qf8_delayed_reset")
+
+
+def quantize_delayed(x, state, q=None, scale_used=None, amax_out=None, nonfinite=None, ws=None, stream=None):
+    """One delayed-scaling iteration. Returns q; scale_used / amax_out are filled when given."""
+    _dev_tensor(x, "x")
+    rows, cols = _rows_cols(x)
+    q = _out(q, tuple(x.shape), torch.uint8, x.device, "q")
+    ws = workspace(x) if ws is None else _dev_tensor(ws, "ws")
+    _check(_load().quantize_delayed(_ptr(x), _dtype_code(x), rows, cols, ctypes.byref(state.struct), _ptr(q),
+                                    _ptr(scale_used), _ptr(amax_out), _ptr(nonfinite), _ptr(ws),
+                                    ws.numel() * ws.element_size(), _stream(stream, x.device)), "quantize_delayed")
+    return q
+
+
+def quantize_block(x, block_rows, block_cols, fmt, q=None, scales=None, amax=None, nonfinite=None, stream=None,
+                   want_amax=True):
+    """1x128 or 128x128 group scaling. Returns (q, scales, amax-or-None)."""
+    _dev_tensor(x, "x")
+    rows, cols = _rows_cols(x)
+    gshape = (-(-rows // block_rows), -(-cols // block_cols))
+    q = _out(q, tuple(x.shape), torch.uint8, x.device, "q")
+    scales = _out(scales, gshape, torch.float32, x.device, "scales")
+    if amax is None and want_amax:
+        amax = torch.empty(gshape, dtype=torch.float32, device=x.device)
+    _check(_load().quantize_block(_ptr(x), _dtype_code(x), rows, cols, block_rows, block_cols, fmt, _ptr(q),
+                                  _ptr(scales), _ptr(amax), _ptr(nonfinite), _stream(stream, x.device)),
+           "quantize_block")
+    return q, scales, amax
+
+
+def quantize_mx_dual(x, fmt, rnd, rowwise=True, colwise=True, q_row=None, s_row=None, q_colT=None, s_colT=None,
+                     nonfinite=None, stream=None):
+    """MX 1x32 quantization. Returns (q_row, s_row, q_colT, s_colT); a direction not asked for is None."""
+    _dev_tensor(x, "x")
+    rows, cols = _rows_cols(x)
+    dev = x.device
+    if rowwise:
+        q_row = _out(q_row, (rows, cols), torch.uint8, dev, "q_row")
+        s_row = _out(s_row, (rows, cols // 32), torch.uint8, dev, "s_row")
+    else:
+        q_row = s_row = None
+    if colwise:
+        q_colT = _out(q_colT, (cols, rows), torch.uint8, dev, "q_colT")
+        s_colT = _out(s_colT, (cols, rows // 32), torch.uint8, dev, "s_colT")
+    else:
+        q_colT = s_colT = None
+    _check(_load().quantize_mx_dual(_ptr(x), _dtype_code(x), rows, cols, fmt, rnd, _ptr(q_row), _ptr(s_row),
+                                    _ptr(q_colT), _ptr(s_colT), _ptr(nonfinite), _stream(stream, dev)),
+           "quantize_mx_dual")
+    return q_row, s_row, q_colT, s_colT

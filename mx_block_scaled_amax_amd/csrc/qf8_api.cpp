@@ -1,0 +1,191 @@
+// qf8_api.cpp -- the C ABI declared in include/qf8.h: argument validation and kernel dispatch.
+// Every check happens on the host before anything is enqueued; nothing here synchronizes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <limits.h>
+
+#include "../../include/qf8.h"
+#include "qf8_internal.h"
+
+namespace {
+
+constexpr int32_t kDelayedMagic = 0x51463844;  // "QF8D"
+constexpr int kMaxHistory = 4096;
+constexpr int kMaxGuard = 64;
+
+inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+inline bool fmt_ok(int fmt) { return fmt == QF8_E4M3 || fmt == QF8_E5M2; }
+inline bool dtype_ok(int dt) { return dt == QF8_IN_BF16 || dt == QF8_IN_FP32; }
+inline hipStream_t as_stream(void *s) { return (hipStream_t)s; }
+
+// rows, cols >= 0 and rows * cols representable
+inline bool dims_ok(int64_t rows, int64_t cols) {
+    if (rows < 0 || cols < 0) return false;
+    if (rows > 0 && cols > INT64_MAX / 16 / rows) return false;
+    return true;
+}
+
+int check_delayed(const qf8_delayed_state *st) {
+    if (!st) return QF8_ERR_NULL;
+    if (st->magic != kDelayedMagic) return QF8_ERR_STATE;
+    if (!st->history || !st->meta || !st->scale) return QF8_ERR_NULL;
+    if (st->hist_len < 1 || st->hist_len > kMaxHistory || st->interval < 1 || st->n_guard < 0 ||
+        st->n_guard > kMaxGuard || !fmt_ok(st->fmt) || st->step < 0)
+        return QF8_ERR_STATE;
+    return QF8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qf8_status_string(int status) {
+    switch (status) {
+        case QF8_OK: return "QF8_OK";
+        case QF8_ERR_NULL: return "QF8_ERR_NULL: a required pointer is NULL";
+        case QF8_ERR_ENUM: return "QF8_ERR_ENUM: format, dtype or rounding mode out of range";
+        case QF8_ERR_SHAPE: return "QF8_ERR_SHAPE: size not accepted by this operation";
+        case QF8_ERR_ALIGN: return "QF8_ERR_ALIGN: pointer not 16-byte aligned";
+        case QF8_ERR_WORKSPACE: return "QF8_ERR_WORKSPACE: workspace missing or too small";
+        case QF8_ERR_STATE: return "QF8_ERR_STATE: delayed-scaling state invalid";
+        case QF8_ERR_HIP: return "QF8_ERR_HIP: kernel launch failed";
+        default: return "unknown qf8 status";
+    }
+}
+
+size_t qf8_workspace_bytes(int64_t rows, int64_t cols, int dtype) {
+    (void)rows; (void)cols; (void)dtype;
+    return qf8::kWorkspaceBytes;
+}
+
+int qf8_cast_scaled(const void *x, int dtype, int64_t n, int fmt, const float *scale, uint8_t *q, void *stream) {
+    if (!dtype_ok(dtype) || !fmt_ok(fmt)) return QF8_ERR_ENUM;
+    if (n < 0) return QF8_ERR_SHAPE;
+    if (n == 0) return QF8_OK;
+    if (!x || !scale || !q) return QF8_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4)) return QF8_ERR_ALIGN;
+    return qf8::launch_cast_scaled(x, dtype, n, fmt, scale, q, nullptr, nullptr, qf8::stream_grid(n, dtype),
+                                   as_stream(stream));
+}
+
+int quantize_per_tensor(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, uint8_t *q, float *amax,
+                        float *scale, int32_t *nonfinite, void *ws, size_t ws_bytes, void *stream) {
+    if (!dtype_ok(dtype) || !fmt_ok(fmt)) return QF8_ERR_ENUM;
+    if (!dims_ok(rows, cols)) return QF8_ERR_SHAPE;
+    const int64_t n = rows * cols;
+    if ((n > 0 && (!x || !q)) || !amax || !scale) return QF8_ERR_NULL;
+    if (!ws || ws_bytes < qf8::kWorkspaceBytes) return QF8_ERR_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(amax, 4) || !aligned(scale, 4) || !aligned(ws, 4) ||
+        (nonfinite && !aligned(nonfinite, 4)))
+        return QF8_ERR_ALIGN;
+    hipStream_t s = as_stream(stream);
+    uint32_t *partials = (uint32_t *)ws;
+    const int grid = qf8::stream_grid(n, dtype);
+    int st = qf8::launch_amax_partials(x, dtype, n, partials, grid, s);
+    if (st != QF8_OK) return st;
+    return qf8::launch_cast_current(x, dtype, n, fmt, q, partials, grid, amax, scale, nonfinite, grid, s);
+}
+
+int qf8_delayed_init(qf8_delayed_state *st, float *history, int32_t *meta, float *scale, int hist_len, int interval,
+                     int n_guard, int fmt, void *stream) {
+    if (!st || !history || !meta || !scale) return QF8_ERR_NULL;
+    if (!fmt_ok(fmt)) return QF8_ERR_ENUM;
+    if (hist_len < 1 || hist_len > kMaxHistory || interval < 1 || n_guard < 0 || n_guard > kMaxGuard)
+        return QF8_ERR_STATE;
+    if (!aligned(history, 4) || !aligned(meta, 4) || !aligned(scale, 4)) return QF8_ERR_ALIGN;
+    st->history = history;
+    st->meta = meta;
+    st->scale = scale;
+    st->hist_len = hist_len;
+    st->interval = interval;
+    st->n_guard = n_guard;
+    st->fmt = fmt;
+    st->step = 0;
+    st->magic = kDelayedMagic;
+    st->reserved = 0;
+    return qf8_delayed_reset(st, stream);
+}
+
+int qf8_delayed_reset(qf8_delayed_state *st, void *stream) {
+    int c = check_delayed(st);
+    if (c != QF8_OK) return c;
+    hipStream_t s = as_stream(stream);
+    // cleared with a fill kernel rather than a memset, so a captured graph replays it correctly
+    int r = qf8::launch_fill_u32((uint32_t *)st->history, st->hist_len, 0u, s);
+    if (r == QF8_OK) r = qf8::launch_fill_u32((uint32_t *)st->meta, 4, 0u, s);
+    if (r == QF8_OK) r = qf8::launch_fill_u32((uint32_t *)st->scale, 1, 0x3F800000u /* 1.0f */, s);
+    if (r == QF8_OK) st->step = 0;
+    return r;
+}
+
+int quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, qf8_delayed_state *st, uint8_t *q,
+                     float *scale_used, float *amax_out, int32_t *nonfinite, void *ws, size_t ws_bytes,
+                     void *stream) {
+    int c = check_delayed(st);
+    if (c != QF8_OK) return c;
+    if (!dtype_ok(dtype)) return QF8_ERR_ENUM;
+    if (!dims_ok(rows, cols)) return QF8_ERR_SHAPE;
+    const int64_t n = rows * cols;
+    if (n > 0 && (!x || !q)) return QF8_ERR_NULL;
+    if (!ws || ws_bytes < qf8::kWorkspaceBytes) return QF8_ERR_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(ws, 4) || (scale_used && !aligned(scale_used, 4)) ||
+        (amax_out && !aligned(amax_out, 4)) || (nonfinite && !aligned(nonfinite, 4)))
+        return QF8_ERR_ALIGN;
+    hipStream_t s = as_stream(stream);
+    uint32_t *partials = (uint32_t *)ws;
+    const int grid = qf8::stream_grid(n, dtype);
+    int r;
+    int update;
+    if (st->step == 0) {
+        // no history yet: current scaling (Eq.(1)-(2), no margin), then append this amax
+        r = qf8::launch_amax_partials(x, dtype, n, partials, grid, s);
+        if (r == QF8_OK)
+            r = qf8::launch_cast_current(x, dtype, n, st->fmt, q, partials, grid, nullptr, scale_used, nullptr, grid, s);
+        update = 1;
+    } else {
+        // cast with the scale the history gave, fusing this step's partial amax into the pass
+        r = qf8::launch_cast_scaled(x, dtype, n, st->fmt, st->scale, q, scale_used, partials, grid, s);
+        update = (st->step % st->interval) == 0;
+    }
+    if (r == QF8_OK)
+        r = qf8::launch_delayed_finalize(partials, grid, st->history, st->meta, st->scale, st->hist_len, st->n_guard,
+                                         st->fmt, update, amax_out, nonfinite, s);
+    if (r == QF8_OK) st->step++;
+    return r;
+}
+
+int quantize_block(const void *x, int dtype, int64_t rows, int64_t cols, int block_rows, int block_cols, int fmt,
+                   uint8_t *q, float *scales, float *amax, int32_t *nonfinite, void *stream) {
+    if (!dtype_ok(dtype) || !fmt_ok(fmt)) return QF8_ERR_ENUM;
+    if (!dims_ok(rows, cols)) return QF8_ERR_SHAPE;
+    if (!((block_rows == 1 || block_rows == 128) && block_cols == 128)) return QF8_ERR_SHAPE;
+    if (cols % (dtype == QF8_IN_BF16 ? 8 : 4) != 0) return QF8_ERR_SHAPE;
+    if (rows > INT32_MAX || cols > INT32_MAX) return QF8_ERR_SHAPE;
+    const int64_t ngroups = ((rows + block_rows - 1) / block_rows) * ((cols + 127) / 128);
+    if (ngroups > INT32_MAX) return QF8_ERR_SHAPE;
+    if (rows * cols == 0) return QF8_OK;
+    if (!x || !q || !scales) return QF8_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scales, 4) || (amax && !aligned(amax, 4)) ||
+        (nonfinite && !aligned(nonfinite, 4)))
+        return QF8_ERR_ALIGN;
+    return qf8::launch_block(x, dtype, rows, cols, block_rows, fmt, q, scales, amax, nonfinite, as_stream(stream));
+}
+
+int quantize_mx_dual(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int rnd, uint8_t *q_row,
+                     uint8_t *s_row, uint8_t *q_colT, uint8_t *s_colT, int32_t *nonfinite, void *stream) {
+    if (!dtype_ok(dtype) || !fmt_ok(fmt) || (rnd != QF8_MX_ROUND_DOWN && rnd != QF8_MX_ROUND_UP)) return QF8_ERR_ENUM;
+    if (!dims_ok(rows, cols) || rows > INT32_MAX || cols > INT32_MAX) return QF8_ERR_SHAPE;
+    if (!q_row && !q_colT) return QF8_ERR_NULL;
+    if ((q_row && !s_row) || (q_colT && !s_colT)) return QF8_ERR_NULL;
+    if (q_row && cols % 32 != 0) return QF8_ERR_SHAPE;
+    if (q_colT && rows % 32 != 0) return QF8_ERR_SHAPE;
+    if (cols % (dtype == QF8_IN_BF16 ? 8 : 4) != 0) return QF8_ERR_SHAPE;
+    if (rows * cols == 0) return QF8_OK;
+    if (!x) return QF8_ERR_NULL;
+    if (!aligned(x, 16) || (q_row && !aligned(q_row, 16)) || (q_colT && !aligned(q_colT, 16)) ||
+        (nonfinite && !aligned(nonfinite, 4)))
+        return QF8_ERR_ALIGN;
+    return qf8::launch_mx(x, dtype, rows, cols, fmt, rnd, q_row, s_row, q_colT, s_colT, nonfinite, as_stream(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+// qf8_block.hip -- fine-grained current scaling: 1x128 per-token groups and 128x128 blocks.
+//
+// Pages (title, section):
+//   [MP-FP8] "混合精度与 FP8 训练" (hs-black.github.io): section 10.2 (activations scaled per
+//            1x128 group of one token, weights per 128x128 block), 10.3 (online quantization:
+//            every group computes its own amax), 8.1 (S = F8max/amax, saturating cast).
+//
+// Both kernels are one HBM pass: load the group into registers, reduce its |x| maximum, derive
+// S_g with one IEEE division, cast from the registers.
+//   1x128: a group of 128 BF16 is 16 lanes x 8 values, i.e. one DPP row, so the maximum is four
+//          DPP steps; a workgroup handles 16 groups per pass and 4 passes (all loads issued
+//          first). FP32 input uses 32 lanes per group.
+//   128x128: one workgroup per block; 8 BF16 rows of 16-byte loads per thread, wave maximum
+//          then a 4-entry LDS maximum.
+// Groups at the right and bottom edges may be partial: lanes outside the tensor load zeros,
+// which never raise a maximum, and store nothing.
+#include "qf8_device.h"
+#include "qf8_internal.h"
+#include "../../include/qf8.h"
+
+namespace qf8 {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <bool BF16>
+__device__ __forceinline__ uint32_t vec_absmax_bits(uint4 v) {
+    if constexpr (BF16) {
+        uint32_t m = pk_max_u16(pk_max_u16(v.x & 0x7FFF7FFFu, v.y & 0x7FFF7FFFu),
+                                pk_max_u16(v.z & 0x7FFF7FFFu, v.w & 0x7FFF7FFFu));
+        return umax(m & 0xFFFFu, m >> 16) << 16;
+    } else {
+        return umax(umax(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu), umax(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu));
+    }
+}
+
+template <bool BF16, int FMT>
+__device__ __forceinline__ void store_cast(uint8_t *q, int64_t off, uint4 v, float s) {
+    if constexpr (BF16) *(uint2 *)(q + off) = cast8_bf16<FMT>(v, s);
+    else *(uint32_t *)(q + off) = cast4_f32<FMT>(v, s);
+}
+
+template <bool BF16, int FMT>
+__global__ __launch_bounds__(kThreads) void block_1x128_kernel(const uint16_t *__restrict__ x16, int64_t cols,
+                                                               int64_t gcols, int64_t ngroups, uint8_t *__restrict__ q,
+                                                               float *__restrict__ scales, float *__restrict__ amax,
+                                                               int32_t *nonfinite) {
+    constexpr int VEC = BF16 ? 8 : 4;
+    constexpr int LPG = 128 / VEC;          // lanes per group
+    constexpr int GPP = kThreads / LPG;     // groups per pass
+    constexpr int ITER = 4;
+    const int sub = threadIdx.x % LPG, gslot = threadIdx.x / LPG;
+    const char *xb = (const char *)x16;
+    uint4 v[ITER];
+    int64_t off[ITER], g[ITER];
+    bool ok[ITER];
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        g[it] = ((int64_t)blockIdx.x * ITER + it) * GPP + gslot;
+        const int64_t r = g[it] / gcols, j = g[it] - r * gcols;
+        const int64_t col = j * 128 + sub * VEC;
+        ok[it] = g[it] < ngroups && col < cols;
+        off[it] = r * cols + col;
+        v[it] = ok[it] ? *(const uint4 *)(xb + off[it] * (BF16 ? 2 : 4)) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        uint32_t m = vec_absmax_bits<BF16>(v[it]);
+        m = max_row16(m);
+        if constexpr (!BF16) m = umax(m, (uint32_t)__shfl_xor((int)m, 16));
+        const float s = scale_from_amax_bits<FMT>(m);
+        if (ok[it]) {
+            store_cast<BF16, FMT>(q, off[it], v[it], s);
+            if (sub == 0) {
+                scales[g[it]] = s;
+                if (amax) amax[g[it]] = __uint_as_float(m);
+                if (nonfinite && m >= 0x7F800000u) *nonfinite = 1;
+            }
+        }
+    }
+}
+
+template <bool BF16, int FMT>
+__global__ __launch_bounds__(kThreads) void block_128x128_kernel(const uint16_t *__restrict__ x16, int64_t rows,
+                                                                 int64_t cols, int64_t gcols, uint8_t *__restrict__ q,
+                                                                 float *__restrict__ scales, float *__restrict__ amax,
+                                                                 int32_t *nonfinite) {
+    constexpr int VEC = BF16 ? 8 : 4;
+    constexpr int TPR = 128 / VEC;          // threads per block row
+    constexpr int RPP = kThreads / TPR;     // rows per pass
+    constexpr int PASSES = 128 / RPP;
+    __shared__ uint32_t red[4];
+    const int64_t bi = blockIdx.x / gcols, bj = blockIdx.x - bi * gcols;
+    const int sub = threadIdx.x % TPR, rr = threadIdx.x / TPR;
+    const int64_t col = bj * 128 + sub * VEC;
+    const bool cok = col < cols;
+    const char *xb = (const char *)x16;
+    uint4 v[PASSES];
+    uint32_t m = 0;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int64_t r = bi * 128 + p * RPP + rr;
+        v[p] = (cok && r < rows) ? *(const uint4 *)(xb + (r * cols + col) * (BF16 ? 2 : 4)) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) m = umax(m, vec_absmax_bits<BF16>(v[p]));
+    m = max_wave(m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = umax(umax(red[0], red[1]), umax(red[2], red[3]));
+    const float s = scale_from_amax_bits<FMT>(m);
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int64_t r = bi * 128 + p * RPP + rr;
+        if (cok && r < rows) store_cast<BF16, FMT>(q, r * cols + col, v[p], s);
+    }
+    if (threadIdx.x == 0) {
+        scales[blockIdx.x] = s;
+        if (amax) amax[blockIdx.x] = __uint_as_float(m);
+        if (nonfinite && m >= 0x7F800000u) *nonfinite = 1;
+    }
+}
+
+}  // namespace
+
+int launch_block(const void *x, int dtype, int64_t rows, int64_t cols, int block_rows, int fmt, uint8_t *q,
+                 float *scales, float *amax, int32_t *nonfinite, hipStream_t s) {
+    const int64_t gcols = (cols + 127) / 128;
+    const uint16_t *x16 = (const uint16_t *)x;
+    if (rows == 0 || cols == 0) return QF8_OK;
+    if (block_rows == 1) {
+        const int64_t ngroups = rows * gcols;
+        const int gpb = (dtype == QF8_IN_BF16 ? 16 : 8) * 4;
+        const int64_t grid = (ngroups + gpb - 1) / gpb;
+#define QF8_LAUNCH_1x128(BF, F)                                                                                    \
+        hipLaunchKernelGGL((block_1x128_kernel<BF, F>), dim3((unsigned)grid), dim3(kThreads), 0, s, x16, cols, gcols, \
+                           ngroups, q, scales, amax, nonfinite)
+        if (dtype == QF8_IN_BF16) { if (fmt == QF8_E4M3) QF8_LAUNCH_1x128(true, kE4M3); else QF8_LAUNCH_1x128(true, kE5M2); }
+        else { if (fmt == QF8_E4M3) QF8_LAUNCH_1x128(false, kE4M3); else QF8_LAUNCH_1x128(false, kE5M2); }
+#undef QF8_LAUNCH_1x128
+    } else {
+        const int64_t grid = ((rows + 127) / 128) * gcols;
+#define QF8_LAUNCH_128(BF, F)                                                                                      \
+        hipLaunchKernelGGL((block_128x128_kernel<BF, F>), dim3((unsigned)grid), dim3(kThreads), 0, s, x16, rows, cols, \
+                           gcols, q, scales, amax, nonfinite)
+        if (dtype == QF8_IN_BF16) { if (fmt == QF8_E4M3) QF8_LAUNCH_128(true, kE4M3); else QF8_LAUNCH_128(true, kE5M2); }
+        else { if (fmt == QF8_E4M3) QF8_LAUNCH_128(false, kE4M3); else QF8_LAUNCH_128(false, kE5M2); }
+#undef QF8_LAUNCH_128
+    }
+    return hipGetLastError() == hipSuccess ? QF8_OK : QF8_ERR_HIP;
+}
+
+}  // namespace qf8

@@ -1,0 +1,191 @@
+// qf8_device.h -- device-side building blocks for the gfx950 FP8 quantization kernels.
+//
+// Pages (title, section):
+//   [MP-FP8]       "混合精度与 FP8 训练" (hs-black.github.io, posts/scaling-mixed-precision)
+//   [MXFP8-recipe] "NVIDIA：Blackwell GPU MXFP8 预训练最佳实践" (51cto.com)
+//
+// Number handling
+//   * amax is taken as an integer maximum over |x| bit patterns (sign bit cleared). For
+//     non-negative IEEE values the bit pattern orders like the value, so the maximum is exact
+//     and independent of reduction order; Inf and NaN patterns sort above every finite value,
+//     so a non-finite block is recognised from its amax alone.
+//   * The fp8 encoders are the gfx950 conversion instructions, used only on operands inside
+//     +-F8max: there they round to nearest even exactly ([MP-FP8 4.1]); outside they produce
+//     NaN/Inf instead of saturating, so every caller clamps first ([MP-FP8 8.1] saturation;
+//     [MXFP8-recipe 4.1] saturating cast).
+//       - v_cvt_pk_{fp8,bf8}_f32: two fp32 values -> two E4M3/E5M2 bytes.
+//       - v_cvt_scalef32_pk_{fp8,bf8}_{bf16,f32}: two values divided by 2^E, where E is the
+//         exponent field of the fp32 scale operand minus 127 -- exactly V/2^X of an MX block
+//         when the operand's bits are (X + 127) << 23 (X = -127 gives the bit pattern 0).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qf8 {
+
+typedef short v2i16 __attribute__((ext_vector_type(2)));
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+
+enum { kE4M3 = 0, kE5M2 = 1 };
+enum { kRoundDown = 0, kRoundUp = 1 };
+
+// Element formats ([MP-FP8 2.2]): largest finite value, and emax = exponent of that value.
+template <int FMT> struct F8;
+template <> struct F8<kE4M3> {
+    static constexpr float kMax = 448.0f;         // 1.75 * 2^8
+    static constexpr int kEmax = 8;
+};
+template <> struct F8<kE5M2> {
+    static constexpr float kMax = 57344.0f;       // 1.75 * 2^15
+    static constexpr int kEmax = 15;
+};
+
+// ---- bit helpers ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(v2u16, a),
+                                                                  __builtin_bit_cast(v2u16, b)));
+}
+__device__ __forceinline__ uint32_t pk_min_u16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(v2u16, a),
+                                                                  __builtin_bit_cast(v2u16, b)));
+}
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
+// take the bits of `v` where `mask` is set, else the bits of `other`
+__device__ __forceinline__ uint32_t bit_select(uint32_t mask, uint32_t v, uint32_t other) {
+    return (v & mask) | (other & ~mask);
+}
+
+// ---- cross-lane maxima (all lanes of the group receive the result; every lane of the wave
+// must be active, which the kernels guarantee by predicating only loads and stores) -------
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+// groups of 4 lanes: quad_perm [1,0,3,2] then [2,3,0,1]
+__device__ __forceinline__ uint32_t max_quad(uint32_t v) {
+    v = umax(v, dpp_mov<0xB1>(v));
+    v = umax(v, dpp_mov<0x4E>(v));
+    return v;
+}
+// groups of 8 lanes: quads, then each lane with its mirror in the half row
+__device__ __forceinline__ uint32_t max_oct(uint32_t v) {
+    v = max_quad(v);
+    v = umax(v, dpp_mov<0x141>(v));                // row_half_mirror
+    return v;
+}
+// groups of 16 lanes (one DPP row): quads, then rotate the row by 4 and by 8
+__device__ __forceinline__ uint32_t max_row16(uint32_t v) {
+    v = max_quad(v);
+    v = umax(v, dpp_mov<0x124>(v));                // row_ror:4
+    v = umax(v, dpp_mov<0x128>(v));                // row_ror:8
+    return v;
+}
+__device__ __forceinline__ uint32_t max_wave(uint32_t v) {
+    v = max_row16(v);
+    v = umax(v, (uint32_t)__shfl_xor((int)v, 16));
+    v = umax(v, (uint32_t)__shfl_xor((int)v, 32));
+    return v;
+}
+
+// ---- fp8 conversions -----------------------------------------------------------------------
+// Two fp32 values inside +-F8max -> two bytes in half HI of `old` (other half kept).
+template <int FMT, bool HI>
+__device__ __forceinline__ uint32_t cvt2_f32(float a, float b, uint32_t old) {
+    if constexpr (FMT == kE4M3) return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+    else return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)old, HI);
+}
+// Two BF16 values (one dword, low half first) divided by 2^X, with scale2x = bits (X+127)<<23.
+template <int FMT, bool HI>
+__device__ __forceinline__ uint32_t cvt2_bf16_div2x(uint32_t pair, float scale2x, uint32_t old) {
+    v2bf16 v = __builtin_bit_cast(v2bf16, pair);
+    v2i16 o = __builtin_bit_cast(v2i16, old);
+    v2i16 r;
+    if constexpr (FMT == kE4M3) r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(o, v, scale2x, HI);
+    else r = __builtin_amdgcn_cvt_scalef32_pk_bf8_bf16(o, v, scale2x, HI);
+    return __builtin_bit_cast(uint32_t, r);
+}
+// Two FP32 values divided by 2^X.
+template <int FMT, bool HI>
+__device__ __forceinline__ uint32_t cvt2_f32_div2x(float a, float b, float scale2x, uint32_t old) {
+    v2i16 o = __builtin_bit_cast(v2i16, old);
+    v2i16 r;
+    if constexpr (FMT == kE4M3) r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, a, b, scale2x, HI);
+    else r = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(o, a, b, scale2x, HI);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// sat_rne8(fl32(x * s)) for four fp32 inputs -> four bytes (x[0] in the lowest byte).
+template <int FMT>
+__device__ __forceinline__ uint32_t cast4(float x0, float x1, float x2, float x3, float s) {
+    constexpr float M = F8<FMT>::kMax;
+    float y0 = __builtin_amdgcn_fmed3f(x0 * s, -M, M);
+    float y1 = __builtin_amdgcn_fmed3f(x1 * s, -M, M);
+    float y2 = __builtin_amdgcn_fmed3f(x2 * s, -M, M);
+    float y3 = __builtin_amdgcn_fmed3f(x3 * s, -M, M);
+    return cvt2_f32<FMT, true>(y2, y3, cvt2_f32<FMT, false>(y0, y1, 0u));
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// 8 BF16 (16 bytes) -> 8 fp8 bytes
+template <int FMT>
+__device__ __forceinline__ uint2 cast8_bf16(uint4 v, float s) {
+    return make_uint2(cast4<FMT>(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y), s),
+                      cast4<FMT>(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w), s));
+}
+// 4 FP32 (16 bytes) -> 4 fp8 bytes
+template <int FMT>
+__device__ __forceinline__ uint32_t cast4_f32(uint4 v, float s) {
+    return cast4<FMT>(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w), s);
+}
+// one element, for ragged tails
+template <int FMT>
+__device__ __forceinline__ uint32_t cast1(float x, float s) {
+    constexpr float M = F8<FMT>::kMax;
+    return cvt2_f32<FMT, false>(__builtin_amdgcn_fmed3f(x * s, -M, M), 0.0f, 0u) & 0xFFu;
+}
+
+// ---- scales ----------------------------------------------------------------------------------
+// Eq.(1): S = fl32(F8max / amax) from the fp32 bit pattern of amax; 1 for amax = 0 or
+// non-finite, FLT_MAX when the quotient overflows. The division is IEEE (correctly rounded).
+template <int FMT>
+__device__ __forceinline__ float scale_from_amax_bits(uint32_t abits) {
+    if (abits == 0u || abits >= 0x7F800000u) return 1.0f;
+    float s = F8<FMT>::kMax / __uint_as_float(abits);
+    return s > 3.40282346638528859812e+38f ? 3.40282346638528859812e+38f : s;
+}
+
+// MX E8M0 byte (= X + 127) from the |amax| bit pattern. For a finite amax = 1.f * 2^E:
+// round-down X = E - emax; round-up adds 1 when 1.f > 1.75, which is ceil(log2(amax/F8max))
+// because F8max = 1.75 * 2^emax. X is clamped below at -127 (subnormal or zero amax); a
+// non-finite amax gives 0xFF.
+template <int FMT, int RND>
+__device__ __forceinline__ uint32_t mx_byte_bf16(uint32_t a) {
+    uint32_t e = a >> 7;
+    int inc = (RND == kRoundUp && (a & 0x7Fu) > 0x60u) ? 1 : 0;
+    int b = (int)e - F8<FMT>::kEmax + inc;
+    b = b < 0 ? 0 : b;
+    return e >= 255u ? 255u : (uint32_t)b;
+}
+template <int FMT, int RND>
+__device__ __forceinline__ uint32_t mx_byte_f32(uint32_t a) {
+    uint32_t e = a >> 23;
+    int inc = (RND == kRoundUp && (a & 0x7FFFFFu) > 0x600000u) ? 1 : 0;
+    int b = (int)e - F8<FMT>::kEmax + inc;
+    b = b < 0 ? 0 : b;
+    return e >= 255u ? 255u : (uint32_t)b;
+}
+// |bits| of F8max * 2^X, the round-down clamp bound (byte = X + 127 <= 254 - emax for finite
+// input, so the result is a finite normal value).
+template <int FMT>
+__device__ __forceinline__ uint32_t mx_clamp_bf16(uint32_t byte) {
+    return ((byte + F8<FMT>::kEmax) << 7) | 0x60u;
+}
+template <int FMT>
+__device__ __forceinline__ uint32_t mx_clamp_f32(uint32_t byte) {
+    return ((byte + F8<FMT>::kEmax) << 23) | 0x600000u;
+}
+
+}  // namespace qf8

@@ -1,0 +1,32 @@
+// qf8_internal.h -- host-side launchers shared between the kernel files and the C ABI layer.
+// Arguments are already validated by the ABI layer; each launcher only enqueues kernels and
+// returns QF8_OK or QF8_ERR_HIP.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+
+namespace qf8 {
+
+// Per-tensor / delayed geometry: number of workgroups of the streaming kernels for n elements.
+int stream_grid(int64_t n, int dtype);
+constexpr int kMaxStreamGrid = 2048;
+constexpr size_t kWorkspaceBytes = kMaxStreamGrid * sizeof(uint32_t);
+
+int launch_amax_partials(const void *x, int dtype, int64_t n, uint32_t *partials, int grid, hipStream_t s);
+int launch_cast_current(const void *x, int dtype, int64_t n, int fmt, uint8_t *q, const uint32_t *partials,
+                        int nparts, float *amax_out, float *scale_out, int32_t *nonfinite, int grid, hipStream_t s);
+int launch_cast_scaled(const void *x, int dtype, int64_t n, int fmt, const float *scale, uint8_t *q,
+                       float *scale_used, uint32_t *partials_out, int grid, hipStream_t s);
+int launch_delayed_finalize(const uint32_t *partials, int nparts, float *history, int32_t *meta, float *scale,
+                            int hist_len, int n_guard, int fmt, int update, float *amax_out,
+                            int32_t *nonfinite, hipStream_t s);
+int launch_fill_u32(uint32_t *p, int64_t n, uint32_t value, hipStream_t s);
+
+int launch_block(const void *x, int dtype, int64_t rows, int64_t cols, int block_rows, int fmt, uint8_t *q,
+                 float *scales, float *amax, int32_t *nonfinite, hipStream_t s);
+
+int launch_mx(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int rnd, uint8_t *q_row,
+              uint8_t *s_row, uint8_t *q_colT, uint8_t *s_colT, int32_t *nonfinite, hipStream_t s);
+
+}  // namespace qf8

@@ -1,0 +1,46 @@
+"""Helpers shared by the GPU parity tests: device transfer, byte comparison, parallel oracle runs."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import torch
+
+ORACLE_THREADS = min(16, os.cpu_count() or 1)
+
+
+def to_device(x, device="cuda"):
+    """numpy uint16 (BF16 bits) or float32 -> contiguous CUDA tensor holding the same bytes."""
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(device)
+    if x.dtype == np.float32:
+        return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+    raise TypeError(x.dtype)
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def assert_bytes_equal(got, want, name, extra=""):
+    got = np.asarray(got)
+    want = np.asarray(want)
+    assert got.shape == want.shape, f"{name}: shape {got.shape} != {want.shape}"
+    if np.array_equal(got.view(np.uint8) if got.dtype != np.uint8 else got,
+                      want.view(np.uint8) if want.dtype != np.uint8 else want):
+        return
+    g8 = got.reshape(-1).view(np.uint8) if got.dtype != np.uint8 else got.reshape(-1)
+    w8 = want.reshape(-1).view(np.uint8) if want.dtype != np.uint8 else want.reshape(-1)
+    bad = np.nonzero(g8 != w8)[0]
+    i = int(bad[0])
+    idx = np.unravel_index(i // max(1, got.dtype.itemsize), got.shape)
+    raise AssertionError(f"{name}{extra}: {len(bad)} differing bytes; first at index {tuple(int(v) for v in idx)}: "
+                         f"got {got.reshape(-1)[i // max(1, got.dtype.itemsize)]!r} "
+                         f"want {want.reshape(-1)[i // max(1, want.dtype.itemsize)]!r}")
+
+
+def parallel_row_slabs(fn, rows, slab):
+    """Run fn(r0, r1) over row slabs [r0, r1) of height `slab` (the oracle is single-threaded C;
+    ctypes releases the GIL, so slabs run concurrently). Returns the list of results in order."""
+    bounds = [(r, min(r + slab, rows)) for r in range(0, rows, slab)]
+    with ThreadPoolExecutor(ORACLE_THREADS) as ex:
+        return list(ex.map(lambda b: fn(*b), bounds))

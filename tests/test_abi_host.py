@@ -1,0 +1,101 @@
+"""Host-side checks of libqf8.so (no GPU needed, nothing is launched): the library loads, exports
+every function include/qf8.h declares, and rejects bad arguments with the documented status
+before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mx_block_scaled_amax_amd as qf8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qf8.h")
+
+OK, NULL, ENUM, SHAPE, ALIGN, WS, STATE = 0, -1, -2, -3, -4, -5, -6
+FAKE = ctypes.c_void_p(0x10000)          # 16-byte aligned, never dereferenced (rejected first)
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\([^;{]*\)\s*;", text)
+    return sorted(set(n for n in names if n not in ("if", "sizeof")))
+
+
+def lib():
+    qf8._load()
+    return qf8._lib
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"quantize_per_tensor", "quantize_delayed", "quantize_block", "quantize_mx_dual"} <= set(names)
+    L = ctypes.CDLL(qf8.library_path())
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for s in range(-7, 1):
+        assert qf8.qf8_status_string(s)
+    assert "unknown" in qf8.qf8_status_string(-99)
+    assert qf8.qf8_workspace_bytes(8192, 8192) >= 2048 * 4
+
+
+def test_mx_argument_errors():
+    f = lib().quantize_mx_dual
+    assert f(FAKE, 0, 64, 64, 2, 0, FAKE, FAKE, None, None, None, None) == ENUM    # bad fmt
+    assert f(FAKE, 3, 64, 64, 0, 0, FAKE, FAKE, None, None, None, None) == ENUM    # bad dtype
+    assert f(FAKE, 0, 64, 64, 0, 5, FAKE, FAKE, None, None, None, None) == ENUM    # bad rounding
+    assert f(FAKE, 0, 64, 64, 0, 0, None, None, None, None, None, None) == NULL    # no direction
+    assert f(FAKE, 0, 64, 64, 0, 0, FAKE, None, None, None, None, None) == NULL    # q without scales
+    assert f(FAKE, 0, 64, 48, 0, 0, FAKE, FAKE, None, None, None, None) == SHAPE   # rowwise cols % 32
+    assert f(FAKE, 0, 40, 64, 0, 0, None, None, FAKE, FAKE, None, None) == SHAPE   # colwise rows % 32
+    assert f(FAKE, 0, -1, 64, 0, 0, FAKE, FAKE, None, None, None, None) == SHAPE
+    assert f(MISALIGNED, 0, 64, 64, 0, 0, FAKE, FAKE, None, None, None, None) == ALIGN
+    assert f(None, 0, 64, 64, 0, 0, FAKE, FAKE, None, None, None, None) == NULL
+
+
+def test_per_tensor_argument_errors():
+    f = lib().quantize_per_tensor
+    fl = ctypes.c_void_p(0x20000)
+    assert f(FAKE, 0, 4, 4, 7, FAKE, fl, fl, None, FAKE, 1 << 20, None) == ENUM
+    assert f(FAKE, 0, 4, 4, 0, FAKE, None, fl, None, FAKE, 1 << 20, None) == NULL
+    assert f(FAKE, 0, 4, 4, 0, FAKE, fl, fl, None, FAKE, 16, None) == WS
+    assert f(FAKE, 0, 4, 4, 0, FAKE, fl, fl, None, None, 1 << 20, None) == WS
+    assert f(FAKE, 0, 4, 4, 0, MISALIGNED, fl, fl, None, FAKE, 1 << 20, None) == ALIGN
+    assert f(FAKE, 0, -4, 4, 0, FAKE, fl, fl, None, FAKE, 1 << 20, None) == SHAPE
+    g = lib().qf8_cast_scaled
+    assert g(FAKE, 0, 0, 0, None, None, None) == OK          # empty: nothing to do
+    assert g(FAKE, 0, 10, 0, None, FAKE, None) == NULL
+    assert g(FAKE, 0, -1, 0, fl, FAKE, None) == SHAPE
+
+
+def test_block_argument_errors():
+    f = lib().quantize_block
+    assert f(FAKE, 0, 128, 128, 2, 128, 0, FAKE, FAKE, None, None, None) == SHAPE   # block rows
+    assert f(FAKE, 0, 128, 128, 1, 64, 0, FAKE, FAKE, None, None, None) == SHAPE    # block cols
+    assert f(FAKE, 0, 128, 132, 1, 128, 0, FAKE, FAKE, None, None, None) == SHAPE   # cols % 8 (bf16)
+    assert f(FAKE, 0, 128, 128, 1, 128, 0, FAKE, None, None, None, None) == NULL
+    assert f(FAKE, 0, 0, 128, 1, 128, 0, None, None, None, None, None) == OK        # empty
+
+
+def test_delayed_state_errors():
+    st = qf8._DelayedStruct()
+    L = lib()
+    ref = ctypes.byref(st)
+    assert L.quantize_delayed(FAKE, 0, 4, 4, ref, FAKE, None, None, None, FAKE, 1 << 20, None) == STATE  # not initialised
+    assert L.qf8_delayed_init(ref, FAKE, FAKE, FAKE, 0, 1, 0, 0, None) == STATE       # hist_len 0
+    assert L.qf8_delayed_init(ref, FAKE, FAKE, FAKE, 16, 0, 0, 0, None) == STATE      # interval 0
+    assert L.qf8_delayed_init(ref, FAKE, FAKE, FAKE, 16, 1, 65, 0, None) == STATE     # n_guard too large
+    assert L.qf8_delayed_init(ref, FAKE, FAKE, FAKE, 16, 1, 0, 9, None) == ENUM
+    assert L.qf8_delayed_init(ref, None, FAKE, FAKE, 16, 1, 0, 0, None) == NULL
+    assert L.qf8_delayed_reset(None, None) == NULL
+
+
+def test_no_cpu_path():
+    import torch
+    with pytest.raises(TypeError):
+        qf8.quantize_mx_dual(torch.zeros(32, 32, dtype=torch.bfloat16), qf8.E4M3, qf8.ROUND_UP)

@@ -1,0 +1,159 @@
+"""GPU parity of quantize_delayed (device-resident amax history) against the oracle state machine.
+
+  * the hand-computed sequence of the oracle tests (history 3, Interval 2, N_guard 1) and the
+    delayed-spike worked example: codes, scales, amax, history after every step;
+  * long random sequences with several (history, Interval, N_guard) settings, both formats;
+  * reset (restart with current scaling), checkpoint/resume of the state, non-finite steps;
+  * the full drifting-std workload: 100 iterations of 4096x14336 (history 16, Interval 5,
+    N_guard 3, E4M3); every step's scale and amax bit-exact against the oracle state machine,
+    and the codes of several steps compared on every byte.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mx_block_scaled_amax_amd as qf8
+import oracle as O
+from synthetic import bf16_bits, delayed_base, delayed_sigmas, delayed_step_input, small_tensor
+from qf8_test_utils import assert_bytes_equal, host, parallel_row_slabs, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+class Pair:
+    """A GPU delayed state and the oracle state machine driven with the same inputs."""
+
+    def __init__(self, hist_len, interval, n_guard, fmt):
+        self.g = qf8.DelayedState(hist_len, interval, n_guard, fmt)
+        self.o = O.Delayed(hist_len, interval, n_guard, fmt)
+        self.fmt = fmt
+        self.nf = torch.zeros(1, dtype=torch.int32, device="cuda")
+        self.s = torch.zeros(1, dtype=torch.float32, device="cuda")
+        self.a = torch.zeros(1, dtype=torch.float32, device="cuda")
+
+    def step(self, x, tag=""):
+        self.nf.zero_()
+        xd = to_device(x)
+        q = qf8.quantize_delayed(xd, self.g, scale_used=self.s, amax_out=self.a, nonfinite=self.nf)
+        torch.cuda.synchronize()
+        wq, ws, wa, wnf = self.o.step(x)
+        assert np.float32(self.s.item()) == ws, f"scale {tag}: {self.s.item()!r} vs {ws!r}"
+        a = np.float32(self.a.item())
+        assert (a == wa) or (np.isnan(a) and np.isnan(wa)), f"amax {tag}"
+        assert int(self.nf.item()) == wnf
+        if not wnf:
+            assert_bytes_equal(host(q), wq, "q", f" [{tag}]")
+        h, c, st = self.o.state()
+        assert self.g.history_list() == list(h), f"history {tag}"
+        assert self.g.step == st
+        return q
+
+
+def tensor_with_amax(a):
+    return np.array([[a, -a / 2, 0.3 * a, -0.01 * a]], np.float32)
+
+
+def test_hand_sequence():
+    p = Pair(3, 2, 1, O.E4M3)
+    for t, a in enumerate([4, 8, 2, 16, 1, 32, 64, 0.5, 0.25, 128, 2]):
+        p.step(tensor_with_amax(a), f"t={t}")
+
+
+def test_spike_example():
+    p = Pair(16, 1, 0, O.E4M3)
+    p.step(np.array([[20.0, 1.0, -3.0]], np.float32), "t=0")
+    q = p.step(np.array([[50.0, 1.0]], np.float32), "t=1")
+    assert host(q)[0, 0] == 0x7E                       # 50 * 22.4 saturates to 448
+
+
+@pytest.mark.parametrize("hist,interval,guard,fmt", [(16, 5, 3, O.E4M3), (1, 1, 0, O.E5M2), (4, 3, 2, O.E4M3),
+                                                     (64, 7, 10, O.E5M2)])
+def test_random_sequences(hist, interval, guard, fmt):
+    rng = np.random.default_rng(hist * 100 + interval)
+    p = Pair(hist, interval, guard, fmt)
+    base = small_tensor(33, 72, seed=hist)
+    basef = (base.astype(np.uint32) << 16).view(np.float32)
+    for t in range(40):
+        x = bf16_bits(basef * np.float32(2.0 ** rng.uniform(-6, 6)))
+        p.step(x, f"t={t}")
+
+
+def test_reset_and_resume():
+    p = Pair(4, 2, 3, O.E4M3)
+    rng = np.random.default_rng(3)
+    xs = [small_tensor(16, 64, seed=i) for i in range(12)]
+    for t in range(5):
+        p.step(xs[t], f"t={t}")
+    # checkpoint: copy the device state and host counter
+    ck = (p.g.history.clone(), p.g.meta.clone(), p.g.scale.clone(), p.g.step)
+    ock = O.Delayed(4, 2, 3, O.E4M3)
+    ock._buf[:] = p.o._buf
+    for t in range(5, 9):
+        p.step(xs[t], f"t={t}")
+    after = [host(qf8.quantize_delayed(to_device(xs[9]), p.g)).copy()]
+    # resume from the checkpoint into a fresh state and replay: identical results
+    r = Pair(4, 2, 3, O.E4M3)
+    r.g.history.copy_(ck[0]); r.g.meta.copy_(ck[1]); r.g.scale.copy_(ck[2]); r.g.step = ck[3]
+    r.o = ock
+    for t in range(5, 9):
+        r.step(xs[t], f"resume t={t}")
+    assert np.array_equal(host(qf8.quantize_delayed(to_device(xs[9]), r.g)), after[0])
+    # reset: next step is current scaling, history restarts
+    qf8.qf8_delayed_reset(p.g)
+    p.o.reset()
+    p.step(xs[10], "after reset")
+    assert p.g.history_list() == [float(np.float32(O.amax(xs[10])))]
+
+
+def test_nonfinite_step_not_pushed():
+    p = Pair(4, 1, 0, O.E4M3)
+    p.step(small_tensor(8, 64, seed=1), "t=0")
+    x = small_tensor(8, 64, seed=2)
+    x[3, 3] = 0x7FC0
+    p.step(x, "nan step")
+    x[3, 3] = 0xFF80
+    p.step(x, "inf step")
+    p.step(small_tensor(8, 64, seed=3), "t=3")
+
+
+def test_fp32_and_ragged():
+    p = Pair(8, 2, 1, O.E5M2)
+    rng = np.random.default_rng(6)
+    for t in range(8):
+        x = (rng.standard_normal((13, 29)) * 10.0 ** rng.uniform(-3, 3)).astype(np.float32)
+        p.step(x, f"t={t}")
+
+
+def test_full_size_drifting_workload():
+    z = delayed_base()
+    sig = delayed_sigmas()
+    zd = torch.from_numpy(z).cuda()
+    st = qf8.DelayedState(16, 5, 3, qf8.E4M3)
+    orc = O.Delayed(16, 5, 3, O.E4M3)
+    s = torch.zeros(1, dtype=torch.float32, device="cuda")
+    a = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(qf8.qf8_workspace_bytes(*z.shape), dtype=torch.uint8, device="cuda")
+    q = torch.empty(z.shape, dtype=torch.uint8, device="cuda")
+    zmax = float(np.max(np.abs(z)))
+    full_steps = {0, 1, 5, 6, 50, 99}
+    rows = np.random.default_rng(0).choice(z.shape[0], 64, replace=False)
+    for t in range(100):
+        xd = (zd * float(sig[t])).to(torch.bfloat16)          # = bf16(fl32(sigma_t * Z))
+        qf8.quantize_delayed(xd, st, q=q, scale_used=s, amax_out=a, ws=ws)
+        torch.cuda.synchronize()
+        if t in (0, 50):   # the device-side input generation reproduces the host generator
+            assert np.array_equal(host(xd.view(torch.int16)).view(np.uint16)[rows],
+                                  delayed_step_input(z[rows], sig[t]))
+        # amax of bf16(sigma*Z) is bf16(sigma*max|Z|): rounding is monotone and odd
+        want_amax = np.float32((np.uint32(bf16_bits(np.array([np.float32(sig[t]) * np.float32(zmax)]))[0]) << 16).view(np.float32))
+        _, ws_o, wa_o, _ = orc.step(bf16_bits(np.array([[np.float32(sig[t]) * np.float32(zmax)]], np.float32)))
+        assert np.float32(a.item()) == want_amax == wa_o, f"amax t={t}"
+        assert np.float32(s.item()) == ws_o, f"scale t={t}"
+        if t in full_steps:
+            x = delayed_step_input(z, sig[t])
+            qh = host(q)
+            parts = parallel_row_slabs(lambda r0, r1: O.cast(x[r0:r1], O.E4M3, ws_o), z.shape[0], 256)
+            assert_bytes_equal(qh, np.concatenate(parts, axis=0), "q", f" [4096x14336 t={t}]")
+        h, c, stp = orc.state()
+        assert st.step == stp
+    assert st.history_list() == list(orc.state()[0])

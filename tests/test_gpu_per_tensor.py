@@ -1,0 +1,146 @@
+"""GPU parity of quantize_per_tensor and qf8_cast_scaled against the CPU oracle (bit-exact codes,
+amax and fp32 scale).
+
+  * the device encoder: every BF16 input times 1259 scales (powers of two over the whole fp32
+    exponent range, the pages' worked-example scales, random scales), and random FP32 inputs;
+  * the scale division: every positive finite BF16 amax -> S = fl32(F8max/amax);
+  * the 256x512 workload and the full 8192x8192 activation workload, E4M3 and E5M2;
+  * ragged and degenerate sizes: empty, one element, lengths that are not multiples of the
+    16-byte vector, all-zero input, amax so small that F8max/amax overflows, Inf/NaN flag.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mx_block_scaled_amax_amd as qf8
+import oracle as O
+from synthetic import bf16_to_f32, per_tensor_activation, per_tensor_small, small_tensor
+from qf8_test_utils import assert_bytes_equal, host, parallel_row_slabs, to_device
+
+pytestmark = pytest.mark.gpu
+FMTS = [O.E4M3, O.E5M2]
+
+
+def scale_set():
+    rng = np.random.default_rng(11)
+    s = [1.0, 22400.0, float(np.float32(448 / 20)), float(np.float32(448 / 50))]
+    s += [2.0 ** -k for k in range(-127, 128)]
+    s += list((2.0 ** rng.uniform(-40, 40, 1000)).astype(np.float32))
+    return np.array(s, np.float32)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_cast_exhaustive_bf16_times_scales(fmt):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    bits = bits[~np.isnan(bf16_to_f32(bits))]
+    xd = to_device(bits)
+    q = torch.empty(len(bits), dtype=torch.uint8, device="cuda")
+    sd = torch.empty(1, dtype=torch.float32, device="cuda")
+    for s in scale_set():
+        sd.fill_(float(s))
+        qf8.qf8_cast_scaled(xd, fmt, sd, q=q)
+        assert_bytes_equal(host(q), O.cast(bits, fmt, s), "q", f" [scale={s!r}]")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_cast_random_fp32(fmt):
+    rng = np.random.default_rng(2)
+    u = rng.integers(0, 2 ** 32, 1 << 20, dtype=np.uint64).astype(np.uint32)
+    x = u.view(np.float32).copy()
+    x[~np.isfinite(x)] = 0.0
+    xd = to_device(x)
+    sd = torch.empty(1, dtype=torch.float32, device="cuda")
+    for s in (1.0, 2.0 ** -100, 2.0 ** 100, 3.0e-20, 7.5e15):
+        sd.fill_(s)
+        q = qf8.qf8_cast_scaled(xd, fmt, sd)
+        assert_bytes_equal(host(q), O.cast(x, fmt, np.float32(s)), "q", f" [fp32 scale={s}]")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_scale_for_every_bf16_amax(fmt):
+    # one 1x128 group per amax value would also do; here a per-tensor call per value is too slow,
+    # so the block kernel's group scales (same division) are checked in test_gpu_block.py and the
+    # per-tensor path is checked on a spread of amax values
+    for a in (0x0001, 0x0080, 0x3C00, 0x3F80, 0x4000, 0x43E0, 0x43E1, 0x7F7F, 0x1234, 0x0A0A):
+        x = np.array([[a, 0x0000, a | 0x8000, 0x3F80 if a > 0x3F80 else 0x0000]], np.uint16)
+        q, am, s = qf8.quantize_per_tensor(to_device(x), fmt)
+        wq, wa, ws, _ = O.quantize_per_tensor(x, fmt)
+        assert am.item() == wa and np.float32(s.item()) == ws, hex(a)
+        assert_bytes_equal(host(q), wq, "q", f" [amax bits {a:#x}]")
+
+
+def run_pt(x, fmt):
+    xd = to_device(x)
+    nf = torch.zeros(1, dtype=torch.int32, device="cuda")
+    q = torch.full(x.shape, 0xA5, dtype=torch.uint8, device="cuda")
+    q, am, s = qf8.quantize_per_tensor(xd, fmt, q=q, nonfinite=nf)
+    torch.cuda.synchronize()
+    return host(q), np.float32(am.item()), np.float32(s.item()), int(nf.item())
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_small_workload(fmt):
+    x = per_tensor_small()
+    q, am, s, nf = run_pt(x, fmt)
+    wq, wa, ws, wnf = O.quantize_per_tensor(x, fmt)
+    assert (am, s, nf) == (wa, ws, wnf)
+    assert_bytes_equal(q, wq, "q")
+
+
+@pytest.mark.parametrize("shape", [(0, 0), (1, 1), (1, 7), (3, 5), (7, 9), (1, 1031), (13, 333), (1, 8 * 1024 * 1024 + 3)])
+@pytest.mark.parametrize("fmt", FMTS)
+def test_ragged_sizes(shape, fmt):
+    x = small_tensor(*shape, seed=shape[0] * 7 + shape[1]) if shape[0] * shape[1] else np.zeros(shape, np.uint16)
+    q, am, s, nf = run_pt(x, fmt)
+    wq, wa, ws, wnf = O.quantize_per_tensor(x, fmt)
+    assert (am, s, nf) == (wa, ws, wnf)
+    assert_bytes_equal(q, wq, "q", f" [{shape}]")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_fp32_input(fmt):
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((100, 37)) * np.where(rng.random((100, 37)) < 0.01, 300, 1)).astype(np.float32)
+    q, am, s, nf = run_pt(x, fmt)
+    wq, wa, ws, wnf = O.quantize_per_tensor(x, fmt)
+    assert (am, s, nf) == (wa, ws, wnf)
+    assert_bytes_equal(q, wq, "q")
+
+
+def test_degenerate_amax():
+    z = np.zeros((4, 64), np.uint16)
+    z[1, 3] = 0x8000
+    q, am, s, nf = run_pt(z, O.E4M3)
+    assert am == 0 and s == 1.0 and nf == 0
+    assert_bytes_equal(q, O.quantize_per_tensor(z, O.E4M3)[0], "q")
+    tiny = np.zeros((2, 16), np.uint16)
+    tiny[0, 0] = 0x0003                   # subnormal amax: F8max/amax overflows fp32
+    q, am, s, nf = run_pt(tiny, O.E4M3)
+    assert s == np.finfo(np.float32).max
+    assert_bytes_equal(q, O.quantize_per_tensor(tiny, O.E4M3)[0], "q")
+
+
+def test_nonfinite_flag():
+    x = small_tensor(8, 64, seed=1)
+    x[2, 2] = 0x7F80
+    q, am, s, nf = run_pt(x, O.E4M3)
+    assert nf == 1 and np.isinf(am) and s == 1.0
+    x[2, 2] = 0xFFC0
+    q, am, s, nf = run_pt(x, O.E5M2)
+    assert nf == 1 and np.isnan(am)
+
+
+@pytest.fixture(scope="module")
+def activation_full():
+    return per_tensor_activation()
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_full_size_activation(activation_full, fmt):
+    x = activation_full
+    q, am, s, nf = run_pt(x, fmt)
+    wa = np.float32(O.amax(x))
+    ws = np.float32(O.scale_from_amax(fmt, wa))
+    assert am == wa and s == ws and nf == 0
+    parts = parallel_row_slabs(lambda r0, r1: O.cast(x[r0:r1], fmt, ws), x.shape[0], 512)
+    assert_bytes_equal(q, np.concatenate(parts, axis=0), "q", " [8192x8192]")
