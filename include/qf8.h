@@ -140,7 +140,8 @@ int quantize_block(const void *x, int dtype, int64_t rows, int64_t cols, int blo
  *   columnwise (q_colT non-NULL): blocks run down a column and are stored transposed:
  *             q_colT [cols][rows], s_colT [cols][rows/32]; needs rows % 32 == 0.
  * At least one direction; s_row / s_colT are required with their q. x, q_row, q_colT 16-byte
- * aligned. A block holding Inf or NaN gets scale byte 0xFF and sets nonfinite. */
+ * aligned; rows, cols <= 2^24. A block holding Inf or NaN gets scale byte 0xFF and sets
+ * nonfinite. One kernel launch for either or both directions. */
 int quantize_mx_dual(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int rnd,
                      uint8_t *q_row, uint8_t *s_row, uint8_t *q_colT, uint8_t *s_colT,
                      int32_t *nonfinite, void *stream);

@@ -12,6 +12,7 @@ namespace {
 constexpr int32_t kDelayedMagic = 0x51463844;  // "QF8D"
 constexpr int kMaxHistory = 4096;
 constexpr int kMaxGuard = 64;
+constexpr int64_t kMaxMxDim = 1 << 24;   // keeps every per-wave buffer offset below 2^31
 
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 inline bool fmt_ok(int fmt) { return fmt == QF8_E4M3 || fmt == QF8_E5M2; }
@@ -174,7 +175,7 @@ int quantize_block(const void *x, int dtype, int64_t rows, int64_t cols, int blo
 int quantize_mx_dual(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int rnd, uint8_t *q_row,
                      uint8_t *s_row, uint8_t *q_colT, uint8_t *s_colT, int32_t *nonfinite, void *stream) {
     if (!dtype_ok(dtype) || !fmt_ok(fmt) || (rnd != QF8_MX_ROUND_DOWN && rnd != QF8_MX_ROUND_UP)) return QF8_ERR_ENUM;
-    if (!dims_ok(rows, cols) || rows > INT32_MAX || cols > INT32_MAX) return QF8_ERR_SHAPE;
+    if (!dims_ok(rows, cols) || rows > kMaxMxDim || cols > kMaxMxDim) return QF8_ERR_SHAPE;
     if (!q_row && !q_colT) return QF8_ERR_NULL;
     if ((q_row && !s_row) || (q_colT && !s_colT)) return QF8_ERR_NULL;
     if (q_row && cols % 32 != 0) return QF8_ERR_SHAPE;

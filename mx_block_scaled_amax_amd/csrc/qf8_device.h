@@ -159,23 +159,21 @@ __device__ __forceinline__ float scale_from_amax_bits(uint32_t abits) {
 
 // MX E8M0 byte (= X + 127) from the |amax| bit pattern. For a finite amax = 1.f * 2^E:
 // round-down X = E - emax; round-up adds 1 when 1.f > 1.75, which is ceil(log2(amax/F8max))
-// because F8max = 1.75 * 2^emax. X is clamped below at -127 (subnormal or zero amax); a
-// non-finite amax gives 0xFF.
+// because F8max = 1.75 * 2^emax. With e = the biased exponent field, round-up's "e + (1.f > 1.75)"
+// is one carry: adding 0x1F (BF16) or 0x1FFFFF (FP32) to the bits carries into the exponent
+// exactly when the 7 (23) mantissa bits exceed those of 1.75. X is clamped below at -127
+// (subnormal or zero amax) by a saturating subtraction; a non-finite amax gives 0xFF.
 template <int FMT, int RND>
 __device__ __forceinline__ uint32_t mx_byte_bf16(uint32_t a) {
-    uint32_t e = a >> 7;
-    int inc = (RND == kRoundUp && (a & 0x7Fu) > 0x60u) ? 1 : 0;
-    int b = (int)e - F8<FMT>::kEmax + inc;
-    b = b < 0 ? 0 : b;
-    return e >= 255u ? 255u : (uint32_t)b;
+    const uint32_t e = (RND == kRoundUp ? a + 0x1Fu : a) >> 7;
+    const uint32_t b = e > (uint32_t)F8<FMT>::kEmax ? e - F8<FMT>::kEmax : 0u;
+    return a >= 0x7F80u ? 255u : b;
 }
 template <int FMT, int RND>
 __device__ __forceinline__ uint32_t mx_byte_f32(uint32_t a) {
-    uint32_t e = a >> 23;
-    int inc = (RND == kRoundUp && (a & 0x7FFFFFu) > 0x600000u) ? 1 : 0;
-    int b = (int)e - F8<FMT>::kEmax + inc;
-    b = b < 0 ? 0 : b;
-    return e >= 255u ? 255u : (uint32_t)b;
+    const uint32_t e = (RND == kRoundUp ? a + 0x1FFFFFu : a) >> 23;
+    const uint32_t b = e > (uint32_t)F8<FMT>::kEmax ? e - F8<FMT>::kEmax : 0u;
+    return a >= 0x7F800000u ? 255u : b;
 }
 // |bits| of F8max * 2^X, the round-down clamp bound (byte = X + 127 <= 254 - emax for finite
 // input, so the result is a finite normal value).
@@ -186,6 +184,46 @@ __device__ __forceinline__ uint32_t mx_clamp_bf16(uint32_t byte) {
 template <int FMT>
 __device__ __forceinline__ uint32_t mx_clamp_f32(uint32_t byte) {
     return ((byte + F8<FMT>::kEmax) << 23) | 0x600000u;
+}
+
+// ---- buffer resources ------------------------------------------------------------------------
+// Raw buffer descriptors (stride 0): addresses are base + voffset (per lane) + soffset (uniform),
+// and any access whose offset reaches num_records is dropped (loads return 0). Kernels set the
+// per-lane offset of idle lanes to kOutOfRange instead of branching around their accesses.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u32 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t num_bytes) {
+    // dword3 0x00020000: 32-bit data format, the value gfx9-family raw buffers use
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)num_bytes, 0x00020000);
+}
+// Cache policy operand: kCached (default) or kNonTemporal, the hint for data read once or
+// written once in whole lines. Partial-line stores stay cached so that L2 can merge them.
+constexpr int kCached = 0;
+constexpr int kNonTemporal = 2;
+template <int CP = kCached>
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    v4u32 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, CP);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <int CP = kCached>
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint4 v) {
+    v4u32 w = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, (int)voff, (int)soff, CP);
+}
+template <int CP = kCached>
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t lo, uint32_t hi) {
+    v2u32 w = {lo, hi};
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, (int)voff, (int)soff, CP);
+}
+template <int CP = kCached>
+__device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t v) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)voff, (int)soff, CP);
+}
+template <int CP = kCached>
+__device__ __forceinline__ void buf_store1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t v) {
+    __builtin_amdgcn_raw_buffer_store_b8((unsigned char)v, r, (int)voff, (int)soff, CP);
 }
 
 }  // namespace qf8

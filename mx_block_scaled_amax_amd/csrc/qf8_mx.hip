@@ -12,20 +12,27 @@
 //                  V/2^X), section 4.2 (each tensor kept quantized along both reduction axes).
 //
 // Work decomposition (one HBM read of x, every output written once):
-//   A workgroup owns a tile of 128 rows x (64 * VEC) columns (VEC = 8 BF16 or 4 FP32 values per
-//   16-byte load); each of its 4 waves owns 32 consecutive rows of the tile, and each lane owns
-//   VEC consecutive columns of those rows, held in 32 x 16-byte registers.
-//   * Columnwise blocks (32 rows x 1 column) are then entirely inside one lane: the block amax
-//     is a register-only reduction, and the lane writes each column's 32 codes as 32
-//     contiguous bytes of the transposed output q_colT[c][r0 .. r0+31].
-//   * Rowwise blocks (1 row x 32 columns) span 32/VEC lanes (4 for BF16): the amax is two (or
-//     three) DPP steps, and each lane writes its VEC codes of the row.
+//   A workgroup owns a tile of 128 rows x (32 * VEC) columns (VEC = 8 BF16 or 4 FP32 values per
+//   16-byte load); each of its 4 waves owns 32 consecutive rows of the tile. Lane l of a wave
+//   owns VEC consecutive columns (column slot l % 32) of 16 rows (half l / 32 of the wave's
+//   rows), held in 16 x 16-byte registers.
+//   * A rowwise block (1 row x 32 columns) spans 32/VEC lanes (4 for BF16): its amax takes two
+//     (or three) DPP steps, and each lane writes its VEC codes of the row.
+//   * A columnwise block (32 rows x 1 column) is split over lanes l and l ^ 32: each lane folds
+//     its 16 rows in registers and one cross-half exchange completes the amax. The lane's 16
+//     codes per column go to an LDS tile [column][128 rows]; after a barrier the workgroup
+//     writes every column's 128 rows of q_colT as whole 128-byte lines, and the E8M0 bytes of
+//     both directions, also gathered in LDS, as 4- or 8-byte runs.
 //   * The conversion is the gfx950 scaled convert (two values per instruction, divided by 2^X
 //     given as an fp32 exponent); OCP round-down first clamps |x| to F8max * 2^X on the bit
 //     pattern, since the instruction does not saturate. Round-up never exceeds F8max.
+//   * All global accesses are raw-buffer operations on per-wave descriptors: row and column
+//     strides become scalar offsets, lanes outside the tensor get an out-of-range offset (their
+//     loads read 0, their stores are dropped), and no per-row 64-bit address math is needed.
+//     The input loads and the whole-line q_colT stores carry the non-temporal hint.
 //   * Tiles are assigned so that each of the 8 XCDs (workgroups are dealt to XCDs round-robin)
-//     receives a contiguous band of rows: the E8M0 rows and column-pieces written by
-//     neighbouring tiles then meet in the same L2.
+//     receives a contiguous band of rows: the E8M0 rows and columns written by neighbouring
+//     tiles then meet in the same L2.
 #include "qf8_device.h"
 #include "qf8_internal.h"
 #include "../../include/qf8.h"
@@ -36,6 +43,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTileRows = 128;
 constexpr int kRowsPerWave = 32;
+constexpr int kRowsPerLane = kRowsPerWave / 2;
 
 template <bool BF16, int FMT, int RND>
 __device__ __forceinline__ uint32_t mx_byte(uint32_t absbits) {
@@ -43,160 +51,256 @@ __device__ __forceinline__ uint32_t mx_byte(uint32_t absbits) {
     else return mx_byte_f32<FMT, RND>(absbits);
 }
 
+// Byte offset of 16-row chunk k of tile column c in the LDS staging tile: one 128-byte line per
+// column, chunks permuted by column so that the lanes of one LDS write spread over the banks.
+__device__ __forceinline__ int colbuf_offset(int c, int k) { return c * kTileRows + ((k ^ ((c >> 3) & 7)) << 4); }
+
 template <bool BF16, int FMT, int RND, bool ROW, bool COL>
-__global__ __launch_bounds__(kThreads) void mx_kernel(const uint4 *__restrict__ x, int rows, int cols,
+__global__ __launch_bounds__(kThreads) void mx_kernel(const void *__restrict__ x, int rows, int cols,
                                                       uint8_t *__restrict__ q_row, uint8_t *__restrict__ s_row,
                                                       uint8_t *__restrict__ q_colT, uint8_t *__restrict__ s_colT,
                                                       int32_t *nonfinite, int tiles_c, int tiles, int per_xcd) {
-    constexpr int VEC = BF16 ? 8 : 4;            // values per lane per row
+    constexpr int VEC = BF16 ? 8 : 4;            // values per lane per row (one 16-byte load)
+    constexpr int ESZ = BF16 ? 2 : 4;            // bytes per input element
     constexpr int LPB = 32 / VEC;                // lanes per rowwise block
+    constexpr int RPL = kRowsPerLane;
+    constexpr int TILE_C = 32 * VEC;             // columns per tile
+    constexpr int NBLK = TILE_C / 32;            // rowwise blocks per tile row
     constexpr uint32_t ABS = BF16 ? 0x7FFF7FFFu : 0x7FFFFFFFu;
+
+    // LDS staging (columnwise pass only): codes [column][128 rows] (16-byte chunks swizzled),
+    // E8M0 bytes of the columnwise blocks [column][4 row blocks] and of the rowwise blocks
+    // [tile row][NBLK]
+    __shared__ __attribute__((aligned(16))) uint8_t colbuf[COL ? TILE_C * kTileRows : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t scol[COL ? TILE_C * 4 : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t srow[(ROW && COL) ? kTileRows * NBLK : 16];
 
     const int b = blockIdx.x, xcd = b & 7, local = b >> 3;
     const int t = xcd * per_xcd + local;
     if (local >= per_xcd || t >= tiles) return;  // whole workgroup idle
     const int tr = t / tiles_c, tc = t - tr * tiles_c;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int r0 = tr * kTileRows + wave * kRowsPerWave;
-    if (r0 >= rows) return;                      // whole wave idle
-    const int c0 = (tc * 64 + lane) * VEC;
-    const bool active = c0 < cols;               // whole rowwise blocks: cols % 32 == 0
-    const int vcols = cols / VEC;
-
-    // ---- load 32 rows x 16 bytes ----------------------------------------------------------
-    uint32_t d[kRowsPerWave][4];
-    const uint4 *p = x + (int64_t)r0 * vcols + c0 / VEC;
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (active && r0 + i < rows) v = p[(int64_t)i * vcols];
-        d[i][0] = v.x; d[i][1] = v.y; d[i][2] = v.z; d[i][3] = v.w;
-    }
-
-    uint32_t cmax[4] = {0, 0, 0, 0};             // columnwise |x| maxima (BF16: two per dword)
+    const int tr0 = tr * kTileRows;              // first row of the tile
+    const int ct0 = tc * TILE_C;                 // first column of the tile
+    const int ncv = cols - ct0 < TILE_C ? cols - ct0 : TILE_C;          // valid columns of the tile
+    const int trows = rows - tr0 < kTileRows ? rows - tr0 : kTileRows;  // valid rows of the tile
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63, half = lane >> 5, slot = lane & 31;
+    const int r0 = tr0 + wave * kRowsPerWave;   // first row of the wave (uniform)
     bool bad = false;
 
-    // ---- rowwise blocks, one row at a time; columnwise maxima accumulate -----------------
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-        uint32_t m[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) m[k] = d[i][k] & ABS;
-        if constexpr (COL) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) cmax[k] = BF16 ? pk_max_u16(cmax[k], m[k]) : umax(cmax[k], m[k]);
-        }
-        if constexpr (ROW) {
-            uint32_t a;
-            if constexpr (BF16) {
-                const uint32_t mm = pk_max_u16(pk_max_u16(m[0], m[1]), pk_max_u16(m[2], m[3]));
-                a = max_quad(umax(mm & 0xFFFFu, mm >> 16));
-            } else {
-                a = max_oct(umax(umax(m[0], m[1]), umax(m[2], m[3])));
-            }
-            const uint32_t byte = mx_byte<BF16, FMT, RND>(a);
-            bad |= byte == 255u;
-            const float sc = __uint_as_float(byte << 23);
-            const uint32_t zero_mask = a == 0u ? 0u : ~0u;            // all-zero block -> 0x00
-            uint32_t v[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) v[k] = d[i][k];
-            if constexpr (RND == kRoundDown) {                          // saturate before the cast
-                if constexpr (BF16) {
-                    const uint32_t cb = mx_clamp_bf16<FMT>(byte), cbp = cb | (cb << 16);
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) v[k] = bit_select(ABS, pk_min_u16(m[k], cbp), v[k]);
-                } else {
-                    const uint32_t cb = mx_clamp_f32<FMT>(byte);
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) v[k] = bit_select(ABS, umin(m[k], cb), v[k]);
-                }
-            }
-            const bool st = active && r0 + i < rows;
-            uint8_t *qr = q_row + (int64_t)(r0 + i) * cols + c0;
-            if constexpr (BF16) {
-                uint32_t o0 = cvt2_bf16_div2x<FMT, true>(v[1], sc, cvt2_bf16_div2x<FMT, false>(v[0], sc, 0u));
-                uint32_t o1 = cvt2_bf16_div2x<FMT, true>(v[3], sc, cvt2_bf16_div2x<FMT, false>(v[2], sc, 0u));
-                if (st) *(uint2 *)qr = make_uint2(o0 & zero_mask, o1 & zero_mask);
-            } else {
-                uint32_t o0 = cvt2_f32_div2x<FMT, true>(__uint_as_float(v[2]), __uint_as_float(v[3]), sc,
-                              cvt2_f32_div2x<FMT, false>(__uint_as_float(v[0]), __uint_as_float(v[1]), sc, 0u));
-                if (st) *(uint32_t *)qr = o0 & zero_mask;
-            }
-            // one lane of each block writes the scale byte; the lanes take turns by row
-            if (st && (lane & (LPB - 1)) == (i & (LPB - 1)))
-                s_row[(int64_t)(r0 + i) * (cols / 32) + c0 / 32] = (uint8_t)byte;
-        }
-    }
+    if (r0 < rows) {                             // else the wave only joins the barrier
+        const int c0 = ct0 + slot * VEC;         // first column of the lane
+        const bool active = c0 < cols;           // rowwise blocks are whole: cols % 32 == 0
+        const int wrows = rows - r0 < kRowsPerWave ? rows - r0 : kRowsPerWave;
 
-    // ---- columnwise blocks: VEC columns x 32 rows per lane ---------------------------------
-    if constexpr (COL) {
-        const int64_t srow = rows / 32;
-        if constexpr (BF16) {
+        // ---- load 16 rows x 16 bytes -----------------------------------------------------
+        const uint32_t rowbytes = (uint32_t)cols * ESZ;
+        const __amdgpu_buffer_rsrc_t xr = make_rsrc((const char *)x + (size_t)r0 * rowbytes,
+                                                    (uint32_t)wrows * rowbytes);
+        const uint32_t xvo = active ? (uint32_t)(half * RPL) * rowbytes + (uint32_t)c0 * ESZ : kOutOfRange;
+        uint32_t d[RPL][4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {                 // dword k holds columns 2k (low) and 2k+1
-                const uint32_t alo = cmax[k] & 0xFFFFu, ahi = cmax[k] >> 16;
-                const uint32_t blo = mx_byte<true, FMT, RND>(alo), bhi = mx_byte<true, FMT, RND>(ahi);
-                bad |= (blo == 255u) | (bhi == 255u);
-                const float slo = __uint_as_float(blo << 23), shi = __uint_as_float(bhi << 23);
-                const uint32_t zlo = alo == 0u ? 0u : ~0u, zhi = ahi == 0u ? 0u : ~0u;
-                uint32_t cbp = 0;
-                if constexpr (RND == kRoundDown) cbp = mx_clamp_bf16<FMT>(blo) | (mx_clamp_bf16<FMT>(bhi) << 16);
-                uint32_t olo[8], ohi[8];
+        for (int i = 0; i < RPL; ++i) {
+            const uint4 v = buf_load16<kNonTemporal>(xr, xvo, (uint32_t)i * rowbytes);
+            d[i][0] = v.x; d[i][1] = v.y; d[i][2] = v.z; d[i][3] = v.w;
+        }
+
+        uint32_t cmax[4] = {0, 0, 0, 0};         // columnwise |x| maxima (BF16: two per dword)
+
+        // ---- rowwise blocks, one row at a time; columnwise maxima accumulate -------------
+        if constexpr (ROW) {
+            const __amdgpu_buffer_rsrc_t qr = make_rsrc(q_row + (size_t)r0 * cols, (uint32_t)wrows * cols);
+            const uint32_t qvo = active ? (uint32_t)(half * RPL) * cols + c0 : kOutOfRange;
+            const uint32_t sstride = cols / 32;
+            const __amdgpu_buffer_rsrc_t sr = make_rsrc(s_row + (size_t)r0 * sstride, (uint32_t)wrows * sstride);
+            const uint32_t svo = active ? (uint32_t)(half * RPL) * sstride + c0 / 32 : kOutOfRange;
 #pragma unroll
-                for (int g = 0; g < 8; ++g) {             // rows 4g .. 4g+3
-                    uint32_t w[4];
+            for (int i = 0; i < RPL; ++i) {
+                uint32_t m[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        w[j] = d[4 * g + j][k];
-                        if constexpr (RND == kRoundDown) w[j] = bit_select(ABS, pk_min_u16(w[j] & ABS, cbp), w[j]);
-                    }
-                    // gather one column's values of two consecutive rows into one dword
-                    const uint32_t l01 = __builtin_amdgcn_perm(w[1], w[0], 0x05040100u);
-                    const uint32_t l23 = __builtin_amdgcn_perm(w[3], w[2], 0x05040100u);
-                    const uint32_t h01 = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);
-                    const uint32_t h23 = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
-                    olo[g] = cvt2_bf16_div2x<FMT, true>(l23, slo, cvt2_bf16_div2x<FMT, false>(l01, slo, 0u)) & zlo;
-                    ohi[g] = cvt2_bf16_div2x<FMT, true>(h23, shi, cvt2_bf16_div2x<FMT, false>(h01, shi, 0u)) & zhi;
+                for (int k = 0; k < 4; ++k) m[k] = d[i][k] & ABS;
+                if constexpr (COL) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) cmax[k] = BF16 ? pk_max_u16(cmax[k], m[k]) : umax(cmax[k], m[k]);
                 }
-                if (active) {
-                    uint4 *ql = (uint4 *)(q_colT + (int64_t)(c0 + 2 * k) * rows + r0);
-                    uint4 *qh = (uint4 *)(q_colT + (int64_t)(c0 + 2 * k + 1) * rows + r0);
-                    ql[0] = make_uint4(olo[0], olo[1], olo[2], olo[3]);
-                    ql[1] = make_uint4(olo[4], olo[5], olo[6], olo[7]);
-                    qh[0] = make_uint4(ohi[0], ohi[1], ohi[2], ohi[3]);
-                    qh[1] = make_uint4(ohi[4], ohi[5], ohi[6], ohi[7]);
-                    s_colT[(int64_t)(c0 + 2 * k) * srow + r0 / 32] = (uint8_t)blo;
-                    s_colT[(int64_t)(c0 + 2 * k + 1) * srow + r0 / 32] = (uint8_t)bhi;
+                uint32_t a;
+                if constexpr (BF16) {
+                    const uint32_t mm = pk_max_u16(pk_max_u16(m[0], m[1]), pk_max_u16(m[2], m[3]));
+                    a = max_quad(umax(mm & 0xFFFFu, mm >> 16));
+                } else {
+                    a = max_oct(umax(umax(m[0], m[1]), umax(m[2], m[3])));
+                }
+                const uint32_t byte = mx_byte<BF16, FMT, RND>(a);
+                bad |= byte == 255u;
+                const float sc = __uint_as_float(byte << 23);
+                const uint32_t zero_mask = a == 0u ? 0u : ~0u;        // all-zero block -> 0x00
+                uint32_t v[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) v[k] = d[i][k];
+                if constexpr (RND == kRoundDown) {                      // saturate before the cast
+                    if constexpr (BF16) {
+                        const uint32_t cb = mx_clamp_bf16<FMT>(byte), cbp = cb | (cb << 16);
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) v[k] = bit_select(ABS, pk_min_u16(m[k], cbp), v[k]);
+                    } else {
+                        const uint32_t cb = mx_clamp_f32<FMT>(byte);
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) v[k] = bit_select(ABS, umin(m[k], cb), v[k]);
+                    }
+                }
+                if constexpr (BF16) {
+                    const uint32_t o0 = cvt2_bf16_div2x<FMT, true>(v[1], sc, cvt2_bf16_div2x<FMT, false>(v[0], sc, 0u));
+                    const uint32_t o1 = cvt2_bf16_div2x<FMT, true>(v[3], sc, cvt2_bf16_div2x<FMT, false>(v[2], sc, 0u));
+                    buf_store8(qr, qvo, (uint32_t)i * cols, o0 & zero_mask, o1 & zero_mask);
+                } else {
+                    const uint32_t o0 = cvt2_f32_div2x<FMT, true>(__uint_as_float(v[2]), __uint_as_float(v[3]), sc,
+                                        cvt2_f32_div2x<FMT, false>(__uint_as_float(v[0]), __uint_as_float(v[1]), sc, 0u));
+                    buf_store4(qr, qvo, (uint32_t)i * cols, o0 & zero_mask);
+                }
+                if constexpr (COL) {
+                    // every lane of the block writes the same byte to the same LDS slot
+                    srow[(wave * kRowsPerWave + half * RPL + i) * NBLK + slot / LPB] = (uint8_t)byte;
+                } else {
+                    // one lane of each block writes the scale byte; the lanes take turns by row
+                    if ((slot & (LPB - 1)) == (i & (LPB - 1))) buf_store1(sr, svo, (uint32_t)i * sstride, byte);
                 }
             }
         } else {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {                 // column c0 + k
-                const uint32_t a = cmax[k];
-                const uint32_t byte = mx_byte<false, FMT, RND>(a);
-                bad |= byte == 255u;
-                const float sc = __uint_as_float(byte << 23);
-                const uint32_t zm = a == 0u ? 0u : ~0u;
-                uint32_t cb = 0;
-                if constexpr (RND == kRoundDown) cb = mx_clamp_f32<FMT>(byte);
-                uint32_t o[8];
+            for (int i = 0; i < RPL; ++i)
 #pragma unroll
-                for (int g = 0; g < 8; ++g) {
-                    float f[4];
+                for (int k = 0; k < 4; ++k)
+                    cmax[k] = BF16 ? pk_max_u16(cmax[k], d[i][k] & ABS) : umax(cmax[k], d[i][k] & ABS);
+        }
+
+        // ---- columnwise blocks: VEC columns x 16 rows per lane, the other 16 rows in lane ^ 32
+        if constexpr (COL) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        uint32_t w = d[4 * g + j][k];
-                        if constexpr (RND == kRoundDown) w = bit_select(ABS, umin(w & ABS, cb), w);
-                        f[j] = __uint_as_float(w);
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t other = (uint32_t)__shfl_xor((int)cmax[k], 32);
+                cmax[k] = BF16 ? pk_max_u16(cmax[k], other) : umax(cmax[k], other);
+            }
+            const int chunk = wave * 2 + half;   // 16-row chunk of the tile
+            if constexpr (BF16) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {     // dword k holds columns 2k (low half) and 2k+1
+                    const uint32_t alo = cmax[k] & 0xFFFFu, ahi = cmax[k] >> 16;
+                    const uint32_t blo = mx_byte<true, FMT, RND>(alo), bhi = mx_byte<true, FMT, RND>(ahi);
+                    bad |= (blo == 255u) | (bhi == 255u);
+                    const float slo = __uint_as_float(blo << 23), shi = __uint_as_float(bhi << 23);
+                    const uint32_t zlo = alo == 0u ? 0u : ~0u, zhi = ahi == 0u ? 0u : ~0u;
+                    uint32_t cbp = 0;
+                    if constexpr (RND == kRoundDown) cbp = mx_clamp_bf16<FMT>(blo) | (mx_clamp_bf16<FMT>(bhi) << 16);
+                    uint32_t olo[4], ohi[4];
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {     // rows 4g .. 4g+3 of the lane
+                        uint32_t w[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            w[j] = d[4 * g + j][k];
+                            if constexpr (RND == kRoundDown) w[j] = bit_select(ABS, pk_min_u16(w[j] & ABS, cbp), w[j]);
+                        }
+                        // one column's values of two consecutive rows in one dword
+                        const uint32_t l01 = __builtin_amdgcn_perm(w[1], w[0], 0x05040100u);
+                        const uint32_t l23 = __builtin_amdgcn_perm(w[3], w[2], 0x05040100u);
+                        const uint32_t h01 = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);
+                        const uint32_t h23 = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
+                        olo[g] = cvt2_bf16_div2x<FMT, true>(l23, slo, cvt2_bf16_div2x<FMT, false>(l01, slo, 0u)) & zlo;
+                        ohi[g] = cvt2_bf16_div2x<FMT, true>(h23, shi, cvt2_bf16_div2x<FMT, false>(h01, shi, 0u)) & zhi;
                     }
-                    o[g] = cvt2_f32_div2x<FMT, true>(f[2], f[3], sc, cvt2_f32_div2x<FMT, false>(f[0], f[1], sc, 0u)) & zm;
+                    const int clo = slot * VEC + 2 * k;           // tile column of the low half
+                    *(uint4 *)(colbuf + colbuf_offset(clo, chunk)) = make_uint4(olo[0], olo[1], olo[2], olo[3]);
+                    *(uint4 *)(colbuf + colbuf_offset(clo + 1, chunk)) = make_uint4(ohi[0], ohi[1], ohi[2], ohi[3]);
+                    if (half == 0) {
+                        scol[clo * 4 + wave] = (uint8_t)blo;
+                        scol[(clo + 1) * 4 + wave] = (uint8_t)bhi;
+                    }
                 }
-                if (active) {
-                    uint4 *qc = (uint4 *)(q_colT + (int64_t)(c0 + k) * rows + r0);
-                    qc[0] = make_uint4(o[0], o[1], o[2], o[3]);
-                    qc[1] = make_uint4(o[4], o[5], o[6], o[7]);
-                    s_colT[(int64_t)(c0 + k) * srow + r0 / 32] = (uint8_t)byte;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {     // tile column slot * 4 + k
+                    const uint32_t a = cmax[k];
+                    const uint32_t byte = mx_byte<false, FMT, RND>(a);
+                    bad |= byte == 255u;
+                    const float sc = __uint_as_float(byte << 23);
+                    const uint32_t zm = a == 0u ? 0u : ~0u;
+                    uint32_t cb = 0;
+                    if constexpr (RND == kRoundDown) cb = mx_clamp_f32<FMT>(byte);
+                    uint32_t o[4];
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float f[4];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            uint32_t w = d[4 * g + j][k];
+                            if constexpr (RND == kRoundDown) w = bit_select(ABS, umin(w & ABS, cb), w);
+                            f[j] = __uint_as_float(w);
+                        }
+                        o[g] = cvt2_f32_div2x<FMT, true>(f[2], f[3], sc, cvt2_f32_div2x<FMT, false>(f[0], f[1], sc, 0u)) & zm;
+                    }
+                    const int c = slot * VEC + k;
+                    *(uint4 *)(colbuf + colbuf_offset(c, chunk)) = make_uint4(o[0], o[1], o[2], o[3]);
+                    if (half == 0) scol[c * 4 + wave] = (uint8_t)byte;
+                }
+            }
+        }
+    }
+
+    // ---- the tile's staged outputs, written by the whole workgroup ---------------------------
+    if constexpr (COL) {
+        __syncthreads();
+        // q_colT: column c of the tile -> q_colT[ct0 + c][tr0 .. tr0 + trows), 16 bytes per lane
+        const __amdgpu_buffer_rsrc_t qc = make_rsrc(q_colT + (size_t)ct0 * rows + tr0, (uint32_t)ncv * rows - tr0);
+#pragma unroll
+        for (int e = threadIdx.x; e < TILE_C * (kTileRows / 16); e += kThreads) {
+            const int c = e >> 3, k = e & 7;
+            const uint4 v = *(const uint4 *)(colbuf + colbuf_offset(c, k));
+            const uint32_t vo = (c < ncv && 16 * k < trows) ? (uint32_t)c * rows + 16 * k : kOutOfRange;
+            buf_store16<kNonTemporal>(qc, vo, 0u, v);
+        }
+        // s_colT: the tile's trows/32 bytes of column c, contiguous in s_colT[ct0 + c]
+        const uint32_t srb = (uint32_t)rows / 32;
+        const int nb = trows / 32;
+        const __amdgpu_buffer_rsrc_t scr = make_rsrc(s_colT + (size_t)ct0 * srb + tr0 / 32, (uint32_t)ncv * srb - tr0 / 32);
+        const bool whole_c = nb == 4 && (srb & 3u) == 0 && (((uintptr_t)s_colT) & 3u) == 0;
+        for (int c = threadIdx.x; c < TILE_C; c += kThreads) {
+            const uint32_t w = *(const uint32_t *)(scol + c * 4);
+            if (whole_c) {
+                buf_store4(scr, c < ncv ? (uint32_t)c * srb : kOutOfRange, 0u, w);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    buf_store1(scr, (c < ncv && j < nb) ? (uint32_t)c * srb + j : kOutOfRange, 0u, w >> (8 * j));
+            }
+        }
+        // s_row: row r of the tile -> its NBLK bytes s_row[tr0 + r][ct0/32 ...]
+        if constexpr (ROW) {
+            const uint32_t ssb = (uint32_t)cols / 32;
+            const int nbl = ncv / 32;
+            const __amdgpu_buffer_rsrc_t srr = make_rsrc(s_row + (size_t)tr0 * ssb + ct0 / 32,
+                                                         (uint32_t)trows * ssb - ct0 / 32);
+            const bool whole_r = nbl == NBLK && (ssb % NBLK) == 0 && (((uintptr_t)s_row) % NBLK) == 0;
+            for (int r = threadIdx.x; r < kTileRows; r += kThreads) {
+                const bool rv = r < trows;
+                if constexpr (NBLK == 8) {
+                    const uint2 w = *(const uint2 *)(srow + r * 8);
+                    if (whole_r) {
+                        buf_store8(srr, rv ? (uint32_t)r * ssb : kOutOfRange, 0u, w.x, w.y);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            buf_store1(srr, (rv && j < nbl) ? (uint32_t)r * ssb + j : kOutOfRange, 0u,
+                                       (j < 4 ? w.x : w.y) >> (8 * (j & 3)));
+                    }
+                } else {
+                    const uint32_t w = *(const uint32_t *)(srow + r * 4);
+                    if (whole_r) {
+                        buf_store4(srr, rv ? (uint32_t)r * ssb : kOutOfRange, 0u, w);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            buf_store1(srr, (rv && j < nbl) ? (uint32_t)r * ssb + j : kOutOfRange, 0u, w >> (8 * j));
+                    }
                 }
             }
         }
@@ -205,11 +309,11 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const uint4 *__restrict__ 
 }
 
 template <bool BF16, int FMT, int RND>
-void launch_dirs(const uint4 *x, int rows, int cols, uint8_t *q_row, uint8_t *s_row, uint8_t *q_colT,
+void launch_dirs(const void *x, int rows, int cols, uint8_t *q_row, uint8_t *s_row, uint8_t *q_colT,
                  uint8_t *s_colT, int32_t *nonfinite, hipStream_t s) {
     constexpr int VEC = BF16 ? 8 : 4;
     const int tiles_r = (rows + kTileRows - 1) / kTileRows;
-    const int tiles_c = (cols + 64 * VEC - 1) / (64 * VEC);
+    const int tiles_c = (cols + 32 * VEC - 1) / (32 * VEC);
     const int tiles = tiles_r * tiles_c;
     const int per_xcd = (tiles + 7) / 8;
     const dim3 grid(8 * per_xcd), block(kThreads);
@@ -229,9 +333,8 @@ void launch_dirs(const uint4 *x, int rows, int cols, uint8_t *q_row, uint8_t *s_
 int launch_mx(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int rnd, uint8_t *q_row,
               uint8_t *s_row, uint8_t *q_colT, uint8_t *s_colT, int32_t *nonfinite, hipStream_t s) {
     if (rows == 0 || cols == 0) return QF8_OK;
-    const uint4 *xv = (const uint4 *)x;
     const int r = (int)rows, c = (int)cols;
-#define QF8_MX(BF, F, R) launch_dirs<BF, F, R>(xv, r, c, q_row, s_row, q_colT, s_colT, nonfinite, s)
+#define QF8_MX(BF, F, R) launch_dirs<BF, F, R>(x, r, c, q_row, s_row, q_colT, s_colT, nonfinite, s)
     if (dtype == QF8_IN_BF16) {
         if (fmt == QF8_E4M3) { if (rnd == QF8_MX_ROUND_DOWN) QF8_MX(true, kE4M3, kRoundDown); else QF8_MX(true, kE4M3, kRoundUp); }
         else { if (rnd == QF8_MX_ROUND_DOWN) QF8_MX(true, kE5M2, kRoundDown); else QF8_MX(true, kE5M2, kRoundUp); }
