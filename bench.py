@@ -120,7 +120,7 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this quantization path has no multi-GPU leg here "
-              "(see DESIGN.md on sharding); use --gpus 1", file=sys.stderr)
+              "; use --gpus 1", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -206,8 +206,123 @@ def main():
     print(json.dumps(line), flush=True)
 
     if args.suite:
-        from bench_suite import run_suite
+        del calls
+        torch.cuda.empty_cache()
         run_suite(args)
+
+
+# ---------------------------------------------------------------------------------------------
+# --suite: every other operation on its own workload (reported to gpurun_out/bench_suite.json)
+# ---------------------------------------------------------------------------------------------
+def _timed(torch, stream, fns, reps, warmup):
+    """Run fns round-robin (each on its own buffers); returns per-call kernel ms (HIP events)."""
+    for i in range(warmup):
+        fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record(stream)
+        fns[i % len(fns)]()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def _summ(name, nbytes, ms, extra=None):
+    import numpy as np
+    ms = np.array(ms)
+    med = float(np.median(ms))
+    d = {"op": name, "algorithmic_bytes": int(nbytes), "median_ms": round(med, 5), "min_ms": round(float(ms.min()), 5),
+         "p90_ms": round(float(np.percentile(ms, 90)), 5), "GBps_median": round(nbytes / med / 1e6, 1),
+         "pct_of_8TBps": round(100 * nbytes / med / 1e6 / PEAK_GBPS, 2)}
+    if extra:
+        d.update(extra)
+    print(json.dumps(d), file=sys.stderr, flush=True)
+    return d
+
+
+def run_suite(args):
+    import numpy as np
+    import torch
+
+    import mx_block_scaled_amax_amd as qf8
+    from synthetic import (block_weight, delayed_base, delayed_sigmas, per_tensor_activation, per_tensor_small,
+                           token_activation)
+    stream = torch.cuda.current_stream()
+    reps, warm = 40, 5
+    res = []
+
+    # plain copy: the achievable streaming ceiling (read 2N + write 2N of a 16384x4096 BF16 tensor)
+    src = [torch.empty(2 * ROWS * COLS, dtype=torch.uint8, device="cuda").fill_(1) for _ in range(4)]
+    dst = [torch.empty_like(t) for t in src]
+    fns = [lambda a=a, b=b: b.copy_(a) for a, b in zip(src, dst)]
+    res.append(_summ("copy 128 MiB -> 128 MiB (torch)", 4 * ROWS * COLS, _timed(torch, stream, fns, reps, warm)))
+    del src, dst
+
+    # per-tensor current scaling, 8192x8192 BF16, E4M3 and E5M2 (4 input copies in rotation)
+    xb = per_tensor_activation()
+    xs = [to_dev(xb) for _ in range(4)]
+    n = xb.size
+    q = torch.empty(xb.shape, dtype=torch.uint8, device="cuda")
+    am = torch.empty(1, dtype=torch.float32, device="cuda")
+    sc = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = torch.empty(qf8.qf8_workspace_bytes(*xb.shape), dtype=torch.uint8, device="cuda")
+    for fmt, name in ((qf8.E4M3, "e4m3"), (qf8.E5M2, "e5m2")):
+        fns = [lambda x=x: qf8.quantize_per_tensor(x, fmt, q=q, amax=am, scale=sc, ws=ws) for x in xs]
+        res.append(_summ(f"per_tensor 8192x8192 {name}", 3 * n + 8, _timed(torch, stream, fns, reps, warm),
+                         {"note": "2 kernels; reads x twice (5N traffic for 3N algorithmic bytes)"}))
+    del xs
+
+    # per-tensor and MX rowwise on the 256x512 tensor (latency-bound)
+    xsm = to_dev(per_tensor_small())
+    qs = torch.empty(xsm.shape, dtype=torch.uint8, device="cuda")
+    res.append(_summ("per_tensor 256x512 e4m3", 3 * xsm.numel() + 8,
+                     _timed(torch, stream, [lambda: qf8.quantize_per_tensor(xsm, qf8.E4M3, q=qs, amax=am, scale=sc, ws=ws)], reps, warm)))
+    res.append(_summ("mx rowwise 256x512 e4m3 round-up", 3 * xsm.numel() + xsm.numel() // 32,
+                     _timed(torch, stream, [lambda: qf8.quantize_mx_dual(xsm, qf8.E4M3, qf8.ROUND_UP, colwise=False)], reps, warm)))
+
+    # delayed scaling: 100 iterations of 4096x14336 (history 16, Interval 5, N 3, E4M3)
+    z = torch.from_numpy(delayed_base()).cuda()
+    sig = delayed_sigmas()
+    xsd = [(z * float(s)).to(torch.bfloat16) for s in sig]
+    del z
+    st = qf8.DelayedState(16, 5, 3, qf8.E4M3)
+    qd = torch.empty(xsd[0].shape, dtype=torch.uint8, device="cuda")
+    wsd = torch.empty(qf8.qf8_workspace_bytes(*xsd[0].shape), dtype=torch.uint8, device="cuda")
+    for _ in range(2):                              # warm the code path on a throwaway state
+        qf8.quantize_delayed(xsd[0], qf8.DelayedState(16, 5, 3, qf8.E4M3), q=qd, ws=wsd)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in xsd]
+    for t, x in enumerate(xsd):
+        ev[t][0].record(stream)
+        qf8.quantize_delayed(x, st, q=qd, ws=wsd)
+        ev[t][1].record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    nd = xsd[0].numel()
+    res.append(_summ("delayed 4096x14336 e4m3, steps 1..99", 3 * nd, ms[1:],
+                     {"step0_ms": round(ms[0], 5), "total_100_steps_ms": round(sum(ms), 4),
+                      "note": "step 0 is current scaling (2 passes); later steps one fused pass + 1-workgroup finalize"}))
+    del xsd
+
+    # fine-grained: 1x128 activations 8192x7168 and 128x128 weights 7168x18432 (E4M3)
+    xa = token_activation()
+    xas = [to_dev(xa) for _ in range(4)]
+    qa = torch.empty(xa.shape, dtype=torch.uint8, device="cuda")
+    sa = torch.empty((xa.shape[0], xa.shape[1] // 128), dtype=torch.float32, device="cuda")
+    res.append(_summ("block 1x128 8192x7168 e4m3", 3 * xa.size + 4 * sa.numel(),
+                     _timed(torch, stream, [lambda x=x: qf8.quantize_block(x, 1, 128, qf8.E4M3, q=qa, scales=sa, want_amax=False) for x in xas], reps, warm)))
+    del xas
+    xw = block_weight()
+    xws = [to_dev(xw) for _ in range(2)]
+    qw = torch.empty(xw.shape, dtype=torch.uint8, device="cuda")
+    sw = torch.empty((xw.shape[0] // 128, xw.shape[1] // 128), dtype=torch.float32, device="cuda")
+    res.append(_summ("block 128x128 7168x18432 e4m3", 3 * xw.size + 4 * sw.numel(),
+                     _timed(torch, stream, [lambda x=x: qf8.quantize_block(x, 128, 128, qf8.E4M3, q=qw, scales=sw, want_amax=False) for x in xws], reps, warm)))
+    del xws
+    os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
+    with open(os.path.join(ROOT, "gpurun_out", "bench_suite.json"), "w") as f:
+        json.dump(res, f, indent=1)
 
 
 if __name__ == "__main__":

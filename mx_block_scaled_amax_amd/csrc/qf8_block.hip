@@ -6,7 +6,7 @@
 //            every group computes its own amax), 8.1 (S = F8max/amax, saturating cast).
 //
 // Both kernels are one HBM pass: load the group into registers, reduce its |x| maximum, derive
-// S_g with one IEEE division, cast from the registers.
+// S_g with one IEEE division, cast from the registers. Loads and stores are non-temporal.
 //   1x128: a group of 128 BF16 is 16 lanes x 8 values, i.e. one DPP row, so the maximum is four
 //          DPP steps; a workgroup handles 16 groups per pass and 4 passes (all loads issued
 //          first). FP32 input uses 32 lanes per group.
@@ -36,8 +36,8 @@ __device__ __forceinline__ uint32_t vec_absmax_bits(uint4 v) {
 
 template <bool BF16, int FMT>
 __device__ __forceinline__ void store_cast(uint8_t *q, int64_t off, uint4 v, float s) {
-    if constexpr (BF16) *(uint2 *)(q + off) = cast8_bf16<FMT>(v, s);
-    else *(uint32_t *)(q + off) = cast4_f32<FMT>(v, s);
+    if constexpr (BF16) st_stream((uint2 *)(q + off), cast8_bf16<FMT>(v, s));
+    else st_stream((uint32_t *)(q + off), cast4_f32<FMT>(v, s));
 }
 
 template <bool BF16, int FMT>
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kThreads) void block_1x128_kernel(const uint16_t *_
         const int64_t col = j * 128 + sub * VEC;
         ok[it] = g[it] < ngroups && col < cols;
         off[it] = r * cols + col;
-        v[it] = ok[it] ? *(const uint4 *)(xb + off[it] * (BF16 ? 2 : 4)) : make_uint4(0, 0, 0, 0);
+        v[it] = ok[it] ? ld_stream((const uint4 *)(xb + off[it] * (BF16 ? 2 : 4))) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kThreads) void block_128x128_kernel(const uint16_t 
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
         const int64_t r = bi * 128 + p * RPP + rr;
-        v[p] = (cok && r < rows) ? *(const uint4 *)(xb + (r * cols + col) * (BF16 ? 2 : 4)) : make_uint4(0, 0, 0, 0);
+        v[p] = (cok && r < rows) ? ld_stream((const uint4 *)(xb + (r * cols + col) * (BF16 ? 2 : 4))) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) m = umax(m, vec_absmax_bits<BF16>(v[p]));

@@ -226,4 +226,19 @@ __device__ __forceinline__ void buf_store1(__amdgpu_buffer_rsrc_t r, uint32_t vo
     __builtin_amdgcn_raw_buffer_store_b8((unsigned char)v, r, (int)voff, (int)soff, CP);
 }
 
+// Non-temporal (streaming) global loads and stores for data touched exactly once.
+__device__ __forceinline__ uint4 ld_stream(const uint4 *p) {
+    const v4u32 v = __builtin_nontemporal_load((const v4u32 *)p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream(uint4 *p, uint4 v) {
+    const v4u32 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, (v4u32 *)p);
+}
+__device__ __forceinline__ void st_stream(uint2 *p, uint2 v) {
+    const v2u32 w = {v.x, v.y};
+    __builtin_nontemporal_store(w, (v2u32 *)p);
+}
+__device__ __forceinline__ void st_stream(uint32_t *p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+
 }  // namespace qf8

@@ -10,7 +10,8 @@ namespace qf8 {
 
 // Per-tensor / delayed geometry: number of workgroups of the streaming kernels for n elements.
 int stream_grid(int64_t n, int dtype);
-constexpr int kMaxStreamGrid = 2048;
+constexpr int kMaxStreamGrid = 2048;   // capacity of the partials workspace
+constexpr int kStreamGridCap = 1024;   // workgroups the streaming kernels use at most
 constexpr size_t kWorkspaceBytes = kMaxStreamGrid * sizeof(uint32_t);
 
 int launch_amax_partials(const void *x, int dtype, int64_t n, uint32_t *partials, int grid, hipStream_t s);

@@ -10,9 +10,8 @@
 // Kernels (all HBM-bandwidth bound; 256 threads, 16-byte vector loads):
 //   amax_partials  -- each workgroup reduces a contiguous chunk of |x| bit patterns to one u32.
 //   cast_current   -- each workgroup first folds all partials into amax and S (so no separate
-//                     single-wave finalize launch is needed), then casts its chunk. Chunks are
-//                     visited in the reverse of the amax pass's order, so the first workgroups
-//                     re-read the data that pass touched last (still in the last-level cache).
+//                     single-wave finalize launch is needed), then casts its chunk with
+//                     non-temporal 16-byte loads and 16-byte stores.
 //   cast_scaled    -- cast with a scale read from device memory; optionally also emits the
 //                     chunk's partial max (the fused amax of a delayed-scaling step).
 //   delayed_finalize -- one workgroup: amax of the step, FIFO push on update steps, next scale.
@@ -89,40 +88,67 @@ __global__ __launch_bounds__(kThreads) void amax_partials_kernel(const void *__r
     if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
 
-// Casts vectors [beg, end) of the chunk plus, for the last chunk, the scalar tail.
-// Returns the chunk's |x| maximum (fp32 bits) when FUSE.
+// One output unit = 16 codes = 16 bytes, from UV 16-byte input vectors (2 BF16, 4 FP32).
+template <bool BF16>
+constexpr int unit_vectors() { return BF16 ? 2 : 4; }
+template <bool BF16>
+constexpr int unit_elems() { return 16; }
+
+template <bool BF16, int FMT>
+__device__ __forceinline__ uint4 cast_unit(const uint4 *v, float s) {
+    if constexpr (BF16) {
+        const uint2 a = cast8_bf16<FMT>(v[0], s), b = cast8_bf16<FMT>(v[1], s);
+        return make_uint4(a.x, a.y, b.x, b.y);
+    } else {
+        return make_uint4(cast4_f32<FMT>(v[0], s), cast4_f32<FMT>(v[1], s), cast4_f32<FMT>(v[2], s),
+                          cast4_f32<FMT>(v[3], s));
+    }
+}
+
+// Casts units [beg, end) of the chunk plus, for the last chunk, the elements past the last whole
+// unit. Streaming loads and stores (read once, written once). Returns the |x| maximum (fp32
+// bits) of everything it read when FUSE.
 template <bool BF16, int FMT, bool FUSE>
-__device__ __forceinline__ uint32_t cast_chunk(const void *__restrict__ x, int64_t n, int64_t nvec, int64_t beg,
+__device__ __forceinline__ uint32_t cast_chunk(const void *__restrict__ x, int64_t n, int64_t nunits, int64_t beg,
                                                int64_t end, bool last, float s, uint8_t *__restrict__ q) {
-    constexpr int VEC = BF16 ? 8 : 4;
+    constexpr int UV = unit_vectors<BF16>();
     const uint4 *xv = (const uint4 *)x;
+    uint4 *qv = (uint4 *)q;
     uint32_t a0 = 0, a1 = 0;
     int64_t i = beg + threadIdx.x;
-    for (; i + 3 * kThreads < end; i += 4 * kThreads) {
-        uint4 v[4];
+    for (; i + kThreads < end; i += 2 * kThreads) {          // two units per thread in flight
+        uint4 v[2][UV];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = xv[i + u * kThreads];
+        for (int k = 0; k < 2; ++k)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < UV; ++u) v[k][u] = ld_stream(xv + (i + k * kThreads) * UV + u);
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
             if constexpr (FUSE) {
-                if (u & 1) a1 = vec_absmax<BF16>(a1, v[u]);
-                else a0 = vec_absmax<BF16>(a0, v[u]);
+#pragma unroll
+                for (int u = 0; u < UV; ++u) {
+                    if (u & 1) a1 = vec_absmax<BF16>(a1, v[k][u]);
+                    else a0 = vec_absmax<BF16>(a0, v[k][u]);
+                }
             }
-            if constexpr (BF16) ((uint2 *)q)[i + u * kThreads] = cast8_bf16<FMT>(v[u], s);
-            else ((uint32_t *)q)[i + u * kThreads] = cast4_f32<FMT>(v[u], s);
+            st_stream(qv + i + k * kThreads, cast_unit<BF16, FMT>(v[k], s));
         }
     }
     for (; i < end; i += kThreads) {
-        uint4 v = xv[i];
-        if constexpr (FUSE) a0 = vec_absmax<BF16>(a0, v);
-        if constexpr (BF16) ((uint2 *)q)[i] = cast8_bf16<FMT>(v, s);
-        else ((uint32_t *)q)[i] = cast4_f32<FMT>(v, s);
+        uint4 v[UV];
+#pragma unroll
+        for (int u = 0; u < UV; ++u) v[u] = ld_stream(xv + i * UV + u);
+        if constexpr (FUSE) {
+#pragma unroll
+            for (int u = 0; u < UV; ++u) a0 = vec_absmax<BF16>(a0, v[u]);
+        }
+        st_stream(qv + i, cast_unit<BF16, FMT>(v, s));
     }
     uint32_t m = 0;
     if constexpr (FUSE) m = umax(acc_to_f32bits<BF16>(a0), acc_to_f32bits<BF16>(a1));
     if (last) {
-        for (int64_t e = nvec * VEC + threadIdx.x; e < n; e += kThreads) {
-            uint32_t b = elem_bits<BF16>(x, e);
+        for (int64_t e = nunits * unit_elems<BF16>() + threadIdx.x; e < n; e += kThreads) {
+            const uint32_t b = elem_bits<BF16>(x, e);
             if constexpr (FUSE) m = umax(m, b & 0x7FFFFFFFu);
             q[e] = (uint8_t)cast1<FMT>(__uint_as_float(b), s);
         }
@@ -131,7 +157,7 @@ __device__ __forceinline__ uint32_t cast_chunk(const void *__restrict__ x, int64
 }
 
 template <bool BF16, int FMT>
-__global__ __launch_bounds__(kThreads) void cast_current_kernel(const void *__restrict__ x, int64_t n, int64_t nvec,
+__global__ __launch_bounds__(kThreads) void cast_current_kernel(const void *__restrict__ x, int64_t n, int64_t nunits,
                                                                 int64_t chunk, uint8_t *__restrict__ q,
                                                                 const uint32_t *__restrict__ partials, int nparts,
                                                                 float *amax_out, float *scale_out, int32_t *nonfinite) {
@@ -140,10 +166,9 @@ __global__ __launch_bounds__(kThreads) void cast_current_kernel(const void *__re
     for (int i = threadIdx.x; i < nparts; i += kThreads) m = umax(m, partials[i]);
     m = block_max_bcast(m, red);
     const float s = scale_from_amax_bits<FMT>(m);
-    const int c = gridDim.x - 1 - blockIdx.x;                       // reverse chunk order
-    const int64_t beg = (int64_t)c * chunk;
-    const int64_t end = beg + chunk < nvec ? beg + chunk : nvec;
-    cast_chunk<BF16, FMT, false>(x, n, nvec, beg, end, c == (int)gridDim.x - 1, s, q);
+    const int64_t beg = (int64_t)blockIdx.x * chunk;
+    const int64_t end = beg + chunk < nunits ? beg + chunk : nunits;
+    cast_chunk<BF16, FMT, false>(x, n, nunits, beg, end, blockIdx.x == gridDim.x - 1, s, q);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         if (amax_out) *amax_out = __uint_as_float(m);
         if (scale_out) *scale_out = s;
@@ -152,15 +177,15 @@ __global__ __launch_bounds__(kThreads) void cast_current_kernel(const void *__re
 }
 
 template <bool BF16, int FMT, bool FUSE>
-__global__ __launch_bounds__(kThreads) void cast_scaled_kernel(const void *__restrict__ x, int64_t n, int64_t nvec,
+__global__ __launch_bounds__(kThreads) void cast_scaled_kernel(const void *__restrict__ x, int64_t n, int64_t nunits,
                                                                int64_t chunk, const float *__restrict__ scale,
                                                                uint8_t *__restrict__ q, float *scale_used,
                                                                uint32_t *__restrict__ partials) {
     __shared__ uint32_t red[4];
     const float s = *scale;
     const int64_t beg = (int64_t)blockIdx.x * chunk;
-    const int64_t end = beg + chunk < nvec ? beg + chunk : nvec;
-    uint32_t m = cast_chunk<BF16, FMT, FUSE>(x, n, nvec, beg, end, blockIdx.x == gridDim.x - 1, s, q);
+    const int64_t end = beg + chunk < nunits ? beg + chunk : nunits;
+    uint32_t m = cast_chunk<BF16, FMT, FUSE>(x, n, nunits, beg, end, blockIdx.x == gridDim.x - 1, s, q);
     if constexpr (FUSE) {
         m = block_max_bcast(m, red);
         if (threadIdx.x == 0) partials[blockIdx.x] = m;
@@ -217,6 +242,7 @@ __global__ void fill_u32_kernel(uint32_t *p, int64_t n, uint32_t value) {
 }
 
 inline int64_t vec_count(int64_t n, int dtype) { return n / (dtype == QF8_IN_BF16 ? 8 : 4); }
+inline int64_t unit_count(int64_t n) { return n / 16; }
 inline int64_t chunk_of(int64_t nvec, int grid) { return (nvec + grid - 1) / grid; }
 inline int status_after_launch() { return hipGetLastError() == hipSuccess ? QF8_OK : QF8_ERR_HIP; }
 
@@ -224,9 +250,9 @@ inline int status_after_launch() { return hipGetLastError() == hipSuccess ? QF8_
 
 int stream_grid(int64_t n, int dtype) {
     int64_t nvec = vec_count(n, dtype);
-    int64_t g = (nvec + 1023) / 1024;
+    int64_t g = (nvec + 2047) / 2048;
     if (g < 1) g = 1;
-    if (g > kMaxStreamGrid) g = kMaxStreamGrid;
+    if (g > kStreamGridCap) g = kStreamGridCap;
     return (int)g;
 }
 
@@ -250,25 +276,25 @@ int launch_amax_partials(const void *x, int dtype, int64_t n, uint32_t *partials
 
 int launch_cast_current(const void *x, int dtype, int64_t n, int fmt, uint8_t *q, const uint32_t *partials,
                         int nparts, float *amax_out, float *scale_out, int32_t *nonfinite, int grid, hipStream_t s) {
-    const int64_t nvec = vec_count(n, dtype);
-    const int64_t chunk = chunk_of(nvec, grid);
+    const int64_t nunits = unit_count(n);
+    const int64_t chunk = chunk_of(nunits, grid);
     QF8_DISPATCH_DT_FMT(dtype, fmt,
-        hipLaunchKernelGGL((cast_current_kernel<BF16, FMT>), dim3(grid), dim3(kThreads), 0, s, x, n, nvec, chunk, q,
+        hipLaunchKernelGGL((cast_current_kernel<BF16, FMT>), dim3(grid), dim3(kThreads), 0, s, x, n, nunits, chunk, q,
                            partials, nparts, amax_out, scale_out, nonfinite));
     return status_after_launch();
 }
 
 int launch_cast_scaled(const void *x, int dtype, int64_t n, int fmt, const float *scale, uint8_t *q,
                        float *scale_used, uint32_t *partials_out, int grid, hipStream_t s) {
-    const int64_t nvec = vec_count(n, dtype);
-    const int64_t chunk = chunk_of(nvec, grid);
+    const int64_t nunits = unit_count(n);
+    const int64_t chunk = chunk_of(nunits, grid);
     if (partials_out)
         QF8_DISPATCH_DT_FMT(dtype, fmt,
-            hipLaunchKernelGGL((cast_scaled_kernel<BF16, FMT, true>), dim3(grid), dim3(kThreads), 0, s, x, n, nvec,
+            hipLaunchKernelGGL((cast_scaled_kernel<BF16, FMT, true>), dim3(grid), dim3(kThreads), 0, s, x, n, nunits,
                                chunk, scale, q, scale_used, partials_out));
     else
         QF8_DISPATCH_DT_FMT(dtype, fmt,
-            hipLaunchKernelGGL((cast_scaled_kernel<BF16, FMT, false>), dim3(grid), dim3(kThreads), 0, s, x, n, nvec,
+            hipLaunchKernelGGL((cast_scaled_kernel<BF16, FMT, false>), dim3(grid), dim3(kThreads), 0, s, x, n, nunits,
                                chunk, scale, q, scale_used, partials_out));
     return status_after_launch();
 }
