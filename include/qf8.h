@@ -115,7 +115,9 @@ int qf8_delayed_reset(qf8_delayed_state *st, void *stream);
 /* One iteration on x (rows*cols elements, 16-byte aligned) -> q (16-byte aligned).
  * scale_used (nullable): the scale this step cast with. amax_out (nullable): this step's true
  * amax (computed in the same pass as the cast; only update steps append it to the history).
- * ws: qf8_workspace_bytes(rows, cols, dtype) bytes. */
+ * ws: qf8_workspace_bytes(rows, cols, dtype) bytes of device scratch.
+ * Steps after the first are two kernel launches (fused cast, one-workgroup finalize); step 0
+ * is three (amax pass, cast, finalize). */
 int quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, qf8_delayed_state *st,
                      uint8_t *q, float *scale_used, float *amax_out, int32_t *nonfinite,
                      void *ws, size_t ws_bytes, void *stream);

@@ -65,8 +65,7 @@ int qf8_cast_scaled(const void *x, int dtype, int64_t n, int fmt, const float *s
     if (n == 0) return QF8_OK;
     if (!x || !scale || !q) return QF8_ERR_NULL;
     if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4)) return QF8_ERR_ALIGN;
-    return qf8::launch_cast_scaled(x, dtype, n, fmt, scale, q, nullptr, nullptr, qf8::stream_grid(n, dtype),
-                                   as_stream(stream));
+    return qf8::launch_cast_scaled(x, dtype, n, fmt, scale, q, qf8::stream_grid(n, dtype), as_stream(stream));
 }
 
 int quantize_per_tensor(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, uint8_t *q, float *amax,
@@ -81,10 +80,11 @@ int quantize_per_tensor(const void *x, int dtype, int64_t rows, int64_t cols, in
         return QF8_ERR_ALIGN;
     hipStream_t s = as_stream(stream);
     uint32_t *partials = (uint32_t *)ws;
-    const int grid = qf8::stream_grid(n, dtype);
-    int st = qf8::launch_amax_partials(x, dtype, n, partials, grid, s);
+    const int agrid = qf8::amax_grid(n, dtype);
+    int st = qf8::launch_amax_partials(x, dtype, n, partials, agrid, s);
     if (st != QF8_OK) return st;
-    return qf8::launch_cast_current(x, dtype, n, fmt, q, partials, grid, amax, scale, nonfinite, grid, s);
+    return qf8::launch_cast_current(x, dtype, n, fmt, q, partials, agrid, amax, scale, nonfinite,
+                                    qf8::stream_grid(n, dtype), s);
 }
 
 int qf8_delayed_init(qf8_delayed_state *st, float *history, int32_t *meta, float *scale, int hist_len, int interval,
@@ -136,21 +136,24 @@ int quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, qf8_d
     uint32_t *partials = (uint32_t *)ws;
     const int grid = qf8::stream_grid(n, dtype);
     int r;
-    int update;
     if (st->step == 0) {
         // no history yet: current scaling (Eq.(1)-(2), no margin), then append this amax
-        r = qf8::launch_amax_partials(x, dtype, n, partials, grid, s);
+        const int agrid = qf8::amax_grid(n, dtype);
+        r = qf8::launch_amax_partials(x, dtype, n, partials, agrid, s);
         if (r == QF8_OK)
-            r = qf8::launch_cast_current(x, dtype, n, st->fmt, q, partials, grid, nullptr, scale_used, nullptr, grid, s);
-        update = 1;
+            r = qf8::launch_cast_current(x, dtype, n, st->fmt, q, partials, agrid, nullptr, scale_used, nullptr, grid, s);
+        if (r == QF8_OK)
+            r = qf8::launch_delayed_finalize(partials, agrid, st->history, st->meta, st->scale, st->hist_len,
+                                             st->n_guard, st->fmt, 1, amax_out, nonfinite, s);
     } else {
-        // cast with the scale the history gave, fusing this step's partial amax into the pass
-        r = qf8::launch_cast_scaled(x, dtype, n, st->fmt, st->scale, q, scale_used, partials, grid, s);
-        update = (st->step % st->interval) == 0;
+        // cast with the scale the history gave, fusing this step's partial maxima into the pass;
+        // then append the amax on update steps and compute the next scale
+        const int update = (st->step % st->interval) == 0;
+        r = qf8::launch_cast_fused(x, dtype, n, st->fmt, st->scale, q, scale_used, partials, grid, s);
+        if (r == QF8_OK)
+            r = qf8::launch_delayed_finalize(partials, grid, st->history, st->meta, st->scale, st->hist_len,
+                                             st->n_guard, st->fmt, update, amax_out, nonfinite, s);
     }
-    if (r == QF8_OK)
-        r = qf8::launch_delayed_finalize(partials, grid, st->history, st->meta, st->scale, st->hist_len, st->n_guard,
-                                         st->fmt, update, amax_out, nonfinite, s);
     if (r == QF8_OK) st->step++;
     return r;
 }

@@ -10,15 +10,19 @@ namespace qf8 {
 
 // Per-tensor / delayed geometry: number of workgroups of the streaming kernels for n elements.
 int stream_grid(int64_t n, int dtype);
-constexpr int kMaxStreamGrid = 2048;   // capacity of the partials workspace
-constexpr int kStreamGridCap = 1024;   // workgroups the streaming kernels use at most
+// Workgroups (= partial maxima) of the per-tensor amax pass.
+int amax_grid(int64_t n, int dtype);
+constexpr int kAmaxGrid = 256;
+constexpr int kMaxStreamGrid = 16384;  // workgroups of the streaming kernels at most (= partials)
 constexpr size_t kWorkspaceBytes = kMaxStreamGrid * sizeof(uint32_t);
 
 int launch_amax_partials(const void *x, int dtype, int64_t n, uint32_t *partials, int grid, hipStream_t s);
 int launch_cast_current(const void *x, int dtype, int64_t n, int fmt, uint8_t *q, const uint32_t *partials,
                         int nparts, float *amax_out, float *scale_out, int32_t *nonfinite, int grid, hipStream_t s);
-int launch_cast_scaled(const void *x, int dtype, int64_t n, int fmt, const float *scale, uint8_t *q,
-                       float *scale_used, uint32_t *partials_out, int grid, hipStream_t s);
+int launch_cast_scaled(const void *x, int dtype, int64_t n, int fmt, const float *scale, uint8_t *q, int grid,
+                       hipStream_t s);
+int launch_cast_fused(const void *x, int dtype, int64_t n, int fmt, const float *scale, uint8_t *q,
+                      float *scale_used, uint32_t *partials, int grid, hipStream_t s);
 int launch_delayed_finalize(const uint32_t *partials, int nparts, float *history, int32_t *meta, float *scale,
                             int hist_len, int n_guard, int fmt, int update, float *amax_out,
                             int32_t *nonfinite, hipStream_t s);

@@ -7,14 +7,25 @@
 //   [MP-FP8]     "混合精度与 FP8 训练" (hs-black.github.io): section 8.1 (S = F8max/amax,
 //                saturation), 8.2 (delayed scaling fuses the amax into the producing pass).
 //
-// Kernels (all HBM-bandwidth bound; 256 threads, 16-byte vector loads):
-//   amax_partials  -- each workgroup reduces a contiguous chunk of |x| bit patterns to one u32.
-//   cast_current   -- each workgroup first folds all partials into amax and S (so no separate
-//                     single-wave finalize launch is needed), then casts its chunk with
-//                     non-temporal 16-byte loads and 16-byte stores.
-//   cast_scaled    -- cast with a scale read from device memory; optionally also emits the
-//                     chunk's partial max (the fused amax of a delayed-scaling step).
-//   delayed_finalize -- one workgroup: amax of the step, FIFO push on update steps, next scale.
+// All kernels are HBM-bandwidth bound. The tensor is cut into runs of 256 * kVecs 16-byte input
+// vectors (8 BF16 or 4 FP32 values each); a workgroup of 256 threads loads a run (kVecs vectors
+// per thread, consecutive threads on consecutive vectors) before converting it. Small runs and
+// many workgroups measured fastest on MI355X for this 2:1 read:write stream. Up to
+// kMaxStreamGrid runs there is one workgroup per run; larger tensors give each workgroup several
+// runs. The elements past the last whole vector (fewer than 8 or 4) are handled by workgroup 0.
+//   amax_partials   -- read-only pass, one u32 |amax| bit pattern per workgroup: at most
+//                      kAmaxGrid workgroups of 1024 threads, 8 loads per thread in flight (few
+//                      partials keep the fold every cast workgroup repeats small).
+//   cast_current    -- every workgroup folds all partials into amax and S itself (so there is
+//                      no separate single-wave finalize launch), then casts its run.
+//   cast_scaled     -- cast with a scale read from device memory.
+//   cast_fused      -- a delayed-scaling step's pass: cast with the scale in the device state and
+//                      write each workgroup's |amax| alongside (amax fused into the cast).
+//   delayed_finalize -- one 1024-thread workgroup: the step's amax from the partials (all loads
+//                      of a thread issued together), FIFO push on update
+//                      steps, next scale into the state. (A single-launch variant that let the
+//                      last workgroup finalize measured slower: device-scope atomics from every
+//                      workgroup to one address serialize at the memory side.)
 #include "qf8_device.h"
 #include "qf8_internal.h"
 #include "../../include/qf8.h"
@@ -23,19 +34,45 @@ namespace qf8 {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kVecs = 2;                        // 16-byte input vectors per thread and run
+constexpr int kAmaxThreads = 1024;              // read-only amax pass: one 16-wave workgroup per CU
+constexpr int kAmaxDepth = 8;                   //   16-byte loads per thread in flight
+constexpr int kFinalizeThreads = 1024;          // single-workgroup fold of the partial maxima
 constexpr uint32_t kAbs16x2 = 0x7FFF7FFFu;
 
+// Maximum over the workgroup of NT threads, broadcast to every thread. red: NT/64 words of LDS.
+template <int NT = kThreads>
 __device__ __forceinline__ uint32_t block_max_bcast(uint32_t v, uint32_t *red) {
+    constexpr int W = NT / 64;
     v = max_wave(v);
-    const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
-    uint32_t m = umax(umax(red[0], red[1]), umax(red[2], red[3]));
+    uint32_t m = red[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) m = umax(m, red[w]);
     __syncthreads();
     return m;
 }
 
-// |x| maximum of one 16-byte vector, accumulated as fp32 bit patterns (BF16 kept packed).
+// Maximum of n u32 values by a workgroup of NT threads (each thread's share; combine with
+// block_max_bcast). 16 independent loads per thread in flight per round.
+template <int NT = kThreads>
+__device__ __forceinline__ uint32_t fold_max(const uint32_t *__restrict__ p, int n) {
+    uint32_t m = 0;
+    for (int base = 0; base < n; base += 16 * NT) {
+        uint32_t v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int i = base + k * NT + (int)threadIdx.x;
+            v[k] = i < n ? p[i] : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) m = umax(m, v[k]);
+    }
+    return m;
+}
+
+// |x| maximum of one 16-byte vector, accumulated as bit patterns (BF16 kept packed).
 template <bool BF16>
 __device__ __forceinline__ uint32_t vec_absmax(uint32_t acc, uint4 v) {
     if constexpr (BF16) {
@@ -64,111 +101,121 @@ __device__ __forceinline__ uint32_t elem_bits(const void *x, int64_t i) {
 }
 
 template <bool BF16>
-__global__ __launch_bounds__(kThreads) void amax_partials_kernel(const void *__restrict__ x, int64_t n, int64_t nvec,
-                                                                 int64_t chunk, uint32_t *__restrict__ partials) {
-    constexpr int VEC = BF16 ? 8 : 4;
-    __shared__ uint32_t red[4];
-    const uint4 *xv = (const uint4 *)x;
-    const int64_t beg = (int64_t)blockIdx.x * chunk;
-    const int64_t end = beg + chunk < nvec ? beg + chunk : nvec;
-    uint32_t a0 = 0, a1 = 0;
-    int64_t i = beg + threadIdx.x;
-    for (; i + 3 * kThreads < end; i += 4 * kThreads) {
-        uint4 v0 = xv[i], v1 = xv[i + kThreads], v2 = xv[i + 2 * kThreads], v3 = xv[i + 3 * kThreads];
-        a0 = vec_absmax<BF16>(a0, v0);
-        a1 = vec_absmax<BF16>(a1, v1);
-        a0 = vec_absmax<BF16>(a0, v2);
-        a1 = vec_absmax<BF16>(a1, v3);
+constexpr int vec_elems() { return BF16 ? 8 : 4; }
+
+// One run of vectors, loaded in one go: vector j of thread t is run * 256 * kVecs + j * 256 + t.
+// Raw-buffer accesses on a per-run descriptor: lanes past the end of the tensor read zeros (which
+// never raise a maximum) and their stores are dropped, so there is no branch around any access.
+template <bool BF16>
+struct Run {
+    static constexpr uint32_t kOutBytes = BF16 ? 8 : 4;   // codes per 16-byte input vector
+    uint4 v[kVecs];
+    int64_t first;                                         // first vector of the run
+    uint32_t nv;                                           // vectors of the run inside the tensor
+
+    __device__ __forceinline__ void load(const void *x, int64_t nvec, int64_t run) {
+        first = run * kThreads * kVecs;
+        const int64_t rem = nvec - first;
+        nv = rem < kThreads * kVecs ? (uint32_t)rem : (uint32_t)(kThreads * kVecs);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc((const uint4 *)x + first, nv * 16u);
+#pragma unroll
+        for (int j = 0; j < kVecs; ++j)
+            v[j] = buf_load16<kNonTemporal>(r, (uint32_t)(j * kThreads + threadIdx.x) * 16u, 0u);
     }
-    for (; i < end; i += kThreads) a0 = vec_absmax<BF16>(a0, xv[i]);
+    __device__ __forceinline__ uint32_t absmax() const {
+        uint32_t a0 = 0, a1 = 0;
+#pragma unroll
+        for (int j = 0; j < kVecs; ++j) {
+            if (j & 1) a1 = vec_absmax<BF16>(a1, v[j]);
+            else a0 = vec_absmax<BF16>(a0, v[j]);
+        }
+        return umax(acc_to_f32bits<BF16>(a0), acc_to_f32bits<BF16>(a1));
+    }
+    template <int FMT>
+    __device__ __forceinline__ void cast_store(uint8_t *q, float s) const {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(q + first * kOutBytes, nv * kOutBytes);
+#pragma unroll
+        for (int j = 0; j < kVecs; ++j) {
+            const uint32_t off = (uint32_t)(j * kThreads + threadIdx.x) * kOutBytes;
+            if constexpr (BF16) {
+                const uint2 o = cast8_bf16<FMT>(v[j], s);
+                buf_store8<kNonTemporal>(r, off, 0u, o.x, o.y);
+            } else {
+                buf_store4<kNonTemporal>(r, off, 0u, cast4_f32<FMT>(v[j], s));
+            }
+        }
+    }
+};
+
+inline __device__ int64_t run_count(int64_t nvec) { return (nvec + kThreads * kVecs - 1) / (kThreads * kVecs); }
+
+// The elements after the last whole vector (workgroup 0 only).
+template <bool BF16>
+__device__ __forceinline__ uint32_t tail_absmax(const void *x, int64_t n, int64_t nvec) {
+    uint32_t m = 0;
+    if (blockIdx.x == 0)
+        for (int64_t e = nvec * vec_elems<BF16>() + threadIdx.x; e < n; e += kThreads)
+            m = umax(m, elem_bits<BF16>(x, e) & 0x7FFFFFFFu);
+    return m;
+}
+template <bool BF16, int FMT>
+__device__ __forceinline__ void tail_cast(const void *x, int64_t n, int64_t nvec, float s, uint8_t *q) {
+    if (blockIdx.x == 0)
+        for (int64_t e = nvec * vec_elems<BF16>() + threadIdx.x; e < n; e += kThreads)
+            q[e] = (uint8_t)cast1<FMT>(__uint_as_float(elem_bits<BF16>(x, e)), s);
+}
+
+// Read-only pass over batches of kAmaxThreads * kAmaxDepth vectors (all loads of a batch in flight
+// together; a read-only stream needs more bytes in flight per CU than the cast kernels, which also
+// have stores queued). Batches are dealt round-robin: at any moment the workgroups read
+// neighbouring batches. (Contiguous per-workgroup chunks measured 1.5x slower at power-of-two
+// chunk sizes, where every workgroup hits the same HBM channels at once.)
+template <bool BF16>
+__global__ __launch_bounds__(kAmaxThreads) void amax_partials_kernel(const void *__restrict__ x, int64_t n, int64_t nvec,
+                                                                     uint32_t *__restrict__ partials) {
+    constexpr int64_t kBatch = (int64_t)kAmaxThreads * kAmaxDepth;
+    __shared__ uint32_t red[kAmaxThreads / 64];
+    const uint4 *xv = (const uint4 *)x;
+    uint32_t a0 = 0, a1 = 0;
+    for (int64_t first = (int64_t)blockIdx.x * kBatch; first < nvec; first += (int64_t)gridDim.x * kBatch) {
+        const int64_t rem = nvec - first;
+        const uint32_t nb = (uint32_t)(rem < kBatch ? rem : kBatch) * 16u;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(xv + first, nb);
+        uint4 v[kAmaxDepth];
+#pragma unroll
+        for (int k = 0; k < kAmaxDepth; ++k)
+            v[k] = buf_load16<kNonTemporal>(r, (uint32_t)(k * kAmaxThreads + threadIdx.x) * 16u, 0u);
+#pragma unroll
+        for (int k = 0; k < kAmaxDepth; ++k) {
+            if (k & 1) a1 = vec_absmax<BF16>(a1, v[k]);
+            else a0 = vec_absmax<BF16>(a0, v[k]);
+        }
+    }
     uint32_t m = umax(acc_to_f32bits<BF16>(a0), acc_to_f32bits<BF16>(a1));
-    if (blockIdx.x == gridDim.x - 1)                               // ragged tail
-        for (int64_t e = nvec * VEC + threadIdx.x; e < n; e += kThreads) m = umax(m, elem_bits<BF16>(x, e) & 0x7FFFFFFFu);
-    m = block_max_bcast(m, red);
+    if (blockIdx.x == 0)                                        // elements after the last whole vector
+        for (int64_t e = nvec * vec_elems<BF16>() + threadIdx.x; e < n; e += kAmaxThreads)
+            m = umax(m, elem_bits<BF16>(x, e) & 0x7FFFFFFFu);
+    m = block_max_bcast<kAmaxThreads>(m, red);
     if (threadIdx.x == 0) partials[blockIdx.x] = m;
 }
 
-// One output unit = 16 codes = 16 bytes, from UV 16-byte input vectors (2 BF16, 4 FP32).
-template <bool BF16>
-constexpr int unit_vectors() { return BF16 ? 2 : 4; }
-template <bool BF16>
-constexpr int unit_elems() { return 16; }
-
 template <bool BF16, int FMT>
-__device__ __forceinline__ uint4 cast_unit(const uint4 *v, float s) {
-    if constexpr (BF16) {
-        const uint2 a = cast8_bf16<FMT>(v[0], s), b = cast8_bf16<FMT>(v[1], s);
-        return make_uint4(a.x, a.y, b.x, b.y);
-    } else {
-        return make_uint4(cast4_f32<FMT>(v[0], s), cast4_f32<FMT>(v[1], s), cast4_f32<FMT>(v[2], s),
-                          cast4_f32<FMT>(v[3], s));
-    }
-}
-
-// Casts units [beg, end) of the chunk plus, for the last chunk, the elements past the last whole
-// unit. Streaming loads and stores (read once, written once). Returns the |x| maximum (fp32
-// bits) of everything it read when FUSE.
-template <bool BF16, int FMT, bool FUSE>
-__device__ __forceinline__ uint32_t cast_chunk(const void *__restrict__ x, int64_t n, int64_t nunits, int64_t beg,
-                                               int64_t end, bool last, float s, uint8_t *__restrict__ q) {
-    constexpr int UV = unit_vectors<BF16>();
-    const uint4 *xv = (const uint4 *)x;
-    uint4 *qv = (uint4 *)q;
-    uint32_t a0 = 0, a1 = 0;
-    int64_t i = beg + threadIdx.x;
-    for (; i + kThreads < end; i += 2 * kThreads) {          // two units per thread in flight
-        uint4 v[2][UV];
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-#pragma unroll
-            for (int u = 0; u < UV; ++u) v[k][u] = ld_stream(xv + (i + k * kThreads) * UV + u);
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            if constexpr (FUSE) {
-#pragma unroll
-                for (int u = 0; u < UV; ++u) {
-                    if (u & 1) a1 = vec_absmax<BF16>(a1, v[k][u]);
-                    else a0 = vec_absmax<BF16>(a0, v[k][u]);
-                }
-            }
-            st_stream(qv + i + k * kThreads, cast_unit<BF16, FMT>(v[k], s));
-        }
-    }
-    for (; i < end; i += kThreads) {
-        uint4 v[UV];
-#pragma unroll
-        for (int u = 0; u < UV; ++u) v[u] = ld_stream(xv + i * UV + u);
-        if constexpr (FUSE) {
-#pragma unroll
-            for (int u = 0; u < UV; ++u) a0 = vec_absmax<BF16>(a0, v[u]);
-        }
-        st_stream(qv + i, cast_unit<BF16, FMT>(v, s));
-    }
-    uint32_t m = 0;
-    if constexpr (FUSE) m = umax(acc_to_f32bits<BF16>(a0), acc_to_f32bits<BF16>(a1));
-    if (last) {
-        for (int64_t e = nunits * unit_elems<BF16>() + threadIdx.x; e < n; e += kThreads) {
-            const uint32_t b = elem_bits<BF16>(x, e);
-            if constexpr (FUSE) m = umax(m, b & 0x7FFFFFFFu);
-            q[e] = (uint8_t)cast1<FMT>(__uint_as_float(b), s);
-        }
-    }
-    return m;
-}
-
-template <bool BF16, int FMT>
-__global__ __launch_bounds__(kThreads) void cast_current_kernel(const void *__restrict__ x, int64_t n, int64_t nunits,
-                                                                int64_t chunk, uint8_t *__restrict__ q,
+__global__ __launch_bounds__(kThreads) void cast_current_kernel(const void *__restrict__ x, int64_t n, int64_t nvec,
+                                                                uint8_t *__restrict__ q,
                                                                 const uint32_t *__restrict__ partials, int nparts,
                                                                 float *amax_out, float *scale_out, int32_t *nonfinite) {
     __shared__ uint32_t red[4];
-    uint32_t m = 0;
-    for (int i = threadIdx.x; i < nparts; i += kThreads) m = umax(m, partials[i]);
-    m = block_max_bcast(m, red);
+    const int64_t nruns = run_count(nvec);
+    Run<BF16> r;
+    r.load(x, nvec, blockIdx.x);               // the first run's loads overlap the partials fold
+    uint32_t m = block_max_bcast(fold_max(partials, nparts), red);
     const float s = scale_from_amax_bits<FMT>(m);
-    const int64_t beg = (int64_t)blockIdx.x * chunk;
-    const int64_t end = beg + chunk < nunits ? beg + chunk : nunits;
-    cast_chunk<BF16, FMT, false>(x, n, nunits, beg, end, blockIdx.x == gridDim.x - 1, s, q);
+    r.template cast_store<FMT>(q, s);
+    for (int64_t run = blockIdx.x + gridDim.x; run < nruns; run += gridDim.x) {
+        r.load(x, nvec, run);
+        r.template cast_store<FMT>(q, s);
+    }
+    tail_cast<BF16, FMT>(x, n, nvec, s, q);
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         if (amax_out) *amax_out = __uint_as_float(m);
         if (scale_out) *scale_out = s;
@@ -176,39 +223,29 @@ __global__ __launch_bounds__(kThreads) void cast_current_kernel(const void *__re
     }
 }
 
-template <bool BF16, int FMT, bool FUSE>
-__global__ __launch_bounds__(kThreads) void cast_scaled_kernel(const void *__restrict__ x, int64_t n, int64_t nunits,
-                                                               int64_t chunk, const float *__restrict__ scale,
-                                                               uint8_t *__restrict__ q, float *scale_used,
-                                                               uint32_t *__restrict__ partials) {
-    __shared__ uint32_t red[4];
+template <bool BF16, int FMT>
+__global__ __launch_bounds__(kThreads) void cast_scaled_kernel(const void *__restrict__ x, int64_t n, int64_t nvec,
+                                                               const float *__restrict__ scale, uint8_t *__restrict__ q) {
     const float s = *scale;
-    const int64_t beg = (int64_t)blockIdx.x * chunk;
-    const int64_t end = beg + chunk < nunits ? beg + chunk : nunits;
-    uint32_t m = cast_chunk<BF16, FMT, FUSE>(x, n, nunits, beg, end, blockIdx.x == gridDim.x - 1, s, q);
-    if constexpr (FUSE) {
-        m = block_max_bcast(m, red);
-        if (threadIdx.x == 0) partials[blockIdx.x] = m;
+    for (int64_t run = blockIdx.x; run < run_count(nvec); run += gridDim.x) {
+        Run<BF16> r;
+        r.load(x, nvec, run);
+        r.template cast_store<FMT>(q, s);
     }
-    if (scale_used && blockIdx.x == 0 && threadIdx.x == 0) *scale_used = s;
+    tail_cast<BF16, FMT>(x, n, nvec, s, q);
 }
 
+// Delayed-scaling state update, by one workgroup: report the step's amax, append it on update
+// steps (dropping the oldest when the FIFO is full), and derive the next scale from the history.
 template <int FMT>
-__global__ __launch_bounds__(kThreads) void delayed_finalize_kernel(const uint32_t *__restrict__ partials, int nparts,
-                                                                    float *history, int32_t *meta, float *scale,
-                                                                    int hist_len, int n_guard, int update,
-                                                                    float *amax_out, int32_t *nonfinite) {
-    __shared__ uint32_t red[4];
-    __shared__ int sh_count, sh_slot;
-    uint32_t m = 0;
-    for (int i = threadIdx.x; i < nparts; i += kThreads) m = umax(m, partials[i]);
-    m = block_max_bcast(m, red);
+__device__ void delayed_update(uint32_t m, float *history, int32_t *meta, float *scale, int hist_len, int n_guard,
+                               int update, float *amax_out, int32_t *nonfinite, uint32_t *red, int *sh) {
     const bool bad = m >= 0x7F800000u;
     if (threadIdx.x == 0) {
         if (amax_out) *amax_out = __uint_as_float(m);
         if (bad && nonfinite) *nonfinite = 1;
         int count = meta[0], head = meta[1], slot = -1;
-        if (update && !bad) {                                        // append; drop the oldest when full
+        if (update && !bad) {
             if (count < hist_len) {                                  // head stays 0 while filling
                 slot = count;
                 meta[0] = ++count;
@@ -218,22 +255,56 @@ __global__ __launch_bounds__(kThreads) void delayed_finalize_kernel(const uint32
             }
             history[slot] = __uint_as_float(m);
         }
-        sh_count = count;
-        sh_slot = slot;
+        sh[0] = count;
+        sh[1] = slot;
     }
     __syncthreads();
     // estimate = max of the history: slots [0, count) are the valid ones, in any order. The slot
     // written above is taken from the register of thread 0, not re-read from memory.
-    const int count = sh_count, slot = sh_slot;
+    const int count = sh[0], slot = sh[1];
     uint32_t e = 0;
-    for (int i = threadIdx.x; i < count; i += kThreads)
+    for (int i = threadIdx.x; i < count; i += kFinalizeThreads)
         if (i != slot) e = umax(e, __float_as_uint(history[i]));
     if (threadIdx.x == 0 && slot >= 0) e = umax(e, m);
-    e = block_max_bcast(e, red);
+    e = block_max_bcast<kFinalizeThreads>(e, red);
     if (threadIdx.x == 0) {
         const float margin = __uint_as_float((uint32_t)(127 - n_guard) << 23);   // 2^-N, exact
         *scale = scale_from_amax_bits<FMT>(e) * margin;
     }
+}
+
+// Cast with the state's scale and record each workgroup's |amax| for the finalize kernel.
+template <bool BF16, int FMT>
+__global__ __launch_bounds__(kThreads) void cast_fused_kernel(const void *__restrict__ x, int64_t n, int64_t nvec,
+                                                              const float *__restrict__ scale, uint8_t *__restrict__ q,
+                                                              float *scale_used, uint32_t *__restrict__ partials) {
+    __shared__ uint32_t red[4];
+    const float s = *scale;
+    uint32_t m = tail_absmax<BF16>(x, n, nvec);
+    for (int64_t run = blockIdx.x; run < run_count(nvec); run += gridDim.x) {
+        Run<BF16> r;
+        r.load(x, nvec, run);
+        r.template cast_store<FMT>(q, s);
+        m = umax(m, r.absmax());
+    }
+    tail_cast<BF16, FMT>(x, n, nvec, s, q);
+    m = block_max_bcast(m, red);
+    if (threadIdx.x == 0) {
+        partials[blockIdx.x] = m;
+        if (blockIdx.x == 0 && scale_used) *scale_used = s;
+    }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kFinalizeThreads) void delayed_finalize_kernel(const uint32_t *__restrict__ partials,
+                                                                            int nparts, float *history, int32_t *meta,
+                                                                            float *scale, int hist_len, int n_guard,
+                                                                            int update, float *amax_out,
+                                                                            int32_t *nonfinite) {
+    __shared__ uint32_t red[kFinalizeThreads / 64];
+    __shared__ int sh[2];
+    const uint32_t m = block_max_bcast<kFinalizeThreads>(fold_max<kFinalizeThreads>(partials, nparts), red);
+    delayed_update<FMT>(m, history, meta, scale, hist_len, n_guard, update, amax_out, nonfinite, red, sh);
 }
 
 __global__ void fill_u32_kernel(uint32_t *p, int64_t n, uint32_t value) {
@@ -242,18 +313,22 @@ __global__ void fill_u32_kernel(uint32_t *p, int64_t n, uint32_t value) {
 }
 
 inline int64_t vec_count(int64_t n, int dtype) { return n / (dtype == QF8_IN_BF16 ? 8 : 4); }
-inline int64_t unit_count(int64_t n) { return n / 16; }
-inline int64_t chunk_of(int64_t nvec, int grid) { return (nvec + grid - 1) / grid; }
 inline int status_after_launch() { return hipGetLastError() == hipSuccess ? QF8_OK : QF8_ERR_HIP; }
 
 }  // namespace
 
 int stream_grid(int64_t n, int dtype) {
-    int64_t nvec = vec_count(n, dtype);
-    int64_t g = (nvec + 2047) / 2048;
-    if (g < 1) g = 1;
-    if (g > kStreamGridCap) g = kStreamGridCap;
-    return (int)g;
+    const int64_t per_run = (int64_t)kThreads * kVecs;
+    int64_t g = (vec_count(n, dtype) + per_run - 1) / per_run;
+    if (g > kMaxStreamGrid) g = kMaxStreamGrid;
+    return (int)(g < 1 ? 1 : g);
+}
+
+int amax_grid(int64_t n, int dtype) {
+    const int64_t per_wg = (int64_t)kAmaxThreads * kAmaxDepth;      // vectors of one full batch
+    int64_t g = (vec_count(n, dtype) + per_wg - 1) / per_wg;
+    if (g > kAmaxGrid) g = kAmaxGrid;
+    return (int)(g < 1 ? 1 : g);
 }
 
 #define QF8_DISPATCH_DT_FMT(dtype, fmt, KERNEL_CALL)                                           \
@@ -266,36 +341,36 @@ int stream_grid(int64_t n, int dtype) {
 
 int launch_amax_partials(const void *x, int dtype, int64_t n, uint32_t *partials, int grid, hipStream_t s) {
     const int64_t nvec = vec_count(n, dtype);
-    const int64_t chunk = chunk_of(nvec, grid);
     if (dtype == QF8_IN_BF16)
-        hipLaunchKernelGGL(amax_partials_kernel<true>, dim3(grid), dim3(kThreads), 0, s, x, n, nvec, chunk, partials);
+        hipLaunchKernelGGL(amax_partials_kernel<true>, dim3(grid), dim3(kAmaxThreads), 0, s, x, n, nvec, partials);
     else
-        hipLaunchKernelGGL(amax_partials_kernel<false>, dim3(grid), dim3(kThreads), 0, s, x, n, nvec, chunk, partials);
+        hipLaunchKernelGGL(amax_partials_kernel<false>, dim3(grid), dim3(kAmaxThreads), 0, s, x, n, nvec, partials);
     return status_after_launch();
 }
 
 int launch_cast_current(const void *x, int dtype, int64_t n, int fmt, uint8_t *q, const uint32_t *partials,
                         int nparts, float *amax_out, float *scale_out, int32_t *nonfinite, int grid, hipStream_t s) {
-    const int64_t nunits = unit_count(n);
-    const int64_t chunk = chunk_of(nunits, grid);
+    const int64_t nvec = vec_count(n, dtype);
     QF8_DISPATCH_DT_FMT(dtype, fmt,
-        hipLaunchKernelGGL((cast_current_kernel<BF16, FMT>), dim3(grid), dim3(kThreads), 0, s, x, n, nunits, chunk, q,
+        hipLaunchKernelGGL((cast_current_kernel<BF16, FMT>), dim3(grid), dim3(kThreads), 0, s, x, n, nvec, q,
                            partials, nparts, amax_out, scale_out, nonfinite));
     return status_after_launch();
 }
 
-int launch_cast_scaled(const void *x, int dtype, int64_t n, int fmt, const float *scale, uint8_t *q,
-                       float *scale_used, uint32_t *partials_out, int grid, hipStream_t s) {
-    const int64_t nunits = unit_count(n);
-    const int64_t chunk = chunk_of(nunits, grid);
-    if (partials_out)
-        QF8_DISPATCH_DT_FMT(dtype, fmt,
-            hipLaunchKernelGGL((cast_scaled_kernel<BF16, FMT, true>), dim3(grid), dim3(kThreads), 0, s, x, n, nunits,
-                               chunk, scale, q, scale_used, partials_out));
-    else
-        QF8_DISPATCH_DT_FMT(dtype, fmt,
-            hipLaunchKernelGGL((cast_scaled_kernel<BF16, FMT, false>), dim3(grid), dim3(kThreads), 0, s, x, n, nunits,
-                               chunk, scale, q, scale_used, partials_out));
+int launch_cast_scaled(const void *x, int dtype, int64_t n, int fmt, const float *scale, uint8_t *q, int grid,
+                       hipStream_t s) {
+    const int64_t nvec = vec_count(n, dtype);
+    QF8_DISPATCH_DT_FMT(dtype, fmt,
+        hipLaunchKernelGGL((cast_scaled_kernel<BF16, FMT>), dim3(grid), dim3(kThreads), 0, s, x, n, nvec, scale, q));
+    return status_after_launch();
+}
+
+int launch_cast_fused(const void *x, int dtype, int64_t n, int fmt, const float *scale, uint8_t *q,
+                      float *scale_used, uint32_t *partials, int grid, hipStream_t s) {
+    const int64_t nvec = vec_count(n, dtype);
+    QF8_DISPATCH_DT_FMT(dtype, fmt,
+        hipLaunchKernelGGL((cast_fused_kernel<BF16, FMT>), dim3(grid), dim3(kThreads), 0, s, x, n, nvec, scale, q,
+                           scale_used, partials));
     return status_after_launch();
 }
 
@@ -303,10 +378,10 @@ int launch_delayed_finalize(const uint32_t *partials, int nparts, float *history
                             int hist_len, int n_guard, int fmt, int update, float *amax_out,
                             int32_t *nonfinite, hipStream_t s) {
     if (fmt == QF8_E4M3)
-        hipLaunchKernelGGL(delayed_finalize_kernel<kE4M3>, dim3(1), dim3(kThreads), 0, s, partials, nparts, history,
+        hipLaunchKernelGGL(delayed_finalize_kernel<kE4M3>, dim3(1), dim3(kFinalizeThreads), 0, s, partials, nparts, history,
                            meta, scale, hist_len, n_guard, update, amax_out, nonfinite);
     else
-        hipLaunchKernelGGL(delayed_finalize_kernel<kE5M2>, dim3(1), dim3(kThreads), 0, s, partials, nparts, history,
+        hipLaunchKernelGGL(delayed_finalize_kernel<kE5M2>, dim3(1), dim3(kFinalizeThreads), 0, s, partials, nparts, history,
                            meta, scale, hist_len, n_guard, update, amax_out, nonfinite);
     return status_after_launch();
 }
