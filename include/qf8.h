@@ -27,8 +27,9 @@
  *     are outside the bit-exact contract except where stated.
  *   - Return value: QF8_OK or a negative qf8_status. Argument errors are detected on the host
  *     before anything is enqueued; QF8_ERR_HIP reports a failed kernel launch.
- *   - Calls are thread-safe (no global mutable state). Calls on the same output buffers or the
- *     same delayed state must be ordered by the caller (same stream or events).
+ *   - Calls are thread-safe. The only global state is a per-device cache of the CU count and
+ *     kernel occupancy, filled on first use. Calls on the same output buffers, the same
+ *     workspace or the same delayed state must be ordered by the caller (same stream or events).
  */
 #ifndef QF8_H
 #define QF8_H
@@ -51,7 +52,7 @@ typedef enum qf8_status {
     QF8_ERR_NULL = -1,       /* a required pointer is NULL */
     QF8_ERR_ENUM = -2,       /* fmt, dtype or rounding mode out of range */
     QF8_ERR_SHAPE = -3,      /* negative size, or a size the operation's grouping cannot take */
-    QF8_ERR_ALIGN = -4,      /* a tensor pointer is not 16-byte aligned (scalars: 4-byte) */
+    QF8_ERR_ALIGN = -4,      /* a tensor or workspace pointer is not 16-byte aligned (scalars: 4-byte) */
     QF8_ERR_WORKSPACE = -5,  /* ws is NULL or smaller than qf8_workspace_bytes() */
     QF8_ERR_STATE = -6,      /* delayed-scaling state invalid or not initialised */
     QF8_ERR_HIP = -7         /* a HIP launch failed */
@@ -61,9 +62,19 @@ typedef enum qf8_status {
 const char *qf8_status_string(int status);
 
 /* Bytes of device workspace quantize_per_tensor and quantize_delayed need for a tensor of
- * rows x cols elements of dtype: per-workgroup partial maxima. The contents need no
- * initialisation and are scratch between calls. */
+ * rows x cols elements of dtype (currently a constant of about 128 KiB): a grid-barrier region
+ * (arrival counter, running maximum, one 128-byte release line per workgroup) and per-workgroup
+ * partial maxima. The workspace must be zero-filled once before its first use (for example
+ * with qf8_workspace_init); every call leaves the barrier region zero again, so the same
+ * workspace serves any number of later calls ordered on one stream. Two calls that may run at
+ * the same time need two workspaces. Word 2 (u32) of the workspace, if non-zero, replaces the
+ * default 1 ms after which a workgroup waiting at the grid barrier gives its slabs to the last
+ * workgroup, in 10 ns ticks (tests set it tiny to exercise that path). */
 size_t qf8_workspace_bytes(int64_t rows, int64_t cols, int dtype);
+
+/* Enqueues a zero fill of the qf8_workspace_bytes() bytes at ws (16-byte aligned, ws_bytes at
+ * least that size) on stream. */
+int qf8_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* Scaled saturating cast (Eq.(2) of [HiF8-train 1.2], [MP-FP8 8.1]):
  *   q[i] = sat_rne8(fl32(x[i] * scale[0])),  i in [0, n).
@@ -76,9 +87,12 @@ int qf8_cast_scaled(const void *x, int dtype, int64_t n, int fmt, const float *s
  *   amax = max |x|;  S = fl32(F8max / amax);  q = sat_rne8(fl32(x * S)).
  * x: rows*cols elements (any rows, cols >= 0), 16-byte aligned. q: rows*cols bytes, 16-byte
  * aligned. amax, scale: one device fp32 each (amax of an empty tensor is 0, its scale 1).
- * ws: qf8_workspace_bytes(rows, cols, dtype) bytes of device scratch.
- * Two kernels: a grid-wide partial max, then the cast (each workgroup finishes the
- * reduction of the partials itself). */
+ * ws: qf8_workspace_bytes(rows, cols, dtype) bytes, 16-byte aligned, initialised as described
+ * at qf8_workspace_bytes.
+ * From 2^22 elements on: one kernel that reads x from HBM once. One workgroup per CU keeps up
+ * to 128 MiB of the tensor in registers and LDS (on 256 CUs) across a grid barrier on the amax
+ * and casts from there; the rest of a larger tensor is re-read. Below 2^22 elements: two
+ * kernels (grid-wide partial maxima, then the cast; each cast workgroup folds the partials). */
 int quantize_per_tensor(const void *x, int dtype, int64_t rows, int64_t cols, int fmt,
                         uint8_t *q, float *amax, float *scale, int32_t *nonfinite,
                         void *ws, size_t ws_bytes, void *stream);
@@ -115,9 +129,10 @@ int qf8_delayed_reset(qf8_delayed_state *st, void *stream);
 /* One iteration on x (rows*cols elements, 16-byte aligned) -> q (16-byte aligned).
  * scale_used (nullable): the scale this step cast with. amax_out (nullable): this step's true
  * amax (computed in the same pass as the cast; only update steps append it to the history).
- * ws: qf8_workspace_bytes(rows, cols, dtype) bytes of device scratch.
+ * ws: qf8_workspace_bytes(rows, cols, dtype) bytes, 16-byte aligned, initialised as described
+ * at qf8_workspace_bytes.
  * Steps after the first are two kernel launches (fused cast, one-workgroup finalize); step 0
- * is three (amax pass, cast, finalize). */
+ * is the current-scaling path of quantize_per_tensor followed by the finalize. */
 int quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, qf8_delayed_state *st,
                      uint8_t *q, float *scale_used, float *amax_out, int32_t *nonfinite,
                      void *ws, size_t ws_bytes, void *stream);

@@ -60,6 +60,7 @@ def _load():
     sigs = {
         "qf8_status_string": (ctypes.c_char_p, [i32]),
         "qf8_workspace_bytes": (sz, [i64, i64, i32]),
+        "qf8_workspace_init": (i32, [vp, sz, vp]),
         "qf8_cast_scaled": (i32, [vp, i32, i64, i32, vp, vp, vp]),
         "quantize_per_tensor": (i32, [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, sz, vp]),
         "qf8_delayed_init": (i32, [ctypes.POINTER(_DelayedStruct), vp, vp, vp, i32, i32, i32, i32, vp]),
@@ -132,10 +133,27 @@ def qf8_workspace_bytes(rows, cols, dtype=torch.bfloat16):
     return _load().qf8_workspace_bytes(rows, cols, _BF16 if dtype == torch.bfloat16 else _FP32)
 
 
-def workspace(x):
-    """A device workspace tensor large enough for quantize_per_tensor / quantize_delayed on x."""
+# Mirrors of two library constants, for tests: the number of leading u32 words of a workspace
+# that form the grid-barrier region (header line + 512 release lines of 32 words), and the
+# element count from which quantize_per_tensor uses the single-pass kernel.
+BARRIER_WORDS = 32 + 512 * 32
+ONEPASS_MIN_ELEMS = 1 << 22
+
+
+def qf8_workspace_init(ws, stream=None):
+    """Zero-fill a workspace (uint8 device tensor) on the stream, as it must be before first use."""
+    _dev_tensor(ws, "ws")
+    _check(_load().qf8_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream, ws.device)),
+           "qf8_workspace_init")
+    return ws
+
+
+def workspace(x, stream=None):
+    """A zero-initialised device workspace for quantize_per_tensor / quantize_delayed on x. It
+    may be reused by any number of later calls ordered on one stream."""
     rows, cols = _rows_cols(x)
-    return torch.empty(qf8_workspace_bytes(rows, cols, x.dtype), dtype=torch.uint8, device=x.device)
+    ws = torch.empty(qf8_workspace_bytes(rows, cols, x.dtype), dtype=torch.uint8, device=x.device)
+    return qf8_workspace_init(ws, stream)
 
 
 def qf8_cast_scaled(x, fmt, scale, q=None, stream=None):

@@ -59,6 +59,13 @@ size_t qf8_workspace_bytes(int64_t rows, int64_t cols, int dtype) {
     return qf8::kWorkspaceBytes;
 }
 
+int qf8_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+    if (!ws) return QF8_ERR_NULL;
+    if (ws_bytes < qf8::kWorkspaceBytes) return QF8_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return QF8_ERR_ALIGN;
+    return qf8::launch_fill_u32((uint32_t *)ws, (int64_t)(qf8::kWorkspaceBytes / 4), 0u, as_stream(stream));
+}
+
 int qf8_cast_scaled(const void *x, int dtype, int64_t n, int fmt, const float *scale, uint8_t *q, void *stream) {
     if (!dtype_ok(dtype) || !fmt_ok(fmt)) return QF8_ERR_ENUM;
     if (n < 0) return QF8_ERR_SHAPE;
@@ -75,11 +82,14 @@ int quantize_per_tensor(const void *x, int dtype, int64_t rows, int64_t cols, in
     const int64_t n = rows * cols;
     if ((n > 0 && (!x || !q)) || !amax || !scale) return QF8_ERR_NULL;
     if (!ws || ws_bytes < qf8::kWorkspaceBytes) return QF8_ERR_WORKSPACE;
-    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(amax, 4) || !aligned(scale, 4) || !aligned(ws, 4) ||
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(amax, 4) || !aligned(scale, 4) || !aligned(ws, 16) ||
         (nonfinite && !aligned(nonfinite, 4)))
         return QF8_ERR_ALIGN;
     hipStream_t s = as_stream(stream);
-    uint32_t *partials = (uint32_t *)ws;
+    const int g1 = qf8::onepass_grid(n, dtype);
+    if (g1 > 0)
+        return qf8::launch_per_tensor_onepass(x, dtype, n, fmt, q, (uint32_t *)ws, amax, scale, nonfinite, nullptr, g1, s);
+    uint32_t *partials = (uint32_t *)ws + qf8::kPartialsOffsetWords;
     const int agrid = qf8::amax_grid(n, dtype);
     int st = qf8::launch_amax_partials(x, dtype, n, partials, agrid, s);
     if (st != QF8_OK) return st;
@@ -129,21 +139,29 @@ int quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, qf8_d
     const int64_t n = rows * cols;
     if (n > 0 && (!x || !q)) return QF8_ERR_NULL;
     if (!ws || ws_bytes < qf8::kWorkspaceBytes) return QF8_ERR_WORKSPACE;
-    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(ws, 4) || (scale_used && !aligned(scale_used, 4)) ||
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(ws, 16) || (scale_used && !aligned(scale_used, 4)) ||
         (amax_out && !aligned(amax_out, 4)) || (nonfinite && !aligned(nonfinite, 4)))
         return QF8_ERR_ALIGN;
     hipStream_t s = as_stream(stream);
-    uint32_t *partials = (uint32_t *)ws;
+    uint32_t *partials = (uint32_t *)ws + qf8::kPartialsOffsetWords;
     const int grid = qf8::stream_grid(n, dtype);
     int r;
     if (st->step == 0) {
         // no history yet: current scaling (Eq.(1)-(2), no margin), then append this amax
-        const int agrid = qf8::amax_grid(n, dtype);
-        r = qf8::launch_amax_partials(x, dtype, n, partials, agrid, s);
+        const int g1 = qf8::onepass_grid(n, dtype);
+        int nparts = 1;
+        if (g1 > 0) {
+            r = qf8::launch_per_tensor_onepass(x, dtype, n, st->fmt, q, (uint32_t *)ws, nullptr, scale_used, nullptr,
+                                               partials, g1, s);
+        } else {
+            nparts = qf8::amax_grid(n, dtype);
+            r = qf8::launch_amax_partials(x, dtype, n, partials, nparts, s);
+            if (r == QF8_OK)
+                r = qf8::launch_cast_current(x, dtype, n, st->fmt, q, partials, nparts, nullptr, scale_used, nullptr,
+                                             grid, s);
+        }
         if (r == QF8_OK)
-            r = qf8::launch_cast_current(x, dtype, n, st->fmt, q, partials, agrid, nullptr, scale_used, nullptr, grid, s);
-        if (r == QF8_OK)
-            r = qf8::launch_delayed_finalize(partials, agrid, st->history, st->meta, st->scale, st->hist_len,
+            r = qf8::launch_delayed_finalize(partials, nparts, st->history, st->meta, st->scale, st->hist_len,
                                              st->n_guard, st->fmt, 1, amax_out, nonfinite, s);
     } else {
         // cast with the scale the history gave, fusing this step's partial maxima into the pass;

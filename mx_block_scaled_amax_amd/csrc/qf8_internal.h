@@ -14,7 +14,26 @@ int stream_grid(int64_t n, int dtype);
 int amax_grid(int64_t n, int dtype);
 constexpr int kAmaxGrid = 256;
 constexpr int kMaxStreamGrid = 16384;  // workgroups of the streaming kernels at most (= partials)
-constexpr size_t kWorkspaceBytes = kMaxStreamGrid * sizeof(uint32_t);
+
+// Workspace layout, in u32 words:
+//   [0, kBarHeaderWords)      grid-barrier header: [0] arrival count, [1] amax bits, [2] give-up
+//                             timeout of a waiting workgroup in 10 ns ticks (0 = default 1 ms)
+//   kBarMaxGroups lines of kBarLineWords words (128 B each): the release line of each workgroup
+//   kMaxStreamGrid words      per-workgroup partial maxima of the multi-kernel paths
+// The barrier region must be zero before the first call; the single-pass kernel leaves it zero.
+constexpr int kBarHeaderWords = 32;
+constexpr int kBarLineWords = 32;
+constexpr int kBarMaxGroups = 512;
+constexpr size_t kPartialsOffsetWords = kBarHeaderWords + (size_t)kBarMaxGroups * kBarLineWords;
+constexpr size_t kWorkspaceBytes = (kPartialsOffsetWords + kMaxStreamGrid) * sizeof(uint32_t);
+
+// Single-pass per-tensor kernel: its grid for n elements of dtype on the current device (one
+// workgroup per CU), or 0 when the two-kernel path is used instead (small tensors, or a device
+// where one workgroup per CU does not fit).
+int onepass_grid(int64_t n, int dtype);
+int launch_per_tensor_onepass(const void *x, int dtype, int64_t n, int fmt, uint8_t *q, uint32_t *ws,
+                              float *amax_out, float *scale_out, int32_t *nonfinite, uint32_t *amax_bits_out,
+                              int grid, hipStream_t s);
 
 int launch_amax_partials(const void *x, int dtype, int64_t n, uint32_t *partials, int grid, hipStream_t s);
 int launch_cast_current(const void *x, int dtype, int64_t n, int fmt, uint8_t *q, const uint32_t *partials,

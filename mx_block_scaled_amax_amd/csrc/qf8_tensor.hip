@@ -26,6 +26,8 @@
 //                      steps, next scale into the state. (A single-launch variant that let the
 //                      last workgroup finalize measured slower: device-scope atomics from every
 //                      workgroup to one address serialize at the memory side.)
+#include <atomic>
+
 #include "qf8_device.h"
 #include "qf8_internal.h"
 #include "../../include/qf8.h"
@@ -38,6 +40,9 @@ constexpr int kVecs = 2;                        // 16-byte input vectors per thr
 constexpr int kAmaxThreads = 1024;              // read-only amax pass: one 16-wave workgroup per CU
 constexpr int kAmaxDepth = 8;                   //   16-byte loads per thread in flight
 constexpr int kFinalizeThreads = 1024;          // single-workgroup fold of the partial maxima
+constexpr int kOpThreads = 512;                 // single-pass kernel: 8 waves, 2 per SIMD
+constexpr int kOpRegSlabs = 48;                 //   slabs held in VGPRs (4 VGPRs each)
+constexpr int kOpLdsSlabs = 16;                 //   slabs held in LDS (8 KiB each)
 constexpr uint32_t kAbs16x2 = 0x7FFF7FFFu;
 
 // Maximum over the workgroup of NT threads, broadcast to every thread. red: NT/64 words of LDS.
@@ -87,6 +92,12 @@ __device__ __forceinline__ uint32_t vec_absmax(uint32_t acc, uint4 v) {
         acc = umax(acc, v.w & 0x7FFFFFFFu);
     }
     return acc;
+}
+// maximum of two accumulators (BF16: per 16-bit half)
+template <bool BF16>
+__device__ __forceinline__ uint32_t acc_max(uint32_t a, uint32_t b) {
+    if constexpr (BF16) return pk_max_u16(a, b);
+    else return umax(a, b);
 }
 // accumulator -> fp32 bit pattern of |amax|
 template <bool BF16>
@@ -295,6 +306,199 @@ __global__ __launch_bounds__(kThreads) void cast_fused_kernel(const void *__rest
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Single-HBM-pass current scaling. One workgroup of kOpThreads per CU (grid = CU count, at most
+// kBarMaxGroups). The tensor is cut into slabs of kOpThreads 16-byte vectors; workgroup b owns
+// slabs b, b + G, b + 2G, ... (neighbouring workgroups read neighbouring slabs, so every HBM
+// channel is busy at once). Its first kOpRegSlabs slabs stay in VGPRs and the next kOpLdsSlabs
+// in LDS (loaded by direct-to-LDS DMA, no VGPR staging), so that a tensor up to
+//   G * kOpThreads * (kOpRegSlabs + kOpLdsSlabs) * 16 bytes   (128 MiB on 256 CUs)
+// is read from HBM exactly once; slabs beyond that are reduced in the first pass and re-read
+// for the cast.
+//
+// Grid barrier (workspace words, all device-scope atomics):
+//   every workgroup: fetch_max(amax word, its |amax|), waiting for the returned value so the
+//     maximum is performed before the arrival; then fetch_add(count, 1).
+//   the workgroup that sees count == G - 1 arrived last: it reads the final maximum, returns
+//     both words to 0, and releases each other workgroup by exchanging RELEASED | amax into that
+//     workgroup's own 128-byte line (one line per poller: no same-address polling).
+//   every other workgroup polls its own line. If it is not released within the timeout it
+//     tries to mark the line GAVE_UP (compare-exchange from 0) and exits without casting; the
+//     last workgroup then finds GAVE_UP in the exchange result and casts all of that
+//     workgroup's slabs from HBM. So the kernel never depends on all workgroups being resident
+//     at once (another kernel may occupy CUs): it only gets slower. Each waiter clears its own
+//     line after reading it, so the workspace is back to all-zero when the kernel ends.
+
+constexpr uint64_t kLineReleased = 1ull << 32;
+constexpr uint64_t kLineGaveUp = 2ull << 32;
+constexpr uint32_t kDefaultGiveUpTicks = 100000;   // 1 ms of the 100 MHz real-time counter
+
+template <bool BF16, int FMT>
+__device__ __forceinline__ void cast_vec_store(__amdgpu_buffer_rsrc_t w, uint32_t off, uint4 v, float s) {
+    if constexpr (BF16) {
+        const uint2 o = cast8_bf16<FMT>(v, s);
+        buf_store8<kNonTemporal>(w, off, 0u, o.x, o.y);
+    } else {
+        buf_store4<kNonTemporal>(w, off, 0u, cast4_f32<FMT>(v, s));
+    }
+}
+
+// Byte count of the vectors [first, nvec) clamped to one buffer descriptor's range.
+__device__ __forceinline__ uint32_t span_bytes(int64_t first, int64_t nvec, uint32_t bytes_per_vec) {
+    const int64_t rem = nvec - first;
+    if (rem <= 0) return 0u;
+    const int64_t b = rem * bytes_per_vec;
+    return b < 0xFFFFFFFFll ? (uint32_t)b : 0xFFFFFFFFu;
+}
+
+// The eight slabs k, k + 1, ..., k + 7 of workgroup j (slab k of workgroup j is k * G + j):
+// load, and cast + store when CAST, return the |x| maximum (accumulator form).
+template <bool BF16, int FMT, bool CAST>
+__device__ __forceinline__ uint32_t stream_slabs8(const uint4 *x, int64_t nvec, uint8_t *q, int64_t k, int j, int G,
+                                                  float s) {
+    constexpr uint32_t kOut = BF16 ? 8u : 4u;
+    const uint32_t step = (uint32_t)G * kOpThreads * 16u;
+    const int64_t first = (k * G + j) * kOpThreads;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(x + first, span_bytes(first, nvec, 16u));
+    uint4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = buf_load16<kNonTemporal>(r, i * step + threadIdx.x * 16u, 0u);
+    uint32_t a = 0;
+    if constexpr (CAST) {
+        const __amdgpu_buffer_rsrc_t w = make_rsrc(q + first * kOut, span_bytes(first, nvec, kOut));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cast_vec_store<BF16, FMT>(w, i * (step / 16u * kOut) + threadIdx.x * kOut, v[i], s);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a = vec_absmax<BF16>(a, v[i]);
+    }
+    return a;
+}
+
+template <bool BF16, int FMT>
+__global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
+        const void *__restrict__ x, int64_t n, int64_t nvec, uint8_t *__restrict__ q, uint32_t *ws,
+        float *amax_out, float *scale_out, int32_t *nonfinite, uint32_t *amax_bits_out) {
+    constexpr int KR = kOpRegSlabs, KL = kOpLdsSlabs;
+    constexpr uint32_t kOut = BF16 ? 8u : 4u;
+    __shared__ uint4 held[KL * kOpThreads];
+    __shared__ uint32_t red[kOpThreads / 64];
+    __shared__ uint32_t sh[3];
+    __shared__ uint16_t gave_up[kBarMaxGroups];
+    const uint4 *xv = (const uint4 *)x;
+    const int G = gridDim.x, b = blockIdx.x, t = threadIdx.x;
+    const int64_t nslabs = (nvec + kOpThreads - 1) / kOpThreads;
+    // held slabs: offsets below (KR + KL) * G * kOpThreads * 16 < 2^32 (G <= kBarMaxGroups)
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(xv, span_bytes(0, nvec, 16u));
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q, span_bytes(0, nvec, kOut));
+    const uint32_t step = (uint32_t)G * kOpThreads * 16u;        // bytes between a workgroup's slabs
+    const uint32_t base = ((uint32_t)b * kOpThreads + t) * 16u;
+
+    // pass 1: slabs that are not held (maximum only), then the LDS-held slabs (DMA), then the
+    // register-held slabs, all loads in flight together
+    uint32_t a0 = 0;
+    for (int64_t k = KR + KL; k * G + b < nslabs; k += 8)
+        a0 = acc_max<BF16>(a0, stream_slabs8<BF16, FMT, false>(xv, nvec, q, k, b, G, 0.f));
+    a0 = acc_to_f32bits<BF16>(a0);
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+#pragma unroll
+    for (int k = 0; k < KL; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void *)&held[k * kOpThreads + wave * 64],
+                                                 16, base + (KR + k) * step, 0, 0, kNonTemporal);
+    uint4 R[KR];
+#pragma unroll
+    for (int k = 0; k < KR; ++k) R[k] = buf_load16<kNonTemporal>(rx, base + k * step, 0u);
+    uint32_t c0 = 0, c1 = 0;
+#pragma unroll
+    for (int k = 0; k < KR; ++k) {
+        if (k & 1) c1 = vec_absmax<BF16>(c1, R[k]);
+        else c0 = vec_absmax<BF16>(c0, R[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < KL; ++k) c1 = vec_absmax<BF16>(c1, held[k * kOpThreads + t]);
+    uint32_t m = umax(a0, umax(acc_to_f32bits<BF16>(c0), acc_to_f32bits<BF16>(c1)));
+    if (b == 0)                                                    // elements after the last vector
+        for (int64_t e = nvec * vec_elems<BF16>() + t; e < n; e += kOpThreads) m = umax(m, elem_bits<BF16>(x, e) & 0x7FFFFFFFu);
+    m = block_max_bcast<kOpThreads>(m, red);
+
+    // grid barrier
+    uint64_t *lines = (uint64_t *)(ws + kBarHeaderWords);
+    uint64_t *own = lines + (size_t)b * (kBarLineWords / 2);
+    if (t == 0) {
+        const uint32_t prev = __hip_atomic_fetch_max(ws + 1, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::"v"(prev) : "memory");   // maximum performed before arriving
+        const uint32_t old = __hip_atomic_fetch_add(ws + 0, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t role = 0, am = 0;
+        if (old == (uint32_t)G - 1) {
+            am = __hip_atomic_load(ws + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(ws + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(ws + 0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            role = 1;
+        } else {
+            const uint32_t limit = ws[2] ? ws[2] : kDefaultGiveUpTicks;
+            const uint64_t start = __builtin_amdgcn_s_memrealtime();
+            uint64_t v;
+            for (;;) {
+                v = __hip_atomic_load(own, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (v != 0) break;
+                if (__builtin_amdgcn_s_memrealtime() - start > limit) {
+                    uint64_t expected = 0;
+                    v = __hip_atomic_compare_exchange_strong(own, &expected, kLineGaveUp, __ATOMIC_RELAXED,
+                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                            ? kLineGaveUp : expected;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            if (v == kLineGaveUp) {
+                role = 2;
+            } else {
+                am = (uint32_t)v;
+                __hip_atomic_store(own, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        sh[0] = role;
+        sh[1] = am;
+        sh[2] = 0;
+    }
+    __syncthreads();
+    const uint32_t role = sh[0];
+    if (role == 2) return;                          // the last workgroup casts this one's slabs
+    m = sh[1];
+    uint64_t xres = 0;
+    if (role == 1 && t < G && t != b)               // release: one line per thread (G <= kOpThreads)
+        xres = __hip_atomic_exchange(lines + (size_t)t * (kBarLineWords / 2), kLineReleased | m, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+    const float s = scale_from_amax_bits<FMT>(m);
+
+    // pass 2: cast the held slabs, then re-read and cast the rest
+    const uint32_t qbase = ((uint32_t)b * kOpThreads + t) * kOut, qstep = step / 16u * kOut;
+#pragma unroll
+    for (int k = 0; k < KR; ++k) cast_vec_store<BF16, FMT>(rq, qbase + k * qstep, R[k], s);
+#pragma unroll
+    for (int k = 0; k < KL; ++k) cast_vec_store<BF16, FMT>(rq, qbase + (KR + k) * qstep, held[k * kOpThreads + t], s);
+    for (int64_t k = KR + KL; k * G + b < nslabs; k += 8) stream_slabs8<BF16, FMT, true>(xv, nvec, q, k, b, G, s);
+
+    if (role == 1) {
+        if (xres == kLineGaveUp) {                  // that workgroup exited: clear its line, cast its slabs
+            __hip_atomic_store(lines + (size_t)t * (kBarLineWords / 2), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            gave_up[atomicAdd(&sh[2], 1u)] = (uint16_t)t;
+        }
+        __syncthreads();
+        const uint32_t ng = sh[2];
+        for (uint32_t i = 0; i < ng; ++i)
+            for (int64_t k = 0; k * G + gave_up[i] < nslabs; k += 8) stream_slabs8<BF16, FMT, true>(xv, nvec, q, k, gave_up[i], G, s);
+        for (int64_t e = nvec * vec_elems<BF16>() + t; e < n; e += kOpThreads)
+            q[e] = (uint8_t)cast1<FMT>(__uint_as_float(elem_bits<BF16>(x, e)), s);
+        if (t == 0) {
+            if (amax_out) *amax_out = __uint_as_float(m);
+            if (scale_out) *scale_out = s;
+            if (amax_bits_out) *amax_bits_out = m;
+            if (nonfinite && m >= 0x7F800000u) *nonfinite = 1;
+        }
+    }
+}
+
 template <int FMT>
 __global__ __launch_bounds__(kFinalizeThreads) void delayed_finalize_kernel(const uint32_t *__restrict__ partials,
                                                                             int nparts, float *history, int32_t *meta,
@@ -371,6 +575,44 @@ int launch_cast_fused(const void *x, int dtype, int64_t n, int fmt, const float 
     QF8_DISPATCH_DT_FMT(dtype, fmt,
         hipLaunchKernelGGL((cast_fused_kernel<BF16, FMT>), dim3(grid), dim3(kThreads), 0, s, x, n, nvec, scale, q,
                            scale_used, partials));
+    return status_after_launch();
+}
+
+namespace {
+constexpr int64_t kOnePassMinElems = 1 << 22;
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_onepass_grid[kMaxDevices][2];   // 0 = not yet known, -1 = not usable
+
+int query_onepass_grid(int dtype) {
+    int dev = 0, cus = 0, occ = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+    std::atomic<int> &slot = g_onepass_grid[dev][dtype == QF8_IN_BF16 ? 0 : 1];
+    int g = slot.load(std::memory_order_relaxed);
+    if (g != 0) return g;
+    const void *fn = dtype == QF8_IN_BF16 ? (const void *)per_tensor_onepass_kernel<true, kE4M3>
+                                          : (const void *)per_tensor_onepass_kernel<false, kE4M3>;
+    g = -1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kOpThreads, 0) == hipSuccess && occ >= 1 && cus >= 1)
+        g = cus < kBarMaxGroups ? cus : kBarMaxGroups;
+    slot.store(g, std::memory_order_relaxed);
+    return g;
+}
+}  // namespace
+
+int onepass_grid(int64_t n, int dtype) {
+    if (n < kOnePassMinElems) return 0;
+    const int g = query_onepass_grid(dtype);
+    return g > 0 ? g : 0;
+}
+
+int launch_per_tensor_onepass(const void *x, int dtype, int64_t n, int fmt, uint8_t *q, uint32_t *ws,
+                              float *amax_out, float *scale_out, int32_t *nonfinite, uint32_t *amax_bits_out,
+                              int grid, hipStream_t s) {
+    const int64_t nvec = vec_count(n, dtype);
+    QF8_DISPATCH_DT_FMT(dtype, fmt,
+        hipLaunchKernelGGL((per_tensor_onepass_kernel<BF16, FMT>), dim3(grid), dim3(kOpThreads), 0, s, x, n, nvec, q,
+                           ws, amax_out, scale_out, nonfinite, amax_bits_out));
     return status_after_launch();
 }
 

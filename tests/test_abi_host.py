@@ -99,3 +99,15 @@ def test_no_cpu_path():
     import torch
     with pytest.raises(TypeError):
         qf8.quantize_mx_dual(torch.zeros(32, 32, dtype=torch.bfloat16), qf8.E4M3, qf8.ROUND_UP)
+
+
+def test_workspace_argument_errors():
+    L = lib()
+    need = qf8.qf8_workspace_bytes(64, 64)
+    assert need >= qf8.BARRIER_WORDS * 4 + 16384 * 4
+    assert L.qf8_workspace_init(None, need, None) == NULL
+    assert L.qf8_workspace_init(FAKE, need - 4, None) == WS
+    assert L.qf8_workspace_init(MISALIGNED, need, None) == ALIGN
+    fl = ctypes.c_void_p(0x20000)
+    f = L.quantize_per_tensor
+    assert f(FAKE, 0, 4, 4, 0, FAKE, fl, fl, None, MISALIGNED, need, None) == ALIGN   # ws 16-byte aligned

@@ -70,3 +70,14 @@ def test_repeat_identical_per_tensor_large():
     xd = to_device(x)
     a = [host(qf8.quantize_per_tensor(xd, qf8.E4M3)[0]) for _ in range(3)]
     assert np.array_equal(a[0], a[1]) and np.array_equal(a[1], a[2])
+
+
+def test_per_tensor_single_pass_canaries():
+    """The single-pass kernel on a ragged length: nothing written past q, every byte of q written."""
+    n = qf8.ONEPASS_MIN_ELEMS + 13
+    x = small_tensor(1, n, seed=9)
+    qv, qfull = guarded(n)
+    qf8.quantize_per_tensor(to_device(x), qf8.E4M3, q=qv.view(x.shape))
+    torch.cuda.synchronize()
+    assert canary_ok(qfull, n)
+    assert_bytes_equal(host(qv).reshape(x.shape), O.quantize_per_tensor(x, O.E4M3)[0], "q")

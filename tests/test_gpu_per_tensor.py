@@ -144,3 +144,83 @@ def test_full_size_activation(activation_full, fmt):
     assert am == wa and s == ws and nf == 0
     parts = parallel_row_slabs(lambda r0, r1: O.cast(x[r0:r1], fmt, ws), x.shape[0], 512)
     assert_bytes_equal(q, np.concatenate(parts, axis=0), "q", " [8192x8192]")
+
+
+# ---- the single-pass kernel (tensors of ONEPASS_MIN_ELEMS elements and more) ----------------
+
+def onchip_capacity_elems(dtype_bytes):
+    """Elements the single-pass kernel keeps on chip: one 512-thread workgroup per CU, 64 slabs
+    of 512 16-byte vectors each."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return min(cus, 512) * 512 * 64 * (16 // dtype_bytes)
+
+
+def oracle_flat(x, fmt):
+    """Oracle per-tensor result for a large tensor, its cast split over flat slabs in threads."""
+    flat = x.reshape(-1)
+    wa = np.float32(O.amax(flat))
+    ws = np.float32(O.scale_from_amax(fmt, wa))
+    step = 1 << 22
+    parts = parallel_row_slabs(lambda i0, i1: O.cast(flat[i0 * step:i1 * step], fmt, ws), (flat.size + step - 1) // step, 1)
+    return np.concatenate(parts).reshape(x.shape), wa, ws
+
+
+def barrier_words(ws):
+    return host(ws.view(torch.int32)[:qf8.BARRIER_WORDS]).astype(np.int64)
+
+
+def run_with_ws(x, fmt, ws):
+    xd = to_device(x)
+    q = torch.full(x.shape, 0xA5, dtype=torch.uint8, device="cuda")
+    nf = torch.zeros(1, dtype=torch.int32, device="cuda")
+    q, am, s = qf8.quantize_per_tensor(xd, fmt, q=q, nonfinite=nf, ws=ws)
+    torch.cuda.synchronize()
+    return host(q), np.float32(am.item()), np.float32(s.item()), int(nf.item())
+
+
+def check_big(x, fmt, ws, tag):
+    q, am, s, nf = run_with_ws(x, fmt, ws)
+    wq, wa, wsc = oracle_flat(x, fmt)
+    assert (am, s, nf) == (wa, wsc, 0), tag
+    assert_bytes_equal(q, wq, "q", f" [{tag}]")
+    words = barrier_words(ws)
+    words[2] = 0                                     # the timeout override is the caller's
+    assert not words.any(), f"barrier region not left zero [{tag}]"
+
+
+def test_onepass_threshold_and_capacity_bf16():
+    ws = qf8.workspace(torch.empty(1, device="cuda"))
+    cap = onchip_capacity_elems(2)
+    for n, seed in ((qf8.ONEPASS_MIN_ELEMS - 1, 1), (qf8.ONEPASS_MIN_ELEMS, 2), (cap + 8, 3), (cap + cap // 2 + 5, 4)):
+        print(f"onepass bf16 n={n}", flush=True)
+        x = small_tensor(1, n, seed=seed)
+        check_big(x, O.E4M3 if seed % 2 else O.E5M2, ws, f"bf16 n={n}")
+
+
+def test_onepass_fp32():
+    ws = qf8.workspace(torch.empty(1, device="cuda"))
+    rng = np.random.default_rng(8)
+    cap = onchip_capacity_elems(4)
+    for shape in ((cap // 4096, 4096), (1, cap + cap // 3 + 3)):
+        print(f"onepass fp32 {shape}", flush=True)
+        x = (rng.standard_normal(shape, dtype=np.float32) * np.float32(3.0)).astype(np.float32)
+        check_big(x, O.E4M3, ws, f"fp32 {shape}")
+
+
+@pytest.mark.parametrize("ticks", [1, 500])
+def test_onepass_give_up_path(activation_full, ticks):
+    """Force waiting workgroups to give up at the grid barrier (timeout override in workspace
+    word 2): their slabs are then cast by the last workgroup. Same bytes, barrier left clean."""
+    ws = qf8.workspace(torch.empty(1, device="cuda"))
+    ws.view(torch.int32)[2] = ticks
+    check_big(activation_full, O.E4M3, ws, f"give-up after {ticks} ticks")
+    ws.view(torch.int32)[2] = 0
+    check_big(activation_full, O.E4M3, ws, "default timeout after a give-up run")
+
+
+def test_onepass_workspace_reuse():
+    """One workspace across calls of both paths and several sizes, in a row on one stream."""
+    ws = qf8.workspace(torch.empty(1, device="cuda"))
+    for n, seed in ((5 << 20, 11), (1000, 12), (6 << 20 | 3, 13), (5 << 20, 14)):
+        x = small_tensor(1, n, seed=seed)
+        check_big(x, O.E4M3, ws, f"reuse n={n}")
