@@ -175,16 +175,23 @@ __device__ __forceinline__ uint32_t mx_byte_f32(uint32_t a) {
     const uint32_t b = e > (uint32_t)F8<FMT>::kEmax ? e - F8<FMT>::kEmax : 0u;
     return a >= 0x7F800000u ? 255u : b;
 }
-// |bits| of F8max * 2^X, the round-down clamp bound (byte = X + 127 <= 254 - emax for finite
-// input, so the result is a finite normal value).
+// Saturation of the round-down MX cast, applied to four packed codes after the scaled convert
+// (which does not saturate). With the round-down exponent every |x| / 2^X is below 2^(emax+1),
+// so a value can only overflow into (F8max, 2^(emax+1)); the convert then returns the overflow
+// code (E4M3: 0x7F, NaN; E5M2: 0x7C, Inf) with the input's sign, and that code minus one is
+// +-F8max. Every other code is left alone. Checked on gfx950 against clamping |x| to
+// F8max * 2^X before the convert: identical for all finite BF16 inputs and all 255 scales.
 template <int FMT>
-__device__ __forceinline__ uint32_t mx_clamp_bf16(uint32_t byte) {
-    return ((byte + F8<FMT>::kEmax) << 7) | 0x60u;
+__device__ __forceinline__ uint32_t mx_saturate_codes(uint32_t w) {
+    if constexpr (FMT == kE4M3) {                 // bytes whose low 7 bits are all ones
+        return w - ((((w & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u) >> 7);
+    } else {                                      // bytes whose low 7 bits are 0x7C
+        const uint32_t z = (w & 0x7F7F7F7Fu) ^ 0x7C7C7C7Cu;
+        const uint32_t nonzero = ((z + 0x7F7F7F7Fu) | z) & 0x80808080u;
+        return w - ((~nonzero & 0x80808080u) >> 7);
+    }
 }
-template <int FMT>
-__device__ __forceinline__ uint32_t mx_clamp_f32(uint32_t byte) {
-    return ((byte + F8<FMT>::kEmax) << 23) | 0x600000u;
-}
+
 
 // ---- buffer resources ------------------------------------------------------------------------
 // Raw buffer descriptors (stride 0): addresses are base + voffset (per lane) + soffset (uniform),

@@ -24,8 +24,9 @@
 //     writes every column's 128 rows of q_colT as whole 128-byte lines, and the E8M0 bytes of
 //     both directions, also gathered in LDS, as 4- or 8-byte runs.
 //   * The conversion is the gfx950 scaled convert (two values per instruction, divided by 2^X
-//     given as an fp32 exponent); OCP round-down first clamps |x| to F8max * 2^X on the bit
-//     pattern, since the instruction does not saturate. Round-up never exceeds F8max.
+//     given as an fp32 exponent). The instruction does not saturate: with OCP round-down a
+//     value can land in (F8max, 2^(emax+1)) and come out as the overflow code, which is then
+//     mapped to +-F8max on the packed codes (mx_saturate_codes). Round-up never exceeds F8max.
 //   * All global accesses are raw-buffer operations on per-wave descriptors: row and column
 //     strides become scalar offsets, lanes outside the tensor get an out-of-range offset (their
 //     loads read 0, their stores are dropped), and no per-row 64-bit address math is needed.
@@ -134,27 +135,16 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const void *__restrict__ x
                 bad |= byte == 255u;
                 const float sc = __uint_as_float(byte << 23);
                 const uint32_t zero_mask = a == 0u ? 0u : ~0u;        // all-zero block -> 0x00
-                uint32_t v[4];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) v[k] = d[i][k];
-                if constexpr (RND == kRoundDown) {                      // saturate before the cast
-                    if constexpr (BF16) {
-                        const uint32_t cb = mx_clamp_bf16<FMT>(byte), cbp = cb | (cb << 16);
-#pragma unroll
-                        for (int k = 0; k < 4; ++k) v[k] = bit_select(ABS, pk_min_u16(m[k], cbp), v[k]);
-                    } else {
-                        const uint32_t cb = mx_clamp_f32<FMT>(byte);
-#pragma unroll
-                        for (int k = 0; k < 4; ++k) v[k] = bit_select(ABS, umin(m[k], cb), v[k]);
-                    }
-                }
+                const uint32_t *v = d[i];
                 if constexpr (BF16) {
-                    const uint32_t o0 = cvt2_bf16_div2x<FMT, true>(v[1], sc, cvt2_bf16_div2x<FMT, false>(v[0], sc, 0u));
-                    const uint32_t o1 = cvt2_bf16_div2x<FMT, true>(v[3], sc, cvt2_bf16_div2x<FMT, false>(v[2], sc, 0u));
+                    uint32_t o0 = cvt2_bf16_div2x<FMT, true>(v[1], sc, cvt2_bf16_div2x<FMT, false>(v[0], sc, 0u));
+                    uint32_t o1 = cvt2_bf16_div2x<FMT, true>(v[3], sc, cvt2_bf16_div2x<FMT, false>(v[2], sc, 0u));
+                    if constexpr (RND == kRoundDown) { o0 = mx_saturate_codes<FMT>(o0); o1 = mx_saturate_codes<FMT>(o1); }
                     buf_store8(qr, qvo, (uint32_t)i * cols, o0 & zero_mask, o1 & zero_mask);
                 } else {
-                    const uint32_t o0 = cvt2_f32_div2x<FMT, true>(__uint_as_float(v[2]), __uint_as_float(v[3]), sc,
-                                        cvt2_f32_div2x<FMT, false>(__uint_as_float(v[0]), __uint_as_float(v[1]), sc, 0u));
+                    uint32_t o0 = cvt2_f32_div2x<FMT, true>(__uint_as_float(v[2]), __uint_as_float(v[3]), sc,
+                                  cvt2_f32_div2x<FMT, false>(__uint_as_float(v[0]), __uint_as_float(v[1]), sc, 0u));
+                    if constexpr (RND == kRoundDown) o0 = mx_saturate_codes<FMT>(o0);
                     buf_store4(qr, qvo, (uint32_t)i * cols, o0 & zero_mask);
                 }
                 if constexpr (COL) {
@@ -189,24 +179,25 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const void *__restrict__ x
                     bad |= (blo == 255u) | (bhi == 255u);
                     const float slo = __uint_as_float(blo << 23), shi = __uint_as_float(bhi << 23);
                     const uint32_t zlo = alo == 0u ? 0u : ~0u, zhi = ahi == 0u ? 0u : ~0u;
-                    uint32_t cbp = 0;
-                    if constexpr (RND == kRoundDown) cbp = mx_clamp_bf16<FMT>(blo) | (mx_clamp_bf16<FMT>(bhi) << 16);
                     uint32_t olo[4], ohi[4];
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {     // rows 4g .. 4g+3 of the lane
                         uint32_t w[4];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            w[j] = d[4 * g + j][k];
-                            if constexpr (RND == kRoundDown) w[j] = bit_select(ABS, pk_min_u16(w[j] & ABS, cbp), w[j]);
-                        }
+                        for (int j = 0; j < 4; ++j) w[j] = d[4 * g + j][k];
                         // one column's values of two consecutive rows in one dword
                         const uint32_t l01 = __builtin_amdgcn_perm(w[1], w[0], 0x05040100u);
                         const uint32_t l23 = __builtin_amdgcn_perm(w[3], w[2], 0x05040100u);
                         const uint32_t h01 = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);
                         const uint32_t h23 = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
-                        olo[g] = cvt2_bf16_div2x<FMT, true>(l23, slo, cvt2_bf16_div2x<FMT, false>(l01, slo, 0u)) & zlo;
-                        ohi[g] = cvt2_bf16_div2x<FMT, true>(h23, shi, cvt2_bf16_div2x<FMT, false>(h01, shi, 0u)) & zhi;
+                        olo[g] = cvt2_bf16_div2x<FMT, true>(l23, slo, cvt2_bf16_div2x<FMT, false>(l01, slo, 0u));
+                        ohi[g] = cvt2_bf16_div2x<FMT, true>(h23, shi, cvt2_bf16_div2x<FMT, false>(h01, shi, 0u));
+                        if constexpr (RND == kRoundDown) {
+                            olo[g] = mx_saturate_codes<FMT>(olo[g]);
+                            ohi[g] = mx_saturate_codes<FMT>(ohi[g]);
+                        }
+                        olo[g] &= zlo;
+                        ohi[g] &= zhi;
                     }
                     const int clo = slot * VEC + 2 * k;           // tile column of the low half
                     *(uint4 *)(colbuf + colbuf_offset(clo, chunk)) = make_uint4(olo[0], olo[1], olo[2], olo[3]);
@@ -224,19 +215,15 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const void *__restrict__ x
                     bad |= byte == 255u;
                     const float sc = __uint_as_float(byte << 23);
                     const uint32_t zm = a == 0u ? 0u : ~0u;
-                    uint32_t cb = 0;
-                    if constexpr (RND == kRoundDown) cb = mx_clamp_f32<FMT>(byte);
                     uint32_t o[4];
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         float f[4];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            uint32_t w = d[4 * g + j][k];
-                            if constexpr (RND == kRoundDown) w = bit_select(ABS, umin(w & ABS, cb), w);
-                            f[j] = __uint_as_float(w);
-                        }
-                        o[g] = cvt2_f32_div2x<FMT, true>(f[2], f[3], sc, cvt2_f32_div2x<FMT, false>(f[0], f[1], sc, 0u)) & zm;
+                        for (int j = 0; j < 4; ++j) f[j] = __uint_as_float(d[4 * g + j][k]);
+                        o[g] = cvt2_f32_div2x<FMT, true>(f[2], f[3], sc, cvt2_f32_div2x<FMT, false>(f[0], f[1], sc, 0u));
+                        if constexpr (RND == kRoundDown) o[g] = mx_saturate_codes<FMT>(o[g]);
+                        o[g] &= zm;
                     }
                     const int c = slot * VEC + k;
                     *(uint4 *)(colbuf + colbuf_offset(c, chunk)) = make_uint4(o[0], o[1], o[2], o[3]);
