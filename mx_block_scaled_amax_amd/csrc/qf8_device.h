@@ -166,13 +166,13 @@ __device__ __forceinline__ float scale_from_amax_bits(uint32_t abits) {
 template <int FMT, int RND>
 __device__ __forceinline__ uint32_t mx_byte_bf16(uint32_t a) {
     const uint32_t e = (RND == kRoundUp ? a + 0x1Fu : a) >> 7;
-    const uint32_t b = e > (uint32_t)F8<FMT>::kEmax ? e - F8<FMT>::kEmax : 0u;
+    const uint32_t b = __builtin_elementwise_sub_sat(e, (uint32_t)F8<FMT>::kEmax);
     return a >= 0x7F80u ? 255u : b;
 }
 template <int FMT, int RND>
 __device__ __forceinline__ uint32_t mx_byte_f32(uint32_t a) {
     const uint32_t e = (RND == kRoundUp ? a + 0x1FFFFFu : a) >> 23;
-    const uint32_t b = e > (uint32_t)F8<FMT>::kEmax ? e - F8<FMT>::kEmax : 0u;
+    const uint32_t b = __builtin_elementwise_sub_sat(e, (uint32_t)F8<FMT>::kEmax);
     return a >= 0x7F800000u ? 255u : b;
 }
 // Saturation of the round-down MX cast, applied to four packed codes after the scaled convert

@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const void *__restrict__ x
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63, half = lane >> 5, slot = lane & 31;
     const int r0 = tr0 + wave * kRowsPerWave;   // first row of the wave (uniform)
-    bool bad = false;
+    uint32_t seen = 0;     // |x| maximum of everything the lane loaded (BF16 or FP32 bit pattern)
 
     if (r0 < rows) {                             // else the wave only joins the barrier
         const int c0 = ct0 + slot * VEC;         // first column of the lane
@@ -131,21 +131,24 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const void *__restrict__ x
                 } else {
                     a = max_oct(umax(umax(m[0], m[1]), umax(m[2], m[3])));
                 }
+                if constexpr (!COL) seen = umax(seen, a);
                 const uint32_t byte = mx_byte<BF16, FMT, RND>(a);
-                bad |= byte == 255u;
                 const float sc = __uint_as_float(byte << 23);
-                const uint32_t zero_mask = a == 0u ? 0u : ~0u;        // all-zero block -> 0x00
                 const uint32_t *v = d[i];
+                // The converts write two of the four code bytes into their "old" operand; m[0] and
+                // m[2] are dead here, so their registers take the codes without a zeroing move.
                 if constexpr (BF16) {
-                    uint32_t o0 = cvt2_bf16_div2x<FMT, true>(v[1], sc, cvt2_bf16_div2x<FMT, false>(v[0], sc, 0u));
-                    uint32_t o1 = cvt2_bf16_div2x<FMT, true>(v[3], sc, cvt2_bf16_div2x<FMT, false>(v[2], sc, 0u));
+                    uint32_t o0 = cvt2_bf16_div2x<FMT, true>(v[1], sc, cvt2_bf16_div2x<FMT, false>(v[0], sc, m[0]));
+                    uint32_t o1 = cvt2_bf16_div2x<FMT, true>(v[3], sc, cvt2_bf16_div2x<FMT, false>(v[2], sc, m[2]));
                     if constexpr (RND == kRoundDown) { o0 = mx_saturate_codes<FMT>(o0); o1 = mx_saturate_codes<FMT>(o1); }
-                    buf_store8(qr, qvo, (uint32_t)i * cols, o0 & zero_mask, o1 & zero_mask);
+                    if (a == 0u) o0 = o1 = 0u;                          // all-zero block: 0x00, not -0
+                    buf_store8(qr, qvo, (uint32_t)i * cols, o0, o1);
                 } else {
                     uint32_t o0 = cvt2_f32_div2x<FMT, true>(__uint_as_float(v[2]), __uint_as_float(v[3]), sc,
-                                  cvt2_f32_div2x<FMT, false>(__uint_as_float(v[0]), __uint_as_float(v[1]), sc, 0u));
+                                  cvt2_f32_div2x<FMT, false>(__uint_as_float(v[0]), __uint_as_float(v[1]), sc, m[0]));
                     if constexpr (RND == kRoundDown) o0 = mx_saturate_codes<FMT>(o0);
-                    buf_store4(qr, qvo, (uint32_t)i * cols, o0 & zero_mask);
+                    if (a == 0u) o0 = 0u;
+                    buf_store4(qr, qvo, (uint32_t)i * cols, o0);
                 }
                 if constexpr (COL) {
                     // every lane of the block writes the same byte to the same LDS slot
@@ -172,13 +175,17 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const void *__restrict__ x
             }
             const int chunk = wave * 2 + half;   // 16-row chunk of the tile
             if constexpr (BF16) {
+                const uint32_t mm = pk_max_u16(pk_max_u16(cmax[0], cmax[1]), pk_max_u16(cmax[2], cmax[3]));
+                seen = umax(mm & 0xFFFFu, mm >> 16);
+            } else {
+                seen = umax(umax(cmax[0], cmax[1]), umax(cmax[2], cmax[3]));
+            }
+            if constexpr (BF16) {
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {     // dword k holds columns 2k (low half) and 2k+1
                     const uint32_t alo = cmax[k] & 0xFFFFu, ahi = cmax[k] >> 16;
                     const uint32_t blo = mx_byte<true, FMT, RND>(alo), bhi = mx_byte<true, FMT, RND>(ahi);
-                    bad |= (blo == 255u) | (bhi == 255u);
                     const float slo = __uint_as_float(blo << 23), shi = __uint_as_float(bhi << 23);
-                    const uint32_t zlo = alo == 0u ? 0u : ~0u, zhi = ahi == 0u ? 0u : ~0u;
                     uint32_t olo[4], ohi[4];
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {     // rows 4g .. 4g+3 of the lane
@@ -190,14 +197,15 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const void *__restrict__ x
                         const uint32_t l23 = __builtin_amdgcn_perm(w[3], w[2], 0x05040100u);
                         const uint32_t h01 = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u);
                         const uint32_t h23 = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
-                        olo[g] = cvt2_bf16_div2x<FMT, true>(l23, slo, cvt2_bf16_div2x<FMT, false>(l01, slo, 0u));
-                        ohi[g] = cvt2_bf16_div2x<FMT, true>(h23, shi, cvt2_bf16_div2x<FMT, false>(h01, shi, 0u));
+                        // w[0] and w[2] are dead after the permutes: they take the codes
+                        olo[g] = cvt2_bf16_div2x<FMT, true>(l23, slo, cvt2_bf16_div2x<FMT, false>(l01, slo, w[0]));
+                        ohi[g] = cvt2_bf16_div2x<FMT, true>(h23, shi, cvt2_bf16_div2x<FMT, false>(h01, shi, w[2]));
                         if constexpr (RND == kRoundDown) {
                             olo[g] = mx_saturate_codes<FMT>(olo[g]);
                             ohi[g] = mx_saturate_codes<FMT>(ohi[g]);
                         }
-                        olo[g] &= zlo;
-                        ohi[g] &= zhi;
+                        if (alo == 0u) olo[g] = 0u;          // all-zero block: 0x00, not -0
+                        if (ahi == 0u) ohi[g] = 0u;
                     }
                     const int clo = slot * VEC + 2 * k;           // tile column of the low half
                     *(uint4 *)(colbuf + colbuf_offset(clo, chunk)) = make_uint4(olo[0], olo[1], olo[2], olo[3]);
@@ -212,18 +220,17 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const void *__restrict__ x
                 for (int k = 0; k < 4; ++k) {     // tile column slot * 4 + k
                     const uint32_t a = cmax[k];
                     const uint32_t byte = mx_byte<false, FMT, RND>(a);
-                    bad |= byte == 255u;
                     const float sc = __uint_as_float(byte << 23);
-                    const uint32_t zm = a == 0u ? 0u : ~0u;
                     uint32_t o[4];
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         float f[4];
 #pragma unroll
                         for (int j = 0; j < 4; ++j) f[j] = __uint_as_float(d[4 * g + j][k]);
-                        o[g] = cvt2_f32_div2x<FMT, true>(f[2], f[3], sc, cvt2_f32_div2x<FMT, false>(f[0], f[1], sc, 0u));
+                        o[g] = cvt2_f32_div2x<FMT, true>(f[2], f[3], sc,
+                                                         cvt2_f32_div2x<FMT, false>(f[0], f[1], sc, d[4 * g][k]));
                         if constexpr (RND == kRoundDown) o[g] = mx_saturate_codes<FMT>(o[g]);
-                        o[g] &= zm;
+                        if (a == 0u) o[g] = 0u;
                     }
                     const int c = slot * VEC + k;
                     *(uint4 *)(colbuf + colbuf_offset(c, chunk)) = make_uint4(o[0], o[1], o[2], o[3]);
@@ -292,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const void *__restrict__ x
             }
         }
     }
-    if (bad && nonfinite) *nonfinite = 1;
+    if (seen >= (BF16 ? 0x7F80u : 0x7F800000u) && nonfinite) *nonfinite = 1;
 }
 
 template <bool BF16, int FMT, int RND>
