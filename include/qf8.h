@@ -62,10 +62,11 @@ typedef enum qf8_status {
 const char *qf8_status_string(int status);
 
 /* Bytes of device workspace quantize_per_tensor and quantize_delayed need for a tensor of
- * rows x cols elements of dtype (currently a constant of about 128 KiB): a grid-barrier region
- * (arrival counter, running maximum, one 128-byte release line per workgroup) and per-workgroup
- * partial maxima. The workspace must be zero-filled once before its first use (for example
- * with qf8_workspace_init); every call leaves the barrier region zero again, so the same
+ * rows x cols elements of dtype (currently a constant of about 160 KiB): a grid-barrier region
+ * (arrival counter, running maximum, one 128-byte release line per workgroup), 256 running
+ * amax slots for the fused delayed-scaling cast, and per-workgroup partial maxima. The
+ * workspace must be zero-filled once before its first use (for example with
+ * qf8_workspace_init); every call leaves the barrier and slot regions zero again, so the same
  * workspace serves any number of later calls ordered on one stream. Two calls that may run at
  * the same time need two workspaces. Word 2 (u32) of the workspace, if non-zero, replaces the
  * default 1 ms after which a workgroup waiting at the grid barrier gives its slabs to the last
@@ -131,8 +132,9 @@ int qf8_delayed_reset(qf8_delayed_state *st, void *stream);
  * amax (computed in the same pass as the cast; only update steps append it to the history).
  * ws: qf8_workspace_bytes(rows, cols, dtype) bytes, 16-byte aligned, initialised as described
  * at qf8_workspace_bytes.
- * Steps after the first are two kernel launches (fused cast, one-workgroup finalize); step 0
- * is the current-scaling path of quantize_per_tensor followed by the finalize. */
+ * Steps after the first are two kernel launches: the cast, which also raises atomic amax
+ * maxima in the workspace, and a one-workgroup finalize that reads and clears them and updates
+ * the state. Step 0 is the current-scaling path of quantize_per_tensor, then the finalize. */
 int quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, qf8_delayed_state *st,
                      uint8_t *q, float *scale_used, float *amax_out, int32_t *nonfinite,
                      void *ws, size_t ws_bytes, void *stream);

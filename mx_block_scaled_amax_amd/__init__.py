@@ -134,9 +134,10 @@ def qf8_workspace_bytes(rows, cols, dtype=torch.bfloat16):
 
 
 # Mirrors of two library constants, for tests: the number of leading u32 words of a workspace
-# that form the grid-barrier region (header line + 512 release lines of 32 words), and the
-# element count from which quantize_per_tensor uses the single-pass kernel.
-BARRIER_WORDS = 32 + 512 * 32
+# that every call leaves zero (grid-barrier header line, 512 release lines and 256 amax slot
+# lines, 32 words each), and the element count from which quantize_per_tensor uses the
+# single-pass kernel.
+BARRIER_WORDS = 32 + 512 * 32 + 256 * 32
 ONEPASS_MIN_ELEMS = 1 << 22
 
 

@@ -144,15 +144,16 @@ int quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, qf8_d
         return QF8_ERR_ALIGN;
     hipStream_t s = as_stream(stream);
     uint32_t *partials = (uint32_t *)ws + qf8::kPartialsOffsetWords;
+    uint32_t *slots = (uint32_t *)ws + qf8::kSlotsOffsetWords;
     const int grid = qf8::stream_grid(n, dtype);
     int r;
     if (st->step == 0) {
         // no history yet: current scaling (Eq.(1)-(2), no margin), then append this amax
         const int g1 = qf8::onepass_grid(n, dtype);
-        int nparts = 1;
-        if (g1 > 0) {
+        int nparts = 0;
+        if (g1 > 0) {              // the single-pass kernel leaves the amax in slot 0
             r = qf8::launch_per_tensor_onepass(x, dtype, n, st->fmt, q, (uint32_t *)ws, nullptr, scale_used, nullptr,
-                                               partials, g1, s);
+                                               slots, g1, s);
         } else {
             nparts = qf8::amax_grid(n, dtype);
             r = qf8::launch_amax_partials(x, dtype, n, partials, nparts, s);
@@ -161,15 +162,16 @@ int quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, qf8_d
                                              grid, s);
         }
         if (r == QF8_OK)
-            r = qf8::launch_delayed_finalize(partials, nparts, st->history, st->meta, st->scale, st->hist_len,
+            r = qf8::launch_delayed_finalize(slots, partials, nparts, st->history, st->meta, st->scale, st->hist_len,
                                              st->n_guard, st->fmt, 1, amax_out, nonfinite, s);
     } else {
-        // cast with the scale the history gave, fusing this step's partial maxima into the pass;
-        // then append the amax on update steps and compute the next scale
+        // cast with the scale the history gave, fusing this step's amax into the pass (atomic
+        // maxima in the workspace slots); then append the amax on update steps and compute the
+        // next scale
         const int update = (st->step % st->interval) == 0;
-        r = qf8::launch_cast_fused(x, dtype, n, st->fmt, st->scale, q, scale_used, partials, grid, s);
+        r = qf8::launch_cast_fused(x, dtype, n, st->fmt, st->scale, q, scale_used, slots, grid, s);
         if (r == QF8_OK)
-            r = qf8::launch_delayed_finalize(partials, grid, st->history, st->meta, st->scale, st->hist_len,
+            r = qf8::launch_delayed_finalize(slots, partials, 0, st->history, st->meta, st->scale, st->hist_len,
                                              st->n_guard, st->fmt, update, amax_out, nonfinite, s);
     }
     if (r == QF8_OK) st->step++;

@@ -19,12 +19,17 @@ constexpr int kMaxStreamGrid = 16384;  // workgroups of the streaming kernels at
 //   [0, kBarHeaderWords)      grid-barrier header: [0] arrival count, [1] amax bits, [2] give-up
 //                             timeout of a waiting workgroup in 10 ns ticks (0 = default 1 ms)
 //   kBarMaxGroups lines of kBarLineWords words (128 B each): the release line of each workgroup
-//   kMaxStreamGrid words      per-workgroup partial maxima of the multi-kernel paths
-// The barrier region must be zero before the first call; the single-pass kernel leaves it zero.
+//   kSlotCount lines of kBarLineWords words: word 0 of each is a running |amax| maximum that the
+//                             fused delayed-scaling cast raises atomically and the finalize
+//                             kernel reads and clears
+//   kMaxStreamGrid words      per-workgroup partial maxima of the two-kernel per-tensor path
+// Everything before the partials must be zero before the first call; every call leaves it zero.
 constexpr int kBarHeaderWords = 32;
 constexpr int kBarLineWords = 32;
 constexpr int kBarMaxGroups = 512;
-constexpr size_t kPartialsOffsetWords = kBarHeaderWords + (size_t)kBarMaxGroups * kBarLineWords;
+constexpr int kSlotCount = 256;
+constexpr size_t kSlotsOffsetWords = kBarHeaderWords + (size_t)kBarMaxGroups * kBarLineWords;
+constexpr size_t kPartialsOffsetWords = kSlotsOffsetWords + (size_t)kSlotCount * kBarLineWords;
 constexpr size_t kWorkspaceBytes = (kPartialsOffsetWords + kMaxStreamGrid) * sizeof(uint32_t);
 
 // Single-pass per-tensor kernel: its grid for n elements of dtype on the current device (one
@@ -41,8 +46,8 @@ int launch_cast_current(const void *x, int dtype, int64_t n, int fmt, uint8_t *q
 int launch_cast_scaled(const void *x, int dtype, int64_t n, int fmt, const float *scale, uint8_t *q, int grid,
                        hipStream_t s);
 int launch_cast_fused(const void *x, int dtype, int64_t n, int fmt, const float *scale, uint8_t *q,
-                      float *scale_used, uint32_t *partials, int grid, hipStream_t s);
-int launch_delayed_finalize(const uint32_t *partials, int nparts, float *history, int32_t *meta, float *scale,
+                      float *scale_used, uint32_t *slots, int grid, hipStream_t s);
+int launch_delayed_finalize(uint32_t *slots, const uint32_t *partials, int nparts, float *history, int32_t *meta, float *scale,
                             int hist_len, int n_guard, int fmt, int update, float *amax_out,
                             int32_t *nonfinite, hipStream_t s);
 int launch_fill_u32(uint32_t *p, int64_t n, uint32_t value, hipStream_t s);

@@ -19,13 +19,15 @@
 //   cast_current    -- every workgroup folds all partials into amax and S itself (so there is
 //                      no separate single-wave finalize launch), then casts its run.
 //   cast_scaled     -- cast with a scale read from device memory.
-//   cast_fused      -- a delayed-scaling step's pass: cast with the scale in the device state and
-//                      write each workgroup's |amax| alongside (amax fused into the cast).
-//   delayed_finalize -- one 1024-thread workgroup: the step's amax from the partials (all loads
-//                      of a thread issued together), FIFO push on update
+//   cast_fused      -- a delayed-scaling step's pass: cast with the scale in the device state;
+//                      each wave raises one of 256 workspace amax slots (128 B apart) with a
+//                      device-scope atomic max that it does not wait for.
+//   delayed_finalize -- one 256-thread workgroup: the step's amax from the slots (one load per
+//                      thread; the slots are cleared for the next step), FIFO push on update
 //                      steps, next scale into the state. (A single-launch variant that let the
 //                      last workgroup finalize measured slower: device-scope atomics from every
 //                      workgroup to one address serialize at the memory side.)
+//   per_tensor_onepass -- current scaling for large tensors in one HBM read (described below).
 #include <atomic>
 
 #include "qf8_device.h"
@@ -39,7 +41,7 @@ constexpr int kThreads = 256;
 constexpr int kVecs = 2;                        // 16-byte input vectors per thread and run
 constexpr int kAmaxThreads = 1024;              // read-only amax pass: one 16-wave workgroup per CU
 constexpr int kAmaxDepth = 8;                   //   16-byte loads per thread in flight
-constexpr int kFinalizeThreads = 1024;          // single-workgroup fold of the partial maxima
+constexpr int kFinalizeThreads = 256;           // single-workgroup finalize: one slot per thread
 constexpr int kOpThreads = 512;                 // single-pass kernel: 8 waves, 2 per SIMD
 constexpr int kOpRegSlabs = 48;                 //   slabs held in VGPRs (4 VGPRs each)
 constexpr int kOpLdsSlabs = 16;                 //   slabs held in LDS (8 KiB each)
@@ -284,12 +286,13 @@ __device__ void delayed_update(uint32_t m, float *history, int32_t *meta, float 
     }
 }
 
-// Cast with the state's scale and record each workgroup's |amax| for the finalize kernel.
+// Cast with the state's scale and raise the running |amax| maximum of one workspace slot per
+// wave (device-scope atomic max, not waited for; waves spread over kSlotCount slots, each on
+// its own 128-byte line, so no single address takes more than a few hundred updates).
 template <bool BF16, int FMT>
 __global__ __launch_bounds__(kThreads) void cast_fused_kernel(const void *__restrict__ x, int64_t n, int64_t nvec,
                                                               const float *__restrict__ scale, uint8_t *__restrict__ q,
-                                                              float *scale_used, uint32_t *__restrict__ partials) {
-    __shared__ uint32_t red[4];
+                                                              float *scale_used, uint32_t *slots) {
     const float s = *scale;
     uint32_t m = tail_absmax<BF16>(x, n, nvec);
     for (int64_t run = blockIdx.x; run < run_count(nvec); run += gridDim.x) {
@@ -299,11 +302,12 @@ __global__ __launch_bounds__(kThreads) void cast_fused_kernel(const void *__rest
         m = umax(m, r.absmax());
     }
     tail_cast<BF16, FMT>(x, n, nvec, s, q);
-    m = block_max_bcast(m, red);
-    if (threadIdx.x == 0) {
-        partials[blockIdx.x] = m;
-        if (blockIdx.x == 0 && scale_used) *scale_used = s;
+    m = max_wave(m);
+    if ((threadIdx.x & 63) == 0) {
+        const uint32_t slot = (blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) % kSlotCount;
+        __hip_atomic_fetch_max(slots + (size_t)slot * kBarLineWords, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    if (blockIdx.x == 0 && threadIdx.x == 0 && scale_used) *scale_used = s;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -499,15 +503,22 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
     }
 }
 
+// The step's amax = maximum of the workspace slots (cleared again for the next step) and of
+// nparts per-workgroup partials (the two-kernel current-scaling path of step 0), then the state
+// update.
 template <int FMT>
-__global__ __launch_bounds__(kFinalizeThreads) void delayed_finalize_kernel(const uint32_t *__restrict__ partials,
+__global__ __launch_bounds__(kFinalizeThreads) void delayed_finalize_kernel(uint32_t *slots, const uint32_t *__restrict__ partials,
                                                                             int nparts, float *history, int32_t *meta,
                                                                             float *scale, int hist_len, int n_guard,
                                                                             int update, float *amax_out,
                                                                             int32_t *nonfinite) {
+    static_assert(kFinalizeThreads == kSlotCount, "one slot per thread");
     __shared__ uint32_t red[kFinalizeThreads / 64];
     __shared__ int sh[2];
-    const uint32_t m = block_max_bcast<kFinalizeThreads>(fold_max<kFinalizeThreads>(partials, nparts), red);
+    uint32_t *own = slots + (size_t)threadIdx.x * kBarLineWords;
+    uint32_t m = umax(*own, fold_max<kFinalizeThreads>(partials, nparts));
+    *own = 0u;
+    m = block_max_bcast<kFinalizeThreads>(m, red);
     delayed_update<FMT>(m, history, meta, scale, hist_len, n_guard, update, amax_out, nonfinite, red, sh);
 }
 
@@ -570,11 +581,11 @@ int launch_cast_scaled(const void *x, int dtype, int64_t n, int fmt, const float
 }
 
 int launch_cast_fused(const void *x, int dtype, int64_t n, int fmt, const float *scale, uint8_t *q,
-                      float *scale_used, uint32_t *partials, int grid, hipStream_t s) {
+                      float *scale_used, uint32_t *slots, int grid, hipStream_t s) {
     const int64_t nvec = vec_count(n, dtype);
     QF8_DISPATCH_DT_FMT(dtype, fmt,
         hipLaunchKernelGGL((cast_fused_kernel<BF16, FMT>), dim3(grid), dim3(kThreads), 0, s, x, n, nvec, scale, q,
-                           scale_used, partials));
+                           scale_used, slots));
     return status_after_launch();
 }
 
@@ -616,15 +627,15 @@ int launch_per_tensor_onepass(const void *x, int dtype, int64_t n, int fmt, uint
     return status_after_launch();
 }
 
-int launch_delayed_finalize(const uint32_t *partials, int nparts, float *history, int32_t *meta, float *scale,
-                            int hist_len, int n_guard, int fmt, int update, float *amax_out,
+int launch_delayed_finalize(uint32_t *slots, const uint32_t *partials, int nparts, float *history, int32_t *meta,
+                            float *scale, int hist_len, int n_guard, int fmt, int update, float *amax_out,
                             int32_t *nonfinite, hipStream_t s) {
     if (fmt == QF8_E4M3)
-        hipLaunchKernelGGL(delayed_finalize_kernel<kE4M3>, dim3(1), dim3(kFinalizeThreads), 0, s, partials, nparts, history,
-                           meta, scale, hist_len, n_guard, update, amax_out, nonfinite);
+        hipLaunchKernelGGL(delayed_finalize_kernel<kE4M3>, dim3(1), dim3(kFinalizeThreads), 0, s, slots, partials, nparts,
+                           history, meta, scale, hist_len, n_guard, update, amax_out, nonfinite);
     else
-        hipLaunchKernelGGL(delayed_finalize_kernel<kE5M2>, dim3(1), dim3(kFinalizeThreads), 0, s, partials, nparts, history,
-                           meta, scale, hist_len, n_guard, update, amax_out, nonfinite);
+        hipLaunchKernelGGL(delayed_finalize_kernel<kE5M2>, dim3(1), dim3(kFinalizeThreads), 0, s, slots, partials, nparts,
+                           history, meta, scale, hist_len, n_guard, update, amax_out, nonfinite);
     return status_after_launch();
 }
 

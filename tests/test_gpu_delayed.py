@@ -157,3 +157,20 @@ def test_full_size_drifting_workload():
         h, c, stp = orc.state()
         assert st.step == stp
     assert st.history_list() == list(orc.state()[0])
+
+
+def test_workspace_clean_after_steps():
+    """The fused steps' amax slots and the step-0 barrier are left zero in the workspace, so one
+    workspace serves consecutive states and sizes (large: single-pass step 0; small: two kernels)."""
+    ws = qf8.workspace(torch.empty(1, device="cuda"))
+    for rows, cols in ((2048, 4096), (13, 29)):
+        p = Pair(8, 2, 1, O.E4M3)
+        for t in range(5):
+            x = small_tensor(rows, cols, seed=100 + t)
+            xd = to_device(x)
+            q = qf8.quantize_delayed(xd, p.g, ws=ws)
+            torch.cuda.synchronize()
+            wq, _, _, _ = p.o.step(x)
+            assert_bytes_equal(host(q), wq, "q", f" [{rows}x{cols} t={t}]")
+            words = host(ws.view(torch.int32)[:qf8.BARRIER_WORDS])
+            assert not words.any(), f"workspace not left zero [{rows}x{cols} t={t}]"
