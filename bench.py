@@ -73,6 +73,8 @@ def parse():
     ap.add_argument("--suite", action="store_true", help="also time every other operation")
     ap.add_argument("--only-dual", action="store_true",
                     help="launch only the dual kernel (E4M3 round-up) --steps times, for counter runs")
+    ap.add_argument("--only-per-tensor", action="store_true",
+                    help="launch only per-tensor E4M3 on the 8192x8192 activation --steps times, for counter runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="launch only a plain 256 MiB device copy --steps times, for counter runs")
     return ap.parse_args()
@@ -144,6 +146,20 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": args.steps}))
+        return
+
+    if args.only_per_tensor:
+        from synthetic import per_tensor_activation
+        xa = to_dev(per_tensor_activation())
+        q = torch.empty(xa.shape, dtype=torch.uint8, device="cuda")
+        am = torch.empty(1, dtype=torch.float32, device="cuda")
+        sc = torch.empty(1, dtype=torch.float32, device="cuda")
+        ws = qf8.workspace(xa)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            qf8.quantize_per_tensor(xa, qf8.E4M3, q=q, amax=am, scale=sc, ws=ws)
+        torch.cuda.synchronize()
+        print(json.dumps({"per_tensor_launches": args.steps, "bytes_per_launch": 3 * xa.numel() + 8}))
         return
 
     xb = mx_gradient(ROWS, COLS, seed=4)
@@ -227,8 +243,22 @@ def main():
 # ---------------------------------------------------------------------------------------------
 # --suite: every other operation on its own workload (reported to gpurun_out/bench_suite.json)
 # ---------------------------------------------------------------------------------------------
+class PreCall:
+    """A library entry point with its ctypes arguments marshalled once, so that back-to-back
+    launches are not limited by Python."""
+
+    def __init__(self, fn, *args):
+        self.fn, self.args = fn, args
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise RuntimeError(f"{self.fn.__name__} failed with status {st}")
+
+
 def _timed(torch, stream, fns, reps, warmup):
-    """Run fns round-robin (each on its own buffers); returns per-call kernel ms (HIP events)."""
+    """Run fns round-robin (each on its own buffers). Returns (per-call ms with an event pair
+    around each call, mean ms per call of reps calls back to back under one event pair)."""
     for i in range(warmup):
         fns[i % len(fns)]()
     torch.cuda.synchronize()
@@ -238,16 +268,26 @@ def _timed(torch, stream, fns, reps, warmup):
         fns[i % len(fns)]()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    return [a.elapsed_time(b) for a, b in ev]
+    per_call = [a.elapsed_time(b) for a, b in ev]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(reps):
+        fns[i % len(fns)]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return per_call, e0.elapsed_time(e1) / reps
 
 
-def _summ(name, nbytes, ms, extra=None):
+def _summ(name, nbytes, timing, extra=None):
+    """One suite line: back-to-back mean (the throughput figure) and the per-call distribution."""
     import numpy as np
+    ms, b2b = timing
     ms = np.array(ms)
     med = float(np.median(ms))
-    d = {"op": name, "algorithmic_bytes": int(nbytes), "median_ms": round(med, 5), "min_ms": round(float(ms.min()), 5),
-         "p90_ms": round(float(np.percentile(ms, 90)), 5), "GBps_median": round(nbytes / med / 1e6, 1),
-         "pct_of_8TBps": round(100 * nbytes / med / 1e6 / PEAK_GBPS, 2)}
+    d = {"op": name, "algorithmic_bytes": int(nbytes), "mean_ms_back_to_back": round(b2b, 5),
+         "GBps": round(nbytes / b2b / 1e6, 1), "pct_of_8TBps": round(100 * nbytes / b2b / 1e6 / PEAK_GBPS, 2),
+         "per_call_event_median_ms": round(med, 5), "per_call_event_min_ms": round(float(ms.min()), 5),
+         "per_call_event_p90_ms": round(float(np.percentile(ms, 90)), 5)}
     if extra:
         d.update(extra)
     print(json.dumps(d), file=sys.stderr, flush=True)
@@ -262,6 +302,9 @@ def run_suite(args):
     from synthetic import (block_weight, delayed_base, delayed_sigmas, per_tensor_activation, per_tensor_small,
                            token_activation)
     stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    L = qf8._load()
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
     reps, warm = 40, 5
     res = []
 
@@ -281,7 +324,8 @@ def run_suite(args):
     sc = torch.empty(1, dtype=torch.float32, device="cuda")
     ws = qf8.workspace(xs[0])
     for fmt, name in ((qf8.E4M3, "e4m3"), (qf8.E5M2, "e5m2")):
-        fns = [lambda x=x: qf8.quantize_per_tensor(x, fmt, q=q, amax=am, scale=sc, ws=ws) for x in xs]
+        fns = [PreCall(L.quantize_per_tensor, vp(x), 0, xb.shape[0], xb.shape[1], fmt, vp(q), vp(am), vp(sc), None,
+                       vp(ws), ws.numel(), sp) for x in xs]
         res.append(_summ(f"per_tensor 8192x8192 {name}", 3 * n + 8, _timed(torch, stream, fns, reps, warm),
                          {"note": "one kernel, x read from HBM once (held on chip across a grid barrier)"}))
     del xs
@@ -289,33 +333,52 @@ def run_suite(args):
     # per-tensor and MX rowwise on the 256x512 tensor (latency-bound)
     xsm = to_dev(per_tensor_small())
     qs = torch.empty(xsm.shape, dtype=torch.uint8, device="cuda")
+    ssm = torch.empty((xsm.shape[0], xsm.shape[1] // 32), dtype=torch.uint8, device="cuda")
     res.append(_summ("per_tensor 256x512 e4m3", 3 * xsm.numel() + 8,
-                     _timed(torch, stream, [lambda: qf8.quantize_per_tensor(xsm, qf8.E4M3, q=qs, amax=am, scale=sc, ws=ws)], reps, warm)))
+                     _timed(torch, stream, [PreCall(L.quantize_per_tensor, vp(xsm), 0, xsm.shape[0], xsm.shape[1], qf8.E4M3,
+                                                    vp(qs), vp(am), vp(sc), None, vp(ws), ws.numel(), sp)], reps, warm)))
     res.append(_summ("mx rowwise 256x512 e4m3 round-up", 3 * xsm.numel() + xsm.numel() // 32,
-                     _timed(torch, stream, [lambda: qf8.quantize_mx_dual(xsm, qf8.E4M3, qf8.ROUND_UP, colwise=False)], reps, warm)))
+                     _timed(torch, stream, [PreCall(L.quantize_mx_dual, vp(xsm), 0, xsm.shape[0], xsm.shape[1], qf8.E4M3,
+                                                    qf8.ROUND_UP, vp(qs), vp(ssm), None, None, None, sp)], reps, warm)))
 
     # delayed scaling: 100 iterations of 4096x14336 (history 16, Interval 5, N 3, E4M3)
     z = torch.from_numpy(delayed_base()).cuda()
     sig = delayed_sigmas()
     xsd = [(z * float(s)).to(torch.bfloat16) for s in sig]
     del z
-    st = qf8.DelayedState(16, 5, 3, qf8.E4M3)
     qd = torch.empty(xsd[0].shape, dtype=torch.uint8, device="cuda")
     wsd = qf8.workspace(xsd[0])
-    for _ in range(2):                              # warm the code path on a throwaway state
-        qf8.quantize_delayed(xsd[0], qf8.DelayedState(16, 5, 3, qf8.E4M3), q=qd, ws=wsd)
+    R, C = xsd[0].shape
+
+    def steps_of(state):
+        return [PreCall(L.quantize_delayed, vp(x), 0, R, C, ctypes.byref(state.struct), vp(qd), None, None, None,
+                        vp(wsd), wsd.numel(), sp) for x in xsd]
+    for c in steps_of(qf8.DelayedState(16, 5, 3, qf8.E4M3))[:3]:     # warm the code paths on a throwaway state
+        c()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in xsd]
-    for t, x in enumerate(xsd):
+    # pass 1: an event pair around every step (distribution, step 0 alone)
+    calls = steps_of(qf8.DelayedState(16, 5, 3, qf8.E4M3))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+    for t, c in enumerate(calls):
         ev[t][0].record(stream)
-        qf8.quantize_delayed(x, st, q=qd, ws=wsd)
+        c()
         ev[t][1].record(stream)
     torch.cuda.synchronize()
     ms = [a.elapsed_time(b) for a, b in ev]
+    # pass 2: a fresh state, steps 1..99 back to back under one event pair
+    calls = steps_of(qf8.DelayedState(16, 5, 3, qf8.E4M3))
+    calls[0]()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for c in calls[1:]:
+        c()
+    e1.record(stream)
+    torch.cuda.synchronize()
     nd = xsd[0].numel()
-    res.append(_summ("delayed 4096x14336 e4m3, steps 1..99", 3 * nd, ms[1:],
-                     {"step0_ms": round(ms[0], 5), "total_100_steps_ms": round(sum(ms), 4),
-                      "note": "step 0 is current scaling (2 passes); later steps one fused pass + 1-workgroup finalize"}))
+    res.append(_summ("delayed 4096x14336 e4m3, steps 1..99", 3 * nd, (ms[1:], e0.elapsed_time(e1) / (len(calls) - 1)),
+                     {"step0_ms": round(ms[0], 5), "total_100_steps_ms_event_per_step": round(sum(ms), 4),
+                      "note": "step 0 is current scaling (single-pass kernel + finalize); later steps one fused "
+                              "cast pass + a one-workgroup finalize"}))
     del xsd
 
     # fine-grained: 1x128 activations 8192x7168 and 128x128 weights 7168x18432 (E4M3)
@@ -324,14 +387,16 @@ def run_suite(args):
     qa = torch.empty(xa.shape, dtype=torch.uint8, device="cuda")
     sa = torch.empty((xa.shape[0], xa.shape[1] // 128), dtype=torch.float32, device="cuda")
     res.append(_summ("block 1x128 8192x7168 e4m3", 3 * xa.size + 4 * sa.numel(),
-                     _timed(torch, stream, [lambda x=x: qf8.quantize_block(x, 1, 128, qf8.E4M3, q=qa, scales=sa, want_amax=False) for x in xas], reps, warm)))
+                     _timed(torch, stream, [PreCall(L.quantize_block, vp(x), 0, xa.shape[0], xa.shape[1], 1, 128, qf8.E4M3,
+                                                    vp(qa), vp(sa), None, None, sp) for x in xas], reps, warm)))
     del xas
     xw = block_weight()
     xws = [to_dev(xw) for _ in range(2)]
     qw = torch.empty(xw.shape, dtype=torch.uint8, device="cuda")
     sw = torch.empty((xw.shape[0] // 128, xw.shape[1] // 128), dtype=torch.float32, device="cuda")
     res.append(_summ("block 128x128 7168x18432 e4m3", 3 * xw.size + 4 * sw.numel(),
-                     _timed(torch, stream, [lambda x=x: qf8.quantize_block(x, 128, 128, qf8.E4M3, q=qw, scales=sw, want_amax=False) for x in xws], reps, warm)))
+                     _timed(torch, stream, [PreCall(L.quantize_block, vp(x), 0, xw.shape[0], xw.shape[1], 128, 128, qf8.E4M3,
+                                                    vp(qw), vp(sw), None, None, sp) for x in xws], reps, warm)))
     del xws
     os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
     with open(os.path.join(ROOT, "gpurun_out", "bench_suite.json"), "w") as f:
