@@ -16,8 +16,9 @@ constexpr int kAmaxGrid = 256;
 constexpr int kMaxStreamGrid = 16384;  // workgroups of the streaming kernels at most (= partials)
 
 // Workspace layout, in u32 words:
-//   [0, kBarHeaderWords)      grid-barrier header: [0] arrival count, [1] amax bits, [2] give-up
-//                             timeout of a waiting workgroup in 10 ns ticks (0 = default 1 ms)
+//   [0, kBarHeaderWords)      grid-barrier header: [0] running amax bits, [1] arrival count (one
+//                             64-bit word), [2] give-up timeout of a waiting workgroup in 10 ns
+//                             ticks (0 = default 1 ms)
 //   kBarMaxGroups lines of kBarLineWords words (128 B each): the release line of each workgroup
 //   kSlotCount lines of kBarLineWords words: word 0 of each is a running |amax| maximum that the
 //                             fused delayed-scaling cast raises atomically and the finalize

@@ -320,12 +320,14 @@ __global__ __launch_bounds__(kThreads) void cast_fused_kernel(const void *__rest
 // is read from HBM exactly once; slabs beyond that are reduced in the first pass and re-read
 // for the cast.
 //
-// Grid barrier (workspace words, all device-scope atomics):
-//   every workgroup: fetch_max(amax word, its |amax|), waiting for the returned value so the
-//     maximum is performed before the arrival; then fetch_add(count, 1).
-//   the workgroup that sees count == G - 1 arrived last: it reads the final maximum, returns
-//     both words to 0, and releases each other workgroup by exchanging RELEASED | amax into that
-//     workgroup's own 128-byte line (one line per poller: no same-address polling).
+// Grid barrier (workspace words 0-1 = one 64-bit word: running amax low, arrival count high; all
+// device-scope atomics on the same 8 bytes):
+//   every workgroup: 32-bit fetch_max on the low word with its |amax|, waiting for the returned
+//     value so the maximum is performed before the arrival; then a 64-bit fetch_add of 2^32,
+//     whose returned value carries both the count and the maximum of every earlier arrival.
+//   the workgroup that sees count == G - 1 arrived last and so already holds the final maximum:
+//     it returns the word to 0 and releases each other workgroup by exchanging RELEASED | amax
+//     into that workgroup's own 128-byte line (one line per poller: no same-address polling).
 //   every other workgroup polls its own line. If it is not released within the timeout it
 //     tries to mark the line GAVE_UP (compare-exchange from 0) and exits without casting; the
 //     last workgroup then finds GAVE_UP in the exchange result and casts all of that
@@ -429,14 +431,14 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
     uint64_t *lines = (uint64_t *)(ws + kBarHeaderWords);
     uint64_t *own = lines + (size_t)b * (kBarLineWords / 2);
     if (t == 0) {
-        const uint32_t prev = __hip_atomic_fetch_max(ws + 1, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint64_t *word = (uint64_t *)ws;                              // [amax | count << 32]
+        const uint32_t prev = __hip_atomic_fetch_max(ws, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         asm volatile("s_waitcnt vmcnt(0)" ::"v"(prev) : "memory");   // maximum performed before arriving
-        const uint32_t old = __hip_atomic_fetch_add(ws + 0, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t old = __hip_atomic_fetch_add(word, 1ull << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         uint32_t role = 0, am = 0;
-        if (old == (uint32_t)G - 1) {
-            am = __hip_atomic_load(ws + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(ws + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(ws + 0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((uint32_t)(old >> 32) == (uint32_t)G - 1) {
+            am = umax((uint32_t)old, m);
+            __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             role = 1;
         } else {
             const uint32_t limit = ws[2] ? ws[2] : kDefaultGiveUpTicks;
