@@ -88,6 +88,27 @@ def _load():
     lib.qf8o_quantize_mx.restype = None
     lib.qf8o_quantize_mx.argtypes = [_c_void_p, ctypes.c_int, _i64, _i64, ctypes.c_int, ctypes.c_int,
                                      _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]
+    lib.qf8o_dequant_one.restype = ctypes.c_float
+    lib.qf8o_dequant_one.argtypes = [ctypes.c_int, ctypes.c_uint, ctypes.c_float]
+    lib.qf8o_dequant_mx_one.restype = ctypes.c_float
+    lib.qf8o_dequant_mx_one.argtypes = [ctypes.c_int, ctypes.c_uint, ctypes.c_uint]
+    lib.qf8o_dequant_scaled.restype = None
+    lib.qf8o_dequant_scaled.argtypes = [_c_void_p, _i64, ctypes.c_int, ctypes.c_float, _c_void_p]
+    lib.qf8o_dequant_block.restype = None
+    lib.qf8o_dequant_block.argtypes = [_c_void_p, _i64, _i64, _i64, _i64, ctypes.c_int, _c_void_p, _c_void_p]
+    lib.qf8o_dequant_mx.restype = None
+    lib.qf8o_dequant_mx.argtypes = [_c_void_p, _c_void_p, _i64, _i64, ctypes.c_int, _c_void_p]
+    lib.qf8o_f32_to_bf16.restype = None
+    lib.qf8o_f32_to_bf16.argtypes = [_c_void_p, _i64, _c_void_p]
+    lib.qf8o_stats_scaled.restype = None
+    lib.qf8o_stats_scaled.argtypes = [_c_void_p, ctypes.c_int, _c_void_p, _i64, ctypes.c_int, ctypes.c_float,
+                                      _c_void_p, _c_void_p]
+    lib.qf8o_stats_block.restype = None
+    lib.qf8o_stats_block.argtypes = [_c_void_p, ctypes.c_int, _c_void_p, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                     _c_void_p, _c_void_p, _c_void_p]
+    lib.qf8o_stats_mx.restype = None
+    lib.qf8o_stats_mx.argtypes = [_c_void_p, ctypes.c_int, _c_void_p, _c_void_p, _i64, _i64, ctypes.c_int,
+                                  _c_void_p, _c_void_p]
     _lib = lib
     return lib
 
@@ -237,3 +258,90 @@ def quantize_mx(x, fmt, rnd, row=True, col=True):
     _load().qf8o_quantize_mx(_ptr(x), _dtype_code(x), rows, cols, fmt, rnd, _ptr(q_row), _ptr(s_row),
                              _ptr(q_colT), _ptr(s_colT), _ptr(nf))
     return q_row, s_row, q_colT, s_colT, int(nf[0])
+
+
+# ---- dequantization and error statistics --------------------------------------------------
+
+STATS_FIELDS = ("count", "nonzero", "zeroed", "saturated", "nonfinite")
+
+
+def dequant_one(fmt, code, scale):
+    """fl32(decode(code) / scale)."""
+    return _load().qf8o_dequant_one(fmt, int(code), float(np.float32(scale)))
+
+
+def dequant_mx_one(fmt, code, sbyte):
+    """fl32(decode(code) * 2^(sbyte - 127)); NaN for sbyte 0xFF."""
+    return _load().qf8o_dequant_mx_one(fmt, int(code), int(sbyte))
+
+
+def dequant_scaled(q, fmt, scale):
+    """Per-tensor (or delayed) dequantization: float32 array of q's shape."""
+    q = np.ascontiguousarray(q, np.uint8)
+    out = np.empty(q.shape, np.float32)
+    _load().qf8o_dequant_scaled(_ptr(q), q.size, fmt, float(np.float32(scale)), _ptr(out))
+    return out
+
+
+def dequant_block(q, br, bc, fmt, scales):
+    q = np.ascontiguousarray(q, np.uint8)
+    scales = np.ascontiguousarray(scales, np.float32)
+    rows, cols = q.shape
+    out = np.empty(q.shape, np.float32)
+    _load().qf8o_dequant_block(_ptr(q), rows, cols, br, bc, fmt, _ptr(scales), _ptr(out))
+    return out
+
+
+def dequant_mx(q, s, fmt):
+    """q [rows][cols] with blocks of 32 along rows, s [rows][cols/32] E8M0 bytes."""
+    q = np.ascontiguousarray(q, np.uint8)
+    s = np.ascontiguousarray(s, np.uint8)
+    rows, cols = q.shape
+    out = np.empty(q.shape, np.float32)
+    _load().qf8o_dequant_mx(_ptr(q), _ptr(s), rows, cols, fmt, _ptr(out))
+    return out
+
+
+def to_bf16(f):
+    """float32 array -> BF16 bit patterns (uint16), round to nearest even."""
+    f = np.ascontiguousarray(f, np.float32)
+    out = np.empty(f.shape, np.uint16)
+    _load().qf8o_f32_to_bf16(_ptr(f), f.size, _ptr(out))
+    return out
+
+
+def _stats_dict(sums, counts):
+    d = {"signal": float(sums[0]), "noise": float(sums[1])}
+    d.update({k: int(v) for k, v in zip(STATS_FIELDS, counts)})
+    return d
+
+
+def stats_scaled(x, q, fmt, scale):
+    x = _contig(x)
+    q = np.ascontiguousarray(q, np.uint8)
+    sums, counts = np.zeros(2, np.float64), np.zeros(5, np.int64)
+    _load().qf8o_stats_scaled(_ptr(x), _dtype_code(x), _ptr(q), x.size, fmt, float(np.float32(scale)),
+                              _ptr(sums), _ptr(counts))
+    return _stats_dict(sums, counts)
+
+
+def stats_block(x, q, br, bc, fmt, scales):
+    x = _contig(x)
+    q = np.ascontiguousarray(q, np.uint8)
+    scales = np.ascontiguousarray(scales, np.float32)
+    rows, cols = x.shape
+    sums, counts = np.zeros(2, np.float64), np.zeros(5, np.int64)
+    _load().qf8o_stats_block(_ptr(x), _dtype_code(x), _ptr(q), rows, cols, br, bc, fmt, _ptr(scales),
+                             _ptr(sums), _ptr(counts))
+    return _stats_dict(sums, counts)
+
+
+def stats_mx(x, q, s, fmt):
+    """x in the layout of q (for a columnwise result: x transposed)."""
+    x = _contig(x)
+    q = np.ascontiguousarray(q, np.uint8)
+    s = np.ascontiguousarray(s, np.uint8)
+    rows, cols = x.shape
+    sums, counts = np.zeros(2, np.float64), np.zeros(5, np.int64)
+    _load().qf8o_stats_mx(_ptr(x), _dtype_code(x), _ptr(q), _ptr(s), rows, cols, fmt, _ptr(sums), _ptr(counts))
+    return _stats_dict(sums, counts)

@@ -17,6 +17,14 @@
  *   [MXFP8-recipe] "NVIDIA：Blackwell GPU MXFP8 预训练最佳实践" (51cto.com):
  *                  section 4.1 (amax = 0 gives X = -127, OCP round-down exponent, the
  *                  round-up exponent of Algorithm 1, saturating RNE cast of V/2^X).
+ *   [Ascend950]    Ascend 950 low-precision format guide (hwcomputing.csdn.net): the HiF8 vs
+ *                  MXFP8 numerical analysis on DeepSeek-V4-Flash (per-layer SQNR and zero-rate
+ *                  of quantized weights, activations and KV cache).
+ *   Dequantization and error statistics follow [MP-FP8] section 8.1 (the worked example
+ *   de-scales the code 22 by S = 22400 to 22/22400 ~ 0.000982; a GEMM multiplies its result
+ *   back by 1/(S_X S_W)), 8.2 (the saturated 50 -> 448 de-scales to 20) and 7.2 (watch amax,
+ *   the fraction of values that underflow to zero, and saturation), and [Ascend950] (SQNR,
+ *   zero-rate).
  *
  * Arithmetic: fp64 throughout. A value is rounded to fp32 exactly where the method keeps an
  * fp32 value (the scale factor S and the scaled product x*S). Both roundings are done by a cast
@@ -38,7 +46,17 @@
  *   R7 delayed: step 0 (after init or reset) is current scaling without the 2^-N margin; later
  *      steps scale with the history as it stood before the step, then append; the update
  *      steps are step % Interval == 0; an empty history estimate counts as amax = 0;
- *   R8 the OCP round-down exponent is floor(log2 amax) - emax (a difference, not a quotient).
+ *   R8 the OCP round-down exponent is floor(log2 amax) - emax (a difference, not a quotient);
+ *   R9 de-scaling by a scale factor S divides in fp32: xhat = fl32(decode(q) / S) (the 22/22400
+ *      example); an MX element is multiplied by its block's 2^X: xhat = fl32(decode(q) * 2^X),
+ *      and an E8M0 byte 0xFF gives NaN;
+ *   R10 a BF16 dequantized output is that fp32 value rounded to BF16 to nearest, ties to even;
+ *   R11 error statistics over the finite elements of the source x: signal = sum x^2,
+ *      noise = sum (x - xhat)^2 (SQNR = 10 log10(signal / noise)), nonzero = #(x != 0),
+ *      zeroed = #(x != 0 and xhat == 0) (the zero-rate numerator), saturated = #(elements whose
+ *      scaled value exceeded F8max before the saturating cast), nonfinite = #(Inf/NaN in x).
+ *      Per-element terms are fp64 operations on exact fp64 copies of x and xhat; the sums run in
+ *      index order (any other order differs only by fp64 rounding).
  */
 #include <stdint.h>
 #include <stddef.h>
@@ -419,4 +437,135 @@ void qf8o_quantize_mx(const void *x, int dtype, int64_t rows, int64_t cols, int 
             }
     }
     if (nonfinite) *nonfinite = bad;
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Dequantization (R9, R10) and quantization error statistics (R11).
+ * ------------------------------------------------------------------------------------------- */
+
+/* xhat = fl32(decode(q) / S): decode(q) and S are both fp32 values, so the fp64 quotient
+ * rounded to fp32 is the correctly rounded fp32 quotient (53 >= 2*24 + 2). */
+float qf8o_dequant_one(int fmt, unsigned code, float scale)
+{
+    return (float)(qf8o_decode(fmt, code) / (double)scale);
+}
+
+/* xhat = fl32(decode(q) * 2^X) with X = byte - 127; exact unless it overflows fp32. */
+float qf8o_dequant_mx_one(int fmt, unsigned code, unsigned sbyte)
+{
+    if ((sbyte & 0xFFu) == 0xFFu) return NAN;
+    return (float)ldexp(qf8o_decode(fmt, code), (int)(sbyte & 0xFFu) - 127);
+}
+
+void qf8o_dequant_scaled(const uint8_t *q, int64_t n, int fmt, float scale, float *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = qf8o_dequant_one(fmt, q[i], scale);
+}
+
+/* Each br x bc group divides by its own S_g; scales is [ceil(rows/br)][ceil(cols/bc)]. */
+void qf8o_dequant_block(const uint8_t *q, int64_t rows, int64_t cols, int64_t br, int64_t bc, int fmt,
+                        const float *scales, float *out)
+{
+    int64_t gc = (cols + bc - 1) / bc;
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            out[r * cols + c] = qf8o_dequant_one(fmt, q[r * cols + c], scales[(r / br) * gc + c / bc]);
+}
+
+/* q [rows][cols] with blocks of 32 along each row and s [rows][cols/32] (a rowwise result, or
+ * a columnwise result in its transposed layout). */
+void qf8o_dequant_mx(const uint8_t *q, const uint8_t *sb, int64_t rows, int64_t cols, int fmt, float *out)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            out[r * cols + c] = qf8o_dequant_mx_one(fmt, q[r * cols + c], sb[r * (cols / 32) + c / 32]);
+}
+
+/* fp32 -> BF16, round to nearest, ties to even (R10). The BF16 values are exactly the fp32
+ * values whose low 16 bits are zero, with the same exponent range, and for finite values of one
+ * sign the bit pattern grows with the magnitude. So the nearest BF16 value is the pattern
+ * rounded to a multiple of 2^16: up when the dropped half exceeds 0x8000, down when below, and
+ * at exactly 0x8000 (a tie) to the even result. Rounding up past the largest finite value gives
+ * the Inf pattern, as IEEE overflow does. NaN stays NaN (quiet, sign kept). */
+uint16_t qf8o_f32_to_bf16_one(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if (isnan(f)) return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t hi = u >> 16, lo = u & 0xFFFFu;
+    if (lo > 0x8000u || (lo == 0x8000u && (hi & 1u))) hi += 1u;
+    return (uint16_t)hi;
+}
+
+void qf8o_f32_to_bf16(const float *in, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) out[i] = qf8o_f32_to_bf16_one(in[i]);
+}
+
+/* Statistics accumulator (R11). sums[0] = signal, sums[1] = noise; counts[0..4] = count,
+ * nonzero, zeroed, saturated, nonfinite. */
+static void stats_add(double *sums, int64_t *counts, double x, float xhat, int saturated)
+{
+    if (!isfinite(x)) { counts[4]++; return; }
+    counts[0]++;
+    sums[0] += x * x;
+    double d = x - (double)xhat;
+    sums[1] += d * d;
+    if (x != 0.0) {
+        counts[1]++;
+        if (xhat == 0.0f) counts[2]++;
+    }
+    if (saturated) counts[3]++;
+}
+
+static void stats_clear(double *sums, int64_t *counts)
+{
+    sums[0] = sums[1] = 0.0;
+    for (int k = 0; k < 5; ++k) counts[k] = 0;
+}
+
+/* A scale-factor element saturates when |fl32(x * S)| > F8max (the cast clips it). */
+static int scaled_saturates(int fmt, double x, float scale)
+{
+    float p = (float)(x * (double)scale);
+    return fabs((double)p) > qf8o_max_finite(fmt);
+}
+
+void qf8o_stats_scaled(const void *x, int dtype, const uint8_t *q, int64_t n, int fmt, float scale,
+                       double *sums, int64_t *counts)
+{
+    stats_clear(sums, counts);
+    for (int64_t i = 0; i < n; ++i) {
+        double v = load_elem(x, dtype, i);
+        stats_add(sums, counts, v, qf8o_dequant_one(fmt, q[i], scale), isfinite(v) && scaled_saturates(fmt, v, scale));
+    }
+}
+
+void qf8o_stats_block(const void *x, int dtype, const uint8_t *q, int64_t rows, int64_t cols, int64_t br,
+                      int64_t bc, int fmt, const float *scales, double *sums, int64_t *counts)
+{
+    int64_t gc = (cols + bc - 1) / bc;
+    stats_clear(sums, counts);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            int64_t i = r * cols + c;
+            float sg = scales[(r / br) * gc + c / bc];
+            double v = load_elem(x, dtype, i);
+            stats_add(sums, counts, v, qf8o_dequant_one(fmt, q[i], sg), isfinite(v) && scaled_saturates(fmt, v, sg));
+        }
+}
+
+/* An MX element saturates when |x| / 2^X > F8max, i.e. |x| > F8max * 2^X (exact in fp64). */
+void qf8o_stats_mx(const void *x, int dtype, const uint8_t *q, const uint8_t *sb, int64_t rows, int64_t cols,
+                   int fmt, double *sums, int64_t *counts)
+{
+    stats_clear(sums, counts);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            int64_t i = r * cols + c;
+            unsigned b = sb[r * (cols / 32) + c / 32];
+            double v = load_elem(x, dtype, i);
+            int sat = isfinite(v) && b != 0xFFu && fabs(v) > ldexp(qf8o_max_finite(fmt), (int)b - 127);
+            stats_add(sums, counts, v, qf8o_dequant_mx_one(fmt, q[i], b), sat);
+        }
 }
