@@ -6,6 +6,8 @@
  *   [HiF8-train]   "HiFloat8：高性能训练之路" (hifloat.gccorg.com blog)
  *   [MP-FP8]       "混合精度与 FP8 训练" (hs-black.github.io, posts/scaling-mixed-precision)
  *   [MXFP8-recipe] "NVIDIA：Blackwell GPU MXFP8 预训练最佳实践" (51cto.com)
+ *   [Ascend950]    Ascend 950 low-precision format guide (hwcomputing.csdn.net), HiF8 vs
+ *                  MXFP8 numerical analysis on DeepSeek-V4-Flash
  *
  * Conventions shared by every entry point
  *   - Tensors are row-major and contiguous: element (r, c) of a [rows][cols] tensor is at
@@ -164,6 +166,53 @@ int quantize_block(const void *x, int dtype, int64_t rows, int64_t cols, int blo
 int quantize_mx_dual(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int rnd,
                      uint8_t *q_row, uint8_t *s_row, uint8_t *q_colT, uint8_t *s_colT,
                      int32_t *nonfinite, void *stream);
+
+/* ---- Dequantization and quantization error statistics -------------------------------------
+ * De-scaling ([MP-FP8 8.1]: the code 22 with S = 22400 gives 22/22400; [MP-FP8 8.2]: the
+ * saturated 448 with S = 22.4 gives 20; [MP-FP8 13.1]: an MX element is a code times 2^X):
+ *   scale factor S (per tensor, delayed step, or group):  xhat = fl32(decode(q) / S);
+ *   MX E8M0 byte b:                    xhat = fl32(decode(q) * 2^(b - 127)), NaN for b = 0xFF.
+ * Output out (nullable): [rows][cols] BF16 (xhat rounded to nearest even) or FP32.
+ * Statistics (nullable; [MP-FP8 7.2] amax / underflow / saturation watch, [Ascend950] SQNR and
+ * zero-rate): the source x (the tensor q was quantized from, same layout as q; for a
+ * columnwise MX result that is x transposed) is read alongside and qf8_error_stats is written
+ * to device memory. Sums are fp64 over the finite elements of x, reduced in a fixed order (the
+ * same input gives the same bits); SQNR = 10 log10(signal / noise), zero-rate = zeroed /
+ * nonzero (or / count). With stats, ws (qf8_workspace_bytes) holds per-workgroup partials.
+ * At least one of out and stats must be given. q, out and x are 16-byte aligned; stats 8-byte.
+ * Sizes: rows * cols < 2^33. */
+typedef enum qf8_out_dtype { QF8_OUT_BF16 = 0, QF8_OUT_FP32 = 1 } qf8_out_dtype;
+
+typedef struct qf8_error_stats {
+    double signal;      /* sum of x^2 over the finite elements of x */
+    double noise;       /* sum of (x - xhat)^2 over the same elements */
+    int64_t count;      /* finite elements of x */
+    int64_t nonzero;    /* finite elements with x != 0 */
+    int64_t zeroed;     /* of those, elements whose xhat is 0 */
+    int64_t saturated;  /* elements whose scaled value exceeded F8max before the saturating cast:
+                           |fl32(x * S)| > F8max, or |x| > F8max * 2^X for MX */
+    int64_t nonfinite;  /* Inf/NaN elements of x, excluded from every other field */
+    int64_t reserved;
+} qf8_error_stats;
+
+/* One scale factor for all n codes (per-tensor current or delayed scaling: pass the scale the
+ * quantization used). scale: one device fp32. */
+int dequantize_scaled(const uint8_t *q, int64_t n, int fmt, const float *scale, void *out, int out_dtype,
+                      const void *x, int x_dtype, qf8_error_stats *stats, void *ws, size_t ws_bytes,
+                      void *stream);
+
+/* Groups of block_rows x block_cols ((1, 128) or (128, 128)) with their fp32 scales
+ * [ceil(rows/block_rows)][ceil(cols/128)] as quantize_block writes them; cols % 4 == 0. */
+int dequantize_block(const uint8_t *q, int64_t rows, int64_t cols, int block_rows, int block_cols, int fmt,
+                     const float *scales, void *out, int out_dtype, const void *x, int x_dtype,
+                     qf8_error_stats *stats, void *ws, size_t ws_bytes, void *stream);
+
+/* MX blocks of 32 along each row of q [rows][cols] with E8M0 bytes s [rows][cols/32]: a rowwise
+ * result, or a columnwise result in its transposed layout (q_colT, s_colT with rows = the
+ * tensor's cols). cols % 32 == 0. */
+int dequantize_mx(const uint8_t *q, const uint8_t *s, int64_t rows, int64_t cols, int fmt, void *out,
+                  int out_dtype, const void *x, int x_dtype, qf8_error_stats *stats, void *ws,
+                  size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -68,6 +68,9 @@ def _load():
         "quantize_delayed": (i32, [vp, i32, i64, i64, ctypes.POINTER(_DelayedStruct), vp, vp, vp, vp, vp, sz, vp]),
         "quantize_block": (i32, [vp, i32, i64, i64, i32, i32, i32, vp, vp, vp, vp, vp]),
         "quantize_mx_dual": (i32, [vp, i32, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp]),
+        "dequantize_scaled": (i32, [vp, i64, i32, vp, vp, i32, vp, i32, vp, vp, sz, vp]),
+        "dequantize_block": (i32, [vp, i64, i64, i32, i32, i32, vp, vp, i32, vp, i32, vp, vp, sz, vp]),
+        "dequantize_mx": (i32, [vp, vp, i64, i64, i32, vp, i32, vp, i32, vp, vp, sz, vp]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(lib, name)
@@ -267,3 +270,85 @@ def quantize_mx_dual(x, fmt, rnd, rowwise=True, colwise=True, q_row=None, s_row=
                                     _ptr(q_colT), _ptr(s_colT), _ptr(nonfinite), _stream(stream, dev)),
            "quantize_mx_dual")
     return q_row, s_row, q_colT, s_colT
+
+
+
+# ---- dequantization and error statistics ------------------------------------------------------
+
+STATS_FIELDS = ("signal", "noise", "count", "nonzero", "zeroed", "saturated", "nonfinite")
+
+
+def stats_to_dict(stats):
+    """Read a qf8_error_stats device tensor (8 x int64) back to the host (synchronizes)."""
+    import numpy as np
+    raw = stats.detach().cpu().numpy().view(np.uint8)
+    f = raw[:16].view(np.float64)
+    i = raw[16:].view(np.int64)
+    return {"signal": float(f[0]), "noise": float(f[1]), "count": int(i[0]), "nonzero": int(i[1]),
+            "zeroed": int(i[2]), "saturated": int(i[3]), "nonfinite": int(i[4])}
+
+
+def _dq_common(q, out_dtype, out, shape, x, want_out, ws, dev):
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    out_code = _BF16 if out_dtype == torch.bfloat16 else _FP32
+    if want_out:
+        out = _out(out, shape, out_dtype, dev, "out")
+    else:
+        out = None
+    stats = None
+    x_code = 0
+    if x is not None:
+        _dev_tensor(x, "x")
+        if tuple(x.shape) != tuple(shape):
+            raise ValueError(f"x must have the shape of q, {tuple(shape)}")
+        x_code = _dtype_code(x)
+        stats = torch.zeros(8, dtype=torch.int64, device=dev)
+        if ws is None:
+            ws = torch.empty(_load().qf8_workspace_bytes(1, 1, 0), dtype=torch.uint8, device=dev)
+        else:
+            _dev_tensor(ws, "ws")
+    if out is None and stats is None:
+        raise ValueError("nothing to do: ask for the output (want_out) or pass x for statistics")
+    return out, out_code, stats, x_code, ws
+
+
+def dequantize_scaled(q, fmt, scale, out_dtype=torch.bfloat16, out=None, x=None, want_out=True, ws=None, stream=None):
+    """xhat = fl32(decode(q) / scale) for a per-tensor (or delayed) result; scale is a 1-element
+    float32 device tensor. With x (the source tensor), also error statistics. Returns
+    (out or None, stats device tensor or None)."""
+    _dev_tensor(q, "q")
+    _dev_tensor(scale, "scale")
+    dev = q.device
+    out, oc, stats, xc, ws = _dq_common(q, out_dtype, out, tuple(q.shape), x, want_out, ws, dev)
+    _check(_load().dequantize_scaled(_ptr(q), q.numel(), fmt, _ptr(scale), _ptr(out), oc, _ptr(x), xc, _ptr(stats),
+                                     _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream, dev)),
+           "dequantize_scaled")
+    return out, stats
+
+
+def dequantize_block(q, block_rows, block_cols, fmt, scales, out_dtype=torch.bfloat16, out=None, x=None,
+                     want_out=True, ws=None, stream=None):
+    """Per-group de-scaling of a quantize_block result (groups of block_rows x block_cols)."""
+    _dev_tensor(q, "q")
+    _dev_tensor(scales, "scales")
+    rows, cols = _rows_cols(q)
+    dev = q.device
+    out, oc, stats, xc, ws = _dq_common(q, out_dtype, out, tuple(q.shape), x, want_out, ws, dev)
+    _check(_load().dequantize_block(_ptr(q), rows, cols, block_rows, block_cols, fmt, _ptr(scales), _ptr(out), oc,
+                                    _ptr(x), xc, _ptr(stats), _ptr(ws), 0 if ws is None else ws.numel(),
+                                    _stream(stream, dev)), "dequantize_block")
+    return out, stats
+
+
+def dequantize_mx(q, s, fmt, out_dtype=torch.bfloat16, out=None, x=None, want_out=True, ws=None, stream=None):
+    """MX de-scaling of q [rows][cols] with E8M0 bytes s [rows][cols/32] (a rowwise result, or a
+    columnwise one in its transposed layout; then x is the source transposed)."""
+    _dev_tensor(q, "q")
+    _dev_tensor(s, "s")
+    rows, cols = _rows_cols(q)
+    dev = q.device
+    out, oc, stats, xc, ws = _dq_common(q, out_dtype, out, tuple(q.shape), x, want_out, ws, dev)
+    _check(_load().dequantize_mx(_ptr(q), _ptr(s), rows, cols, fmt, _ptr(out), oc, _ptr(x), xc, _ptr(stats),
+                                 _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream, dev)), "dequantize_mx")
+    return out, stats

@@ -213,3 +213,65 @@ int quantize_mx_dual(const void *x, int dtype, int64_t rows, int64_t cols, int f
 }
 
 }  // extern "C"
+
+// ---- dequantization and error statistics ---------------------------------------------------
+namespace {
+constexpr int64_t kMaxDequantElems = (int64_t)1 << 33;   // 4-code units stay below 2^31
+
+int check_dequant(const uint8_t *q, int64_t rows, int64_t cols, int fmt, void *out, int out_dtype, const void *x,
+                  int x_dtype, qf8_error_stats *stats, void *ws, size_t ws_bytes) {
+    if (!fmt_ok(fmt)) return QF8_ERR_ENUM;
+    if (out && out_dtype != QF8_OUT_BF16 && out_dtype != QF8_OUT_FP32) return QF8_ERR_ENUM;
+    if (stats && !dtype_ok(x_dtype)) return QF8_ERR_ENUM;
+    if (!dims_ok(rows, cols) || rows * cols >= kMaxDequantElems) return QF8_ERR_SHAPE;
+    if (!out && !stats) return QF8_ERR_NULL;
+    const int64_t n = rows * cols;
+    if (n > 0 && !q) return QF8_ERR_NULL;
+    if (stats && ((n > 0 && !x) || !ws)) return QF8_ERR_NULL;
+    if (stats && ws_bytes < qf8::kWorkspaceBytes) return QF8_ERR_WORKSPACE;
+    if (!aligned(q, 16) || (out && !aligned(out, 16)) || (x && !aligned(x, 16)) || (stats && !aligned(stats, 8)) ||
+        (ws && !aligned(ws, 16)))
+        return QF8_ERR_ALIGN;
+    return QF8_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int dequantize_scaled(const uint8_t *q, int64_t n, int fmt, const float *scale, void *out, int out_dtype,
+                      const void *x, int x_dtype, qf8_error_stats *stats, void *ws, size_t ws_bytes, void *stream) {
+    int c = check_dequant(q, 1, n, fmt, out, out_dtype, x, x_dtype, stats, ws, ws_bytes);
+    if (c != QF8_OK) return c;
+    if (!scale) return QF8_ERR_NULL;
+    if (!aligned(scale, 4)) return QF8_ERR_ALIGN;
+    if (n == 0 && !stats) return QF8_OK;
+    return qf8::launch_dequant(0, fmt, q, 1, n, 1, scale, nullptr, out, out_dtype, x, x_dtype, stats, ws,
+                               as_stream(stream));
+}
+
+int dequantize_block(const uint8_t *q, int64_t rows, int64_t cols, int block_rows, int block_cols, int fmt,
+                     const float *scales, void *out, int out_dtype, const void *x, int x_dtype,
+                     qf8_error_stats *stats, void *ws, size_t ws_bytes, void *stream) {
+    int c = check_dequant(q, rows, cols, fmt, out, out_dtype, x, x_dtype, stats, ws, ws_bytes);
+    if (c != QF8_OK) return c;
+    if (!((block_rows == 1 || block_rows == 128) && block_cols == 128)) return QF8_ERR_SHAPE;
+    if (cols % 4 != 0) return QF8_ERR_SHAPE;
+    if (rows * cols > 0 && !scales) return QF8_ERR_NULL;
+    if (scales && !aligned(scales, 4)) return QF8_ERR_ALIGN;
+    if (rows * cols == 0 && !stats) return QF8_OK;
+    return qf8::launch_dequant(1, fmt, q, rows, cols, block_rows, scales, nullptr, out, out_dtype, x, x_dtype, stats,
+                               ws, as_stream(stream));
+}
+
+int dequantize_mx(const uint8_t *q, const uint8_t *s, int64_t rows, int64_t cols, int fmt, void *out, int out_dtype,
+                  const void *x, int x_dtype, qf8_error_stats *stats, void *ws, size_t ws_bytes, void *stream) {
+    int c = check_dequant(q, rows, cols, fmt, out, out_dtype, x, x_dtype, stats, ws, ws_bytes);
+    if (c != QF8_OK) return c;
+    if (cols % 32 != 0) return QF8_ERR_SHAPE;
+    if (rows * cols > 0 && !s) return QF8_ERR_NULL;
+    if (rows * cols == 0 && !stats) return QF8_OK;
+    return qf8::launch_dequant(2, fmt, q, rows, cols, 1, nullptr, s, out, out_dtype, x, x_dtype, stats, ws,
+                               as_stream(stream));
+}
+
+}  // extern "C"

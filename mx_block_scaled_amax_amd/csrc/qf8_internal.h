@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <hip/hip_runtime.h>
 
+#include "../../include/qf8.h"
+
 namespace qf8 {
 
 // Per-tensor / delayed geometry: number of workgroups of the streaming kernels for n elements.
@@ -58,5 +60,12 @@ int launch_block(const void *x, int dtype, int64_t rows, int64_t cols, int block
 
 int launch_mx(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int rnd, uint8_t *q_row,
               uint8_t *s_row, uint8_t *q_colT, uint8_t *s_colT, int32_t *nonfinite, hipStream_t s);
+
+// De-scaling and error statistics. mode: 0 = one scale factor (scale -> 1 fp32), 1 = groups of
+// block_rows x 128 (scale -> the group scale array), 2 = MX (sb -> E8M0 bytes [rows][cols/32]).
+// out and stats are each optional (not both absent); stats needs x and the workspace.
+int launch_dequant(int mode, int fmt, const uint8_t *q, int64_t rows, int64_t cols, int block_rows,
+                   const float *scale, const uint8_t *sb, void *out, int out_dtype, const void *x, int x_dtype,
+                   qf8_error_stats *stats, void *ws, hipStream_t s);
 
 }  // namespace qf8

@@ -9,10 +9,12 @@ ORACLE_THREADS = min(16, os.cpu_count() or 1)
 
 
 def to_device(x, device="cuda"):
-    """numpy uint16 (BF16 bits) or float32 -> contiguous CUDA tensor holding the same bytes."""
+    """numpy uint16 (BF16 bits), float32 or uint8 -> contiguous CUDA tensor holding the same bytes."""
     if x.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(device)
     if x.dtype == np.float32:
+        return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+    if x.dtype == np.uint8:
         return torch.from_numpy(np.ascontiguousarray(x)).to(device)
     raise TypeError(x.dtype)
 

@@ -111,3 +111,28 @@ def test_workspace_argument_errors():
     fl = ctypes.c_void_p(0x20000)
     f = L.quantize_per_tensor
     assert f(FAKE, 0, 4, 4, 0, FAKE, fl, fl, None, MISALIGNED, need, None) == ALIGN   # ws 16-byte aligned
+
+
+def test_dequant_argument_errors():
+    L = lib()
+    fl = ctypes.c_void_p(0x20000)
+    need = qf8.qf8_workspace_bytes(1, 1)
+    f = L.dequantize_scaled
+    assert f(FAKE, 64, 7, fl, FAKE, 0, None, 0, None, None, 0, None) == ENUM            # fmt
+    assert f(FAKE, 64, 0, fl, FAKE, 5, None, 0, None, None, 0, None) == ENUM            # out dtype
+    assert f(FAKE, 64, 0, fl, None, 0, None, 0, None, None, 0, None) == NULL            # no out, no stats
+    assert f(FAKE, 64, 0, None, FAKE, 0, None, 0, None, None, 0, None) == NULL          # no scale
+    assert f(FAKE, 64, 0, fl, None, 0, None, 0, FAKE, FAKE, need, None) == NULL         # stats without x
+    assert f(FAKE, 64, 0, fl, None, 0, FAKE, 0, FAKE, FAKE, 16, None) == WS             # small workspace
+    assert f(FAKE, 64, 0, fl, None, 0, FAKE, 9, FAKE, FAKE, need, None) == ENUM         # x dtype
+    assert f(MISALIGNED, 64, 0, fl, FAKE, 0, None, 0, None, None, 0, None) == ALIGN
+    assert f(FAKE, -1, 0, fl, FAKE, 0, None, 0, None, None, 0, None) == SHAPE
+    assert f(FAKE, 1 << 33, 0, fl, FAKE, 0, None, 0, None, None, 0, None) == SHAPE
+    assert f(FAKE, 0, 0, fl, FAKE, 0, None, 0, None, None, 0, None) == OK               # empty: nothing to do
+    g = L.dequantize_block
+    assert g(FAKE, 128, 128, 2, 128, 0, fl, FAKE, 0, None, 0, None, None, 0, None) == SHAPE   # block rows
+    assert g(FAKE, 128, 130, 1, 128, 0, fl, FAKE, 0, None, 0, None, None, 0, None) == SHAPE   # cols % 4
+    assert g(FAKE, 128, 128, 1, 128, 0, None, FAKE, 0, None, 0, None, None, 0, None) == NULL  # scales
+    h = L.dequantize_mx
+    assert h(FAKE, FAKE, 64, 48, 0, FAKE, 0, None, 0, None, None, 0, None) == SHAPE      # cols % 32
+    assert h(FAKE, None, 64, 64, 0, FAKE, 0, None, 0, None, None, 0, None) == NULL       # scale bytes
