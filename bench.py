@@ -299,8 +299,8 @@ def run_suite(args):
     import torch
 
     import mx_block_scaled_amax_amd as qf8
-    from synthetic import (block_weight, delayed_base, delayed_sigmas, per_tensor_activation, per_tensor_small,
-                           token_activation)
+    from synthetic import (block_weight, delayed_base, delayed_sigmas, mx_gradient, per_tensor_activation,
+                           per_tensor_small, token_activation)
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     L = qf8._load()
@@ -398,6 +398,29 @@ def run_suite(args):
                      _timed(torch, stream, [PreCall(L.quantize_block, vp(x), 0, xw.shape[0], xw.shape[1], 128, 128, qf8.E4M3,
                                                     vp(qw), vp(sw), None, None, sp) for x in xws], reps, warm)))
     del xws
+
+    # dequantization (and fused error statistics) of the MX dual result and the per-tensor result
+    xg = to_dev(mx_gradient(ROWS, COLS, seed=4))
+    q_row, s_row, q_colT, s_colT = qf8.quantize_mx_dual(xg, qf8.E4M3, qf8.ROUND_DOWN)
+    o16 = torch.empty((ROWS, COLS), dtype=torch.bfloat16, device="cuda")
+    st = torch.zeros(8, dtype=torch.int64, device="cuda")
+    wsg = qf8.workspace(xg)
+    N = ROWS * COLS
+    res.append(_summ("dequant mx rowwise 16384x4096 -> bf16", N + N // 32 + 2 * N,
+                     _timed(torch, stream, [PreCall(L.dequantize_mx, vp(q_row), vp(s_row), ROWS, COLS, qf8.E4M3, vp(o16), 0,
+                                                    None, 0, None, None, 0, sp)], reps, warm)))
+    res.append(_summ("dequant mx rowwise + stats 16384x4096 -> bf16", N + N // 32 + 2 * N + 2 * N,
+                     _timed(torch, stream, [PreCall(L.dequantize_mx, vp(q_row), vp(s_row), ROWS, COLS, qf8.E4M3, vp(o16), 0,
+                                                    vp(xg), 0, vp(st), vp(wsg), wsg.numel(), sp)], reps, warm)))
+    res.append(_summ("stats only, mx rowwise 16384x4096", N + N // 32 + 2 * N,
+                     _timed(torch, stream, [PreCall(L.dequantize_mx, vp(q_row), vp(s_row), ROWS, COLS, qf8.E4M3, None, 0,
+                                                    vp(xg), 0, vp(st), vp(wsg), wsg.numel(), sp)], reps, warm)))
+    del q_row, s_row, q_colT, s_colT
+    qp, amp, scp = qf8.quantize_per_tensor(xg, qf8.E4M3)
+    res.append(_summ("dequant per-tensor 16384x4096 -> bf16", N + 2 * N + 4,
+                     _timed(torch, stream, [PreCall(L.dequantize_scaled, vp(qp), N, qf8.E4M3, vp(scp), vp(o16), 0,
+                                                    None, 0, None, None, 0, sp)], reps, warm)))
+    del xg, o16, qp
     os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
     with open(os.path.join(ROOT, "gpurun_out", "bench_suite.json"), "w") as f:
         json.dump(res, f, indent=1)

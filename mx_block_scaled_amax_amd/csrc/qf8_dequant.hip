@@ -20,13 +20,16 @@
 //   value beyond F8max before the cast: |fl32(x S)| > F8max, or |x| > F8max 2^X for MX) and of
 //   Inf/NaN x (excluded from the rest).
 //
-// Work: a unit is 4 consecutive codes (one dword of q). A thread takes 4 units per iteration
-// (consecutive threads on consecutive units, so each load instruction of a wave covers 256
-// contiguous bytes of q), decodes with the gfx950 fp8/bf8 -> f32 converts (exact), de-scales
-// and stores 4 BF16 (8 bytes) or 4 FP32 (16 bytes) per unit. Group scales and E8M0 bytes are
-// read per unit and hit in cache. With statistics, each workgroup reduces its fp64 sums and
-// counts in a fixed order into a 64-byte partial in the workspace, and one workgroup folds the
-// partials in a fixed order: the same input always gives the same bits.
+// Work: a unit is 16 consecutive codes (one 16-byte load of q; 4 codes when a group's rows are
+// only a multiple of 4 long), always inside one row, one group and one MX block, so its scale
+// is looked up once. A thread takes 2 units per iteration (consecutive threads on consecutive
+// units), decodes with the gfx950 fp8/bf8 -> f32 converts (exact), de-scales (MX: ldexp;
+// groups: IEEE division; one tensor scale: a 256-entry LDS table of decode(c) / S built per
+// workgroup) and stores 16 BF16 (32 bytes) or 16 FP32 (64 bytes). With statistics, the fp64
+// terms go to 4 independent running sums per thread (short dependency chains); each
+// workgroup reduces its sums and counts in a fixed order into a 64-byte partial in the
+// workspace, and one workgroup folds the partials in a fixed order: the same input always gives
+// the same bits.
 #include "qf8_device.h"
 #include "qf8_internal.h"
 #include "../../include/qf8.h"
@@ -35,7 +38,6 @@ namespace qf8 {
 namespace {
 
 constexpr int kDqThreads = 256;
-constexpr int kUnitsPerThread = 4;
 constexpr int kDqMaxGrid = 16384;
 constexpr int kStatsGrid = 1024;                 // workgroups (= 64-byte partials) with statistics
 static_assert(kStatsGrid * 64 <= kMaxStreamGrid * 4, "partials fit the workspace partial region");
@@ -84,32 +86,59 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Running statistics of one thread: the fp64 sums in 4 independent chains (element k of a unit
+// goes to chain k % 4; short dependency chains, fixed order), counts in u32.
 struct Acc {
-    double signal = 0.0, noise = 0.0;
+    double signal[4] = {0.0, 0.0, 0.0, 0.0}, noise[4] = {0.0, 0.0, 0.0, 0.0};
     uint32_t count = 0, nonzero = 0, zeroed = 0, saturated = 0, nonfinite = 0;
-    __device__ __forceinline__ void add(float x, float xh, bool sat) {
-        if (!(fabsf(x) <= 3.40282346638528859812e+38f)) { ++nonfinite; return; }
-        ++count;
-        const double xd = (double)x, d = xd - (double)xh;
-        signal += xd * xd;
-        noise += d * d;
-        if (x != 0.0f) {
-            ++nonzero;
-            if (xh == 0.0f) ++zeroed;
-        }
-        if (sat) ++saturated;
-    }
+    __device__ __forceinline__ double signal_sum() const { return (signal[0] + signal[1]) + (signal[2] + signal[3]); }
+    __device__ __forceinline__ double noise_sum() const { return (noise[0] + noise[1]) + (noise[2] + noise[3]); }
 };
 
-template <int XK>
-__device__ __forceinline__ void load_x4(const void *x, uint32_t u, float *xv) {
+__device__ __forceinline__ bool finite_f32(float x) { return fabsf(x) <= 3.40282346638528859812e+38f; }
+
+template <int W>
+__device__ __forceinline__ void acc_add_unit(Acc &acc, const float *x, const float *xh, const bool *sat) {
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+        const bool fin = finite_f32(x[k]);
+        const double xd = fin ? (double)x[k] : 0.0, d = fin ? xd - (double)xh[k] : 0.0;
+        acc.signal[k & 3] += xd * xd;
+        acc.noise[k & 3] += d * d;
+        acc.nonfinite += fin ? 0u : 1u;
+        acc.count += fin ? 1u : 0u;
+        const bool nz = fin && x[k] != 0.0f;
+        acc.nonzero += nz ? 1u : 0u;
+        acc.zeroed += (nz && xh[k] == 0.0f) ? 1u : 0u;
+        acc.saturated += (fin && sat[k]) ? 1u : 0u;
+    }
+}
+
+// W consecutive elements of x (W = 4 or 16) of unit u.
+template <int XK, int W>
+__device__ __forceinline__ void load_x(const void *x, uint32_t u, float *xv) {
     if constexpr (XK == kBF16) {
-        const uint2 w = ((const uint2 *)x)[u];
-        xv[0] = __uint_as_float(w.x << 16); xv[1] = __uint_as_float(w.x & 0xFFFF0000u);
-        xv[2] = __uint_as_float(w.y << 16); xv[3] = __uint_as_float(w.y & 0xFFFF0000u);
+        const uint32_t *p = (const uint32_t *)x + (size_t)u * (W / 2);
+        uint32_t w[W / 2];
+        if constexpr (W == 16) {
+            const uint4 a0 = ((const uint4 *)p)[0], a1 = ((const uint4 *)p)[1];
+            w[0] = a0.x; w[1] = a0.y; w[2] = a0.z; w[3] = a0.w; w[4] = a1.x; w[5] = a1.y; w[6] = a1.z; w[7] = a1.w;
+        } else {
+            const uint2 a0 = *(const uint2 *)p;
+            w[0] = a0.x; w[1] = a0.y;
+        }
+#pragma unroll
+        for (int k = 0; k < W / 2; ++k) {
+            xv[2 * k] = __uint_as_float(w[k] << 16);
+            xv[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        }
     } else {
-        const float4 w = ((const float4 *)x)[u];
-        xv[0] = w.x; xv[1] = w.y; xv[2] = w.z; xv[3] = w.w;
+        const float4 *p = (const float4 *)x + (size_t)u * (W / 4);
+#pragma unroll
+        for (int k = 0; k < W / 4; ++k) {
+            const float4 f = p[k];
+            xv[4 * k] = f.x; xv[4 * k + 1] = f.y; xv[4 * k + 2] = f.z; xv[4 * k + 3] = f.w;
+        }
     }
 }
 template <int XK>
@@ -118,12 +147,23 @@ __device__ __forceinline__ float load_x1(const void *x, int64_t e) {
     else return ((const float *)x)[e];
 }
 
-template <int OUTK>
-__device__ __forceinline__ void store4(void *out, uint32_t u, const float *v) {
+template <int OUTK, int W>
+__device__ __forceinline__ void store_out(void *out, uint32_t u, const float *v) {
     if constexpr (OUTK == kBF16) {
-        ((uint2 *)out)[u] = make_uint2(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16));
+        uint32_t w[W / 2];
+#pragma unroll
+        for (int k = 0; k < W / 2; ++k) w[k] = bf16_rne(v[2 * k]) | (bf16_rne(v[2 * k + 1]) << 16);
+        uint32_t *p = (uint32_t *)out + (size_t)u * (W / 2);
+        if constexpr (W == 16) {
+            ((uint4 *)p)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            ((uint4 *)p)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        } else {
+            *(uint2 *)p = make_uint2(w[0], w[1]);
+        }
     } else if constexpr (OUTK == kFP32) {
-        ((float4 *)out)[u] = make_float4(v[0], v[1], v[2], v[3]);
+        float4 *p = (float4 *)out + (size_t)u * (W / 4);
+#pragma unroll
+        for (int k = 0; k < W / 4; ++k) p[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
     }
 }
 template <int OUTK>
@@ -139,15 +179,16 @@ struct UnitScale {
     bool nan;     // MX byte 0xFF
 };
 
-template <int FMT, int MODE>
+// Scale of unit u (W codes, all in one row and one group: cols % W == 0, W divides 32 and 128).
+template <int FMT, int MODE, int W>
 __device__ __forceinline__ UnitScale unit_scale(const DqArgs &a, uint32_t u, float s_tensor) {
     UnitScale us{s_tensor, 0, false};
     if constexpr (MODE == kModeBlock) {
-        const uint32_t r = u / a.upr, c = (u - r * a.upr) * 4u;
+        const uint32_t r = u / a.upr, c = (u - r * a.upr) * W;
         us.s = a.scale[(size_t)(r / a.br) * a.gcols + (c >> 7)];
     } else if constexpr (MODE == kModeMx) {
-        const uint32_t r = u / a.upr, c = (u - r * a.upr) * 4u;
-        const uint32_t b = a.sb[(size_t)r * (a.upr >> 3) + (c >> 5)];
+        const uint32_t r = u / a.upr, c = (u - r * a.upr) * W;
+        const uint32_t b = a.sb[(size_t)r * (a.upr * W / 32) + (c >> 5)];
         us.nan = b == 0xFFu;
         us.xexp = (int)b - 127;
         us.s = __builtin_ldexpf(F8<FMT>::kMax, us.xexp);
@@ -178,7 +219,7 @@ __device__ __forceinline__ T wave_sum(T v) {
 __device__ void block_store_partial(const Acc &acc, StatsPart *dst) {
     __shared__ double sd[2][kDqThreads / 64];
     __shared__ uint32_t sc[5][kDqThreads / 64];
-    const double sg = wave_sum(acc.signal), ns = wave_sum(acc.noise);
+    const double sg = wave_sum(acc.signal_sum()), ns = wave_sum(acc.noise_sum());
     const uint32_t c0 = wave_sum(acc.count), c1 = wave_sum(acc.nonzero), c2 = wave_sum(acc.zeroed),
                    c3 = wave_sum(acc.saturated), c4 = wave_sum(acc.nonfinite);
     const int w = threadIdx.x >> 6;
@@ -198,51 +239,78 @@ __device__ void block_store_partial(const Acc &acc, StatsPart *dst) {
     }
 }
 
-template <int FMT, int MODE, int OUTK, int XK>
+// W = 16 (one 16-byte load of codes per unit) or 4 (one dword; groups whose rows are only a
+// multiple of 4 codes long). With one scale factor the workgroup first tabulates
+// fl32(decode(c) / S) for all 256 codes in LDS, so an element costs a table read, not a division.
+template <int FMT, int MODE, int OUTK, int XK, int W>
 __global__ __launch_bounds__(kDqThreads) void dequant_kernel(DqArgs a) {
     constexpr bool STATS = XK != kNone;
-    const float s_tensor = MODE == kModeScaled ? *a.scale : 1.0f;
+    constexpr int UPT = W == 16 ? 2 : 4;        // units per thread and iteration
+    constexpr int ND = W / 4;                     // dwords of codes per unit
+    __shared__ float tab[MODE == kModeScaled ? 256 : 1];
+    float s_tensor = 1.0f;
+    if constexpr (MODE == kModeScaled) {
+        s_tensor = *a.scale;
+        float v[4];
+        decode4<FMT>(threadIdx.x, v);            // 256 threads: code = threadIdx.x
+        tab[threadIdx.x] = v[0] / s_tensor;
+        __syncthreads();
+    }
     Acc acc;
-    const uint32_t *q32 = (const uint32_t *)a.q;
-    const uint32_t stride = gridDim.x * kDqThreads * kUnitsPerThread;
-    for (uint32_t base = blockIdx.x * kDqThreads * kUnitsPerThread; base < a.units; base += stride) {
-        uint32_t codes[kUnitsPerThread];
-        float xv[kUnitsPerThread][4];
+    const uint32_t stride = gridDim.x * kDqThreads * UPT;
+    for (uint32_t base = blockIdx.x * kDqThreads * UPT; base < a.units; base += stride) {
+        uint32_t codes[UPT][ND];
+        float xv[UPT][W];
 #pragma unroll
-        for (int j = 0; j < kUnitsPerThread; ++j) {
+        for (int j = 0; j < UPT; ++j) {
             const uint32_t u = base + j * kDqThreads + threadIdx.x;
-            codes[j] = u < a.units ? __builtin_nontemporal_load(q32 + u) : 0u;
-            if constexpr (STATS) {
-                if (u < a.units) load_x4<XK>(a.x, u, xv[j]);
+            if (u < a.units) {
+                if constexpr (W == 16) {
+                    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+                    const v4u c = __builtin_nontemporal_load((const v4u *)a.q + u);
+                    codes[j][0] = c.x; codes[j][1] = c.y; codes[j][2] = c.z; codes[j][3] = c.w;
+                } else {
+                    codes[j][0] = __builtin_nontemporal_load((const uint32_t *)a.q + u);
+                }
+                if constexpr (STATS) load_x<XK, W>(a.x, u, xv[j]);
             }
         }
 #pragma unroll
-        for (int j = 0; j < kUnitsPerThread; ++j) {
+        for (int j = 0; j < UPT; ++j) {
             const uint32_t u = base + j * kDqThreads + threadIdx.x;
             if (u >= a.units) continue;
-            const UnitScale us = unit_scale<FMT, MODE>(a, u, s_tensor);
-            float v[4];
-            decode4<FMT>(codes[j], v);
+            const UnitScale us = unit_scale<FMT, MODE, W>(a, u, s_tensor);
+            float v[W];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) v[k] = descale<MODE>(v[k], us);
-            store4<OUTK>(a.out, u, v);
+            for (int d = 0; d < ND; ++d) {
+                if constexpr (MODE == kModeScaled) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) v[4 * d + k] = tab[(codes[j][d] >> (8 * k)) & 0xFFu];
+                } else {
+                    decode4<FMT>(codes[j][d], v + 4 * d);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) v[4 * d + k] = descale<MODE>(v[4 * d + k], us);
+                }
+            }
+            store_out<OUTK, W>(a.out, u, v);
             if constexpr (STATS) {
+                bool sat[W];
 #pragma unroll
-                for (int k = 0; k < 4; ++k) acc.add(xv[j][k], v[k], saturates<FMT, MODE>(xv[j][k], us));
+                for (int k = 0; k < W; ++k) sat[k] = saturates<FMT, MODE>(xv[j][k], us);
+                acc_add_unit<W>(acc, xv[j], v, sat);
             }
         }
     }
-    if (MODE == kModeScaled && blockIdx.x == 0) {            // the last n % 4 elements
-        const int64_t e = (int64_t)a.units * 4 + threadIdx.x;
+    if (MODE == kModeScaled && blockIdx.x == 0) {            // the last n % W elements
+        const int64_t e = (int64_t)a.units * W + threadIdx.x;
         if (e < a.n) {
             const UnitScale us{s_tensor, 0, false};
-            float v[4];
-            decode4<FMT>(a.q[e], v);
-            const float xh = descale<MODE>(v[0], us);
+            const float xh = tab[a.q[e]];
             store1<OUTK>(a.out, e, xh);
             if constexpr (STATS) {
-                const float xe = load_x1<XK>(a.x, e);
-                acc.add(xe, xh, saturates<FMT, MODE>(xe, us));
+                float xe[1] = {load_x1<XK>(a.x, e)}, xhv[1] = {xh};
+                bool sat[1] = {saturates<FMT, MODE>(xe[0], us)};
+                acc_add_unit<1>(acc, xe, xhv, sat);
             }
         }
     }
@@ -281,25 +349,28 @@ __global__ __launch_bounds__(kDqThreads) void stats_finalize_kernel(const StatsP
 }
 
 template <int FMT, int MODE, int OUTK, int XK>
-void launch_t(const DqArgs &a, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((dequant_kernel<FMT, MODE, OUTK, XK>), dim3(grid), dim3(kDqThreads), 0, s, a);
+void launch_t(const DqArgs &a, int w, int grid, hipStream_t s) {
+    if (w == 16)
+        hipLaunchKernelGGL((dequant_kernel<FMT, MODE, OUTK, XK, 16>), dim3(grid), dim3(kDqThreads), 0, s, a);
+    else if constexpr (MODE == kModeBlock)
+        hipLaunchKernelGGL((dequant_kernel<FMT, MODE, OUTK, XK, 4>), dim3(grid), dim3(kDqThreads), 0, s, a);
 }
 template <int FMT, int MODE, int OUTK>
-void by_x(int xk, const DqArgs &a, int grid, hipStream_t s) {
-    if (xk == kBF16) launch_t<FMT, MODE, OUTK, kBF16>(a, grid, s);
-    else if (xk == kFP32) launch_t<FMT, MODE, OUTK, kFP32>(a, grid, s);
-    else if constexpr (OUTK != kNone) launch_t<FMT, MODE, OUTK, kNone>(a, grid, s);
+void by_x(int xk, const DqArgs &a, int w, int grid, hipStream_t s) {
+    if (xk == kBF16) launch_t<FMT, MODE, OUTK, kBF16>(a, w, grid, s);
+    else if (xk == kFP32) launch_t<FMT, MODE, OUTK, kFP32>(a, w, grid, s);
+    else if constexpr (OUTK != kNone) launch_t<FMT, MODE, OUTK, kNone>(a, w, grid, s);
 }
 template <int FMT, int MODE>
-void by_out(int outk, int xk, const DqArgs &a, int grid, hipStream_t s) {
-    if (outk == kBF16) by_x<FMT, MODE, kBF16>(xk, a, grid, s);
-    else if (outk == kFP32) by_x<FMT, MODE, kFP32>(xk, a, grid, s);
-    else by_x<FMT, MODE, kNone>(xk, a, grid, s);
+void by_out(int outk, int xk, const DqArgs &a, int w, int grid, hipStream_t s) {
+    if (outk == kBF16) by_x<FMT, MODE, kBF16>(xk, a, w, grid, s);
+    else if (outk == kFP32) by_x<FMT, MODE, kFP32>(xk, a, w, grid, s);
+    else by_x<FMT, MODE, kNone>(xk, a, w, grid, s);
 }
 template <int MODE>
-void by_fmt(int fmt, int outk, int xk, const DqArgs &a, int grid, hipStream_t s) {
-    if (fmt == QF8_E4M3) by_out<kE4M3, MODE>(outk, xk, a, grid, s);
-    else by_out<kE5M2, MODE>(outk, xk, a, grid, s);
+void by_fmt(int fmt, int outk, int xk, const DqArgs &a, int w, int grid, hipStream_t s) {
+    if (fmt == QF8_E4M3) by_out<kE4M3, MODE>(outk, xk, a, w, grid, s);
+    else by_out<kE5M2, MODE>(outk, xk, a, w, grid, s);
 }
 
 }  // namespace
@@ -308,11 +379,13 @@ int launch_dequant(int mode, int fmt, const uint8_t *q, int64_t rows, int64_t co
                    const float *scale, const uint8_t *sb, void *out, int out_dtype, const void *x, int x_dtype,
                    qf8_error_stats *stats, void *ws, hipStream_t s) {
     const int64_t n = rows * cols;
+    // 16-code units wherever every unit stays inside one row (and so one group / MX block)
+    const int w = (mode == kModeScaled || cols % 16 == 0) ? 16 : 4;
     DqArgs a{};
     a.q = q;
     a.n = n;
-    a.units = (uint32_t)(n / 4);
-    a.upr = (uint32_t)(cols / 4);
+    a.units = (uint32_t)(n / w);
+    a.upr = (uint32_t)(cols / w);
     a.br = (uint32_t)(block_rows > 0 ? block_rows : 1);
     a.gcols = (uint32_t)((cols + 127) / 128);
     a.scale = scale;
@@ -322,16 +395,15 @@ int launch_dequant(int mode, int fmt, const uint8_t *q, int64_t rows, int64_t co
     a.parts = stats ? (StatsPart *)((uint32_t *)ws + kPartialsOffsetWords) : nullptr;
     const int outk = out ? (out_dtype == QF8_IN_BF16 ? kBF16 : kFP32) : kNone;
     const int xk = stats ? (x_dtype == QF8_IN_BF16 ? kBF16 : kFP32) : kNone;
-    const int64_t per_wg = (int64_t)kDqThreads * kUnitsPerThread;
+    const int64_t per_wg = (int64_t)kDqThreads * (w == 16 ? 2 : 4);
     int64_t grid = ((int64_t)a.units + per_wg - 1) / per_wg;
     const int cap = stats ? kStatsGrid : kDqMaxGrid;
     if (grid > cap) grid = cap;
     if (grid < 1) grid = 1;
     if (n > 0 || stats) {
-        const int md = mode;
-        if (md == kModeScaled) by_fmt<kModeScaled>(fmt, outk, xk, a, (int)grid, s);
-        else if (md == kModeBlock) by_fmt<kModeBlock>(fmt, outk, xk, a, (int)grid, s);
-        else by_fmt<kModeMx>(fmt, outk, xk, a, (int)grid, s);
+        if (mode == kModeScaled) by_fmt<kModeScaled>(fmt, outk, xk, a, w, (int)grid, s);
+        else if (mode == kModeBlock) by_fmt<kModeBlock>(fmt, outk, xk, a, w, (int)grid, s);
+        else by_fmt<kModeMx>(fmt, outk, xk, a, w, (int)grid, s);
     }
     if (stats)
         hipLaunchKernelGGL(stats_finalize_kernel, dim3(1), dim3(kDqThreads), 0, s, a.parts, (int)grid, stats);
