@@ -109,6 +109,14 @@ def _load():
     lib.qf8o_stats_mx.restype = None
     lib.qf8o_stats_mx.argtypes = [_c_void_p, ctypes.c_int, _c_void_p, _c_void_p, _i64, _i64, ctypes.c_int,
                                   _c_void_p, _c_void_p]
+    lib.qf8o_scale_pow2.restype = ctypes.c_float
+    lib.qf8o_scale_pow2.argtypes = [ctypes.c_int, ctypes.c_double]
+    lib.qf8o_quantize_block_ex.restype = None
+    lib.qf8o_quantize_block_ex.argtypes = [_c_void_p, ctypes.c_int, _i64, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int,
+                                           _c_void_p, _c_void_p, _c_void_p, _c_void_p]
+    lib.qf8o_requant_1x128_to_128x1.restype = None
+    lib.qf8o_requant_1x128_to_128x1.argtypes = [_c_void_p, _c_void_p, _i64, _i64, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_int, _c_void_p, _c_void_p, _c_void_p, _c_void_p]
     _lib = lib
     return lib
 
@@ -345,3 +353,40 @@ def stats_mx(x, q, s, fmt):
     sums, counts = np.zeros(2, np.float64), np.zeros(5, np.int64)
     _load().qf8o_stats_mx(_ptr(x), _dtype_code(x), _ptr(q), _ptr(s), rows, cols, fmt, _ptr(sums), _ptr(counts))
     return _stats_dict(sums, counts)
+
+
+# ---- power-of-two group scales and the 1x128 -> 128x1 re-grouping ----------------------------
+
+def scale_pow2(fmt, a):
+    """Largest power of two S with a * S <= F8max (1 for a = 0 or non-finite)."""
+    return _load().qf8o_scale_pow2(fmt, float(a))
+
+
+def quantize_block_ex(x, br, bc, fmt, pow2):
+    """quantize_block with Eq.(1) scales (pow2 False) or power-of-two scales (pow2 True).
+    Returns (q, scales, amax, nonfinite)."""
+    x = _contig(x)
+    rows, cols = x.shape
+    gr, gc = -(-rows // br), -(-cols // bc)
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((gr, gc), np.float32)
+    a = np.empty((gr, gc), np.float32)
+    nf = np.zeros(1, np.int32)
+    _load().qf8o_quantize_block_ex(_ptr(x), _dtype_code(x), rows, cols, br, bc, fmt, int(bool(pow2)), _ptr(q),
+                                   _ptr(s), _ptr(a), _ptr(nf))
+    return q, s, a, int(nf[0])
+
+
+def requant_1x128_to_128x1(q, scales, fmt_in, fmt_out, pow2_out):
+    """De-scale q [rows][cols] (1x128 groups), transpose, quantize again in 1x128 groups of the
+    transpose. Returns (qT [cols][rows], scalesT [cols][ceil(rows/128)], nonfinite)."""
+    q = np.ascontiguousarray(q, np.uint8)
+    scales = np.ascontiguousarray(scales, np.float32)
+    rows, cols = q.shape
+    tmp = np.empty(rows * cols, np.float32)
+    qT = np.empty((cols, rows), np.uint8)
+    sT = np.empty((cols, -(-rows // 128)), np.float32)
+    nf = np.zeros(1, np.int32)
+    _load().qf8o_requant_1x128_to_128x1(_ptr(q), _ptr(scales), rows, cols, fmt_in, fmt_out, int(bool(pow2_out)),
+                                        _ptr(tmp), _ptr(qT), _ptr(sT), _ptr(nf))
+    return qT, sT, int(nf[0])

@@ -56,7 +56,16 @@
  *      zeroed = #(x != 0 and xhat == 0) (the zero-rate numerator), saturated = #(elements whose
  *      scaled value exceeded F8max before the saturating cast), nonfinite = #(Inf/NaN in x).
  *      Per-element terms are fp64 operations on exact fp64 copies of x and xhat; the sums run in
- *      index order (any other order differs only by fp64 rounding).
+ *      index order (any other order differs only by fp64 rounding);
+ *   R12 a power-of-two group scale ([MP-FP8 10.4]: the tensors that are re-grouped from 1x128 to
+ *      128x1 take integer powers of two as scale factors) is the largest power of two S with
+ *      amax * S <= F8max, i.e. S = 2^-X with X = ceil(log2(amax / F8max)) clamped to
+ *      [-127, 127] (the exponent rule of the MX round-up recipe applied to the group), and 1 for
+ *      amax = 0 or non-finite;
+ *   R13 the 1x128 -> 128x1 re-grouping ([MP-FP8 10.5]: read, dequantize, transpose, quantize
+ *      again in 128x1 groups, write back) de-scales with R9 and quantizes the transposed fp32
+ *      values in 1x128 groups along the rows of the transpose, so the result is stored
+ *      transposed: qT [cols][rows], scalesT [cols][ceil(rows/128)].
  */
 #include <stdint.h>
 #include <stddef.h>
@@ -568,4 +577,55 @@ void qf8o_stats_mx(const void *x, int dtype, const uint8_t *q, const uint8_t *sb
             int sat = isfinite(v) && b != 0xFFu && fabs(v) > ldexp(qf8o_max_finite(fmt), (int)b - 127);
             stats_add(sums, counts, v, qf8o_dequant_mx_one(fmt, q[i], b), sat);
         }
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * Power-of-two group scales (R12) and the 1x128 -> 128x1 re-grouping (R13).
+ * ------------------------------------------------------------------------------------------- */
+float qf8o_scale_pow2(int fmt, double amax)
+{
+    if (!isfinite(amax) || amax == 0.0) return 1.0f;
+    int X = qf8o_mx_exponent(fmt, QF8O_ROUND_UP, amax);   /* smallest X with amax / 2^X <= F8max */
+    return (float)ldexp(1.0, -X);
+}
+
+/* quantize_block with a choice of scale rule: pow2 = 0 gives Eq.(1), pow2 = 1 gives R12. */
+void qf8o_quantize_block_ex(const void *x, int dtype, int64_t rows, int64_t cols, int64_t br, int64_t bc,
+                            int fmt, int pow2, uint8_t *q, float *scales, float *amax_out, int32_t *nonfinite)
+{
+    int64_t gr = (rows + br - 1) / br, gc = (cols + bc - 1) / bc;
+    int bad = 0;
+    for (int64_t bi = 0; bi < gr; ++bi) {
+        for (int64_t bj = 0; bj < gc; ++bj) {
+            int64_t r0 = bi * br, r1 = r0 + br < rows ? r0 + br : rows;
+            int64_t c0 = bj * bc, c1 = c0 + bc < cols ? c0 + bc : cols;
+            amax_acc a;
+            acc_init(&a);
+            for (int64_t r = r0; r < r1; ++r)
+                for (int64_t c = c0; c < c1; ++c) acc_add(&a, load_elem(x, dtype, r * cols + c));
+            double amax = acc_value(&a);
+            float s = pow2 ? qf8o_scale_pow2(fmt, amax) : qf8o_scale_from_amax(fmt, amax);
+            if (!isfinite(amax)) bad = 1;
+            for (int64_t r = r0; r < r1; ++r)
+                for (int64_t c = c0; c < c1; ++c)
+                    q[r * cols + c] = (uint8_t)qf8o_cast_one(fmt, load_elem(x, dtype, r * cols + c), s);
+            if (scales) scales[bi * gc + bj] = s;
+            if (amax_out) amax_out[bi * gc + bj] = (float)amax;
+        }
+    }
+    if (nonfinite) *nonfinite = bad;
+}
+
+/* R13: q [rows][cols] in 1x128 groups with scales [rows][ceil(cols/128)] (format fmt_in) ->
+ * qT [cols][rows] in 1x128 groups of the transpose (128x1 groups of the original) with scalesT
+ * [cols][ceil(rows/128)] (format fmt_out, scale rule pow2_out). tmp: rows*cols floats. */
+void qf8o_requant_1x128_to_128x1(const uint8_t *q, const float *scales, int64_t rows, int64_t cols,
+                                 int fmt_in, int fmt_out, int pow2_out, float *tmp, uint8_t *qT,
+                                 float *scalesT, int32_t *nonfinite)
+{
+    int64_t gc = (cols + 127) / 128;
+    for (int64_t c = 0; c < cols; ++c)                    /* de-scale and transpose */
+        for (int64_t r = 0; r < rows; ++r)
+            tmp[c * rows + r] = qf8o_dequant_one(fmt_in, q[r * cols + c], scales[r * gc + c / 128]);
+    qf8o_quantize_block_ex(tmp, QF8O_FP32, cols, rows, 1, 128, fmt_out, pow2_out, qT, scalesT, NULL, nonfinite);
 }
