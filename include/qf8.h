@@ -152,6 +152,30 @@ int quantize_block(const void *x, int dtype, int64_t rows, int64_t cols, int blo
                    int block_cols, int fmt, uint8_t *q, float *scales, float *amax,
                    int32_t *nonfinite, void *stream);
 
+/* Flags of quantize_block_ex and requantize_1x128_to_128x1. */
+#define QF8_FLAG_POW2_SCALES 1   /* group scales are the largest power of two S with amax*S <= F8max */
+
+/* quantize_block with flags. QF8_FLAG_POW2_SCALES ([MP-FP8 10.4]: the tensors re-grouped from
+ * 1x128 to 128x1 use integer powers of two as scale factors, so the re-grouping adds no error):
+ * S_g = 2^-X, X = ceil(log2(amax_g / F8max)) clamped to [-127, 127]; 1 for amax_g = 0 or
+ * non-finite. Unknown flag bits give QF8_ERR_ENUM. quantize_block is this call with flags 0. */
+int quantize_block_ex(const void *x, int dtype, int64_t rows, int64_t cols, int block_rows,
+                      int block_cols, int fmt, int flags, uint8_t *q, float *scales, float *amax,
+                      int32_t *nonfinite, void *stream);
+
+/* Re-grouping of 1x128 groups into 128x1 groups ([MP-FP8 10.5]: read, de-scale, transpose,
+ * quantize again, write back). Input: q [rows][cols] (fmt_in) with its 1x128 group scales
+ * [rows][ceil(cols/128)] as quantize_block(_ex) writes them. Each value is de-scaled as
+ * dequantize_block does (fl32(decode(q) / S)); every column's groups of 128 rows are quantized
+ * again (fmt_out, Eq.(1) scales or QF8_FLAG_POW2_SCALES) and stored transposed: qT [cols][rows]
+ * with scalesT [cols][ceil(rows/128)], i.e. the 1x128 groups of the transpose. With power-of-two
+ * scales on both sides and fmt_in == fmt_out, every value whose re-scaled magnitude is at least
+ * the smallest normal fp8 value is carried over exactly. rows % 16 == 0, cols % 16 == 0; q, qT
+ * 16-byte aligned. nonfinite (nullable) is set when a group holds Inf/NaN. */
+int requantize_1x128_to_128x1(const uint8_t *q, const float *scales, int64_t rows, int64_t cols,
+                              int fmt_in, int fmt_out, int flags, uint8_t *qT, float *scalesT,
+                              int32_t *nonfinite, void *stream);
+
 /* MX quantization with 1x32 blocks and E8M0 shared scales ([MP-FP8 13.1]; [MXFP8-recipe 4.1]),
  * rowwise and/or columnwise from the same high-precision input in one pass.
  * Per block of 32: amax = 0 gives X = -127 and 32 zero bytes; otherwise X from the rounding

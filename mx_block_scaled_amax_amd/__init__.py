@@ -24,6 +24,7 @@ __all__ = [
 
 E4M3, E5M2 = 0, 1
 ROUND_DOWN, ROUND_UP = 0, 1
+FLAG_POW2_SCALES = 1
 _BF16, _FP32 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -67,6 +68,8 @@ def _load():
         "qf8_delayed_reset": (i32, [ctypes.POINTER(_DelayedStruct), vp]),
         "quantize_delayed": (i32, [vp, i32, i64, i64, ctypes.POINTER(_DelayedStruct), vp, vp, vp, vp, vp, sz, vp]),
         "quantize_block": (i32, [vp, i32, i64, i64, i32, i32, i32, vp, vp, vp, vp, vp]),
+        "quantize_block_ex": (i32, [vp, i32, i64, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
+        "requantize_1x128_to_128x1": (i32, [vp, vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]),
         "quantize_mx_dual": (i32, [vp, i32, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp]),
         "dequantize_scaled": (i32, [vp, i64, i32, vp, vp, i32, vp, i32, vp, vp, sz, vp]),
         "dequantize_block": (i32, [vp, i64, i64, i32, i32, i32, vp, vp, i32, vp, i32, vp, vp, sz, vp]),
@@ -235,8 +238,9 @@ def quantize_delayed(x, state, q=None, scale_used=None, amax_out=None, nonfinite
 
 
 def quantize_block(x, block_rows, block_cols, fmt, q=None, scales=None, amax=None, nonfinite=None, stream=None,
-                   want_amax=True):
-    """1x128 or 128x128 group scaling. Returns (q, scales, amax-or-None)."""
+                   want_amax=True, pow2_scales=False):
+    """1x128 or 128x128 group scaling (power-of-two group scales with pow2_scales).
+    Returns (q, scales, amax-or-None)."""
     _dev_tensor(x, "x")
     rows, cols = _rows_cols(x)
     gshape = (-(-rows // block_rows), -(-cols // block_cols))
@@ -244,10 +248,26 @@ def quantize_block(x, block_rows, block_cols, fmt, q=None, scales=None, amax=Non
     scales = _out(scales, gshape, torch.float32, x.device, "scales")
     if amax is None and want_amax:
         amax = torch.empty(gshape, dtype=torch.float32, device=x.device)
-    _check(_load().quantize_block(_ptr(x), _dtype_code(x), rows, cols, block_rows, block_cols, fmt, _ptr(q),
-                                  _ptr(scales), _ptr(amax), _ptr(nonfinite), _stream(stream, x.device)),
-           "quantize_block")
+    _check(_load().quantize_block_ex(_ptr(x), _dtype_code(x), rows, cols, block_rows, block_cols, fmt,
+                                     FLAG_POW2_SCALES if pow2_scales else 0, _ptr(q), _ptr(scales), _ptr(amax),
+                                     _ptr(nonfinite), _stream(stream, x.device)), "quantize_block_ex")
     return q, scales, amax
+
+
+def requantize_1x128_to_128x1(q, scales, fmt_in, fmt_out, pow2_scales=True, qT=None, scalesT=None, nonfinite=None,
+                              stream=None):
+    """Re-group 1x128-quantized q [rows][cols] (with its group scales) into 128x1 groups, stored
+    transposed. Returns (qT [cols][rows], scalesT [cols][ceil(rows/128)])."""
+    _dev_tensor(q, "q")
+    _dev_tensor(scales, "scales")
+    rows, cols = _rows_cols(q)
+    dev = q.device
+    qT = _out(qT, (cols, rows), torch.uint8, dev, "qT")
+    scalesT = _out(scalesT, (cols, -(-rows // 128)), torch.float32, dev, "scalesT")
+    _check(_load().requantize_1x128_to_128x1(_ptr(q), _ptr(scales), rows, cols, fmt_in, fmt_out,
+                                             FLAG_POW2_SCALES if pow2_scales else 0, _ptr(qT), _ptr(scalesT),
+                                             _ptr(nonfinite), _stream(stream, dev)), "requantize_1x128_to_128x1")
+    return qT, scalesT
 
 
 def quantize_mx_dual(x, fmt, rnd, rowwise=True, colwise=True, q_row=None, s_row=None, q_colT=None, s_colT=None,

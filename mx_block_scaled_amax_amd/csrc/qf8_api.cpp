@@ -178,9 +178,10 @@ int quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, qf8_d
     return r;
 }
 
-int quantize_block(const void *x, int dtype, int64_t rows, int64_t cols, int block_rows, int block_cols, int fmt,
-                   uint8_t *q, float *scales, float *amax, int32_t *nonfinite, void *stream) {
+int quantize_block_ex(const void *x, int dtype, int64_t rows, int64_t cols, int block_rows, int block_cols, int fmt,
+                      int flags, uint8_t *q, float *scales, float *amax, int32_t *nonfinite, void *stream) {
     if (!dtype_ok(dtype) || !fmt_ok(fmt)) return QF8_ERR_ENUM;
+    if (flags & ~QF8_FLAG_POW2_SCALES) return QF8_ERR_ENUM;
     if (!dims_ok(rows, cols)) return QF8_ERR_SHAPE;
     if (!((block_rows == 1 || block_rows == 128) && block_cols == 128)) return QF8_ERR_SHAPE;
     if (cols % (dtype == QF8_IN_BF16 ? 8 : 4) != 0) return QF8_ERR_SHAPE;
@@ -192,7 +193,29 @@ int quantize_block(const void *x, int dtype, int64_t rows, int64_t cols, int blo
     if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scales, 4) || (amax && !aligned(amax, 4)) ||
         (nonfinite && !aligned(nonfinite, 4)))
         return QF8_ERR_ALIGN;
-    return qf8::launch_block(x, dtype, rows, cols, block_rows, fmt, q, scales, amax, nonfinite, as_stream(stream));
+    return qf8::launch_block(x, dtype, rows, cols, block_rows, fmt, flags & QF8_FLAG_POW2_SCALES, q, scales, amax,
+                             nonfinite, as_stream(stream));
+}
+
+int quantize_block(const void *x, int dtype, int64_t rows, int64_t cols, int block_rows, int block_cols, int fmt,
+                   uint8_t *q, float *scales, float *amax, int32_t *nonfinite, void *stream) {
+    return quantize_block_ex(x, dtype, rows, cols, block_rows, block_cols, fmt, 0, q, scales, amax, nonfinite, stream);
+}
+
+int requantize_1x128_to_128x1(const uint8_t *q, const float *scales, int64_t rows, int64_t cols, int fmt_in,
+                              int fmt_out, int flags, uint8_t *qT, float *scalesT, int32_t *nonfinite, void *stream) {
+    if (!fmt_ok(fmt_in) || !fmt_ok(fmt_out)) return QF8_ERR_ENUM;
+    if (flags & ~QF8_FLAG_POW2_SCALES) return QF8_ERR_ENUM;
+    if (!dims_ok(rows, cols) || rows % 16 != 0 || cols % 16 != 0) return QF8_ERR_SHAPE;
+    if (rows > INT32_MAX || cols > INT32_MAX || ((rows + 127) / 128) * ((cols + 127) / 128) > INT32_MAX)
+        return QF8_ERR_SHAPE;
+    if (rows * cols == 0) return QF8_OK;
+    if (!q || !scales || !qT || !scalesT) return QF8_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(qT, 16) || !aligned(scales, 4) || !aligned(scalesT, 4) ||
+        (nonfinite && !aligned(nonfinite, 4)))
+        return QF8_ERR_ALIGN;
+    return qf8::launch_requant_t(q, scales, rows, cols, fmt_in, fmt_out, flags & QF8_FLAG_POW2_SCALES, qT, scalesT,
+                                 nonfinite, as_stream(stream));
 }
 
 int quantize_mx_dual(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int rnd, uint8_t *q_row,

@@ -5,6 +5,8 @@
 //            1x128 group of one token, weights per 128x128 block), 10.3 (online quantization:
 //            every group computes its own amax), 8.1 (S = F8max/amax, saturating cast).
 //
+// Scale rule: Eq.(1) S_g = F8max / amax_g, or (power-of-two option, [MP-FP8 10.4]) the largest
+// power of two S_g with amax_g * S_g <= F8max.
 // Both kernels are one HBM pass: load the group into registers, reduce its |x| maximum, derive
 // S_g with one IEEE division, cast from the registers. Loads and stores are non-temporal.
 //   1x128: a group of 128 BF16 is 16 lanes x 8 values, i.e. one DPP row, so the maximum is four
@@ -40,7 +42,13 @@ __device__ __forceinline__ void store_cast(uint8_t *q, int64_t off, uint4 v, flo
     else st_stream((uint32_t *)(q + off), cast4_f32<FMT>(v, s));
 }
 
-template <bool BF16, int FMT>
+template <int FMT, bool POW2>
+__device__ __forceinline__ float group_scale(uint32_t m) {
+    if constexpr (POW2) return scale_pow2_from_amax_bits<FMT>(m);
+    else return scale_from_amax_bits<FMT>(m);
+}
+
+template <bool BF16, int FMT, bool POW2>
 __global__ __launch_bounds__(kThreads) void block_1x128_kernel(const uint16_t *__restrict__ x16, int64_t cols,
                                                                int64_t gcols, int64_t ngroups, uint8_t *__restrict__ q,
                                                                float *__restrict__ scales, float *__restrict__ amax,
@@ -68,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void block_1x128_kernel(const uint16_t *_
         uint32_t m = vec_absmax_bits<BF16>(v[it]);
         m = max_row16(m);
         if constexpr (!BF16) m = umax(m, (uint32_t)__shfl_xor((int)m, 16));
-        const float s = scale_from_amax_bits<FMT>(m);
+        const float s = group_scale<FMT, POW2>(m);
         if (ok[it]) {
             store_cast<BF16, FMT>(q, off[it], v[it], s);
             if (sub == 0) {
@@ -80,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void block_1x128_kernel(const uint16_t *_
     }
 }
 
-template <bool BF16, int FMT>
+template <bool BF16, int FMT, bool POW2>
 __global__ __launch_bounds__(kThreads) void block_128x128_kernel(const uint16_t *__restrict__ x16, int64_t rows,
                                                                  int64_t cols, int64_t gcols, uint8_t *__restrict__ q,
                                                                  float *__restrict__ scales, float *__restrict__ amax,
@@ -108,7 +116,7 @@ __global__ __launch_bounds__(kThreads) void block_128x128_kernel(const uint16_t 
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
     m = umax(umax(red[0], red[1]), umax(red[2], red[3]));
-    const float s = scale_from_amax_bits<FMT>(m);
+    const float s = group_scale<FMT, POW2>(m);
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
         const int64_t r = bi * 128 + p * RPP + rr;
@@ -123,29 +131,32 @@ __global__ __launch_bounds__(kThreads) void block_128x128_kernel(const uint16_t 
 
 }  // namespace
 
-int launch_block(const void *x, int dtype, int64_t rows, int64_t cols, int block_rows, int fmt, uint8_t *q,
+int launch_block(const void *x, int dtype, int64_t rows, int64_t cols, int block_rows, int fmt, int pow2, uint8_t *q,
                  float *scales, float *amax, int32_t *nonfinite, hipStream_t s) {
     const int64_t gcols = (cols + 127) / 128;
     const uint16_t *x16 = (const uint16_t *)x;
     if (rows == 0 || cols == 0) return QF8_OK;
+    const bool bf = dtype == QF8_IN_BF16, e4 = fmt == QF8_E4M3;
     if (block_rows == 1) {
         const int64_t ngroups = rows * gcols;
-        const int gpb = (dtype == QF8_IN_BF16 ? 16 : 8) * 4;
-        const int64_t grid = (ngroups + gpb - 1) / gpb;
-#define QF8_LAUNCH_1x128(BF, F)                                                                                    \
-        hipLaunchKernelGGL((block_1x128_kernel<BF, F>), dim3((unsigned)grid), dim3(kThreads), 0, s, x16, cols, gcols, \
-                           ngroups, q, scales, amax, nonfinite)
-        if (dtype == QF8_IN_BF16) { if (fmt == QF8_E4M3) QF8_LAUNCH_1x128(true, kE4M3); else QF8_LAUNCH_1x128(true, kE5M2); }
-        else { if (fmt == QF8_E4M3) QF8_LAUNCH_1x128(false, kE4M3); else QF8_LAUNCH_1x128(false, kE5M2); }
-#undef QF8_LAUNCH_1x128
+        const int gpb = (bf ? 16 : 8) * 4;
+        const dim3 grid((unsigned)((ngroups + gpb - 1) / gpb));
+#define QF8_L1(BF, F, P) hipLaunchKernelGGL((block_1x128_kernel<BF, F, P>), grid, dim3(kThreads), 0, s, x16, cols, gcols, \
+                                            ngroups, q, scales, amax, nonfinite)
+#define QF8_L1P(BF, F) do { if (pow2) QF8_L1(BF, F, true); else QF8_L1(BF, F, false); } while (0)
+        if (bf) { if (e4) QF8_L1P(true, kE4M3); else QF8_L1P(true, kE5M2); }
+        else { if (e4) QF8_L1P(false, kE4M3); else QF8_L1P(false, kE5M2); }
+#undef QF8_L1P
+#undef QF8_L1
     } else {
-        const int64_t grid = ((rows + 127) / 128) * gcols;
-#define QF8_LAUNCH_128(BF, F)                                                                                      \
-        hipLaunchKernelGGL((block_128x128_kernel<BF, F>), dim3((unsigned)grid), dim3(kThreads), 0, s, x16, rows, cols, \
-                           gcols, q, scales, amax, nonfinite)
-        if (dtype == QF8_IN_BF16) { if (fmt == QF8_E4M3) QF8_LAUNCH_128(true, kE4M3); else QF8_LAUNCH_128(true, kE5M2); }
-        else { if (fmt == QF8_E4M3) QF8_LAUNCH_128(false, kE4M3); else QF8_LAUNCH_128(false, kE5M2); }
-#undef QF8_LAUNCH_128
+        const dim3 grid((unsigned)(((rows + 127) / 128) * gcols));
+#define QF8_L128(BF, F, P) hipLaunchKernelGGL((block_128x128_kernel<BF, F, P>), grid, dim3(kThreads), 0, s, x16, rows, \
+                                              cols, gcols, q, scales, amax, nonfinite)
+#define QF8_L128P(BF, F) do { if (pow2) QF8_L128(BF, F, true); else QF8_L128(BF, F, false); } while (0)
+        if (bf) { if (e4) QF8_L128P(true, kE4M3); else QF8_L128P(true, kE5M2); }
+        else { if (e4) QF8_L128P(false, kE4M3); else QF8_L128P(false, kE5M2); }
+#undef QF8_L128P
+#undef QF8_L128
     }
     return hipGetLastError() == hipSuccess ? QF8_OK : QF8_ERR_HIP;
 }

@@ -175,6 +175,17 @@ __device__ __forceinline__ uint32_t mx_byte_f32(uint32_t a) {
     const uint32_t b = __builtin_elementwise_sub_sat(e, (uint32_t)F8<FMT>::kEmax);
     return a >= 0x7F800000u ? 255u : b;
 }
+// Power-of-two group scale from the |amax| fp32 bit pattern: the largest power of two S with
+// amax * S <= F8max, i.e. S = 2^-X with X the round-up MX exponent of the group (byte = X + 127
+// is at most 247 for finite amax, so S = 2^(127 - byte) is a normal fp32 value with exponent
+// field 254 - byte). amax = 0 or non-finite gives 1, like the Eq.(1) scale.
+template <int FMT>
+__device__ __forceinline__ float scale_pow2_from_amax_bits(uint32_t abits) {
+    if (abits == 0u || abits >= 0x7F800000u) return 1.0f;
+    const uint32_t byte = mx_byte_f32<FMT, kRoundUp>(abits);
+    return __uint_as_float((254u - byte) << 23);
+}
+
 // Saturation of the round-down MX cast, applied to four packed codes after the scaled convert
 // (which does not saturate). With the round-down exponent every |x| / 2^X is below 2^(emax+1),
 // so a value can only overflow into (F8max, 2^(emax+1)); the convert then returns the overflow

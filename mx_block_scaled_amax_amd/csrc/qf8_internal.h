@@ -55,8 +55,13 @@ int launch_delayed_finalize(uint32_t *slots, const uint32_t *partials, int npart
                             int32_t *nonfinite, hipStream_t s);
 int launch_fill_u32(uint32_t *p, int64_t n, uint32_t value, hipStream_t s);
 
-int launch_block(const void *x, int dtype, int64_t rows, int64_t cols, int block_rows, int fmt, uint8_t *q,
+int launch_block(const void *x, int dtype, int64_t rows, int64_t cols, int block_rows, int fmt, int pow2, uint8_t *q,
                  float *scales, float *amax, int32_t *nonfinite, hipStream_t s);
+
+// 1x128 groups of q [rows][cols] -> 1x128 groups of the transpose, stored qT [cols][rows] with
+// scalesT [cols][ceil(rows/128)]; rows % 16 == 0 and cols % 16 == 0.
+int launch_requant_t(const uint8_t *q, const float *scales, int64_t rows, int64_t cols, int fmt_in, int fmt_out,
+                     int pow2, uint8_t *qT, float *scalesT, int32_t *nonfinite, hipStream_t s);
 
 int launch_mx(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int rnd, uint8_t *q_row,
               uint8_t *s_row, uint8_t *q_colT, uint8_t *s_colT, int32_t *nonfinite, hipStream_t s);

@@ -136,3 +136,17 @@ def test_dequant_argument_errors():
     h = L.dequantize_mx
     assert h(FAKE, FAKE, 64, 48, 0, FAKE, 0, None, 0, None, None, 0, None) == SHAPE      # cols % 32
     assert h(FAKE, None, 64, 64, 0, FAKE, 0, None, 0, None, None, 0, None) == NULL       # scale bytes
+
+
+def test_block_ex_and_requant_argument_errors():
+    L = lib()
+    f = L.quantize_block_ex
+    assert f(FAKE, 0, 128, 128, 1, 128, 0, 2, FAKE, FAKE, None, None, None) == ENUM       # unknown flag
+    assert f(FAKE, 0, 128, 128, 1, 64, 0, 1, FAKE, FAKE, None, None, None) == SHAPE
+    g = L.requantize_1x128_to_128x1
+    assert g(FAKE, FAKE, 128, 128, 0, 3, 1, FAKE, FAKE, None, None) == ENUM               # fmt_out
+    assert g(FAKE, FAKE, 128, 120, 0, 0, 1, FAKE, FAKE, None, None) == SHAPE              # cols % 16
+    assert g(FAKE, FAKE, 136, 128, 0, 0, 1, FAKE, FAKE, None, None) == SHAPE              # rows % 16
+    assert g(FAKE, FAKE, 128, 128, 0, 0, 1, FAKE, None, None, None) == NULL               # scalesT
+    assert g(FAKE, FAKE, 0, 128, 0, 0, 1, None, None, None, None) == OK                   # empty
+    assert g(MISALIGNED, FAKE, 128, 128, 0, 0, 1, FAKE, FAKE, None, None) == ALIGN
