@@ -399,6 +399,25 @@ def run_suite(args):
                                                     vp(qw), vp(sw), None, None, sp) for x in xws], reps, warm)))
     del xws
 
+    # power-of-two 1x128 groups and the 1x128 -> 128x1 transposed re-grouping, 8192x7168 E4M3
+    xa = token_activation()
+    xads = [to_dev(xa) for _ in range(4)]
+    na = xa.size
+    gsz = xa.shape[0] * (xa.shape[1] // 128)
+    qa2 = torch.empty(xa.shape, dtype=torch.uint8, device="cuda")
+    sa2 = torch.empty((xa.shape[0], xa.shape[1] // 128), dtype=torch.float32, device="cuda")
+    res.append(_summ("block 1x128 pow2 scales 8192x7168 e4m3", 3 * na + 4 * gsz,
+                     _timed(torch, stream, [PreCall(L.quantize_block_ex, vp(x), 0, xa.shape[0], xa.shape[1], 1, 128,
+                                                    qf8.E4M3, qf8.FLAG_POW2_SCALES, vp(qa2), vp(sa2), None, None, sp)
+                                            for x in xads], reps, warm)))
+    qT2 = torch.empty((xa.shape[1], xa.shape[0]), dtype=torch.uint8, device="cuda")
+    sT2 = torch.empty((xa.shape[1], xa.shape[0] // 128), dtype=torch.float32, device="cuda")
+    res.append(_summ("requant 1x128 -> 128x1 transposed 8192x7168 e4m3 pow2", na + 4 * gsz + na + 4 * (na // 128),
+                     _timed(torch, stream, [PreCall(L.requantize_1x128_to_128x1, vp(qa2), vp(sa2), xa.shape[0], xa.shape[1],
+                                                    qf8.E4M3, qf8.E4M3, qf8.FLAG_POW2_SCALES, vp(qT2), vp(sT2), None, sp)],
+                            reps, warm)))
+    del xads, qa2, qT2
+
     # dequantization (and fused error statistics) of the MX dual result and the per-tensor result
     xg = to_dev(mx_gradient(ROWS, COLS, seed=4))
     q_row, s_row, q_colT, s_colT = qf8.quantize_mx_dual(xg, qf8.E4M3, qf8.ROUND_DOWN)

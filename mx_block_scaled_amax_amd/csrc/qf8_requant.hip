@@ -12,12 +12,15 @@
 // power-of-two rule), qT[c][r] = sat_rne8(fl32(v * S')), scalesT[c][g] = S'. The result holds
 // the transpose in 1x128 groups, ready for a GEMM that reduces over the rows of the input.
 //
-// Work: one workgroup of 256 threads per 128 x 128 tile. The tile's codes (16 KiB) and its 128
-// row scales go to LDS with 16-byte loads; thread t then owns column t % 128 and 64 of its rows:
-// it de-scales them in registers, the two halves of a column exchange their maxima through LDS,
-// and the new codes are written, transposed, into a second 16 KiB LDS tile (16-byte chunks
-// permuted by column so the writes spread over the banks). The workgroup stores each column's
-// 128 new codes as one 128-byte line of qT.
+// Work: one workgroup of 512 threads per 128 x 128 tile. The tile's codes (16 KiB) and its 128
+// row scales go to LDS with 16-byte loads; each thread then owns 4 columns x 8 rows (one dword
+// of codes per row, two values per convert instruction) and de-scales them in registers. When a
+// row's scale is a power of two (the rule the pages use for these tensors) the division is the
+// multiplication by its exact reciprocal (the same correctly rounded quotient); the branch is
+// taken alike by the 32 lanes that share a row. Column maxima meet through a lane exchange and LDS; the new codes of a
+// column's 8 rows go as 8 bytes into a second 16 KiB LDS tile, transposed (16-byte chunks
+// permuted by column so the writes spread over the banks), and the workgroup stores each
+// column's 128 new codes as one 128-byte line of qT.
 #include "qf8_device.h"
 #include "qf8_internal.h"
 #include "../../include/qf8.h"
@@ -25,16 +28,33 @@
 namespace qf8 {
 namespace {
 
-constexpr int kRqThreads = 256;
 constexpr int kTile = 128;
+constexpr int kRqThreads = 512;          // thread = 4 columns x 8 rows of the tile
+constexpr int kWaves = kRqThreads / 64;
 
 __device__ __forceinline__ int ot_offset(int c, int k) { return c * kTile + ((k ^ ((c >> 3) & 7)) << 4); }
 
 template <int FMT>
-__device__ __forceinline__ float decode1(uint32_t code) {
+__device__ __forceinline__ void decode4(uint32_t w, float *d) {
     typedef float v2f __attribute__((ext_vector_type(2)));
-    const v2f d = FMT == kE4M3 ? __builtin_amdgcn_cvt_pk_f32_fp8(code, false) : __builtin_amdgcn_cvt_pk_f32_bf8(code, false);
-    return d.x;
+    v2f lo, hi;
+    if constexpr (FMT == kE4M3) {
+        lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+        hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+    } else {
+        lo = __builtin_amdgcn_cvt_pk_f32_bf8(w, false);
+        hi = __builtin_amdgcn_cvt_pk_f32_bf8(w, true);
+    }
+    d[0] = lo.x; d[1] = lo.y; d[2] = hi.x; d[3] = hi.y;
+}
+
+// 1/S exactly when S is a power of two whose reciprocal is a normal fp32 value (then x / S and
+// x * (1/S) are the same correctly rounded quotient), else 0.
+__device__ __forceinline__ float exact_reciprocal(float s) {
+    const uint32_t u = __float_as_uint(s);
+    const uint32_t e = (u >> 23) & 0xFFu;
+    if ((u & 0x807FFFFFu) != 0u || e < 1u || e > 253u) return 0.0f;
+    return __uint_as_float((254u - e) << 23);
 }
 
 template <int FIN, int FOUT, bool POW2>
@@ -44,8 +64,8 @@ __global__ __launch_bounds__(kRqThreads) void requant_t_kernel(const uint8_t *__
                                                                float *__restrict__ scalesT, int32_t *nonfinite) {
     __shared__ __attribute__((aligned(16))) uint8_t qs[kTile * kTile];     // [row][col]
     __shared__ __attribute__((aligned(16))) uint8_t ot[kTile * kTile];     // [col][row], chunks permuted
-    __shared__ float srow[kTile];
-    __shared__ uint32_t half_max[2][kTile];
+    __shared__ float srow[kTile], srec[kTile], scol[kTile];
+    __shared__ uint32_t part[kWaves][kTile];
     const int tr = blockIdx.x / tiles_c, tc = blockIdx.x - tr * tiles_c;
     const int64_t r0 = (int64_t)tr * kTile, c0 = (int64_t)tc * kTile;
     const int nr = rows - r0 < kTile ? (int)(rows - r0) : kTile;          // multiples of 16
@@ -55,52 +75,75 @@ __global__ __launch_bounds__(kRqThreads) void requant_t_kernel(const uint8_t *__
 
     // codes and row scales of the tile into LDS
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kTile * kTile / 16 / kRqThreads; ++j) {
         const int k = t + j * kRqThreads, row = k >> 3, ch = k & 7;
         uint4 v = make_uint4(0, 0, 0, 0);
         if (row < nr && ch * 16 < nc) v = *(const uint4 *)(q + (r0 + row) * cols + c0 + ch * 16);
         *(uint4 *)(qs + row * kTile + ch * 16) = v;
     }
-    if (t < kTile) srow[t] = t < nr ? scales[(r0 + t) * gcols + tc] : 1.0f;
-    __syncthreads();
-
-    // column cl, rows 64h .. 64h+63: de-scale, column maximum
-    const int cl = t & (kTile - 1), h = t >> 7;
-    float v[64];
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 64; ++i) {
-        const int row = 64 * h + i;
-        v[i] = decode1<FIN>(qs[row * kTile + cl]) / srow[row];
-        if (row < nr) m = umax(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+    if (t < kTile) {
+        const float sr = t < nr ? scales[(r0 + t) * gcols + tc] : 1.0f;
+        srow[t] = sr;
+        srec[t] = exact_reciprocal(sr);
     }
-    half_max[h][cl] = m;
     __syncthreads();
-    m = umax(half_max[0][cl], half_max[1][cl]);
-    const float s = POW2 ? scale_pow2_from_amax_bits<FOUT>(m) : scale_from_amax_bits<FOUT>(m);
 
-    // the column's new codes, transposed into the output tile
+    // columns 4cg .. 4cg+3, rows 8rg .. 8rg+7: de-scale (v = fl32(decode / S_row)), column maxima
+    const int cg = t & 31, rg = t >> 5, wave = t >> 6;
+    float v[8][4];
+    uint32_t m[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        uint32_t w[4];
+    for (int i = 0; i < 8; ++i) {
+        const int row = 8 * rg + i;
+        decode4<FIN>(((const uint32_t *)qs)[row * (kTile / 4) + cg], v[i]);
+        const float rec = srec[row];                     // the same for the 32 lanes of this row
+        if (rec != 0.0f) {
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            uint32_t b = 0;
+            for (int j = 0; j < 4; ++j) v[i][j] *= rec;
+        } else {
+            const float sr = srow[row];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) b |= cast1<FOUT>(v[16 * k + 4 * d + e], s) << (8 * e);
-            w[d] = b;
+            for (int j = 0; j < 4; ++j) v[i][j] = v[i][j] / sr;
         }
-        *(uint4 *)(ot + ot_offset(cl, 4 * h + k)) = make_uint4(w[0], w[1], w[2], w[3]);
+        if (row < nr) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) m[j] = umax(m[j], __float_as_uint(v[i][j]) & 0x7FFFFFFFu);
+        }
     }
-    if (h == 0 && cl < nc) {
-        scalesT[(c0 + cl) * ((rows + 127) / 128) + tr] = s;
-        if (nonfinite && m >= 0x7F800000u) *nonfinite = 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m[j] = umax(m[j], (uint32_t)__shfl_xor((int)m[j], 32));   // the wave's 16 rows
+    if ((t & 63) < 32) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) part[wave][4 * cg + j] = m[j];
+    }
+    __syncthreads();
+    if (t < kTile) {                                     // column t: maximum over the 8 waves, new scale
+        uint32_t mc = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) mc = umax(mc, part[w][t]);
+        const float sc = POW2 ? scale_pow2_from_amax_bits<FOUT>(mc) : scale_from_amax_bits<FOUT>(mc);
+        scol[t] = sc;
+        if (t < nc) {
+            scalesT[(c0 + t) * ((rows + 127) / 128) + tr] = sc;
+            if (nonfinite && mc >= 0x7F800000u) *nonfinite = 1;
+        }
+    }
+    __syncthreads();
+
+    // new codes: for each column, its 8 rows as 8 bytes of the transposed output tile
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int col = 4 * cg + j;
+        const float sc = scol[col];
+        const uint32_t lo = cast4<FOUT>(v[0][j], v[1][j], v[2][j], v[3][j], sc);
+        const uint32_t hi = cast4<FOUT>(v[4][j], v[5][j], v[6][j], v[7][j], sc);
+        *(uint2 *)(ot + ot_offset(col, rg >> 1) + (rg & 1) * 8) = make_uint2(lo, hi);
     }
     __syncthreads();
 
     // each column's 128 codes: one line of qT
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kTile * kTile / 16 / kRqThreads; ++j) {
         const int k = t + j * kRqThreads, col = k >> 3, ch = k & 7;
         if (col < nc && ch * 16 < nr)
             *(uint4 *)(qT + (c0 + col) * rows + r0 + ch * 16) = *(const uint4 *)(ot + ot_offset(col, ch));
