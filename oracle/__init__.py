@@ -17,6 +17,7 @@ import numpy as np
 
 E4M3, E5M2, E8M0 = 0, 1, 2
 ROUND_DOWN, ROUND_UP = 0, 1
+EST_MAX, EST_RECENT, EST_MEAN = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "qf8_oracle.c")
@@ -76,6 +77,8 @@ def _load():
     lib.qf8o_delayed_step.restype = None
     lib.qf8o_delayed_step.argtypes = [_c_void_p, _c_void_p, ctypes.c_int, _i64, _i64,
                                       _c_void_p, _c_void_p, _c_void_p, _c_void_p]
+    lib.qf8o_delayed_set_estimator.restype = ctypes.c_int
+    lib.qf8o_delayed_set_estimator.argtypes = [_c_void_p, ctypes.c_int]
     lib.qf8o_delayed_get.restype = None
     lib.qf8o_delayed_get.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p]
     lib.qf8o_quantize_block.restype = None
@@ -200,11 +203,14 @@ def quantize_per_tensor(x, fmt):
 class Delayed:
     """Delayed-scaling state machine (amax history FIFO, Interval, 2^-N margin)."""
 
-    def __init__(self, hist_len, interval, n_guard, fmt):
+    def __init__(self, hist_len, interval, n_guard, fmt, estimator=0):
+        """estimator: 0 max of the history, 1 most recent entry, 2 mean (R14)."""
         lib = _load()
         self._buf = np.zeros(lib.qf8o_delayed_sizeof(), np.uint8)
         if lib.qf8o_delayed_init(_ptr(self._buf), hist_len, interval, n_guard, fmt) != 0:
             raise ValueError("bad delayed-scaling configuration")
+        if lib.qf8o_delayed_set_estimator(_ptr(self._buf), estimator) != 0:
+            raise ValueError("bad estimator")
         self.hist_len = hist_len
         self.fmt = fmt
 

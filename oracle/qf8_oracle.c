@@ -62,6 +62,10 @@
  *      amax * S <= F8max, i.e. S = 2^-X with X = ceil(log2(amax / F8max)) clamped to
  *      [-127, 127] (the exponent rule of the MX round-up recipe applied to the group), and 1 for
  *      amax = 0 or non-finite;
+ *   R14 delayed-scaling estimators ([HiF8-train 1.2] names the maximum of the history and, as
+ *      other rules, the most recent entry and the mean): max; the newest entry; the mean as the
+ *      fp32 sum of the entries from oldest to newest (each addition rounded to fp32) divided by
+ *      the count in fp32. An empty history estimates 0 under every rule;
  *   R13 the 1x128 -> 128x1 re-grouping ([MP-FP8 10.5]: read, dequantize, transpose, quantize
  *      again in 128x1 groups, write back) de-scales with R9 and quantizes the transposed fp32
  *      values in 1x128 groups along the rows of the transpose, so the result is stored
@@ -256,6 +260,7 @@ typedef struct {
     int32_t hist_len, interval, n_guard, fmt;
     int32_t count, head;        /* head = slot of the oldest entry */
     int64_t step;
+    int32_t estimator;          /* R14: 0 max, 1 most recent, 2 mean */
     float hist[QF8O_MAX_HIST];
 } qf8o_delayed;
 
@@ -291,12 +296,29 @@ static void delayed_push(qf8o_delayed *st, float v)
     }
 }
 
+/* The amax estimate from the history ([HiF8-train 1.2]: the maximum of the buffer, or another
+ * rule such as the most recent entry or the mean; R14). */
 float qf8o_delayed_estimate(const qf8o_delayed *st)
 {
-    float e = 0.0f;                                    /* R7: empty history counts as 0 */
+    if (st->count == 0) return 0.0f;                   /* R7: empty history counts as 0 */
+    if (st->estimator == 1)                            /* the newest entry */
+        return st->hist[(st->head + st->count - 1) % st->hist_len];
+    if (st->estimator == 2) {                          /* fp32 sum, oldest to newest, / count */
+        float sum = 0.0f;
+        for (int i = 0; i < st->count; ++i) sum = sum + st->hist[(st->head + i) % st->hist_len];
+        return sum / (float)st->count;
+    }
+    float e = 0.0f;
     for (int i = 0; i < st->count; ++i)
         if (st->hist[(st->head + i) % st->hist_len] > e) e = st->hist[(st->head + i) % st->hist_len];
     return e;
+}
+
+int qf8o_delayed_set_estimator(qf8o_delayed *st, int estimator)
+{
+    if (estimator < 0 || estimator > 2) return -1;
+    st->estimator = estimator;
+    return 0;
 }
 
 /* The scale a step uses, from the state before the step. */
