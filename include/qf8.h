@@ -106,7 +106,8 @@ int quantize_per_tensor(const void *x, int dtype, int64_t rows, int64_t cols, in
  * Step 0 after init or reset has no history and runs current scaling (no margin). Every step
  * t >= 1 casts with the scale the history gave before the step; when t % interval == 0 (and
  * at step 0) the step's own amax is appended afterwards, dropping the oldest entry when the
- * FIFO is full. A non-finite amax is never appended (it sets nonfinite instead).
+ * FIFO is full, and the next scale is derived with the state's estimator. A non-finite amax is
+ * never appended (it sets nonfinite instead).
  * history (hist_len fp32), meta (4 int32) and scale (1 fp32) are caller-owned device buffers
  * that must outlive every queued step; step is a host counter the library advances.
  * Checkpoint = copy history, meta, scale and step; resume = copy them back. */
@@ -120,12 +121,22 @@ typedef struct qf8_delayed_state {
     int32_t fmt;         /* qf8_fmt */
     int64_t step;        /* host: number of steps since init or reset */
     int32_t magic;       /* set by qf8_delayed_init */
-    int32_t reserved;
+    int32_t estimator;   /* qf8_estimator (0 with qf8_delayed_init) */
 } qf8_delayed_state;
 
-/* Fills the host fields, clears history/meta/scale on the device, step = 0. */
+/* How the amax estimate is taken from the history ([HiF8-train 1.2]: the maximum of the buffer,
+ * or another rule such as the most recent entry or the mean). The mean is the fp32 sum of the
+ * entries from oldest to newest divided by the count in fp32. An empty history estimates 0. */
+typedef enum qf8_estimator { QF8_EST_MAX = 0, QF8_EST_RECENT = 1, QF8_EST_MEAN = 2 } qf8_estimator;
+
+/* Fills the host fields, clears history/meta/scale on the device, step = 0; the estimator is the
+ * maximum of the history. */
 int qf8_delayed_init(qf8_delayed_state *st, float *history, int32_t *meta, float *scale,
                      int hist_len, int interval, int n_guard, int fmt, void *stream);
+/* The same with an estimator (qf8_estimator; anything else gives QF8_ERR_ENUM). */
+int qf8_delayed_init_ex(qf8_delayed_state *st, float *history, int32_t *meta, float *scale,
+                        int hist_len, int interval, int n_guard, int fmt, int estimator,
+                        void *stream);
 /* Empties the history and sets step = 0, so the next step is current scaling again (the
  * restart after an anomaly, [HiF8-train 5.2]). */
 int qf8_delayed_reset(qf8_delayed_state *st, void *stream);

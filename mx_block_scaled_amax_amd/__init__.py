@@ -18,13 +18,15 @@ import torch  # loaded first: the library binds to the HIP runtime torch has alr
 __all__ = [
     "E4M3", "E5M2", "ROUND_DOWN", "ROUND_UP", "QF8Error", "library_path",
     "qf8_status_string", "qf8_workspace_bytes", "qf8_cast_scaled", "quantize_per_tensor",
-    "DelayedState", "qf8_delayed_init", "qf8_delayed_reset", "quantize_delayed",
+    "DelayedState", "qf8_delayed_init", "qf8_delayed_init_ex", "qf8_delayed_reset", "quantize_delayed",
+    "EST_MAX", "EST_RECENT", "EST_MEAN",
     "quantize_block", "quantize_mx_dual",
 ]
 
 E4M3, E5M2 = 0, 1
 ROUND_DOWN, ROUND_UP = 0, 1
 FLAG_POW2_SCALES = 1
+EST_MAX, EST_RECENT, EST_MEAN = 0, 1, 2   # delayed-scaling estimators (qf8_estimator)
 _BF16, _FP32 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -42,7 +44,7 @@ class _DelayedStruct(ctypes.Structure):
     _fields_ = [("history", ctypes.c_void_p), ("meta", ctypes.c_void_p), ("scale", ctypes.c_void_p),
                 ("hist_len", ctypes.c_int32), ("interval", ctypes.c_int32), ("n_guard", ctypes.c_int32),
                 ("fmt", ctypes.c_int32), ("step", ctypes.c_int64), ("magic", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("estimator", ctypes.c_int32)]
 
 
 def library_path():
@@ -65,6 +67,7 @@ def _load():
         "qf8_cast_scaled": (i32, [vp, i32, i64, i32, vp, vp, vp]),
         "quantize_per_tensor": (i32, [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, sz, vp]),
         "qf8_delayed_init": (i32, [ctypes.POINTER(_DelayedStruct), vp, vp, vp, i32, i32, i32, i32, vp]),
+        "qf8_delayed_init_ex": (i32, [ctypes.POINTER(_DelayedStruct), vp, vp, vp, i32, i32, i32, i32, i32, vp]),
         "qf8_delayed_reset": (i32, [ctypes.POINTER(_DelayedStruct), vp]),
         "quantize_delayed": (i32, [vp, i32, i64, i64, ctypes.POINTER(_DelayedStruct), vp, vp, vp, vp, vp, sz, vp]),
         "quantize_block": (i32, [vp, i32, i64, i64, i32, i32, i32, vp, vp, vp, vp, vp]),
@@ -191,13 +194,16 @@ def quantize_per_tensor(x, fmt, q=None, amax=None, scale=None, nonfinite=None, w
 class DelayedState:
     """Device state of per-tensor delayed scaling: history FIFO, meta (count, head), next scale."""
 
-    def __init__(self, hist_len, interval, n_guard, fmt, device="cuda", stream=None):
+    def __init__(self, hist_len, interval, n_guard, fmt, device="cuda", stream=None, estimator=None):
         self.history = torch.zeros(hist_len, dtype=torch.float32, device=device)
         self.meta = torch.zeros(4, dtype=torch.int32, device=device)
         self.scale = torch.ones(1, dtype=torch.float32, device=device)
         self.struct = _DelayedStruct()
         self.device = self.history.device
-        qf8_delayed_init(self, hist_len, interval, n_guard, fmt, stream)
+        if estimator is None:
+            qf8_delayed_init(self, hist_len, interval, n_guard, fmt, stream)
+        else:
+            qf8_delayed_init_ex(self, hist_len, interval, n_guard, fmt, estimator, stream)
 
     @property
     def step(self):
@@ -219,6 +225,12 @@ def qf8_delayed_init(state, hist_len, interval, n_guard, fmt, stream=None):
     _check(_load().qf8_delayed_init(ctypes.byref(state.struct), _ptr(state.history), _ptr(state.meta),
                                     _ptr(state.scale), hist_len, interval, n_guard, fmt,
                                     _stream(stream, state.device)), "qf8_delayed_init")
+
+
+def qf8_delayed_init_ex(state, hist_len, interval, n_guard, fmt, estimator, stream=None):
+    _check(_load().qf8_delayed_init_ex(ctypes.byref(state.struct), _ptr(state.history), _ptr(state.meta),
+                                       _ptr(state.scale), hist_len, interval, n_guard, fmt, estimator,
+                                       _stream(stream, state.device)), "qf8_delayed_init_ex")
 
 
 def qf8_delayed_reset(state, stream=None):

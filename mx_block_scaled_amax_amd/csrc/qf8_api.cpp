@@ -31,7 +31,8 @@ int check_delayed(const qf8_delayed_state *st) {
     if (st->magic != kDelayedMagic) return QF8_ERR_STATE;
     if (!st->history || !st->meta || !st->scale) return QF8_ERR_NULL;
     if (st->hist_len < 1 || st->hist_len > kMaxHistory || st->interval < 1 || st->n_guard < 0 ||
-        st->n_guard > kMaxGuard || !fmt_ok(st->fmt) || st->step < 0)
+        st->n_guard > kMaxGuard || !fmt_ok(st->fmt) || st->step < 0 || st->estimator < 0 ||
+        st->estimator > QF8_EST_MEAN)
         return QF8_ERR_STATE;
     return QF8_OK;
 }
@@ -97,10 +98,10 @@ int quantize_per_tensor(const void *x, int dtype, int64_t rows, int64_t cols, in
                                     qf8::stream_grid(n, dtype), s);
 }
 
-int qf8_delayed_init(qf8_delayed_state *st, float *history, int32_t *meta, float *scale, int hist_len, int interval,
-                     int n_guard, int fmt, void *stream) {
+int qf8_delayed_init_ex(qf8_delayed_state *st, float *history, int32_t *meta, float *scale, int hist_len,
+                        int interval, int n_guard, int fmt, int estimator, void *stream) {
     if (!st || !history || !meta || !scale) return QF8_ERR_NULL;
-    if (!fmt_ok(fmt)) return QF8_ERR_ENUM;
+    if (!fmt_ok(fmt) || estimator < QF8_EST_MAX || estimator > QF8_EST_MEAN) return QF8_ERR_ENUM;
     if (hist_len < 1 || hist_len > kMaxHistory || interval < 1 || n_guard < 0 || n_guard > kMaxGuard)
         return QF8_ERR_STATE;
     if (!aligned(history, 4) || !aligned(meta, 4) || !aligned(scale, 4)) return QF8_ERR_ALIGN;
@@ -113,8 +114,13 @@ int qf8_delayed_init(qf8_delayed_state *st, float *history, int32_t *meta, float
     st->fmt = fmt;
     st->step = 0;
     st->magic = kDelayedMagic;
-    st->reserved = 0;
+    st->estimator = estimator;
     return qf8_delayed_reset(st, stream);
+}
+
+int qf8_delayed_init(qf8_delayed_state *st, float *history, int32_t *meta, float *scale, int hist_len, int interval,
+                     int n_guard, int fmt, void *stream) {
+    return qf8_delayed_init_ex(st, history, meta, scale, hist_len, interval, n_guard, fmt, QF8_EST_MAX, stream);
 }
 
 int qf8_delayed_reset(qf8_delayed_state *st, void *stream) {
@@ -163,7 +169,7 @@ int quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, qf8_d
         }
         if (r == QF8_OK)
             r = qf8::launch_delayed_finalize(slots, partials, nparts, st->history, st->meta, st->scale, st->hist_len,
-                                             st->n_guard, st->fmt, 1, amax_out, nonfinite, s);
+                                             st->n_guard, st->fmt, 1, st->estimator, amax_out, nonfinite, s);
     } else {
         // cast with the scale the history gave, fusing this step's amax into the pass (atomic
         // maxima in the workspace slots); then append the amax on update steps and compute the
@@ -172,7 +178,7 @@ int quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, qf8_d
         r = qf8::launch_cast_fused(x, dtype, n, st->fmt, st->scale, q, scale_used, slots, grid, s);
         if (r == QF8_OK)
             r = qf8::launch_delayed_finalize(slots, partials, 0, st->history, st->meta, st->scale, st->hist_len,
-                                             st->n_guard, st->fmt, update, amax_out, nonfinite, s);
+                                             st->n_guard, st->fmt, update, st->estimator, amax_out, nonfinite, s);
     }
     if (r == QF8_OK) st->step++;
     return r;

@@ -249,10 +249,15 @@ __global__ __launch_bounds__(kThreads) void cast_scaled_kernel(const void *__res
 }
 
 // Delayed-scaling state update, by one workgroup: report the step's amax, append it on update
-// steps (dropping the oldest when the FIFO is full), and derive the next scale from the history.
+// steps (dropping the oldest when the FIFO is full), and on update steps derive the next scale
+// from the history with the state's estimator (0 maximum, 1 newest entry, 2 mean as the fp32 sum
+// from oldest to newest divided by the count). Between update steps the history and so the
+// scale do not change. The FIFO is slots [0, count) while filling (head 0), then a ring whose
+// oldest entry is at head.
 template <int FMT>
 __device__ void delayed_update(uint32_t m, float *history, int32_t *meta, float *scale, int hist_len, int n_guard,
-                               int update, float *amax_out, int32_t *nonfinite, uint32_t *red, int *sh) {
+                               int update, int estimator, float *amax_out, int32_t *nonfinite, uint32_t *red,
+                               int *sh) {
     const bool bad = m >= 0x7F800000u;
     if (threadIdx.x == 0) {
         if (amax_out) *amax_out = __uint_as_float(m);
@@ -264,22 +269,38 @@ __device__ void delayed_update(uint32_t m, float *history, int32_t *meta, float 
                 meta[0] = ++count;
             } else {
                 slot = head;
-                meta[1] = head + 1 == hist_len ? 0 : head + 1;
+                head = head + 1 == hist_len ? 0 : head + 1;
+                meta[1] = head;
             }
             history[slot] = __uint_as_float(m);
         }
         sh[0] = count;
         sh[1] = slot;
+        sh[2] = head;
     }
     __syncthreads();
-    // estimate = max of the history: slots [0, count) are the valid ones, in any order. The slot
-    // written above is taken from the register of thread 0, not re-read from memory.
-    const int count = sh[0], slot = sh[1];
+    if (!update) return;
+    // The slot written above is taken from the register of thread 0, not re-read from memory.
+    const int count = sh[0], slot = sh[1], head = sh[2];
     uint32_t e = 0;
-    for (int i = threadIdx.x; i < count; i += kFinalizeThreads)
-        if (i != slot) e = umax(e, __float_as_uint(history[i]));
-    if (threadIdx.x == 0 && slot >= 0) e = umax(e, m);
-    e = block_max_bcast<kFinalizeThreads>(e, red);
+    if (estimator == 0) {                      // maximum: slots [0, count) in any order
+        for (int i = threadIdx.x; i < count; i += kFinalizeThreads)
+            if (i != slot) e = umax(e, __float_as_uint(history[i]));
+        if (threadIdx.x == 0 && slot >= 0) e = umax(e, m);
+        e = block_max_bcast<kFinalizeThreads>(e, red);
+    } else if (threadIdx.x == 0 && count > 0) {
+        if (estimator == 1) {                  // the newest entry
+            const int idx = (head + count - 1) % hist_len;
+            e = idx == slot ? m : __float_as_uint(history[idx]);
+        } else {                               // mean, summed oldest to newest in fp32
+            float sum = 0.0f;
+            for (int i = 0; i < count; ++i) {
+                const int idx = (head + i) % hist_len;
+                sum = sum + (idx == slot ? __uint_as_float(m) : history[idx]);
+            }
+            e = __float_as_uint(sum / (float)count);
+        }
+    }
     if (threadIdx.x == 0) {
         const float margin = __uint_as_float((uint32_t)(127 - n_guard) << 23);   // 2^-N, exact
         *scale = scale_from_amax_bits<FMT>(e) * margin;
@@ -512,16 +533,16 @@ template <int FMT>
 __global__ __launch_bounds__(kFinalizeThreads) void delayed_finalize_kernel(uint32_t *slots, const uint32_t *__restrict__ partials,
                                                                             int nparts, float *history, int32_t *meta,
                                                                             float *scale, int hist_len, int n_guard,
-                                                                            int update, float *amax_out,
+                                                                            int update, int estimator, float *amax_out,
                                                                             int32_t *nonfinite) {
     static_assert(kFinalizeThreads == kSlotCount, "one slot per thread");
     __shared__ uint32_t red[kFinalizeThreads / 64];
-    __shared__ int sh[2];
+    __shared__ int sh[3];
     uint32_t *own = slots + (size_t)threadIdx.x * kBarLineWords;
     uint32_t m = umax(*own, fold_max<kFinalizeThreads>(partials, nparts));
     *own = 0u;
     m = block_max_bcast<kFinalizeThreads>(m, red);
-    delayed_update<FMT>(m, history, meta, scale, hist_len, n_guard, update, amax_out, nonfinite, red, sh);
+    delayed_update<FMT>(m, history, meta, scale, hist_len, n_guard, update, estimator, amax_out, nonfinite, red, sh);
 }
 
 __global__ void fill_u32_kernel(uint32_t *p, int64_t n, uint32_t value) {
@@ -630,14 +651,14 @@ int launch_per_tensor_onepass(const void *x, int dtype, int64_t n, int fmt, uint
 }
 
 int launch_delayed_finalize(uint32_t *slots, const uint32_t *partials, int nparts, float *history, int32_t *meta,
-                            float *scale, int hist_len, int n_guard, int fmt, int update, float *amax_out,
-                            int32_t *nonfinite, hipStream_t s) {
+                            float *scale, int hist_len, int n_guard, int fmt, int update, int estimator,
+                            float *amax_out, int32_t *nonfinite, hipStream_t s) {
     if (fmt == QF8_E4M3)
         hipLaunchKernelGGL(delayed_finalize_kernel<kE4M3>, dim3(1), dim3(kFinalizeThreads), 0, s, slots, partials, nparts,
-                           history, meta, scale, hist_len, n_guard, update, amax_out, nonfinite);
+                           history, meta, scale, hist_len, n_guard, update, estimator, amax_out, nonfinite);
     else
         hipLaunchKernelGGL(delayed_finalize_kernel<kE5M2>, dim3(1), dim3(kFinalizeThreads), 0, s, slots, partials, nparts,
-                           history, meta, scale, hist_len, n_guard, update, amax_out, nonfinite);
+                           history, meta, scale, hist_len, n_guard, update, estimator, amax_out, nonfinite);
     return status_after_launch();
 }
 

@@ -4,6 +4,9 @@
     delayed-spike worked example: codes, scales, amax, history after every step;
   * long random sequences with several (history, Interval, N_guard) settings, both formats;
   * reset (restart with current scaling), checkpoint/resume of the state, non-finite steps;
+  * the estimators (maximum, most recent, mean as the fp32 sum oldest to newest): hand
+    sequence, long histories (64 and 1024 entries) that wrap several times, an input whose mean
+    depends on the summation order, and a history whose fp32 sum overflows;
   * the full drifting-std workload: 100 iterations of 4096x14336 (history 16, Interval 5,
     N_guard 3, E4M3); every step's scale and amax bit-exact against the oracle state machine,
     and the codes of several steps compared on every byte.
@@ -23,9 +26,9 @@ pytestmark = pytest.mark.gpu
 class Pair:
     """A GPU delayed state and the oracle state machine driven with the same inputs."""
 
-    def __init__(self, hist_len, interval, n_guard, fmt):
-        self.g = qf8.DelayedState(hist_len, interval, n_guard, fmt)
-        self.o = O.Delayed(hist_len, interval, n_guard, fmt)
+    def __init__(self, hist_len, interval, n_guard, fmt, estimator=None):
+        self.g = qf8.DelayedState(hist_len, interval, n_guard, fmt, estimator=estimator)
+        self.o = O.Delayed(hist_len, interval, n_guard, fmt, estimator=estimator or 0)
         self.fmt = fmt
         self.nf = torch.zeros(1, dtype=torch.int32, device="cuda")
         self.s = torch.zeros(1, dtype=torch.float32, device="cuda")
@@ -76,6 +79,53 @@ def test_random_sequences(hist, interval, guard, fmt):
     for t in range(40):
         x = bf16_bits(basef * np.float32(2.0 ** rng.uniform(-6, 6)))
         p.step(x, f"t={t}")
+
+
+ESTIMATORS = [qf8.EST_MAX, qf8.EST_RECENT, qf8.EST_MEAN]
+
+
+@pytest.mark.parametrize("est", ESTIMATORS)
+def test_estimator_hand_sequence(est):
+    p = Pair(3, 2, 1, O.E4M3, est)
+    assert p.g.struct.estimator == est
+    for t, a in enumerate([4, 8, 2, 16, 1, 32, 64, 0.5, 0.25, 128, 2, 3]):
+        p.step(tensor_with_amax(a), f"est={est} t={t}")
+
+
+@pytest.mark.parametrize("est", ESTIMATORS)
+@pytest.mark.parametrize("hist,interval,steps", [(64, 1, 150), (1024, 1, 1100), (1024, 3, 60)])
+def test_estimator_long_histories(est, hist, interval, steps):
+    """Histories of 64 and 1024 entries: the mean sums up to 1024 fp32 values in FIFO order, and
+    the ring wraps (150 steps through 64 entries, 1100 through 1024)."""
+    rng = np.random.default_rng(7 * hist + est)
+    p = Pair(hist, interval, 2, O.E4M3 if est != qf8.EST_RECENT else O.E5M2, est)
+    basef = (small_tensor(8, 40, seed=hist + est).astype(np.uint32) << 16).view(np.float32)
+    for t in range(steps):
+        p.step(bf16_bits(basef * np.float32(2.0 ** rng.uniform(-20, 20))), f"est={est} t={t}")
+
+
+def test_mean_summation_order():
+    """History 2^24, 1, 1, 1 (then wrapping): in fp32 the oldest-to-newest sum stays 2^24 (each +1
+    is a tie to even), so the next step casts with 448 / 2^22; newest-to-oldest would sum to
+    2^24 + 4 and give another scale."""
+    p = Pair(4, 1, 0, O.E4M3, qf8.EST_MEAN)
+    for t, a in enumerate([2.0 ** 24, 1.0, 1.0, 1.0]):
+        p.step(tensor_with_amax(a), f"t={t}")
+    p.step(tensor_with_amax(3.0), "t=4")
+    assert np.float32(p.s.item()) == np.float32(448.0 * 2.0 ** -22)
+    for t, a in enumerate([2.0 ** 24, 1.0, 1.0, 5.0], start=5):
+        p.step(tensor_with_amax(a), f"t={t}")
+
+
+def test_mean_sum_overflow():
+    """Two amaxes near the largest BF16 value overflow the fp32 sum; the estimate is infinite and
+    the scale falls back to 1 (with the margin), on both sides."""
+    p = Pair(4, 1, 1, O.E5M2, qf8.EST_MEAN)
+    big = float(np.float32(3.3e38))
+    for t, a in enumerate([big, big, 2.0, 4.0, 8.0, 16.0]):
+        p.step(bf16_bits(tensor_with_amax(a)), f"t={t}")
+    with np.errstate(over="ignore"):
+        assert np.isinf(np.float32(big) + np.float32(big))
 
 
 def test_reset_and_resume():
