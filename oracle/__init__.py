@@ -79,6 +79,10 @@ def _load():
                                       _c_void_p, _c_void_p, _c_void_p, _c_void_p]
     lib.qf8o_delayed_set_estimator.restype = ctypes.c_int
     lib.qf8o_delayed_set_estimator.argtypes = [_c_void_p, ctypes.c_int]
+    lib.qf8o_delayed_set_split.restype = ctypes.c_int
+    lib.qf8o_delayed_set_split.argtypes = [_c_void_p, ctypes.c_int]
+    lib.qf8o_delayed_piece.restype = None
+    lib.qf8o_delayed_piece.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int64, _c_void_p, _c_void_p]
     lib.qf8o_delayed_get.restype = None
     lib.qf8o_delayed_get.argtypes = [_c_void_p, _c_void_p, _c_void_p, _c_void_p]
     lib.qf8o_quantize_block.restype = None
@@ -200,17 +204,29 @@ def quantize_per_tensor(x, fmt):
     return q, am[0], sc[0], int(nf[0])
 
 
+def delayed_piece(step, interval, n):
+    """[lo, hi) of the piece a split-mode step measures (R15)."""
+    lo = np.zeros(1, np.int64)
+    hi = np.zeros(1, np.int64)
+    _load().qf8o_delayed_piece(step, interval, n, _ptr(lo), _ptr(hi))
+    return int(lo[0]), int(hi[0])
+
+
 class Delayed:
     """Delayed-scaling state machine (amax history FIFO, Interval, 2^-N margin)."""
 
-    def __init__(self, hist_len, interval, n_guard, fmt, estimator=0):
-        """estimator: 0 max of the history, 1 most recent entry, 2 mean (R14)."""
+    def __init__(self, hist_len, interval, n_guard, fmt, estimator=0, split=False):
+        """estimator: 0 max of the history, 1 most recent entry, 2 mean (R14).
+        split: measure one of `interval` pieces of the tensor per step and append the window's
+        maximum on update steps (R15)."""
         lib = _load()
         self._buf = np.zeros(lib.qf8o_delayed_sizeof(), np.uint8)
         if lib.qf8o_delayed_init(_ptr(self._buf), hist_len, interval, n_guard, fmt) != 0:
             raise ValueError("bad delayed-scaling configuration")
         if lib.qf8o_delayed_set_estimator(_ptr(self._buf), estimator) != 0:
             raise ValueError("bad estimator")
+        if lib.qf8o_delayed_set_split(_ptr(self._buf), 1 if split else 0) != 0:
+            raise ValueError("bad split flag")
         self.hist_len = hist_len
         self.fmt = fmt
 

@@ -70,6 +70,14 @@
  *      again in 128x1 groups, write back) de-scales with R9 and quantizes the transposed fp32
  *      values in 1x128 groups along the rows of the transpose, so the result is stored
  *      transposed: qT [cols][rows], scalesT [cols][ceil(rows/128)].
+ *   R15 the amax computation spread over the Interval steps ([HiF8-train], the section that
+ *      compares HiF8 with FP8 and MXFP8: the tensor is cut into equal sub-tensors, one measured
+ *      per step of the Interval): the flattened tensor is cut into I consecutive pieces
+ *      [floor(k n / I), floor((k+1) n / I)); step t >= 1 measures piece (t - 1) mod I; the
+ *      maximum of the I piece amaxes of the window t-I+1 .. t is appended on the update step
+ *      t % I == 0 (the same schedule as whole-tensor updates), unless a piece of the window
+ *      held Inf/NaN. Step 0 is current scaling with the whole amax as always. The reported
+ *      amax and the non-finite flag still cover the whole tensor.
  */
 #include <stdint.h>
 #include <stddef.h>
@@ -261,6 +269,9 @@ typedef struct {
     int32_t count, head;        /* head = slot of the oldest entry */
     int64_t step;
     int32_t estimator;          /* R14: 0 max, 1 most recent, 2 mean */
+    int32_t split;              /* R15: amax measured on one of Interval sub-tensors per step */
+    int32_t window_bad;         /* a sub-tensor of the current window held Inf/NaN */
+    double window;              /* maximum of the sub-tensor amaxes measured in the window */
     float hist[QF8O_MAX_HIST];
 } qf8o_delayed;
 
@@ -282,6 +293,8 @@ void qf8o_delayed_reset(qf8o_delayed *st)
     st->count = 0;
     st->head = 0;
     st->step = 0;
+    st->window = 0.0;
+    st->window_bad = 0;
     memset(st->hist, 0, sizeof(st->hist));
 }
 
@@ -321,6 +334,24 @@ int qf8o_delayed_set_estimator(qf8o_delayed *st, int estimator)
     return 0;
 }
 
+int qf8o_delayed_set_split(qf8o_delayed *st, int split)
+{
+    if (split != 0 && split != 1) return -1;
+    st->split = split;
+    return 0;
+}
+
+/* R15: the sub-tensor a split-mode step t >= 1 measures. The flattened tensor of n elements is cut
+ * into Interval near-equal consecutive pieces, piece k = [floor(k n / I), floor((k+1) n / I)),
+ * and step t measures piece (t - 1) mod I, so the window of steps t-I+1 .. t that ends on an
+ * update step (t % I == 0) has measured every piece once (R15). */
+void qf8o_delayed_piece(int64_t step, int interval, int64_t n, int64_t *lo, int64_t *hi)
+{
+    int64_t k = (step - 1) % interval;
+    *lo = (int64_t)(((__int128)k * n) / interval);
+    *hi = (int64_t)(((__int128)(k + 1) * n) / interval);
+}
+
 /* The scale a step uses, from the state before the step. */
 float qf8o_delayed_scale(const qf8o_delayed *st)
 {
@@ -343,7 +374,21 @@ void qf8o_delayed_step(qf8o_delayed *st, const void *x, int dtype, int64_t rows,
         update = (st->step % st->interval) == 0;
     }
     qf8o_cast(x, dtype, n, st->fmt, s, q);
-    if (update && isfinite(amax)) delayed_push(st, (float)amax);
+    if (st->split && st->step > 0) {                   /* R15: fold this step's piece into the window */
+        int64_t lo, hi;
+        qf8o_delayed_piece(st->step, st->interval, n, &lo, &hi);
+        size_t esz = dtype == QF8O_BF16 ? 2 : 4;
+        double a = qf8o_amax((const char *)x + (size_t)lo * esz, dtype, hi - lo);
+        if (!isfinite(a)) st->window_bad = 1;
+        else if (a > st->window) st->window = a;
+        if (update) {                                  /* the window ends: append its maximum */
+            if (!st->window_bad) delayed_push(st, (float)st->window);
+            st->window = 0.0;
+            st->window_bad = 0;
+        }
+    } else if (update && isfinite(amax)) {
+        delayed_push(st, (float)amax);
+    }
     st->step++;
     if (scale_used) *scale_used = s;
     if (amax_out) *amax_out = (float)amax;
