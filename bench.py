@@ -379,6 +379,17 @@ def run_suite(args):
                      {"step0_ms": round(ms[0], 5), "total_100_steps_ms_event_per_step": round(sum(ms), 4),
                       "note": "step 0 is current scaling (single-pass kernel + finalize); later steps one fused "
                               "cast pass + a one-workgroup finalize"}))
+    # the same 99 steps with the amax split over the Interval, and with the mean estimator
+    for label, kw in (("split amax", {"split": True}), ("mean estimator", {"estimator": qf8.EST_MEAN})):
+        calls = steps_of(qf8.DelayedState(16, 5, 3, qf8.E4M3, **kw))
+        calls[0]()
+        e0.record(stream)
+        for c in calls[1:]:
+            c()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        b2b = e0.elapsed_time(e1) / (len(calls) - 1)
+        res.append(_summ(f"delayed 4096x14336 e4m3 {label}, steps 1..99", 3 * nd, ([b2b], b2b)))
     del xsd
 
     # fine-grained: 1x128 activations 8192x7168 and 128x128 weights 7168x18432 (E4M3)

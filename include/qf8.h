@@ -113,7 +113,8 @@ int quantize_per_tensor(const void *x, int dtype, int64_t rows, int64_t cols, in
  * Checkpoint = copy history, meta, scale and step; resume = copy them back. */
 typedef struct qf8_delayed_state {
     float *history;      /* device: hist_len fp32 slots */
-    int32_t *meta;       /* device: [0] count, [1] head (oldest slot), [2..3] reserved */
+    int32_t *meta;       /* device: [0] count, [1] head (oldest slot), [2] split-amax window
+                            maximum (fp32 bits), [3] reserved */
     float *scale;        /* device: the scale the next delayed step uses */
     int32_t hist_len;    /* 1 .. 4096 */
     int32_t interval;    /* >= 1 */
@@ -122,6 +123,8 @@ typedef struct qf8_delayed_state {
     int64_t step;        /* host: number of steps since init or reset */
     int32_t magic;       /* set by qf8_delayed_init */
     int32_t estimator;   /* qf8_estimator (0 with qf8_delayed_init) */
+    int32_t flags;       /* qf8_delayed_flags (0 with qf8_delayed_init) */
+    int32_t reserved;
 } qf8_delayed_state;
 
 /* How the amax estimate is taken from the history ([HiF8-train 1.2]: the maximum of the buffer,
@@ -129,20 +132,31 @@ typedef struct qf8_delayed_state {
  * entries from oldest to newest divided by the count in fp32. An empty history estimates 0. */
 typedef enum qf8_estimator { QF8_EST_MAX = 0, QF8_EST_RECENT = 1, QF8_EST_MEAN = 2 } qf8_estimator;
 
+/* QF8_DELAYED_SPLIT_AMAX: spread the amax measurement over the interval ([HiF8-train], the
+ * section comparing HiF8 with FP8 and MXFP8: the tensor is cut into equal sub-tensors and one
+ * is measured per step). The flattened tensor of n elements is cut into interval consecutive
+ * pieces [floor(k n / I), floor((k+1) n / I)); step t >= 1 measures piece (t - 1) mod I, and
+ * the update step t % I == 0 appends the maximum of the window's I piece amaxes (nothing when
+ * one of them was Inf/NaN). Step 0 is unchanged. amax_out and nonfinite still describe the
+ * whole tensor, which the fused pass reads anyway. */
+typedef enum qf8_delayed_flags { QF8_DELAYED_SPLIT_AMAX = 1 } qf8_delayed_flags;
+
 /* Fills the host fields, clears history/meta/scale on the device, step = 0; the estimator is the
  * maximum of the history. */
 int qf8_delayed_init(qf8_delayed_state *st, float *history, int32_t *meta, float *scale,
                      int hist_len, int interval, int n_guard, int fmt, void *stream);
-/* The same with an estimator (qf8_estimator; anything else gives QF8_ERR_ENUM). */
+/* The same with an estimator (qf8_estimator) and flags (qf8_delayed_flags); other values give
+ * QF8_ERR_ENUM. */
 int qf8_delayed_init_ex(qf8_delayed_state *st, float *history, int32_t *meta, float *scale,
                         int hist_len, int interval, int n_guard, int fmt, int estimator,
-                        void *stream);
+                        int flags, void *stream);
 /* Empties the history and sets step = 0, so the next step is current scaling again (the
  * restart after an anomaly, [HiF8-train 5.2]). */
 int qf8_delayed_reset(qf8_delayed_state *st, void *stream);
 /* One iteration on x (rows*cols elements, 16-byte aligned) -> q (16-byte aligned).
  * scale_used (nullable): the scale this step cast with. amax_out (nullable): this step's true
- * amax (computed in the same pass as the cast; only update steps append it to the history).
+ * amax over the whole tensor (computed in the same pass as the cast; only update steps append
+ * it to the history, or with QF8_DELAYED_SPLIT_AMAX the window's maximum over its pieces).
  * ws: qf8_workspace_bytes(rows, cols, dtype) bytes, 16-byte aligned, initialised as described
  * at qf8_workspace_bytes.
  * Steps after the first are two kernel launches: the cast, which also raises atomic amax

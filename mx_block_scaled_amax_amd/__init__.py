@@ -19,7 +19,7 @@ __all__ = [
     "E4M3", "E5M2", "ROUND_DOWN", "ROUND_UP", "QF8Error", "library_path",
     "qf8_status_string", "qf8_workspace_bytes", "qf8_cast_scaled", "quantize_per_tensor",
     "DelayedState", "qf8_delayed_init", "qf8_delayed_init_ex", "qf8_delayed_reset", "quantize_delayed",
-    "EST_MAX", "EST_RECENT", "EST_MEAN",
+    "EST_MAX", "EST_RECENT", "EST_MEAN", "DELAYED_SPLIT_AMAX",
     "quantize_block", "quantize_mx_dual",
 ]
 
@@ -27,6 +27,7 @@ E4M3, E5M2 = 0, 1
 ROUND_DOWN, ROUND_UP = 0, 1
 FLAG_POW2_SCALES = 1
 EST_MAX, EST_RECENT, EST_MEAN = 0, 1, 2   # delayed-scaling estimators (qf8_estimator)
+DELAYED_SPLIT_AMAX = 1                    # qf8_delayed_flags
 _BF16, _FP32 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,7 +45,7 @@ class _DelayedStruct(ctypes.Structure):
     _fields_ = [("history", ctypes.c_void_p), ("meta", ctypes.c_void_p), ("scale", ctypes.c_void_p),
                 ("hist_len", ctypes.c_int32), ("interval", ctypes.c_int32), ("n_guard", ctypes.c_int32),
                 ("fmt", ctypes.c_int32), ("step", ctypes.c_int64), ("magic", ctypes.c_int32),
-                ("estimator", ctypes.c_int32)]
+                ("estimator", ctypes.c_int32), ("flags", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 def library_path():
@@ -67,7 +68,7 @@ def _load():
         "qf8_cast_scaled": (i32, [vp, i32, i64, i32, vp, vp, vp]),
         "quantize_per_tensor": (i32, [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, sz, vp]),
         "qf8_delayed_init": (i32, [ctypes.POINTER(_DelayedStruct), vp, vp, vp, i32, i32, i32, i32, vp]),
-        "qf8_delayed_init_ex": (i32, [ctypes.POINTER(_DelayedStruct), vp, vp, vp, i32, i32, i32, i32, i32, vp]),
+        "qf8_delayed_init_ex": (i32, [ctypes.POINTER(_DelayedStruct), vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]),
         "qf8_delayed_reset": (i32, [ctypes.POINTER(_DelayedStruct), vp]),
         "quantize_delayed": (i32, [vp, i32, i64, i64, ctypes.POINTER(_DelayedStruct), vp, vp, vp, vp, vp, sz, vp]),
         "quantize_block": (i32, [vp, i32, i64, i64, i32, i32, i32, vp, vp, vp, vp, vp]),
@@ -194,16 +195,17 @@ def quantize_per_tensor(x, fmt, q=None, amax=None, scale=None, nonfinite=None, w
 class DelayedState:
     """Device state of per-tensor delayed scaling: history FIFO, meta (count, head), next scale."""
 
-    def __init__(self, hist_len, interval, n_guard, fmt, device="cuda", stream=None, estimator=None):
+    def __init__(self, hist_len, interval, n_guard, fmt, device="cuda", stream=None, estimator=None, split=False):
         self.history = torch.zeros(hist_len, dtype=torch.float32, device=device)
         self.meta = torch.zeros(4, dtype=torch.int32, device=device)
         self.scale = torch.ones(1, dtype=torch.float32, device=device)
         self.struct = _DelayedStruct()
         self.device = self.history.device
-        if estimator is None:
+        if estimator is None and not split:
             qf8_delayed_init(self, hist_len, interval, n_guard, fmt, stream)
         else:
-            qf8_delayed_init_ex(self, hist_len, interval, n_guard, fmt, estimator, stream)
+            qf8_delayed_init_ex(self, hist_len, interval, n_guard, fmt, estimator or EST_MAX,
+                                DELAYED_SPLIT_AMAX if split else 0, stream)
 
     @property
     def step(self):
@@ -227,9 +229,9 @@ def qf8_delayed_init(state, hist_len, interval, n_guard, fmt, stream=None):
                                     _stream(stream, state.device)), "qf8_delayed_init")
 
 
-def qf8_delayed_init_ex(state, hist_len, interval, n_guard, fmt, estimator, stream=None):
+def qf8_delayed_init_ex(state, hist_len, interval, n_guard, fmt, estimator, flags=0, stream=None):
     _check(_load().qf8_delayed_init_ex(ctypes.byref(state.struct), _ptr(state.history), _ptr(state.meta),
-                                       _ptr(state.scale), hist_len, interval, n_guard, fmt, estimator,
+                                       _ptr(state.scale), hist_len, interval, n_guard, fmt, estimator, flags,
                                        _stream(stream, state.device)), "qf8_delayed_init_ex")
 
 

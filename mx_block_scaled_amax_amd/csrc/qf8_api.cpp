@@ -32,7 +32,7 @@ int check_delayed(const qf8_delayed_state *st) {
     if (!st->history || !st->meta || !st->scale) return QF8_ERR_NULL;
     if (st->hist_len < 1 || st->hist_len > kMaxHistory || st->interval < 1 || st->n_guard < 0 ||
         st->n_guard > kMaxGuard || !fmt_ok(st->fmt) || st->step < 0 || st->estimator < 0 ||
-        st->estimator > QF8_EST_MEAN)
+        st->estimator > QF8_EST_MEAN || (st->flags & ~QF8_DELAYED_SPLIT_AMAX) != 0)
         return QF8_ERR_STATE;
     return QF8_OK;
 }
@@ -99,9 +99,10 @@ int quantize_per_tensor(const void *x, int dtype, int64_t rows, int64_t cols, in
 }
 
 int qf8_delayed_init_ex(qf8_delayed_state *st, float *history, int32_t *meta, float *scale, int hist_len,
-                        int interval, int n_guard, int fmt, int estimator, void *stream) {
+                        int interval, int n_guard, int fmt, int estimator, int flags, void *stream) {
     if (!st || !history || !meta || !scale) return QF8_ERR_NULL;
-    if (!fmt_ok(fmt) || estimator < QF8_EST_MAX || estimator > QF8_EST_MEAN) return QF8_ERR_ENUM;
+    if (!fmt_ok(fmt) || estimator < QF8_EST_MAX || estimator > QF8_EST_MEAN || (flags & ~QF8_DELAYED_SPLIT_AMAX))
+        return QF8_ERR_ENUM;
     if (hist_len < 1 || hist_len > kMaxHistory || interval < 1 || n_guard < 0 || n_guard > kMaxGuard)
         return QF8_ERR_STATE;
     if (!aligned(history, 4) || !aligned(meta, 4) || !aligned(scale, 4)) return QF8_ERR_ALIGN;
@@ -115,12 +116,14 @@ int qf8_delayed_init_ex(qf8_delayed_state *st, float *history, int32_t *meta, fl
     st->step = 0;
     st->magic = kDelayedMagic;
     st->estimator = estimator;
+    st->flags = flags;
+    st->reserved = 0;
     return qf8_delayed_reset(st, stream);
 }
 
 int qf8_delayed_init(qf8_delayed_state *st, float *history, int32_t *meta, float *scale, int hist_len, int interval,
                      int n_guard, int fmt, void *stream) {
-    return qf8_delayed_init_ex(st, history, meta, scale, hist_len, interval, n_guard, fmt, QF8_EST_MAX, stream);
+    return qf8_delayed_init_ex(st, history, meta, scale, hist_len, interval, n_guard, fmt, QF8_EST_MAX, 0, stream);
 }
 
 int qf8_delayed_reset(qf8_delayed_state *st, void *stream) {
@@ -169,16 +172,26 @@ int quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, qf8_d
         }
         if (r == QF8_OK)
             r = qf8::launch_delayed_finalize(slots, partials, nparts, st->history, st->meta, st->scale, st->hist_len,
-                                             st->n_guard, st->fmt, 1, st->estimator, amax_out, nonfinite, s);
+                                             st->n_guard, st->fmt, 1, st->estimator, 0, amax_out, nonfinite, s);
     } else {
         // cast with the scale the history gave, fusing this step's amax into the pass (atomic
         // maxima in the workspace slots); then append the amax on update steps and compute the
         // next scale
         const int update = (st->step % st->interval) == 0;
-        r = qf8::launch_cast_fused(x, dtype, n, st->fmt, st->scale, q, scale_used, slots, grid, s);
+        const int split = (st->flags & QF8_DELAYED_SPLIT_AMAX) != 0;
+        int64_t lo = 0, hi = 0;
+        if (split) {
+            // piece k = (t - 1) mod I: [floor(k n / I), floor((k+1) n / I)), computed as
+            // k (n / I) + k (n % I) / I so that no product exceeds I^2 < 2^62
+            const int64_t I = st->interval, k = (st->step - 1) % I, qn = n / I, rn = n % I;
+            lo = k * qn + (k * rn) / I;
+            hi = (k + 1) * qn + ((k + 1) * rn) / I;
+        }
+        r = qf8::launch_cast_fused(x, dtype, n, st->fmt, st->scale, q, scale_used, slots, split, lo, hi, grid, s);
         if (r == QF8_OK)
             r = qf8::launch_delayed_finalize(slots, partials, 0, st->history, st->meta, st->scale, st->hist_len,
-                                             st->n_guard, st->fmt, update, st->estimator, amax_out, nonfinite, s);
+                                             st->n_guard, st->fmt, update, st->estimator, split, amax_out, nonfinite,
+                                             s);
     }
     if (r == QF8_OK) st->step++;
     return r;

@@ -49,10 +49,11 @@ int launch_cast_current(const void *x, int dtype, int64_t n, int fmt, uint8_t *q
 int launch_cast_scaled(const void *x, int dtype, int64_t n, int fmt, const float *scale, uint8_t *q, int grid,
                        hipStream_t s);
 int launch_cast_fused(const void *x, int dtype, int64_t n, int fmt, const float *scale, uint8_t *q,
-                      float *scale_used, uint32_t *slots, int grid, hipStream_t s);
+                      float *scale_used, uint32_t *slots, int split, int64_t lo, int64_t hi, int grid,
+                      hipStream_t s);
 int launch_delayed_finalize(uint32_t *slots, const uint32_t *partials, int nparts, float *history, int32_t *meta,
                             float *scale, int hist_len, int n_guard, int fmt, int update, int estimator,
-                            float *amax_out, int32_t *nonfinite, hipStream_t s);
+                            int split, float *amax_out, int32_t *nonfinite, hipStream_t s);
 int launch_fill_u32(uint32_t *p, int64_t n, uint32_t value, hipStream_t s);
 
 int launch_block(const void *x, int dtype, int64_t rows, int64_t cols, int block_rows, int fmt, int pow2, uint8_t *q,

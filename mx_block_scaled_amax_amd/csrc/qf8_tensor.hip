@@ -178,6 +178,23 @@ __device__ __forceinline__ void tail_cast(const void *x, int64_t n, int64_t nvec
             q[e] = (uint8_t)cast1<FMT>(__uint_as_float(elem_bits<BF16>(x, e)), s);
 }
 
+// |x| maximum (fp32 bits) of the elements of one 16-byte vector (first element e0) that lie in
+// [lo, hi): the whole vector's maximum when it lies inside, else element by element.
+template <bool BF16>
+__device__ __forceinline__ uint32_t vec_absmax_in(uint4 v, int64_t e0, int64_t lo, int64_t hi) {
+    constexpr int E = vec_elems<BF16>();
+    if (e0 >= hi || e0 + E <= lo) return 0u;
+    if (e0 >= lo && e0 + E <= hi) return acc_to_f32bits<BF16>(vec_absmax<BF16>(0u, v));
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+        const uint32_t b = BF16 ? (w[i >> 1] >> ((i & 1) * 16)) << 16 : w[i];
+        if (e0 + i >= lo && e0 + i < hi) m = umax(m, b & 0x7FFFFFFFu);
+    }
+    return m;
+}
+
 // Read-only pass over batches of kAmaxThreads * kAmaxDepth vectors (all loads of a batch in flight
 // together; a read-only stream needs more bytes in flight per CU than the cast kernels, which also
 // have stores queued). Batches are dealt round-robin: at any moment the workgroups read
@@ -248,22 +265,29 @@ __global__ __launch_bounds__(kThreads) void cast_scaled_kernel(const void *__res
     tail_cast<BF16, FMT>(x, n, nvec, s, q);
 }
 
-// Delayed-scaling state update, by one workgroup: report the step's amax, append it on update
-// steps (dropping the oldest when the FIFO is full), and on update steps derive the next scale
+// Delayed-scaling state update, by one workgroup. m is the step's whole-tensor |amax| (reported,
+// and the flag for Inf/NaN). The value appended on update steps is m itself, or with split set
+// the maximum of the window: meta[2] holds the running maximum of the pieces measured since the
+// last update step (mp = this step's piece), and a window that saw Inf/NaN appends nothing.
+// The oldest entry is dropped when the FIFO is full. On update steps the next scale is derived
 // from the history with the state's estimator (0 maximum, 1 newest entry, 2 mean as the fp32 sum
-// from oldest to newest divided by the count). Between update steps the history and so the
-// scale do not change. The FIFO is slots [0, count) while filling (head 0), then a ring whose
-// oldest entry is at head.
+// from oldest to newest divided by the count); between them neither changes. The FIFO is
+// slots [0, count) while filling (head 0), then a ring whose oldest entry is at head.
 template <int FMT>
-__device__ void delayed_update(uint32_t m, float *history, int32_t *meta, float *scale, int hist_len, int n_guard,
-                               int update, int estimator, float *amax_out, int32_t *nonfinite, uint32_t *red,
-                               int *sh) {
-    const bool bad = m >= 0x7F800000u;
+__device__ void delayed_update(uint32_t m, uint32_t mp, int split, float *history, int32_t *meta, float *scale,
+                               int hist_len, int n_guard, int update, int estimator, float *amax_out,
+                               int32_t *nonfinite, uint32_t *red, int *sh) {
     if (threadIdx.x == 0) {
         if (amax_out) *amax_out = __uint_as_float(m);
-        if (bad && nonfinite) *nonfinite = 1;
+        if (m >= 0x7F800000u && nonfinite) *nonfinite = 1;
+        uint32_t v = m;                                              // the value to append
+        if (split) {
+            const uint32_t w = umax((uint32_t)meta[2], mp);
+            meta[2] = update ? 0 : (int32_t)w;                       // a window ends on update steps
+            v = w;
+        }
         int count = meta[0], head = meta[1], slot = -1;
-        if (update && !bad) {
+        if (update && v < 0x7F800000u) {
             if (count < hist_len) {                                  // head stays 0 while filling
                 slot = count;
                 meta[0] = ++count;
@@ -272,31 +296,33 @@ __device__ void delayed_update(uint32_t m, float *history, int32_t *meta, float 
                 head = head + 1 == hist_len ? 0 : head + 1;
                 meta[1] = head;
             }
-            history[slot] = __uint_as_float(m);
+            history[slot] = __uint_as_float(v);
         }
         sh[0] = count;
         sh[1] = slot;
         sh[2] = head;
+        sh[3] = (int)v;
     }
     __syncthreads();
     if (!update) return;
-    // The slot written above is taken from the register of thread 0, not re-read from memory.
+    // The slot written above is taken from shared memory, not re-read from global memory.
     const int count = sh[0], slot = sh[1], head = sh[2];
+    const uint32_t v = (uint32_t)sh[3];
     uint32_t e = 0;
     if (estimator == 0) {                      // maximum: slots [0, count) in any order
         for (int i = threadIdx.x; i < count; i += kFinalizeThreads)
             if (i != slot) e = umax(e, __float_as_uint(history[i]));
-        if (threadIdx.x == 0 && slot >= 0) e = umax(e, m);
+        if (threadIdx.x == 0 && slot >= 0) e = umax(e, v);
         e = block_max_bcast<kFinalizeThreads>(e, red);
     } else if (threadIdx.x == 0 && count > 0) {
         if (estimator == 1) {                  // the newest entry
             const int idx = (head + count - 1) % hist_len;
-            e = idx == slot ? m : __float_as_uint(history[idx]);
+            e = idx == slot ? v : __float_as_uint(history[idx]);
         } else {                               // mean, summed oldest to newest in fp32
             float sum = 0.0f;
             for (int i = 0; i < count; ++i) {
                 const int idx = (head + i) % hist_len;
-                sum = sum + (idx == slot ? __uint_as_float(m) : history[idx]);
+                sum = sum + (idx == slot ? __uint_as_float(v) : history[idx]);
             }
             e = __float_as_uint(sum / (float)count);
         }
@@ -310,23 +336,40 @@ __device__ void delayed_update(uint32_t m, float *history, int32_t *meta, float 
 // Cast with the state's scale and raise the running |amax| maximum of one workspace slot per
 // wave (device-scope atomic max, not waited for; waves spread over kSlotCount slots, each on
 // its own 128-byte line, so no single address takes more than a few hundred updates).
-template <bool BF16, int FMT>
+// SPLIT: the wave also raises word 1 of its slot line with the maximum over the elements
+// [lo, hi) only (the piece of the tensor a split-amax delayed step measures).
+template <bool BF16, int FMT, bool SPLIT>
 __global__ __launch_bounds__(kThreads) void cast_fused_kernel(const void *__restrict__ x, int64_t n, int64_t nvec,
                                                               const float *__restrict__ scale, uint8_t *__restrict__ q,
-                                                              float *scale_used, uint32_t *slots) {
+                                                              float *scale_used, uint32_t *slots, int64_t lo,
+                                                              int64_t hi) {
+    constexpr int E = vec_elems<BF16>();
     const float s = *scale;
-    uint32_t m = tail_absmax<BF16>(x, n, nvec);
+    uint32_t m = tail_absmax<BF16>(x, n, nvec), mp = 0;
+    if (SPLIT && blockIdx.x == 0)
+        for (int64_t e = nvec * E + threadIdx.x; e < n; e += kThreads)
+            if (e >= lo && e < hi) mp = umax(mp, elem_bits<BF16>(x, e) & 0x7FFFFFFFu);
     for (int64_t run = blockIdx.x; run < run_count(nvec); run += gridDim.x) {
         Run<BF16> r;
         r.load(x, nvec, run);
         r.template cast_store<FMT>(q, s);
         m = umax(m, r.absmax());
+        if constexpr (SPLIT) {
+            // vectors past the end of the tensor were loaded as zeros and add nothing
+#pragma unroll
+            for (int j = 0; j < kVecs; ++j)
+                mp = umax(mp, vec_absmax_in<BF16>(r.v[j], (r.first + j * kThreads + threadIdx.x) * E, lo, hi));
+        }
     }
     tail_cast<BF16, FMT>(x, n, nvec, s, q);
     m = max_wave(m);
+    if constexpr (SPLIT) mp = max_wave(mp);
     if ((threadIdx.x & 63) == 0) {
         const uint32_t slot = (blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) % kSlotCount;
         __hip_atomic_fetch_max(slots + (size_t)slot * kBarLineWords, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (SPLIT && mp != 0u)
+            __hip_atomic_fetch_max(slots + (size_t)slot * kBarLineWords + 1, mp, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
     }
     if (blockIdx.x == 0 && threadIdx.x == 0 && scale_used) *scale_used = s;
 }
@@ -533,16 +576,22 @@ template <int FMT>
 __global__ __launch_bounds__(kFinalizeThreads) void delayed_finalize_kernel(uint32_t *slots, const uint32_t *__restrict__ partials,
                                                                             int nparts, float *history, int32_t *meta,
                                                                             float *scale, int hist_len, int n_guard,
-                                                                            int update, int estimator, float *amax_out,
-                                                                            int32_t *nonfinite) {
+                                                                            int update, int estimator, int split,
+                                                                            float *amax_out, int32_t *nonfinite) {
     static_assert(kFinalizeThreads == kSlotCount, "one slot per thread");
     __shared__ uint32_t red[kFinalizeThreads / 64];
-    __shared__ int sh[3];
+    __shared__ int sh[4];
     uint32_t *own = slots + (size_t)threadIdx.x * kBarLineWords;
-    uint32_t m = umax(*own, fold_max<kFinalizeThreads>(partials, nparts));
-    *own = 0u;
+    uint32_t m = umax(own[0], fold_max<kFinalizeThreads>(partials, nparts)), mp = 0u;
+    own[0] = 0u;
+    if (split) {
+        mp = own[1];
+        own[1] = 0u;
+    }
     m = block_max_bcast<kFinalizeThreads>(m, red);
-    delayed_update<FMT>(m, history, meta, scale, hist_len, n_guard, update, estimator, amax_out, nonfinite, red, sh);
+    if (split) mp = block_max_bcast<kFinalizeThreads>(mp, red);
+    delayed_update<FMT>(m, mp, split, history, meta, scale, hist_len, n_guard, update, estimator, amax_out, nonfinite,
+                        red, sh);
 }
 
 __global__ void fill_u32_kernel(uint32_t *p, int64_t n, uint32_t value) {
@@ -604,11 +653,17 @@ int launch_cast_scaled(const void *x, int dtype, int64_t n, int fmt, const float
 }
 
 int launch_cast_fused(const void *x, int dtype, int64_t n, int fmt, const float *scale, uint8_t *q,
-                      float *scale_used, uint32_t *slots, int grid, hipStream_t s) {
+                      float *scale_used, uint32_t *slots, int split, int64_t lo, int64_t hi, int grid,
+                      hipStream_t s) {
     const int64_t nvec = vec_count(n, dtype);
-    QF8_DISPATCH_DT_FMT(dtype, fmt,
-        hipLaunchKernelGGL((cast_fused_kernel<BF16, FMT>), dim3(grid), dim3(kThreads), 0, s, x, n, nvec, scale, q,
-                           scale_used, slots));
+    if (split)
+        QF8_DISPATCH_DT_FMT(dtype, fmt,
+            hipLaunchKernelGGL((cast_fused_kernel<BF16, FMT, true>), dim3(grid), dim3(kThreads), 0, s, x, n, nvec,
+                               scale, q, scale_used, slots, lo, hi));
+    else
+        QF8_DISPATCH_DT_FMT(dtype, fmt,
+            hipLaunchKernelGGL((cast_fused_kernel<BF16, FMT, false>), dim3(grid), dim3(kThreads), 0, s, x, n, nvec,
+                               scale, q, scale_used, slots, (int64_t)0, (int64_t)0));
     return status_after_launch();
 }
 
@@ -652,13 +707,13 @@ int launch_per_tensor_onepass(const void *x, int dtype, int64_t n, int fmt, uint
 
 int launch_delayed_finalize(uint32_t *slots, const uint32_t *partials, int nparts, float *history, int32_t *meta,
                             float *scale, int hist_len, int n_guard, int fmt, int update, int estimator,
-                            float *amax_out, int32_t *nonfinite, hipStream_t s) {
+                            int split, float *amax_out, int32_t *nonfinite, hipStream_t s) {
     if (fmt == QF8_E4M3)
         hipLaunchKernelGGL(delayed_finalize_kernel<kE4M3>, dim3(1), dim3(kFinalizeThreads), 0, s, slots, partials, nparts,
-                           history, meta, scale, hist_len, n_guard, update, estimator, amax_out, nonfinite);
+                           history, meta, scale, hist_len, n_guard, update, estimator, split, amax_out, nonfinite);
     else
         hipLaunchKernelGGL(delayed_finalize_kernel<kE5M2>, dim3(1), dim3(kFinalizeThreads), 0, s, slots, partials, nparts,
-                           history, meta, scale, hist_len, n_guard, update, estimator, amax_out, nonfinite);
+                           history, meta, scale, hist_len, n_guard, update, estimator, split, amax_out, nonfinite);
     return status_after_launch();
 }
 

@@ -95,13 +95,16 @@ def test_delayed_state_errors():
     assert L.qf8_delayed_reset(None, None) == NULL
     # estimator outside qf8_estimator: init_ex refuses it before touching the device, and a
     # state whose estimator field was overwritten is refused before any launch
-    assert L.qf8_delayed_init_ex(ref, FAKE, FAKE, FAKE, 16, 1, 0, 0, 3, None) == ENUM
-    assert L.qf8_delayed_init_ex(ref, FAKE, FAKE, FAKE, 16, 1, 0, 0, -1, None) == ENUM
+    assert L.qf8_delayed_init_ex(ref, FAKE, FAKE, FAKE, 16, 1, 0, 0, 3, 0, None) == ENUM
+    assert L.qf8_delayed_init_ex(ref, FAKE, FAKE, FAKE, 16, 1, 0, 0, -1, 0, None) == ENUM
+    assert L.qf8_delayed_init_ex(ref, FAKE, FAKE, FAKE, 16, 1, 0, 0, 0, 2, None) == ENUM      # unknown flag
     st.history = st.meta = st.scale = FAKE
     st.hist_len, st.interval, st.n_guard, st.fmt, st.step = 16, 1, 0, 0, 0
     st.magic, st.estimator = 0x51463844, 3
     assert L.quantize_delayed(FAKE, 0, 4, 4, ref, FAKE, None, None, None, FAKE, 1 << 20, None) == STATE
     assert L.qf8_delayed_reset(ref, None) == STATE
+    st.estimator, st.flags = 0, 4
+    assert L.quantize_delayed(FAKE, 0, 4, 4, ref, FAKE, None, None, None, FAKE, 1 << 20, None) == STATE
 
 
 def test_no_cpu_path():

@@ -7,6 +7,10 @@
   * the estimators (maximum, most recent, mean as the fp32 sum oldest to newest): hand
     sequence, long histories (64 and 1024 entries) that wrap several times, an input whose mean
     depends on the summation order, and a history whose fp32 sum overflows;
+  * the amax split over the Interval steps (one piece of the flattened tensor measured per step,
+    the window's maximum appended on update steps): a hand sequence, pieces that start and end
+    inside 16-byte vectors and in the scalar tail, BF16 and FP32, every estimator, Inf/NaN in
+    and out of the measured piece, and the full drifting workload;
   * the full drifting-std workload: 100 iterations of 4096x14336 (history 16, Interval 5,
     N_guard 3, E4M3); every step's scale and amax bit-exact against the oracle state machine,
     and the codes of several steps compared on every byte.
@@ -26,9 +30,9 @@ pytestmark = pytest.mark.gpu
 class Pair:
     """A GPU delayed state and the oracle state machine driven with the same inputs."""
 
-    def __init__(self, hist_len, interval, n_guard, fmt, estimator=None):
-        self.g = qf8.DelayedState(hist_len, interval, n_guard, fmt, estimator=estimator)
-        self.o = O.Delayed(hist_len, interval, n_guard, fmt, estimator=estimator or 0)
+    def __init__(self, hist_len, interval, n_guard, fmt, estimator=None, split=False):
+        self.g = qf8.DelayedState(hist_len, interval, n_guard, fmt, estimator=estimator, split=split)
+        self.o = O.Delayed(hist_len, interval, n_guard, fmt, estimator=estimator or 0, split=split)
         self.fmt = fmt
         self.nf = torch.zeros(1, dtype=torch.int32, device="cuda")
         self.s = torch.zeros(1, dtype=torch.float32, device="cuda")
@@ -128,6 +132,83 @@ def test_mean_sum_overflow():
         assert np.isinf(np.float32(big) + np.float32(big))
 
 
+def row(*v):
+    return np.array([v], np.float32)
+
+
+def test_split_hand_sequence():
+    p = Pair(4, 2, 0, O.E4M3, split=True)
+    assert p.g.struct.flags == qf8.DELAYED_SPLIT_AMAX
+    for t, x in enumerate([row(1, 2, 3, 4), row(8, 1, 100, 1), row(100, 1, 2, 16), row(1, 1, 1, 1),
+                           row(0.5, 0.5, 0.5, 2), row(3, 0, 0, 0)]):
+        p.step(x, f"t={t}")
+    assert p.g.history_list() == [4.0, 16.0, 2.0]
+
+
+def outlier_steps(rng, shape, steps, fp32):
+    """Random tensors whose few large entries move from step to step, so the piece amaxes differ
+    from the whole amax and from each other."""
+    for _ in range(steps):
+        x = rng.standard_normal(shape).astype(np.float32) * np.float32(2.0 ** rng.uniform(-6, 6))
+        flat = x.reshape(-1)
+        idx = rng.choice(flat.size, size=3, replace=False)
+        flat[idx] *= np.float32(rng.uniform(10, 1000))
+        yield x if fp32 else bf16_bits(x)
+
+
+@pytest.mark.parametrize("est", ESTIMATORS)
+@pytest.mark.parametrize("interval,shape,fp32", [(5, (33, 73), False), (3, (7, 5), False), (7, (129, 1001), True),
+                                                 (4, (301, 4096), False), (2, (1, 3), True), (6, (1024, 999), False)])
+def test_split_random_sequences(est, interval, shape, fp32):
+    """Pieces of 2409 elements cut in 5 (boundaries inside vectors, 1-element tail), 35 in 3,
+    129129 fp32 in 7, a multi-run tensor in 4, 3 elements in 2, and 1023K elements in 6."""
+    rng = np.random.default_rng(interval * 1000 + shape[1] + est)
+    p = Pair(6, interval, 1, O.E4M3 if est != qf8.EST_MEAN else O.E5M2, est, split=True)
+    for t, x in enumerate(outlier_steps(rng, shape, 3 * interval + 2, fp32)):
+        p.step(x, f"t={t}")
+
+
+def test_split_nonfinite_inside_and_outside_the_piece():
+    p = Pair(4, 2, 0, O.E4M3, split=True)
+    base = small_tensor(16, 40, seed=9)
+    x = base.copy()
+    p.step(x, "t=0")
+    x = base.copy()
+    x[2, 5] = 0x7FC0                                   # NaN in piece [0, 320) at step 1
+    p.step(x, "nan inside")
+    p.step(base, "window dropped")
+    assert len(p.g.history_list()) == 1
+    x = base.copy()
+    x[12, 1] = 0x7F80                                  # Inf outside piece [0, 320) at step 3
+    p.step(x, "inf outside")
+    p.step(base, "window appended")
+    assert len(p.g.history_list()) == 2
+
+
+def test_split_full_size_drifting_workload():
+    """The 4096x14336 drifting workload with the amax split over Interval = 5 steps (pieces of
+    11744051 or 11744052 elements): every step's scale, amax and history, codes of three steps."""
+    z = delayed_base()
+    sig = delayed_sigmas()
+    zd = torch.from_numpy(z).cuda()
+    st = qf8.DelayedState(16, 5, 3, qf8.E4M3, split=True)
+    orc = O.Delayed(16, 5, 3, O.E4M3, split=True)
+    s = torch.zeros(1, dtype=torch.float32, device="cuda")
+    a = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ws = qf8.workspace(zd)
+    q = torch.empty(z.shape, dtype=torch.uint8, device="cuda")
+    for t in range(11):
+        xd = (zd * float(sig[t])).to(torch.bfloat16)
+        qf8.quantize_delayed(xd, st, q=q, scale_used=s, amax_out=a, ws=ws)
+        torch.cuda.synchronize()
+        wq, ws_o, wa_o, _ = orc.step(delayed_step_input(z, sig[t]))
+        assert np.float32(a.item()) == wa_o, f"amax t={t}"
+        assert np.float32(s.item()) == ws_o, f"scale t={t}"
+        if t in (0, 4, 10):
+            assert_bytes_equal(host(q), wq, "q", f" [4096x14336 split t={t}]")
+        assert st.history_list() == list(orc.state()[0]), f"history t={t}"
+
+
 def test_reset_and_resume():
     p = Pair(4, 2, 3, O.E4M3)
     rng = np.random.default_rng(3)
@@ -213,14 +294,14 @@ def test_workspace_clean_after_steps():
     """The fused steps' amax slots and the step-0 barrier are left zero in the workspace, so one
     workspace serves consecutive states and sizes (large: single-pass step 0; small: two kernels)."""
     ws = qf8.workspace(torch.empty(1, device="cuda"))
-    for rows, cols in ((2048, 4096), (13, 29)):
-        p = Pair(8, 2, 1, O.E4M3)
+    for rows, cols, split in ((2048, 4096, False), (13, 29, False), (2048, 4096, True), (13, 29, True)):
+        p = Pair(8, 2, 1, O.E4M3, split=split)
         for t in range(5):
             x = small_tensor(rows, cols, seed=100 + t)
             xd = to_device(x)
             q = qf8.quantize_delayed(xd, p.g, ws=ws)
             torch.cuda.synchronize()
             wq, _, _, _ = p.o.step(x)
-            assert_bytes_equal(host(q), wq, "q", f" [{rows}x{cols} t={t}]")
+            assert_bytes_equal(host(q), wq, "q", f" [{rows}x{cols} split={split} t={t}]")
             words = host(ws.view(torch.int32)[:qf8.BARRIER_WORDS])
-            assert not words.any(), f"workspace not left zero [{rows}x{cols} t={t}]"
+            assert not words.any(), f"workspace not left zero [{rows}x{cols} split={split} t={t}]"
