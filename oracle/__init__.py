@@ -15,7 +15,7 @@ import subprocess
 
 import numpy as np
 
-E4M3, E5M2, E8M0 = 0, 1, 2
+E4M3, E5M2, E8M0, E2M1 = 0, 1, 2, 3
 ROUND_DOWN, ROUND_UP = 0, 1
 EST_MAX, EST_RECENT, EST_MEAN = 0, 1, 2
 
@@ -105,6 +105,25 @@ def _load():
     lib.qf8o_dequant_block.argtypes = [_c_void_p, _i64, _i64, _i64, _i64, ctypes.c_int, _c_void_p, _c_void_p]
     lib.qf8o_dequant_mx.restype = None
     lib.qf8o_dequant_mx.argtypes = [_c_void_p, _c_void_p, _i64, _i64, ctypes.c_int, _c_void_p]
+    lib.qf8o_pack_fp4.restype = None
+    lib.qf8o_pack_fp4.argtypes = [_c_void_p, _i64, _c_void_p]
+    lib.qf8o_unpack_fp4.restype = None
+    lib.qf8o_unpack_fp4.argtypes = [_c_void_p, _i64, _c_void_p]
+    lib.qf8o_nvfp4_tensor_scale.restype = ctypes.c_float
+    lib.qf8o_nvfp4_tensor_scale.argtypes = [ctypes.c_double]
+    lib.qf8o_nvfp4_block.restype = None
+    lib.qf8o_nvfp4_block.argtypes = [ctypes.c_double, ctypes.c_float, _c_void_p, _c_void_p]
+    lib.qf8o_quantize_nvfp4.restype = None
+    lib.qf8o_quantize_nvfp4.argtypes = [_c_void_p, ctypes.c_int, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
+                                        _c_void_p, _c_void_p]
+    lib.qf8o_dequant_mxfp4_one.restype = ctypes.c_float
+    lib.qf8o_dequant_mxfp4_one.argtypes = [ctypes.c_uint, ctypes.c_uint]
+    lib.qf8o_dequant_nvfp4_one.restype = ctypes.c_float
+    lib.qf8o_dequant_nvfp4_one.argtypes = [ctypes.c_uint, ctypes.c_uint, ctypes.c_float]
+    lib.qf8o_dequant_nvfp4.restype = None
+    lib.qf8o_dequant_nvfp4.argtypes = [_c_void_p, _c_void_p, _i64, _i64, ctypes.c_float, _c_void_p]
+    lib.qf8o_dequant_mxfp4.restype = None
+    lib.qf8o_dequant_mxfp4.argtypes = [_c_void_p, _c_void_p, _i64, _i64, _c_void_p]
     lib.qf8o_f32_to_bf16.restype = None
     lib.qf8o_f32_to_bf16.argtypes = [_c_void_p, _i64, _c_void_p]
     lib.qf8o_stats_scaled.restype = None
@@ -412,3 +431,80 @@ def requant_1x128_to_128x1(q, scales, fmt_in, fmt_out, pow2_out):
     _load().qf8o_requant_1x128_to_128x1(_ptr(q), _ptr(scales), rows, cols, fmt_in, fmt_out, int(bool(pow2_out)),
                                         _ptr(tmp), _ptr(qT), _ptr(sT), _ptr(nf))
     return qT, sT, int(nf[0])
+
+
+# ---- FP4 (R16 MXFP4, R17 NVFP4) -----------------------------------------------------------------
+
+def pack_fp4(codes):
+    """4-bit codes (one per byte, even count along the last axis) -> bytes, c[2j] | c[2j+1] << 4."""
+    c = np.ascontiguousarray(codes, np.uint8)
+    out = np.empty(c.shape[:-1] + (c.shape[-1] // 2,), np.uint8)
+    _load().qf8o_pack_fp4(_ptr(c), c.size, _ptr(out))
+    return out
+
+
+def unpack_fp4(packed):
+    p = np.ascontiguousarray(packed, np.uint8)
+    out = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), np.uint8)
+    _load().qf8o_unpack_fp4(_ptr(p), out.size, _ptr(out))
+    return out
+
+
+def quantize_mxfp4(x, rnd, row=True, col=True):
+    """Returns (q_row [rows][cols/2], s_row, q_colT [cols][rows/2], s_colT, nonfinite), packed."""
+    q_row, s_row, q_colT, s_colT, nf = quantize_mx(x, E2M1, rnd, row, col)
+    return (pack_fp4(q_row) if row else None, s_row, pack_fp4(q_colT) if col else None, s_colT, nf)
+
+
+def nvfp4_tensor_scale(a):
+    return _load().qf8o_nvfp4_tensor_scale(float(a))
+
+
+def nvfp4_block(amax_b, s_t):
+    """(E4M3 block-scale code, encode factor r_b) of one block (R17)."""
+    e = np.zeros(1, np.uint32)
+    r = np.zeros(1, np.float32)
+    _load().qf8o_nvfp4_block(float(amax_b), float(np.float32(s_t)), _ptr(e), _ptr(r))
+    return int(e[0]), np.float32(r[0])
+
+
+def quantize_nvfp4(x):
+    """Returns (q [rows][cols/2] packed, s_blk [rows][cols/16] E4M3 codes, S_t, amax, nonfinite)."""
+    x = _contig(x)
+    rows, cols = x.shape
+    codes = np.empty((rows, cols), np.uint8)
+    s_blk = np.empty((rows, cols // 16), np.uint8)
+    st = np.zeros(1, np.float32)
+    a = np.zeros(1, np.float32)
+    nf = np.zeros(1, np.int32)
+    _load().qf8o_quantize_nvfp4(_ptr(x), _dtype_code(x), rows, cols, _ptr(codes), _ptr(s_blk), _ptr(st), _ptr(a),
+                                _ptr(nf))
+    return pack_fp4(codes), s_blk, np.float32(st[0]), np.float32(a[0]), int(nf[0])
+
+
+def dequant_mxfp4(q, s):
+    """q [rows][cols/2] packed, s [rows][cols/32] E8M0 -> float32 [rows][cols]."""
+    codes = unpack_fp4(q)
+    s = np.ascontiguousarray(s, np.uint8)
+    rows, cols = codes.shape
+    out = np.empty((rows, cols), np.float32)
+    _load().qf8o_dequant_mxfp4(_ptr(codes), _ptr(s), rows, cols, _ptr(out))
+    return out
+
+
+def dequant_nvfp4(q, s_blk, s_t):
+    """q [rows][cols/2] packed, s_blk [rows][cols/16] E4M3, S_t -> float32 [rows][cols]."""
+    codes = unpack_fp4(q)
+    s_blk = np.ascontiguousarray(s_blk, np.uint8)
+    rows, cols = codes.shape
+    out = np.empty((rows, cols), np.float32)
+    _load().qf8o_dequant_nvfp4(_ptr(codes), _ptr(s_blk), rows, cols, float(np.float32(s_t)), _ptr(out))
+    return out
+
+
+def dequant_nvfp4_one(code, e_code, s_t):
+    return _load().qf8o_dequant_nvfp4_one(int(code), int(e_code), float(np.float32(s_t)))
+
+
+def dequant_mxfp4_one(code, sbyte):
+    return _load().qf8o_dequant_mxfp4_one(int(code), int(sbyte))

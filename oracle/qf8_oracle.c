@@ -88,6 +88,7 @@
 #define QF8O_E4M3 0
 #define QF8O_E5M2 1
 #define QF8O_E8M0 2
+#define QF8O_E2M1 3
 
 #define QF8O_BF16 0
 #define QF8O_FP32 1
@@ -100,11 +101,14 @@
  * [MP-FP8 2.1]: sign, biased exponent, trailing mantissa; exponent field 0 = subnormal with the
  * minimum exponent; [MP-FP8 2.2]: E5M2 follows IEEE (all-ones exponent = Inf/NaN); E4M3 has no
  * Inf and one NaN pattern S.1111.111, so the all-ones exponent also holds finite values up to 448.
- * Bias is 2^(e-1) - 1.
+ * Bias is 2^(e-1) - 1. E2M1 ([MP-FP8 13.2]: the FP4 element of MXFP4 and NVFP4, values 0, 0.5,
+ * 1, 1.5, 2, 3, 4, 6 and their negatives) is the 4-bit code S.EE.M with bias 1 and no Inf/NaN;
+ * code 1 is the one subnormal, 0.5.
  * ------------------------------------------------------------------------------------------- */
-static int fmt_mbits(int fmt) { return fmt == QF8O_E4M3 ? 3 : 2; }
-static int fmt_ebits(int fmt) { return fmt == QF8O_E4M3 ? 4 : 5; }
+static int fmt_mbits(int fmt) { return fmt == QF8O_E4M3 ? 3 : fmt == QF8O_E2M1 ? 1 : 2; }
+static int fmt_ebits(int fmt) { return fmt == QF8O_E4M3 ? 4 : fmt == QF8O_E2M1 ? 2 : 5; }
 static int fmt_bias(int fmt) { return (1 << (fmt_ebits(fmt) - 1)) - 1; }
+static int fmt_bits(int fmt) { return 1 + fmt_ebits(fmt) + fmt_mbits(fmt); }
 
 double qf8o_decode(int fmt, unsigned code)
 {
@@ -114,7 +118,8 @@ double qf8o_decode(int fmt, unsigned code)
         return ldexp(1.0, (int)code - 127);
     }
     int mb = fmt_mbits(fmt), eb = fmt_ebits(fmt), bias = fmt_bias(fmt);
-    int s = (int)(code >> 7);
+    code &= (1u << fmt_bits(fmt)) - 1u;
+    int s = (int)(code >> (eb + mb));
     int e = (int)(code >> mb) & ((1 << eb) - 1);
     int m = (int)code & ((1 << mb) - 1);
     int eall = (1 << eb) - 1;
@@ -133,14 +138,14 @@ double qf8o_decode(int fmt, unsigned code)
 
 /* Ascending list of the non-negative finite values. Codes 0, 1, 2, ... decode in increasing
  * order, so the index in the list is the code itself (checked by the test suite). */
-static double g_vals[2][128];
-static int g_nvals[2] = {0, 0};
+static double g_vals[4][128];
+static int g_nvals[4] = {0, 0, 0, 0};
 
 static void build_table(int fmt)
 {
     if (g_nvals[fmt]) return;
     int n = 0;
-    for (unsigned c = 0; c < 128; ++c) {
+    for (unsigned c = 0; c < (1u << (fmt_bits(fmt) - 1)); ++c) {
         double v = qf8o_decode(fmt, c);
         if (!isfinite(v)) break;
         g_vals[fmt][n++] = v;
@@ -154,14 +159,16 @@ double qf8o_max_finite(int fmt) { build_table(fmt); return g_vals[fmt][g_nvals[f
 /* sat_rne8(y): nearest fp8 value, ties to the even code, with magnitudes at or above the largest
  * finite value clamped to it ([MP-FP8 4.1] RNE; [MP-FP8 8.1] overflow saturates, it is not
  * skipped; [MXFP8-recipe 4.1] the cast saturates). Sign kept, so -0 and negative values that
- * round to zero give 0x80 (R3). NaN gives the positive NaN code (R6). */
+ * round to zero give 0x80 (R3). NaN gives the positive NaN code (R6). E2M1 has no NaN: its codes
+ * are 4 bits with the sign in bit 3, and NaN gives +6 (outside the compared results, R6). */
 unsigned qf8o_encode(int fmt, double y)
 {
     build_table(fmt);
     const double *v = g_vals[fmt];
     int n = g_nvals[fmt];
-    if (isnan(y)) return 0x7Fu;
-    unsigned sign = signbit(y) ? 0x80u : 0u;
+    const unsigned sbit = 1u << (fmt_bits(fmt) - 1);
+    if (isnan(y)) return fmt == QF8O_E2M1 ? (unsigned)(n - 1) : 0x7Fu;
+    unsigned sign = signbit(y) ? sbit : 0u;
     double a = fabs(y);
     int i;
     if (a >= v[n - 1]) {
@@ -695,4 +702,121 @@ void qf8o_requant_1x128_to_128x1(const uint8_t *q, const float *scales, int64_t 
         for (int64_t r = 0; r < rows; ++r)
             tmp[c * rows + r] = qf8o_dequant_one(fmt_in, q[r * cols + c], scales[r * gc + c / 128]);
     qf8o_quantize_block_ex(tmp, QF8O_FP32, cols, rows, 1, 128, fmt_out, pow2_out, qT, scalesT, NULL, nonfinite);
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * FP4 ([MP-FP8 13.1-13.2]; [Ascend950 2.4] MXFP4 = 32 FP4 values + one shared scale).
+ * R16 MXFP4: the MX rule of qf8o_quantize_mx with E2M1 elements (emax = 2, largest value 6): X
+ *     = floor(log2 amax) - 2 (round-down) or the smallest X with amax / 2^X <= 6 (round-up),
+ *     clamped to [-127, 127]; amax = 0 gives X = -127 and zero codes; a block with Inf/NaN gets
+ *     scale byte 0xFF. Codes are stored two per byte, element 2j in the low nibble of byte j
+ *     and element 2j+1 in the high nibble (the pages do not fix the order; this is the order
+ *     of the OCP MX format).
+ * R17 NVFP4: blocks of 16 along a row, one E4M3 block scale each and one fp32 tensor scale.
+ *     The pages fix the block scale as amax_b / 6 stored in E4M3 and add the fp32 tensor scale
+ *     because E4M3's range is too small, without its formula. Reading: the tensor scale S_t is
+ *     chosen so that the largest block scale lands on E4M3's largest value 448:
+ *       S_t = fl32(448 * 6 / A) with A the tensor amax (1 for A = 0 or non-finite, FLT_MAX on
+ *             overflow, as Eq.(1));
+ *       e_b = sat_rne(E4M3, fl32(fl32(amax_b / 6) * S_t))   (the stored block-scale code);
+ *       r_b = fl32(S_t / decode(e_b)), or 0 when e_b decodes to 0 (the block is negligible
+ *             against the tensor and encodes as signed zeros);
+ *       code = sat_rne(E2M1, fl32(x * r_b)),
+ *     so that x is divided by the real block scale decode(e_b) / S_t through one per-block
+ *     reciprocal. The pages' example (amax 5.3, S_t = 1): 5.3/6 = 0.883 -> E4M3 0.875,
+ *     5.3 / 0.875 = 6.06 -> 6, de-scaled 5.25. A block with Inf/NaN gets the E4M3 NaN code
+ *     0x7F and sets nonfinite.
+ * ------------------------------------------------------------------------------------------- */
+
+/* Pairs of 4-bit codes into bytes: out[j] = c[2j] | c[2j+1] << 4 (n even). */
+void qf8o_pack_fp4(const uint8_t *codes, int64_t n, uint8_t *out)
+{
+    for (int64_t j = 0; j < n / 2; ++j)
+        out[j] = (uint8_t)((codes[2 * j] & 0xFu) | ((codes[2 * j + 1] & 0xFu) << 4));
+}
+
+void qf8o_unpack_fp4(const uint8_t *packed, int64_t n, uint8_t *codes)
+{
+    for (int64_t j = 0; j < n / 2; ++j) {
+        codes[2 * j] = packed[j] & 0xFu;
+        codes[2 * j + 1] = packed[j] >> 4;
+    }
+}
+
+/* R17: the tensor scale from the tensor amax. */
+float qf8o_nvfp4_tensor_scale(double amax)
+{
+    if (!isfinite(amax) || amax == 0.0) return 1.0f;
+    float s = (float)(448.0 * 6.0 / amax);
+    if (isinf(s)) s = FLT_MAX;
+    return s;
+}
+
+/* R17, for one block of 16 given its amax: the E4M3 block-scale code and the encode factor. */
+void qf8o_nvfp4_block(double amax_b, float s_t, unsigned *e_code, float *r)
+{
+    float d = (float)(amax_b / 6.0);                     /* amax_b / 6, rounded to fp32 */
+    unsigned e = qf8o_encode(QF8O_E4M3, (double)(float)((double)d * (double)s_t));
+    double dec = qf8o_decode(QF8O_E4M3, e);
+    *e_code = e;
+    *r = (dec == 0.0 || isnan(dec)) ? 0.0f : (float)((double)s_t / dec);
+}
+
+/* x [rows][cols] (cols % 16 == 0) -> codes [rows][cols] (one 4-bit code per byte, unpacked),
+ * s_blk [rows][cols/16] E4M3 codes, the tensor scale S_t and amax, nonfinite. */
+void qf8o_quantize_nvfp4(const void *x, int dtype, int64_t rows, int64_t cols, uint8_t *codes, uint8_t *s_blk,
+                         float *tensor_scale, float *amax_out, int32_t *nonfinite)
+{
+    double A = qf8o_amax(x, dtype, rows * cols);
+    float s_t = qf8o_nvfp4_tensor_scale(A);
+    int bad = !isfinite(A);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t g = 0; g < cols / 16; ++g) {
+            int64_t base = r * cols + g * 16;
+            double a = qf8o_amax((const char *)x + (size_t)base * (dtype == QF8O_BF16 ? 2 : 4), dtype, 16);
+            if (!isfinite(a)) {
+                s_blk[r * (cols / 16) + g] = 0x7F;       /* the E4M3 NaN code */
+                for (int k = 0; k < 16; ++k) codes[base + k] = 0;
+                continue;
+            }
+            unsigned e;
+            float rb;
+            qf8o_nvfp4_block(a, s_t, &e, &rb);
+            s_blk[r * (cols / 16) + g] = (uint8_t)e;
+            for (int k = 0; k < 16; ++k) {
+                float v = (float)(load_elem(x, dtype, base + k) * (double)rb);   /* fl32(x * r_b) */
+                codes[base + k] = (uint8_t)qf8o_encode(QF8O_E2M1, (double)v);
+            }
+        }
+    if (tensor_scale) *tensor_scale = s_t;
+    if (amax_out) *amax_out = (float)A;
+    if (nonfinite) *nonfinite = bad;
+}
+
+/* De-scaling (R9 applied to FP4): MXFP4 decode(c) * 2^X, exact, NaN for byte 0xFF; NVFP4
+ * fl32(decode(c) * decode(e_b) / S_t), where the product of the two short significands is exact. */
+float qf8o_dequant_mxfp4_one(unsigned code, unsigned sbyte)
+{
+    if (sbyte == 0xFFu) return NAN;
+    return (float)ldexp(qf8o_decode(QF8O_E2M1, code), (int)sbyte - 127);
+}
+
+float qf8o_dequant_nvfp4_one(unsigned code, unsigned e_code, float s_t)
+{
+    double p = qf8o_decode(QF8O_E2M1, code) * qf8o_decode(QF8O_E4M3, e_code);
+    return (float)(p / (double)s_t);
+}
+
+void qf8o_dequant_nvfp4(const uint8_t *codes, const uint8_t *s_blk, int64_t rows, int64_t cols, float s_t, float *out)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            out[r * cols + c] = qf8o_dequant_nvfp4_one(codes[r * cols + c], s_blk[r * (cols / 16) + c / 16], s_t);
+}
+
+void qf8o_dequant_mxfp4(const uint8_t *codes, const uint8_t *sb, int64_t rows, int64_t cols, float *out)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            out[r * cols + c] = qf8o_dequant_mxfp4_one(codes[r * cols + c], sb[r * (cols / 32) + c / 32]);
 }
