@@ -115,7 +115,7 @@ def _load():
     lib.qf8o_nvfp4_block.argtypes = [ctypes.c_double, ctypes.c_float, _c_void_p, _c_void_p]
     lib.qf8o_quantize_nvfp4.restype = None
     lib.qf8o_quantize_nvfp4.argtypes = [_c_void_p, ctypes.c_int, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
-                                        _c_void_p, _c_void_p]
+                                        _c_void_p, _c_void_p, _c_void_p]
     lib.qf8o_dequant_mxfp4_one.restype = ctypes.c_float
     lib.qf8o_dequant_mxfp4_one.argtypes = [ctypes.c_uint, ctypes.c_uint]
     lib.qf8o_dequant_nvfp4_one.restype = ctypes.c_float
@@ -468,17 +468,19 @@ def nvfp4_block(amax_b, s_t):
     return int(e[0]), np.float32(r[0])
 
 
-def quantize_nvfp4(x):
-    """Returns (q [rows][cols/2] packed, s_blk [rows][cols/16] E4M3 codes, S_t, amax, nonfinite)."""
+def quantize_nvfp4(x, amax_in=None):
+    """Returns (q [rows][cols/2] packed, s_blk [rows][cols/16] E4M3 codes, S_t, amax, nonfinite).
+    amax_in: a tensor amax to use in place of the measured one."""
     x = _contig(x)
+    ain = None if amax_in is None else np.array([amax_in], np.float32)
     rows, cols = x.shape
     codes = np.empty((rows, cols), np.uint8)
     s_blk = np.empty((rows, cols // 16), np.uint8)
     st = np.zeros(1, np.float32)
     a = np.zeros(1, np.float32)
     nf = np.zeros(1, np.int32)
-    _load().qf8o_quantize_nvfp4(_ptr(x), _dtype_code(x), rows, cols, _ptr(codes), _ptr(s_blk), _ptr(st), _ptr(a),
-                                _ptr(nf))
+    _load().qf8o_quantize_nvfp4(_ptr(x), _dtype_code(x), rows, cols, _ptr(ain), _ptr(codes), _ptr(s_blk), _ptr(st),
+                                _ptr(a), _ptr(nf))
     return pack_fp4(codes), s_blk, np.float32(st[0]), np.float32(a[0]), int(nf[0])
 
 

@@ -719,8 +719,8 @@ void qf8o_requant_1x128_to_128x1(const uint8_t *q, const float *scales, int64_t 
  *       S_t = fl32(448 * 6 / A) with A the tensor amax (1 for A = 0 or non-finite, FLT_MAX on
  *             overflow, as Eq.(1));
  *       e_b = sat_rne(E4M3, fl32(fl32(amax_b / 6) * S_t))   (the stored block-scale code);
- *       r_b = fl32(S_t / decode(e_b)), or 0 when e_b decodes to 0 (the block is negligible
- *             against the tensor and encodes as signed zeros);
+ *       r_b = fl32(S_t / decode(e_b)) (FLT_MAX if that overflows), or 0 when e_b decodes to 0
+ *             (the block is negligible against the tensor and encodes as signed zeros);
  *       code = sat_rne(E2M1, fl32(x * r_b)),
  *     so that x is divided by the real block scale decode(e_b) / S_t through one per-block
  *     reciprocal. The pages' example (amax 5.3, S_t = 1): 5.3/6 = 0.883 -> E4M3 0.875,
@@ -759,15 +759,18 @@ void qf8o_nvfp4_block(double amax_b, float s_t, unsigned *e_code, float *r)
     unsigned e = qf8o_encode(QF8O_E4M3, (double)(float)((double)d * (double)s_t));
     double dec = qf8o_decode(QF8O_E4M3, e);
     *e_code = e;
-    *r = (dec == 0.0 || isnan(dec)) ? 0.0f : (float)((double)s_t / dec);
+    float rr = (dec == 0.0 || isnan(dec)) ? 0.0f : (float)((double)s_t / dec);
+    *r = isinf(rr) ? FLT_MAX : rr;
 }
 
 /* x [rows][cols] (cols % 16 == 0) -> codes [rows][cols] (one 4-bit code per byte, unpacked),
- * s_blk [rows][cols/16] E4M3 codes, the tensor scale S_t and amax, nonfinite. */
-void qf8o_quantize_nvfp4(const void *x, int dtype, int64_t rows, int64_t cols, uint8_t *codes, uint8_t *s_blk,
-                         float *tensor_scale, float *amax_out, int32_t *nonfinite)
+ * s_blk [rows][cols/16] E4M3 codes, the tensor scale S_t and amax, nonfinite. amax_in (nullable):
+ * a tensor amax given by the caller (its magnitude is used) in place of the measured one, as
+ * when it comes from an amax history. */
+void qf8o_quantize_nvfp4(const void *x, int dtype, int64_t rows, int64_t cols, const float *amax_in, uint8_t *codes,
+                         uint8_t *s_blk, float *tensor_scale, float *amax_out, int32_t *nonfinite)
 {
-    double A = qf8o_amax(x, dtype, rows * cols);
+    double A = amax_in ? fabs((double)*amax_in) : qf8o_amax(x, dtype, rows * cols);
     float s_t = qf8o_nvfp4_tensor_scale(A);
     int bad = !isfinite(A);
     for (int64_t r = 0; r < rows; ++r)
@@ -775,6 +778,7 @@ void qf8o_quantize_nvfp4(const void *x, int dtype, int64_t rows, int64_t cols, u
             int64_t base = r * cols + g * 16;
             double a = qf8o_amax((const char *)x + (size_t)base * (dtype == QF8O_BF16 ? 2 : 4), dtype, 16);
             if (!isfinite(a)) {
+                bad = 1;
                 s_blk[r * (cols / 16) + g] = 0x7F;       /* the E4M3 NaN code */
                 for (int k = 0; k < 16; ++k) codes[base + k] = 0;
                 continue;

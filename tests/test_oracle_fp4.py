@@ -173,3 +173,31 @@ def test_nvfp4_nonfinite():
     q, s_blk, s_t, a, nf = O.quantize_nvfp4(x)
     assert nf == 1 and s_t == 1.0 and s_blk[1, 1] == 0x7F
     assert s_blk[0, 0] != 0x7F
+
+
+def test_nvfp4_caller_amax():
+    x = (np.random.default_rng(8).standard_normal((8, 64)) * 3.0).astype(np.float32)
+    ref = O.quantize_nvfp4(x)
+    same = O.quantize_nvfp4(x, amax_in=-float(ref[3]))        # the magnitude is used
+    assert all(np.array_equal(a, b) for a, b in zip(ref[:2], same[:2])) and ref[2] == same[2]
+    # an amax below the data's: block scales saturate at 448 and the top codes at +-6
+    q, s_blk, s_t, a, _ = O.quantize_nvfp4(x, amax_in=float(ref[3]) / 8)
+    assert a == np.float32(ref[3] / 8) and s_t == O.nvfp4_tensor_scale(a)
+    top = np.abs(x).reshape(-1, 16).max(axis=1) > a
+    assert np.all(s_blk.reshape(-1)[top] == 0x7E)
+
+
+def test_nvfp4_tiny_tensor_keeps_zero_codes():
+    """With the tensor amax in the fp32 subnormal range S_t is FLT_MAX and S_t / decode(e_b) can
+    overflow; r_b is then FLT_MAX, so zeros stay zero codes and other values saturate."""
+    x = np.zeros((1, 32), np.float32)
+    x[0, 0] = np.float32(1e-40)
+    x[0, 16] = np.float32(3e-45)
+    q, s_blk, s_t, _, _ = O.quantize_nvfp4(x)
+    codes = O.unpack_fp4(q)[0]
+    fmax = np.finfo(np.float32).max
+    assert s_t == fmax
+    e, r = O.nvfp4_block(1e-40, s_t)
+    assert O.decode(O.E4M3, e) < 1.0 and r == fmax           # S_t / decode(e_b) overflowed
+    assert np.all(codes == 0)                                # 1e-40 * FLT_MAX = 0.034 -> 0; zeros stay 0
+    assert O.nvfp4_block(3e-45, s_t) == (0, 0.0)             # scale below E4M3: zero factor
