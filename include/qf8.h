@@ -208,13 +208,52 @@ int requantize_1x128_to_128x1(const uint8_t *q, const float *scales, int64_t row
  *   rowwise   (q_row non-NULL): blocks run along a row. q_row [rows][cols],
  *             s_row [rows][cols/32]; needs cols % 32 == 0.
  *   columnwise (q_colT non-NULL): blocks run down a column and are stored transposed:
- *             q_colT [cols][rows], s_colT [cols][rows/32]; needs rows % 32 == 0.
+ *             q_colT [cols][rows], s_colT [cols][rows/32]; needs rows % 32 == 0 and
+ *             rows <= 2^23.
  * At least one direction; s_row / s_colT are required with their q. x, q_row, q_colT 16-byte
  * aligned; rows, cols <= 2^24. A block holding Inf or NaN gets scale byte 0xFF and sets
  * nonfinite. One kernel launch for either or both directions. */
 int quantize_mx_dual(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int rnd,
                      uint8_t *q_row, uint8_t *s_row, uint8_t *q_colT, uint8_t *s_colT,
                      int32_t *nonfinite, void *stream);
+
+/* ---- FP4: E2M1 elements ([MP-FP8 13.2]: values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives; a
+ * 4-bit code S.EE.M, sign in bit 3). Codes are packed two per byte, element 2j in the low
+ * nibble of byte j and element 2j+1 in the high nibble. The cast rounds to nearest even and
+ * saturates to +-6.
+ *
+ * MXFP4 ([MP-FP8 13.1]; [Ascend950 2.4]: 32 FP4 values share one E8M0 scale): the MX rule of
+ * quantize_mx_dual with emax = 2 and largest value 6: round-down X = floor(log2 amax) - 2,
+ * round-up X = ceil(log2(amax / 6)), clamped to [-127, 127]; amax = 0 gives X = -127 and zero
+ * codes; byte = X + 127 (0xFF and nonfinite for a block with Inf/NaN); code = E2M1(x / 2^X).
+ *   rowwise    (q_row non-NULL): q_row [rows][cols/2] packed along the row, s_row
+ *              [rows][cols/32]; cols % 32 == 0.
+ *   columnwise (q_colT non-NULL): blocks down a column, stored transposed: q_colT
+ *              [cols][rows/2] (rows 2j, 2j+1 of a column in byte j), s_colT [cols][rows/32];
+ *              rows % 32 == 0.
+ * At least one direction; x, q_row, q_colT 16-byte aligned; cols % 8 (BF16) or % 4 (FP32);
+ * rows, cols <= 2^24. One kernel launch. */
+int quantize_mxfp4_dual(const void *x, int dtype, int64_t rows, int64_t cols, int rnd,
+                        uint8_t *q_row, uint8_t *s_row, uint8_t *q_colT, uint8_t *s_colT,
+                        int32_t *nonfinite, void *stream);
+
+/* NVFP4 ([MP-FP8 13.2]: blocks of 16 along a row, each with an E4M3 scale amax_b / 6 that can
+ * align the block maximum to 6, under one fp32 tensor scale because E4M3's range is too
+ * small). The tensor scale maps the largest block scale onto E4M3's largest value 448:
+ *   S_t = fl32(448 * 6 / A)  (A = tensor amax; 1 for A = 0 or non-finite; FLT_MAX on overflow)
+ *   e_b = E4M3 code of fl32(fl32(amax_b / 6) * S_t), saturating      -> s_blk
+ *   r_b = fl32(S_t / decode(e_b)), FLT_MAX on overflow, 0 if e_b decodes to 0
+ *   code = E2M1(fl32(x * r_b))                                       -> q
+ * De-scaled: xhat = code * decode(e_b) / S_t. A block with Inf/NaN gets the E4M3 NaN code 0x7F
+ * and sets nonfinite. Layout: q [rows][cols/2] packed, s_blk [rows][cols/16]; cols % 16 == 0;
+ * x and q 16-byte aligned. tensor_scale (required) receives S_t, amax_out (nullable) A.
+ * amax_in (nullable, device fp32): a tensor amax from the caller (its magnitude is used, e.g.
+ * from an amax history); then x is read once and ws may be NULL. Otherwise A is measured by a
+ * read-only pass first and ws (qf8_workspace_bytes bytes, 16-byte aligned) holds its
+ * per-workgroup partials. */
+int quantize_nvfp4(const void *x, int dtype, int64_t rows, int64_t cols, const float *amax_in,
+                   uint8_t *q, uint8_t *s_blk, float *tensor_scale, float *amax_out,
+                   int32_t *nonfinite, void *ws, size_t ws_bytes, void *stream);
 
 /* ---- Dequantization and quantization error statistics -------------------------------------
  * De-scaling ([MP-FP8 8.1]: the code 22 with S = 22400 gives 22/22400; [MP-FP8 8.2]: the

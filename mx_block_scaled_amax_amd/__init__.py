@@ -20,7 +20,7 @@ __all__ = [
     "qf8_status_string", "qf8_workspace_bytes", "qf8_cast_scaled", "quantize_per_tensor",
     "DelayedState", "qf8_delayed_init", "qf8_delayed_init_ex", "qf8_delayed_reset", "quantize_delayed",
     "EST_MAX", "EST_RECENT", "EST_MEAN", "DELAYED_SPLIT_AMAX",
-    "quantize_block", "quantize_mx_dual",
+    "quantize_block", "quantize_mx_dual", "quantize_mxfp4_dual", "quantize_nvfp4",
 ]
 
 E4M3, E5M2 = 0, 1
@@ -75,6 +75,8 @@ def _load():
         "quantize_block_ex": (i32, [vp, i32, i64, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
         "requantize_1x128_to_128x1": (i32, [vp, vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]),
         "quantize_mx_dual": (i32, [vp, i32, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp]),
+        "quantize_mxfp4_dual": (i32, [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, vp]),
+        "quantize_nvfp4": (i32, [vp, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "dequantize_scaled": (i32, [vp, i64, i32, vp, vp, i32, vp, i32, vp, vp, sz, vp]),
         "dequantize_block": (i32, [vp, i64, i64, i32, i32, i32, vp, vp, i32, vp, i32, vp, vp, sz, vp]),
         "dequantize_mx": (i32, [vp, vp, i64, i64, i32, vp, i32, vp, i32, vp, vp, sz, vp]),
@@ -304,6 +306,48 @@ def quantize_mx_dual(x, fmt, rnd, rowwise=True, colwise=True, q_row=None, s_row=
                                     _ptr(q_colT), _ptr(s_colT), _ptr(nonfinite), _stream(stream, dev)),
            "quantize_mx_dual")
     return q_row, s_row, q_colT, s_colT
+
+
+def quantize_mxfp4_dual(x, rnd, rowwise=True, colwise=True, q_row=None, s_row=None, q_colT=None, s_colT=None,
+                        nonfinite=None, stream=None):
+    """MXFP4 (E2M1, 1x32 E8M0). Codes packed two per byte. Returns (q_row [rows][cols/2], s_row,
+    q_colT [cols][rows/2], s_colT); a direction not asked for is None."""
+    _dev_tensor(x, "x")
+    rows, cols = _rows_cols(x)
+    dev = x.device
+    if rowwise:
+        q_row = _out(q_row, (rows, cols // 2), torch.uint8, dev, "q_row")
+        s_row = _out(s_row, (rows, cols // 32), torch.uint8, dev, "s_row")
+    else:
+        q_row = s_row = None
+    if colwise:
+        q_colT = _out(q_colT, (cols, rows // 2), torch.uint8, dev, "q_colT")
+        s_colT = _out(s_colT, (cols, rows // 32), torch.uint8, dev, "s_colT")
+    else:
+        q_colT = s_colT = None
+    _check(_load().quantize_mxfp4_dual(_ptr(x), _dtype_code(x), rows, cols, rnd, _ptr(q_row), _ptr(s_row),
+                                       _ptr(q_colT), _ptr(s_colT), _ptr(nonfinite), _stream(stream, dev)),
+           "quantize_mxfp4_dual")
+    return q_row, s_row, q_colT, s_colT
+
+
+def quantize_nvfp4(x, amax_in=None, q=None, s_blk=None, tensor_scale=None, amax_out=None, nonfinite=None, ws=None,
+                   stream=None):
+    """NVFP4 (E2M1, 1x16 E4M3 block scales, fp32 tensor scale). Returns (q [rows][cols/2] packed,
+    s_blk [rows][cols/16], tensor_scale [1]). amax_in: optional device fp32 tensor amax."""
+    _dev_tensor(x, "x")
+    rows, cols = _rows_cols(x)
+    dev = x.device
+    q = _out(q, (rows, cols // 2), torch.uint8, dev, "q")
+    s_blk = _out(s_blk, (rows, cols // 16), torch.uint8, dev, "s_blk")
+    tensor_scale = _out(tensor_scale, (1,), torch.float32, dev, "tensor_scale")
+    if amax_in is None and ws is None:
+        ws = workspace(x)
+    _check(_load().quantize_nvfp4(_ptr(x), _dtype_code(x), rows, cols, _ptr(amax_in), _ptr(q), _ptr(s_blk),
+                                  _ptr(tensor_scale), _ptr(amax_out), _ptr(nonfinite), _ptr(ws),
+                                  0 if ws is None else ws.numel() * ws.element_size(), _stream(stream, dev)),
+           "quantize_nvfp4")
+    return q, s_blk, tensor_scale
 
 
 

@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqf8.so")
-SOURCES = ["qf8_api.cpp", "qf8_tensor.hip", "qf8_block.hip", "qf8_mx.hip", "qf8_dequant.hip", "qf8_requant.hip"]
+SOURCES = ["qf8_api.cpp", "qf8_tensor.hip", "qf8_block.hip", "qf8_mx.hip", "qf8_dequant.hip", "qf8_requant.hip", "qf8_fp4.hip"]
 ARCH = "gfx950"
 
 

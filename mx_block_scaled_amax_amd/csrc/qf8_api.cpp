@@ -13,6 +13,9 @@ constexpr int32_t kDelayedMagic = 0x51463844;  // "QF8D"
 constexpr int kMaxHistory = 4096;
 constexpr int kMaxGuard = 64;
 constexpr int64_t kMaxMxDim = 1 << 24;   // keeps every per-wave buffer offset below 2^31
+// The columnwise FP8 output of one 256-column tile spans 256 * rows bytes of one buffer
+// descriptor; the parking offset 2^31 of idle lanes must stay outside it.
+constexpr int64_t kMaxMxColRows = 1 << 23;
 
 inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 inline bool fmt_ok(int fmt) { return fmt == QF8_E4M3 || fmt == QF8_E5M2; }
@@ -244,7 +247,7 @@ int quantize_mx_dual(const void *x, int dtype, int64_t rows, int64_t cols, int f
     if (!q_row && !q_colT) return QF8_ERR_NULL;
     if ((q_row && !s_row) || (q_colT && !s_colT)) return QF8_ERR_NULL;
     if (q_row && cols % 32 != 0) return QF8_ERR_SHAPE;
-    if (q_colT && rows % 32 != 0) return QF8_ERR_SHAPE;
+    if (q_colT && (rows % 32 != 0 || rows > kMaxMxColRows)) return QF8_ERR_SHAPE;
     if (cols % (dtype == QF8_IN_BF16 ? 8 : 4) != 0) return QF8_ERR_SHAPE;
     if (rows * cols == 0) return QF8_OK;
     if (!x) return QF8_ERR_NULL;
@@ -252,6 +255,45 @@ int quantize_mx_dual(const void *x, int dtype, int64_t rows, int64_t cols, int f
         (nonfinite && !aligned(nonfinite, 4)))
         return QF8_ERR_ALIGN;
     return qf8::launch_mx(x, dtype, rows, cols, fmt, rnd, q_row, s_row, q_colT, s_colT, nonfinite, as_stream(stream));
+}
+
+int quantize_mxfp4_dual(const void *x, int dtype, int64_t rows, int64_t cols, int rnd, uint8_t *q_row, uint8_t *s_row,
+                        uint8_t *q_colT, uint8_t *s_colT, int32_t *nonfinite, void *stream) {
+    if (!dtype_ok(dtype) || (rnd != QF8_MX_ROUND_DOWN && rnd != QF8_MX_ROUND_UP)) return QF8_ERR_ENUM;
+    if (!dims_ok(rows, cols) || rows > kMaxMxDim || cols > kMaxMxDim) return QF8_ERR_SHAPE;
+    if (!q_row && !q_colT) return QF8_ERR_NULL;
+    if ((q_row && !s_row) || (q_colT && !s_colT)) return QF8_ERR_NULL;
+    if (q_row && cols % 32 != 0) return QF8_ERR_SHAPE;
+    if (q_colT && rows % 32 != 0) return QF8_ERR_SHAPE;
+    if (cols % (dtype == QF8_IN_BF16 ? 8 : 4) != 0) return QF8_ERR_SHAPE;
+    if (rows * cols == 0) return QF8_OK;
+    if (!x) return QF8_ERR_NULL;
+    if (!aligned(x, 16) || (q_row && !aligned(q_row, 16)) || (q_colT && !aligned(q_colT, 16)) ||
+        (nonfinite && !aligned(nonfinite, 4)))
+        return QF8_ERR_ALIGN;
+    return qf8::launch_mxfp4(x, dtype, rows, cols, rnd, q_row, s_row, q_colT, s_colT, nonfinite, as_stream(stream));
+}
+
+int quantize_nvfp4(const void *x, int dtype, int64_t rows, int64_t cols, const float *amax_in, uint8_t *q,
+                   uint8_t *s_blk, float *tensor_scale, float *amax_out, int32_t *nonfinite, void *ws, size_t ws_bytes,
+                   void *stream) {
+    if (!dtype_ok(dtype)) return QF8_ERR_ENUM;
+    if (!dims_ok(rows, cols) || cols % 16 != 0) return QF8_ERR_SHAPE;
+    const int64_t n = rows * cols;
+    if ((n > 0 && (!x || !q || !s_blk)) || !tensor_scale) return QF8_ERR_NULL;
+    if (!amax_in && (!ws || ws_bytes < qf8::kWorkspaceBytes)) return QF8_ERR_WORKSPACE;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(tensor_scale, 4) || (amax_in && !aligned(amax_in, 4)) ||
+        (amax_out && !aligned(amax_out, 4)) || (nonfinite && !aligned(nonfinite, 4)) || (ws && !aligned(ws, 16)))
+        return QF8_ERR_ALIGN;
+    hipStream_t s = as_stream(stream);
+    uint32_t *partials = ws ? (uint32_t *)ws + qf8::kPartialsOffsetWords : nullptr;
+    int nparts = 0;
+    if (!amax_in && n > 0) {          // the tensor amax first: the read-only amax pass
+        nparts = qf8::amax_grid(n, dtype);
+        const int r = qf8::launch_amax_partials(x, dtype, n, partials, nparts, s);
+        if (r != QF8_OK) return r;
+    }
+    return qf8::launch_nvfp4(x, dtype, n, partials, nparts, amax_in, q, s_blk, tensor_scale, amax_out, nonfinite, s);
 }
 
 }  // extern "C"

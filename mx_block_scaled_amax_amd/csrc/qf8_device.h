@@ -89,6 +89,39 @@ __device__ __forceinline__ uint32_t max_wave(uint32_t v) {
     return v;
 }
 
+// ---- workgroup-wide maxima ------------------------------------------------------------------
+// Maximum over the workgroup of NT threads, broadcast to every thread. red: NT/64 words of LDS.
+template <int NT>
+__device__ __forceinline__ uint32_t block_max_bcast(uint32_t v, uint32_t *red) {
+    constexpr int W = NT / 64;
+    v = max_wave(v);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint32_t m = red[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) m = umax(m, red[w]);
+    __syncthreads();
+    return m;
+}
+
+// Maximum of n u32 values by a workgroup of NT threads (each thread's share; combine with
+// block_max_bcast). 16 independent loads per thread in flight per round.
+template <int NT>
+__device__ __forceinline__ uint32_t fold_max(const uint32_t *__restrict__ p, int n) {
+    uint32_t m = 0;
+    for (int base = 0; base < n; base += 16 * NT) {
+        uint32_t v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            const int i = base + k * NT + (int)threadIdx.x;
+            v[k] = i < n ? p[i] : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) m = umax(m, v[k]);
+    }
+    return m;
+}
+
 // ---- fp8 conversions -----------------------------------------------------------------------
 // Two fp32 values inside +-F8max -> two bytes in half HI of `old` (other half kept).
 template <int FMT, bool HI>
@@ -238,6 +271,10 @@ __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t vo
 template <int CP = kCached>
 __device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t v) {
     __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)voff, (int)soff, CP);
+}
+template <int CP = kCached>
+__device__ __forceinline__ void buf_store2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t v) {
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, (int)voff, (int)soff, CP);
 }
 template <int CP = kCached>
 __device__ __forceinline__ void buf_store1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t v) {

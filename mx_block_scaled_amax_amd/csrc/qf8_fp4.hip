@@ -1,0 +1,453 @@
+// qf8_fp4.hip -- FP4 (E2M1) quantization: MXFP4 (1x32 blocks with E8M0 scales, rowwise and
+// columnwise from one read of x) and NVFP4 (1x16 blocks along rows with E4M3 block scales under
+// one fp32 tensor scale).
+//
+// Pages (title, section):
+//   [MP-FP8]       "混合精度与 FP8 训练" (hs-black.github.io): section 13.1 (MX rule: shared
+//                  exponent floor(log2 amax) - emax, emax of E2M1 = 2, elements divided by 2^X and
+//                  quantized with saturation; a tensor and its transpose each quantized from the
+//                  original), section 13.2 (E2M1 values 0, 0.5, 1, 1.5, 2, 3, 4, 6; NVFP4: a
+//                  block of 16 shares an E4M3 scale amax/6, plus an fp32 tensor scale).
+//   [MXFP8-recipe] "NVIDIA：Blackwell GPU MXFP8 预训练最佳实践" (51cto.com): section 4.1 (the
+//                  round-up exponent; amax = 0 gives X = -127 and zero elements).
+//   [Ascend950]    Ascend 950 low-precision format guide: section 2.4 (MXFP4 = 32 FP4 values +
+//                  one shared scale).
+//
+// Definitions (the readings the library documents):
+//   MXFP4: X = floor(log2 amax) - 2 (round-down) or the smallest X with amax / 2^X <= 6
+//     (round-up), clamped to [-127, 127]; byte = X + 127 (0xFF for a block with Inf/NaN);
+//     code = sat_rne(E2M1, x / 2^X); amax = 0 gives zero codes.
+//   NVFP4: S_t = fl32(2688 / A) (A the tensor amax; 1 for A = 0 or non-finite, FLT_MAX on
+//     overflow); e_b = sat_rne(E4M3, fl32(fl32(amax_b / 6) * S_t)); r_b = fl32(S_t / decode(e_b))
+//     (FLT_MAX on overflow, 0 when e_b decodes to 0); code = sat_rne(E2M1, fl32(x * r_b)).
+//   Codes are packed two per byte, element 2j in the low nibble of byte j.
+//
+// Conversion: v_cvt_scalef32_pk_fp4_{bf16,f32} turns two values into one byte of two E2M1 codes
+// (the first value in the low nibble) in a chosen byte of its 32-bit result, dividing by 2^E
+// where E is the exponent field of the fp32 scale operand minus 127, rounding to nearest even
+// and saturating to +-6 (Inf too). Checked on gfx950 against an exact nearest-value reference
+// for every BF16 value with all 255 scale exponents, and for every fp32 value below 16 in
+// magnitude with scale 1 (a scale of 1.5 acts as 1: only the exponent field is used). So the MX
+// path needs no separate clamp, and the NVFP4 path multiplies by r_b in fp32 first and converts
+// with scale 1.
+#include "qf8_device.h"
+#include "qf8_internal.h"
+#include "../../include/qf8.h"
+
+namespace qf8 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTileRows = 128;
+constexpr int kRowsPerWave = 32;
+constexpr int kRowsPerLane = kRowsPerWave / 2;
+constexpr uint32_t kE2M1Emax = 2;              // 6 = 1.5 * 2^2
+constexpr int kNvBlocksPerThread = 1;
+
+// E8M0 byte of an MXFP4 block from its |amax| bit pattern. For amax = 1.f * 2^E: round-down
+// X = E - 2; round-up adds 1 when 1.f > 1.5, which is one carry into the exponent field from
+// adding 0x3F (BF16, 7 mantissa bits, 1.5 = 0x40) or 0x3FFFFF (FP32). X is clamped below at -127
+// by a saturating subtraction (subnormal or zero amax); a non-finite amax gives 0xFF.
+template <bool BF16, int RND>
+__device__ __forceinline__ uint32_t fp4_mx_byte(uint32_t a) {
+    if constexpr (BF16) {
+        const uint32_t e = (RND == kRoundUp ? a + 0x3Fu : a) >> 7;
+        return a >= 0x7F80u ? 255u : __builtin_elementwise_sub_sat(e, kE2M1Emax);
+    } else {
+        const uint32_t e = (RND == kRoundUp ? a + 0x3FFFFFu : a) >> 23;
+        return a >= 0x7F800000u ? 255u : __builtin_elementwise_sub_sat(e, kE2M1Emax);
+    }
+}
+
+// Two BF16 values (one dword, the lower-addressed element in the low half) -> byte SEL of `old`.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_bf16(uint32_t old, uint32_t pair, float scale) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(old, __builtin_bit_cast(v2bf16, pair), scale, SEL);
+}
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4_f32(uint32_t old, float a, float b, float scale) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, SEL);
+}
+
+// Offset of the 8-byte unit u (rows 16u .. 16u+15, packed) of tile column c in the columnwise
+// LDS tile: one 64-byte line per column (128 rows, two codes per byte). The lines of each group
+// of 4 columns are permuted by bits 3-4 of c and the units' 16-byte pairs by bits 5-6, so that
+// the 32 lanes of a half-wave, whose columns are 8 apart, write different banks; a 16-byte pair
+// (units 2j, 2j+1) stays contiguous and in order.
+__device__ __forceinline__ int fp4_col_offset(int c, int u) {
+    return ((c ^ ((c >> 3) & 3)) << 6) + ((u ^ (((c >> 5) & 3) << 1)) << 3);
+}
+
+// ---------------------------------------------------------------------------------------------
+// MXFP4: the tiling of the MXFP8 kernel. A workgroup of 4 waves owns 128 rows x (32 * VEC)
+// columns; lane l of a wave owns VEC columns (slot l % 32) of 16 rows (half l / 32 of the wave's
+// 32 rows) in 16 x 16-byte registers. Rowwise: block amax over 32/VEC lanes by DPP, VEC codes
+// of a row leave as VEC/2 bytes. Columnwise: a column's block spans lanes l and l ^ 32; each
+// lane packs its 16 rows into 8 bytes per column, staged in LDS, and the workgroup writes each
+// column's 64 bytes of q_colT (and the E8M0 bytes of both directions) after one barrier.
+template <bool BF16, int RND, bool ROW, bool COL>
+__global__ __launch_bounds__(kThreads) void mxfp4_kernel(const void *__restrict__ x, int rows, int cols,
+                                                         uint8_t *__restrict__ q_row, uint8_t *__restrict__ s_row,
+                                                         uint8_t *__restrict__ q_colT, uint8_t *__restrict__ s_colT,
+                                                         int32_t *nonfinite, int tiles_c, int tiles, int per_xcd) {
+    constexpr int VEC = BF16 ? 8 : 4;            // values per lane per row (one 16-byte load)
+    constexpr int ESZ = BF16 ? 2 : 4;
+    constexpr int LPB = 32 / VEC;                // lanes per rowwise block
+    constexpr int RPL = kRowsPerLane;
+    constexpr int TILE_C = 32 * VEC;
+    constexpr int NBLK = TILE_C / 32;            // rowwise blocks per tile row
+    constexpr uint32_t ABS = BF16 ? 0x7FFF7FFFu : 0x7FFFFFFFu;
+
+    __shared__ __attribute__((aligned(16))) uint8_t colbuf[COL ? TILE_C * (kTileRows / 2) : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t scol[COL ? TILE_C * 4 : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t srow[(ROW && COL) ? kTileRows * NBLK : 16];
+
+    const int b = blockIdx.x, xcd = b & 7, local = b >> 3;
+    const int t = xcd * per_xcd + local;
+    if (local >= per_xcd || t >= tiles) return;  // whole workgroup idle
+    const int tr = t / tiles_c, tc = t - tr * tiles_c;
+    const int tr0 = tr * kTileRows, ct0 = tc * TILE_C;
+    const int ncv = cols - ct0 < TILE_C ? cols - ct0 : TILE_C;
+    const int trows = rows - tr0 < kTileRows ? rows - tr0 : kTileRows;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63, half = lane >> 5, slot = lane & 31;
+    const int r0 = tr0 + wave * kRowsPerWave;
+    uint32_t seen = 0;
+
+    if (r0 < rows) {
+        const int c0 = ct0 + slot * VEC;
+        const bool active = c0 < cols;           // rowwise blocks are whole: cols % 32 == 0
+        const int wrows = rows - r0 < kRowsPerWave ? rows - r0 : kRowsPerWave;
+
+        const uint32_t rowbytes = (uint32_t)cols * ESZ;
+        const __amdgpu_buffer_rsrc_t xr = make_rsrc((const char *)x + (size_t)r0 * rowbytes,
+                                                    (uint32_t)wrows * rowbytes);
+        const uint32_t xvo = active ? (uint32_t)(half * RPL) * rowbytes + (uint32_t)c0 * ESZ : kOutOfRange;
+        uint32_t d[RPL][4];
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const uint4 v = buf_load16<kNonTemporal>(xr, xvo, (uint32_t)i * rowbytes);
+            d[i][0] = v.x; d[i][1] = v.y; d[i][2] = v.z; d[i][3] = v.w;
+        }
+        uint32_t cmax[4] = {0, 0, 0, 0};
+
+        if constexpr (ROW) {
+            const uint32_t qstride = (uint32_t)cols / 2;
+            const __amdgpu_buffer_rsrc_t qr = make_rsrc(q_row + (size_t)r0 * qstride, (uint32_t)wrows * qstride);
+            const uint32_t qvo = active ? (uint32_t)(half * RPL) * qstride + c0 / 2 : kOutOfRange;
+            const uint32_t sstride = cols / 32;
+            const __amdgpu_buffer_rsrc_t sr = make_rsrc(s_row + (size_t)r0 * sstride, (uint32_t)wrows * sstride);
+            const uint32_t svo = active ? (uint32_t)(half * RPL) * sstride + c0 / 32 : kOutOfRange;
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                uint32_t m[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) m[k] = d[i][k] & ABS;
+                if constexpr (COL) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) cmax[k] = BF16 ? pk_max_u16(cmax[k], m[k]) : umax(cmax[k], m[k]);
+                }
+                uint32_t a;
+                if constexpr (BF16) {
+                    const uint32_t mm = pk_max_u16(pk_max_u16(m[0], m[1]), pk_max_u16(m[2], m[3]));
+                    a = max_quad(umax(mm & 0xFFFFu, mm >> 16));
+                } else {
+                    a = max_oct(umax(umax(m[0], m[1]), umax(m[2], m[3])));
+                }
+                if constexpr (!COL) seen = umax(seen, a);
+                const uint32_t byte = fp4_mx_byte<BF16, RND>(a);
+                const float sc = __uint_as_float(byte << 23);
+                if constexpr (BF16) {
+                    uint32_t o = fp4_bf16<0>(0u, d[i][0], sc);
+                    o = fp4_bf16<1>(o, d[i][1], sc);
+                    o = fp4_bf16<2>(o, d[i][2], sc);
+                    o = fp4_bf16<3>(o, d[i][3], sc);
+                    if (a == 0u) o = 0u;                            // all-zero block: zero codes
+                    buf_store4(qr, qvo, (uint32_t)i * qstride, o);
+                } else {
+                    uint32_t o = fp4_f32<0>(0u, __uint_as_float(d[i][0]), __uint_as_float(d[i][1]), sc);
+                    o = fp4_f32<1>(o, __uint_as_float(d[i][2]), __uint_as_float(d[i][3]), sc);
+                    if (a == 0u) o = 0u;
+                    buf_store2(qr, qvo, (uint32_t)i * qstride, o);
+                }
+                if constexpr (COL) {
+                    srow[(wave * kRowsPerWave + half * RPL + i) * NBLK + slot / LPB] = (uint8_t)byte;
+                } else {
+                    if ((slot & (LPB - 1)) == (i & (LPB - 1))) buf_store1(sr, svo, (uint32_t)i * sstride, byte);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < RPL; ++i)
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    cmax[k] = BF16 ? pk_max_u16(cmax[k], d[i][k] & ABS) : umax(cmax[k], d[i][k] & ABS);
+        }
+
+        if constexpr (COL) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t other = (uint32_t)__shfl_xor((int)cmax[k], 32);
+                cmax[k] = BF16 ? pk_max_u16(cmax[k], other) : umax(cmax[k], other);
+            }
+            const int unit = wave * 2 + half;    // 16-row chunk of the tile = 8-byte unit
+            if constexpr (BF16) {
+                const uint32_t mm = pk_max_u16(pk_max_u16(cmax[0], cmax[1]), pk_max_u16(cmax[2], cmax[3]));
+                seen = umax(mm & 0xFFFFu, mm >> 16);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {     // dword k holds columns 2k (low half) and 2k+1
+                    const uint32_t alo = cmax[k] & 0xFFFFu, ahi = cmax[k] >> 16;
+                    const uint32_t blo = fp4_mx_byte<true, RND>(alo), bhi = fp4_mx_byte<true, RND>(ahi);
+                    const float slo = __uint_as_float(blo << 23), shi = __uint_as_float(bhi << 23);
+                    uint32_t olo[2] = {0u, 0u}, ohi[2] = {0u, 0u};
+#pragma unroll
+                    for (int g = 0; g < 8; ++g) {     // rows 2g, 2g+1 of the lane -> byte g
+                        const uint32_t l = __builtin_amdgcn_perm(d[2 * g + 1][k], d[2 * g][k], 0x05040100u);
+                        const uint32_t h = __builtin_amdgcn_perm(d[2 * g + 1][k], d[2 * g][k], 0x07060302u);
+                        switch (g & 3) {
+                            case 0: olo[g >> 2] = fp4_bf16<0>(olo[g >> 2], l, slo); ohi[g >> 2] = fp4_bf16<0>(ohi[g >> 2], h, shi); break;
+                            case 1: olo[g >> 2] = fp4_bf16<1>(olo[g >> 2], l, slo); ohi[g >> 2] = fp4_bf16<1>(ohi[g >> 2], h, shi); break;
+                            case 2: olo[g >> 2] = fp4_bf16<2>(olo[g >> 2], l, slo); ohi[g >> 2] = fp4_bf16<2>(ohi[g >> 2], h, shi); break;
+                            default: olo[g >> 2] = fp4_bf16<3>(olo[g >> 2], l, slo); ohi[g >> 2] = fp4_bf16<3>(ohi[g >> 2], h, shi); break;
+                        }
+                    }
+                    if (alo == 0u) olo[0] = olo[1] = 0u;
+                    if (ahi == 0u) ohi[0] = ohi[1] = 0u;
+                    const int clo = slot * VEC + 2 * k;
+                    *(uint2 *)(colbuf + fp4_col_offset(clo, unit)) = make_uint2(olo[0], olo[1]);
+                    *(uint2 *)(colbuf + fp4_col_offset(clo + 1, unit)) = make_uint2(ohi[0], ohi[1]);
+                    if (half == 0) {
+                        scol[clo * 4 + wave] = (uint8_t)blo;
+                        scol[(clo + 1) * 4 + wave] = (uint8_t)bhi;
+                    }
+                }
+            } else {
+                seen = umax(umax(cmax[0], cmax[1]), umax(cmax[2], cmax[3]));
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {     // tile column slot * 4 + k
+                    const uint32_t a = cmax[k];
+                    const uint32_t byte = fp4_mx_byte<false, RND>(a);
+                    const float sc = __uint_as_float(byte << 23);
+                    uint32_t o[2] = {0u, 0u};
+#pragma unroll
+                    for (int g = 0; g < 8; ++g) {
+                        const float f0 = __uint_as_float(d[2 * g][k]), f1 = __uint_as_float(d[2 * g + 1][k]);
+                        switch (g & 3) {
+                            case 0: o[g >> 2] = fp4_f32<0>(o[g >> 2], f0, f1, sc); break;
+                            case 1: o[g >> 2] = fp4_f32<1>(o[g >> 2], f0, f1, sc); break;
+                            case 2: o[g >> 2] = fp4_f32<2>(o[g >> 2], f0, f1, sc); break;
+                            default: o[g >> 2] = fp4_f32<3>(o[g >> 2], f0, f1, sc); break;
+                        }
+                    }
+                    if (a == 0u) o[0] = o[1] = 0u;
+                    const int c = slot * VEC + k;
+                    *(uint2 *)(colbuf + fp4_col_offset(c, unit)) = make_uint2(o[0], o[1]);
+                    if (half == 0) scol[c * 4 + wave] = (uint8_t)byte;
+                }
+            }
+        }
+    }
+
+    if constexpr (COL) {
+        __syncthreads();
+        // q_colT: column c of the tile -> q_colT[ct0 + c][tr0/2 .. (tr0 + trows)/2), 16 bytes a lane
+        const uint32_t cstride = (uint32_t)rows / 2;
+        const __amdgpu_buffer_rsrc_t qc = make_rsrc(q_colT + (size_t)ct0 * cstride + tr0 / 2,
+                                                    (uint32_t)ncv * cstride - tr0 / 2);
+#pragma unroll
+        for (int e = threadIdx.x; e < TILE_C * 4; e += kThreads) {
+            const int c = e >> 2, j = e & 3;     // 16-byte chunk j = rows 32j .. 32j+31
+            const uint4 v = *(const uint4 *)(colbuf + fp4_col_offset(c, 2 * j));
+            const uint32_t vo = (c < ncv && 32 * j < trows) ? (uint32_t)c * cstride + 16 * j : kOutOfRange;
+            buf_store16<kNonTemporal>(qc, vo, 0u, v);
+        }
+        const uint32_t srb = (uint32_t)rows / 32;
+        const int nb = trows / 32;
+        const __amdgpu_buffer_rsrc_t scr = make_rsrc(s_colT + (size_t)ct0 * srb + tr0 / 32, (uint32_t)ncv * srb - tr0 / 32);
+        const bool whole_c = nb == 4 && (srb & 3u) == 0 && (((uintptr_t)s_colT) & 3u) == 0;
+        for (int c = threadIdx.x; c < TILE_C; c += kThreads) {
+            const uint32_t w = *(const uint32_t *)(scol + c * 4);
+            if (whole_c) {
+                buf_store4(scr, c < ncv ? (uint32_t)c * srb : kOutOfRange, 0u, w);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    buf_store1(scr, (c < ncv && j < nb) ? (uint32_t)c * srb + j : kOutOfRange, 0u, w >> (8 * j));
+            }
+        }
+        if constexpr (ROW) {
+            const uint32_t ssb = (uint32_t)cols / 32;
+            const int nbl = ncv / 32;
+            const __amdgpu_buffer_rsrc_t srr = make_rsrc(s_row + (size_t)tr0 * ssb + ct0 / 32,
+                                                         (uint32_t)trows * ssb - ct0 / 32);
+            const bool whole_r = nbl == NBLK && (ssb % NBLK) == 0 && (((uintptr_t)s_row) % NBLK) == 0;
+            for (int r = threadIdx.x; r < kTileRows; r += kThreads) {
+                const bool rv = r < trows;
+                if constexpr (NBLK == 8) {
+                    const uint2 w = *(const uint2 *)(srow + r * 8);
+                    if (whole_r) {
+                        buf_store8(srr, rv ? (uint32_t)r * ssb : kOutOfRange, 0u, w.x, w.y);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j)
+                            buf_store1(srr, (rv && j < nbl) ? (uint32_t)r * ssb + j : kOutOfRange, 0u,
+                                       (j < 4 ? w.x : w.y) >> (8 * (j & 3)));
+                    }
+                } else {
+                    const uint32_t w = *(const uint32_t *)(srow + r * 4);
+                    if (whole_r) {
+                        buf_store4(srr, rv ? (uint32_t)r * ssb : kOutOfRange, 0u, w);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            buf_store1(srr, (rv && j < nbl) ? (uint32_t)r * ssb + j : kOutOfRange, 0u, w >> (8 * j));
+                    }
+                }
+            }
+        }
+    }
+    if (seen >= (BF16 ? 0x7F80u : 0x7F800000u) && nonfinite) *nonfinite = 1;
+}
+
+template <bool BF16, int RND>
+void launch_mxfp4_dirs(const void *x, int rows, int cols, uint8_t *q_row, uint8_t *s_row, uint8_t *q_colT,
+                       uint8_t *s_colT, int32_t *nonfinite, hipStream_t s) {
+    constexpr int VEC = BF16 ? 8 : 4;
+    const int tiles_r = (rows + kTileRows - 1) / kTileRows;
+    const int tiles_c = (cols + 32 * VEC - 1) / (32 * VEC);
+    const int tiles = tiles_r * tiles_c;
+    const int per_xcd = (tiles + 7) / 8;
+    const dim3 grid(8 * per_xcd), block(kThreads);
+    if (q_row && q_colT)
+        hipLaunchKernelGGL((mxfp4_kernel<BF16, RND, true, true>), grid, block, 0, s, x, rows, cols, q_row, s_row,
+                           q_colT, s_colT, nonfinite, tiles_c, tiles, per_xcd);
+    else if (q_row)
+        hipLaunchKernelGGL((mxfp4_kernel<BF16, RND, true, false>), grid, block, 0, s, x, rows, cols, q_row, s_row,
+                           q_colT, s_colT, nonfinite, tiles_c, tiles, per_xcd);
+    else
+        hipLaunchKernelGGL((mxfp4_kernel<BF16, RND, false, true>), grid, block, 0, s, x, rows, cols, q_row, s_row,
+                           q_colT, s_colT, nonfinite, tiles_c, tiles, per_xcd);
+}
+
+// ---------------------------------------------------------------------------------------------
+// NVFP4: one thread per block of 16 consecutive elements (cols % 16 == 0, so a block never
+// crosses a row and block b of the flattened tensor is row b / (cols/16)). Every workgroup first
+// takes the tensor amax (the caller's value, or the fold of the amax pass's partials) and S_t;
+// a thread then loads its 32 (BF16) or 64 (FP32) bytes, takes the block amax, the E4M3 block
+// scale (two IEEE divisions per block: amax_b / 6 and S_t / decode(e_b)) and writes 8 bytes of
+// codes and the scale byte.
+
+__device__ __forceinline__ float nv_tensor_scale(uint32_t abits) {
+    if (abits == 0u || abits >= 0x7F800000u) return 1.0f;
+    const float s = 2688.0f / __uint_as_float(abits);                // 448 * 6 / A
+    return s > 3.40282346638528859812e+38f ? 3.40282346638528859812e+38f : s;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void nvfp4_kernel(const void *__restrict__ x, int64_t nblk,
+                                                         const uint32_t *__restrict__ partials, int nparts,
+                                                         const float *amax_in, uint8_t *__restrict__ q,
+                                                         uint8_t *__restrict__ s_blk, float *tensor_scale,
+                                                         float *amax_out, int32_t *nonfinite) {
+    __shared__ uint32_t red[kThreads / 64];
+    const uint32_t A = amax_in ? (__float_as_uint(*amax_in) & 0x7FFFFFFFu)
+                               : block_max_bcast<kThreads>(fold_max<kThreads>(partials, nparts), red);
+    const float st = nv_tensor_scale(A);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        if (tensor_scale) *tensor_scale = st;
+        if (amax_out) *amax_out = __uint_as_float(A);
+        if (nonfinite && A >= 0x7F800000u) *nonfinite = 1;
+    }
+    constexpr int NV = BF16 ? 2 : 4;             // 16-byte loads per block
+    const uint4 *xv = (const uint4 *)x;
+    bool bad = false;
+    for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblk; blk += (int64_t)gridDim.x * kThreads) {
+        uint4 v[NV];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) v[j] = ld_stream(xv + blk * NV + j);
+        float f[16];
+        if constexpr (BF16) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    f[8 * j + 2 * k] = __uint_as_float(w[k] << 16);
+                    f[8 * j + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                f[4 * j] = __uint_as_float(v[j].x); f[4 * j + 1] = __uint_as_float(v[j].y);
+                f[4 * j + 2] = __uint_as_float(v[j].z); f[4 * j + 3] = __uint_as_float(v[j].w);
+            }
+        }
+        uint32_t a = 0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) a = umax(a, __float_as_uint(f[k]) & 0x7FFFFFFFu);
+        uint32_t e;
+        float r;
+        if (a >= 0x7F800000u) {                  // Inf/NaN block: E4M3 NaN scale code
+            bad = true;
+            e = 0x7Fu;
+            r = 0.0f;
+        } else {
+            const float dd = __uint_as_float(a) / 6.0f;
+            const float p = fminf(dd * st, 448.0f);                     // saturating E4M3 input
+            e = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p, p, 0, false) & 0xFFu;
+            const float dec = __builtin_amdgcn_cvt_f32_fp8((int)e, 0);
+            r = dec == 0.0f ? 0.0f : fminf(st / dec, 3.40282346638528859812e+38f);
+        }
+        uint32_t o0 = 0u, o1 = 0u;
+        o0 = fp4_f32<0>(o0, f[0] * r, f[1] * r, 1.0f);
+        o0 = fp4_f32<1>(o0, f[2] * r, f[3] * r, 1.0f);
+        o0 = fp4_f32<2>(o0, f[4] * r, f[5] * r, 1.0f);
+        o0 = fp4_f32<3>(o0, f[6] * r, f[7] * r, 1.0f);
+        o1 = fp4_f32<0>(o1, f[8] * r, f[9] * r, 1.0f);
+        o1 = fp4_f32<1>(o1, f[10] * r, f[11] * r, 1.0f);
+        o1 = fp4_f32<2>(o1, f[12] * r, f[13] * r, 1.0f);
+        o1 = fp4_f32<3>(o1, f[14] * r, f[15] * r, 1.0f);
+        st_stream((uint2 *)q + blk, make_uint2(o0, o1));
+        s_blk[blk] = (uint8_t)e;
+    }
+    if (bad && nonfinite) *nonfinite = 1;
+}
+
+int nvfp4_grid(int64_t nblk) {
+    int64_t g = (nblk + (int64_t)kThreads * kNvBlocksPerThread - 1) / ((int64_t)kThreads * kNvBlocksPerThread);
+    if (g > kMaxStreamGrid) g = kMaxStreamGrid;
+    return (int)(g < 1 ? 1 : g);
+}
+
+}  // namespace
+
+int launch_mxfp4(const void *x, int dtype, int64_t rows, int64_t cols, int rnd, uint8_t *q_row, uint8_t *s_row,
+                 uint8_t *q_colT, uint8_t *s_colT, int32_t *nonfinite, hipStream_t s) {
+    if (rows == 0 || cols == 0) return QF8_OK;
+    const int r = (int)rows, c = (int)cols;
+    if (dtype == QF8_IN_BF16) {
+        if (rnd == QF8_MX_ROUND_DOWN) launch_mxfp4_dirs<true, kRoundDown>(x, r, c, q_row, s_row, q_colT, s_colT, nonfinite, s);
+        else launch_mxfp4_dirs<true, kRoundUp>(x, r, c, q_row, s_row, q_colT, s_colT, nonfinite, s);
+    } else {
+        if (rnd == QF8_MX_ROUND_DOWN) launch_mxfp4_dirs<false, kRoundDown>(x, r, c, q_row, s_row, q_colT, s_colT, nonfinite, s);
+        else launch_mxfp4_dirs<false, kRoundUp>(x, r, c, q_row, s_row, q_colT, s_colT, nonfinite, s);
+    }
+    return hipGetLastError() == hipSuccess ? QF8_OK : QF8_ERR_HIP;
+}
+
+
+int launch_nvfp4(const void *x, int dtype, int64_t n, const uint32_t *partials, int nparts, const float *amax_in,
+                 uint8_t *q, uint8_t *s_blk, float *tensor_scale, float *amax_out, int32_t *nonfinite, hipStream_t s) {
+    const int64_t nblk = n / 16;
+    const int grid = nvfp4_grid(nblk);
+    if (dtype == QF8_IN_BF16)
+        hipLaunchKernelGGL(nvfp4_kernel<true>, dim3(grid), dim3(kThreads), 0, s, x, nblk, partials, nparts, amax_in, q,
+                           s_blk, tensor_scale, amax_out, nonfinite);
+    else
+        hipLaunchKernelGGL(nvfp4_kernel<false>, dim3(grid), dim3(kThreads), 0, s, x, nblk, partials, nparts, amax_in,
+                           q, s_blk, tensor_scale, amax_out, nonfinite);
+    return hipGetLastError() == hipSuccess ? QF8_OK : QF8_ERR_HIP;
+}
+
+}  // namespace qf8

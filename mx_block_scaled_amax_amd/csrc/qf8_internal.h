@@ -43,6 +43,10 @@ int launch_per_tensor_onepass(const void *x, int dtype, int64_t n, int fmt, uint
                               float *amax_out, float *scale_out, int32_t *nonfinite, uint32_t *amax_bits_out,
                               int grid, hipStream_t s);
 
+int launch_mxfp4(const void *x, int dtype, int64_t rows, int64_t cols, int rnd, uint8_t *q_row, uint8_t *s_row,
+                 uint8_t *q_colT, uint8_t *s_colT, int32_t *nonfinite, hipStream_t s);
+int launch_nvfp4(const void *x, int dtype, int64_t n, const uint32_t *partials, int nparts, const float *amax_in,
+                 uint8_t *q, uint8_t *s_blk, float *tensor_scale, float *amax_out, int32_t *nonfinite, hipStream_t s);
 int launch_amax_partials(const void *x, int dtype, int64_t n, uint32_t *partials, int grid, hipStream_t s);
 int launch_cast_current(const void *x, int dtype, int64_t n, int fmt, uint8_t *q, const uint32_t *partials,
                         int nparts, float *amax_out, float *scale_out, int32_t *nonfinite, int grid, hipStream_t s);

@@ -47,38 +47,6 @@ constexpr int kOpRegSlabs = 48;                 //   slabs held in VGPRs (4 VGPR
 constexpr int kOpLdsSlabs = 16;                 //   slabs held in LDS (8 KiB each)
 constexpr uint32_t kAbs16x2 = 0x7FFF7FFFu;
 
-// Maximum over the workgroup of NT threads, broadcast to every thread. red: NT/64 words of LDS.
-template <int NT = kThreads>
-__device__ __forceinline__ uint32_t block_max_bcast(uint32_t v, uint32_t *red) {
-    constexpr int W = NT / 64;
-    v = max_wave(v);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    uint32_t m = red[0];
-#pragma unroll
-    for (int w = 1; w < W; ++w) m = umax(m, red[w]);
-    __syncthreads();
-    return m;
-}
-
-// Maximum of n u32 values by a workgroup of NT threads (each thread's share; combine with
-// block_max_bcast). 16 independent loads per thread in flight per round.
-template <int NT = kThreads>
-__device__ __forceinline__ uint32_t fold_max(const uint32_t *__restrict__ p, int n) {
-    uint32_t m = 0;
-    for (int base = 0; base < n; base += 16 * NT) {
-        uint32_t v[16];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int i = base + k * NT + (int)threadIdx.x;
-            v[k] = i < n ? p[i] : 0u;
-        }
-#pragma unroll
-        for (int k = 0; k < 16; ++k) m = umax(m, v[k]);
-    }
-    return m;
-}
-
 // |x| maximum of one 16-byte vector, accumulated as bit patterns (BF16 kept packed).
 template <bool BF16>
 __device__ __forceinline__ uint32_t vec_absmax(uint32_t acc, uint4 v) {
@@ -238,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void cast_current_kernel(const void *__re
     const int64_t nruns = run_count(nvec);
     Run<BF16> r;
     r.load(x, nvec, blockIdx.x);               // the first run's loads overlap the partials fold
-    uint32_t m = block_max_bcast(fold_max(partials, nparts), red);
+    uint32_t m = block_max_bcast<kThreads>(fold_max<kThreads>(partials, nparts), red);
     const float s = scale_from_amax_bits<FMT>(m);
     r.template cast_store<FMT>(q, s);
     for (int64_t run = blockIdx.x + gridDim.x; run < nruns; run += gridDim.x) {

@@ -56,6 +56,31 @@ def test_mx_argument_errors():
     assert f(FAKE, 0, -1, 64, 0, 0, FAKE, FAKE, None, None, None, None) == SHAPE
     assert f(MISALIGNED, 0, 64, 64, 0, 0, FAKE, FAKE, None, None, None, None) == ALIGN
     assert f(None, 0, 64, 64, 0, 0, FAKE, FAKE, None, None, None, None) == NULL
+    # columnwise FP8 is limited to 2^23 rows (one tile's output must stay below 2^31 bytes)
+    assert f(FAKE, 0, (1 << 23) + 32, 256, 0, 0, None, None, FAKE, FAKE, None, None) == SHAPE
+
+
+def test_fp4_argument_errors():
+    f = lib().quantize_mxfp4_dual
+    assert f(FAKE, 3, 64, 64, 0, FAKE, FAKE, None, None, None, None) == ENUM       # bad dtype
+    assert f(FAKE, 0, 64, 64, 5, FAKE, FAKE, None, None, None, None) == ENUM       # bad rounding
+    assert f(FAKE, 0, 64, 64, 0, None, None, None, None, None, None) == NULL       # no direction
+    assert f(FAKE, 0, 64, 64, 0, None, None, FAKE, None, None, None) == NULL       # q without scales
+    assert f(FAKE, 0, 64, 48, 0, FAKE, FAKE, None, None, None, None) == SHAPE      # rowwise cols % 32
+    assert f(FAKE, 0, 40, 64, 0, None, None, FAKE, FAKE, None, None) == SHAPE      # colwise rows % 32
+    assert f(FAKE, 0, 64, 36, 0, None, None, FAKE, FAKE, None, None) == SHAPE      # BF16 cols % 8
+    assert f(FAKE, 0, (1 << 24) + 32, 32, 0, FAKE, FAKE, None, None, None, None) == SHAPE
+    assert f(MISALIGNED, 0, 64, 64, 0, FAKE, FAKE, None, None, None, None) == ALIGN
+    assert f(None, 0, 64, 64, 0, FAKE, FAKE, None, None, None, None) == NULL
+    assert f(None, 0, 0, 64, 0, FAKE, FAKE, None, None, None, None) == OK          # empty: nothing to do
+    g = lib().quantize_nvfp4
+    assert g(FAKE, 2, 4, 16, None, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 20, None) == ENUM
+    assert g(FAKE, 0, 4, 24, None, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 20, None) == SHAPE   # cols % 16
+    assert g(FAKE, 0, 4, 16, None, FAKE, None, FAKE, None, None, FAKE, 1 << 20, None) == NULL    # no s_blk
+    assert g(FAKE, 0, 4, 16, None, FAKE, FAKE, None, None, None, FAKE, 1 << 20, None) == NULL    # no S_t out
+    assert g(FAKE, 0, 4, 16, None, FAKE, FAKE, FAKE, None, None, None, 0, None) == WS            # amax pass needs ws
+    assert g(FAKE, 0, 4, 16, None, FAKE, FAKE, FAKE, None, None, FAKE, 64, None) == WS
+    assert g(FAKE, 0, 4, 16, None, MISALIGNED, FAKE, FAKE, None, None, FAKE, 1 << 20, None) == ALIGN
 
 
 def test_per_tensor_argument_errors():

@@ -1,0 +1,279 @@
+"""GPU parity of the FP4 quantizers against the CPU oracle, byte-exact on packed E2M1 codes and on
+the scale bytes (E8M0 for MXFP4, E4M3 for NVFP4) and bit-exact on the NVFP4 tensor scale.
+
+MXFP4 (quantize_mxfp4_dual):
+  * an exhaustive domain: for every BF16 amax exponent (mantissas on both sides of the 1.5
+    round-up boundary) blocks holding every BF16 magnitude not above that amax, random signs,
+    rowwise and columnwise, both rounding modes;
+  * small and ragged shapes over several 128-row tiles, BF16 and FP32, single directions,
+    all-zero blocks and -0, extreme magnitudes, Inf/NaN (flag and 0xFF scale);
+  * the full 16384 x 4096 gradient workload in both rounding modes, every byte.
+NVFP4 (quantize_nvfp4):
+  * blocks whose amax spans the E4M3 block-scale range under S_t = 1 (a 2688 in the tensor),
+    each holding every BF16 magnitude down to amax / 4096 with random signs;
+  * random BF16 and FP32 tensors of several shapes (S_t != 1), a caller-given amax equal to and
+    below the measured one, an all-zero tensor, a tensor with a subnormal amax, Inf/NaN;
+  * the full 16384 x 4096 workload, every byte.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mx_block_scaled_amax_amd as qf8
+import oracle as O
+from synthetic import bf16_bits, mx_gradient, small_tensor
+from qf8_test_utils import assert_bytes_equal, host, parallel_row_slabs, to_device
+
+pytestmark = pytest.mark.gpu
+
+RND = [O.ROUND_DOWN, O.ROUND_UP]
+RID = ["down", "up"]
+
+
+# ---- MXFP4 -------------------------------------------------------------------------------------
+
+def run_mx(x, rnd, row=True, col=True):
+    xd = to_device(x)
+    nf = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rows, cols = x.shape
+    out = {}                                  # poisoned, so that any byte left unwritten shows
+    if row:
+        out["q_row"] = torch.full((rows, cols // 2), 0xA5, dtype=torch.uint8, device="cuda")
+        out["s_row"] = torch.full((rows, cols // 32), 0xA5, dtype=torch.uint8, device="cuda")
+    if col:
+        out["q_colT"] = torch.full((cols, rows // 2), 0xA5, dtype=torch.uint8, device="cuda")
+        out["s_colT"] = torch.full((cols, rows // 32), 0xA5, dtype=torch.uint8, device="cuda")
+    r = qf8.quantize_mxfp4_dual(xd, rnd, rowwise=row, colwise=col, nonfinite=nf, **out)
+    torch.cuda.synchronize()
+    return [None if t is None else host(t) for t in r] + [int(nf.item())]
+
+
+def check_mx(x, rnd, row=True, col=True, tag=""):
+    g = run_mx(x, rnd, row, col)
+    w = O.quantize_mxfp4(x, rnd, row=row, col=col)
+    for i, name in enumerate(("q_row", "s_row", "q_colT", "s_colT")):
+        if w[i] is None:
+            assert g[i] is None
+            continue
+        assert_bytes_equal(g[i], w[i], name, f" [{tag} rnd={rnd} shape={x.shape}]")
+    assert g[4] == w[4]
+
+
+def exhaustive_blocks(seed=0):
+    """[G, 32] BF16 blocks: for each amax A (every exponent field, mantissas 0x00/0x40/0x41/0x7F
+    and a few subnormals) every BF16 magnitude <= A, 31 per block next to A, random signs, A at
+    a varying position."""
+    rng = np.random.default_rng(seed)
+    mags = np.arange(0, 0x7F80, dtype=np.uint32)
+    amaxes = [a for e in range(1, 255) for a in ((e << 7) | 0x00, (e << 7) | 0x40, (e << 7) | 0x41, (e << 7) | 0x7F)]
+    amaxes += [0x0001, 0x0040, 0x007F]
+    blocks = []
+    for a in amaxes:
+        below = mags[: a + 1]
+        ng = -(-len(below) // 31)
+        body = np.resize(below, ng * 31).reshape(ng, 31)
+        blocks.append(np.concatenate([np.full((ng, 1), a, np.uint32), body], axis=1))
+    b = np.concatenate(blocks, axis=0)
+    b |= (rng.integers(0, 2, b.shape, dtype=np.uint32) << 15)
+    shift = np.arange(b.shape[0]) % 32
+    cols = (np.arange(32)[None, :] - shift[:, None]) % 32
+    b = np.take_along_axis(b, cols, axis=1)
+    pad = (-b.shape[0]) % 64
+    if pad:
+        b = np.concatenate([b, np.zeros((pad, 32), np.uint32)], axis=0)
+    return b.astype(np.uint16)
+
+
+@pytest.fixture(scope="module")
+def exhaustive():
+    return exhaustive_blocks()
+
+
+@pytest.mark.parametrize("rnd", RND, ids=RID)
+def test_mxfp4_exhaustive_rowwise(exhaustive, rnd):
+    check_mx(exhaustive, rnd, row=True, col=False, tag="exhaustive-row")
+
+
+@pytest.mark.parametrize("rnd", RND, ids=RID)
+def test_mxfp4_exhaustive_columnwise(exhaustive, rnd):
+    check_mx(np.ascontiguousarray(exhaustive.T), rnd, row=False, col=True, tag="exhaustive-col")
+
+
+@pytest.mark.parametrize("shape", [(32, 32), (64, 96), (128, 512), (256, 1024), (160, 544), (96, 1056)])
+@pytest.mark.parametrize("rnd", RND, ids=RID)
+def test_mxfp4_dual_small_bf16(shape, rnd):
+    check_mx(mx_gradient(*shape, seed=sum(shape)), rnd, tag="dual-bf16")
+
+
+@pytest.mark.parametrize("shape", [(32, 32), (64, 288), (160, 544)])
+@pytest.mark.parametrize("rnd", RND, ids=RID)
+def test_mxfp4_dual_small_fp32(shape, rnd):
+    rng = np.random.default_rng(5)
+    x = (rng.laplace(0, 1e-3, shape) * np.where(rng.random(shape) < 0.01, 1e4, 1.0)).astype(np.float32)
+    check_mx(x, rnd, tag="dual-fp32")
+
+
+@pytest.mark.parametrize("rnd", RND, ids=RID)
+def test_mxfp4_single_direction_and_ragged(rnd):
+    check_mx(small_tensor(37, 64, seed=3), rnd, row=True, col=False, tag="row-ragged-rows")
+    check_mx(small_tensor(130, 96, seed=4), rnd, row=True, col=False, tag="row-ragged-rows")
+    check_mx(small_tensor(64, 40, seed=5), rnd, row=False, col=True, tag="col-narrow")
+    check_mx(small_tensor(96, 520, seed=6), rnd, row=False, col=True, tag="col-ragged-cols")
+    x = (np.random.default_rng(7).standard_normal((96, 36)) * 10).astype(np.float32)
+    check_mx(x, rnd, row=False, col=True, tag="col-fp32-ragged")
+
+
+def test_mxfp4_zero_blocks_and_extremes():
+    x = np.zeros((64, 64), np.uint16)
+    x[3, 5] = 0x8000                     # -0 inside an all-zero block -> zero codes
+    x[40, 40] = 0x4000
+    x[41, 41] = 0x8001                   # negative subnormal
+    x[0, 32:] = 0x7F7F                   # largest finite BF16
+    x[1, 32:] = 0x0001                   # smallest subnormal
+    x[2, 32] = 0x7F7F
+    x[2, 33] = 0x0001
+    x[5, 32:] = 0x80FF
+    for rnd in RND:
+        check_mx(x, rnd, tag="zeros-extremes")
+
+
+def test_mxfp4_nonfinite():
+    x = small_tensor(64, 64, seed=9)
+    x[7, 9] = 0x7F80
+    x[50, 33] = 0x7FC1
+    g = run_mx(x, O.ROUND_UP)
+    w = O.quantize_mxfp4(x, O.ROUND_UP)
+    assert g[4] == 1 and w[4] == 1
+    assert g[1][7, 0] == 0xFF and g[1][50, 1] == 0xFF and g[3][9, 0] == 0xFF and g[3][33, 1] == 0xFF
+    ok = np.ones(g[1].shape, bool)
+    ok[7, 0] = ok[50, 1] = False
+    assert np.array_equal(g[1][ok], w[1][ok])
+    qok = np.repeat(ok, 16, axis=1)      # 16 packed bytes per block of 32
+    assert np.array_equal(g[0][qok], w[0][qok])
+
+
+@pytest.fixture(scope="module")
+def gradient_full():
+    return mx_gradient()
+
+
+@pytest.mark.parametrize("rnd", RND, ids=RID)
+def test_mxfp4_full_size_gradient(gradient_full, rnd):
+    x = gradient_full
+    rows, cols = x.shape
+    g = run_mx(x, rnd)
+    parts = parallel_row_slabs(lambda r0, r1: O.quantize_mxfp4(x[r0:r1], rnd), rows, 1024)
+    assert_bytes_equal(g[0], np.concatenate([p[0] for p in parts], axis=0), "q_row", " [16384x4096]")
+    assert_bytes_equal(g[1], np.concatenate([p[1] for p in parts], axis=0), "s_row", " [16384x4096]")
+    assert_bytes_equal(g[2], np.concatenate([p[2] for p in parts], axis=1), "q_colT", " [16384x4096]")
+    assert_bytes_equal(g[3], np.concatenate([p[3] for p in parts], axis=1), "s_colT", " [16384x4096]")
+    assert g[4] == 0
+
+
+# ---- NVFP4 -------------------------------------------------------------------------------------
+
+def run_nv(x, amax_in=None):
+    xd = to_device(x)
+    rows, cols = x.shape
+    q = torch.full((rows, cols // 2), 0xA5, dtype=torch.uint8, device="cuda")
+    s = torch.full((rows, cols // 16), 0xA5, dtype=torch.uint8, device="cuda")
+    st = torch.full((1,), -1.0, dtype=torch.float32, device="cuda")
+    a = torch.full((1,), -1.0, dtype=torch.float32, device="cuda")
+    nf = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ain = None if amax_in is None else torch.tensor([amax_in], dtype=torch.float32, device="cuda")
+    qf8.quantize_nvfp4(xd, amax_in=ain, q=q, s_blk=s, tensor_scale=st, amax_out=a, nonfinite=nf)
+    torch.cuda.synchronize()
+    return host(q), host(s), np.float32(st.item()), np.float32(a.item()), int(nf.item())
+
+
+def check_nv(x, amax_in=None, tag=""):
+    g = run_nv(x, amax_in)
+    w = O.quantize_nvfp4(x, amax_in=amax_in)
+    extra = f" [{tag} shape={x.shape}]"
+    assert g[2] == w[2], f"tensor scale{extra}: {g[2]!r} vs {w[2]!r}"
+    assert g[3] == w[3] and g[4] == w[4], extra
+    assert_bytes_equal(g[1], w[1], "s_blk", extra)
+    assert_bytes_equal(g[0], w[0], "q", extra)
+    return g
+
+
+def nv_domain(seed=1):
+    """[G, 16] BF16 blocks under S_t = 1: a 2688 in the first block; block amaxes with every
+    exponent from 2^-10 to 2^10 and mantissas 0x00/0x20/0x40/0x41/0x55/0x7F, each block holding
+    15 BF16 magnitudes between amax / 4096 and amax (all of them over consecutive blocks)."""
+    rng = np.random.default_rng(seed)
+    blocks = [np.array([0x4528] + [0] * 15, np.uint32)]          # 2688.0
+    for e in range(127 - 10, 127 + 11):                          # amax < 2048 < 2688
+        for m in (0x00, 0x20, 0x40, 0x41, 0x55, 0x7F):
+            a = (e << 7) | m
+            lo = a - (12 << 7)
+            below = np.arange(max(lo, 0), a + 1, dtype=np.uint32)
+            ng = -(-len(below) // 15)
+            body = np.resize(below, ng * 15).reshape(ng, 15)
+            blocks.append(np.concatenate([np.full((ng, 1), a, np.uint32), body], axis=1).reshape(-1))
+    b = np.concatenate(blocks).reshape(-1, 16)
+    b |= (rng.integers(0, 2, b.shape, dtype=np.uint32) << 15)
+    b[0, 0] = 0x4528
+    pad = (-b.shape[0]) % 8
+    if pad:
+        b = np.concatenate([b, np.zeros((pad, 16), np.uint32)], axis=0)
+    return b.reshape(-1, 128).astype(np.uint16)
+
+
+def test_nvfp4_block_scale_domain():
+    x = nv_domain()
+    g = check_nv(x, tag="domain")
+    assert g[2] == 1.0
+
+
+@pytest.mark.parametrize("shape", [(1, 16), (16, 16), (64, 256), (33, 48), (1000, 1008)])
+def test_nvfp4_random_bf16(shape):
+    x = mx_gradient(*shape, seed=sum(shape) + 1)
+    check_nv(x, tag="bf16")
+
+
+@pytest.mark.parametrize("shape,scale", [((32, 64), 1.0), ((129, 496), 1e-4), ((7, 4096), 3e5)])
+def test_nvfp4_random_fp32(shape, scale):
+    rng = np.random.default_rng(shape[0])
+    x = (rng.standard_normal(shape) * np.exp(rng.uniform(-4, 4, (shape[0], 1))) * scale).astype(np.float32)
+    check_nv(x, tag="fp32")
+
+
+def test_nvfp4_caller_amax():
+    x = mx_gradient(64, 256, seed=12)
+    a = float(O.amax(x))
+    check_nv(x, amax_in=a, tag="amax_in=measured")
+    check_nv(x, amax_in=-a, tag="amax_in=-measured")
+    check_nv(x, amax_in=a / 16, tag="amax_in=measured/16")
+    check_nv(x, amax_in=a * 1000, tag="amax_in=measured*1000")
+
+
+def test_nvfp4_zero_tiny_and_nonfinite():
+    check_nv(np.zeros((4, 64), np.uint16), tag="zeros")
+    t = np.zeros((2, 32), np.float32)
+    t[0, 0] = np.float32(1e-40)
+    t[1, 16] = np.float32(-3e-45)
+    t[1, 17] = np.float32(-0.0)
+    check_nv(t, tag="tiny")
+    x = small_tensor(16, 64, seed=3)
+    x[5, 20] = 0x7FC0
+    x[9, 63] = 0xFF80
+    g = run_nv(x)
+    w = O.quantize_nvfp4(x)
+    assert g[4] == 1 and w[4] == 1 and g[2] == w[2] == 1.0
+    assert g[1][5, 1] == 0x7F and g[1][9, 3] == 0x7F
+    ok = np.ones(g[1].shape, bool)
+    ok[5, 1] = ok[9, 3] = False
+    assert np.array_equal(g[1][ok], w[1][ok])
+    assert np.array_equal(g[0][np.repeat(ok, 8, axis=1)], w[0][np.repeat(ok, 8, axis=1)])
+
+
+def test_nvfp4_full_size(gradient_full):
+    x = gradient_full
+    rows, _ = x.shape
+    g = run_nv(x)
+    a = float(O.amax(x))
+    parts = parallel_row_slabs(lambda r0, r1: O.quantize_nvfp4(x[r0:r1], amax_in=a), rows, 1024)
+    assert g[2] == parts[0][2] and g[3] == np.float32(a) and g[4] == 0
+    assert_bytes_equal(g[1], np.concatenate([p[1] for p in parts], axis=0), "s_blk", " [16384x4096]")
+    assert_bytes_equal(g[0], np.concatenate([p[0] for p in parts], axis=0), "q", " [16384x4096]")
