@@ -429,13 +429,39 @@ def run_suite(args):
                             reps, warm)))
     del xads, qa2, qT2
 
-    # dequantization (and fused error statistics) of the MX dual result and the per-tensor result
+    # FP4 on the same gradient workload: MXFP4 dual / rowwise, NVFP4 (amax pass + cast, or a
+    # caller-given amax and one read). Algorithmic bytes count x once.
     xg = to_dev(mx_gradient(ROWS, COLS, seed=4))
+    N = ROWS * COLS
+    f4r = torch.empty((ROWS, COLS // 2), dtype=torch.uint8, device="cuda")
+    f4rs = torch.empty((ROWS, COLS // 32), dtype=torch.uint8, device="cuda")
+    f4c = torch.empty((COLS, ROWS // 2), dtype=torch.uint8, device="cuda")
+    f4cs = torch.empty((COLS, ROWS // 32), dtype=torch.uint8, device="cuda")
+    for rnd, rname in ((qf8.ROUND_DOWN, "round-down"), (qf8.ROUND_UP, "round-up")):
+        res.append(_summ(f"mxfp4 dual 16384x4096 bf16 {rname}", 2 * N + N + N // 16,
+                         _timed(torch, stream, [PreCall(L.quantize_mxfp4_dual, vp(xg), 0, ROWS, COLS, rnd, vp(f4r),
+                                                        vp(f4rs), vp(f4c), vp(f4cs), None, sp)], reps, warm)))
+    res.append(_summ("mxfp4 rowwise 16384x4096 bf16 round-down", 2 * N + N // 2 + N // 32,
+                     _timed(torch, stream, [PreCall(L.quantize_mxfp4_dual, vp(xg), 0, ROWS, COLS, qf8.ROUND_DOWN, vp(f4r),
+                                                    vp(f4rs), None, None, None, sp)], reps, warm)))
+    del f4c, f4cs
+    nvs = torch.empty((ROWS, COLS // 16), dtype=torch.uint8, device="cuda")
+    nvt = torch.empty(1, dtype=torch.float32, device="cuda")
+    nva = torch.empty(1, dtype=torch.float32, device="cuda")
+    wsn = qf8.workspace(xg)
+    res.append(_summ("nvfp4 16384x4096 bf16 (amax pass + cast)", 2 * N + N // 2 + N // 16,
+                     _timed(torch, stream, [PreCall(L.quantize_nvfp4, vp(xg), 0, ROWS, COLS, None, vp(f4r), vp(nvs),
+                                                    vp(nvt), vp(nva), None, vp(wsn), wsn.numel(), sp)], reps, warm)))
+    res.append(_summ("nvfp4 16384x4096 bf16 (caller amax, one read)", 2 * N + N // 2 + N // 16,
+                     _timed(torch, stream, [PreCall(L.quantize_nvfp4, vp(xg), 0, ROWS, COLS, vp(nva), vp(f4r), vp(nvs),
+                                                    vp(nvt), None, None, None, 0, sp)], reps, warm)))
+    del f4r, f4rs, nvs
+
+    # dequantization (and fused error statistics) of the MX dual result and the per-tensor result
     q_row, s_row, q_colT, s_colT = qf8.quantize_mx_dual(xg, qf8.E4M3, qf8.ROUND_DOWN)
     o16 = torch.empty((ROWS, COLS), dtype=torch.bfloat16, device="cuda")
     st = torch.zeros(8, dtype=torch.int64, device="cuda")
     wsg = qf8.workspace(xg)
-    N = ROWS * COLS
     res.append(_summ("dequant mx rowwise 16384x4096 -> bf16", N + N // 32 + 2 * N,
                      _timed(torch, stream, [PreCall(L.dequantize_mx, vp(q_row), vp(s_row), ROWS, COLS, qf8.E4M3, vp(o16), 0,
                                                     None, 0, None, None, 0, sp)], reps, warm)))
