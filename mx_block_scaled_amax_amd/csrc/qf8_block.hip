@@ -36,10 +36,18 @@ __device__ __forceinline__ uint32_t vec_absmax_bits(uint4 v) {
     }
 }
 
-template <bool BF16, int FMT>
+// Codes of one 16-byte input vector. STREAM: non-temporal store (the 1x128 kernel); the 128x128
+// kernel, whose workgroup writes a 128-row block in 128-byte pieces spread over 128 rows, runs
+// faster with ordinary cached stores (63 vs 68 us on 7168x18432), measured both ways.
+template <bool BF16, int FMT, bool STREAM>
 __device__ __forceinline__ void store_cast(uint8_t *q, int64_t off, uint4 v, float s) {
-    if constexpr (BF16) st_stream((uint2 *)(q + off), cast8_bf16<FMT>(v, s));
-    else st_stream((uint32_t *)(q + off), cast4_f32<FMT>(v, s));
+    if constexpr (STREAM) {
+        if constexpr (BF16) st_stream((uint2 *)(q + off), cast8_bf16<FMT>(v, s));
+        else st_stream((uint32_t *)(q + off), cast4_f32<FMT>(v, s));
+    } else {
+        if constexpr (BF16) *(uint2 *)(q + off) = cast8_bf16<FMT>(v, s);
+        else *(uint32_t *)(q + off) = cast4_f32<FMT>(v, s);
+    }
 }
 
 template <int FMT, bool POW2>
@@ -78,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void block_1x128_kernel(const uint16_t *_
         if constexpr (!BF16) m = umax(m, (uint32_t)__shfl_xor((int)m, 16));
         const float s = group_scale<FMT, POW2>(m);
         if (ok[it]) {
-            store_cast<BF16, FMT>(q, off[it], v[it], s);
+            store_cast<BF16, FMT, true>(q, off[it], v[it], s);
             if (sub == 0) {
                 scales[g[it]] = s;
                 if (amax) amax[g[it]] = __uint_as_float(m);
@@ -120,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void block_128x128_kernel(const uint16_t 
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
         const int64_t r = bi * 128 + p * RPP + rr;
-        if (cok && r < rows) store_cast<BF16, FMT>(q, r * cols + col, v[p], s);
+        if (cok && r < rows) store_cast<BF16, FMT, false>(q, r * cols + col, v[p], s);
     }
     if (threadIdx.x == 0) {
         scales[blockIdx.x] = s;
