@@ -248,9 +248,10 @@ int quantize_mxfp4_dual(const void *x, int dtype, int64_t rows, int64_t cols, in
  * and sets nonfinite. Layout: q [rows][cols/2] packed, s_blk [rows][cols/16]; cols % 16 == 0;
  * x and q 16-byte aligned. tensor_scale (required) receives S_t, amax_out (nullable) A.
  * amax_in (nullable, device fp32): a tensor amax from the caller (its magnitude is used, e.g.
- * from an amax history); then x is read once and ws may be NULL. Otherwise A is measured by a
- * read-only pass first and ws (qf8_workspace_bytes bytes, 16-byte aligned) holds its
- * per-workgroup partials. */
+ * from an amax history); then x is read once and ws may be NULL. Otherwise A is measured: from
+ * 2^22 elements by the single-pass kernel of quantize_per_tensor (x held on chip across a grid
+ * barrier, read once), below that by a read-only pass first. ws: qf8_workspace_bytes bytes,
+ * 16-byte aligned, zero-initialised once as described at qf8_workspace_bytes. */
 int quantize_nvfp4(const void *x, int dtype, int64_t rows, int64_t cols, const float *amax_in,
                    uint8_t *q, uint8_t *s_blk, float *tensor_scale, float *amax_out,
                    int32_t *nonfinite, void *ws, size_t ws_bytes, void *stream);

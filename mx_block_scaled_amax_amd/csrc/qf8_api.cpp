@@ -288,7 +288,13 @@ int quantize_nvfp4(const void *x, int dtype, int64_t rows, int64_t cols, const f
     hipStream_t s = as_stream(stream);
     uint32_t *partials = ws ? (uint32_t *)ws + qf8::kPartialsOffsetWords : nullptr;
     int nparts = 0;
-    if (!amax_in && n > 0) {          // the tensor amax first: the read-only amax pass
+    if (!amax_in && n > 0) {
+        // large tensors: amax and cast in one read (the single-pass kernel of per-tensor scaling)
+        const int g1 = qf8::onepass_grid(n, dtype);
+        if (g1 > 0)
+            return qf8::launch_nvfp4_onepass(x, dtype, n, q, s_blk, (uint32_t *)ws, tensor_scale, amax_out, nonfinite,
+                                             g1, s);
+        // otherwise the read-only amax pass first
         nparts = qf8::amax_grid(n, dtype);
         const int r = qf8::launch_amax_partials(x, dtype, n, partials, nparts, s);
         if (r != QF8_OK) return r;

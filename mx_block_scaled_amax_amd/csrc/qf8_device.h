@@ -237,6 +237,34 @@ __device__ __forceinline__ uint32_t mx_saturate_codes(uint32_t w) {
 }
 
 
+// ---- NVFP4 block scaling (E2M1 codes under an E4M3 block scale and an fp32 tensor scale) -----
+// S_t = fl32(448 * 6 / A) from the tensor |amax| bits (1 for A = 0 or non-finite, FLT_MAX on
+// overflow); per block: e_b = E4M3 code of fl32(fl32(amax_b / 6) * S_t) (clamped to 448 first,
+// so the exact-RNE fp8 convert saturates), r_b = fl32(S_t / decode(e_b)) (FLT_MAX on overflow,
+// 0 when e_b decodes to 0); a block with Inf/NaN gets the E4M3 NaN code 0x7F and r_b = 0.
+__device__ __forceinline__ float nv_tensor_scale(uint32_t abits) {
+    if (abits == 0u || abits >= 0x7F800000u) return 1.0f;
+    const float s = 2688.0f / __uint_as_float(abits);
+    return s > 3.40282346638528859812e+38f ? 3.40282346638528859812e+38f : s;
+}
+__device__ __forceinline__ uint32_t nv_block_scale(uint32_t amax_bits, float st, float &r) {
+    if (amax_bits >= 0x7F800000u) {
+        r = 0.0f;
+        return 0x7Fu;
+    }
+    const float p = fminf(__uint_as_float(amax_bits) / 6.0f * st, 448.0f);
+    const uint32_t e = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p, p, 0, false) & 0xFFu;
+    const float dec = __builtin_amdgcn_cvt_f32_fp8((int)e, 0);
+    r = dec == 0.0f ? 0.0f : fminf(st / dec, 3.40282346638528859812e+38f);
+    return e;
+}
+// Two fp32 values -> one byte of two E2M1 codes (first value in the low nibble) in byte SEL of
+// `old`: v_cvt_scalef32_pk_fp4_f32 with scale 1 rounds to nearest even and saturates to +-6.
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_fp4_f32(uint32_t old, float a, float b, float scale) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, SEL);
+}
+
 // ---- buffer resources ------------------------------------------------------------------------
 // Raw buffer descriptors (stride 0): addresses are base + voffset (per lane) + soffset (uniform),
 // and any access whose offset reaches num_records is dropped (loads return 0). Kernels set the

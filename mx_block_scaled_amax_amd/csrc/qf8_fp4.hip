@@ -66,7 +66,7 @@ __device__ __forceinline__ uint32_t fp4_bf16(uint32_t old, uint32_t pair, float 
 }
 template <int SEL>
 __device__ __forceinline__ uint32_t fp4_f32(uint32_t old, float a, float b, float scale) {
-    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, SEL);
+    return cvt_fp4_f32<SEL>(old, a, b, scale);
 }
 
 // Offset of the 8-byte unit u (rows 16u .. 16u+15, packed) of tile column c in the columnwise
@@ -337,11 +337,6 @@ void launch_mxfp4_dirs(const void *x, int rows, int cols, uint8_t *q_row, uint8_
 // scale (two IEEE divisions per block: amax_b / 6 and S_t / decode(e_b)) and writes 8 bytes of
 // codes and the scale byte.
 
-__device__ __forceinline__ float nv_tensor_scale(uint32_t abits) {
-    if (abits == 0u || abits >= 0x7F800000u) return 1.0f;
-    const float s = 2688.0f / __uint_as_float(abits);                // 448 * 6 / A
-    return s > 3.40282346638528859812e+38f ? 3.40282346638528859812e+38f : s;
-}
 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void nvfp4_kernel(const void *__restrict__ x, int64_t nblk,
@@ -386,19 +381,9 @@ __global__ __launch_bounds__(kThreads) void nvfp4_kernel(const void *__restrict_
         uint32_t a = 0;
 #pragma unroll
         for (int k = 0; k < 16; ++k) a = umax(a, __float_as_uint(f[k]) & 0x7FFFFFFFu);
-        uint32_t e;
+        if (a >= 0x7F800000u) bad = true;        // Inf/NaN block: E4M3 NaN scale code
         float r;
-        if (a >= 0x7F800000u) {                  // Inf/NaN block: E4M3 NaN scale code
-            bad = true;
-            e = 0x7Fu;
-            r = 0.0f;
-        } else {
-            const float dd = __uint_as_float(a) / 6.0f;
-            const float p = fminf(dd * st, 448.0f);                     // saturating E4M3 input
-            e = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p, p, 0, false) & 0xFFu;
-            const float dec = __builtin_amdgcn_cvt_f32_fp8((int)e, 0);
-            r = dec == 0.0f ? 0.0f : fminf(st / dec, 3.40282346638528859812e+38f);
-        }
+        const uint32_t e = nv_block_scale(a, st, r);
         uint32_t o0 = 0u, o1 = 0u;
         o0 = fp4_f32<0>(o0, f[0] * r, f[1] * r, 1.0f);
         o0 = fp4_f32<1>(o0, f[2] * r, f[3] * r, 1.0f);

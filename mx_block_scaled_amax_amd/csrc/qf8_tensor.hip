@@ -45,6 +45,8 @@ constexpr int kFinalizeThreads = 256;           // single-workgroup finalize: on
 constexpr int kOpThreads = 512;                 // single-pass kernel: 8 waves, 2 per SIMD
 constexpr int kOpRegSlabs = 48;                 //   slabs held in VGPRs (4 VGPRs each)
 constexpr int kOpLdsSlabs = 16;                 //   slabs held in LDS (8 KiB each)
+constexpr int kOpRegSlabsNv = 42;               // NVFP4 output: its block arithmetic needs more
+constexpr int kOpLdsSlabsNv = 18;               //   VGPRs, so fewer register slabs, more LDS ones
 constexpr uint32_t kAbs16x2 = 0x7FFF7FFFu;
 
 // |x| maximum of one 16-byte vector, accumulated as bit patterns (BF16 kept packed).
@@ -381,6 +383,47 @@ __device__ __forceinline__ void cast_vec_store(__amdgpu_buffer_rsrc_t w, uint32_
     }
 }
 
+// The single-pass kernel's outputs. kOpFp8: per-tensor FP8 cast (8 or 4 code bytes per 16-byte
+// input vector). kOpNvfp4: NVFP4 with the tensor scale S_t: a 16-element block is 2 (BF16) or 4
+// (FP32) vectors held by adjacent lanes, whose amax meets by DPP; each lane writes its 4 or 2
+// code bytes and the block's first lane the E4M3 scale byte. All lanes must be active.
+constexpr int kOpFp8 = 0, kOpNvfp4 = 1;
+template <int OP, bool BF16>
+constexpr uint32_t op_out_bytes() { return OP == kOpFp8 ? (BF16 ? 8u : 4u) : (BF16 ? 4u : 2u); }
+
+template <bool BF16>
+__device__ __forceinline__ void nv_vec_store(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t wsb, uint32_t vrel,
+                                             uint4 v, float st) {
+    uint32_t a = acc_to_f32bits<BF16>(vec_absmax<BF16>(0u, v));
+    if constexpr (BF16) a = umax(a, dpp_mov<0xB1>(a));         // lanes 2j, 2j+1 hold one block
+    else a = max_quad(a);                                       // lanes 4j .. 4j+3
+    float r;
+    const uint32_t e = nv_block_scale(a, st, r);
+    if constexpr (BF16) {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t o = 0u;
+        o = cvt_fp4_f32<0>(o, __uint_as_float(w[0] << 16) * r, __uint_as_float(w[0] & 0xFFFF0000u) * r, 1.0f);
+        o = cvt_fp4_f32<1>(o, __uint_as_float(w[1] << 16) * r, __uint_as_float(w[1] & 0xFFFF0000u) * r, 1.0f);
+        o = cvt_fp4_f32<2>(o, __uint_as_float(w[2] << 16) * r, __uint_as_float(w[2] & 0xFFFF0000u) * r, 1.0f);
+        o = cvt_fp4_f32<3>(o, __uint_as_float(w[3] << 16) * r, __uint_as_float(w[3] & 0xFFFF0000u) * r, 1.0f);
+        buf_store4<kNonTemporal>(wq, vrel * 4u, 0u, o);
+        if ((vrel & 1u) == 0u) buf_store1(wsb, vrel >> 1, 0u, e);
+    } else {
+        uint32_t o = 0u;
+        o = cvt_fp4_f32<0>(o, __uint_as_float(v.x) * r, __uint_as_float(v.y) * r, 1.0f);
+        o = cvt_fp4_f32<1>(o, __uint_as_float(v.z) * r, __uint_as_float(v.w) * r, 1.0f);
+        buf_store2(wq, vrel * 2u, 0u, o);
+        if ((vrel & 3u) == 0u) buf_store1(wsb, vrel >> 2, 0u, e);
+    }
+}
+
+template <int OP, bool BF16, int FMT>
+__device__ __forceinline__ void op_vec_store(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t wsb, uint32_t vrel,
+                                             uint4 v, float s) {
+    if constexpr (OP == kOpFp8) cast_vec_store<BF16, FMT>(wq, vrel * op_out_bytes<OP, BF16>(), v, s);
+    else nv_vec_store<BF16>(wq, wsb, vrel, v, s);
+}
+
 // Byte count of the vectors [first, nvec) clamped to one buffer descriptor's range.
 __device__ __forceinline__ uint32_t span_bytes(int64_t first, int64_t nvec, uint32_t bytes_per_vec) {
     const int64_t rem = nvec - first;
@@ -391,10 +434,11 @@ __device__ __forceinline__ uint32_t span_bytes(int64_t first, int64_t nvec, uint
 
 // The eight slabs k, k + 1, ..., k + 7 of workgroup j (slab k of workgroup j is k * G + j):
 // load, and cast + store when CAST, return the |x| maximum (accumulator form).
-template <bool BF16, int FMT, bool CAST>
-__device__ __forceinline__ uint32_t stream_slabs8(const uint4 *x, int64_t nvec, uint8_t *q, int64_t k, int j, int G,
-                                                  float s) {
-    constexpr uint32_t kOut = BF16 ? 8u : 4u;
+template <int OP, bool BF16, int FMT, bool CAST>
+__device__ __forceinline__ uint32_t stream_slabs8(const uint4 *x, int64_t nvec, uint8_t *q, uint8_t *sb, int64_t k,
+                                                  int j, int G, float s) {
+    constexpr uint32_t kOut = op_out_bytes<OP, BF16>();
+    constexpr uint32_t kVpb = BF16 ? 2u : 4u;                      // vectors per NVFP4 block
     const uint32_t step = (uint32_t)G * kOpThreads * 16u;
     const int64_t first = (k * G + j) * kOpThreads;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(x + first, span_bytes(first, nvec, 16u));
@@ -404,8 +448,10 @@ __device__ __forceinline__ uint32_t stream_slabs8(const uint4 *x, int64_t nvec, 
     uint32_t a = 0;
     if constexpr (CAST) {
         const __amdgpu_buffer_rsrc_t w = make_rsrc(q + first * kOut, span_bytes(first, nvec, kOut));
+        const __amdgpu_buffer_rsrc_t wsb = make_rsrc(OP == kOpNvfp4 ? sb + first / kVpb : q,
+                                                     OP == kOpNvfp4 ? span_bytes(first, nvec, 1u) / kVpb : 0u);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) cast_vec_store<BF16, FMT>(w, i * (step / 16u * kOut) + threadIdx.x * kOut, v[i], s);
+        for (int i = 0; i < 8; ++i) op_vec_store<OP, BF16, FMT>(w, wsb, i * (step / 16u) + threadIdx.x, v[i], s);
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) a = vec_absmax<BF16>(a, v[i]);
@@ -413,12 +459,14 @@ __device__ __forceinline__ uint32_t stream_slabs8(const uint4 *x, int64_t nvec, 
     return a;
 }
 
-template <bool BF16, int FMT>
+template <bool BF16, int FMT, int OP>
 __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
-        const void *__restrict__ x, int64_t n, int64_t nvec, uint8_t *__restrict__ q, uint32_t *ws,
-        float *amax_out, float *scale_out, int32_t *nonfinite, uint32_t *amax_bits_out) {
-    constexpr int KR = kOpRegSlabs, KL = kOpLdsSlabs;
-    constexpr uint32_t kOut = BF16 ? 8u : 4u;
+        const void *__restrict__ x, int64_t n, int64_t nvec, uint8_t *__restrict__ q, uint8_t *__restrict__ sb,
+        uint32_t *ws, float *amax_out, float *scale_out, int32_t *nonfinite, uint32_t *amax_bits_out) {
+    constexpr int KR = OP == kOpFp8 ? kOpRegSlabs : kOpRegSlabsNv;
+    constexpr int KL = OP == kOpFp8 ? kOpLdsSlabs : kOpLdsSlabsNv;
+    constexpr uint32_t kOut = op_out_bytes<OP, BF16>();
+    constexpr uint32_t kVpb = BF16 ? 2u : 4u;
     __shared__ uint4 held[KL * kOpThreads];
     __shared__ uint32_t red[kOpThreads / 64];
     __shared__ uint32_t sh[3];
@@ -429,6 +477,7 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
     // held slabs: offsets below (KR + KL) * G * kOpThreads * 16 < 2^32 (G <= kBarMaxGroups)
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(xv, span_bytes(0, nvec, 16u));
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(q, span_bytes(0, nvec, kOut));
+    const __amdgpu_buffer_rsrc_t rsb = make_rsrc(OP == kOpNvfp4 ? sb : q, OP == kOpNvfp4 ? span_bytes(0, nvec, 1u) / kVpb : 0u);
     const uint32_t step = (uint32_t)G * kOpThreads * 16u;        // bytes between a workgroup's slabs
     const uint32_t base = ((uint32_t)b * kOpThreads + t) * 16u;
 
@@ -436,7 +485,7 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
     // register-held slabs, all loads in flight together
     uint32_t a0 = 0;
     for (int64_t k = KR + KL; k * G + b < nslabs; k += 8)
-        a0 = acc_max<BF16>(a0, stream_slabs8<BF16, FMT, false>(xv, nvec, q, k, b, G, 0.f));
+        a0 = acc_max<BF16>(a0, stream_slabs8<OP, BF16, FMT, false>(xv, nvec, q, sb, k, b, G, 0.f));
     a0 = acc_to_f32bits<BF16>(a0);
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
 #pragma unroll
@@ -507,15 +556,15 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
     if (role == 1 && t < G && t != b)               // release: one line per thread (G <= kOpThreads)
         xres = __hip_atomic_exchange(lines + (size_t)t * (kBarLineWords / 2), kLineReleased | m, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
-    const float s = scale_from_amax_bits<FMT>(m);
+    const float s = OP == kOpFp8 ? scale_from_amax_bits<FMT>(m) : nv_tensor_scale(m);
 
-    // pass 2: cast the held slabs, then re-read and cast the rest
-    const uint32_t qbase = ((uint32_t)b * kOpThreads + t) * kOut, qstep = step / 16u * kOut;
+    // pass 2: cast the held slabs, then re-read and cast the rest (vector indices: vbase + k * vstep)
+    const uint32_t vbase = (uint32_t)b * kOpThreads + t, vstep = step / 16u;
 #pragma unroll
-    for (int k = 0; k < KR; ++k) cast_vec_store<BF16, FMT>(rq, qbase + k * qstep, R[k], s);
+    for (int k = 0; k < KR; ++k) op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + k * vstep, R[k], s);
 #pragma unroll
-    for (int k = 0; k < KL; ++k) cast_vec_store<BF16, FMT>(rq, qbase + (KR + k) * qstep, held[k * kOpThreads + t], s);
-    for (int64_t k = KR + KL; k * G + b < nslabs; k += 8) stream_slabs8<BF16, FMT, true>(xv, nvec, q, k, b, G, s);
+    for (int k = 0; k < KL; ++k) op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + (KR + k) * vstep, held[k * kOpThreads + t], s);
+    for (int64_t k = KR + KL; k * G + b < nslabs; k += 8) stream_slabs8<OP, BF16, FMT, true>(xv, nvec, q, sb, k, b, G, s);
 
     if (role == 1) {
         if (xres == kLineGaveUp) {                  // that workgroup exited: clear its line, cast its slabs
@@ -525,9 +574,11 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
         __syncthreads();
         const uint32_t ng = sh[2];
         for (uint32_t i = 0; i < ng; ++i)
-            for (int64_t k = 0; k * G + gave_up[i] < nslabs; k += 8) stream_slabs8<BF16, FMT, true>(xv, nvec, q, k, gave_up[i], G, s);
-        for (int64_t e = nvec * vec_elems<BF16>() + t; e < n; e += kOpThreads)
-            q[e] = (uint8_t)cast1<FMT>(__uint_as_float(elem_bits<BF16>(x, e)), s);
+            for (int64_t k = 0; k * G + gave_up[i] < nslabs; k += 8)
+                stream_slabs8<OP, BF16, FMT, true>(xv, nvec, q, sb, k, gave_up[i], G, s);
+        if constexpr (OP == kOpFp8)          // NVFP4 sizes are whole vectors (n % 16 == 0)
+            for (int64_t e = nvec * vec_elems<BF16>() + t; e < n; e += kOpThreads)
+                q[e] = (uint8_t)cast1<FMT>(__uint_as_float(elem_bits<BF16>(x, e)), s);
         if (t == 0) {
             if (amax_out) *amax_out = __uint_as_float(m);
             if (scale_out) *scale_out = s;
@@ -646,8 +697,8 @@ int query_onepass_grid(int dtype) {
     std::atomic<int> &slot = g_onepass_grid[dev][dtype == QF8_IN_BF16 ? 0 : 1];
     int g = slot.load(std::memory_order_relaxed);
     if (g != 0) return g;
-    const void *fn = dtype == QF8_IN_BF16 ? (const void *)per_tensor_onepass_kernel<true, kE4M3>
-                                          : (const void *)per_tensor_onepass_kernel<false, kE4M3>;
+    const void *fn = dtype == QF8_IN_BF16 ? (const void *)per_tensor_onepass_kernel<true, kE4M3, kOpFp8>
+                                          : (const void *)per_tensor_onepass_kernel<false, kE4M3, kOpFp8>;
     g = -1;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
         hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kOpThreads, 0) == hipSuccess && occ >= 1 && cus >= 1)
@@ -668,8 +719,20 @@ int launch_per_tensor_onepass(const void *x, int dtype, int64_t n, int fmt, uint
                               int grid, hipStream_t s) {
     const int64_t nvec = vec_count(n, dtype);
     QF8_DISPATCH_DT_FMT(dtype, fmt,
-        hipLaunchKernelGGL((per_tensor_onepass_kernel<BF16, FMT>), dim3(grid), dim3(kOpThreads), 0, s, x, n, nvec, q,
-                           ws, amax_out, scale_out, nonfinite, amax_bits_out));
+        hipLaunchKernelGGL((per_tensor_onepass_kernel<BF16, FMT, kOpFp8>), dim3(grid), dim3(kOpThreads), 0, s, x, n,
+                           nvec, q, (uint8_t *)nullptr, ws, amax_out, scale_out, nonfinite, amax_bits_out));
+    return status_after_launch();
+}
+
+int launch_nvfp4_onepass(const void *x, int dtype, int64_t n, uint8_t *q, uint8_t *s_blk, uint32_t *ws,
+                         float *tensor_scale, float *amax_out, int32_t *nonfinite, int grid, hipStream_t s) {
+    const int64_t nvec = vec_count(n, dtype);
+    if (dtype == QF8_IN_BF16)
+        hipLaunchKernelGGL((per_tensor_onepass_kernel<true, kE4M3, kOpNvfp4>), dim3(grid), dim3(kOpThreads), 0, s, x, n,
+                           nvec, q, s_blk, ws, amax_out, tensor_scale, nonfinite, (uint32_t *)nullptr);
+    else
+        hipLaunchKernelGGL((per_tensor_onepass_kernel<false, kE4M3, kOpNvfp4>), dim3(grid), dim3(kOpThreads), 0, s, x,
+                           n, nvec, q, s_blk, ws, amax_out, tensor_scale, nonfinite, (uint32_t *)nullptr);
     return status_after_launch();
 }
 

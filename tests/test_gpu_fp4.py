@@ -277,3 +277,49 @@ def test_nvfp4_full_size(gradient_full):
     assert g[2] == parts[0][2] and g[3] == np.float32(a) and g[4] == 0
     assert_bytes_equal(g[1], np.concatenate([p[1] for p in parts], axis=0), "s_blk", " [16384x4096]")
     assert_bytes_equal(g[0], np.concatenate([p[0] for p in parts], axis=0), "q", " [16384x4096]")
+
+
+def run_nv_ws(x, ws):
+    xd = to_device(x)
+    rows, cols = x.shape
+    q = torch.full((rows, cols // 2), 0xA5, dtype=torch.uint8, device="cuda")
+    s = torch.full((rows, cols // 16), 0xA5, dtype=torch.uint8, device="cuda")
+    st = torch.full((1,), -1.0, dtype=torch.float32, device="cuda")
+    a = torch.full((1,), -1.0, dtype=torch.float32, device="cuda")
+    nf = torch.zeros(1, dtype=torch.int32, device="cuda")
+    qf8.quantize_nvfp4(xd, q=q, s_blk=s, tensor_scale=st, amax_out=a, nonfinite=nf, ws=ws)
+    torch.cuda.synchronize()
+    return host(q), host(s), np.float32(st.item()), np.float32(a.item()), int(nf.item())
+
+
+def check_nv_big(x, ws, tag):
+    """Large inputs (the single-pass path from 2^22 elements), compared on every byte; the oracle
+    runs on row slabs with the whole tensor's amax."""
+    g = run_nv_ws(x, ws)
+    a = float(O.amax(x))
+    parts = parallel_row_slabs(lambda r0, r1: O.quantize_nvfp4(x[r0:r1], amax_in=a), x.shape[0], 256)
+    assert g[2] == parts[0][2] and g[3] == np.float32(a) and g[4] == 0, tag
+    assert_bytes_equal(g[1], np.concatenate([p[1] for p in parts], axis=0), "s_blk", f" [{tag}]")
+    assert_bytes_equal(g[0], np.concatenate([p[0] for p in parts], axis=0), "q", f" [{tag}]")
+    words = host(ws.view(torch.int32)[:qf8.BARRIER_WORDS]).copy()
+    words[2] = 0                                   # the give-up timeout override a test may set
+    assert not words.any(), f"workspace not left zero [{tag}]"
+
+
+def test_nvfp4_single_pass_threshold_and_fp32():
+    ws = qf8.workspace(torch.empty(1, device="cuda"))
+    check_nv_big(mx_gradient(1, (1 << 22) - 16, seed=21), ws, "2^22 - 16 elements (amax pass)")
+    check_nv_big(mx_gradient(1, 1 << 22, seed=22), ws, "2^22 elements (single pass)")
+    rng = np.random.default_rng(23)
+    x = (rng.standard_normal((4096, 8192)) * np.exp(rng.uniform(-2, 2, (4096, 1)))).astype(np.float32)
+    check_nv_big(x, ws, "4096x8192 fp32 (beyond the held capacity)")
+
+
+@pytest.mark.parametrize("ticks", [1, 500])
+def test_nvfp4_single_pass_give_up(gradient_full, ticks):
+    """Waiting workgroups forced to give up at the grid barrier: the last one casts their slabs."""
+    ws = qf8.workspace(torch.empty(1, device="cuda"))
+    ws.view(torch.int32)[2] = ticks
+    check_nv_big(gradient_full, ws, f"give-up after {ticks} ticks")
+    ws.view(torch.int32)[2] = 0
+    check_nv_big(gradient_full[:2048], ws, "default timeout after a give-up run")
