@@ -247,16 +247,31 @@ __device__ __forceinline__ float nv_tensor_scale(uint32_t abits) {
     const float s = 2688.0f / __uint_as_float(abits);
     return s > 3.40282346638528859812e+38f ? 3.40282346638528859812e+38f : s;
 }
-__device__ __forceinline__ uint32_t nv_block_scale(uint32_t amax_bits, float st, float &r) {
-    if (amax_bits >= 0x7F800000u) {
-        r = 0.0f;
-        return 0x7Fu;
+// fl32(a / 6) for a finite |a| bit pattern: the product with fl32(1/6), corrected by one fused
+// multiply-add, is the correctly rounded quotient for every a >= 2^-125 (checked on the host over
+// all such fp32 values); smaller a (subnormal quotients) take the IEEE division.
+__device__ __forceinline__ float div6(uint32_t abits) {
+    const float a = __uint_as_float(abits);
+    if (__builtin_expect(abits < 0x01000000u, 0)) return a / 6.0f;
+    const float c = 0x1.555556p-3f;
+    const float q0 = a * c;
+    return __builtin_fmaf(__builtin_fmaf(-q0, 6.0f, a), c, q0);
+}
+// e_b of a block from its |amax| bits and S_t.
+__device__ __forceinline__ uint32_t nv_block_code(uint32_t amax_bits, float st) {
+    if (amax_bits >= 0x7F800000u) return 0x7Fu;
+    const float p = fminf(div6(amax_bits) * st, 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p, p, 0, false) & 0xFFu;
+}
+// r_b for every E4M3 code, written by threads 0..127 of the workgroup (S_t is the same for the
+// whole tensor, so each block looks its factor up instead of dividing); code 0x7F (non-finite
+// block) gets 0. The caller synchronizes before reading.
+__device__ __forceinline__ void nv_factor_table(float *tab, float st) {
+    const int e = (int)threadIdx.x;
+    if (e < 128) {
+        const float dec = __builtin_amdgcn_cvt_f32_fp8(e, 0);
+        tab[e] = (e == 0x7F || dec == 0.0f) ? 0.0f : fminf(st / dec, 3.40282346638528859812e+38f);
     }
-    const float p = fminf(__uint_as_float(amax_bits) / 6.0f * st, 448.0f);
-    const uint32_t e = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p, p, 0, false) & 0xFFu;
-    const float dec = __builtin_amdgcn_cvt_f32_fp8((int)e, 0);
-    r = dec == 0.0f ? 0.0f : fminf(st / dec, 3.40282346638528859812e+38f);
-    return e;
 }
 // Two fp32 values -> one byte of two E2M1 codes (first value in the low nibble) in byte SEL of
 // `old`: v_cvt_scalef32_pk_fp4_f32 with scale 1 rounds to nearest even and saturates to +-6.

@@ -345,9 +345,12 @@ __global__ __launch_bounds__(kThreads) void nvfp4_kernel(const void *__restrict_
                                                          uint8_t *__restrict__ s_blk, float *tensor_scale,
                                                          float *amax_out, int32_t *nonfinite) {
     __shared__ uint32_t red[kThreads / 64];
+    __shared__ float tab[128];                   // r_b per E4M3 block-scale code
     const uint32_t A = amax_in ? (__float_as_uint(*amax_in) & 0x7FFFFFFFu)
                                : block_max_bcast<kThreads>(fold_max<kThreads>(partials, nparts), red);
     const float st = nv_tensor_scale(A);
+    nv_factor_table(tab, st);
+    __syncthreads();
     if (blockIdx.x == 0 && threadIdx.x == 0) {
         if (tensor_scale) *tensor_scale = st;
         if (amax_out) *amax_out = __uint_as_float(A);
@@ -382,8 +385,8 @@ __global__ __launch_bounds__(kThreads) void nvfp4_kernel(const void *__restrict_
 #pragma unroll
         for (int k = 0; k < 16; ++k) a = umax(a, __float_as_uint(f[k]) & 0x7FFFFFFFu);
         if (a >= 0x7F800000u) bad = true;        // Inf/NaN block: E4M3 NaN scale code
-        float r;
-        const uint32_t e = nv_block_scale(a, st, r);
+        const uint32_t e = nv_block_code(a, st);
+        const float r = tab[e];
         uint32_t o0 = 0u, o1 = 0u;
         o0 = fp4_f32<0>(o0, f[0] * r, f[1] * r, 1.0f);
         o0 = fp4_f32<1>(o0, f[2] * r, f[3] * r, 1.0f);

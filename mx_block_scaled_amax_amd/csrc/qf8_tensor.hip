@@ -393,12 +393,12 @@ constexpr uint32_t op_out_bytes() { return OP == kOpFp8 ? (BF16 ? 8u : 4u) : (BF
 
 template <bool BF16>
 __device__ __forceinline__ void nv_vec_store(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t wsb, uint32_t vrel,
-                                             uint4 v, float st) {
+                                             uint4 v, float st, const float *tab) {
     uint32_t a = acc_to_f32bits<BF16>(vec_absmax<BF16>(0u, v));
     if constexpr (BF16) a = umax(a, dpp_mov<0xB1>(a));         // lanes 2j, 2j+1 hold one block
     else a = max_quad(a);                                       // lanes 4j .. 4j+3
-    float r;
-    const uint32_t e = nv_block_scale(a, st, r);
+    const uint32_t e = nv_block_code(a, st);
+    const float r = tab[e];
     if constexpr (BF16) {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
         uint32_t o = 0u;
@@ -419,9 +419,9 @@ __device__ __forceinline__ void nv_vec_store(__amdgpu_buffer_rsrc_t wq, __amdgpu
 
 template <int OP, bool BF16, int FMT>
 __device__ __forceinline__ void op_vec_store(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t wsb, uint32_t vrel,
-                                             uint4 v, float s) {
+                                             uint4 v, float s, const float *tab) {
     if constexpr (OP == kOpFp8) cast_vec_store<BF16, FMT>(wq, vrel * op_out_bytes<OP, BF16>(), v, s);
-    else nv_vec_store<BF16>(wq, wsb, vrel, v, s);
+    else nv_vec_store<BF16>(wq, wsb, vrel, v, s, tab);
 }
 
 // Byte count of the vectors [first, nvec) clamped to one buffer descriptor's range.
@@ -436,7 +436,7 @@ __device__ __forceinline__ uint32_t span_bytes(int64_t first, int64_t nvec, uint
 // load, and cast + store when CAST, return the |x| maximum (accumulator form).
 template <int OP, bool BF16, int FMT, bool CAST>
 __device__ __forceinline__ uint32_t stream_slabs8(const uint4 *x, int64_t nvec, uint8_t *q, uint8_t *sb, int64_t k,
-                                                  int j, int G, float s) {
+                                                  int j, int G, float s, const float *tab) {
     constexpr uint32_t kOut = op_out_bytes<OP, BF16>();
     constexpr uint32_t kVpb = BF16 ? 2u : 4u;                      // vectors per NVFP4 block
     const uint32_t step = (uint32_t)G * kOpThreads * 16u;
@@ -451,7 +451,7 @@ __device__ __forceinline__ uint32_t stream_slabs8(const uint4 *x, int64_t nvec, 
         const __amdgpu_buffer_rsrc_t wsb = make_rsrc(OP == kOpNvfp4 ? sb + first / kVpb : q,
                                                      OP == kOpNvfp4 ? span_bytes(first, nvec, 1u) / kVpb : 0u);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) op_vec_store<OP, BF16, FMT>(w, wsb, i * (step / 16u) + threadIdx.x, v[i], s);
+        for (int i = 0; i < 8; ++i) op_vec_store<OP, BF16, FMT>(w, wsb, i * (step / 16u) + threadIdx.x, v[i], s, tab);
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) a = vec_absmax<BF16>(a, v[i]);
@@ -471,6 +471,7 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
     __shared__ uint32_t red[kOpThreads / 64];
     __shared__ uint32_t sh[3];
     __shared__ uint16_t gave_up[kBarMaxGroups];
+    __shared__ float nvtab[OP == kOpNvfp4 ? 128 : 1];             // NVFP4: r_b per E4M3 code
     const uint4 *xv = (const uint4 *)x;
     const int G = gridDim.x, b = blockIdx.x, t = threadIdx.x;
     const int64_t nslabs = (nvec + kOpThreads - 1) / kOpThreads;
@@ -485,7 +486,7 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
     // register-held slabs, all loads in flight together
     uint32_t a0 = 0;
     for (int64_t k = KR + KL; k * G + b < nslabs; k += 8)
-        a0 = acc_max<BF16>(a0, stream_slabs8<OP, BF16, FMT, false>(xv, nvec, q, sb, k, b, G, 0.f));
+        a0 = acc_max<BF16>(a0, stream_slabs8<OP, BF16, FMT, false>(xv, nvec, q, sb, k, b, G, 0.f, nvtab));
     a0 = acc_to_f32bits<BF16>(a0);
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
 #pragma unroll
@@ -557,14 +558,20 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
         xres = __hip_atomic_exchange(lines + (size_t)t * (kBarLineWords / 2), kLineReleased | m, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
     const float s = OP == kOpFp8 ? scale_from_amax_bits<FMT>(m) : nv_tensor_scale(m);
+    if constexpr (OP == kOpNvfp4) {
+        nv_factor_table(nvtab, s);
+        __syncthreads();
+    }
 
     // pass 2: cast the held slabs, then re-read and cast the rest (vector indices: vbase + k * vstep)
     const uint32_t vbase = (uint32_t)b * kOpThreads + t, vstep = step / 16u;
 #pragma unroll
-    for (int k = 0; k < KR; ++k) op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + k * vstep, R[k], s);
+    for (int k = 0; k < KR; ++k) op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + k * vstep, R[k], s, nvtab);
 #pragma unroll
-    for (int k = 0; k < KL; ++k) op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + (KR + k) * vstep, held[k * kOpThreads + t], s);
-    for (int64_t k = KR + KL; k * G + b < nslabs; k += 8) stream_slabs8<OP, BF16, FMT, true>(xv, nvec, q, sb, k, b, G, s);
+    for (int k = 0; k < KL; ++k)
+        op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + (KR + k) * vstep, held[k * kOpThreads + t], s, nvtab);
+    for (int64_t k = KR + KL; k * G + b < nslabs; k += 8)
+        stream_slabs8<OP, BF16, FMT, true>(xv, nvec, q, sb, k, b, G, s, nvtab);
 
     if (role == 1) {
         if (xres == kLineGaveUp) {                  // that workgroup exited: clear its line, cast its slabs
@@ -575,7 +582,7 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
         const uint32_t ng = sh[2];
         for (uint32_t i = 0; i < ng; ++i)
             for (int64_t k = 0; k * G + gave_up[i] < nslabs; k += 8)
-                stream_slabs8<OP, BF16, FMT, true>(xv, nvec, q, sb, k, gave_up[i], G, s);
+                stream_slabs8<OP, BF16, FMT, true>(xv, nvec, q, sb, k, gave_up[i], G, s, nvtab);
         if constexpr (OP == kOpFp8)          // NVFP4 sizes are whole vectors (n % 16 == 0)
             for (int64_t e = nvec * vec_elems<BF16>() + t; e < n; e += kOpThreads)
                 q[e] = (uint8_t)cast1<FMT>(__uint_as_float(elem_bits<BF16>(x, e)), s);
