@@ -455,7 +455,16 @@ def run_suite(args):
     res.append(_summ("nvfp4 16384x4096 bf16 (caller amax, one read)", 2 * N + N // 2 + N // 16,
                      _timed(torch, stream, [PreCall(L.quantize_nvfp4, vp(xg), 0, ROWS, COLS, vp(nva), vp(f4r), vp(nvs),
                                                     vp(nvt), None, None, None, 0, sp)], reps, warm)))
-    del f4r, f4rs, nvs
+    o16f = torch.empty((ROWS, COLS), dtype=torch.bfloat16, device="cuda")
+    L.quantize_mxfp4_dual(vp(xg), 0, ROWS, COLS, qf8.ROUND_DOWN, vp(f4r), vp(f4rs), None, None, None, sp)
+    res.append(_summ("dequant mxfp4 rowwise 16384x4096 -> bf16", N // 2 + N // 32 + 2 * N,
+                     _timed(torch, stream, [PreCall(L.dequantize_mxfp4, vp(f4r), vp(f4rs), ROWS, COLS, vp(o16f), 0, sp)],
+                            reps, warm)))
+    L.quantize_nvfp4(vp(xg), 0, ROWS, COLS, vp(nva), vp(f4r), vp(nvs), vp(nvt), None, None, None, 0, sp)
+    res.append(_summ("dequant nvfp4 16384x4096 -> bf16", N // 2 + N // 16 + 2 * N,
+                     _timed(torch, stream, [PreCall(L.dequantize_nvfp4, vp(f4r), vp(nvs), vp(nvt), ROWS, COLS, vp(o16f), 0,
+                                                    sp)], reps, warm)))
+    del f4r, f4rs, nvs, o16f
 
     # dequantization (and fused error statistics) of the MX dual result and the per-tensor result
     q_row, s_row, q_colT, s_colT = qf8.quantize_mx_dual(xg, qf8.E4M3, qf8.ROUND_DOWN)

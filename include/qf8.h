@@ -303,6 +303,22 @@ int dequantize_mx(const uint8_t *q, const uint8_t *s, int64_t rows, int64_t cols
                   int out_dtype, const void *x, int x_dtype, qf8_error_stats *stats, void *ws,
                   size_t ws_bytes, void *stream);
 
+/* FP4 de-scaling (the FP4 counterpart of the calls above; no statistics). q is packed two codes
+ * per byte as the FP4 quantizers write it; element i uses the scale of its block in flattened
+ * order.
+ *   dequantize_mxfp4: q [rows][cols/2], sb [rows][cols/32] E8M0 bytes (a columnwise result is
+ *     passed as its transpose: q_colT with rows = cols of x); xhat = decode(c) * 2^(b - 127),
+ *     exact in fp32 (Inf on overflow), NaN for b = 0xFF. cols % 32 == 0.
+ *   dequantize_nvfp4: q [rows][cols/2], s_blk [rows][cols/16] E4M3 codes, tensor_scale (device
+ *     fp32 S_t); xhat = fl32(decode(c) * decode(e_b) / S_t) (the product is exact), NaN for
+ *     e_b = 0x7F. cols % 16 == 0.
+ * out: [rows][cols] BF16 (round to nearest even) or FP32 (qf8_out_dtype). q and out 16-byte
+ * aligned; rows * cols < 2^36. */
+int dequantize_mxfp4(const uint8_t *q, const uint8_t *sb, int64_t rows, int64_t cols, void *out,
+                     int out_dtype, void *stream);
+int dequantize_nvfp4(const uint8_t *q, const uint8_t *s_blk, const float *tensor_scale,
+                     int64_t rows, int64_t cols, void *out, int out_dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,8 @@ __all__ = [
     "qf8_status_string", "qf8_workspace_bytes", "qf8_cast_scaled", "quantize_per_tensor",
     "DelayedState", "qf8_delayed_init", "qf8_delayed_init_ex", "qf8_delayed_reset", "quantize_delayed",
     "EST_MAX", "EST_RECENT", "EST_MEAN", "DELAYED_SPLIT_AMAX",
-    "quantize_block", "quantize_mx_dual", "quantize_mxfp4_dual", "quantize_nvfp4",
+    "quantize_block", "quantize_mx_dual", "quantize_mxfp4_dual", "quantize_nvfp4", "dequantize_mxfp4",
+    "dequantize_nvfp4",
 ]
 
 E4M3, E5M2 = 0, 1
@@ -77,6 +78,8 @@ def _load():
         "quantize_mx_dual": (i32, [vp, i32, i64, i64, i32, i32, vp, vp, vp, vp, vp, vp]),
         "quantize_mxfp4_dual": (i32, [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, vp]),
         "quantize_nvfp4": (i32, [vp, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "dequantize_mxfp4": (i32, [vp, vp, i64, i64, vp, i32, vp]),
+        "dequantize_nvfp4": (i32, [vp, vp, vp, i64, i64, vp, i32, vp]),
         "dequantize_scaled": (i32, [vp, i64, i32, vp, vp, i32, vp, i32, vp, vp, sz, vp]),
         "dequantize_block": (i32, [vp, i64, i64, i32, i32, i32, vp, vp, i32, vp, i32, vp, vp, sz, vp]),
         "dequantize_mx": (i32, [vp, vp, i64, i64, i32, vp, i32, vp, i32, vp, vp, sz, vp]),
@@ -349,6 +352,37 @@ def quantize_nvfp4(x, amax_in=None, q=None, s_blk=None, tensor_scale=None, amax_
            "quantize_nvfp4")
     return q, s_blk, tensor_scale
 
+
+
+def _fp4_out(out, out_dtype, rows, cols, dev):
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+    return _out(out, (rows, cols), out_dtype, dev, "out")
+
+
+def dequantize_mxfp4(q, sb, out_dtype=torch.bfloat16, out=None, stream=None):
+    """MXFP4 de-scaling: q [rows][cols/2] packed, sb [rows][cols/32] E8M0 -> out [rows][cols]."""
+    _dev_tensor(q, "q")
+    _dev_tensor(sb, "sb")
+    rows, cols = q.shape[0], q.shape[1] * 2
+    out = _fp4_out(out, out_dtype, rows, cols, q.device)
+    _check(_load().dequantize_mxfp4(_ptr(q), _ptr(sb), rows, cols, _ptr(out),
+                                    _BF16 if out.dtype == torch.bfloat16 else _FP32,
+                                    _stream(stream, q.device)), "dequantize_mxfp4")
+    return out
+
+
+def dequantize_nvfp4(q, s_blk, tensor_scale, out_dtype=torch.bfloat16, out=None, stream=None):
+    """NVFP4 de-scaling: q [rows][cols/2] packed, s_blk [rows][cols/16] E4M3, tensor_scale [1]."""
+    _dev_tensor(q, "q")
+    _dev_tensor(s_blk, "s_blk")
+    _dev_tensor(tensor_scale, "tensor_scale")
+    rows, cols = q.shape[0], q.shape[1] * 2
+    out = _fp4_out(out, out_dtype, rows, cols, q.device)
+    _check(_load().dequantize_nvfp4(_ptr(q), _ptr(s_blk), _ptr(tensor_scale), rows, cols, _ptr(out),
+                                    _BF16 if out.dtype == torch.bfloat16 else _FP32,
+                                    _stream(stream, q.device)), "dequantize_nvfp4")
+    return out
 
 
 # ---- dequantization and error statistics ------------------------------------------------------

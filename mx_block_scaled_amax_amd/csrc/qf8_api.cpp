@@ -302,6 +302,28 @@ int quantize_nvfp4(const void *x, int dtype, int64_t rows, int64_t cols, const f
     return qf8::launch_nvfp4(x, dtype, n, partials, nparts, amax_in, q, s_blk, tensor_scale, amax_out, nonfinite, s);
 }
 
+int dequantize_mxfp4(const uint8_t *q, const uint8_t *sb, int64_t rows, int64_t cols, void *out, int out_dtype,
+                     void *stream) {
+    if (out_dtype != QF8_OUT_BF16 && out_dtype != QF8_OUT_FP32) return QF8_ERR_ENUM;
+    if (!dims_ok(rows, cols) || cols % 32 != 0 || rows * cols >= ((int64_t)1 << 36)) return QF8_ERR_SHAPE;
+    const int64_t n = rows * cols;
+    if (n == 0) return QF8_OK;
+    if (!q || !sb || !out) return QF8_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(out, 16)) return QF8_ERR_ALIGN;
+    return qf8::launch_dequant_fp4(0, q, sb, nullptr, n, out, out_dtype, as_stream(stream));
+}
+
+int dequantize_nvfp4(const uint8_t *q, const uint8_t *s_blk, const float *tensor_scale, int64_t rows, int64_t cols,
+                     void *out, int out_dtype, void *stream) {
+    if (out_dtype != QF8_OUT_BF16 && out_dtype != QF8_OUT_FP32) return QF8_ERR_ENUM;
+    if (!dims_ok(rows, cols) || cols % 16 != 0 || rows * cols >= ((int64_t)1 << 36)) return QF8_ERR_SHAPE;
+    const int64_t n = rows * cols;
+    if (n == 0) return QF8_OK;
+    if (!q || !s_blk || !tensor_scale || !out) return QF8_ERR_NULL;
+    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(tensor_scale, 4)) return QF8_ERR_ALIGN;
+    return qf8::launch_dequant_fp4(1, q, s_blk, tensor_scale, n, out, out_dtype, as_stream(stream));
+}
+
 }  // extern "C"
 
 // ---- dequantization and error statistics ---------------------------------------------------

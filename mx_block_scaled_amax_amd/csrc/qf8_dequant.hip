@@ -79,13 +79,6 @@ __device__ __forceinline__ void decode4(uint32_t codes, float *v) {
     v[0] = lo.x; v[1] = lo.y; v[2] = hi.x; v[3] = hi.y;
 }
 
-// fp32 -> BF16 bits, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 // Running statistics of one thread: the fp64 sums in 4 independent chains (element k of a unit
 // goes to chain k % 4; short dependency chains, fixed order), counts in u32.
 struct Acc {

@@ -280,6 +280,13 @@ __device__ __forceinline__ uint32_t cvt_fp4_f32(uint32_t old, float a, float b, 
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, scale, SEL);
 }
 
+// fp32 -> BF16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 // ---- buffer resources ------------------------------------------------------------------------
 // Raw buffer descriptors (stride 0): addresses are base + voffset (per lane) + soffset (uniform),
 // and any access whose offset reaches num_records is dropped (loads return 0). Kernels set the

@@ -402,6 +402,75 @@ __global__ __launch_bounds__(kThreads) void nvfp4_kernel(const void *__restrict_
     if (bad && nonfinite) *nonfinite = 1;
 }
 
+// ---------------------------------------------------------------------------------------------
+// FP4 de-scaling. One thread per unit of 16 codes (8 bytes), taken in flattened order: element i
+// belongs to MX block i / 32 (cols % 32 == 0) or NVFP4 block i / 16 (cols % 16 == 0), whose scale
+// bytes are contiguous in the same order. MXFP4: decode(c) * 2^X is exact in fp32 for every code
+// and X >= -127 (at most two significant bits, at least 2^-128), or Inf, and NaN for byte 0xFF.
+// NVFP4: code * decode(e_b) takes at most 16 x 128 values and is exact in fp32, so each workgroup
+// fills an LDS table of fl32(decode(c) * decode(e) / S_t) (IEEE division, S_t read once) and
+// every element is one lookup. BF16 output rounds to nearest even.
+constexpr int kDqThreads = 256;
+constexpr int kDqMaxGrid = 2048;
+
+// E2M1 code -> value: 0, 0.5 (the subnormal), then 1.m * 2^(e-1); sign in bit 3 (-0 for code 8).
+__device__ __forceinline__ float e2m1_value(int c) {
+    const int m = c & 7;
+    const float mag = m < 2 ? 0.5f * (float)m : __builtin_ldexpf(1.0f + 0.5f * (float)(m & 1), (m >> 1) - 1);
+    return (c & 8) ? -mag : mag;
+}
+
+template <int NV, bool OUTBF16>
+__global__ __launch_bounds__(kDqThreads) void dequant_fp4_kernel(const uint8_t *__restrict__ q,
+                                                                 const uint8_t *__restrict__ sb,
+                                                                 const float *__restrict__ tensor_scale,
+                                                                 int64_t nunits, void *__restrict__ out) {
+    __shared__ float tab[NV ? 128 * 16 : 16];
+    if constexpr (NV) {
+        const float st = *tensor_scale;
+        for (int i = threadIdx.x; i < 128 * 16; i += kDqThreads) {
+            const int e = i >> 4, c = i & 15;
+            const float dec = __builtin_amdgcn_cvt_f32_fp8(e, 0);        // NaN for 0x7F
+            const float p = e2m1_value(c) * dec;                         // exact
+            tab[i] = p / st;
+        }
+    } else {
+        if (threadIdx.x < 16) tab[threadIdx.x] = e2m1_value((int)threadIdx.x);
+    }
+    __syncthreads();
+    for (int64_t u = (int64_t)blockIdx.x * kDqThreads + threadIdx.x; u < nunits; u += (int64_t)gridDim.x * kDqThreads) {
+        const uint2 w = *(const uint2 *)(q + 8 * u);
+        float v[16];
+        if constexpr (NV) {
+            const int e = sb[u];                                         // one 16-element block per unit
+#pragma unroll
+            for (int k = 0; k < 16; ++k) v[k] = tab[e * 16 + (((k < 8 ? w.x : w.y) >> (4 * (k & 7))) & 15u)];
+        } else {
+            const uint32_t b = sb[u >> 1];                               // two units per 32-element block
+            const int X = (int)b - 127;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const float d = tab[((k < 8 ? w.x : w.y) >> (4 * (k & 7))) & 15u];
+                v[k] = b == 0xFFu ? __uint_as_float(0x7FC00000u) : __builtin_ldexpf(d, X);
+            }
+        }
+        if constexpr (OUTBF16) {
+            uint32_t o[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) o[k] = bf16_rne(v[2 * k]) | (bf16_rne(v[2 * k + 1]) << 16);
+            uint4 *dst = (uint4 *)out + 2 * u;
+            dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+            dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        } else {
+            uint4 *dst = (uint4 *)out + 4 * u;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                dst[k] = make_uint4(__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
+                                    __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3]));
+        }
+    }
+}
+
 int nvfp4_grid(int64_t nblk) {
     int64_t g = (nblk + (int64_t)kThreads * kNvBlocksPerThread - 1) / ((int64_t)kThreads * kNvBlocksPerThread);
     if (g > kMaxStreamGrid) g = kMaxStreamGrid;
@@ -409,6 +478,27 @@ int nvfp4_grid(int64_t nblk) {
 }
 
 }  // namespace
+
+int launch_dequant_fp4(int nv, const uint8_t *q, const uint8_t *sb, const float *tensor_scale, int64_t n, void *out,
+                       int out_dtype, hipStream_t s) {
+    const int64_t nunits = n / 16;
+    if (nunits == 0) return QF8_OK;
+    int64_t g = (nunits + kDqThreads - 1) / kDqThreads;
+    if (g > kDqMaxGrid) g = kDqMaxGrid;
+    const dim3 grid((unsigned)g), block(kDqThreads);
+    if (nv) {
+        if (out_dtype == QF8_OUT_BF16)
+            hipLaunchKernelGGL((dequant_fp4_kernel<1, true>), grid, block, 0, s, q, sb, tensor_scale, nunits, out);
+        else
+            hipLaunchKernelGGL((dequant_fp4_kernel<1, false>), grid, block, 0, s, q, sb, tensor_scale, nunits, out);
+    } else {
+        if (out_dtype == QF8_OUT_BF16)
+            hipLaunchKernelGGL((dequant_fp4_kernel<0, true>), grid, block, 0, s, q, sb, tensor_scale, nunits, out);
+        else
+            hipLaunchKernelGGL((dequant_fp4_kernel<0, false>), grid, block, 0, s, q, sb, tensor_scale, nunits, out);
+    }
+    return hipGetLastError() == hipSuccess ? QF8_OK : QF8_ERR_HIP;
+}
 
 int launch_mxfp4(const void *x, int dtype, int64_t rows, int64_t cols, int rnd, uint8_t *q_row, uint8_t *s_row,
                  uint8_t *q_colT, uint8_t *s_colT, int32_t *nonfinite, hipStream_t s) {

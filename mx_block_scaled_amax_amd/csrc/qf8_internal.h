@@ -45,6 +45,8 @@ int launch_per_tensor_onepass(const void *x, int dtype, int64_t n, int fmt, uint
                               float *amax_out, float *scale_out, int32_t *nonfinite, uint32_t *amax_bits_out,
                               int grid, hipStream_t s);
 
+int launch_dequant_fp4(int nv, const uint8_t *q, const uint8_t *sb, const float *tensor_scale, int64_t n, void *out,
+                       int out_dtype, hipStream_t s);
 int launch_mxfp4(const void *x, int dtype, int64_t rows, int64_t cols, int rnd, uint8_t *q_row, uint8_t *s_row,
                  uint8_t *q_colT, uint8_t *s_colT, int32_t *nonfinite, hipStream_t s);
 int launch_nvfp4(const void *x, int dtype, int64_t n, const uint32_t *partials, int nparts, const float *amax_in,

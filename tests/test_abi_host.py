@@ -187,3 +187,18 @@ def test_block_ex_and_requant_argument_errors():
     assert g(FAKE, FAKE, 128, 128, 0, 0, 1, FAKE, None, None, None) == NULL               # scalesT
     assert g(FAKE, FAKE, 0, 128, 0, 0, 1, None, None, None, None) == OK                   # empty
     assert g(MISALIGNED, FAKE, 128, 128, 0, 0, 1, FAKE, FAKE, None, None) == ALIGN
+
+
+def test_fp4_dequant_argument_errors():
+    f = lib().dequantize_mxfp4
+    assert f(FAKE, FAKE, 4, 64, FAKE, 2, None) == ENUM                 # bad out dtype
+    assert f(FAKE, FAKE, 4, 48, FAKE, 0, None) == SHAPE                # cols % 32
+    assert f(None, FAKE, 4, 64, FAKE, 0, None) == NULL
+    assert f(FAKE, FAKE, 4, 64, MISALIGNED, 0, None) == ALIGN
+    assert f(None, None, 0, 64, None, 0, None) == OK                   # empty
+    g = lib().dequantize_nvfp4
+    assert g(FAKE, FAKE, FAKE, 4, 64, FAKE, 7, None) == ENUM
+    assert g(FAKE, FAKE, FAKE, 4, 40, FAKE, 0, None) == SHAPE          # cols % 16
+    assert g(FAKE, FAKE, None, 4, 64, FAKE, 0, None) == NULL           # no tensor scale
+    assert g(MISALIGNED, FAKE, FAKE, 4, 64, FAKE, 0, None) == ALIGN
+    assert g(FAKE, FAKE, FAKE, 1 << 20, 1 << 16, FAKE, 0, None) == SHAPE   # 2^36 elements

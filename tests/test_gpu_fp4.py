@@ -323,3 +323,69 @@ def test_nvfp4_single_pass_give_up(gradient_full, ticks):
     check_nv_big(gradient_full, ws, f"give-up after {ticks} ticks")
     ws.view(torch.int32)[2] = 0
     check_nv_big(gradient_full[:2048], ws, "default timeout after a give-up run")
+
+
+# ---- FP4 de-scaling ------------------------------------------------------------------------------
+
+def _f32_equal(got, want, what):
+    got = np.asarray(got, np.float32)
+    want = np.asarray(want, np.float32)
+    gn, wn = np.isnan(got), np.isnan(want)
+    assert np.array_equal(gn, wn), f"{what}: NaN positions differ"
+    g, w = got[~gn].view(np.uint32), want[~wn].view(np.uint32)
+    bad = np.nonzero(g != w)[0]
+    assert bad.size == 0, f"{what}: {bad.size} values differ, first {got[~gn][bad[0]]!r} vs {want[~wn][bad[0]]!r}"
+
+
+def _bf16_of(got_bits, want_f32, what):
+    wb = O.to_bf16(want_f32)
+    nan = np.isnan(np.asarray(want_f32, np.float32))
+    assert np.array_equal(((got_bits & 0x7FFF) > 0x7F80), nan), f"{what}: NaN positions differ"
+    assert_bytes_equal(got_bits[~nan].view(np.uint8), wb[~nan].view(np.uint8), what)
+
+
+def _both_outputs(run, want, what):
+    out32 = run(torch.float32)
+    torch.cuda.synchronize()
+    _f32_equal(out32.cpu().numpy(), want, what + " fp32")
+    out16 = run(torch.bfloat16)
+    torch.cuda.synchronize()
+    _bf16_of(out16.cpu().view(torch.int16).numpy().view(np.uint16), want, what + " bf16")
+
+
+def test_dequant_mxfp4_every_code_pair_every_scale_byte():
+    """256 rows x 512 columns: each row's 256 code bytes are all byte values (every ordered pair
+    of codes), and the 16 scale bytes of row r are (r + 17 b) mod 256: every code with every
+    E8M0 byte, 0xFF (NaN) included."""
+    rows, cols = 256, 512
+    q = np.tile(np.arange(256, dtype=np.uint8), (rows, 1))
+    sb = ((np.arange(rows)[:, None] + 17 * np.arange(cols // 32)[None, :]) % 256).astype(np.uint8)
+    want = O.dequant_mxfp4(q, sb)
+    qd, sd = to_device(q), to_device(sb)
+    _both_outputs(lambda dt: qf8.dequantize_mxfp4(qd, sd, out_dtype=dt), want, "mxfp4 exhaustive")
+
+
+@pytest.mark.parametrize("s_t", [1.0, 3.7, 2688.0 / 5.3, 1e-30, 7.9e-36, 1e30, 3.4028235e38])
+def test_dequant_nvfp4_every_code_every_block_scale(s_t):
+    """128 rows x 512 columns: every code byte in every row, and the 32 block-scale codes of row r
+    are (r + 5 b) mod 128: every E2M1 code with every E4M3 scale code (0x7F, NaN, included)."""
+    rows, cols = 128, 512
+    q = np.tile(np.arange(256, dtype=np.uint8), (rows, 1))
+    sb = ((np.arange(rows)[:, None] + 5 * np.arange(cols // 16)[None, :]) % 128).astype(np.uint8)
+    want = O.dequant_nvfp4(q, sb, s_t)
+    qd, sd = to_device(q), to_device(sb)
+    st = torch.tensor([np.float32(s_t)], dtype=torch.float32, device="cuda")
+    _both_outputs(lambda dt: qf8.dequantize_nvfp4(qd, sd, st, out_dtype=dt), want, f"nvfp4 exhaustive S_t={s_t}")
+
+
+def test_dequant_fp4_round_trip_full(gradient_full):
+    """Quantize the 16384 x 4096 workload on the GPU, de-scale on the GPU, and compare with the
+    oracle's de-scaling of the same codes (both MXFP4 directions and NVFP4)."""
+    xd = to_device(gradient_full)
+    q_row, s_row, q_colT, s_colT = qf8.quantize_mxfp4_dual(xd, O.ROUND_DOWN)
+    for q, s, name in ((q_row, s_row, "mxfp4 rowwise"), (q_colT, s_colT, "mxfp4 columnwise")):
+        want = O.dequant_mxfp4(host(q), host(s))
+        _both_outputs(lambda dt: qf8.dequantize_mxfp4(q, s, out_dtype=dt), want, name)
+    qn, sn, st = qf8.quantize_nvfp4(xd)
+    want = O.dequant_nvfp4(host(qn), host(sn), np.float32(st.item()))
+    _both_outputs(lambda dt: qf8.dequantize_nvfp4(qn, sn, st, out_dtype=dt), want, "nvfp4")
