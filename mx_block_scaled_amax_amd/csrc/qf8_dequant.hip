@@ -92,6 +92,25 @@ __device__ __forceinline__ bool finite_f32(float x) { return fabsf(x) <= 3.40282
 
 template <int W>
 __device__ __forceinline__ void acc_add_unit(Acc &acc, const float *x, const float *xh, const bool *sat) {
+    bool all_fin = true;
+#pragma unroll
+    for (int k = 0; k < W; ++k) all_fin = all_fin && finite_f32(x[k]);
+    if (all_fin) {                 // the usual case, without the selects that drop Inf/NaN
+#pragma unroll
+        for (int k = 0; k < W; ++k) {
+            const double xd = (double)x[k], d = xd - (double)xh[k];
+            acc.signal[k & 3] += xd * xd;
+            acc.noise[k & 3] += d * d;
+            const bool nz = x[k] != 0.0f;
+            acc.nonzero += nz ? 1u : 0u;
+            acc.zeroed += (nz && xh[k] == 0.0f) ? 1u : 0u;
+            acc.saturated += sat[k] ? 1u : 0u;
+        }
+        acc.count += W;
+        return;
+    }
+    // a unit with Inf/NaN: those elements add +0 to the sums (which leaves them unchanged) and
+    // count as non-finite only
 #pragma unroll
     for (int k = 0; k < W; ++k) {
         const bool fin = finite_f32(x[k]);
