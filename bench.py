@@ -15,13 +15,16 @@ variant finds the previous variant's data in the 256 MB last-level cache.
                    peak = 8000 GB/s (MI355X HBM3E). A separate, untimed pass with an event
                    pair around every launch gives the per-variant split (those events add a
                    few microseconds of gap per launch, so they stay out of the timed region).
+  config.cold_median_ms_per_variant = median of single launches each preceded by a 1 GiB
+                   scratch fill that evicts L2 and the last-level cache (also outside `value`).
   roofline.traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE counters (in
                    profiles/), scaled by the same counters' reading for a plain copy of known
                    size; null when the kernel sources changed since the counters were taken.
   cpu_baseline   = the CPU oracle (single-threaded C) on the first 4096 rows, all four variants.
 
---suite also times every other operation on its workload (per-tensor, delayed, 1x128, 128x128,
-MX rowwise on the small tensor, a plain copy) and writes gpurun_out/bench_suite.json.
+--suite also times every other operation on its workload (per-tensor, delayed with its variants,
+1x128, 128x128, re-grouping, MXFP4, NVFP4, de-scaling and error statistics, MX rowwise on the small
+tensor, a plain copy) and writes gpurun_out/bench_suite.json.
 """
 import argparse
 import ctypes
@@ -205,6 +208,21 @@ def main():
             ends[k][j].record(stream)
     torch.cuda.synchronize()
     kms = np.array([[starts[k][j].elapsed_time(ends[k][j]) for j in range(len(calls))] for k in range(split_steps)])
+    # cold launches (untimed for `value`): a 1 GiB scratch fill before each one evicts L2 and the
+    # last-level cache, then one event pair around the launch; median over the reps
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    cold = [[] for _ in calls]
+    for k in range(min(args.steps, 20)):
+        for j, c in enumerate(calls):
+            flush.fill_(k & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            c()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold[j].append(e0.elapsed_time(e1))
+    del flush
+    cold_med = [float(np.median(v)) for v in cold]
     value = len(calls) * DUAL_BYTES * args.steps / wall / 1e9
     traffic = stored_traffic()
     line = {
@@ -226,7 +244,10 @@ def main():
                    "bytes_per_variant": DUAL_BYTES, "pct_of_hbm_peak": round(100 * value / PEAK_GBPS, 2),
                    "avg_launch_ms": round(avg_launch_s * 1e3, 5),
                    "launch_ms_per_variant_event_bracketed": {v: round(float(kms[:, j].mean()), 5) for j, v in enumerate(
-                       ["e4m3-round_down", "e4m3-round_up", "e5m2-round_down", "e5m2-round_up"])}},
+                       ["e4m3-round_down", "e4m3-round_up", "e5m2-round_down", "e5m2-round_up"])},
+                   "cold_median_ms_per_variant": {v: round(cold_med[j], 5) for j, v in enumerate(
+                       ["e4m3-round_down", "e4m3-round_up", "e5m2-round_down", "e5m2-round_up"])},
+                   "cold_pct_of_hbm_peak": round(100 * DUAL_BYTES / (float(np.mean(cold_med)) / 1e3) / 1e9 / PEAK_GBPS, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic},
     }
