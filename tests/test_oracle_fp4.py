@@ -201,3 +201,38 @@ def test_nvfp4_tiny_tensor_keeps_zero_codes():
     assert O.decode(O.E4M3, e) < 1.0 and r == fmax           # S_t / decode(e_b) overflowed
     assert np.all(codes == 0)                                # 1e-40 * FLT_MAX = 0.034 -> 0; zeros stay 0
     assert O.nvfp4_block(3e-45, s_t) == (0, 0.0)             # scale below E4M3: zero factor
+
+
+def _golden(golden_dir, name):
+    import json
+    import os
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+def test_golden_e2m1_values(golden_dir):
+    g = _golden(golden_dir, "w10_e2m1_values.json")
+    assert [O.decode(O.E2M1, c) for c in range(8)] == g["values"]
+
+
+def test_golden_mxfp4_example(golden_dir):
+    g = _golden(golden_dir, "w8_mxfp4_example.json")
+    assert O.emax(O.E2M1) == g["emax_e2m1"]
+    assert O.mx_exponent(O.E2M1, O.ROUND_DOWN, g["amax"]) == g["shared_exponent"]
+    assert 2.0 ** g["shared_exponent"] == g["scale"]
+    assert O.decode(O.E2M1, O.encode(O.E2M1, g["amax"] / g["scale"])) == g["rounded_amax"]
+    err = abs(g["rounded_amax"] - g["amax"]) / g["amax"]
+    assert round(100 * err) == g["relative_error_pct"]
+
+
+def test_golden_nvfp4_example(golden_dir):
+    g = _golden(golden_dir, "w9_nvfp4_example.json")
+    e, r = O.nvfp4_block(g["amax"], 1.0)               # S_t = 1, as in the example
+    assert round(g["amax"] / 6, 3) == g["block_scale_exact"]
+    assert O.decode(O.E4M3, e) == g["block_scale_e4m3"]
+    assert round(g["amax"] / g["block_scale_e4m3"], 2) == g["scaled_amax"]
+    code = O.encode(O.E2M1, float(np.float32(np.float32(g["amax"]) * r)))
+    assert O.decode(O.E2M1, code) == g["rounded_amax"]
+    assert O.dequant_nvfp4_one(code, e, 1.0) == g["dequantized"]
+    assert abs(g["dequantized"] - g["amax"]) / g["amax"] * 100 < g["relative_error_below_pct"]
+    assert (g["block_size"] * 4 + 8) / g["block_size"] == g["bits_per_element"]
