@@ -224,3 +224,36 @@ def test_onepass_workspace_reuse():
     for n, seed in ((5 << 20, 11), (1000, 12), (6 << 20 | 3, 13), (5 << 20, 14)):
         x = small_tensor(1, n, seed=seed)
         check_big(x, O.E4M3, ws, f"reuse n={n}")
+
+
+def test_onepass_beside_a_busy_stream(activation_full):
+    """The single-pass kernel while another stream keeps CUs busy with a long fp32 matmul: some
+    workgroups may not be resident when the others reach the grid barrier, so waiters can give
+    up and the last workgroup casts their slabs. The bytes must not depend on it."""
+    x = activation_full
+    xd = to_device(x)
+    ws = qf8.workspace(xd)
+    a = torch.randn(8192, 8192, device="cuda")
+    b = torch.randn(8192, 8192, device="cuda")
+    busy = torch.cuda.Stream()
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    results = []
+    for rep in range(3):
+        with torch.cuda.stream(busy):
+            c = a @ b                                     # several milliseconds of work
+        with torch.cuda.stream(side):
+            q, am, sc = qf8.quantize_per_tensor(xd, O.E4M3, ws=ws)
+        torch.cuda.synchronize()
+        results.append((host(q), float(am.item()), float(sc.item())))
+        del c
+    wa = np.float32(O.amax(x))
+    wsc = np.float32(O.scale_from_amax(O.E4M3, wa))
+    parts = parallel_row_slabs(lambda r0, r1: O.cast(x[r0:r1], O.E4M3, wsc), x.shape[0], 512)
+    want = np.concatenate(parts, axis=0)
+    for rep, (q, am, sc) in enumerate(results):
+        assert np.float32(am) == wa and np.float32(sc) == wsc, rep
+        assert_bytes_equal(q, want, "q", f" [beside a busy stream, rep {rep}]")
+    words = barrier_words(ws)
+    words[2] = 0
+    assert not words.any(), "barrier region not left zero"
