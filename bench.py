@@ -24,7 +24,7 @@ variant finds the previous variant's data in the 256 MB last-level cache.
 
 --suite also times every other operation on its workload (per-tensor, delayed with its variants,
 1x128, 128x128, re-grouping, MXFP4, NVFP4, de-scaling and error statistics, MX rowwise on the small
-tensor, a plain copy) and writes gpurun_out/bench_suite.json.
+tensor, a plain copy): one JSON line per operation on stderr, and the list to --suite-out if given.
 """
 import argparse
 import ctypes
@@ -74,6 +74,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--suite", action="store_true", help="also time every other operation")
+    ap.add_argument("--suite-out", default=None, help="also write the suite's lines to this JSON file")
     ap.add_argument("--only-dual", action="store_true",
                     help="launch only the dual kernel (E4M3 round-up) --steps times, for counter runs")
     ap.add_argument("--only-per-tensor", action="store_true",
@@ -262,7 +263,7 @@ def main():
 
 
 # ---------------------------------------------------------------------------------------------
-# --suite: every other operation on its own workload (reported to gpurun_out/bench_suite.json)
+# --suite: every other operation on its own workload (one JSON line each on stderr)
 # ---------------------------------------------------------------------------------------------
 class PreCall:
     """A library entry point with its ctypes arguments marshalled once, so that back-to-back
@@ -507,9 +508,11 @@ def run_suite(args):
                      _timed(torch, stream, [PreCall(L.dequantize_scaled, vp(qp), N, qf8.E4M3, vp(scp), vp(o16), 0,
                                                     None, 0, None, None, 0, sp)], reps, warm)))
     del xg, o16, qp
-    os.makedirs(os.path.join(ROOT, "gpurun_out"), exist_ok=True)
-    with open(os.path.join(ROOT, "gpurun_out", "bench_suite.json"), "w") as f:
-        json.dump(res, f, indent=1)
+    if args.suite_out:
+        d = os.path.dirname(os.path.abspath(args.suite_out))
+        os.makedirs(d, exist_ok=True)
+        with open(args.suite_out, "w") as f:
+            json.dump(res, f, indent=1)
 
 
 if __name__ == "__main__":
