@@ -372,9 +372,9 @@ def run_suite(args):
     wsd = qf8.workspace(xsd[0])
     R, C = xsd[0].shape
 
-    def steps_of(state):
-        return [PreCall(L.quantize_delayed, vp(x), 0, R, C, ctypes.byref(state.struct), vp(qd), None, None, None,
-                        vp(wsd), wsd.numel(), sp) for x in xsd]
+    def steps_of(state, amax_out=None):
+        return [PreCall(L.quantize_delayed, vp(x), 0, R, C, ctypes.byref(state.struct), vp(qd), None,
+                        None if amax_out is None else vp(amax_out), None, vp(wsd), wsd.numel(), sp) for x in xsd]
     for c in steps_of(qf8.DelayedState(16, 5, 3, qf8.E4M3))[:3]:     # warm the code paths on a throwaway state
         c()
     torch.cuda.synchronize()
@@ -399,11 +399,13 @@ def run_suite(args):
     nd = xsd[0].numel()
     res.append(_summ("delayed 4096x14336 e4m3, steps 1..99", 3 * nd, (ms[1:], e0.elapsed_time(e1) / (len(calls) - 1)),
                      {"step0_ms": round(ms[0], 5), "total_100_steps_ms_event_per_step": round(sum(ms), 4),
-                      "note": "step 0 is current scaling (single-pass kernel + finalize); later steps one fused "
-                              "cast pass + a one-workgroup finalize"}))
+                      "note": "step 0 is current scaling (single-pass kernel + finalize); update steps one fused "
+                              "cast pass + a one-workgroup finalize; reuse steps, asked for no amax, the cast alone"}))
     # the same 99 steps with the amax split over the Interval, and with the mean estimator
-    for label, kw in (("split amax", {"split": True}), ("mean estimator", {"estimator": qf8.EST_MEAN})):
-        calls = steps_of(qf8.DelayedState(16, 5, 3, qf8.E4M3, **kw))
+    amax_every = torch.empty(1, dtype=torch.float32, device="cuda")
+    for label, kw, ao in (("amax_out every step", {}, amax_every), ("split amax", {"split": True}, None),
+                          ("mean estimator", {"estimator": qf8.EST_MEAN}, None)):
+        calls = steps_of(qf8.DelayedState(16, 5, 3, qf8.E4M3, **kw), ao)
         calls[0]()
         e0.record(stream)
         for c in calls[1:]:

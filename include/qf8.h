@@ -161,7 +161,9 @@ int qf8_delayed_reset(qf8_delayed_state *st, void *stream);
  * at qf8_workspace_bytes.
  * Steps after the first are two kernel launches: the cast, which also raises atomic amax
  * maxima in the workspace, and a one-workgroup finalize that reads and clears them and updates
- * the state. Step 0 is the current-scaling path of quantize_per_tensor, then the finalize. */
+ * the state. A reuse step (not an update step, no QF8_DELAYED_SPLIT_AMAX) called with
+ * scale_used, amax_out and nonfinite all NULL is the cast alone: its amax would only be
+ * reported. Step 0 is the current-scaling path of quantize_per_tensor, then the finalize. */
 int quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, qf8_delayed_state *st,
                      uint8_t *q, float *scale_used, float *amax_out, int32_t *nonfinite,
                      void *ws, size_t ws_bytes, void *stream);

@@ -190,6 +190,13 @@ int quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, qf8_d
             lo = k * qn + (k * rn) / I;
             hi = (k + 1) * qn + ((k + 1) * rn) / I;
         }
+        if (!update && !split && !scale_used && !amax_out && !nonfinite) {
+            // a reuse step whose caller wants no diagnostics: the cast alone (its amax would
+            // only be reported, and the state does not change)
+            r = qf8::launch_cast_scaled(x, dtype, n, st->fmt, st->scale, q, grid, s);
+            if (r == QF8_OK) st->step++;
+            return r;
+        }
         r = qf8::launch_cast_fused(x, dtype, n, st->fmt, st->scale, q, scale_used, slots, split, lo, hi, grid, s);
         if (r == QF8_OK)
             r = qf8::launch_delayed_finalize(slots, partials, 0, st->history, st->meta, st->scale, st->hist_len,

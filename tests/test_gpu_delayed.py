@@ -305,3 +305,48 @@ def test_workspace_clean_after_steps():
             assert_bytes_equal(host(q), wq, "q", f" [{rows}x{cols} split={split} t={t}]")
             words = host(ws.view(torch.int32)[:qf8.BARRIER_WORDS])
             assert not words.any(), f"workspace not left zero [{rows}x{cols} split={split} t={t}]"
+
+
+@pytest.mark.parametrize("interval", [1, 3, 5])
+def test_reuse_steps_without_diagnostics(interval):
+    """Steps called with no scale_used / amax_out / nonfinite: reuse steps are the cast alone.
+    Codes and history still follow the oracle at every step, and the workspace stays clean."""
+    rng = np.random.default_rng(40 + interval)
+    st = qf8.DelayedState(8, interval, 2, qf8.E4M3)
+    orc = O.Delayed(8, interval, 2, O.E4M3)
+    ws = qf8.workspace(torch.empty(1, device="cuda"))
+    base = (small_tensor(129, 1000, seed=interval).astype(np.uint32) << 16).view(np.float32)
+    for t in range(4 * interval + 3):
+        x = bf16_bits(base * np.float32(2.0 ** rng.uniform(-8, 8)))
+        q = qf8.quantize_delayed(to_device(x), st, ws=ws)
+        torch.cuda.synchronize()
+        wq, _, _, _ = orc.step(x)
+        assert_bytes_equal(host(q), wq, "q", f" [I={interval} t={t}]")
+        assert st.history_list() == list(orc.state()[0]), f"history I={interval} t={t}"
+    assert not host(ws.view(torch.int32)[:qf8.BARRIER_WORDS]).any()
+
+
+def test_full_size_without_diagnostics_on_reuse_steps():
+    """The drifting workload with diagnostics asked for on update steps only (reuse steps are the
+    cast alone): every step's codes on sampled rows, the scale of update steps, the history."""
+    z = delayed_base()
+    sig = delayed_sigmas()
+    zd = torch.from_numpy(z).cuda()
+    st = qf8.DelayedState(16, 5, 3, qf8.E4M3)
+    orc = O.Delayed(16, 5, 3, O.E4M3)
+    s = torch.zeros(1, dtype=torch.float32, device="cuda")
+    ws = qf8.workspace(zd)
+    q = torch.empty(z.shape, dtype=torch.uint8, device="cuda")
+    rows = np.random.default_rng(1).choice(z.shape[0], 32, replace=False)
+    zmax = float(np.max(np.abs(z)))
+    for t in range(21):
+        xd = (zd * float(sig[t])).to(torch.bfloat16)
+        update = t % 5 == 0
+        qf8.quantize_delayed(xd, st, q=q, scale_used=s if update else None, ws=ws)
+        torch.cuda.synchronize()
+        _, s_o, _, _ = orc.step(bf16_bits(np.array([[np.float32(sig[t]) * np.float32(zmax)]], np.float32)))
+        if update:
+            assert np.float32(s.item()) == s_o, f"scale t={t}"
+        want = O.cast(delayed_step_input(z[rows], sig[t]), O.E4M3, s_o)
+        assert_bytes_equal(host(q)[rows], want, "q", f" [sampled rows t={t}]")
+    assert st.history_list() == list(orc.state()[0])
