@@ -22,6 +22,8 @@ constexpr int kMaxStreamGrid = 16384;  // workgroups of the streaming kernels at
 //                             64-bit word), [2] give-up timeout of a waiting workgroup in 10 ns
 //                             ticks (0 = default 1 ms)
 //   kBarMaxGroups lines of kBarLineWords words (128 B each): the release line of each workgroup
+//                             (words 0-1); words 16-17 of every 16th line are a first-level
+//                             barrier word of the single-pass kernel
 //   kSlotCount lines of kBarLineWords words: word 0 of each is a running |amax| maximum that the
 //                             fused delayed-scaling cast raises atomically and the finalize
 //                             kernel reads and clears

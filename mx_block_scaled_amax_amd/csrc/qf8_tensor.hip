@@ -354,14 +354,20 @@ __global__ __launch_bounds__(kThreads) void cast_fused_kernel(const void *__rest
 // is read from HBM exactly once; slabs beyond that are reduced in the first pass and re-read
 // for the cast.
 //
-// Grid barrier (workspace words 0-1 = one 64-bit word: running amax low, arrival count high; all
-// device-scope atomics on the same 8 bytes):
-//   every workgroup: 32-bit fetch_max on the low word with its |amax|, waiting for the returned
-//     value so the maximum is performed before the arrival; then a 64-bit fetch_add of 2^32,
-//     whose returned value carries both the count and the maximum of every earlier arrival.
-//   the workgroup that sees count == G - 1 arrived last and so already holds the final maximum:
-//     it returns the word to 0 and releases each other workgroup by exchanging RELEASED | amax
-//     into that workgroup's own 128-byte line (one line per poller: no same-address polling).
+// Grid barrier. A barrier word is 64 bits: running amax low, arrival count high. Arrival is in
+// two levels, because device-scope atomics on one address are performed one after another at
+// the memory side (256 workgroups x 2 atomics on a single word took ~8 µs on MI355X, groups of
+// 16 bring it to ~2.5 µs):
+//   every workgroup arrives at its group's word (groups of kBarGroup consecutive workgroups;
+//     the word is words 16-17 of the release line of the group's first workgroup): a 32-bit
+//     fetch_max on the low half, waiting for the returned value so the maximum is performed
+//     before the arrival, then a 64-bit fetch_add of 2^32, whose returned value carries both the
+//     count and the maximum of every earlier arrival.
+//   the group's last arriver zeroes the group word and arrives the same way at the header word
+//     (workspace words 0-1) with the group maximum; the one that completes the header word
+//     holds the final maximum: it zeroes that word and releases each other workgroup by
+//     exchanging RELEASED | amax into words 0-1 of that workgroup's own 128-byte line (one line
+//     per poller: no same-address polling).
 //   every other workgroup polls its own line. If it is not released within the timeout it
 //     tries to mark the line GAVE_UP (compare-exchange from 0) and exits without casting; the
 //     last workgroup then finds GAVE_UP in the exchange result and casts all of that
@@ -369,6 +375,8 @@ __global__ __launch_bounds__(kThreads) void cast_fused_kernel(const void *__rest
 //     at once (another kernel may occupy CUs): it only gets slower. Each waiter clears its own
 //     line after reading it, so the workspace is back to all-zero when the kernel ends.
 
+constexpr int kBarGroup = 16;                       // workgroups per first-level barrier word
+constexpr int kBarGroupWord = 16;                   // its u32 offset in the group's first line
 constexpr uint64_t kLineReleased = 1ull << 32;
 constexpr uint64_t kLineGaveUp = 2ull << 32;
 constexpr uint32_t kDefaultGiveUpTicks = 100000;   // 1 ms of the 100 MHz real-time counter
@@ -459,6 +467,20 @@ __device__ __forceinline__ uint32_t stream_slabs8(const uint4 *x, int64_t nvec, 
     return a;
 }
 
+// One arrival at a barrier word [amax | count << 32] shared by `expected` arrivals: raise the
+// maximum (waiting for the atomic to be performed, so it is in the word before this arrival is
+// counted), then count. The last arrival gets true and the maximum over all arrivals in *total,
+// and zeroes the word for the next call.
+__device__ __forceinline__ bool arrive(uint64_t *word, uint32_t m, uint32_t expected, uint32_t &total) {
+    const uint32_t prev = __hip_atomic_fetch_max((uint32_t *)word, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::"v"(prev) : "memory");
+    const uint64_t old = __hip_atomic_fetch_add(word, 1ull << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(old >> 32) != expected - 1) return false;
+    total = umax((uint32_t)old, m);
+    __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+}
+
 template <bool BF16, int FMT, int OP>
 __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
         const void *__restrict__ x, int64_t n, int64_t nvec, uint8_t *__restrict__ q, uint8_t *__restrict__ sb,
@@ -513,16 +535,15 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
     uint64_t *lines = (uint64_t *)(ws + kBarHeaderWords);
     uint64_t *own = lines + (size_t)b * (kBarLineWords / 2);
     if (t == 0) {
-        uint64_t *word = (uint64_t *)ws;                              // [amax | count << 32]
-        const uint32_t prev = __hip_atomic_fetch_max(ws, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        asm volatile("s_waitcnt vmcnt(0)" ::"v"(prev) : "memory");   // maximum performed before arriving
-        const uint64_t old = __hip_atomic_fetch_add(word, 1ull << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // arrival in two levels: the group's word, then (the group's last arriver) the header word
+        const int grp = b / kBarGroup, ngrp = (G + kBarGroup - 1) / kBarGroup;
+        const uint32_t gsize = (uint32_t)min(kBarGroup, G - grp * kBarGroup);
         uint32_t role = 0, am = 0;
-        if ((uint32_t)(old >> 32) == (uint32_t)G - 1) {
-            am = umax((uint32_t)old, m);
-            __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t gm = 0;
+        if (arrive(lines + (size_t)grp * kBarGroup * (kBarLineWords / 2) + kBarGroupWord / 2, m, gsize, gm) &&
+            arrive((uint64_t *)ws, gm, (uint32_t)ngrp, am))
             role = 1;
-        } else {
+        if (role == 0) {
             const uint32_t limit = ws[2] ? ws[2] : kDefaultGiveUpTicks;
             const uint64_t start = __builtin_amdgcn_s_memrealtime();
             uint64_t v;
