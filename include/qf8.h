@@ -75,6 +75,16 @@ const char *qf8_status_string(int status);
  * workgroup, in 10 ns ticks (tests set it tiny to exercise that path). */
 size_t qf8_workspace_bytes(int64_t rows, int64_t cols, int dtype);
 
+/* Sets the number of workgroups of the single-pass kernel (quantize_per_tensor from 2^22
+ * elements, delayed-scaling step 0, quantize_nvfp4 with a measured amax) on the current device:
+ * grid in [1, 512], or 0 for the default of one workgroup per CU. A tuning and test hook: a grid
+ * larger than the number of workgroups that fit on the device at once still gives the same
+ * bytes (waiters give their slabs to the last workgroup after the give-up timeout), only
+ * slower. The setting is per process and device and applies to calls made after it; calls
+ * already enqueued keep their grid. Returns QF8_ERR_SHAPE for a grid outside [0, 512] (checked
+ * before any HIP call), QF8_ERR_HIP if the current device cannot be queried. */
+int qf8_set_onepass_grid(int grid);
+
 /* Enqueues a zero fill of the qf8_workspace_bytes() bytes at ws (16-byte aligned, ws_bytes at
  * least that size) on stream. */
 int qf8_workspace_init(void *ws, size_t ws_bytes, void *stream);

@@ -17,7 +17,7 @@ import torch  # loaded first: the library binds to the HIP runtime torch has alr
 
 __all__ = [
     "E4M3", "E5M2", "ROUND_DOWN", "ROUND_UP", "QF8Error", "library_path",
-    "qf8_status_string", "qf8_workspace_bytes", "qf8_cast_scaled", "quantize_per_tensor",
+    "qf8_status_string", "qf8_workspace_bytes", "qf8_set_onepass_grid", "qf8_cast_scaled", "quantize_per_tensor",
     "DelayedState", "qf8_delayed_init", "qf8_delayed_init_ex", "qf8_delayed_reset", "quantize_delayed",
     "EST_MAX", "EST_RECENT", "EST_MEAN", "DELAYED_SPLIT_AMAX",
     "quantize_block", "quantize_mx_dual", "quantize_mxfp4_dual", "quantize_nvfp4", "dequantize_mxfp4",
@@ -66,6 +66,7 @@ def _load():
         "qf8_status_string": (ctypes.c_char_p, [i32]),
         "qf8_workspace_bytes": (sz, [i64, i64, i32]),
         "qf8_workspace_init": (i32, [vp, sz, vp]),
+        "qf8_set_onepass_grid": (i32, [i32]),
         "qf8_cast_scaled": (i32, [vp, i32, i64, i32, vp, vp, vp]),
         "quantize_per_tensor": (i32, [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, sz, vp]),
         "qf8_delayed_init": (i32, [ctypes.POINTER(_DelayedStruct), vp, vp, vp, i32, i32, i32, i32, vp]),
@@ -154,6 +155,11 @@ def qf8_workspace_bytes(rows, cols, dtype=torch.bfloat16):
 # single-pass kernel.
 BARRIER_WORDS = 32 + 512 * 32 + 256 * 32
 ONEPASS_MIN_ELEMS = 1 << 22
+
+
+def qf8_set_onepass_grid(grid):
+    """Workgroups of the single-pass kernel on the current device (1..512), 0 = one per CU."""
+    _check(_load().qf8_set_onepass_grid(int(grid)), "qf8_set_onepass_grid")
 
 
 def qf8_workspace_init(ws, stream=None):

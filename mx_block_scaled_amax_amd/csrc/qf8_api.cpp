@@ -70,6 +70,11 @@ int qf8_workspace_init(void *ws, size_t ws_bytes, void *stream) {
     return qf8::launch_fill_u32((uint32_t *)ws, (int64_t)(qf8::kWorkspaceBytes / 4), 0u, as_stream(stream));
 }
 
+int qf8_set_onepass_grid(int grid) {
+    if (grid < 0 || grid > qf8::kBarMaxGroups) return QF8_ERR_SHAPE;
+    return qf8::set_onepass_grid(grid);
+}
+
 int qf8_cast_scaled(const void *x, int dtype, int64_t n, int fmt, const float *scale, uint8_t *q, void *stream) {
     if (!dtype_ok(dtype) || !fmt_ok(fmt)) return QF8_ERR_ENUM;
     if (n < 0) return QF8_ERR_SHAPE;

@@ -41,6 +41,8 @@ constexpr size_t kWorkspaceBytes = (kPartialsOffsetWords + kMaxStreamGrid) * siz
 // workgroup per CU), or 0 when the two-kernel path is used instead (small tensors, or a device
 // where one workgroup per CU does not fit).
 int onepass_grid(int64_t n, int dtype);
+// Overrides that grid on the current device (grid in [1, kBarMaxGroups], 0 = default).
+int set_onepass_grid(int grid);
 int launch_nvfp4_onepass(const void *x, int dtype, int64_t n, uint8_t *q, uint8_t *s_blk, uint32_t *ws,
                          float *tensor_scale, float *amax_out, int32_t *nonfinite, int grid, hipStream_t s);
 int launch_per_tensor_onepass(const void *x, int dtype, int64_t n, int fmt, uint8_t *q, uint32_t *ws,

@@ -718,6 +718,7 @@ namespace {
 constexpr int64_t kOnePassMinElems = 1 << 22;
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_onepass_grid[kMaxDevices][2];   // 0 = not yet known, -1 = not usable
+std::atomic<int> g_onepass_override[kMaxDevices];  // 0 = one workgroup per CU
 
 int query_onepass_grid(int dtype) {
     int dev = 0, cus = 0, occ = 0;
@@ -739,7 +740,18 @@ int query_onepass_grid(int dtype) {
 int onepass_grid(int64_t n, int dtype) {
     if (n < kOnePassMinElems) return 0;
     const int g = query_onepass_grid(dtype);
-    return g > 0 ? g : 0;
+    if (g <= 0) return 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return g;
+    const int o = g_onepass_override[dev].load(std::memory_order_relaxed);
+    return o > 0 ? o : g;
+}
+
+int set_onepass_grid(int grid) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QF8_ERR_HIP;
+    g_onepass_override[dev].store(grid, std::memory_order_relaxed);
+    return QF8_OK;
 }
 
 int launch_per_tensor_onepass(const void *x, int dtype, int64_t n, int fmt, uint8_t *q, uint32_t *ws,

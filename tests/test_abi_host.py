@@ -44,6 +44,14 @@ def test_status_strings():
     assert qf8.qf8_workspace_bytes(8192, 8192) >= 2048 * 4
 
 
+def test_set_onepass_grid_range():
+    """The grid is range-checked before any HIP call."""
+    f = lib().qf8_set_onepass_grid
+    assert f(-1) == SHAPE
+    assert f(513) == SHAPE
+    assert f(1 << 30) == SHAPE
+
+
 def test_mx_argument_errors():
     f = lib().quantize_mx_dual
     assert f(FAKE, 0, 64, 64, 2, 0, FAKE, FAKE, None, None, None, None) == ENUM    # bad fmt

@@ -325,6 +325,19 @@ def test_nvfp4_single_pass_give_up(gradient_full, ticks):
     check_nv_big(gradient_full[:2048], ws, "default timeout after a give-up run")
 
 
+@pytest.mark.parametrize("grid", [17, 300])
+def test_nvfp4_single_pass_other_grids(grid):
+    """Other workgroup counts of the single-pass kernel: a ragged last barrier group (17), and
+    more workgroups than fit at once on a 256-CU device (300: the late ones find given-up
+    waiters, whose slabs the last workgroup casts)."""
+    ws = qf8.workspace(torch.empty(1, device="cuda"))
+    qf8.qf8_set_onepass_grid(grid)
+    try:
+        check_nv_big(mx_gradient(2048, 4096, seed=40 + grid), ws, f"grid {grid}")
+    finally:
+        qf8.qf8_set_onepass_grid(0)
+
+
 # ---- FP4 de-scaling ------------------------------------------------------------------------------
 
 def _f32_equal(got, want, what):

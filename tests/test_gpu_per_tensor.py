@@ -218,6 +218,23 @@ def test_onepass_give_up_path(activation_full, ticks):
     check_big(activation_full, O.E4M3, ws, "default timeout after a give-up run")
 
 
+@pytest.mark.parametrize("grid", [1, 17, 250, 300])
+def test_onepass_other_grids(grid):
+    """The single-pass kernel with other workgroup counts: one workgroup; 17 and 250 (the last
+    barrier group of 16 is ragged: 1 and 10 workgroups); 300 on a 256-CU device, where 44
+    workgroups only become resident after waiters have given up, so the last one casts their
+    slabs. A tensor above the 128 MiB held on chip by 256 workgroups also streams slabs."""
+    ws = qf8.workspace(torch.empty(1, device="cuda"))
+    qf8.qf8_set_onepass_grid(grid)
+    try:
+        for n, seed in ((qf8.ONEPASS_MIN_ELEMS + 24, 31 + grid), ((3 << 22) + 5, 32 + grid)):
+            print(f"onepass grid={grid} n={n}", flush=True)
+            x = small_tensor(1, n, seed=seed)
+            check_big(x, O.E4M3 if seed % 2 else O.E5M2, ws, f"grid {grid}, n={n}")
+    finally:
+        qf8.qf8_set_onepass_grid(0)
+
+
 def test_onepass_workspace_reuse():
     """One workspace across calls of both paths and several sizes, in a row on one stream."""
     ws = qf8.workspace(torch.empty(1, device="cuda"))
