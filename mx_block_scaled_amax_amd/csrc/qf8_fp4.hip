@@ -38,7 +38,8 @@ namespace qf8 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTileRows = 128;
+constexpr int kTileRows = 128;              // MXFP4 rowwise only
+constexpr int kColTileRows = 256;           // MXFP4 with the columnwise direction
 constexpr int kRowsPerWave = 32;
 constexpr int kRowsPerLane = kRowsPerWave / 2;
 constexpr uint32_t kE2M1Emax = 2;              // 6 = 1.5 * 2^2
@@ -70,23 +71,30 @@ __device__ __forceinline__ uint32_t fp4_f32(uint32_t old, float a, float b, floa
 }
 
 // Offset of the 8-byte unit u (rows 16u .. 16u+15, packed) of tile column c in the columnwise
-// LDS tile: one 64-byte line per column (128 rows, two codes per byte). The lines of each group
-// of 4 columns are permuted by bits 3-4 of c and the units' 16-byte pairs by bits 5-6, so that
-// the 32 lanes of a half-wave, whose columns are 8 apart, write different banks; a 16-byte pair
-// (units 2j, 2j+1) stays contiguous and in order.
+// LDS tile of TR rows: one TR/2-byte line per column (two codes per byte). 128 rows: the lines
+// of each group of 4 columns are permuted by bits 3-4 of c and the units' 16-byte pairs by bits
+// 5-6, so that the 32 lanes of a half-wave, whose columns are 8 apart, write different banks.
+// 256 rows: the 16-byte pairs of a line are permuted by bits 3-5 of c. A 16-byte pair (units
+// 2j, 2j+1) stays contiguous and in order.
+template <int TR>
 __device__ __forceinline__ int fp4_col_offset(int c, int u) {
-    return ((c ^ ((c >> 3) & 3)) << 6) + ((u ^ (((c >> 5) & 3) << 1)) << 3);
+    if constexpr (TR == 128) return ((c ^ ((c >> 3) & 3)) << 6) + ((u ^ (((c >> 5) & 3) << 1)) << 3);
+    else return c * (TR / 2) + ((((u >> 1) ^ ((c >> 3) & (TR / 32 - 1)))) << 4) + ((u & 1) << 3);
 }
 
 // ---------------------------------------------------------------------------------------------
-// MXFP4: the tiling of the MXFP8 kernel. A workgroup of 4 waves owns 128 rows x (32 * VEC)
-// columns; lane l of a wave owns VEC columns (slot l % 32) of 16 rows (half l / 32 of the wave's
-// 32 rows) in 16 x 16-byte registers. Rowwise: block amax over 32/VEC lanes by DPP, VEC codes
-// of a row leave as VEC/2 bytes. Columnwise: a column's block spans lanes l and l ^ 32; each
-// lane packs its 16 rows into 8 bytes per column, staged in LDS, and the workgroup writes each
-// column's 64 bytes of q_colT (and the E8M0 bytes of both directions) after one barrier.
-template <bool BF16, int RND, bool ROW, bool COL>
-__global__ __launch_bounds__(kThreads) void mxfp4_kernel(const void *__restrict__ x, int rows, int cols,
+// MXFP4: the tiling of the MXFP8 kernel, with TR rows per tile. A workgroup of TR / 32 waves
+// owns TR rows x (32 * VEC) columns; lane l of a wave owns VEC columns (slot l % 32) of 16 rows
+// (half l / 32 of the wave's 32 rows) in 16 x 16-byte registers. Rowwise: block amax over
+// 32/VEC lanes by DPP, VEC codes of a row leave as VEC/2 bytes. Columnwise: a column's block
+// spans lanes l and l ^ 32; each lane packs its 16 rows into 8 bytes per column, staged in
+// LDS, and the workgroup writes each column's TR / 2 bytes of q_colT (and the E8M0 bytes of
+// both directions) after one barrier. With the columnwise direction TR = 256: a tile column is
+// then one whole 128-byte line of q_colT and its E8M0 bytes one 8-byte store (with 128 rows,
+// half lines and 4-byte stores, the dual kernel took 41.8 instead of 39.1 µs on 16384x4096
+// BF16 on MI355X; 512 rows took 43.4 µs).
+template <bool BF16, int RND, bool ROW, bool COL, int TR>
+__global__ __launch_bounds__(2 * TR) void mxfp4_kernel(const void *__restrict__ x, int rows, int cols,
                                                          uint8_t *__restrict__ q_row, uint8_t *__restrict__ s_row,
                                                          uint8_t *__restrict__ q_colT, uint8_t *__restrict__ s_colT,
                                                          int32_t *nonfinite, int tiles_c, int tiles, int per_xcd) {
@@ -97,18 +105,20 @@ __global__ __launch_bounds__(kThreads) void mxfp4_kernel(const void *__restrict_
     constexpr int TILE_C = 32 * VEC;
     constexpr int NBLK = TILE_C / 32;            // rowwise blocks per tile row
     constexpr uint32_t ABS = BF16 ? 0x7FFF7FFFu : 0x7FFFFFFFu;
+    constexpr int NT = 2 * TR;                   // threads: one wave per 32 rows
+    constexpr int NRB = TR / 32;                 // columnwise blocks per tile column
 
-    __shared__ __attribute__((aligned(16))) uint8_t colbuf[COL ? TILE_C * (kTileRows / 2) : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t scol[COL ? TILE_C * 4 : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t srow[(ROW && COL) ? kTileRows * NBLK : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t colbuf[COL ? TILE_C * (TR / 2) : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t scol[COL ? TILE_C * NRB : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t srow[(ROW && COL) ? TR * NBLK : 16];
 
     const int b = blockIdx.x, xcd = b & 7, local = b >> 3;
     const int t = xcd * per_xcd + local;
     if (local >= per_xcd || t >= tiles) return;  // whole workgroup idle
     const int tr = t / tiles_c, tc = t - tr * tiles_c;
-    const int tr0 = tr * kTileRows, ct0 = tc * TILE_C;
+    const int tr0 = tr * TR, ct0 = tc * TILE_C;
     const int ncv = cols - ct0 < TILE_C ? cols - ct0 : TILE_C;
-    const int trows = rows - tr0 < kTileRows ? rows - tr0 : kTileRows;
+    const int trows = rows - tr0 < TR ? rows - tr0 : TR;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63, half = lane >> 5, slot = lane & 31;
     const int r0 = tr0 + wave * kRowsPerWave;
@@ -214,11 +224,11 @@ __global__ __launch_bounds__(kThreads) void mxfp4_kernel(const void *__restrict_
                     if (alo == 0u) olo[0] = olo[1] = 0u;
                     if (ahi == 0u) ohi[0] = ohi[1] = 0u;
                     const int clo = slot * VEC + 2 * k;
-                    *(uint2 *)(colbuf + fp4_col_offset(clo, unit)) = make_uint2(olo[0], olo[1]);
-                    *(uint2 *)(colbuf + fp4_col_offset(clo + 1, unit)) = make_uint2(ohi[0], ohi[1]);
+                    *(uint2 *)(colbuf + fp4_col_offset<TR>(clo, unit)) = make_uint2(olo[0], olo[1]);
+                    *(uint2 *)(colbuf + fp4_col_offset<TR>(clo + 1, unit)) = make_uint2(ohi[0], ohi[1]);
                     if (half == 0) {
-                        scol[clo * 4 + wave] = (uint8_t)blo;
-                        scol[(clo + 1) * 4 + wave] = (uint8_t)bhi;
+                        scol[clo * NRB + wave] = (uint8_t)blo;
+                        scol[(clo + 1) * NRB + wave] = (uint8_t)bhi;
                     }
                 }
             } else {
@@ -241,8 +251,8 @@ __global__ __launch_bounds__(kThreads) void mxfp4_kernel(const void *__restrict_
                     }
                     if (a == 0u) o[0] = o[1] = 0u;
                     const int c = slot * VEC + k;
-                    *(uint2 *)(colbuf + fp4_col_offset(c, unit)) = make_uint2(o[0], o[1]);
-                    if (half == 0) scol[c * 4 + wave] = (uint8_t)byte;
+                    *(uint2 *)(colbuf + fp4_col_offset<TR>(c, unit)) = make_uint2(o[0], o[1]);
+                    if (half == 0) scol[c * NRB + wave] = (uint8_t)byte;
                 }
             }
         }
@@ -255,24 +265,36 @@ __global__ __launch_bounds__(kThreads) void mxfp4_kernel(const void *__restrict_
         const __amdgpu_buffer_rsrc_t qc = make_rsrc(q_colT + (size_t)ct0 * cstride + tr0 / 2,
                                                     (uint32_t)ncv * cstride - tr0 / 2);
 #pragma unroll
-        for (int e = threadIdx.x; e < TILE_C * 4; e += kThreads) {
-            const int c = e >> 2, j = e & 3;     // 16-byte chunk j = rows 32j .. 32j+31
-            const uint4 v = *(const uint4 *)(colbuf + fp4_col_offset(c, 2 * j));
+        for (int e = threadIdx.x; e < TILE_C * NRB; e += NT) {
+            const int c = e / NRB, j = e % NRB;  // 16-byte chunk j = rows 32j .. 32j+31
+            const uint4 v = *(const uint4 *)(colbuf + fp4_col_offset<TR>(c, 2 * j));
             const uint32_t vo = (c < ncv && 32 * j < trows) ? (uint32_t)c * cstride + 16 * j : kOutOfRange;
             buf_store16<kNonTemporal>(qc, vo, 0u, v);
         }
         const uint32_t srb = (uint32_t)rows / 32;
         const int nb = trows / 32;
         const __amdgpu_buffer_rsrc_t scr = make_rsrc(s_colT + (size_t)ct0 * srb + tr0 / 32, (uint32_t)ncv * srb - tr0 / 32);
-        const bool whole_c = nb == 4 && (srb & 3u) == 0 && (((uintptr_t)s_colT) & 3u) == 0;
-        for (int c = threadIdx.x; c < TILE_C; c += kThreads) {
-            const uint32_t w = *(const uint32_t *)(scol + c * 4);
-            if (whole_c) {
-                buf_store4(scr, c < ncv ? (uint32_t)c * srb : kOutOfRange, 0u, w);
-            } else {
+        const bool whole_c = nb == NRB && (srb % NRB) == 0 && (((uintptr_t)s_colT) % NRB) == 0;
+        for (int c = threadIdx.x; c < TILE_C; c += NT) {
+            if constexpr (NRB == 8) {
+                const uint2 w = *(const uint2 *)(scol + c * 8);
+                if (whole_c) {
+                    buf_store8(scr, c < ncv ? (uint32_t)c * srb : kOutOfRange, 0u, w.x, w.y);
+                } else {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    buf_store1(scr, (c < ncv && j < nb) ? (uint32_t)c * srb + j : kOutOfRange, 0u, w >> (8 * j));
+                    for (int j = 0; j < 8; ++j)
+                        buf_store1(scr, (c < ncv && j < nb) ? (uint32_t)c * srb + j : kOutOfRange, 0u,
+                                   (j < 4 ? w.x : w.y) >> (8 * (j & 3)));
+                }
+            } else {
+                const uint32_t w = *(const uint32_t *)(scol + c * 4);
+                if (whole_c) {
+                    buf_store4(scr, c < ncv ? (uint32_t)c * srb : kOutOfRange, 0u, w);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        buf_store1(scr, (c < ncv && j < nb) ? (uint32_t)c * srb + j : kOutOfRange, 0u, w >> (8 * j));
+                }
             }
         }
         if constexpr (ROW) {
@@ -281,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void mxfp4_kernel(const void *__restrict_
             const __amdgpu_buffer_rsrc_t srr = make_rsrc(s_row + (size_t)tr0 * ssb + ct0 / 32,
                                                          (uint32_t)trows * ssb - ct0 / 32);
             const bool whole_r = nbl == NBLK && (ssb % NBLK) == 0 && (((uintptr_t)s_row) % NBLK) == 0;
-            for (int r = threadIdx.x; r < kTileRows; r += kThreads) {
+            for (int r = threadIdx.x; r < TR; r += NT) {
                 const bool rv = r < trows;
                 if constexpr (NBLK == 8) {
                     const uint2 w = *(const uint2 *)(srow + r * 8);
@@ -313,20 +335,23 @@ template <bool BF16, int RND>
 void launch_mxfp4_dirs(const void *x, int rows, int cols, uint8_t *q_row, uint8_t *s_row, uint8_t *q_colT,
                        uint8_t *s_colT, int32_t *nonfinite, hipStream_t s) {
     constexpr int VEC = BF16 ? 8 : 4;
-    const int tiles_r = (rows + kTileRows - 1) / kTileRows;
+    // the columnwise direction takes tiles of kColTileRows rows, so that a tile column's codes
+    // are whole 128-byte lines of q_colT; rowwise alone keeps kTileRows
+    const int tr = q_colT ? kColTileRows : kTileRows;
+    const int tiles_r = (rows + tr - 1) / tr;
     const int tiles_c = (cols + 32 * VEC - 1) / (32 * VEC);
     const int tiles = tiles_r * tiles_c;
     const int per_xcd = (tiles + 7) / 8;
-    const dim3 grid(8 * per_xcd), block(kThreads);
+    const dim3 grid(8 * per_xcd), block(2 * tr);
     if (q_row && q_colT)
-        hipLaunchKernelGGL((mxfp4_kernel<BF16, RND, true, true>), grid, block, 0, s, x, rows, cols, q_row, s_row,
-                           q_colT, s_colT, nonfinite, tiles_c, tiles, per_xcd);
+        hipLaunchKernelGGL((mxfp4_kernel<BF16, RND, true, true, kColTileRows>), grid, block, 0, s, x, rows, cols,
+                           q_row, s_row, q_colT, s_colT, nonfinite, tiles_c, tiles, per_xcd);
     else if (q_row)
-        hipLaunchKernelGGL((mxfp4_kernel<BF16, RND, true, false>), grid, block, 0, s, x, rows, cols, q_row, s_row,
-                           q_colT, s_colT, nonfinite, tiles_c, tiles, per_xcd);
+        hipLaunchKernelGGL((mxfp4_kernel<BF16, RND, true, false, kTileRows>), grid, block, 0, s, x, rows, cols,
+                           q_row, s_row, q_colT, s_colT, nonfinite, tiles_c, tiles, per_xcd);
     else
-        hipLaunchKernelGGL((mxfp4_kernel<BF16, RND, false, true>), grid, block, 0, s, x, rows, cols, q_row, s_row,
-                           q_colT, s_colT, nonfinite, tiles_c, tiles, per_xcd);
+        hipLaunchKernelGGL((mxfp4_kernel<BF16, RND, false, true, kColTileRows>), grid, block, 0, s, x, rows, cols,
+                           q_row, s_row, q_colT, s_colT, nonfinite, tiles_c, tiles, per_xcd);
 }
 
 // ---------------------------------------------------------------------------------------------

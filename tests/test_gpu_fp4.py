@@ -99,13 +99,14 @@ def test_mxfp4_exhaustive_columnwise(exhaustive, rnd):
     check_mx(np.ascontiguousarray(exhaustive.T), rnd, row=False, col=True, tag="exhaustive-col")
 
 
-@pytest.mark.parametrize("shape", [(32, 32), (64, 96), (128, 512), (256, 1024), (160, 544), (96, 1056)])
+@pytest.mark.parametrize("shape", [(32, 32), (64, 96), (128, 512), (256, 1024), (160, 544), (96, 1056), (416, 800),
+                                   (544, 256)])
 @pytest.mark.parametrize("rnd", RND, ids=RID)
 def test_mxfp4_dual_small_bf16(shape, rnd):
     check_mx(mx_gradient(*shape, seed=sum(shape)), rnd, tag="dual-bf16")
 
 
-@pytest.mark.parametrize("shape", [(32, 32), (64, 288), (160, 544)])
+@pytest.mark.parametrize("shape", [(32, 32), (64, 288), (160, 544), (288, 160)])
 @pytest.mark.parametrize("rnd", RND, ids=RID)
 def test_mxfp4_dual_small_fp32(shape, rnd):
     rng = np.random.default_rng(5)
@@ -119,6 +120,7 @@ def test_mxfp4_single_direction_and_ragged(rnd):
     check_mx(small_tensor(130, 96, seed=4), rnd, row=True, col=False, tag="row-ragged-rows")
     check_mx(small_tensor(64, 40, seed=5), rnd, row=False, col=True, tag="col-narrow")
     check_mx(small_tensor(96, 520, seed=6), rnd, row=False, col=True, tag="col-ragged-cols")
+    check_mx(small_tensor(320, 288, seed=8), rnd, row=False, col=True, tag="col-two-tile-rows")
     x = (np.random.default_rng(7).standard_normal((96, 36)) * 10).astype(np.float32)
     check_mx(x, rnd, row=False, col=True, tag="col-fp32-ragged")
 
