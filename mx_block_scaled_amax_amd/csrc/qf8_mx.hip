@@ -243,38 +243,48 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const void *__restrict__ x
     // ---- the tile's staged outputs, written by the whole workgroup ---------------------------
     if constexpr (COL) {
         __syncthreads();
-        // q_colT: column c of the tile -> q_colT[ct0 + c][tr0 .. tr0 + trows), 16 bytes per lane
+        // q_colT: column c of the tile -> q_colT[ct0 + c][tr0 .. tr0 + trows), 16 bytes per lane.
+        // Thread t writes 16-row chunk t % 8 of tile columns t / 8 + 32 j. The offsets are 32-bit and
+        // the validity tests are combined without short-circuit branches: after the barrier each
+        // store costs a handful of instructions, which shortens the tail of every workgroup.
         const __amdgpu_buffer_rsrc_t qc = make_rsrc(q_colT + (size_t)ct0 * rows + tr0, (uint32_t)ncv * rows - tr0);
+        const uint32_t urows = (uint32_t)rows, k = threadIdx.x & 7u, cb = threadIdx.x >> 3;
+        const bool kv = (int)(16u * k) < trows;
 #pragma unroll
-        for (int e = threadIdx.x; e < TILE_C * (kTileRows / 16); e += kThreads) {
-            const int c = e >> 3, k = e & 7;
-            const uint4 v = *(const uint4 *)(colbuf + colbuf_offset(c, k));
-            const uint32_t vo = (c < ncv && 16 * k < trows) ? (uint32_t)c * rows + 16 * k : kOutOfRange;
+        for (int j = 0; j < TILE_C / 32; ++j) {
+            const uint32_t c = cb + 32u * j;
+            const uint4 v = *(const uint4 *)(colbuf + colbuf_offset((int)c, (int)k));
+            const uint32_t vo = (((int)c < ncv) & kv) ? c * urows + 16u * k : kOutOfRange;
             buf_store16<kNonTemporal>(qc, vo, 0u, v);
         }
-        // s_colT: the tile's trows/32 bytes of column c, contiguous in s_colT[ct0 + c]
+        // s_colT: the tile's trows/32 bytes of column c, contiguous in s_colT[ct0 + c]; one column per
+        // thread (TILE_C <= kThreads). Whole tiles store them as one word, a ragged last tile row
+        // byte by byte (the choice is uniform over the workgroup).
+        static_assert(TILE_C <= kThreads && kTileRows <= kThreads, "one column and one row per thread");
         const uint32_t srb = (uint32_t)rows / 32;
         const int nb = trows / 32;
         const __amdgpu_buffer_rsrc_t scr = make_rsrc(s_colT + (size_t)ct0 * srb + tr0 / 32, (uint32_t)ncv * srb - tr0 / 32);
         const bool whole_c = nb == 4 && (srb & 3u) == 0 && (((uintptr_t)s_colT) & 3u) == 0;
-        for (int c = threadIdx.x; c < TILE_C; c += kThreads) {
-            const uint32_t w = *(const uint32_t *)(scol + c * 4);
+        const int ct = threadIdx.x;
+        if (ct < TILE_C) {
+            const uint32_t w = *(const uint32_t *)(scol + ct * 4);
             if (whole_c) {
-                buf_store4(scr, c < ncv ? (uint32_t)c * srb : kOutOfRange, 0u, w);
+                buf_store4(scr, ct < ncv ? (uint32_t)ct * srb : kOutOfRange, 0u, w);
             } else {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    buf_store1(scr, (c < ncv && j < nb) ? (uint32_t)c * srb + j : kOutOfRange, 0u, w >> (8 * j));
+                    buf_store1(scr, ((ct < ncv) & (j < nb)) ? (uint32_t)ct * srb + j : kOutOfRange, 0u, w >> (8 * j));
             }
         }
-        // s_row: row r of the tile -> its NBLK bytes s_row[tr0 + r][ct0/32 ...]
+        // s_row: row r of the tile -> its NBLK bytes s_row[tr0 + r][ct0/32 ...]; one row per thread
         if constexpr (ROW) {
             const uint32_t ssb = (uint32_t)cols / 32;
             const int nbl = ncv / 32;
             const __amdgpu_buffer_rsrc_t srr = make_rsrc(s_row + (size_t)tr0 * ssb + ct0 / 32,
                                                          (uint32_t)trows * ssb - ct0 / 32);
             const bool whole_r = nbl == NBLK && (ssb % NBLK) == 0 && (((uintptr_t)s_row) % NBLK) == 0;
-            for (int r = threadIdx.x; r < kTileRows; r += kThreads) {
+            const int r = threadIdx.x;
+            if (r < kTileRows) {
                 const bool rv = r < trows;
                 if constexpr (NBLK == 8) {
                     const uint2 w = *(const uint2 *)(srow + r * 8);
@@ -283,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const void *__restrict__ x
                     } else {
 #pragma unroll
                         for (int j = 0; j < 8; ++j)
-                            buf_store1(srr, (rv && j < nbl) ? (uint32_t)r * ssb + j : kOutOfRange, 0u,
+                            buf_store1(srr, (rv & (j < nbl)) ? (uint32_t)r * ssb + j : kOutOfRange, 0u,
                                        (j < 4 ? w.x : w.y) >> (8 * (j & 3)));
                     }
                 } else {
@@ -293,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const void *__restrict__ x
                     } else {
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
-                            buf_store1(srr, (rv && j < nbl) ? (uint32_t)r * ssb + j : kOutOfRange, 0u, w >> (8 * j));
+                            buf_store1(srr, (rv & (j < nbl)) ? (uint32_t)r * ssb + j : kOutOfRange, 0u, w >> (8 * j));
                     }
                 }
             }
