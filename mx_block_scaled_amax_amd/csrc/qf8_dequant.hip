@@ -56,7 +56,9 @@ struct DqArgs {
     int64_t n;
     uint32_t units;              // whole 4-code units
     uint32_t upr;                // units per row (block, MX)
-    uint32_t br;                 // block rows (block)
+    uint64_t upr_mul;            // u / upr = (u * upr_mul) >> upr_shift for every u < 2^31
+    uint32_t upr_shift;
+    uint32_t br_shift;           // log2 of the block rows, 1 or 128 (block)
     uint32_t gcols;              // groups per row of the scale array (block)
     const float *scale;          // per-tensor S (scaled) or group scales (block)
     const uint8_t *sb;           // E8M0 bytes (MX)
@@ -126,7 +128,7 @@ __device__ __forceinline__ void acc_add_unit(Acc &acc, const float *x, const flo
     }
 }
 
-// W consecutive elements of x (W = 4 or 16) of unit u.
+// W consecutive elements of x (W = 4, 8 or 16) of unit u.
 template <int XK, int W>
 __device__ __forceinline__ void load_x(const void *x, uint32_t u, float *xv) {
     if constexpr (XK == kBF16) {
@@ -135,6 +137,9 @@ __device__ __forceinline__ void load_x(const void *x, uint32_t u, float *xv) {
         if constexpr (W == 16) {
             const uint4 a0 = ((const uint4 *)p)[0], a1 = ((const uint4 *)p)[1];
             w[0] = a0.x; w[1] = a0.y; w[2] = a0.z; w[3] = a0.w; w[4] = a1.x; w[5] = a1.y; w[6] = a1.z; w[7] = a1.w;
+        } else if constexpr (W == 8) {
+            const uint4 a0 = *(const uint4 *)p;
+            w[0] = a0.x; w[1] = a0.y; w[2] = a0.z; w[3] = a0.w;
         } else {
             const uint2 a0 = *(const uint2 *)p;
             w[0] = a0.x; w[1] = a0.y;
@@ -169,13 +174,20 @@ __device__ __forceinline__ void store_out(void *out, uint32_t u, const float *v)
         if constexpr (W == 16) {
             ((uint4 *)p)[0] = make_uint4(w[0], w[1], w[2], w[3]);
             ((uint4 *)p)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        } else if constexpr (W == 8) {
+            st_stream((uint4 *)p, make_uint4(w[0], w[1], w[2], w[3]));
         } else {
             *(uint2 *)p = make_uint2(w[0], w[1]);
         }
     } else if constexpr (OUTK == kFP32) {
-        float4 *p = (float4 *)out + (size_t)u * (W / 4);
+        uint4 *p = (uint4 *)out + (size_t)u * (W / 4);
 #pragma unroll
-        for (int k = 0; k < W / 4; ++k) p[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+        for (int k = 0; k < W / 4; ++k) {
+            const uint4 o = make_uint4(__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
+                                       __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3]));
+            if constexpr (W == 4) st_stream(p + k, o);
+            else p[k] = o;
+        }
     }
 }
 template <int OUTK>
@@ -191,15 +203,21 @@ struct UnitScale {
     bool nan;     // MX byte 0xFF
 };
 
+// Row of unit u (u < 2^31) without a division instruction sequence: the multiplier and shift are
+// computed on the host (round-up reciprocal, exact below 2^31; see launch_dequant).
+__device__ __forceinline__ uint32_t unit_row(const DqArgs &a, uint32_t u) {
+    return (uint32_t)(((uint64_t)u * a.upr_mul) >> a.upr_shift);
+}
+
 // Scale of unit u (W codes, all in one row and one group: cols % W == 0, W divides 32 and 128).
 template <int FMT, int MODE, int W>
 __device__ __forceinline__ UnitScale unit_scale(const DqArgs &a, uint32_t u, float s_tensor) {
     UnitScale us{s_tensor, 0, false};
     if constexpr (MODE == kModeBlock) {
-        const uint32_t r = u / a.upr, c = (u - r * a.upr) * W;
-        us.s = a.scale[(size_t)(r / a.br) * a.gcols + (c >> 7)];
+        const uint32_t r = unit_row(a, u), c = (u - r * a.upr) * W;
+        us.s = a.scale[(size_t)(r >> a.br_shift) * a.gcols + (c >> 7)];
     } else if constexpr (MODE == kModeMx) {
-        const uint32_t r = u / a.upr, c = (u - r * a.upr) * W;
+        const uint32_t r = unit_row(a, u), c = (u - r * a.upr) * W;
         const uint32_t b = a.sb[(size_t)r * (a.upr * W / 32) + (c >> 5)];
         us.nan = b == 0xFFu;
         us.xexp = (int)b - 127;
@@ -251,13 +269,20 @@ __device__ void block_store_partial(const Acc &acc, StatsPart *dst) {
     }
 }
 
-// W = 16 (one 16-byte load of codes per unit) or 4 (one dword; groups whose rows are only a
-// multiple of 4 codes long). With one scale factor the workgroup first tabulates
+// W codes per unit. De-scaling alone takes 8 or 4, so that each lane moves one 16-byte piece of the
+// output and consecutive lanes move consecutive pieces: 8 codes (an 8-byte load) make 16 bytes of
+// BF16, 4 codes 16 bytes of FP32, and whole 16-byte outputs leave as non-temporal stores (a lane
+// writing 32 bytes as two 16-byte stores leaves every store instruction half-dense over its span,
+// which measured ~10% slower for this stream). With the statistics, whose fp64 terms make the
+// kernel VALU-bound, 16-code units (one 16-byte load of codes) halve the per-unit overhead.
+// 4-code units also serve rows that are only a multiple of 4 codes long (8-byte BF16 stores,
+// cached so that L2 merges them). With one scale factor the workgroup first tabulates
 // fl32(decode(c) / S) for all 256 codes in LDS, so an element costs a table read, not a division.
 template <int FMT, int MODE, int OUTK, int XK, int W>
 __global__ __launch_bounds__(kDqThreads) void dequant_kernel(DqArgs a) {
     constexpr bool STATS = XK != kNone;
-    constexpr int UPT = W == 16 ? 2 : 4;        // units per thread and iteration
+    static_assert(W == 16 || W == 8 || W == 4, "16-, 8- or 4-code units");
+    constexpr int UPT = 32 / W;                 // units per thread and iteration: 32 codes
     constexpr int ND = W / 4;                     // dwords of codes per unit
     __shared__ float tab[MODE == kModeScaled ? 256 : 1];
     float s_tensor = 1.0f;
@@ -281,6 +306,10 @@ __global__ __launch_bounds__(kDqThreads) void dequant_kernel(DqArgs a) {
                     typedef unsigned int v4u __attribute__((ext_vector_type(4)));
                     const v4u c = __builtin_nontemporal_load((const v4u *)a.q + u);
                     codes[j][0] = c.x; codes[j][1] = c.y; codes[j][2] = c.z; codes[j][3] = c.w;
+                } else if constexpr (W == 8) {
+                    typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+                    const v2u c = __builtin_nontemporal_load((const v2u *)a.q + u);
+                    codes[j][0] = c.x; codes[j][1] = c.y;
                 } else {
                     codes[j][0] = __builtin_nontemporal_load((const uint32_t *)a.q + u);
                 }
@@ -362,10 +391,17 @@ __global__ __launch_bounds__(kDqThreads) void stats_finalize_kernel(const StatsP
 
 template <int FMT, int MODE, int OUTK, int XK>
 void launch_t(const DqArgs &a, int w, int grid, hipStream_t s) {
-    if (w == 16)
-        hipLaunchKernelGGL((dequant_kernel<FMT, MODE, OUTK, XK, 16>), dim3(grid), dim3(kDqThreads), 0, s, a);
-    else if constexpr (MODE == kModeBlock)
-        hipLaunchKernelGGL((dequant_kernel<FMT, MODE, OUTK, XK, 4>), dim3(grid), dim3(kDqThreads), 0, s, a);
+    if constexpr (XK != kNone) {
+        if (w == 16)
+            hipLaunchKernelGGL((dequant_kernel<FMT, MODE, OUTK, XK, 16>), dim3(grid), dim3(kDqThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((dequant_kernel<FMT, MODE, OUTK, XK, 4>), dim3(grid), dim3(kDqThreads), 0, s, a);
+    } else {
+        if (w == 8)
+            hipLaunchKernelGGL((dequant_kernel<FMT, MODE, OUTK, XK, 8>), dim3(grid), dim3(kDqThreads), 0, s, a);
+        else
+            hipLaunchKernelGGL((dequant_kernel<FMT, MODE, OUTK, XK, 4>), dim3(grid), dim3(kDqThreads), 0, s, a);
+    }
 }
 template <int FMT, int MODE, int OUTK>
 void by_x(int xk, const DqArgs &a, int w, int grid, hipStream_t s) {
@@ -391,23 +427,36 @@ int launch_dequant(int mode, int fmt, const uint8_t *q, int64_t rows, int64_t co
                    const float *scale, const uint8_t *sb, void *out, int out_dtype, const void *x, int x_dtype,
                    qf8_error_stats *stats, void *ws, hipStream_t s) {
     const int64_t n = rows * cols;
-    // 16-code units wherever every unit stays inside one row (and so one group / MX block)
-    const int w = (mode == kModeScaled || cols % 16 == 0) ? 16 : 4;
+    const int outk = out ? (out_dtype == QF8_IN_BF16 ? kBF16 : kFP32) : kNone;
+    const int xk = stats ? (x_dtype == QF8_IN_BF16 ? kBF16 : kFP32) : kNone;
+    // Units stay inside one row (and so one group / MX block). With the statistics: 16 codes where
+    // rows allow it, else 4. De-scaling alone: 8 codes for BF16 output where rows allow it, else 4.
+    const bool whole_rows = mode == kModeScaled;
+    const int w = stats ? ((whole_rows || cols % 16 == 0) ? 16 : 4)
+                        : ((whole_rows || cols % 8 == 0) && outk == kBF16 ? 8 : 4);
     DqArgs a{};
     a.q = q;
     a.n = n;
     a.units = (uint32_t)(n / w);
     a.upr = (uint32_t)(cols / w);
-    a.br = (uint32_t)(block_rows > 0 ? block_rows : 1);
+    // floor(u / d) = (u * m) >> (31 + l) for all u < 2^31 with l = ceil(log2 d), m = ceil(2^(31+l) / d):
+    // m d - 2^(31+l) = e lies in [0, d), so u m / 2^(31+l) = u / d + u e / (d 2^(31+l)) and the
+    // second term is below 2^31 / 2^(31+l) <= 1 / d, too small to reach the next integer
+    {
+        const uint64_t d = a.upr > 0 ? a.upr : 1u;
+        uint32_t l = 0;
+        while ((1ull << l) < d) ++l;
+        a.upr_shift = 31u + l;
+        a.upr_mul = ((1ull << a.upr_shift) + d - 1) / d;
+    }
+    a.br_shift = block_rows == 128 ? 7u : 0u;
     a.gcols = (uint32_t)((cols + 127) / 128);
     a.scale = scale;
     a.sb = sb;
     a.out = out;
     a.x = x;
     a.parts = stats ? (StatsPart *)((uint32_t *)ws + kPartialsOffsetWords) : nullptr;
-    const int outk = out ? (out_dtype == QF8_IN_BF16 ? kBF16 : kFP32) : kNone;
-    const int xk = stats ? (x_dtype == QF8_IN_BF16 ? kBF16 : kFP32) : kNone;
-    const int64_t per_wg = (int64_t)kDqThreads * (w == 16 ? 2 : 4);
+    const int64_t per_wg = (int64_t)kDqThreads * (32 / w);
     int64_t grid = ((int64_t)a.units + per_wg - 1) / per_wg;
     const int cap = stats ? kStatsGrid : kDqMaxGrid;
     if (grid > cap) grid = cap;
