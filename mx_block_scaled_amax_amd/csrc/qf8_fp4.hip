@@ -445,11 +445,18 @@ __device__ __forceinline__ float e2m1_value(int c) {
     return (c & 8) ? -mag : mag;
 }
 
+// A unit is UC codes whose output is one 16-byte piece: 8 codes (4 bytes) for BF16, 4 codes (2
+// bytes) for FP32. Lane l of a wave handles unit base + l, so each store instruction writes one
+// dense 1 KiB run (non-temporal); a lane writing its output as several 16-byte stores would
+// leave every store instruction half- or quarter-dense over its span, which measured slower.
 template <int NV, bool OUTBF16>
 __global__ __launch_bounds__(kDqThreads) void dequant_fp4_kernel(const uint8_t *__restrict__ q,
                                                                  const uint8_t *__restrict__ sb,
                                                                  const float *__restrict__ tensor_scale,
                                                                  int64_t nunits, void *__restrict__ out) {
+    constexpr int UC = OUTBF16 ? 8 : 4;                                  // codes per unit
+    constexpr int UPT = 4;                                               // units per thread and pass
+    constexpr int BSH = (NV ? 4 : 5) - (OUTBF16 ? 3 : 2);                // unit -> scale block: u >> BSH
     __shared__ float tab[NV ? 128 * 16 : 16];
     if constexpr (NV) {
         const float st = *tensor_scale;
@@ -463,35 +470,43 @@ __global__ __launch_bounds__(kDqThreads) void dequant_fp4_kernel(const uint8_t *
         if (threadIdx.x < 16) tab[threadIdx.x] = e2m1_value((int)threadIdx.x);
     }
     __syncthreads();
-    for (int64_t u = (int64_t)blockIdx.x * kDqThreads + threadIdx.x; u < nunits; u += (int64_t)gridDim.x * kDqThreads) {
-        const uint2 w = *(const uint2 *)(q + 8 * u);
-        float v[16];
-        if constexpr (NV) {
-            const int e = sb[u];                                         // one 16-element block per unit
+    const int64_t stride = (int64_t)gridDim.x * kDqThreads * UPT;
+    for (int64_t base = (int64_t)blockIdx.x * kDqThreads * UPT + threadIdx.x; base < nunits; base += stride) {
+        uint32_t w[UPT], b[UPT];
 #pragma unroll
-            for (int k = 0; k < 16; ++k) v[k] = tab[e * 16 + (((k < 8 ? w.x : w.y) >> (4 * (k & 7))) & 15u)];
-        } else {
-            const uint32_t b = sb[u >> 1];                               // two units per 32-element block
-            const int X = (int)b - 127;
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const float d = tab[((k < 8 ? w.x : w.y) >> (4 * (k & 7))) & 15u];
-                v[k] = b == 0xFFu ? __uint_as_float(0x7FC00000u) : __builtin_ldexpf(d, X);
+        for (int j = 0; j < UPT; ++j) {
+            const int64_t u = base + (int64_t)j * kDqThreads;
+            w[j] = 0u; b[j] = 0u;
+            if (u < nunits) {
+                if constexpr (UC == 8) w[j] = *(const uint32_t *)(q + 4 * u);
+                else w[j] = *(const uint16_t *)(q + 2 * u);
+                b[j] = sb[u >> BSH];
             }
         }
-        if constexpr (OUTBF16) {
-            uint32_t o[8];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) o[k] = bf16_rne(v[2 * k]) | (bf16_rne(v[2 * k + 1]) << 16);
-            uint4 *dst = (uint4 *)out + 2 * u;
-            dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
-            dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
-        } else {
-            uint4 *dst = (uint4 *)out + 4 * u;
+        for (int j = 0; j < UPT; ++j) {
+            const int64_t u = base + (int64_t)j * kDqThreads;
+            if (u >= nunits) continue;
+            float v[UC];
+            if constexpr (NV) {
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                dst[k] = make_uint4(__float_as_uint(v[4 * k]), __float_as_uint(v[4 * k + 1]),
-                                    __float_as_uint(v[4 * k + 2]), __float_as_uint(v[4 * k + 3]));
+                for (int k = 0; k < UC; ++k) v[k] = tab[b[j] * 16 + ((w[j] >> (4 * k)) & 15u)];
+            } else {
+                const int X = (int)b[j] - 127;
+#pragma unroll
+                for (int k = 0; k < UC; ++k) {
+                    const float d = tab[(w[j] >> (4 * k)) & 15u];
+                    v[k] = b[j] == 0xFFu ? __uint_as_float(0x7FC00000u) : __builtin_ldexpf(d, X);
+                }
+            }
+            uint4 o;
+            if constexpr (OUTBF16) {
+                o = make_uint4(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16),
+                               bf16_rne(v[4]) | (bf16_rne(v[5]) << 16), bf16_rne(v[6]) | (bf16_rne(v[7]) << 16));
+            } else {
+                o = make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+            }
+            st_stream((uint4 *)out + u, o);
         }
     }
 }
@@ -506,9 +521,10 @@ int nvfp4_grid(int64_t nblk) {
 
 int launch_dequant_fp4(int nv, const uint8_t *q, const uint8_t *sb, const float *tensor_scale, int64_t n, void *out,
                        int out_dtype, hipStream_t s) {
-    const int64_t nunits = n / 16;
+    // units of 8 codes (BF16 output) or 4 codes (FP32 output); n is a multiple of 16
+    const int64_t nunits = n / (out_dtype == QF8_OUT_BF16 ? 8 : 4);
     if (nunits == 0) return QF8_OK;
-    int64_t g = (nunits + kDqThreads - 1) / kDqThreads;
+    int64_t g = (nunits + 4 * kDqThreads - 1) / (4 * kDqThreads);
     if (g > kDqMaxGrid) g = kDqMaxGrid;
     const dim3 grid((unsigned)g), block(kDqThreads);
     if (nv) {
