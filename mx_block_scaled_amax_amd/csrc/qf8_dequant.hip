@@ -20,12 +20,13 @@
 //   value beyond F8max before the cast: |fl32(x S)| > F8max, or |x| > F8max 2^X for MX) and of
 //   Inf/NaN x (excluded from the rest).
 //
-// Work: a unit is 16 consecutive codes (one 16-byte load of q; 4 codes when a group's rows are
-// only a multiple of 4 long), always inside one row, one group and one MX block, so its scale
-// is looked up once. A thread takes 2 units per iteration (consecutive threads on consecutive
-// units), decodes with the gfx950 fp8/bf8 -> f32 converts (exact), de-scales (MX: ldexp;
-// groups: IEEE division; one tensor scale: a 256-entry LDS table of decode(c) / S built per
-// workgroup) and stores 16 BF16 (32 bytes) or 16 FP32 (64 bytes). With statistics, the fp64
+// Work: a unit is 8 consecutive codes for BF16 output, 4 for FP32 output, 16 with statistics (4
+// when a group's rows are only a multiple of 4 or 8 long), always inside one row, one group and
+// one MX block, so its scale is looked up once. A thread takes 32 codes per iteration
+// (consecutive threads on consecutive units), decodes with the gfx950 fp8/bf8 -> f32 converts
+// (exact), de-scales (MX: ldexp; groups: IEEE division; one tensor scale: a 256-entry LDS table
+// of decode(c) / S built per workgroup) and stores each 8-code BF16 or 4-code FP32 unit as one
+// 16-byte piece, consecutive lanes on consecutive pieces. With statistics, the fp64
 // terms go to 4 independent running sums per thread (short dependency chains); each
 // workgroup reduces its sums and counts in a fixed order into a 64-byte partial in the
 // workspace, and one workgroup folds the partials in a fixed order: the same input always gives

@@ -428,7 +428,8 @@ __global__ __launch_bounds__(kThreads) void nvfp4_kernel(const void *__restrict_
 }
 
 // ---------------------------------------------------------------------------------------------
-// FP4 de-scaling. One thread per unit of 16 codes (8 bytes), taken in flattened order: element i
+// FP4 de-scaling. Units of 8 codes (BF16 output) or 4 codes (FP32 output), taken in flattened
+// order, one 16-byte output piece each: element i
 // belongs to MX block i / 32 (cols % 32 == 0) or NVFP4 block i / 16 (cols % 16 == 0), whose scale
 // bytes are contiguous in the same order. MXFP4: decode(c) * 2^X is exact in fp32 for every code
 // and X >= -127 (at most two significant bits, at least 2^-128), or Inf, and NaN for byte 0xFF.
