@@ -383,11 +383,19 @@ __global__ __launch_bounds__(kThreads) void nvfp4_kernel(const void *__restrict_
     }
     constexpr int NV = BF16 ? 2 : 4;             // 16-byte loads per block
     const uint4 *xv = (const uint4 *)x;
+    __shared__ __attribute__((aligned(16))) uint8_t sbuf[kThreads];
+    // The workgroup's 256 consecutive blocks per pass have 256 consecutive scale bytes: gathered
+    // in LDS, they leave as 16 non-temporal 16-byte stores (single cached bytes from every thread
+    // cost several times more per byte on this path); a ragged last pass or an s_blk that is not
+    // 16-byte aligned stores bytes.
+    const bool sb_aligned = (((uintptr_t)s_blk) & 15u) == 0;
     bool bad = false;
-    for (int64_t blk = (int64_t)blockIdx.x * kThreads + threadIdx.x; blk < nblk; blk += (int64_t)gridDim.x * kThreads) {
+    for (int64_t base = (int64_t)blockIdx.x * kThreads; base < nblk; base += (int64_t)gridDim.x * kThreads) {
+        const int64_t blk = base + threadIdx.x;
+        const bool valid = blk < nblk;
         uint4 v[NV];
 #pragma unroll
-        for (int j = 0; j < NV; ++j) v[j] = ld_stream(xv + blk * NV + j);
+        for (int j = 0; j < NV; ++j) v[j] = valid ? ld_stream(xv + blk * NV + j) : make_uint4(0, 0, 0, 0);
         float f[16];
         if constexpr (BF16) {
 #pragma unroll
@@ -421,8 +429,16 @@ __global__ __launch_bounds__(kThreads) void nvfp4_kernel(const void *__restrict_
         o1 = fp4_f32<1>(o1, f[10] * r, f[11] * r, 1.0f);
         o1 = fp4_f32<2>(o1, f[12] * r, f[13] * r, 1.0f);
         o1 = fp4_f32<3>(o1, f[14] * r, f[15] * r, 1.0f);
-        st_stream((uint2 *)q + blk, make_uint2(o0, o1));
-        s_blk[blk] = (uint8_t)e;
+        if (valid) st_stream((uint2 *)q + blk, make_uint2(o0, o1));
+        if (sb_aligned && base + kThreads <= nblk) {     // uniform over the workgroup
+            sbuf[threadIdx.x] = (uint8_t)e;
+            __syncthreads();
+            if (threadIdx.x < kThreads / 16)
+                st_stream((uint4 *)(s_blk + base) + threadIdx.x, *(const uint4 *)(sbuf + 16 * threadIdx.x));
+            __syncthreads();                             // sbuf is written again by the next pass
+        } else if (valid) {
+            s_blk[blk] = (uint8_t)e;
+        }
     }
     if (bad && nonfinite) *nonfinite = 1;
 }
