@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const void *__restrict__ x
     // [tile row][NBLK]
     __shared__ __attribute__((aligned(16))) uint8_t colbuf[COL ? TILE_C * kTileRows : 16];
     __shared__ __attribute__((aligned(16))) uint8_t scol[COL ? TILE_C * 4 : 16];
-    __shared__ __attribute__((aligned(16))) uint8_t srow[(ROW && COL) ? kTileRows * NBLK : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t srow[ROW ? kTileRows * NBLK : 16];
 
     const int b = blockIdx.x, xcd = b & 7, local = b >> 3;
     const int t = xcd * per_xcd + local;
@@ -113,8 +113,6 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const void *__restrict__ x
             const __amdgpu_buffer_rsrc_t qr = make_rsrc(q_row + (size_t)r0 * cols, (uint32_t)wrows * cols);
             const uint32_t qvo = active ? (uint32_t)(half * RPL) * cols + c0 : kOutOfRange;
             const uint32_t sstride = cols / 32;
-            const __amdgpu_buffer_rsrc_t sr = make_rsrc(s_row + (size_t)r0 * sstride, (uint32_t)wrows * sstride);
-            const uint32_t svo = active ? (uint32_t)(half * RPL) * sstride + c0 / 32 : kOutOfRange;
 #pragma unroll
             for (int i = 0; i < RPL; ++i) {
                 uint32_t m[4];
@@ -150,12 +148,44 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const void *__restrict__ x
                     if (a == 0u) o0 = 0u;
                     buf_store4(qr, qvo, (uint32_t)i * cols, o0);
                 }
-                if constexpr (COL) {
-                    // every lane of the block writes the same byte to the same LDS slot
-                    srow[(wave * kRowsPerWave + half * RPL + i) * NBLK + slot / LPB] = (uint8_t)byte;
-                } else {
-                    // one lane of each block writes the scale byte; the lanes take turns by row
-                    if ((slot & (LPB - 1)) == (i & (LPB - 1))) buf_store1(sr, svo, (uint32_t)i * sstride, byte);
+                // every lane of the block writes the same byte to the same LDS slot
+                srow[(wave * kRowsPerWave + half * RPL + i) * NBLK + slot / LPB] = (uint8_t)byte;
+            }
+            if constexpr (!COL) {
+                // rowwise only: the wave's 32 rows of E8M0 bytes leave from LDS as one NBLK-byte store
+                // per row (single byte stores from the lanes of every block cost more); the rows of
+                // this wave are its own, so a wave-level fence orders the LDS bytes
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                const int nbl = ncv / 32;
+                const bool whole = nbl == NBLK && (sstride % NBLK) == 0 && (((uintptr_t)s_row) % NBLK) == 0;
+                const __amdgpu_buffer_rsrc_t sw = make_rsrc(s_row + (size_t)r0 * sstride + ct0 / 32,
+                                                            (uint32_t)wrows * sstride - ct0 / 32);
+                if (lane < kRowsPerWave) {
+                    const bool rv = lane < wrows;
+                    const uint8_t *src = srow + (wave * kRowsPerWave + lane) * NBLK;
+                    if constexpr (NBLK == 8) {
+                        const uint2 w = *(const uint2 *)src;
+                        if (whole) {
+                            buf_store8(sw, rv ? (uint32_t)lane * sstride : kOutOfRange, 0u, w.x, w.y);
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < 8; ++j)
+                                buf_store1(sw, (rv & (j < nbl)) ? (uint32_t)lane * sstride + j : kOutOfRange, 0u,
+                                           (j < 4 ? w.x : w.y) >> (8 * (j & 3)));
+                        }
+                    } else {
+                        const uint32_t w = *(const uint32_t *)src;
+                        if (whole) {
+                            buf_store4(sw, rv ? (uint32_t)lane * sstride : kOutOfRange, 0u, w);
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                buf_store1(sw, (rv & (j < nbl)) ? (uint32_t)lane * sstride + j : kOutOfRange, 0u,
+                                           w >> (8 * j));
+                        }
+                    }
                 }
             }
         } else {
