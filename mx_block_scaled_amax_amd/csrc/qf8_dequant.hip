@@ -55,7 +55,7 @@ static_assert(sizeof(StatsPart) == 64, "64-byte partials");
 struct DqArgs {
     const uint8_t *q;
     int64_t n;
-    uint32_t units;              // whole 4-code units
+    uint32_t units;              // whole W-code units
     uint32_t upr;                // units per row (block, MX)
     uint64_t upr_mul;            // u / upr = (u * upr_mul) >> upr_shift for every u < 2^31
     uint32_t upr_shift;
@@ -129,18 +129,16 @@ __device__ __forceinline__ void acc_add_unit(Acc &acc, const float *x, const flo
     }
 }
 
-// W consecutive elements of x (W = 4, 8 or 16) of unit u.
+// W consecutive elements of x (W = 4 or 16: the units of the statistics) of unit u.
 template <int XK, int W>
 __device__ __forceinline__ void load_x(const void *x, uint32_t u, float *xv) {
+    static_assert(W == 4 || W == 16, "statistics units");
     if constexpr (XK == kBF16) {
         const uint32_t *p = (const uint32_t *)x + (size_t)u * (W / 2);
         uint32_t w[W / 2];
         if constexpr (W == 16) {
             const uint4 a0 = ((const uint4 *)p)[0], a1 = ((const uint4 *)p)[1];
             w[0] = a0.x; w[1] = a0.y; w[2] = a0.z; w[3] = a0.w; w[4] = a1.x; w[5] = a1.y; w[6] = a1.z; w[7] = a1.w;
-        } else if constexpr (W == 8) {
-            const uint4 a0 = *(const uint4 *)p;
-            w[0] = a0.x; w[1] = a0.y; w[2] = a0.z; w[3] = a0.w;
         } else {
             const uint2 a0 = *(const uint2 *)p;
             w[0] = a0.x; w[1] = a0.y;
