@@ -60,13 +60,20 @@ __device__ __forceinline__ float exact_reciprocal(float s) {
 template <int FIN, int FOUT, bool POW2>
 __global__ __launch_bounds__(kRqThreads) void requant_t_kernel(const uint8_t *__restrict__ q,
                                                                const float *__restrict__ scales, int64_t rows,
-                                                               int64_t cols, int tiles_c, uint8_t *__restrict__ qT,
-                                                               float *__restrict__ scalesT, int32_t *nonfinite) {
+                                                               int64_t cols, int tiles_c, int tiles, int per_xcd,
+                                                               uint8_t *__restrict__ qT, float *__restrict__ scalesT,
+                                                               int32_t *nonfinite) {
     __shared__ __attribute__((aligned(16))) uint8_t qs[kTile * kTile];     // [row][col]
     __shared__ __attribute__((aligned(16))) uint8_t ot[kTile * kTile];     // [col][row], chunks permuted
     __shared__ float srow[kTile], srec[kTile], scol[kTile];
     __shared__ uint32_t part[kWaves][kTile];
-    const int tr = blockIdx.x / tiles_c, tc = blockIdx.x - tr * tiles_c;
+    // workgroups are dealt to the 8 XCDs round-robin; each XCD takes a contiguous run of tiles in
+    // row-major order, so the tiles of a tile row, which gather their row scales from the same
+    // lines, share one L2 (dealt round-robin, every XCD fetched those lines again: 1.21x the
+    // algorithmic bytes read instead of ~1.0x, at the same speed)
+    const int b = blockIdx.x, local = b >> 3, tile = (b & 7) * per_xcd + local;
+    if (local >= per_xcd || tile >= tiles) return;       // whole workgroup idle
+    const int tr = tile / tiles_c, tc = tile - tr * tiles_c;
     const int64_t r0 = (int64_t)tr * kTile, c0 = (int64_t)tc * kTile;
     const int nr = rows - r0 < kTile ? (int)(rows - r0) : kTile;          // multiples of 16
     const int nc = cols - c0 < kTile ? (int)(cols - c0) : kTile;
@@ -156,9 +163,10 @@ int launch_requant_t(const uint8_t *q, const float *scales, int64_t rows, int64_
                      int pow2, uint8_t *qT, float *scalesT, int32_t *nonfinite, hipStream_t s) {
     if (rows == 0 || cols == 0) return QF8_OK;
     const int tiles_r = (int)((rows + kTile - 1) / kTile), tiles_c = (int)((cols + kTile - 1) / kTile);
-    const dim3 grid((unsigned)tiles_r * (unsigned)tiles_c), block(kRqThreads);
+    const int tiles = tiles_r * tiles_c, per_xcd = (tiles + 7) / 8;
+    const dim3 grid((unsigned)(8 * per_xcd)), block(kRqThreads);
 #define QF8_RQ(FI, FO, P) hipLaunchKernelGGL((requant_t_kernel<FI, FO, P>), grid, block, 0, s, q, scales, rows, cols, \
-                                             tiles_c, qT, scalesT, nonfinite)
+                                             tiles_c, tiles, per_xcd, qT, scalesT, nonfinite)
 #define QF8_RQP(FI, FO) do { if (pow2) QF8_RQ(FI, FO, true); else QF8_RQ(FI, FO, false); } while (0)
     if (fmt_in == QF8_E4M3) { if (fmt_out == QF8_E4M3) QF8_RQP(kE4M3, kE4M3); else QF8_RQP(kE4M3, kE5M2); }
     else { if (fmt_out == QF8_E4M3) QF8_RQP(kE5M2, kE4M3); else QF8_RQP(kE5M2, kE5M2); }
