@@ -317,6 +317,17 @@ def test_nvfp4_single_pass_threshold_and_fp32():
     check_nv_big(x, ws, "4096x8192 fp32 (beyond the held capacity)")
 
 
+def test_nvfp4_single_pass_ragged_scale_groups():
+    """Single-pass sizes with ragged ends: the vector count is not a multiple of the 8 (BF16) or
+    16 (FP32) vectors that one 16-lane row of a wave holds, so the last rows run partly out of
+    range; BF16 and FP32, every byte compared."""
+    ws = qf8.workspace(torch.empty(1, device="cuda"))
+    check_nv_big(mx_gradient(2049, 2064, seed=24), ws, "2049x2064 bf16 (vectors % 8 = 2)")
+    rng = np.random.default_rng(25)
+    x = (rng.standard_normal((1025, 4112)) * np.exp(rng.uniform(-2, 2, (1025, 1)))).astype(np.float32)
+    check_nv_big(x, ws, "1025x4112 fp32 (vectors % 16 = 4)")
+
+
 @pytest.mark.parametrize("ticks", [1, 500])
 def test_nvfp4_single_pass_give_up(gradient_full, ticks):
     """Waiting workgroups forced to give up at the grid barrier: the last one casts their slabs."""

@@ -6,7 +6,7 @@ is aligned, and byte by byte when it is not (or when a tile or pass is ragged). 
 hand every scale array in at an odd address (a view one byte into a poisoned buffer), compare
 the bytes with the CPU oracle, and check that the guard bytes on both sides are untouched:
 MXFP8 rowwise-only and dual, MXFP4 rowwise-only, and NVFP4 with a caller amax and with the
-measured amax.
+measured amax (below and above the single-pass size of 2^22 elements).
 """
 import numpy as np
 import pytest
@@ -79,7 +79,7 @@ def test_mxfp4_rowwise_odd_scale_array(shape):
         check_guards(sbuf, "s_row" + tag)
 
 
-@pytest.mark.parametrize("shape", [(64, 4096), (33, 48), (1000, 1008)])
+@pytest.mark.parametrize("shape", [(64, 4096), (33, 48), (1000, 1008), (2048, 2048), (2049, 2064)])
 @pytest.mark.parametrize("caller_amax", [False, True], ids=["measured", "caller"])
 def test_nvfp4_odd_scale_array(shape, caller_amax):
     rows, cols = shape
