@@ -16,8 +16,10 @@
 // row scales go to LDS with 16-byte loads; each thread then owns 4 columns x 8 rows (one dword
 // of codes per row, two values per convert instruction) and de-scales them in registers. When a
 // row's scale is a power of two (the rule the pages use for these tensors) the division is the
-// multiplication by its exact reciprocal (the same correctly rounded quotient); the branch is
-// taken alike by the 32 lanes that share a row. Column maxima meet through a lane exchange and LDS; the new codes of a
+// multiplication by its exact reciprocal (the same correctly rounded quotient); a wave whose rows
+// all exist and all have such scales multiplies without per-row branches, and with power-of-two
+// output scales a wave whose columns are all finite casts without the saturating clamp (the
+// products cannot exceed F8max there). Column maxima meet through a lane exchange and LDS; the new codes of a
 // column's 8 rows go as 8 bytes into a second 16 KiB LDS tile, transposed (16-byte chunks
 // permuted by column so the writes spread over the banks), and the workgroup stores each
 // column's 128 new codes as one 128-byte line of qT.
@@ -48,6 +50,13 @@ __device__ __forceinline__ void decode4(uint32_t w, float *d) {
     d[0] = lo.x; d[1] = lo.y; d[2] = hi.x; d[3] = hi.y;
 }
 
+// sat_rne8(fl32(x * s)) for products known to lie within +-F8max (power-of-two scale of a finite
+// column amax): the clamp of cast4 is the identity there, so it is left out.
+template <int FMT>
+__device__ __forceinline__ uint32_t cast4_in_range(float x0, float x1, float x2, float x3, float s) {
+    return cvt2_f32<FMT, true>(x2 * s, x3 * s, cvt2_f32<FMT, false>(x0 * s, x1 * s, 0u));
+}
+
 // 1/S exactly when S is a power of two whose reciprocal is a normal fp32 value (then x / S and
 // x * (1/S) are the same correctly rounded quotient), else 0.
 __device__ __forceinline__ float exact_reciprocal(float s) {
@@ -55,6 +64,49 @@ __device__ __forceinline__ float exact_reciprocal(float s) {
     const uint32_t e = (u >> 23) & 0xFFu;
     if ((u & 0x807FFFFFu) != 0u || e < 1u || e > 253u) return 0.0f;
     return __uint_as_float((254u - e) << 23);
+}
+
+// De-scale rows 8rg .. 8rg+7, columns 4cg .. 4cg+3 of the tile (v = fl32(decode / S_row)) and take
+// the column maxima of |v| as bit patterns. FULL: all 128 rows exist and every row scale has an
+// exact reciprocal, so every row multiplies; otherwise each row multiplies or divides (the 32
+// lanes of a row take the same side) and rows beyond the tile's end stay out of the maxima.
+template <int FIN, bool FULL>
+__device__ __forceinline__ void descale_rows(const uint8_t *qs, const float *srow, const float *srec, int rg, int cg,
+                                             int nr, float (&v)[8][4], uint32_t (&m)[4]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = 8 * rg + i;
+        decode4<FIN>(((const uint32_t *)qs)[row * (kTile / 4) + cg], v[i]);
+        const float rec = srec[row];
+        if (FULL || rec != 0.0f) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[i][j] *= rec;
+        } else {
+            const float sr = srow[row];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[i][j] = v[i][j] / sr;
+        }
+        if (FULL || row < nr) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) m[j] = umax(m[j], __float_as_uint(v[i][j]) & 0x7FFFFFFFu);
+        }
+    }
+}
+
+// New codes of columns 4cg .. 4cg+3, rows 8rg .. 8rg+7: 8 bytes per column into the transposed
+// LDS tile. CLAMP: the saturating cast; otherwise every product is known to lie within +-F8max.
+template <int FOUT, bool CLAMP>
+__device__ __forceinline__ void cast_columns(const float (&v)[8][4], const float *scol, uint8_t *ot, int rg, int cg) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int col = 4 * cg + j;
+        const float sc = scol[col];
+        const uint32_t lo = CLAMP ? cast4<FOUT>(v[0][j], v[1][j], v[2][j], v[3][j], sc)
+                                  : cast4_in_range<FOUT>(v[0][j], v[1][j], v[2][j], v[3][j], sc);
+        const uint32_t hi = CLAMP ? cast4<FOUT>(v[4][j], v[5][j], v[6][j], v[7][j], sc)
+                                  : cast4_in_range<FOUT>(v[4][j], v[5][j], v[6][j], v[7][j], sc);
+        *(uint2 *)(ot + ot_offset(col, rg >> 1) + (rg & 1) * 8) = make_uint2(lo, hi);
+    }
 }
 
 template <int FIN, int FOUT, bool POW2>
@@ -65,7 +117,8 @@ __global__ __launch_bounds__(kRqThreads) void requant_t_kernel(const uint8_t *__
                                                                int32_t *nonfinite) {
     __shared__ __attribute__((aligned(16))) uint8_t qs[kTile * kTile];     // [row][col]
     __shared__ __attribute__((aligned(16))) uint8_t ot[kTile * kTile];     // [col][row], chunks permuted
-    __shared__ float srow[kTile], srec[kTile], scol[kTile];
+    __shared__ __attribute__((aligned(16))) float srow[kTile], srec[kTile], scol[kTile];
+    __shared__ __attribute__((aligned(4))) uint8_t snf[kTile];           // column amax non-finite
     __shared__ uint32_t part[kWaves][kTile];
     // workgroups are dealt to the 8 XCDs round-robin; each XCD takes a contiguous run of tiles in
     // row-major order, so the tiles of a tile row, which gather their row scales from the same
@@ -95,28 +148,18 @@ __global__ __launch_bounds__(kRqThreads) void requant_t_kernel(const uint8_t *__
     }
     __syncthreads();
 
-    // columns 4cg .. 4cg+3, rows 8rg .. 8rg+7: de-scale (v = fl32(decode / S_row)), column maxima
+    // columns 4cg .. 4cg+3, rows 8rg .. 8rg+7: de-scale (v = fl32(decode / S_row)), column maxima.
+    // A wave whose 16 rows all exist and all have exact reciprocals (the usual case: power-of-two
+    // row scales) takes the path without per-row branches.
     const int cg = t & 31, rg = t >> 5, wave = t >> 6;
+    const float4 ra = *(const float4 *)(srec + 8 * rg), rb = *(const float4 *)(srec + 8 * rg + 4);
+    const bool own_fast = 8 * rg + 8 <= nr && ra.x != 0.0f && ra.y != 0.0f && ra.z != 0.0f && ra.w != 0.0f &&
+                          rb.x != 0.0f && rb.y != 0.0f && rb.z != 0.0f && rb.w != 0.0f;
+    const bool fast = __builtin_amdgcn_ballot_w64(!own_fast) == 0u;
     float v[8][4];
     uint32_t m[4] = {0, 0, 0, 0};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = 8 * rg + i;
-        decode4<FIN>(((const uint32_t *)qs)[row * (kTile / 4) + cg], v[i]);
-        const float rec = srec[row];                     // the same for the 32 lanes of this row
-        if (rec != 0.0f) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[i][j] *= rec;
-        } else {
-            const float sr = srow[row];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[i][j] = v[i][j] / sr;
-        }
-        if (row < nr) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) m[j] = umax(m[j], __float_as_uint(v[i][j]) & 0x7FFFFFFFu);
-        }
-    }
+    if (fast) descale_rows<FIN, true>(qs, srow, srec, rg, cg, nr, v, m);
+    else descale_rows<FIN, false>(qs, srow, srec, rg, cg, nr, v, m);
 #pragma unroll
     for (int j = 0; j < 4; ++j) m[j] = umax(m[j], (uint32_t)__shfl_xor((int)m[j], 32));   // the wave's 16 rows
     if ((t & 63) < 32) {
@@ -130,22 +173,20 @@ __global__ __launch_bounds__(kRqThreads) void requant_t_kernel(const uint8_t *__
         for (int w = 0; w < kWaves; ++w) mc = umax(mc, part[w][t]);
         const float sc = POW2 ? scale_pow2_from_amax_bits<FOUT>(mc) : scale_from_amax_bits<FOUT>(mc);
         scol[t] = sc;
+        snf[t] = mc >= 0x7F800000u;
         if (t < nc) {
             scalesT[(c0 + t) * ((rows + 127) / 128) + tr] = sc;
             if (nonfinite && mc >= 0x7F800000u) *nonfinite = 1;
         }
     }
     __syncthreads();
+    // power-of-two scales put every product of a finite column within +-F8max (S' <= F8max / amax),
+    // so the saturating clamp is needed only for Eq.(1) scales or in a wave with a non-finite column
+    const bool clamp = !POW2 || __builtin_amdgcn_ballot_w64(*(const uint32_t *)(snf + 4 * cg) != 0u) != 0u;
 
     // new codes: for each column, its 8 rows as 8 bytes of the transposed output tile
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int col = 4 * cg + j;
-        const float sc = scol[col];
-        const uint32_t lo = cast4<FOUT>(v[0][j], v[1][j], v[2][j], v[3][j], sc);
-        const uint32_t hi = cast4<FOUT>(v[4][j], v[5][j], v[6][j], v[7][j], sc);
-        *(uint2 *)(ot + ot_offset(col, rg >> 1) + (rg & 1) * 8) = make_uint2(lo, hi);
-    }
+    if (clamp) cast_columns<FOUT, true>(v, scol, ot, rg, cg);
+    else cast_columns<FOUT, false>(v, scol, ot, rg, cg);
     __syncthreads();
 
     // each column's 128 codes: one line of qT

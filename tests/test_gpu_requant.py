@@ -7,6 +7,8 @@
     and columns multiples of 16, partial 128-row groups), and on the full 8192x7168 activation
     quantized with power-of-two scales, where it also adds no error (values re-scaled into the
     normal range de-scale to exactly their 1x128 values);
+  * tiles mixing power-of-two and general row scales, and non-finite columns next to finite
+    ones, on every code;
   * non-finite groups set the flag.
 """
 import numpy as np
@@ -69,6 +71,40 @@ def test_requant_small(shape):
             q, s, _, _ = O.quantize_block_ex(x, 1, 128, fin, pow2=pow2)
             for fout in FMTS:
                 check_requant(q, s, fin, fout, pow2, f" [{shape} {fin}->{fout} pow2={pow2}]")
+
+
+@pytest.mark.parametrize("fin", FMTS)
+def test_requant_mixed_row_scales_and_nonfinite_columns(fin):
+    """Tiles where some waves see only power-of-two row scales and others do not (rows 20..27
+    and 150..151 get general scales; 208 rows leave a partial second tile of 80), and where a few
+    columns hold NaN or Inf codes, so that waves with and without non-finite columns meet in one
+    tile: every scale and every code but the NaN ones (non-finite input is outside the bit-exact
+    contract; Inf still saturates to +-F8max and is compared) against the oracle, for both output
+    formats and scale rules."""
+    x = small_tensor(208, 384, seed=31)
+    q, s, _, _ = O.quantize_block_ex(x, 1, 128, fin, pow2=True)
+    s = s.copy()
+    s[20:28] *= np.float32(1.5)
+    s[150:152] *= np.float32(0.7)
+    q = q.copy()
+    nan_code = 0x7F if fin == O.E4M3 else 0x7E
+    q[5, 9] = nan_code
+    q[130, 200] = 0x80 | nan_code
+    if fin == O.E5M2:
+        q[60, 300] = 0x7C                                    # +Inf
+        q[207, 301] = 0xFC                                   # -Inf
+    nan_at = [(5, 9), (130, 200)]                            # NaN codes are outside the contract
+    for pow2 in (True, False):
+        for fout in FMTS:
+            tag = f" [mixed {fin}->{fout} pow2={pow2}]"
+            qT, sT = qf8.requantize_1x128_to_128x1(to_device(q), torch.from_numpy(s).cuda(), fin, fout,
+                                                   pow2_scales=pow2)
+            wqT, wsT, _ = O.requant_1x128_to_128x1(q, s, fin, fout, pow2)
+            got, want = host(qT).copy(), wqT.copy()
+            for r, c in nan_at:
+                got[c, r] = want[c, r] = 0
+            assert_bytes_equal(host(sT).view(np.uint32), wsT.view(np.uint32), "scalesT", tag)
+            assert_bytes_equal(got, want, "qT (NaN positions excluded)", tag)
 
 
 def test_requant_nonfinite_flag():
