@@ -189,12 +189,13 @@ __global__ __launch_bounds__(kRqThreads) void requant_t_kernel(const uint8_t *__
     else cast_columns<FOUT, false>(v, scol, ot, rg, cg);
     __syncthreads();
 
-    // each column's 128 codes: one line of qT
+    // each column's 128 codes: one line of qT, written once, so non-temporal (cached stores took
+    // 25.2 µs on 8192x7168 against 24.0; the code loads stay cached: non-temporal loads took 31.0)
 #pragma unroll
     for (int j = 0; j < kTile * kTile / 16 / kRqThreads; ++j) {
         const int k = t + j * kRqThreads, col = k >> 3, ch = k & 7;
         if (col < nc && ch * 16 < nr)
-            *(uint4 *)(qT + (c0 + col) * rows + r0 + ch * 16) = *(const uint4 *)(ot + ot_offset(col, ch));
+            st_stream((uint4 *)(qT + (c0 + col) * rows + r0 + ch * 16), *(const uint4 *)(ot + ot_offset(col, ch)));
     }
 }
 
