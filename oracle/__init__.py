@@ -111,8 +111,12 @@ def _load():
     lib.qf8o_unpack_fp4.argtypes = [_c_void_p, _i64, _c_void_p]
     lib.qf8o_nvfp4_tensor_scale.restype = ctypes.c_float
     lib.qf8o_nvfp4_tensor_scale.argtypes = [ctypes.c_double]
-    lib.qf8o_nvfp4_block.restype = None
-    lib.qf8o_nvfp4_block.argtypes = [ctypes.c_double, ctypes.c_float, _c_void_p, _c_void_p]
+    lib.qf8o_nvfp4_block.restype = ctypes.c_uint
+    lib.qf8o_nvfp4_block.argtypes = [ctypes.c_double, ctypes.c_float]
+    lib.qf8o_nvfp4_element.restype = ctypes.c_uint
+    lib.qf8o_nvfp4_element.argtypes = [ctypes.c_double, ctypes.c_float, ctypes.c_uint]
+    lib.qf8o_encode_ratio.restype = ctypes.c_uint
+    lib.qf8o_encode_ratio.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_double]
     lib.qf8o_quantize_nvfp4.restype = None
     lib.qf8o_quantize_nvfp4.argtypes = [_c_void_p, ctypes.c_int, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                                         _c_void_p, _c_void_p, _c_void_p]
@@ -461,11 +465,18 @@ def nvfp4_tensor_scale(a):
 
 
 def nvfp4_block(amax_b, s_t):
-    """(E4M3 block-scale code, encode factor r_b) of one block (R17)."""
-    e = np.zeros(1, np.uint32)
-    r = np.zeros(1, np.float32)
-    _load().qf8o_nvfp4_block(float(amax_b), float(np.float32(s_t)), _ptr(e), _ptr(r))
-    return int(e[0]), np.float32(r[0])
+    """E4M3 block-scale code of one block: amax_b * S_t / 6 rounded once (R17)."""
+    return int(_load().qf8o_nvfp4_block(float(amax_b), float(np.float32(s_t))))
+
+
+def nvfp4_element(x, s_t, e):
+    """E2M1 code of one element under block-scale code e: x * S_t / decode(e) rounded once (R17)."""
+    return int(_load().qf8o_nvfp4_element(float(x), float(np.float32(s_t)), int(e)))
+
+
+def encode_ratio(fmt, num, den):
+    """sat_rne of the exact quotient num / den (products of num's format values with den exact)."""
+    return int(_load().qf8o_encode_ratio(int(fmt), float(num), float(den)))
 
 
 def quantize_nvfp4(x, amax_in=None):

@@ -189,6 +189,38 @@ unsigned qf8o_encode(int fmt, double y)
     return sign | (unsigned)i;
 }
 
+/* sat_rne of the exact quotient num / den (den > 0), rounded once: the nearest value, ties to the
+ * even code, saturated at the largest finite value, with num's sign. Every comparison is between
+ * num and a value or midpoint of the format times den; the caller passes num and den such that
+ * those products are exact in fp64 (then each test decides the exact quotient's side). */
+unsigned qf8o_encode_ratio(int fmt, double num, double den)
+{
+    build_table(fmt);
+    const double *v = g_vals[fmt];
+    int n = g_nvals[fmt];
+    const unsigned sbit = 1u << (fmt_bits(fmt) - 1);
+    if (isnan(num) || !(den > 0.0)) return fmt == QF8O_E2M1 ? (unsigned)(n - 1) : 0x7Fu;
+    unsigned sign = signbit(num) ? sbit : 0u;
+    double a = fabs(num);
+    int i;
+    if (a >= v[n - 1] * den) {
+        i = n - 1;
+    } else {
+        int lo = 0, hi = n - 1;                /* invariant: v[lo] * den <= a < v[hi] * den */
+        while (hi - lo > 1) {
+            int mid = (lo + hi) / 2;
+            if (v[mid] * den <= a) lo = mid; else hi = mid;
+        }
+        i = lo;
+        if (v[i] * den != a) {
+            double t = 0.5 * (v[i] + v[i + 1]) * den;    /* the midpoint, scaled: exact */
+            if (a > t) i = i + 1;
+            else if (a == t && (i & 1)) i = i + 1;       /* tie: the even code */
+        }
+    }
+    return sign | (unsigned)i;
+}
+
 /* ---------------------------------------------------------------------------------------------
  * Inputs. BF16 is the upper half of an fp32 ([MP-FP8 2.2]); widening is exact.
  * ------------------------------------------------------------------------------------------- */
@@ -713,19 +745,24 @@ void qf8o_requant_1x128_to_128x1(const uint8_t *q, const float *scales, int64_t 
  *     and element 2j+1 in the high nibble (the pages do not fix the order; this is the order
  *     of the OCP MX format).
  * R17 NVFP4: blocks of 16 along a row, one E4M3 block scale each and one fp32 tensor scale.
- *     The pages fix the block scale as amax_b / 6 stored in E4M3 and add the fp32 tensor scale
- *     because E4M3's range is too small, without its formula. Reading: the tensor scale S_t is
- *     chosen so that the largest block scale lands on E4M3's largest value 448:
+ *     The pages fix the block scale as amax_b / 6 stored in E4M3, divide each element by the
+ *     stored block scale and round it to E2M1, and add the fp32 tensor scale because E4M3's range
+ *     is too small, without its formula. Reading: the tensor scale S_t lifts every block scale
+ *     into E4M3's range so that the largest lands on 448, and the stored code holds the block
+ *     scale in those lifted units:
  *       S_t = fl32(448 * 6 / A) with A the tensor amax (1 for A = 0 or non-finite, FLT_MAX on
  *             overflow, as Eq.(1));
- *       e_b = sat_rne(E4M3, fl32(fl32(amax_b / 6) * S_t))   (the stored block-scale code);
- *       r_b = fl32(S_t / decode(e_b)) (FLT_MAX if that overflows), or 0 when e_b decodes to 0
- *             (the block is negligible against the tensor and encodes as signed zeros);
- *       code = sat_rne(E2M1, fl32(x * r_b)),
- *     so that x is divided by the real block scale decode(e_b) / S_t through one per-block
- *     reciprocal. The pages' example (amax 5.3, S_t = 1): 5.3/6 = 0.883 -> E4M3 0.875,
- *     5.3 / 0.875 = 6.06 -> 6, de-scaled 5.25. A block with Inf/NaN gets the E4M3 NaN code
- *     0x7F and sets nonfinite.
+ *       e_b = sat_rne(E4M3, amax_b * S_t / 6)          (one rounding of the exact quotient);
+ *       code = sat_rne(E2M1, x * S_t / decode(e_b))    (x divided by the real block scale
+ *             decode(e_b) / S_t, one rounding of the exact quotient);
+ *     a block whose e_b decodes to 0 (negligible against the tensor; it de-scales to 0 whatever
+ *     its codes) encodes its elements as zeros of their signs. The pages' example (amax 5.3,
+ *     S_t = 1): 5.3/6 = 0.883 -> E4M3 0.875, 5.3 / 0.875 = 6.06 -> 6, de-scaled 5.25. A block
+ *     with Inf/NaN gets the E4M3 NaN code 0x7F and sets nonfinite.
+ *     Both quotients are rounded from their exact values: qf8o_encode_ratio compares the
+ *     numerator with the format's values and midpoints times the denominator, products that are
+ *     exact in fp64 (the numerator x * S_t has at most 48 significant bits, the denominator at
+ *     most 24, the values and midpoints at most 5).
  * ------------------------------------------------------------------------------------------- */
 
 /* Pairs of 4-bit codes into bytes: out[j] = c[2j] | c[2j+1] << 4 (n even). */
@@ -752,15 +789,20 @@ float qf8o_nvfp4_tensor_scale(double amax)
     return s;
 }
 
-/* R17, for one block of 16 given its amax: the E4M3 block-scale code and the encode factor. */
-void qf8o_nvfp4_block(double amax_b, float s_t, unsigned *e_code, float *r)
+/* R17, for one block of 16 given its amax: the E4M3 block-scale code, amax_b * S_t / 6 rounded
+ * once. */
+unsigned qf8o_nvfp4_block(double amax_b, float s_t)
 {
-    float d = (float)(amax_b / 6.0);                     /* amax_b / 6, rounded to fp32 */
-    unsigned e = qf8o_encode(QF8O_E4M3, (double)(float)((double)d * (double)s_t));
+    return qf8o_encode_ratio(QF8O_E4M3, amax_b * (double)s_t, 6.0);
+}
+
+/* R17, one element of a block with block-scale code e: x * S_t / decode(e) rounded once to E2M1,
+ * or a zero of x's sign when decode(e) is 0. */
+unsigned qf8o_nvfp4_element(double x, float s_t, unsigned e)
+{
     double dec = qf8o_decode(QF8O_E4M3, e);
-    *e_code = e;
-    float rr = (dec == 0.0 || isnan(dec)) ? 0.0f : (float)((double)s_t / dec);
-    *r = isinf(rr) ? FLT_MAX : rr;
+    if (dec == 0.0) return signbit(x) ? 0x8u : 0x0u;
+    return qf8o_encode_ratio(QF8O_E2M1, x * (double)s_t, dec);
 }
 
 /* x [rows][cols] (cols % 16 == 0) -> codes [rows][cols] (one 4-bit code per byte, unpacked),
@@ -783,14 +825,10 @@ void qf8o_quantize_nvfp4(const void *x, int dtype, int64_t rows, int64_t cols, c
                 for (int k = 0; k < 16; ++k) codes[base + k] = 0;
                 continue;
             }
-            unsigned e;
-            float rb;
-            qf8o_nvfp4_block(a, s_t, &e, &rb);
+            unsigned e = qf8o_nvfp4_block(a, s_t);
             s_blk[r * (cols / 16) + g] = (uint8_t)e;
-            for (int k = 0; k < 16; ++k) {
-                float v = (float)(load_elem(x, dtype, base + k) * (double)rb);   /* fl32(x * r_b) */
-                codes[base + k] = (uint8_t)qf8o_encode(QF8O_E2M1, (double)v);
-            }
+            for (int k = 0; k < 16; ++k)
+                codes[base + k] = (uint8_t)qf8o_nvfp4_element(load_elem(x, dtype, base + k), s_t, e);
         }
     if (tensor_scale) *tensor_scale = s_t;
     if (amax_out) *amax_out = (float)A;

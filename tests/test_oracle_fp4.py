@@ -187,9 +187,11 @@ def test_nvfp4_caller_amax():
     assert np.all(s_blk.reshape(-1)[top] == 0x7E)
 
 
-def test_nvfp4_tiny_tensor_keeps_zero_codes():
-    """With the tensor amax in the fp32 subnormal range S_t is FLT_MAX and S_t / decode(e_b) can
-    overflow; r_b is then FLT_MAX, so zeros stay zero codes and other values saturate."""
+def test_nvfp4_tiny_tensor_scale_overflow():
+    """With the tensor amax in the fp32 subnormal range S_t overflows to FLT_MAX (Eq.(1)'s rule).
+    The element quotient x * S_t / decode(e_b) is still exact: the block's largest element lands
+    on 6 and de-scales back to about its value; a block whose scale underflows E4M3 keeps signed
+    zero codes."""
     x = np.zeros((1, 32), np.float32)
     x[0, 0] = np.float32(1e-40)
     x[0, 16] = np.float32(3e-45)
@@ -197,10 +199,13 @@ def test_nvfp4_tiny_tensor_keeps_zero_codes():
     codes = O.unpack_fp4(q)[0]
     fmax = np.finfo(np.float32).max
     assert s_t == fmax
-    e, r = O.nvfp4_block(1e-40, s_t)
-    assert O.decode(O.E4M3, e) < 1.0 and r == fmax           # S_t / decode(e_b) overflowed
-    assert np.all(codes == 0)                                # 1e-40 * FLT_MAX = 0.034 -> 0; zeros stay 0
-    assert O.nvfp4_block(3e-45, s_t) == (0, 0.0)             # scale below E4M3: zero factor
+    e = O.nvfp4_block(1e-40, s_t)
+    assert s_blk[0, 0] == e and O.decode(O.E4M3, e) == 3 / 512          # 1e-40 * FLT_MAX / 6 = 0.00567
+    assert codes[0] == 7 and np.all(codes[1:16] == 0)
+    xh = O.dequant_nvfp4_one(codes[0], e, s_t)
+    assert abs(xh - float(x[0, 0])) / float(x[0, 0]) < 0.04            # 6 * (3/512) / FLT_MAX
+    assert O.nvfp4_block(3e-45, s_t) == 0 == s_blk[0, 1]                 # below E4M3's range
+    assert np.all(codes[16:] == 0)
 
 
 def _golden(golden_dir, name):
@@ -227,11 +232,11 @@ def test_golden_mxfp4_example(golden_dir):
 
 def test_golden_nvfp4_example(golden_dir):
     g = _golden(golden_dir, "w9_nvfp4_example.json")
-    e, r = O.nvfp4_block(g["amax"], 1.0)               # S_t = 1, as in the example
+    e = O.nvfp4_block(g["amax"], 1.0)                  # S_t = 1, as in the example
     assert round(g["amax"] / 6, 3) == g["block_scale_exact"]
     assert O.decode(O.E4M3, e) == g["block_scale_e4m3"]
     assert round(g["amax"] / g["block_scale_e4m3"], 2) == g["scaled_amax"]
-    code = O.encode(O.E2M1, float(np.float32(np.float32(g["amax"]) * r)))
+    code = O.nvfp4_element(g["amax"], 1.0, e)
     assert O.decode(O.E2M1, code) == g["rounded_amax"]
     assert O.dequant_nvfp4_one(code, e, 1.0) == g["dequantized"]
     assert abs(g["dequantized"] - g["amax"]) / g["amax"] * 100 < g["relative_error_below_pct"]
