@@ -239,39 +239,73 @@ __device__ __forceinline__ uint32_t mx_saturate_codes(uint32_t w) {
 
 // ---- NVFP4 block scaling (E2M1 codes under an E4M3 block scale and an fp32 tensor scale) -----
 // S_t = fl32(448 * 6 / A) from the tensor |amax| bits (1 for A = 0 or non-finite, FLT_MAX on
-// overflow); per block: e_b = E4M3 code of fl32(fl32(amax_b / 6) * S_t) (clamped to 448 first,
-// so the exact-RNE fp8 convert saturates), r_b = fl32(S_t / decode(e_b)) (FLT_MAX on overflow,
-// 0 when e_b decodes to 0); a block with Inf/NaN gets the E4M3 NaN code 0x7F and r_b = 0.
+// overflow). Per block: e_b = E4M3(amax_b * S_t / 6) and per element code = E2M1(x * S_t /
+// decode(e_b)), each the nearest value of the exact quotient, ties to the even code (saturating);
+// a block whose e_b decodes to 0 gives zero codes of the elements' signs, and a block with
+// Inf/NaN gets the E4M3 NaN code 0x7F.
+// Both quotients are found the same way. An fp32 estimate of the quotient is formed twice, pushed
+// once below and once above the exact value by a factor (1 -/+ 2^-21 or 2^-20) larger than the
+// estimate's own rounding error (at most three roundings of 2^-24). Rounding to the format is
+// monotone, so when both estimates give the same code, so does the exact quotient. When they
+// differ, the quotient lies within about 2^-20 of the midpoint t/d between the two codes, and
+// fma(n1, n2, -t) = n1*n2 - t rounded once has the sign (and the zero) of the exact difference,
+// which decides the side, or the tie.
 __device__ __forceinline__ float nv_tensor_scale(uint32_t abits) {
     if (abits == 0u || abits >= 0x7F800000u) return 1.0f;
     const float s = 2688.0f / __uint_as_float(abits);
     return s > 3.40282346638528859812e+38f ? 3.40282346638528859812e+38f : s;
 }
-// fl32(a / 6) for a finite |a| bit pattern: the product with fl32(1/6), corrected by one fused
-// multiply-add, is the correctly rounded quotient for every a >= 2^-125 (checked on the host over
-// all such fp32 values); smaller a (subnormal quotients) take the IEEE division.
-__device__ __forceinline__ float div6(uint32_t abits) {
-    const float a = __uint_as_float(abits);
-    if (__builtin_expect(abits < 0x01000000u, 0)) return a / 6.0f;
-    const float c = 0x1.555556p-3f;
-    const float q0 = a * c;
-    return __builtin_fmaf(__builtin_fmaf(-q0, 6.0f, a), c, q0);
+// E4M3 code of a non-negative fp32 value not above 448: the gfx950 convert rounds to nearest even.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false) & 0xFFu;
 }
 // e_b of a block from its |amax| bits and S_t.
 __device__ __forceinline__ uint32_t nv_block_code(uint32_t amax_bits, float st) {
     if (amax_bits >= 0x7F800000u) return 0x7Fu;
-    const float p = fminf(div6(amax_bits) * st, 448.0f);
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(p, p, 0, false) & 0xFFu;
+    const float a = __uint_as_float(amax_bits);
+    const float p = a * st;                       // inf when the caller's tensor amax is far too small
+    constexpr float kSixthLo = (float)((1.0 / 6.0) * (1.0 - 0x1p-20));
+    constexpr float kSixthHi = (float)((1.0 / 6.0) * (1.0 + 0x1p-20));
+    const uint32_t clo = e4m3_code(fminf(p * kSixthLo, 448.0f));
+    const uint32_t chi = e4m3_code(fminf(p * kSixthHi, 448.0f));
+    if (clo == chi) return clo;
+    // adjacent codes: 6 * their midpoint = 3 * (sum of the two values), exact in fp32
+    const float t = 3.0f * (__builtin_amdgcn_cvt_f32_fp8(clo, 0) + __builtin_amdgcn_cvt_f32_fp8(chi, 0));
+    const float s = __builtin_fmaf(a, st, -t);
+    return s > 0.0f ? chi : s < 0.0f ? clo : ((clo & 1u) ? chi : clo);
 }
-// r_b for every E4M3 code, written by threads 0..127 of the workgroup (S_t is the same for the
-// whole tensor, so each block looks its factor up instead of dividing); code 0x7F (non-finite
-// block) gets 0. The caller synchronizes before reading.
-__device__ __forceinline__ void nv_factor_table(float *tab, float st) {
+// The element estimates' factors for every E4M3 block-scale code, written by threads 0..127 of the
+// workgroup (S_t is one value for the whole tensor, so each block looks its pair up): (r_lo, r_hi)
+// = fl32(S_t / decode(e)) times (1 - 2^-21, 1 + 2^-21). A code that decodes to 0 (and the NaN code)
+// gets (0, 0), so its elements become signed zeros; a quotient S_t / decode(e) that overflows gets
+// (0, Inf), so every nonzero element of such a block takes the exact path. The caller synchronizes
+// before reading.
+__device__ __forceinline__ void nv_factor_table(float2 *tab, float st) {
     const int e = (int)threadIdx.x;
     if (e < 128) {
         const float dec = __builtin_amdgcn_cvt_f32_fp8(e, 0);
-        tab[e] = (e == 0x7F || dec == 0.0f) ? 0.0f : fminf(st / dec, 3.40282346638528859812e+38f);
+        float2 f = make_float2(0.0f, 0.0f);
+        if (e != 0x7F && dec != 0.0f) {
+            const float r = st / dec;
+            f = r <= 3.40282346638528859812e+38f ? make_float2(r * (1.0f - 0x1p-21f), r * (1.0f + 0x1p-21f))
+                                                 : make_float2(0.0f, __builtin_inff());
+        }
+        tab[e] = f;
     }
+}
+// The exact E2M1 code of x * S_t / dec (dec > 0): the number of E2M1 midpoints (0.25, 0.75, 1.25,
+// 1.75, 2.5, 3.5, 5) the exact quotient lies above, a tie counting when the even code is the upper
+// one; saturation at 6 follows. Each midpoint times dec is exact (3 x 4 significant bits).
+__device__ __forceinline__ uint32_t nv_elem_exact(float x, float st, float dec) {
+    const float ax = __builtin_fabsf(x);
+    constexpr float kMid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+        const float s = __builtin_fmaf(ax, st, -(kMid[j] * dec));
+        c += (s > 0.0f || (s == 0.0f && (j & 1))) ? 1u : 0u;
+    }
+    return c | ((__float_as_uint(x) >> 31) << 3);
 }
 // Two fp32 values -> one byte of two E2M1 codes (first value in the low nibble) in byte SEL of
 // `old`: v_cvt_scalef32_pk_fp4_f32 with scale 1 rounds to nearest even and saturates to +-6.

@@ -18,8 +18,9 @@
 //     (round-up), clamped to [-127, 127]; byte = X + 127 (0xFF for a block with Inf/NaN);
 //     code = sat_rne(E2M1, x / 2^X); amax = 0 gives zero codes.
 //   NVFP4: S_t = fl32(2688 / A) (A the tensor amax; 1 for A = 0 or non-finite, FLT_MAX on
-//     overflow); e_b = sat_rne(E4M3, fl32(fl32(amax_b / 6) * S_t)); r_b = fl32(S_t / decode(e_b))
-//     (FLT_MAX on overflow, 0 when e_b decodes to 0); code = sat_rne(E2M1, fl32(x * r_b)).
+//     overflow); e_b = sat_rne(E4M3, amax_b * S_t / 6) and code = sat_rne(E2M1, x * S_t /
+//     decode(e_b)), each rounded once from the exact quotient; a block whose e_b decodes to 0
+//     gives zero codes of the elements' signs.
 //   Codes are packed two per byte, element 2j in the low nibble of byte j.
 //
 // Conversion: v_cvt_scalef32_pk_fp4_{bf16,f32} turns two values into one byte of two E2M1 codes
@@ -28,8 +29,9 @@
 // and saturating to +-6 (Inf too). Checked on gfx950 against an exact nearest-value reference
 // for every BF16 value with all 255 scale exponents, and for every fp32 value below 16 in
 // magnitude with scale 1 (a scale of 1.5 acts as 1: only the exponent field is used). So the MX
-// path needs no separate clamp, and the NVFP4 path multiplies by r_b in fp32 first and converts
-// with scale 1.
+// path needs no separate clamp, and the NVFP4 path converts two fp32 estimates of x * S_t /
+// decode(e_b) (one below, one above the exact quotient) with scale 1 and settles the rare elements
+// where they disagree exactly (nv_elem_exact).
 #include "qf8_device.h"
 #include "qf8_internal.h"
 #include "../../include/qf8.h"
@@ -389,10 +391,11 @@ void launch_mxfp4_dirs(const void *x, int rows, int cols, uint8_t *q_row, uint8_
 // ---------------------------------------------------------------------------------------------
 // NVFP4: one thread per block of 16 consecutive elements (cols % 16 == 0, so a block never
 // crosses a row and block b of the flattened tensor is row b / (cols/16)). Every workgroup first
-// takes the tensor amax (the caller's value, or the fold of the amax pass's partials) and S_t;
-// a thread then loads its 32 (BF16) or 64 (FP32) bytes, takes the block amax, the E4M3 block
-// scale (two IEEE divisions per block: amax_b / 6 and S_t / decode(e_b)) and writes 8 bytes of
-// codes and the scale byte.
+// takes the tensor amax (the caller's value, or the fold of the amax pass's partials), S_t and the
+// table of element factors; a thread then loads its 32 (BF16) or 64 (FP32) bytes, takes the block
+// amax and the E4M3 block scale, converts the two bracketing estimates of every element and
+// writes 8 bytes of codes and the scale byte. A wave in which some block's estimates disagree
+// recomputes those blocks' codes exactly.
 
 
 template <bool BF16>
@@ -402,7 +405,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_kernel(const void *__restrict_
                                                          uint8_t *__restrict__ s_blk, float *tensor_scale,
                                                          float *amax_out, int32_t *nonfinite) {
     __shared__ uint32_t red[kThreads / 64];
-    __shared__ float tab[128];                   // r_b per E4M3 block-scale code
+    __shared__ float2 tab[128];                  // (r_lo, r_hi) per E4M3 block-scale code
     const uint32_t A = amax_in ? (__float_as_uint(*amax_in) & 0x7FFFFFFFu)
                                : block_max_bcast<kThreads>(fold_max<kThreads>(partials, nparts), red);
     const float st = nv_tensor_scale(A);
@@ -451,16 +454,32 @@ __global__ __launch_bounds__(kThreads) void nvfp4_kernel(const void *__restrict_
         for (int k = 0; k < 16; ++k) a = umax(a, __float_as_uint(f[k]) & 0x7FFFFFFFu);
         if (a >= 0x7F800000u) bad = true;        // Inf/NaN block: E4M3 NaN scale code
         const uint32_t e = nv_block_code(a, st);
-        const float r = tab[e];
-        uint32_t o0 = 0u, o1 = 0u;
-        o0 = fp4_f32<0>(o0, f[0] * r, f[1] * r, 1.0f);
-        o0 = fp4_f32<1>(o0, f[2] * r, f[3] * r, 1.0f);
-        o0 = fp4_f32<2>(o0, f[4] * r, f[5] * r, 1.0f);
-        o0 = fp4_f32<3>(o0, f[6] * r, f[7] * r, 1.0f);
-        o1 = fp4_f32<0>(o1, f[8] * r, f[9] * r, 1.0f);
-        o1 = fp4_f32<1>(o1, f[10] * r, f[11] * r, 1.0f);
-        o1 = fp4_f32<2>(o1, f[12] * r, f[13] * r, 1.0f);
-        o1 = fp4_f32<3>(o1, f[14] * r, f[15] * r, 1.0f);
+        const float2 r = tab[e];
+        uint32_t o[2], h[2];
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+            const float *g = f + 8 * w;
+            uint32_t lo = 0u, hi = 0u;
+            lo = fp4_f32<0>(lo, g[0] * r.x, g[1] * r.x, 1.0f);
+            lo = fp4_f32<1>(lo, g[2] * r.x, g[3] * r.x, 1.0f);
+            lo = fp4_f32<2>(lo, g[4] * r.x, g[5] * r.x, 1.0f);
+            lo = fp4_f32<3>(lo, g[6] * r.x, g[7] * r.x, 1.0f);
+            hi = fp4_f32<0>(hi, g[0] * r.y, g[1] * r.y, 1.0f);
+            hi = fp4_f32<1>(hi, g[2] * r.y, g[3] * r.y, 1.0f);
+            hi = fp4_f32<2>(hi, g[4] * r.y, g[5] * r.y, 1.0f);
+            hi = fp4_f32<3>(hi, g[6] * r.y, g[7] * r.y, 1.0f);
+            o[w] = lo; h[w] = hi;
+        }
+        const bool miss = (o[0] != h[0]) | (o[1] != h[1]);
+        if (__builtin_amdgcn_ballot_w64(miss) != 0u) {            // rare: wave-uniform branch
+            if (miss) {
+                const float dec = __builtin_amdgcn_cvt_f32_fp8(e, 0);
+                o[0] = o[1] = 0u;
+#pragma unroll
+                for (int k = 0; k < 16; ++k) o[k >> 3] |= nv_elem_exact(f[k], st, dec) << (4 * (k & 7));
+            }
+        }
+        const uint32_t o0 = o[0], o1 = o[1];
         if (valid) st_stream((uint2 *)q + blk, make_uint2(o0, o1));
         if (sb_aligned && base + kThreads <= nblk) {     // uniform over the workgroup
             sbuf[threadIdx.x] = (uint8_t)e;

@@ -399,37 +399,93 @@ constexpr int kOpFp8 = 0, kOpNvfp4 = 1;
 template <int OP, bool BF16>
 constexpr uint32_t op_out_bytes() { return OP == kOpFp8 ? (BF16 ? 8u : 4u) : (BF16 ? 4u : 2u); }
 
+// NVFP4 codes of one input vector from two estimates of x * S_t / decode(e_b), one below and one
+// above the exact quotient (nv_factor_table); returns them in `lo`, and whether they disagree
+// somewhere (the vector is then recomputed exactly by nv_fix_vec after the caller's stores).
 template <bool BF16>
-__device__ __forceinline__ void nv_vec_store(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t wsb, uint32_t vrel,
-                                             uint4 v, float st, const float *tab) {
+__device__ __forceinline__ bool nv_vec_codes(uint4 v, float2 r, uint32_t &lo) {
+    uint32_t l = 0u, h = 0u;
+    if constexpr (BF16) {
+        l = cvt_fp4_f32<0>(l, bf16_lo(v.x) * r.x, bf16_hi(v.x) * r.x, 1.0f);
+        l = cvt_fp4_f32<1>(l, bf16_lo(v.y) * r.x, bf16_hi(v.y) * r.x, 1.0f);
+        l = cvt_fp4_f32<2>(l, bf16_lo(v.z) * r.x, bf16_hi(v.z) * r.x, 1.0f);
+        l = cvt_fp4_f32<3>(l, bf16_lo(v.w) * r.x, bf16_hi(v.w) * r.x, 1.0f);
+        h = cvt_fp4_f32<0>(h, bf16_lo(v.x) * r.y, bf16_hi(v.x) * r.y, 1.0f);
+        h = cvt_fp4_f32<1>(h, bf16_lo(v.y) * r.y, bf16_hi(v.y) * r.y, 1.0f);
+        h = cvt_fp4_f32<2>(h, bf16_lo(v.z) * r.y, bf16_hi(v.z) * r.y, 1.0f);
+        h = cvt_fp4_f32<3>(h, bf16_lo(v.w) * r.y, bf16_hi(v.w) * r.y, 1.0f);
+    } else {
+        l = cvt_fp4_f32<0>(l, __uint_as_float(v.x) * r.x, __uint_as_float(v.y) * r.x, 1.0f);
+        l = cvt_fp4_f32<1>(l, __uint_as_float(v.z) * r.x, __uint_as_float(v.w) * r.x, 1.0f);
+        h = cvt_fp4_f32<0>(h, __uint_as_float(v.x) * r.y, __uint_as_float(v.y) * r.y, 1.0f);
+        h = cvt_fp4_f32<1>(h, __uint_as_float(v.z) * r.y, __uint_as_float(v.w) * r.y, 1.0f);
+    }
+    lo = l;
+    return l != h;
+}
+
+// A block of 16 is 2 (BF16) or 4 (FP32) vectors held by adjacent lanes, whose amax meets by DPP;
+// each lane writes its 4 or 2 code bytes and the block's first lane the E4M3 scale byte. All lanes
+// must be active. Returns whether the vector needs nv_fix_vec.
+template <bool BF16>
+__device__ __forceinline__ bool nv_vec_store(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t wsb, uint32_t vrel,
+                                             uint4 v, float st, const float2 *tab) {
     uint32_t a = acc_to_f32bits<BF16>(vec_absmax<BF16>(0u, v));
     if constexpr (BF16) a = umax(a, dpp_mov<0xB1>(a));         // lanes 2j, 2j+1 hold one block
     else a = max_quad(a);                                       // lanes 4j .. 4j+3
     const uint32_t e = nv_block_code(a, st);
-    const float r = tab[e];
+    uint32_t o;
+    const bool miss = nv_vec_codes<BF16>(v, tab[e], o);
     if constexpr (BF16) {
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        uint32_t o = 0u;
-        o = cvt_fp4_f32<0>(o, __uint_as_float(w[0] << 16) * r, __uint_as_float(w[0] & 0xFFFF0000u) * r, 1.0f);
-        o = cvt_fp4_f32<1>(o, __uint_as_float(w[1] << 16) * r, __uint_as_float(w[1] & 0xFFFF0000u) * r, 1.0f);
-        o = cvt_fp4_f32<2>(o, __uint_as_float(w[2] << 16) * r, __uint_as_float(w[2] & 0xFFFF0000u) * r, 1.0f);
-        o = cvt_fp4_f32<3>(o, __uint_as_float(w[3] << 16) * r, __uint_as_float(w[3] & 0xFFFF0000u) * r, 1.0f);
         buf_store4<kNonTemporal>(wq, vrel * 4u, 0u, o);
         if ((vrel & 1u) == 0u) buf_store1(wsb, vrel >> 1, 0u, e);
     } else {
-        uint32_t o = 0u;
-        o = cvt_fp4_f32<0>(o, __uint_as_float(v.x) * r, __uint_as_float(v.y) * r, 1.0f);
-        o = cvt_fp4_f32<1>(o, __uint_as_float(v.z) * r, __uint_as_float(v.w) * r, 1.0f);
         buf_store2(wq, vrel * 2u, 0u, o);
         if ((vrel & 3u) == 0u) buf_store1(wsb, vrel >> 2, 0u, e);
     }
+    return miss;
+}
+
+// The exact codes of vector vabs (its index in x; vrel is its index in wq), by one lane alone: the
+// block's vectors are read again from memory for its amax, and every element takes nv_elem_exact.
+// The lane's earlier store of the same bytes was issued first, so this one is the one that stays.
+template <bool BF16>
+__device__ __forceinline__ void nv_fix_vec(const uint4 *xv, __amdgpu_buffer_rsrc_t wq, uint32_t vrel, int64_t vabs,
+                                        float st) {
+    constexpr int64_t kVpb = BF16 ? 2 : 4;
+    const int64_t b0 = vabs - vabs % kVpb;
+    uint32_t a = 0u;
+    for (int64_t i = 0; i < kVpb; ++i) a = vec_absmax<BF16>(a, xv[b0 + i]);
+    const uint32_t e = nv_block_code(acc_to_f32bits<BF16>(a), st);
+    const float dec = __builtin_amdgcn_cvt_f32_fp8(e, 0);
+    const uint4 v = xv[vabs];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o = 0u;
+    if (dec == dec && dec != 0.0f) {               // else signed zeros (or a non-finite block)
+        if constexpr (BF16) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                o |= nv_elem_exact(bf16_lo(w[k]), st, dec) << (8 * k);
+                o |= nv_elem_exact(bf16_hi(w[k]), st, dec) << (8 * k + 4);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) o |= nv_elem_exact(__uint_as_float(w[k]), st, dec) << (4 * k);
+        }
+    }
+    if constexpr (BF16) buf_store4<kNonTemporal>(wq, vrel * 4u, 0u, o);
+    else buf_store2(wq, vrel * 2u, 0u, o);
 }
 
 template <int OP, bool BF16, int FMT>
-__device__ __forceinline__ void op_vec_store(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t wsb, uint32_t vrel,
-                                             uint4 v, float s, const float *tab) {
-    if constexpr (OP == kOpFp8) cast_vec_store<BF16, FMT>(wq, vrel * op_out_bytes<OP, BF16>(), v, s);
-    else nv_vec_store<BF16>(wq, wsb, vrel, v, s, tab);
+__device__ __forceinline__ bool op_vec_store(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t wsb, uint32_t vrel,
+                                             uint4 v, float s, const float2 *tab) {
+    if constexpr (OP == kOpFp8) {
+        cast_vec_store<BF16, FMT>(wq, vrel * op_out_bytes<OP, BF16>(), v, s);
+        return false;
+    } else {
+        return nv_vec_store<BF16>(wq, wsb, vrel, v, s, tab);
+    }
 }
 
 // Byte count of the vectors [first, nvec) clamped to one buffer descriptor's range.
@@ -444,7 +500,7 @@ __device__ __forceinline__ uint32_t span_bytes(int64_t first, int64_t nvec, uint
 // load, and cast + store when CAST, return the |x| maximum (accumulator form).
 template <int OP, bool BF16, int FMT, bool CAST>
 __device__ __forceinline__ uint32_t stream_slabs8(const uint4 *x, int64_t nvec, uint8_t *q, uint8_t *sb, int64_t k,
-                                                  int j, int G, float s, const float *tab) {
+                                                  int j, int G, float s, const float2 *tab) {
     constexpr uint32_t kOut = op_out_bytes<OP, BF16>();
     constexpr uint32_t kVpb = BF16 ? 2u : 4u;                      // vectors per NVFP4 block
     const uint32_t step = (uint32_t)G * kOpThreads * 16u;
@@ -458,8 +514,19 @@ __device__ __forceinline__ uint32_t stream_slabs8(const uint4 *x, int64_t nvec, 
         const __amdgpu_buffer_rsrc_t w = make_rsrc(q + first * kOut, span_bytes(first, nvec, kOut));
         const __amdgpu_buffer_rsrc_t wsb = make_rsrc(OP == kOpNvfp4 ? sb + first / kVpb : q,
                                                      OP == kOpNvfp4 ? span_bytes(first, nvec, 1u) / kVpb : 0u);
+        uint32_t miss = 0u;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) op_vec_store<OP, BF16, FMT>(w, wsb, i * (step / 16u) + threadIdx.x, v[i], s, tab);
+        for (int i = 0; i < 8; ++i)
+            miss |= (uint32_t)op_vec_store<OP, BF16, FMT>(w, wsb, i * (step / 16u) + threadIdx.x, v[i], s, tab) << i;
+        if constexpr (OP == kOpNvfp4) {
+            if (__builtin_amdgcn_ballot_w64(miss != 0u) != 0u) {        // rare: wave-uniform branch
+                while (miss != 0u) {                // the lane's set bits, lowest first
+                    const uint32_t vr = (uint32_t)__builtin_ctz(miss) * (step / 16u) + threadIdx.x;
+                    miss &= miss - 1u;
+                    nv_fix_vec<BF16>(x, w, vr, first + vr, s);
+                }
+            }
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) a = vec_absmax<BF16>(a, v[i]);
@@ -493,7 +560,7 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
     __shared__ uint32_t red[kOpThreads / 64];
     __shared__ uint32_t sh[3];
     __shared__ uint16_t gave_up[kBarMaxGroups];
-    __shared__ float nvtab[OP == kOpNvfp4 ? 128 : 1];             // NVFP4: r_b per E4M3 code
+    __shared__ float2 nvtab[OP == kOpNvfp4 ? 128 : 1];            // NVFP4: (r_lo, r_hi) per E4M3 code
     const uint4 *xv = (const uint4 *)x;
     const int G = gridDim.x, b = blockIdx.x, t = threadIdx.x;
     const int64_t nslabs = (nvec + kOpThreads - 1) / kOpThreads;
@@ -586,11 +653,33 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
 
     // pass 2: cast the held slabs, then re-read and cast the rest (vector indices: vbase + k * vstep)
     const uint32_t vbase = (uint32_t)b * kOpThreads + t, vstep = step / 16u;
+    // NVFP4: one bit per held vector whose two estimates disagree. Each bit is pinned in a register
+    // as soon as it is known (the empty asm), so that the compiler does not carry every vector's
+    // inputs down to the fix-up below.
+    uint32_t miss_w[2] = {0u, 0u};
 #pragma unroll
-    for (int k = 0; k < KR; ++k) op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + k * vstep, R[k], s, nvtab);
+    for (int k = 0; k < KR; ++k) {
+        miss_w[k >> 5] |= (uint32_t)op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + k * vstep, R[k], s, nvtab) << (k & 31);
+        if constexpr (OP == kOpNvfp4) asm volatile("" : "+v"(miss_w[k >> 5]));
+    }
 #pragma unroll
-    for (int k = 0; k < KL; ++k)
-        op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + (KR + k) * vstep, held[k * kOpThreads + t], s, nvtab);
+    for (int k = 0; k < KL; ++k) {
+        miss_w[(KR + k) >> 5] |= (uint32_t)op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + (KR + k) * vstep,
+                                                                       held[k * kOpThreads + t], s, nvtab)
+                                 << ((KR + k) & 31);
+        if constexpr (OP == kOpNvfp4) asm volatile("" : "+v"(miss_w[(KR + k) >> 5]));
+    }
+    uint64_t miss = (uint64_t)miss_w[0] | ((uint64_t)miss_w[1] << 32);
+    if constexpr (OP == kOpNvfp4) {
+        static_assert(KR + KL <= 64, "one miss bit per held slab");
+        if (__builtin_amdgcn_ballot_w64(miss != 0u) != 0u) {            // rare: wave-uniform branch
+            while (miss != 0u) {                    // the lane's set bits, lowest first
+                const uint32_t k = (uint32_t)__builtin_ctzll(miss);
+                miss &= miss - 1u;
+                nv_fix_vec<BF16>(xv, rq, vbase + k * vstep, vbase + k * vstep, s);
+            }
+        }
+    }
     for (int64_t k = KR + KL; k * G + b < nslabs; k += 8)
         stream_slabs8<OP, BF16, FMT, true>(xv, nvec, q, sb, k, b, G, s, nvtab);
 

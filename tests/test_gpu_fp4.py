@@ -11,6 +11,8 @@ MXFP4 (quantize_mxfp4_dual):
 NVFP4 (quantize_nvfp4):
   * blocks whose amax spans the E4M3 block-scale range under S_t = 1 (a 2688 in the tensor),
     each holding every BF16 magnitude down to amax / 4096 with random signs;
+  * quotients x * S_t / decode(e_b) on and next to every E2M1 midpoint, fp32 and BF16, unit and
+    random tensor scales, through both kernels (the oracle rounds each quotient once);
   * random BF16 and FP32 tensors of several shapes (S_t != 1), a caller-given amax equal to and
     below the measured one, an all-zero tensor, a tensor with a subnormal amax, Inf/NaN;
   * the full 16384 x 4096 workload, every byte.
@@ -349,6 +351,61 @@ def test_nvfp4_single_pass_other_grids(grid):
         check_nv_big(mx_gradient(2048, 4096, seed=40 + grid), ws, f"grid {grid}")
     finally:
         qf8.qf8_set_onepass_grid(0)
+
+
+MIDPOINTS = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]          # between consecutive E2M1 values
+
+
+def nv_tie_tensor(rows, cols, seed, dtype, unit_scale):
+    """A tensor whose blocks put x * S_t / decode(e_b) on and next to the E2M1 midpoints, where
+    one rounding of the exact quotient decides the code. Element [0, 0] is the tensor amax A:
+    2688 (S_t = 1) when unit_scale, else a random A. Every block takes a random E4M3 code e,
+    holds its amax 6 * decode(e) / S_t and elements m * decode(e) / S_t for random midpoints m,
+    exact or moved by up to two steps of the input format (fp32 or BF16), with random signs."""
+    rng = np.random.default_rng(seed)
+    f32 = np.float32
+    A = f32(2688.0) if unit_scale else f32(rng.uniform(1, 2) * 2.0 ** int(rng.integers(-8, 8)))
+    s_t = O.nvfp4_tensor_scale(float(A))
+    nb = rows * cols // 16
+    e = rng.integers(1, 127, nb)
+    dec = np.array([O.decode(O.E4M3, c) for c in range(128)])[e]
+    m = np.array(MIDPOINTS)[rng.integers(0, 7, (nb, 16))]
+    x = (m * dec[:, None] / float(s_t)).astype(np.float32)
+    x[:, 0] = (6.0 * dec / float(s_t)).astype(np.float32)
+    if dtype == "bf16":
+        bits = (x.view(np.uint32) >> 16).astype(np.int32)        # exact: at most 7 significant bits
+        bits[:, 1:] += rng.integers(-2, 3, (nb, 15))
+        bits |= rng.integers(0, 2, bits.shape) << 15
+        out = bits.astype(np.uint16).reshape(rows, cols)
+        out[0, 0] = 0x4528                                        # 2688.0
+        return out
+    u = x.view(np.int32)
+    u[:, 1:] += rng.integers(-2, 3, (nb, 15)).astype(np.int32)
+    x = u.view(np.float32) * np.where(rng.integers(0, 2, x.shape) == 1, f32(-1), f32(1))
+    x = x.reshape(rows, cols)
+    x[0, 0] = A
+    return x
+
+
+@pytest.mark.parametrize("dtype,unit", [("fp32", True), ("fp32", False), ("bf16", True)])
+def test_nvfp4_midpoint_ties_streaming(dtype, unit):
+    """Quotients on and within two input steps of every E2M1 midpoint (and block amaxes on E4M3
+    midpoints' neighbours), through the streaming kernel: every byte equals the oracle, which
+    rounds each quotient once."""
+    x = nv_tie_tensor(96, 512, seed=31 + unit, dtype=dtype, unit_scale=unit)
+    g = check_nv(x, tag=f"ties {dtype} unit_scale={unit}")
+    if unit:
+        assert g[2] == 1.0
+
+
+@pytest.mark.parametrize("dtype,unit", [("fp32", False), ("bf16", True)])
+def test_nvfp4_midpoint_ties_single_pass(dtype, unit):
+    """The same construction at 2^22 elements, through the single-pass kernel (the tensor held on
+    chip across its grid barrier; vectors whose two estimates disagree are recomputed exactly
+    from memory after the held slabs are written)."""
+    ws = qf8.workspace(torch.empty(1, device="cuda"))
+    x = nv_tie_tensor(2048, 2048, seed=35 + unit, dtype=dtype, unit_scale=unit)
+    check_nv_big(x, ws, f"ties {dtype} unit_scale={unit} 2048x2048")
 
 
 # ---- FP4 de-scaling ------------------------------------------------------------------------------
