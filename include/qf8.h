@@ -110,6 +110,22 @@ int quantize_per_tensor(const void *x, int dtype, int64_t rows, int64_t cols, in
                         uint8_t *q, float *amax, float *scale, int32_t *nonfinite,
                         void *ws, size_t ws_bytes, void *stream);
 
+/* quantize_per_tensor without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments (minus ws, ws_bytes), results and errors as quantize_per_tensor; it allocates
+ * nothing (no hipMalloc, hipFree or allocating library call). The workspace is a file-scope
+ * device array of qf8_workspace_bytes() bytes (about 160 KiB) inside the library: each GPU the
+ * library runs on holds its own copy until the process ends. Its size does not depend on the
+ * tensor, so no shape quantize_per_tensor accepts is refused for lack of scratch (QF8_ERR_WORKSPACE
+ * would mean a library built with a smaller array). The array starts zero and every call leaves it
+ * zero again, so calls ordered on one stream need no set-up; calls that overlap on one GPU (two
+ * streams or two threads without ordering between them) share that array and race. The first call
+ * on a device looks the array's device address up (QF8_ERR_HIP if that fails). The give-up timeout
+ * of the single-pass kernel is the default (word 2 of the array stays 0). */
+int quantize_per_tensor_noalloc(const void *x, int dtype, int64_t rows, int64_t cols, int fmt,
+                                uint8_t *q, float *amax, float *scale, int32_t *nonfinite,
+                                void *stream);
+
 /* Per-tensor delayed scaling ([HiF8-train 1.2] Eq.(3)-(4) and section 5.2; [MP-FP8 8.2]).
  * State: a FIFO of the last hist_len amax values kept on the device; the estimate is the
  * maximum over it; the scale a step uses is S = fl32(F8max / estimate) * 2^-n_guard.

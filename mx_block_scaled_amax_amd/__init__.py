@@ -69,6 +69,7 @@ def _load():
         "qf8_set_onepass_grid": (i32, [i32]),
         "qf8_cast_scaled": (i32, [vp, i32, i64, i32, vp, vp, vp]),
         "quantize_per_tensor": (i32, [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, sz, vp]),
+        "quantize_per_tensor_noalloc": (i32, [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp]),
         "qf8_delayed_init": (i32, [ctypes.POINTER(_DelayedStruct), vp, vp, vp, i32, i32, i32, i32, vp]),
         "qf8_delayed_init_ex": (i32, [ctypes.POINTER(_DelayedStruct), vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]),
         "qf8_delayed_reset": (i32, [ctypes.POINTER(_DelayedStruct), vp]),

@@ -106,6 +106,24 @@ int quantize_per_tensor(const void *x, int dtype, int64_t rows, int64_t cols, in
                                     qf8::stream_grid(n, dtype), s);
 }
 
+int quantize_per_tensor_noalloc(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, uint8_t *q,
+                                float *amax, float *scale, int32_t *nonfinite, void *stream) {
+    // the argument checks of quantize_per_tensor come first, so a bad call touches no device state
+    if (!dtype_ok(dtype) || !fmt_ok(fmt)) return QF8_ERR_ENUM;
+    if (!dims_ok(rows, cols)) return QF8_ERR_SHAPE;
+    const int64_t n = rows * cols;
+    if ((n > 0 && (!x || !q)) || !amax || !scale) return QF8_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(q, 16) || !aligned(amax, 4) || !aligned(scale, 4) ||
+        (nonfinite && !aligned(nonfinite, 4)))
+        return QF8_ERR_ALIGN;
+    uint32_t *ws = nullptr;
+    size_t ws_bytes = 0;
+    const int st = qf8::scratch_workspace(&ws, &ws_bytes);
+    if (st != QF8_OK) return st;
+    if (ws_bytes < qf8::kWorkspaceBytes) return QF8_ERR_WORKSPACE;   // fixed size: every shape fits
+    return quantize_per_tensor(x, dtype, rows, cols, fmt, q, amax, scale, nonfinite, ws, ws_bytes, stream);
+}
+
 int qf8_delayed_init_ex(qf8_delayed_state *st, float *history, int32_t *meta, float *scale, int hist_len,
                         int interval, int n_guard, int fmt, int estimator, int flags, void *stream) {
     if (!st || !history || !meta || !scale) return QF8_ERR_NULL;

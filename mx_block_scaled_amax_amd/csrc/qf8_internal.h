@@ -67,6 +67,9 @@ int launch_delayed_finalize(uint32_t *slots, const uint32_t *partials, int npart
                             float *scale, int hist_len, int n_guard, int fmt, int update, int estimator,
                             int split, float *amax_out, int32_t *nonfinite, hipStream_t s);
 int launch_fill_u32(uint32_t *p, int64_t n, uint32_t value, hipStream_t s);
+// The current device's file-scope workspace (quantize_per_tensor_noalloc): its device address and
+// size, looked up once per device. QF8_ERR_HIP if the device or the symbol cannot be queried.
+int scratch_workspace(uint32_t **ws, size_t *ws_bytes);
 
 int launch_block(const void *x, int dtype, int64_t rows, int64_t cols, int block_rows, int fmt, int pow2, uint8_t *q,
                  float *scales, float *amax, int32_t *nonfinite, hipStream_t s);

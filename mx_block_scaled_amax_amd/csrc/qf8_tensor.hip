@@ -29,6 +29,7 @@
 //                      workgroup to one address serialize at the memory side.)
 //   per_tensor_onepass -- current scaling for large tensors in one HBM read (described below).
 #include <atomic>
+#include <mutex>
 
 #include "qf8_device.h"
 #include "qf8_internal.h"
@@ -875,6 +876,41 @@ int launch_delayed_finalize(uint32_t *slots, const uint32_t *partials, int npart
         hipLaunchKernelGGL(delayed_finalize_kernel<kE5M2>, dim3(1), dim3(kFinalizeThreads), 0, s, slots, partials, nparts,
                            history, meta, scale, hist_len, n_guard, update, estimator, split, amax_out, nonfinite);
     return status_after_launch();
+}
+
+// ---- the per-tensor workspace for callers that cannot allocate -------------------------------
+// A file-scope device array with the layout of a caller's workspace: each GPU holds its own copy
+// (each device loads its own copy of this code object) from load until the process ends. It starts
+// zero (a device object without initializer is zero-filled when the code object is loaded), and
+// every call leaves its barrier and slot words zero again, as with a caller's workspace. In host
+// code `scratch` names a host-side stand-in, not device memory: the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only that address is handed
+// to kernels.
+static __device__ __align__(256) uint32_t scratch[kWorkspaceBytes / sizeof(uint32_t)];
+static_assert(sizeof(scratch) >= kWorkspaceBytes, "the scratch array holds a whole workspace");
+
+namespace {
+std::atomic<uint32_t *> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mutex;
+}  // namespace
+
+int scratch_workspace(uint32_t **ws, size_t *ws_bytes) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QF8_ERR_HIP;
+    uint32_t *p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            void *addr = nullptr;
+            if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return QF8_ERR_HIP;
+            p = (uint32_t *)addr;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ws = p;
+    *ws_bytes = sizeof(scratch);
+    return QF8_OK;
 }
 
 int launch_fill_u32(uint32_t *p, int64_t n, uint32_t value, hipStream_t s) {
