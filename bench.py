@@ -20,7 +20,11 @@ variant finds the previous variant's data in the 256 MB last-level cache.
   roofline.traffic = HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE counters (in
                    profiles/), scaled by the same counters' reading for a plain copy of known
                    size; null when the kernel sources changed since the counters were taken.
-  cpu_baseline   = the CPU oracle (single-threaded C) on the first 4096 rows, all four variants.
+  config.per_tensor_8192x8192 = per-tensor current scaling of the 8192x8192 BF16 activation, E4M3
+                   and E5M2, each launch's average over back-to-back launches under one event pair
+                   (algorithmic bytes 2N + N + 8 = 201,326,600), with its % of HBM peak.
+  cpu_baseline   = the CPU oracle (plain C) on the whole input, all four variants, on 1 thread and on
+                   T threads over row bands (T = the usable CPUs, at most 16), with the CPU model.
 
 --suite also times every other operation on its workload (per-tensor, delayed with its variants,
 1x128, 128x128, re-grouping, MXFP4, NVFP4, de-scaling and error statistics, MX rowwise on the small
@@ -111,18 +115,98 @@ class DualCall:
             raise RuntimeError(f"quantize_mx_dual failed with status {st}")
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(xb):
+    """The CPU oracle (plain single-threaded C, test infrastructure) on the whole 16384x4096
+    workload, all four dual variants: once on one thread, once with the rows cut into T bands of
+    a multiple of 32 rows run on T threads (ctypes releases the GIL, so the bands run in parallel;
+    each band's columnwise blocks lie inside it). T = the CPUs this process may use, at most 16 (a
+    GPU's share of the host). The T-thread rate is the reported value."""
+    from concurrent.futures import ThreadPoolExecutor
     import oracle as O
-    sample = xb[:4096]
+    variants = [(f, r) for f in (O.E4M3, O.E5M2) for r in (O.ROUND_DOWN, O.ROUND_UP)]
+    nbytes = len(variants) * DUAL_BYTES
+    nproc = os.cpu_count() or 1
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = nproc
+    threads = max(1, min(16, usable))
     t0 = time.perf_counter()
-    for fmt in (O.E4M3, O.E5M2):
-        for rnd in (O.ROUND_DOWN, O.ROUND_UP):
-            O.quantize_mx(sample, fmt, rnd)
-    dt = time.perf_counter() - t0
-    nbytes = 4 * (4 * sample.size + 2 * (sample.size // 32))
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"rows 0..4095 of the 16384x4096 input (1/4 of it), all four variants, "
-                      f"single-threaded C oracle, {dt:.2f} s on {platform.processor() or platform.machine()}"}
+    for fmt, rnd in variants:
+        O.quantize_mx(xb, fmt, rnd)
+    one = time.perf_counter() - t0
+    band = -(-ROWS // threads)
+    band = -(-band // 32) * 32
+    bounds = [(r, min(r + band, ROWS)) for r in range(0, ROWS, band)]
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        for fmt, rnd in variants:
+            list(ex.map(lambda b: O.quantize_mx(xb[b[0]:b[1]], fmt, rnd), bounds))
+    par = time.perf_counter() - t0
+    return {"value": round(nbytes / par / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole 16384x4096 input, all four dual variants ({nbytes} algorithmic bytes): "
+                      f"{par:.2f} s on {threads} threads (row bands of {band}), {one:.2f} s on 1 thread",
+            "one_thread_GBps": round(nbytes / one / 1e9, 4), "cpu_model": cpu_model(), "nproc": nproc,
+            "usable_cpus": usable}
+
+
+def time_per_tensor(args, qf8, stream):
+    """Per-tensor current scaling of the 8192x8192 BF16 activation (N(0,1), 0.1% entries x1000,
+    seed 2), E4M3 and E5M2: args.steps rounds over four device-resident input copies, launches back
+    to back under one HIP event pair on the launch stream; algorithmic bytes 2N read + N written +
+    the fp32 amax and scale = 201,326,600 per launch."""
+    import torch
+    from synthetic import per_tensor_activation
+    xb = per_tensor_activation()
+    xs = [to_dev(xb) for _ in range(4)]
+    n = xb.size
+    nbytes = 3 * n + 8
+    q = torch.empty(xb.shape, dtype=torch.uint8, device="cuda")
+    am = torch.empty(1, dtype=torch.float32, device="cuda")
+    sc = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = qf8.workspace(xs[0])
+    lib = qf8._load()
+    vp = ctypes.c_void_p
+    sp = vp(stream.cuda_stream)
+    out = {"workload": "per_tensor_current_8192x8192", "values": "N(0,1), 0.1% entries x1000, seed 2",
+           "algorithmic_bytes": nbytes}
+    for fmt, name in ((qf8.E4M3, "e4m3"), (qf8.E5M2, "e5m2")):
+        args_of = [(vp(x.data_ptr()), 0, xb.shape[0], xb.shape[1], fmt, vp(q.data_ptr()), vp(am.data_ptr()),
+                    vp(sc.data_ptr()), None, vp(ws.data_ptr()), ws.numel(), sp) for x in xs]
+
+        def run():
+            for a in args_of:
+                st = lib.quantize_per_tensor(*a)
+                if st != 0:
+                    raise RuntimeError(f"quantize_per_tensor failed with status {st}")
+        for _ in range(args.warmup):
+            run()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (4 * args.steps)
+        gbps = nbytes / (ms / 1e3) / 1e9
+        out[name] = {"avg_launch_ms": round(ms, 5), "GBps": round(gbps, 1),
+                     "pct_of_hbm_peak": round(100 * gbps / PEAK_GBPS, 2)}
+    del xs
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -224,6 +308,8 @@ def main():
             cold[j].append(e0.elapsed_time(e1))
     del flush
     cold_med = [float(np.median(v)) for v in cold]
+    cold_all = np.concatenate([np.array(v) for v in cold])
+    per_tensor = time_per_tensor(args, qf8, stream)
     value = len(calls) * DUAL_BYTES * args.steps / wall / 1e9
     traffic = stored_traffic()
     line = {
@@ -248,7 +334,11 @@ def main():
                        ["e4m3-round_down", "e4m3-round_up", "e5m2-round_down", "e5m2-round_up"])},
                    "cold_median_ms_per_variant": {v: round(cold_med[j], 5) for j, v in enumerate(
                        ["e4m3-round_down", "e4m3-round_up", "e5m2-round_down", "e5m2-round_up"])},
-                   "cold_pct_of_hbm_peak": round(100 * DUAL_BYTES / (float(np.mean(cold_med)) / 1e3) / 1e9 / PEAK_GBPS, 2)},
+                   "cold_pct_of_hbm_peak": round(100 * DUAL_BYTES / (float(np.mean(cold_med)) / 1e3) / 1e9 / PEAK_GBPS, 2),
+                   "cold_ms_all_variants": {"median": round(float(np.median(cold_all)), 5),
+                                            "min": round(float(cold_all.min()), 5),
+                                            "p90": round(float(np.percentile(cold_all, 90)), 5)},
+                   "per_tensor_8192x8192": per_tensor},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBPS, 4), "traffic": traffic},
     }
