@@ -463,7 +463,7 @@ def run_suite(args):
     R, C = xsd[0].shape
 
     def steps_of(state, amax_out=None):
-        return [PreCall(L.quantize_delayed, vp(x), 0, R, C, ctypes.byref(state.struct), vp(qd), None,
+        return [PreCall(L.quantize_delayed, vp(x), 0, R, C, state.struct.fmt, ctypes.byref(state.struct), vp(qd), None,
                         None if amax_out is None else vp(amax_out), None, vp(wsd), wsd.numel(), sp) for x in xsd]
     for c in steps_of(qf8.DelayedState(16, 5, 3, qf8.E4M3))[:3]:     # warm the code paths on a throwaway state
         c()

@@ -61,7 +61,7 @@ typedef enum qf8_status {
 } qf8_status;
 
 /* Human-readable name of a status code. Never NULL. */
-const char *qf8_status_string(int status);
+const char *qf8_status_string(qf8_status status);
 
 /* Bytes of device workspace quantize_per_tensor and quantize_delayed need for a tensor of
  * rows x cols elements of dtype (currently a constant of about 160 KiB): a grid-barrier region
@@ -73,7 +73,7 @@ const char *qf8_status_string(int status);
  * the same time need two workspaces. Word 2 (u32) of the workspace, if non-zero, replaces the
  * default 1 ms after which a workgroup waiting at the grid barrier gives its slabs to the last
  * workgroup, in 10 ns ticks (tests set it tiny to exercise that path). */
-size_t qf8_workspace_bytes(int64_t rows, int64_t cols, int dtype);
+size_t qf8_workspace_bytes(int64_t rows, int64_t cols, qf8_dtype dtype);
 
 /* Sets the number of workgroups of the single-pass kernel (quantize_per_tensor from 2^22
  * elements, delayed-scaling step 0, quantize_nvfp4 with a measured amax) on the current device:
@@ -83,18 +83,18 @@ size_t qf8_workspace_bytes(int64_t rows, int64_t cols, int dtype);
  * slower. The setting is per process and device and applies to calls made after it; calls
  * already enqueued keep their grid. Returns QF8_ERR_SHAPE for a grid outside [0, 512] (checked
  * before any HIP call), QF8_ERR_HIP if the current device cannot be queried. */
-int qf8_set_onepass_grid(int grid);
+qf8_status qf8_set_onepass_grid(int grid);
 
 /* Enqueues a zero fill of the qf8_workspace_bytes() bytes at ws (16-byte aligned, ws_bytes at
  * least that size) on stream. */
-int qf8_workspace_init(void *ws, size_t ws_bytes, void *stream);
+qf8_status qf8_workspace_init(void *ws, size_t ws_bytes, void *stream);
 
 /* Scaled saturating cast (Eq.(2) of [HiF8-train 1.2], [MP-FP8 8.1]):
  *   q[i] = sat_rne8(fl32(x[i] * scale[0])),  i in [0, n).
  * x: n elements of dtype, 16-byte aligned. scale: one device fp32 value. q: n bytes, 16-byte
  * aligned. n >= 0 (n = 0 enqueues nothing). */
-int qf8_cast_scaled(const void *x, int dtype, int64_t n, int fmt, const float *scale,
-                    uint8_t *q, void *stream);
+qf8_status qf8_cast_scaled(const void *x, qf8_dtype dtype, int64_t n, qf8_fmt fmt, const float *scale, uint8_t *q,
+                           void *stream);
 
 /* Per-tensor current scaling ([HiF8-train 1.2] Eq.(1)-(2); [MP-FP8 8.1]):
  *   amax = max |x|;  S = fl32(F8max / amax);  q = sat_rne8(fl32(x * S)).
@@ -106,9 +106,9 @@ int qf8_cast_scaled(const void *x, int dtype, int64_t n, int fmt, const float *s
  * to 128 MiB of the tensor in registers and LDS (on 256 CUs) across a grid barrier on the amax
  * and casts from there; the rest of a larger tensor is re-read. Below 2^22 elements: two
  * kernels (grid-wide partial maxima, then the cast; each cast workgroup folds the partials). */
-int quantize_per_tensor(const void *x, int dtype, int64_t rows, int64_t cols, int fmt,
-                        uint8_t *q, float *amax, float *scale, int32_t *nonfinite,
-                        void *ws, size_t ws_bytes, void *stream);
+qf8_status quantize_per_tensor(const void *x, qf8_dtype dtype, int64_t rows, int64_t cols, qf8_fmt fmt, uint8_t *q,
+                               float *amax, float *scale, int32_t *nonfinite, void *ws, size_t ws_bytes,
+                               void *stream);
 
 /* quantize_per_tensor without a workspace argument, for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
@@ -122,9 +122,8 @@ int quantize_per_tensor(const void *x, int dtype, int64_t rows, int64_t cols, in
  * streams or two threads without ordering between them) share that array and race. The first call
  * on a device looks the array's device address up (QF8_ERR_HIP if that fails). The give-up timeout
  * of the single-pass kernel is the default (word 2 of the array stays 0). */
-int quantize_per_tensor_noalloc(const void *x, int dtype, int64_t rows, int64_t cols, int fmt,
-                                uint8_t *q, float *amax, float *scale, int32_t *nonfinite,
-                                void *stream);
+qf8_status quantize_per_tensor_noalloc(const void *x, qf8_dtype dtype, int64_t rows, int64_t cols, qf8_fmt fmt,
+                                       uint8_t *q, float *amax, float *scale, int32_t *nonfinite, void *stream);
 
 /* Per-tensor delayed scaling ([HiF8-train 1.2] Eq.(3)-(4) and section 5.2; [MP-FP8 8.2]).
  * State: a FIFO of the last hist_len amax values kept on the device; the estimate is the
@@ -169,17 +168,19 @@ typedef enum qf8_delayed_flags { QF8_DELAYED_SPLIT_AMAX = 1 } qf8_delayed_flags;
 
 /* Fills the host fields, clears history/meta/scale on the device, step = 0; the estimator is the
  * maximum of the history. */
-int qf8_delayed_init(qf8_delayed_state *st, float *history, int32_t *meta, float *scale,
-                     int hist_len, int interval, int n_guard, int fmt, void *stream);
+qf8_status qf8_delayed_init(qf8_delayed_state *st, float *history, int32_t *meta, float *scale, int hist_len,
+                            int interval, int n_guard, qf8_fmt fmt, void *stream);
 /* The same with an estimator (qf8_estimator) and flags (qf8_delayed_flags); other values give
  * QF8_ERR_ENUM. */
-int qf8_delayed_init_ex(qf8_delayed_state *st, float *history, int32_t *meta, float *scale,
-                        int hist_len, int interval, int n_guard, int fmt, int estimator,
-                        int flags, void *stream);
+qf8_status qf8_delayed_init_ex(qf8_delayed_state *st, float *history, int32_t *meta, float *scale, int hist_len,
+                               int interval, int n_guard, qf8_fmt fmt, qf8_estimator estimator, int flags,
+                               void *stream);
 /* Empties the history and sets step = 0, so the next step is current scaling again (the
  * restart after an anomaly, [HiF8-train 5.2]). */
-int qf8_delayed_reset(qf8_delayed_state *st, void *stream);
-/* One iteration on x (rows*cols elements, 16-byte aligned) -> q (16-byte aligned).
+qf8_status qf8_delayed_reset(qf8_delayed_state *st, void *stream);
+/* One iteration on x (rows*cols elements, 16-byte aligned) -> q (16-byte aligned). fmt must be
+ * the format the state was initialised with (QF8_ERR_STATE otherwise): the history holds amax
+ * values whose scales are F8max of that format over the estimate.
  * scale_used (nullable): the scale this step cast with. amax_out (nullable): this step's true
  * amax over the whole tensor (computed in the same pass as the cast; only update steps append
  * it to the history, or with QF8_DELAYED_SPLIT_AMAX the window's maximum over its pieces).
@@ -190,9 +191,9 @@ int qf8_delayed_reset(qf8_delayed_state *st, void *stream);
  * the state. A reuse step (not an update step, no QF8_DELAYED_SPLIT_AMAX) called with
  * scale_used, amax_out and nonfinite all NULL is the cast alone: its amax would only be
  * reported. Step 0 is the current-scaling path of quantize_per_tensor, then the finalize. */
-int quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, qf8_delayed_state *st,
-                     uint8_t *q, float *scale_used, float *amax_out, int32_t *nonfinite,
-                     void *ws, size_t ws_bytes, void *stream);
+qf8_status quantize_delayed(const void *x, qf8_dtype dtype, int64_t rows, int64_t cols, qf8_fmt fmt,
+                            qf8_delayed_state *st, uint8_t *q, float *scale_used, float *amax_out, int32_t *nonfinite,
+                            void *ws, size_t ws_bytes, void *stream);
 
 /* Fine-grained current scaling ([MP-FP8 10.2] and 10.3): Eq.(1)-(2) applied to each group of
  * block_rows x block_cols elements on its own; (block_rows, block_cols) is (1, 128) (per-token
@@ -201,9 +202,8 @@ int quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, qf8_d
  * q: [rows][cols] bytes, 16-byte aligned.
  * scales: [ceil(rows/block_rows)][ceil(cols/block_cols)] fp32, the S_g of each group.
  * amax (nullable): same shape, each group's amax. */
-int quantize_block(const void *x, int dtype, int64_t rows, int64_t cols, int block_rows,
-                   int block_cols, int fmt, uint8_t *q, float *scales, float *amax,
-                   int32_t *nonfinite, void *stream);
+qf8_status quantize_block(const void *x, qf8_dtype dtype, int64_t rows, int64_t cols, int block_rows, int block_cols,
+                          qf8_fmt fmt, uint8_t *q, float *scales, float *amax, int32_t *nonfinite, void *stream);
 
 /* Flags of quantize_block_ex and requantize_1x128_to_128x1. */
 #define QF8_FLAG_POW2_SCALES 1   /* group scales are the largest power of two S with amax*S <= F8max */
@@ -212,9 +212,9 @@ int quantize_block(const void *x, int dtype, int64_t rows, int64_t cols, int blo
  * 1x128 to 128x1 use integer powers of two as scale factors, so the re-grouping adds no error):
  * S_g = 2^-X, X = ceil(log2(amax_g / F8max)) clamped to [-127, 127]; 1 for amax_g = 0 or
  * non-finite. Unknown flag bits give QF8_ERR_ENUM. quantize_block is this call with flags 0. */
-int quantize_block_ex(const void *x, int dtype, int64_t rows, int64_t cols, int block_rows,
-                      int block_cols, int fmt, int flags, uint8_t *q, float *scales, float *amax,
-                      int32_t *nonfinite, void *stream);
+qf8_status quantize_block_ex(const void *x, qf8_dtype dtype, int64_t rows, int64_t cols, int block_rows,
+                             int block_cols, qf8_fmt fmt, int flags, uint8_t *q, float *scales, float *amax,
+                             int32_t *nonfinite, void *stream);
 
 /* Re-grouping of 1x128 groups into 128x1 groups ([MP-FP8 10.5]: read, de-scale, transpose,
  * quantize again, write back). Input: q [rows][cols] (fmt_in) with its 1x128 group scales
@@ -225,9 +225,9 @@ int quantize_block_ex(const void *x, int dtype, int64_t rows, int64_t cols, int 
  * scales on both sides and fmt_in == fmt_out, every value whose re-scaled magnitude is at least
  * the smallest normal fp8 value is carried over exactly. rows % 16 == 0, cols % 16 == 0; q, qT
  * 16-byte aligned. nonfinite (nullable) is set when a group holds Inf/NaN. */
-int requantize_1x128_to_128x1(const uint8_t *q, const float *scales, int64_t rows, int64_t cols,
-                              int fmt_in, int fmt_out, int flags, uint8_t *qT, float *scalesT,
-                              int32_t *nonfinite, void *stream);
+qf8_status requantize_1x128_to_128x1(const uint8_t *q, const float *scales, int64_t rows, int64_t cols,
+                                     qf8_fmt fmt_in, qf8_fmt fmt_out, int flags, uint8_t *qT, float *scalesT,
+                                     int32_t *nonfinite, void *stream);
 
 /* MX quantization with 1x32 blocks and E8M0 shared scales ([MP-FP8 13.1]; [MXFP8-recipe 4.1]),
  * rowwise and/or columnwise from the same high-precision input in one pass.
@@ -241,9 +241,9 @@ int requantize_1x128_to_128x1(const uint8_t *q, const float *scales, int64_t row
  * At least one direction; s_row / s_colT are required with their q. x, q_row, q_colT 16-byte
  * aligned; rows, cols <= 2^24. A block holding Inf or NaN gets scale byte 0xFF and sets
  * nonfinite. One kernel launch for either or both directions. */
-int quantize_mx_dual(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int rnd,
-                     uint8_t *q_row, uint8_t *s_row, uint8_t *q_colT, uint8_t *s_colT,
-                     int32_t *nonfinite, void *stream);
+qf8_status quantize_mx_dual(const void *x, qf8_dtype dtype, int64_t rows, int64_t cols, qf8_fmt fmt, qf8_mx_round rnd,
+                            uint8_t *q_row, uint8_t *s_row, uint8_t *q_colT, uint8_t *s_colT, int32_t *nonfinite,
+                            void *stream);
 
 /* ---- FP4: E2M1 elements ([MP-FP8 13.2]: values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives; a
  * 4-bit code S.EE.M, sign in bit 3). Codes are packed two per byte, element 2j in the low
@@ -261,17 +261,18 @@ int quantize_mx_dual(const void *x, int dtype, int64_t rows, int64_t cols, int f
  *              rows % 32 == 0.
  * At least one direction; x, q_row, q_colT 16-byte aligned; cols % 8 (BF16) or % 4 (FP32);
  * rows, cols <= 2^24. One kernel launch. */
-int quantize_mxfp4_dual(const void *x, int dtype, int64_t rows, int64_t cols, int rnd,
-                        uint8_t *q_row, uint8_t *s_row, uint8_t *q_colT, uint8_t *s_colT,
-                        int32_t *nonfinite, void *stream);
+qf8_status quantize_mxfp4_dual(const void *x, qf8_dtype dtype, int64_t rows, int64_t cols, qf8_mx_round rnd,
+                               uint8_t *q_row, uint8_t *s_row, uint8_t *q_colT, uint8_t *s_colT, int32_t *nonfinite,
+                               void *stream);
 
 /* NVFP4 ([MP-FP8 13.2]: blocks of 16 along a row, each with an E4M3 scale amax_b / 6 that can
  * align the block maximum to 6, under one fp32 tensor scale because E4M3's range is too
- * small). The tensor scale maps the largest block scale onto E4M3's largest value 448:
+ * small). The tensor scale maps the largest block scale onto E4M3's largest value 448, and each
+ * element is divided by its block's real scale decode(e_b) / S_t:
  *   S_t = fl32(448 * 6 / A)  (A = tensor amax; 1 for A = 0 or non-finite; FLT_MAX on overflow)
- *   e_b = E4M3 code of fl32(fl32(amax_b / 6) * S_t), saturating      -> s_blk
- *   r_b = fl32(S_t / decode(e_b)), FLT_MAX on overflow, 0 if e_b decodes to 0
- *   code = E2M1(fl32(x * r_b))                                       -> q
+ *   e_b = E4M3(amax_b * S_t / 6), saturating                           -> s_blk
+ *   code = E2M1(x * S_t / decode(e_b)); zero codes of x's sign when decode(e_b) = 0   -> q
+ * where E4M3(.) and E2M1(.) round the exact quotient once to the nearest value, ties to even.
  * De-scaled: xhat = code * decode(e_b) / S_t. A block with Inf/NaN gets the E4M3 NaN code 0x7F
  * and sets nonfinite. Layout: q [rows][cols/2] packed, s_blk [rows][cols/16]; cols % 16 == 0;
  * x and q 16-byte aligned. tensor_scale (required) receives S_t, amax_out (nullable) A.
@@ -280,9 +281,9 @@ int quantize_mxfp4_dual(const void *x, int dtype, int64_t rows, int64_t cols, in
  * 2^22 elements by the single-pass kernel of quantize_per_tensor (x held on chip across a grid
  * barrier, read once), below that by a read-only pass first. ws: qf8_workspace_bytes bytes,
  * 16-byte aligned, zero-initialised once as described at qf8_workspace_bytes. */
-int quantize_nvfp4(const void *x, int dtype, int64_t rows, int64_t cols, const float *amax_in,
-                   uint8_t *q, uint8_t *s_blk, float *tensor_scale, float *amax_out,
-                   int32_t *nonfinite, void *ws, size_t ws_bytes, void *stream);
+qf8_status quantize_nvfp4(const void *x, qf8_dtype dtype, int64_t rows, int64_t cols, const float *amax_in,
+                          uint8_t *q, uint8_t *s_blk, float *tensor_scale, float *amax_out, int32_t *nonfinite,
+                          void *ws, size_t ws_bytes, void *stream);
 
 /* ---- Dequantization and quantization error statistics -------------------------------------
  * De-scaling ([MP-FP8 8.1]: the code 22 with S = 22400 gives 22/22400; [MP-FP8 8.2]: the
@@ -314,22 +315,22 @@ typedef struct qf8_error_stats {
 
 /* One scale factor for all n codes (per-tensor current or delayed scaling: pass the scale the
  * quantization used). scale: one device fp32. */
-int dequantize_scaled(const uint8_t *q, int64_t n, int fmt, const float *scale, void *out, int out_dtype,
-                      const void *x, int x_dtype, qf8_error_stats *stats, void *ws, size_t ws_bytes,
-                      void *stream);
+qf8_status dequantize_scaled(const uint8_t *q, int64_t n, qf8_fmt fmt, const float *scale, void *out,
+                             qf8_out_dtype out_dtype, const void *x, qf8_dtype x_dtype, qf8_error_stats *stats,
+                             void *ws, size_t ws_bytes, void *stream);
 
 /* Groups of block_rows x block_cols ((1, 128) or (128, 128)) with their fp32 scales
  * [ceil(rows/block_rows)][ceil(cols/128)] as quantize_block writes them; cols % 4 == 0. */
-int dequantize_block(const uint8_t *q, int64_t rows, int64_t cols, int block_rows, int block_cols, int fmt,
-                     const float *scales, void *out, int out_dtype, const void *x, int x_dtype,
-                     qf8_error_stats *stats, void *ws, size_t ws_bytes, void *stream);
+qf8_status dequantize_block(const uint8_t *q, int64_t rows, int64_t cols, int block_rows, int block_cols, qf8_fmt fmt,
+                            const float *scales, void *out, qf8_out_dtype out_dtype, const void *x, qf8_dtype x_dtype,
+                            qf8_error_stats *stats, void *ws, size_t ws_bytes, void *stream);
 
 /* MX blocks of 32 along each row of q [rows][cols] with E8M0 bytes s [rows][cols/32]: a rowwise
  * result, or a columnwise result in its transposed layout (q_colT, s_colT with rows = the
  * tensor's cols). cols % 32 == 0. */
-int dequantize_mx(const uint8_t *q, const uint8_t *s, int64_t rows, int64_t cols, int fmt, void *out,
-                  int out_dtype, const void *x, int x_dtype, qf8_error_stats *stats, void *ws,
-                  size_t ws_bytes, void *stream);
+qf8_status dequantize_mx(const uint8_t *q, const uint8_t *s, int64_t rows, int64_t cols, qf8_fmt fmt, void *out,
+                         qf8_out_dtype out_dtype, const void *x, qf8_dtype x_dtype, qf8_error_stats *stats, void *ws,
+                         size_t ws_bytes, void *stream);
 
 /* FP4 de-scaling (the FP4 counterpart of the calls above; no statistics). q is packed two codes
  * per byte as the FP4 quantizers write it; element i uses the scale of its block in flattened
@@ -342,10 +343,10 @@ int dequantize_mx(const uint8_t *q, const uint8_t *s, int64_t rows, int64_t cols
  *     e_b = 0x7F. cols % 16 == 0.
  * out: [rows][cols] BF16 (round to nearest even) or FP32 (qf8_out_dtype). q and out 16-byte
  * aligned; rows * cols < 2^36. */
-int dequantize_mxfp4(const uint8_t *q, const uint8_t *sb, int64_t rows, int64_t cols, void *out,
-                     int out_dtype, void *stream);
-int dequantize_nvfp4(const uint8_t *q, const uint8_t *s_blk, const float *tensor_scale,
-                     int64_t rows, int64_t cols, void *out, int out_dtype, void *stream);
+qf8_status dequantize_mxfp4(const uint8_t *q, const uint8_t *sb, int64_t rows, int64_t cols, void *out,
+                            qf8_out_dtype out_dtype, void *stream);
+qf8_status dequantize_nvfp4(const uint8_t *q, const uint8_t *s_blk, const float *tensor_scale, int64_t rows,
+                            int64_t cols, void *out, qf8_out_dtype out_dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -73,7 +73,7 @@ def _load():
         "qf8_delayed_init": (i32, [ctypes.POINTER(_DelayedStruct), vp, vp, vp, i32, i32, i32, i32, vp]),
         "qf8_delayed_init_ex": (i32, [ctypes.POINTER(_DelayedStruct), vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]),
         "qf8_delayed_reset": (i32, [ctypes.POINTER(_DelayedStruct), vp]),
-        "quantize_delayed": (i32, [vp, i32, i64, i64, ctypes.POINTER(_DelayedStruct), vp, vp, vp, vp, vp, sz, vp]),
+        "quantize_delayed": (i32, [vp, i32, i64, i64, i32, ctypes.POINTER(_DelayedStruct), vp, vp, vp, vp, vp, sz, vp]),
         "quantize_block": (i32, [vp, i32, i64, i64, i32, i32, i32, vp, vp, vp, vp, vp]),
         "quantize_block_ex": (i32, [vp, i32, i64, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
         "requantize_1x128_to_128x1": (i32, [vp, vp, i64, i64, i32, i32, i32, vp, vp, vp, vp]),
@@ -252,12 +252,14 @@ def qf8_delayed_reset(state, stream=None):
 
 
 def quantize_delayed(x, state, q=None, scale_used=None, amax_out=None, nonfinite=None, ws=None, stream=None):
-    """One delayed-scaling iteration. Returns q; scale_used / amax_out are filled when given."""
+    """One delayed-scaling iteration in the state's format. Returns q; scale_used / amax_out are
+    filled when given."""
     _dev_tensor(x, "x")
     rows, cols = _rows_cols(x)
     q = _out(q, tuple(x.shape), torch.uint8, x.device, "q")
     ws = workspace(x) if ws is None else _dev_tensor(ws, "ws")
-    _check(_load().quantize_delayed(_ptr(x), _dtype_code(x), rows, cols, ctypes.byref(state.struct), _ptr(q),
+    _check(_load().quantize_delayed(_ptr(x), _dtype_code(x), rows, cols, state.struct.fmt, ctypes.byref(state.struct),
+                                    _ptr(q),
                                     _ptr(scale_used), _ptr(amax_out), _ptr(nonfinite), _ptr(ws),
                                     ws.numel() * ws.element_size(), _stream(stream, x.device)), "quantize_delayed")
     return q

@@ -21,6 +21,8 @@ inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)
 inline bool fmt_ok(int fmt) { return fmt == QF8_E4M3 || fmt == QF8_E5M2; }
 inline bool dtype_ok(int dt) { return dt == QF8_IN_BF16 || dt == QF8_IN_FP32; }
 inline hipStream_t as_stream(void *s) { return (hipStream_t)s; }
+// kernel launchers report an int status; the entry points return it as qf8_status
+inline qf8_status status_of(int v) { return static_cast<qf8_status>(v); }
 
 // rows, cols >= 0 and rows * cols representable
 inline bool dims_ok(int64_t rows, int64_t cols) {
@@ -44,7 +46,7 @@ int check_delayed(const qf8_delayed_state *st) {
 
 extern "C" {
 
-const char *qf8_status_string(int status) {
+const char *qf8_status_string(qf8_status status) {
     switch (status) {
         case QF8_OK: return "QF8_OK";
         case QF8_ERR_NULL: return "QF8_ERR_NULL: a required pointer is NULL";
@@ -58,34 +60,38 @@ const char *qf8_status_string(int status) {
     }
 }
 
-size_t qf8_workspace_bytes(int64_t rows, int64_t cols, int dtype) {
+size_t qf8_workspace_bytes(int64_t rows, int64_t cols, qf8_dtype dtype) {
     (void)rows; (void)cols; (void)dtype;
     return qf8::kWorkspaceBytes;
 }
 
-int qf8_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+qf8_status qf8_workspace_init(void *ws, size_t ws_bytes, void *stream) {
     if (!ws) return QF8_ERR_NULL;
     if (ws_bytes < qf8::kWorkspaceBytes) return QF8_ERR_WORKSPACE;
     if (!aligned(ws, 16)) return QF8_ERR_ALIGN;
-    return qf8::launch_fill_u32((uint32_t *)ws, (int64_t)(qf8::kWorkspaceBytes / 4), 0u, as_stream(stream));
+    return status_of(qf8::launch_fill_u32((uint32_t *)ws, (int64_t)(qf8::kWorkspaceBytes / 4), 0u,
+                                          as_stream(stream)));
 }
 
-int qf8_set_onepass_grid(int grid) {
+qf8_status qf8_set_onepass_grid(int grid) {
     if (grid < 0 || grid > qf8::kBarMaxGroups) return QF8_ERR_SHAPE;
-    return qf8::set_onepass_grid(grid);
+    return status_of(qf8::set_onepass_grid(grid));
 }
 
-int qf8_cast_scaled(const void *x, int dtype, int64_t n, int fmt, const float *scale, uint8_t *q, void *stream) {
+qf8_status qf8_cast_scaled(const void *x, qf8_dtype dtype, int64_t n, qf8_fmt fmt, const float *scale, uint8_t *q,
+                           void *stream) {
     if (!dtype_ok(dtype) || !fmt_ok(fmt)) return QF8_ERR_ENUM;
     if (n < 0) return QF8_ERR_SHAPE;
     if (n == 0) return QF8_OK;
     if (!x || !scale || !q) return QF8_ERR_NULL;
     if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4)) return QF8_ERR_ALIGN;
-    return qf8::launch_cast_scaled(x, dtype, n, fmt, scale, q, qf8::stream_grid(n, dtype), as_stream(stream));
+    return status_of(qf8::launch_cast_scaled(x, dtype, n, fmt, scale, q, qf8::stream_grid(n, dtype),
+                                             as_stream(stream)));
 }
 
-int quantize_per_tensor(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, uint8_t *q, float *amax,
-                        float *scale, int32_t *nonfinite, void *ws, size_t ws_bytes, void *stream) {
+qf8_status quantize_per_tensor(const void *x, qf8_dtype dtype, int64_t rows, int64_t cols, qf8_fmt fmt, uint8_t *q,
+                               float *amax, float *scale, int32_t *nonfinite, void *ws, size_t ws_bytes,
+                               void *stream) {
     if (!dtype_ok(dtype) || !fmt_ok(fmt)) return QF8_ERR_ENUM;
     if (!dims_ok(rows, cols)) return QF8_ERR_SHAPE;
     const int64_t n = rows * cols;
@@ -97,17 +103,18 @@ int quantize_per_tensor(const void *x, int dtype, int64_t rows, int64_t cols, in
     hipStream_t s = as_stream(stream);
     const int g1 = qf8::onepass_grid(n, dtype);
     if (g1 > 0)
-        return qf8::launch_per_tensor_onepass(x, dtype, n, fmt, q, (uint32_t *)ws, amax, scale, nonfinite, nullptr, g1, s);
+        return status_of(qf8::launch_per_tensor_onepass(x, dtype, n, fmt, q, (uint32_t *)ws, amax, scale, nonfinite,
+                                                        nullptr, g1, s));
     uint32_t *partials = (uint32_t *)ws + qf8::kPartialsOffsetWords;
     const int agrid = qf8::amax_grid(n, dtype);
     int st = qf8::launch_amax_partials(x, dtype, n, partials, agrid, s);
-    if (st != QF8_OK) return st;
-    return qf8::launch_cast_current(x, dtype, n, fmt, q, partials, agrid, amax, scale, nonfinite,
-                                    qf8::stream_grid(n, dtype), s);
+    if (st != QF8_OK) return status_of(st);
+    return status_of(qf8::launch_cast_current(x, dtype, n, fmt, q, partials, agrid, amax, scale, nonfinite,
+                                              qf8::stream_grid(n, dtype), s));
 }
 
-int quantize_per_tensor_noalloc(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, uint8_t *q,
-                                float *amax, float *scale, int32_t *nonfinite, void *stream) {
+qf8_status quantize_per_tensor_noalloc(const void *x, qf8_dtype dtype, int64_t rows, int64_t cols, qf8_fmt fmt,
+                                       uint8_t *q, float *amax, float *scale, int32_t *nonfinite, void *stream) {
     // the argument checks of quantize_per_tensor come first, so a bad call touches no device state
     if (!dtype_ok(dtype) || !fmt_ok(fmt)) return QF8_ERR_ENUM;
     if (!dims_ok(rows, cols)) return QF8_ERR_SHAPE;
@@ -119,13 +126,14 @@ int quantize_per_tensor_noalloc(const void *x, int dtype, int64_t rows, int64_t 
     uint32_t *ws = nullptr;
     size_t ws_bytes = 0;
     const int st = qf8::scratch_workspace(&ws, &ws_bytes);
-    if (st != QF8_OK) return st;
+    if (st != QF8_OK) return status_of(st);
     if (ws_bytes < qf8::kWorkspaceBytes) return QF8_ERR_WORKSPACE;   // fixed size: every shape fits
-    return quantize_per_tensor(x, dtype, rows, cols, fmt, q, amax, scale, nonfinite, ws, ws_bytes, stream);
+    return status_of(quantize_per_tensor(x, dtype, rows, cols, fmt, q, amax, scale, nonfinite, ws, ws_bytes, stream));
 }
 
-int qf8_delayed_init_ex(qf8_delayed_state *st, float *history, int32_t *meta, float *scale, int hist_len,
-                        int interval, int n_guard, int fmt, int estimator, int flags, void *stream) {
+qf8_status qf8_delayed_init_ex(qf8_delayed_state *st, float *history, int32_t *meta, float *scale, int hist_len,
+                               int interval, int n_guard, qf8_fmt fmt, qf8_estimator estimator, int flags,
+                               void *stream) {
     if (!st || !history || !meta || !scale) return QF8_ERR_NULL;
     if (!fmt_ok(fmt) || estimator < QF8_EST_MAX || estimator > QF8_EST_MEAN || (flags & ~QF8_DELAYED_SPLIT_AMAX))
         return QF8_ERR_ENUM;
@@ -144,32 +152,34 @@ int qf8_delayed_init_ex(qf8_delayed_state *st, float *history, int32_t *meta, fl
     st->estimator = estimator;
     st->flags = flags;
     st->reserved = 0;
-    return qf8_delayed_reset(st, stream);
+    return status_of(qf8_delayed_reset(st, stream));
 }
 
-int qf8_delayed_init(qf8_delayed_state *st, float *history, int32_t *meta, float *scale, int hist_len, int interval,
-                     int n_guard, int fmt, void *stream) {
-    return qf8_delayed_init_ex(st, history, meta, scale, hist_len, interval, n_guard, fmt, QF8_EST_MAX, 0, stream);
+qf8_status qf8_delayed_init(qf8_delayed_state *st, float *history, int32_t *meta, float *scale, int hist_len,
+                            int interval, int n_guard, qf8_fmt fmt, void *stream) {
+    return status_of(qf8_delayed_init_ex(st, history, meta, scale, hist_len, interval, n_guard, fmt, QF8_EST_MAX, 0,
+                                         stream));
 }
 
-int qf8_delayed_reset(qf8_delayed_state *st, void *stream) {
+qf8_status qf8_delayed_reset(qf8_delayed_state *st, void *stream) {
     int c = check_delayed(st);
-    if (c != QF8_OK) return c;
+    if (c != QF8_OK) return status_of(c);
     hipStream_t s = as_stream(stream);
     // cleared with a fill kernel rather than a memset, so a captured graph replays it correctly
     int r = qf8::launch_fill_u32((uint32_t *)st->history, st->hist_len, 0u, s);
     if (r == QF8_OK) r = qf8::launch_fill_u32((uint32_t *)st->meta, 4, 0u, s);
     if (r == QF8_OK) r = qf8::launch_fill_u32((uint32_t *)st->scale, 1, 0x3F800000u /* 1.0f */, s);
     if (r == QF8_OK) st->step = 0;
-    return r;
+    return status_of(r);
 }
 
-int quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, qf8_delayed_state *st, uint8_t *q,
-                     float *scale_used, float *amax_out, int32_t *nonfinite, void *ws, size_t ws_bytes,
-                     void *stream) {
+qf8_status quantize_delayed(const void *x, qf8_dtype dtype, int64_t rows, int64_t cols, qf8_fmt fmt,
+                            qf8_delayed_state *st, uint8_t *q, float *scale_used, float *amax_out, int32_t *nonfinite,
+                            void *ws, size_t ws_bytes, void *stream) {
     int c = check_delayed(st);
-    if (c != QF8_OK) return c;
-    if (!dtype_ok(dtype)) return QF8_ERR_ENUM;
+    if (c != QF8_OK) return status_of(c);
+    if (!dtype_ok(dtype) || !fmt_ok(fmt)) return QF8_ERR_ENUM;
+    if (fmt != st->fmt) return QF8_ERR_STATE;     // the state was initialised for another format
     if (!dims_ok(rows, cols)) return QF8_ERR_SHAPE;
     const int64_t n = rows * cols;
     if (n > 0 && (!x || !q)) return QF8_ERR_NULL;
@@ -218,7 +228,7 @@ int quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, qf8_d
             // only be reported, and the state does not change)
             r = qf8::launch_cast_scaled(x, dtype, n, st->fmt, st->scale, q, grid, s);
             if (r == QF8_OK) st->step++;
-            return r;
+            return status_of(r);
         }
         r = qf8::launch_cast_fused(x, dtype, n, st->fmt, st->scale, q, scale_used, slots, split, lo, hi, grid, s);
         if (r == QF8_OK)
@@ -227,11 +237,12 @@ int quantize_delayed(const void *x, int dtype, int64_t rows, int64_t cols, qf8_d
                                              s);
     }
     if (r == QF8_OK) st->step++;
-    return r;
+    return status_of(r);
 }
 
-int quantize_block_ex(const void *x, int dtype, int64_t rows, int64_t cols, int block_rows, int block_cols, int fmt,
-                      int flags, uint8_t *q, float *scales, float *amax, int32_t *nonfinite, void *stream) {
+qf8_status quantize_block_ex(const void *x, qf8_dtype dtype, int64_t rows, int64_t cols, int block_rows,
+                             int block_cols, qf8_fmt fmt, int flags, uint8_t *q, float *scales, float *amax,
+                             int32_t *nonfinite, void *stream) {
     if (!dtype_ok(dtype) || !fmt_ok(fmt)) return QF8_ERR_ENUM;
     if (flags & ~QF8_FLAG_POW2_SCALES) return QF8_ERR_ENUM;
     if (!dims_ok(rows, cols)) return QF8_ERR_SHAPE;
@@ -245,17 +256,19 @@ int quantize_block_ex(const void *x, int dtype, int64_t rows, int64_t cols, int 
     if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scales, 4) || (amax && !aligned(amax, 4)) ||
         (nonfinite && !aligned(nonfinite, 4)))
         return QF8_ERR_ALIGN;
-    return qf8::launch_block(x, dtype, rows, cols, block_rows, fmt, flags & QF8_FLAG_POW2_SCALES, q, scales, amax,
-                             nonfinite, as_stream(stream));
+    return status_of(qf8::launch_block(x, dtype, rows, cols, block_rows, fmt, flags & QF8_FLAG_POW2_SCALES, q, scales,
+                                       amax, nonfinite, as_stream(stream)));
 }
 
-int quantize_block(const void *x, int dtype, int64_t rows, int64_t cols, int block_rows, int block_cols, int fmt,
-                   uint8_t *q, float *scales, float *amax, int32_t *nonfinite, void *stream) {
-    return quantize_block_ex(x, dtype, rows, cols, block_rows, block_cols, fmt, 0, q, scales, amax, nonfinite, stream);
+qf8_status quantize_block(const void *x, qf8_dtype dtype, int64_t rows, int64_t cols, int block_rows, int block_cols,
+                          qf8_fmt fmt, uint8_t *q, float *scales, float *amax, int32_t *nonfinite, void *stream) {
+    return status_of(quantize_block_ex(x, dtype, rows, cols, block_rows, block_cols, fmt, 0, q, scales, amax,
+                                       nonfinite, stream));
 }
 
-int requantize_1x128_to_128x1(const uint8_t *q, const float *scales, int64_t rows, int64_t cols, int fmt_in,
-                              int fmt_out, int flags, uint8_t *qT, float *scalesT, int32_t *nonfinite, void *stream) {
+qf8_status requantize_1x128_to_128x1(const uint8_t *q, const float *scales, int64_t rows, int64_t cols,
+                                     qf8_fmt fmt_in, qf8_fmt fmt_out, int flags, uint8_t *qT, float *scalesT,
+                                     int32_t *nonfinite, void *stream) {
     if (!fmt_ok(fmt_in) || !fmt_ok(fmt_out)) return QF8_ERR_ENUM;
     if (flags & ~QF8_FLAG_POW2_SCALES) return QF8_ERR_ENUM;
     if (!dims_ok(rows, cols) || rows % 16 != 0 || cols % 16 != 0) return QF8_ERR_SHAPE;
@@ -266,12 +279,13 @@ int requantize_1x128_to_128x1(const uint8_t *q, const float *scales, int64_t row
     if (!aligned(q, 16) || !aligned(qT, 16) || !aligned(scales, 4) || !aligned(scalesT, 4) ||
         (nonfinite && !aligned(nonfinite, 4)))
         return QF8_ERR_ALIGN;
-    return qf8::launch_requant_t(q, scales, rows, cols, fmt_in, fmt_out, flags & QF8_FLAG_POW2_SCALES, qT, scalesT,
-                                 nonfinite, as_stream(stream));
+    return status_of(qf8::launch_requant_t(q, scales, rows, cols, fmt_in, fmt_out, flags & QF8_FLAG_POW2_SCALES, qT,
+                                           scalesT, nonfinite, as_stream(stream)));
 }
 
-int quantize_mx_dual(const void *x, int dtype, int64_t rows, int64_t cols, int fmt, int rnd, uint8_t *q_row,
-                     uint8_t *s_row, uint8_t *q_colT, uint8_t *s_colT, int32_t *nonfinite, void *stream) {
+qf8_status quantize_mx_dual(const void *x, qf8_dtype dtype, int64_t rows, int64_t cols, qf8_fmt fmt, qf8_mx_round rnd,
+                            uint8_t *q_row, uint8_t *s_row, uint8_t *q_colT, uint8_t *s_colT, int32_t *nonfinite,
+                            void *stream) {
     if (!dtype_ok(dtype) || !fmt_ok(fmt) || (rnd != QF8_MX_ROUND_DOWN && rnd != QF8_MX_ROUND_UP)) return QF8_ERR_ENUM;
     if (!dims_ok(rows, cols) || rows > kMaxMxDim || cols > kMaxMxDim) return QF8_ERR_SHAPE;
     if (!q_row && !q_colT) return QF8_ERR_NULL;
@@ -284,11 +298,13 @@ int quantize_mx_dual(const void *x, int dtype, int64_t rows, int64_t cols, int f
     if (!aligned(x, 16) || (q_row && !aligned(q_row, 16)) || (q_colT && !aligned(q_colT, 16)) ||
         (nonfinite && !aligned(nonfinite, 4)))
         return QF8_ERR_ALIGN;
-    return qf8::launch_mx(x, dtype, rows, cols, fmt, rnd, q_row, s_row, q_colT, s_colT, nonfinite, as_stream(stream));
+    return status_of(qf8::launch_mx(x, dtype, rows, cols, fmt, rnd, q_row, s_row, q_colT, s_colT, nonfinite,
+                                    as_stream(stream)));
 }
 
-int quantize_mxfp4_dual(const void *x, int dtype, int64_t rows, int64_t cols, int rnd, uint8_t *q_row, uint8_t *s_row,
-                        uint8_t *q_colT, uint8_t *s_colT, int32_t *nonfinite, void *stream) {
+qf8_status quantize_mxfp4_dual(const void *x, qf8_dtype dtype, int64_t rows, int64_t cols, qf8_mx_round rnd,
+                               uint8_t *q_row, uint8_t *s_row, uint8_t *q_colT, uint8_t *s_colT, int32_t *nonfinite,
+                               void *stream) {
     if (!dtype_ok(dtype) || (rnd != QF8_MX_ROUND_DOWN && rnd != QF8_MX_ROUND_UP)) return QF8_ERR_ENUM;
     if (!dims_ok(rows, cols) || rows > kMaxMxDim || cols > kMaxMxDim) return QF8_ERR_SHAPE;
     if (!q_row && !q_colT) return QF8_ERR_NULL;
@@ -301,12 +317,13 @@ int quantize_mxfp4_dual(const void *x, int dtype, int64_t rows, int64_t cols, in
     if (!aligned(x, 16) || (q_row && !aligned(q_row, 16)) || (q_colT && !aligned(q_colT, 16)) ||
         (nonfinite && !aligned(nonfinite, 4)))
         return QF8_ERR_ALIGN;
-    return qf8::launch_mxfp4(x, dtype, rows, cols, rnd, q_row, s_row, q_colT, s_colT, nonfinite, as_stream(stream));
+    return status_of(qf8::launch_mxfp4(x, dtype, rows, cols, rnd, q_row, s_row, q_colT, s_colT, nonfinite,
+                                       as_stream(stream)));
 }
 
-int quantize_nvfp4(const void *x, int dtype, int64_t rows, int64_t cols, const float *amax_in, uint8_t *q,
-                   uint8_t *s_blk, float *tensor_scale, float *amax_out, int32_t *nonfinite, void *ws, size_t ws_bytes,
-                   void *stream) {
+qf8_status quantize_nvfp4(const void *x, qf8_dtype dtype, int64_t rows, int64_t cols, const float *amax_in,
+                          uint8_t *q, uint8_t *s_blk, float *tensor_scale, float *amax_out, int32_t *nonfinite,
+                          void *ws, size_t ws_bytes, void *stream) {
     if (!dtype_ok(dtype)) return QF8_ERR_ENUM;
     if (!dims_ok(rows, cols) || cols % 16 != 0) return QF8_ERR_SHAPE;
     const int64_t n = rows * cols;
@@ -322,36 +339,37 @@ int quantize_nvfp4(const void *x, int dtype, int64_t rows, int64_t cols, const f
         // large tensors: amax and cast in one read (the single-pass kernel of per-tensor scaling)
         const int g1 = qf8::onepass_grid(n, dtype);
         if (g1 > 0)
-            return qf8::launch_nvfp4_onepass(x, dtype, n, q, s_blk, (uint32_t *)ws, tensor_scale, amax_out, nonfinite,
-                                             g1, s);
+            return status_of(qf8::launch_nvfp4_onepass(x, dtype, n, q, s_blk, (uint32_t *)ws, tensor_scale, amax_out,
+                                                       nonfinite, g1, s));
         // otherwise the read-only amax pass first
         nparts = qf8::amax_grid(n, dtype);
         const int r = qf8::launch_amax_partials(x, dtype, n, partials, nparts, s);
-        if (r != QF8_OK) return r;
+        if (r != QF8_OK) return status_of(r);
     }
-    return qf8::launch_nvfp4(x, dtype, n, partials, nparts, amax_in, q, s_blk, tensor_scale, amax_out, nonfinite, s);
+    return status_of(qf8::launch_nvfp4(x, dtype, n, partials, nparts, amax_in, q, s_blk, tensor_scale, amax_out,
+                                       nonfinite, s));
 }
 
-int dequantize_mxfp4(const uint8_t *q, const uint8_t *sb, int64_t rows, int64_t cols, void *out, int out_dtype,
-                     void *stream) {
+qf8_status dequantize_mxfp4(const uint8_t *q, const uint8_t *sb, int64_t rows, int64_t cols, void *out,
+                            qf8_out_dtype out_dtype, void *stream) {
     if (out_dtype != QF8_OUT_BF16 && out_dtype != QF8_OUT_FP32) return QF8_ERR_ENUM;
     if (!dims_ok(rows, cols) || cols % 32 != 0 || rows * cols >= ((int64_t)1 << 36)) return QF8_ERR_SHAPE;
     const int64_t n = rows * cols;
     if (n == 0) return QF8_OK;
     if (!q || !sb || !out) return QF8_ERR_NULL;
     if (!aligned(q, 16) || !aligned(out, 16)) return QF8_ERR_ALIGN;
-    return qf8::launch_dequant_fp4(0, q, sb, nullptr, n, out, out_dtype, as_stream(stream));
+    return status_of(qf8::launch_dequant_fp4(0, q, sb, nullptr, n, out, out_dtype, as_stream(stream)));
 }
 
-int dequantize_nvfp4(const uint8_t *q, const uint8_t *s_blk, const float *tensor_scale, int64_t rows, int64_t cols,
-                     void *out, int out_dtype, void *stream) {
+qf8_status dequantize_nvfp4(const uint8_t *q, const uint8_t *s_blk, const float *tensor_scale, int64_t rows,
+                            int64_t cols, void *out, qf8_out_dtype out_dtype, void *stream) {
     if (out_dtype != QF8_OUT_BF16 && out_dtype != QF8_OUT_FP32) return QF8_ERR_ENUM;
     if (!dims_ok(rows, cols) || cols % 16 != 0 || rows * cols >= ((int64_t)1 << 36)) return QF8_ERR_SHAPE;
     const int64_t n = rows * cols;
     if (n == 0) return QF8_OK;
     if (!q || !s_blk || !tensor_scale || !out) return QF8_ERR_NULL;
     if (!aligned(q, 16) || !aligned(out, 16) || !aligned(tensor_scale, 4)) return QF8_ERR_ALIGN;
-    return qf8::launch_dequant_fp4(1, q, s_blk, tensor_scale, n, out, out_dtype, as_stream(stream));
+    return status_of(qf8::launch_dequant_fp4(1, q, s_blk, tensor_scale, n, out, out_dtype, as_stream(stream)));
 }
 
 }  // extern "C"
@@ -380,40 +398,42 @@ int check_dequant(const uint8_t *q, int64_t rows, int64_t cols, int fmt, void *o
 
 extern "C" {
 
-int dequantize_scaled(const uint8_t *q, int64_t n, int fmt, const float *scale, void *out, int out_dtype,
-                      const void *x, int x_dtype, qf8_error_stats *stats, void *ws, size_t ws_bytes, void *stream) {
+qf8_status dequantize_scaled(const uint8_t *q, int64_t n, qf8_fmt fmt, const float *scale, void *out,
+                             qf8_out_dtype out_dtype, const void *x, qf8_dtype x_dtype, qf8_error_stats *stats,
+                             void *ws, size_t ws_bytes, void *stream) {
     int c = check_dequant(q, 1, n, fmt, out, out_dtype, x, x_dtype, stats, ws, ws_bytes);
-    if (c != QF8_OK) return c;
+    if (c != QF8_OK) return status_of(c);
     if (!scale) return QF8_ERR_NULL;
     if (!aligned(scale, 4)) return QF8_ERR_ALIGN;
     if (n == 0 && !stats) return QF8_OK;
-    return qf8::launch_dequant(0, fmt, q, 1, n, 1, scale, nullptr, out, out_dtype, x, x_dtype, stats, ws,
-                               as_stream(stream));
+    return status_of(qf8::launch_dequant(0, fmt, q, 1, n, 1, scale, nullptr, out, out_dtype, x, x_dtype, stats, ws,
+                                         as_stream(stream)));
 }
 
-int dequantize_block(const uint8_t *q, int64_t rows, int64_t cols, int block_rows, int block_cols, int fmt,
-                     const float *scales, void *out, int out_dtype, const void *x, int x_dtype,
-                     qf8_error_stats *stats, void *ws, size_t ws_bytes, void *stream) {
+qf8_status dequantize_block(const uint8_t *q, int64_t rows, int64_t cols, int block_rows, int block_cols, qf8_fmt fmt,
+                            const float *scales, void *out, qf8_out_dtype out_dtype, const void *x, qf8_dtype x_dtype,
+                            qf8_error_stats *stats, void *ws, size_t ws_bytes, void *stream) {
     int c = check_dequant(q, rows, cols, fmt, out, out_dtype, x, x_dtype, stats, ws, ws_bytes);
-    if (c != QF8_OK) return c;
+    if (c != QF8_OK) return status_of(c);
     if (!((block_rows == 1 || block_rows == 128) && block_cols == 128)) return QF8_ERR_SHAPE;
     if (cols % 4 != 0) return QF8_ERR_SHAPE;
     if (rows * cols > 0 && !scales) return QF8_ERR_NULL;
     if (scales && !aligned(scales, 4)) return QF8_ERR_ALIGN;
     if (rows * cols == 0 && !stats) return QF8_OK;
-    return qf8::launch_dequant(1, fmt, q, rows, cols, block_rows, scales, nullptr, out, out_dtype, x, x_dtype, stats,
-                               ws, as_stream(stream));
+    return status_of(qf8::launch_dequant(1, fmt, q, rows, cols, block_rows, scales, nullptr, out, out_dtype, x,
+                                         x_dtype, stats, ws, as_stream(stream)));
 }
 
-int dequantize_mx(const uint8_t *q, const uint8_t *s, int64_t rows, int64_t cols, int fmt, void *out, int out_dtype,
-                  const void *x, int x_dtype, qf8_error_stats *stats, void *ws, size_t ws_bytes, void *stream) {
+qf8_status dequantize_mx(const uint8_t *q, const uint8_t *s, int64_t rows, int64_t cols, qf8_fmt fmt, void *out,
+                         qf8_out_dtype out_dtype, const void *x, qf8_dtype x_dtype, qf8_error_stats *stats, void *ws,
+                         size_t ws_bytes, void *stream) {
     int c = check_dequant(q, rows, cols, fmt, out, out_dtype, x, x_dtype, stats, ws, ws_bytes);
-    if (c != QF8_OK) return c;
+    if (c != QF8_OK) return status_of(c);
     if (cols % 32 != 0) return QF8_ERR_SHAPE;
     if (rows * cols > 0 && !s) return QF8_ERR_NULL;
     if (rows * cols == 0 && !stats) return QF8_OK;
-    return qf8::launch_dequant(2, fmt, q, rows, cols, 1, nullptr, s, out, out_dtype, x, x_dtype, stats, ws,
-                               as_stream(stream));
+    return status_of(qf8::launch_dequant(2, fmt, q, rows, cols, 1, nullptr, s, out, out_dtype, x, x_dtype, stats, ws,
+                                         as_stream(stream)));
 }
 
 }  // extern "C"

@@ -20,7 +20,7 @@ void qf8o_dequant_mx(const uint8_t *q, const uint8_t *sb, int64_t rows, int64_t 
 }
 
 #define HIP_OK(x) do { hipError_t e_ = (x); if (e_ != hipSuccess) { std::printf("HIP error %s at line %d\n", hipGetErrorString(e_), __LINE__); return 1; } } while (0)
-#define QF8_OK_(x) do { int s_ = (x); if (s_ != QF8_OK) { std::printf("%s at line %d\n", qf8_status_string(s_), __LINE__); return 1; } } while (0)
+#define QF8_OK_(x) do { qf8_status s_ = (x); if (s_ != QF8_OK) { std::printf("%s at line %d\n", qf8_status_string(s_), __LINE__); return 1; } } while (0)
 
 static int same(const void *a, const void *b, size_t n, const char *what) {
     if (std::memcmp(a, b, n) == 0) return 0;

@@ -119,7 +119,7 @@ def test_delayed_state_errors():
     st = qf8._DelayedStruct()
     L = lib()
     ref = ctypes.byref(st)
-    assert L.quantize_delayed(FAKE, 0, 4, 4, ref, FAKE, None, None, None, FAKE, 1 << 20, None) == STATE  # not initialised
+    assert L.quantize_delayed(FAKE, 0, 4, 4, 0, ref, FAKE, None, None, None, FAKE, 1 << 20, None) == STATE  # not initialised
     assert L.qf8_delayed_init(ref, FAKE, FAKE, FAKE, 0, 1, 0, 0, None) == STATE       # hist_len 0
     assert L.qf8_delayed_init(ref, FAKE, FAKE, FAKE, 16, 0, 0, 0, None) == STATE      # interval 0
     assert L.qf8_delayed_init(ref, FAKE, FAKE, FAKE, 16, 1, 65, 0, None) == STATE     # n_guard too large
@@ -134,10 +134,14 @@ def test_delayed_state_errors():
     st.history = st.meta = st.scale = FAKE
     st.hist_len, st.interval, st.n_guard, st.fmt, st.step = 16, 1, 0, 0, 0
     st.magic, st.estimator = 0x51463844, 3
-    assert L.quantize_delayed(FAKE, 0, 4, 4, ref, FAKE, None, None, None, FAKE, 1 << 20, None) == STATE
+    assert L.quantize_delayed(FAKE, 0, 4, 4, 0, ref, FAKE, None, None, None, FAKE, 1 << 20, None) == STATE
     assert L.qf8_delayed_reset(ref, None) == STATE
     st.estimator, st.flags = 0, 4
-    assert L.quantize_delayed(FAKE, 0, 4, 4, ref, FAKE, None, None, None, FAKE, 1 << 20, None) == STATE
+    assert L.quantize_delayed(FAKE, 0, 4, 4, 0, ref, FAKE, None, None, None, FAKE, 1 << 20, None) == STATE
+    # the call's format must be the state's: a mismatch is refused before any launch
+    st.flags = 0
+    assert L.quantize_delayed(FAKE, 0, 4, 4, 1, ref, FAKE, None, None, None, FAKE, 1 << 20, None) == STATE
+    assert L.quantize_delayed(FAKE, 0, 4, 4, 7, ref, FAKE, None, None, None, FAKE, 1 << 20, None) == ENUM
 
 
 def test_no_cpu_path():
