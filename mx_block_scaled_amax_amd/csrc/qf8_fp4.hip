@@ -394,8 +394,8 @@ void launch_mxfp4_dirs(const void *x, int rows, int cols, uint8_t *q_row, uint8_
 // takes the tensor amax (the caller's value, or the fold of the amax pass's partials), S_t and the
 // table of element factors; a thread then loads its 32 (BF16) or 64 (FP32) bytes, takes the block
 // amax and the E4M3 block scale, converts the two bracketing estimates of every element and
-// writes 8 bytes of codes and the scale byte. A wave in which some block's estimates disagree
-// recomputes those blocks' codes exactly.
+// writes 8 bytes of codes and the scale byte. The elements whose two estimates disagree (those
+// within about 2^-20 of an E2M1 midpoint) are recomputed exactly, each by its own lane.
 
 
 template <bool BF16>
@@ -419,6 +419,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_kernel(const void *__restrict_
     constexpr int NV = BF16 ? 2 : 4;             // 16-byte loads per block
     const uint4 *xv = (const uint4 *)x;
     __shared__ __attribute__((aligned(16))) uint8_t sbuf[kThreads];
+    __shared__ __attribute__((aligned(16))) float fbuf[kThreads * 16];   // a lane's elements, for the exact path
     // The workgroup's 256 consecutive blocks per pass have 256 consecutive scale bytes: gathered
     // in LDS, they leave as 16 non-temporal 16-byte stores (single cached bytes from every thread
     // cost several times more per byte on this path); a ragged last pass or an s_blk that is not
@@ -470,14 +471,24 @@ __global__ __launch_bounds__(kThreads) void nvfp4_kernel(const void *__restrict_
             hi = fp4_f32<3>(hi, g[6] * r.y, g[7] * r.y, 1.0f);
             o[w] = lo; h[w] = hi;
         }
-        const bool miss = (o[0] != h[0]) | (o[1] != h[1]);
-        if (__builtin_amdgcn_ballot_w64(miss) != 0u) {            // rare: wave-uniform branch
-            if (miss) {
-                const float dec = __builtin_amdgcn_cvt_f32_fp8(e, 0);
-                o[0] = o[1] = 0u;
+        // elements whose two estimates disagree (nibbles of d) are recomputed exactly, one per
+        // loop trip and lane; the lane's values go through LDS so that the trip reads element k
+        // by index
+        uint64_t d = (uint64_t)(o[0] ^ h[0]) | ((uint64_t)(o[1] ^ h[1]) << 32);
+        if (__builtin_amdgcn_ballot_w64(d != 0u) != 0u) {          // wave-uniform branch
+            float4 *fl = (float4 *)(fbuf + threadIdx.x * 16);
 #pragma unroll
-                for (int k = 0; k < 16; ++k) o[k >> 3] |= nv_elem_exact(f[k], st, dec) << (4 * (k & 7));
+            for (int k = 0; k < 4; ++k) fl[k] = make_float4(f[4 * k], f[4 * k + 1], f[4 * k + 2], f[4 * k + 3]);
+            const float dec = __builtin_amdgcn_cvt_f32_fp8(e, 0);
+            uint64_t oc = (uint64_t)o[0] | ((uint64_t)o[1] << 32);
+            while (d != 0u) {
+                const int sh = __builtin_ctzll(d) & ~3;             // nibble of the lowest set bit
+                d &= ~(0xFull << sh);
+                const uint64_t c = nv_elem_exact(fbuf[threadIdx.x * 16 + (sh >> 2)], st, dec);
+                oc = (oc & ~(0xFull << sh)) | (c << sh);
             }
+            o[0] = (uint32_t)oc;
+            o[1] = (uint32_t)(oc >> 32);
         }
         const uint32_t o0 = o[0], o1 = o[1];
         if (valid) st_stream((uint2 *)q + blk, make_uint2(o0, o1));

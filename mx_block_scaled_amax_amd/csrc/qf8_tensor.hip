@@ -402,7 +402,7 @@ constexpr uint32_t op_out_bytes() { return OP == kOpFp8 ? (BF16 ? 8u : 4u) : (BF
 
 // NVFP4 codes of one input vector from two estimates of x * S_t / decode(e_b), one below and one
 // above the exact quotient (nv_factor_table); returns them in `lo`, and whether they disagree
-// somewhere (the vector is then recomputed exactly by nv_fix_vec after the caller's stores).
+// somewhere (the vector is then recomputed exactly by nv_fix_vecs4 after the caller's stores).
 template <bool BF16>
 __device__ __forceinline__ bool nv_vec_codes(uint4 v, float2 r, uint32_t &lo) {
     uint32_t l = 0u, h = 0u;
@@ -427,7 +427,7 @@ __device__ __forceinline__ bool nv_vec_codes(uint4 v, float2 r, uint32_t &lo) {
 
 // A block of 16 is 2 (BF16) or 4 (FP32) vectors held by adjacent lanes, whose amax meets by DPP;
 // each lane writes its 4 or 2 code bytes and the block's first lane the E4M3 scale byte. All lanes
-// must be active. Returns whether the vector needs nv_fix_vec.
+// must be active. Returns whether the vector needs nv_fix_vecs4.
 template <bool BF16>
 __device__ __forceinline__ bool nv_vec_store(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t wsb, uint32_t vrel,
                                              uint4 v, float st, const float2 *tab) {
@@ -447,20 +447,23 @@ __device__ __forceinline__ bool nv_vec_store(__amdgpu_buffer_rsrc_t wq, __amdgpu
     return miss;
 }
 
-// The exact codes of vector vabs (its index in x; vrel is its index in wq), by one lane alone: the
-// block's vectors are read again from memory for its amax, and every element takes nv_elem_exact.
-// The lane's earlier store of the same bytes was issued first, so this one is the one that stays.
+// The exact codes of one vector, by one lane alone, from its block's vectors b0, b1 (BF16) or
+// b0..b3 (FP32), read again from memory by the caller, and its place sel in the block: the block
+// amax, e_b, then every
+// element through nv_elem_exact. The lane's earlier store of the same bytes was issued first, so
+// this one is the one that stays.
 template <bool BF16>
-__device__ __forceinline__ void nv_fix_vec(const uint4 *xv, __amdgpu_buffer_rsrc_t wq, uint32_t vrel, int64_t vabs,
-                                        float st) {
-    constexpr int64_t kVpb = BF16 ? 2 : 4;
-    const int64_t b0 = vabs - vabs % kVpb;
-    uint32_t a = 0u;
-    for (int64_t i = 0; i < kVpb; ++i) a = vec_absmax<BF16>(a, xv[b0 + i]);
+__device__ __forceinline__ void nv_fix_one(__amdgpu_buffer_rsrc_t wq, uint32_t vrel, uint4 b0, uint4 b1, uint4 b2,
+                                           uint4 b3, int sel, bool ok, float st) {
+    uint32_t a = vec_absmax<BF16>(vec_absmax<BF16>(0u, b0), b1);
+    if constexpr (!BF16) a = vec_absmax<BF16>(vec_absmax<BF16>(a, b2), b3);
     const uint32_t e = nv_block_code(acc_to_f32bits<BF16>(a), st);
     const float dec = __builtin_amdgcn_cvt_f32_fp8(e, 0);
-    const uint4 v = xv[vabs];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    // the vector's own values, chosen by value (b0..b3 stay in registers)
+    const uint32_t w[4] = {sel == 0 ? b0.x : sel == 1 ? b1.x : sel == 2 ? b2.x : b3.x,
+                           sel == 0 ? b0.y : sel == 1 ? b1.y : sel == 2 ? b2.y : b3.y,
+                           sel == 0 ? b0.z : sel == 1 ? b1.z : sel == 2 ? b2.z : b3.z,
+                           sel == 0 ? b0.w : sel == 1 ? b1.w : sel == 2 ? b2.w : b3.w};
     uint32_t o = 0u;
     if (dec == dec && dec != 0.0f) {               // else signed zeros (or a non-finite block)
         if constexpr (BF16) {
@@ -474,8 +477,28 @@ __device__ __forceinline__ void nv_fix_vec(const uint4 *xv, __amdgpu_buffer_rsrc
             for (int k = 0; k < 4; ++k) o |= nv_elem_exact(__uint_as_float(w[k]), st, dec) << (4 * k);
         }
     }
-    if constexpr (BF16) buf_store4<kNonTemporal>(wq, vrel * 4u, 0u, o);
-    else buf_store2(wq, vrel * 2u, 0u, o);
+    if (ok) {
+        if constexpr (BF16) buf_store4<kNonTemporal>(wq, vrel * 4u, 0u, o);
+        else buf_store2(wq, vrel * 2u, 0u, o);
+    }
+}
+
+// Up to four vectors (indices vrel[j] in wq, vabs[j] in x; ok[j] false for unused places) recomputed
+// exactly: every block is read again before any is used, so the loads are in flight together.
+template <bool BF16>
+__device__ __forceinline__ void nv_fix_vecs4(const uint4 *xv, __amdgpu_buffer_rsrc_t wq, const uint32_t (&vrel)[4],
+                                             const int64_t (&vabs)[4], const bool (&ok)[4], float st) {
+    constexpr int kVpb = BF16 ? 2 : 4;
+    uint4 v[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t s = ok[j] ? vabs[j] - vabs[j] % kVpb : 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[j][i] = (ok[j] && i < kVpb) ? xv[s + i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        nv_fix_one<BF16>(wq, vrel[j], v[j][0], v[j][1], v[j][2], v[j][3], (int)(vabs[j] % kVpb), ok[j], st);
 }
 
 template <int OP, bool BF16, int FMT>
@@ -521,10 +544,18 @@ __device__ __forceinline__ uint32_t stream_slabs8(const uint4 *x, int64_t nvec, 
             miss |= (uint32_t)op_vec_store<OP, BF16, FMT>(w, wsb, i * (step / 16u) + threadIdx.x, v[i], s, tab) << i;
         if constexpr (OP == kOpNvfp4) {
             if (__builtin_amdgcn_ballot_w64(miss != 0u) != 0u) {        // rare: wave-uniform branch
-                while (miss != 0u) {                // the lane's set bits, lowest first
-                    const uint32_t vr = (uint32_t)__builtin_ctz(miss) * (step / 16u) + threadIdx.x;
-                    miss &= miss - 1u;
-                    nv_fix_vec<BF16>(x, w, vr, first + vr, s);
+                while (miss != 0u) {                // four of the lane's set bits per trip
+                    uint32_t vr[4];
+                    int64_t va[4];
+                    bool ok[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        ok[j] = miss != 0u;
+                        vr[j] = ok[j] ? (uint32_t)__builtin_ctz(miss) * (step / 16u) + threadIdx.x : 0u;
+                        va[j] = first + vr[j];
+                        miss &= miss - 1u;
+                    }
+                    nv_fix_vecs4<BF16>(x, w, vr, va, ok, s);
                 }
             }
         }
@@ -674,10 +705,18 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
     if constexpr (OP == kOpNvfp4) {
         static_assert(KR + KL <= 64, "one miss bit per held slab");
         if (__builtin_amdgcn_ballot_w64(miss != 0u) != 0u) {            // rare: wave-uniform branch
-            while (miss != 0u) {                    // the lane's set bits, lowest first
-                const uint32_t k = (uint32_t)__builtin_ctzll(miss);
-                miss &= miss - 1u;
-                nv_fix_vec<BF16>(xv, rq, vbase + k * vstep, vbase + k * vstep, s);
+            while (miss != 0u) {                    // four of the lane's set bits per trip
+                uint32_t vr[4];
+                int64_t va[4];
+                bool ok[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    ok[j] = miss != 0u;
+                    vr[j] = ok[j] ? vbase + (uint32_t)__builtin_ctzll(miss) * vstep : 0u;
+                    va[j] = vr[j];
+                    miss &= miss - 1u;
+                }
+                nv_fix_vecs4<BF16>(xv, rq, vr, va, ok, s);
             }
         }
     }
