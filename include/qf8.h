@@ -71,16 +71,17 @@ const char *qf8_status_string(qf8_status status);
  * qf8_workspace_init); every call leaves the barrier and slot regions zero again, so the same
  * workspace serves any number of later calls ordered on one stream. Two calls that may run at
  * the same time need two workspaces. Word 2 (u32) of the workspace, if non-zero, replaces the
- * default 1 ms after which a workgroup waiting at the grid barrier gives its slabs to the last
- * workgroup, in 10 ns ticks (tests set it tiny to exercise that path). */
+ * default time after which a workgroup waiting at the grid barrier of the single-pass kernel
+ * may give up and leave its slabs to the others (50 us plus 10 ns per 500 KB of input, the size
+ * term at most 1 ms), in 10 ns ticks (tests set it tiny to exercise that path). */
 size_t qf8_workspace_bytes(int64_t rows, int64_t cols, qf8_dtype dtype);
 
 /* Sets the number of workgroups of the single-pass kernel (quantize_per_tensor from 2^22
  * elements, delayed-scaling step 0, quantize_nvfp4 with a measured amax) on the current device:
  * grid in [1, 512], or 0 for the default of one workgroup per CU. A tuning and test hook: a grid
  * larger than the number of workgroups that fit on the device at once still gives the same
- * bytes (waiters give their slabs to the last workgroup after the give-up timeout), only
- * slower. The setting is per process and device and applies to calls made after it; calls
+ * bytes (after the give-up timeout about as many waiters leave as are missing, and the others
+ * cast their slabs), only slower. The setting is per process and device and applies to calls made after it; calls
  * already enqueued keep their grid. Returns QF8_ERR_SHAPE for a grid outside [0, 512] (checked
  * before any HIP call), QF8_ERR_HIP if the current device cannot be queried. */
 qf8_status qf8_set_onepass_grid(int grid);

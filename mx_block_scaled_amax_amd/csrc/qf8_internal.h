@@ -20,10 +20,14 @@ constexpr int kMaxStreamGrid = 16384;  // workgroups of the streaming kernels at
 // Workspace layout, in u32 words:
 //   [0, kBarHeaderWords)      grid-barrier header: [0] running amax bits, [1] arrival count (one
 //                             64-bit word), [2] give-up timeout of a waiting workgroup in 10 ns
-//                             ticks (0 = default 1 ms)
+//                             ticks (0 = the default: 50 us + 10 ns per 500 KB of input, the
+//                             size term at most 1 ms), [3] [4] the single-pass kernel's counters
+//                             of given-up slabs (claimed units, finished workgroups)
 //   kBarMaxGroups lines of kBarLineWords words (128 B each): the release line of each workgroup
-//                             (words 0-1); words 16-17 of every 16th line are a first-level
-//                             barrier word of the single-pass kernel
+//                             (words 0-1), an entry of the given-up list (word 4), the count of
+//                             workgroups that gave up on one shader engine (word 5 of lines
+//                             0-31); words 16-17 of every 16th line are a first-level barrier
+//                             word of the single-pass kernel
 //   kSlotCount lines of kBarLineWords words: word 0 of each is a running |amax| maximum that the
 //                             fused delayed-scaling cast raises atomically and the finalize
 //                             kernel reads and clears

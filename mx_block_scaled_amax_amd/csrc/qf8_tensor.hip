@@ -365,22 +365,49 @@ __global__ __launch_bounds__(kThreads) void cast_fused_kernel(const void *__rest
 //     before the arrival, then a 64-bit fetch_add of 2^32, whose returned value carries both the
 //     count and the maximum of every earlier arrival.
 //   the group's last arriver zeroes the group word and arrives the same way at the header word
-//     (workspace words 0-1) with the group maximum; the one that completes the header word
+//     (workspace words 0-1) with the group maximum, adding the group's size: the header counts
+//     the workgroups of complete groups. The one that completes the header word
 //     holds the final maximum: it zeroes that word and releases each other workgroup by
 //     exchanging RELEASED | amax into words 0-1 of that workgroup's own 128-byte line (one line
 //     per poller: no same-address polling).
-//   every other workgroup polls its own line. If it is not released within the timeout it
-//     tries to mark the line GAVE_UP (compare-exchange from 0) and exits without casting; the
-//     last workgroup then finds GAVE_UP in the exchange result and casts all of that
-//     workgroup's slabs from HBM. So the kernel never depends on all workgroups being resident
-//     at once (another kernel may occupy CUs): it only gets slower. Each waiter clears its own
-//     line after reading it, so the workspace is back to all-zero when the kernel ends.
+//   every other workgroup polls its own line. If it is not released within the timeout it may
+//     give up: mark the line GAVE_UP (compare-exchange from 0) and exit without casting, which
+//     frees its CU for a workgroup that is not resident yet (another kernel may hold CUs). So
+//     the kernel never depends on all workgroups being resident at once: it only gets slower.
+//     A timed-out waiter gives up only while the workgroups of its shader engine that gave up
+//     are fewer than a 32nd of those that have not arrived (at most G minus the header count),
+//     so that about as many leave as are missing, on every shader engine, and the rest stay to
+//     share the given-up slabs; otherwise it waits another timeout. After kGiveUpTimeouts time-outs it gives up anyway,
+//     so that every resident workgroup leaves in the end whatever holds the CUs.
+// Given-up slabs. The releaser learns from its exchanges which workgroups gave up. After casting
+// its held slabs it clears their lines, writes their numbers to a list (word 4 of lines 0, 1, ...)
+// and ORs INFO | (count << 48) into the line of every released workgroup. Each released
+// workgroup, when its own slabs are done, polls its line for INFO (the releaser is running, so
+// the wait ends), clears the line, and if the count is not zero joins the releaser in casting the
+// given-up slabs: units of 8 slabs (one stream_slabs8 call) are claimed from a counter (header
+// word 3), and the last workgroup to finish (counted in header word 4) clears the list and the
+// counters. So the workspace is back to all-zero when the kernel ends, and the slabs of a
+// workgroup that gave up are spread over all the others.
 
 constexpr int kBarGroup = 16;                       // workgroups per first-level barrier word
 constexpr int kBarGroupWord = 16;                   // its u32 offset in the group's first line
 constexpr uint64_t kLineReleased = 1ull << 32;
 constexpr uint64_t kLineGaveUp = 2ull << 32;
-constexpr uint32_t kDefaultGiveUpTicks = 100000;   // 1 ms of the 100 MHz real-time counter
+constexpr uint64_t kLineInfo = 4ull << 32;          // + the number of given-up workgroups << 48
+constexpr int kLineListWord = 4;                    // u32 offset of a list entry in its line
+constexpr int kClaimWord = 3, kDoneWord = 4;        // header words of the recast counters
+// Workgroups that gave up, counted per shader engine (8 XCDs x 4 SEs; the count of bucket i is
+// word kLineBucketWord of line i): a workgroup that is not resident waits for a CU of the XCD and
+// shader engine the dispatcher picked for it, so every shader engine gives up its share of the
+// missing workgroups, not only the first waiters to time out.
+constexpr int kGiveUpBuckets = 32;
+constexpr int kLineBucketWord = 5;                  // u32 offset of a bucket count in its line
+constexpr int kGiveUpTimeouts = 8;                  // a waiter gives up at the latest after this many
+// Default timeout of a waiter, in ticks of the 100 MHz real-time counter: 50 us, plus one tick
+// per 500 KB of input (a tenth of the time the first pass takes to stream it at 5 TB/s), since
+// the arrivals of a large streamed tensor spread wider (10-20 us at 1 GiB).
+constexpr uint32_t kDefaultGiveUpTicks = 5000;
+constexpr int64_t kGiveUpBytesPerTick = 500000, kGiveUpMaxExtra = 100000;   // the size term: 1 ms at most
 
 template <bool BF16, int FMT>
 __device__ __forceinline__ void cast_vec_store(__amdgpu_buffer_rsrc_t w, uint32_t off, uint4 v, float s) {
@@ -570,11 +597,11 @@ __device__ __forceinline__ uint32_t stream_slabs8(const uint4 *x, int64_t nvec, 
 // maximum (waiting for the atomic to be performed, so it is in the word before this arrival is
 // counted), then count. The last arrival gets true and the maximum over all arrivals in *total,
 // and zeroes the word for the next call.
-__device__ __forceinline__ bool arrive(uint64_t *word, uint32_t m, uint32_t expected, uint32_t &total) {
+__device__ __forceinline__ bool arrive(uint64_t *word, uint32_t m, uint32_t inc, uint32_t expected, uint32_t &total) {
     const uint32_t prev = __hip_atomic_fetch_max((uint32_t *)word, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     asm volatile("s_waitcnt vmcnt(0)" ::"v"(prev) : "memory");
-    const uint64_t old = __hip_atomic_fetch_add(word, 1ull << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((uint32_t)(old >> 32) != expected - 1) return false;
+    const uint64_t old = __hip_atomic_fetch_add(word, (uint64_t)inc << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((uint32_t)(old >> 32) + inc != expected) return false;
     total = umax((uint32_t)old, m);
     __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return true;
@@ -590,7 +617,7 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
     constexpr uint32_t kVpb = BF16 ? 2u : 4u;
     __shared__ uint4 held[KL * kOpThreads];
     __shared__ uint32_t red[kOpThreads / 64];
-    __shared__ uint32_t sh[3];
+    __shared__ uint32_t sh[4];
     __shared__ uint16_t gave_up[kBarMaxGroups];
     __shared__ float2 nvtab[OP == kOpNvfp4 ? 128 : 1];            // NVFP4: (r_lo, r_hi) per E4M3 code
     const uint4 *xv = (const uint4 *)x;
@@ -635,35 +662,52 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
     uint64_t *own = lines + (size_t)b * (kBarLineWords / 2);
     if (t == 0) {
         // arrival in two levels: the group's word, then (the group's last arriver) the header word
-        const int grp = b / kBarGroup, ngrp = (G + kBarGroup - 1) / kBarGroup;
+        const int grp = b / kBarGroup;
         const uint32_t gsize = (uint32_t)min(kBarGroup, G - grp * kBarGroup);
         uint32_t role = 0, am = 0;
         uint32_t gm = 0;
-        if (arrive(lines + (size_t)grp * kBarGroup * (kBarLineWords / 2) + kBarGroupWord / 2, m, gsize, gm) &&
-            arrive((uint64_t *)ws, gm, (uint32_t)ngrp, am))
+        if (arrive(lines + (size_t)grp * kBarGroup * (kBarLineWords / 2) + kBarGroupWord / 2, m, 1u, gsize, gm) &&
+            arrive((uint64_t *)ws, gm, gsize, (uint32_t)G, am))
             role = 1;
         if (role == 0) {
-            const uint32_t limit = ws[2] ? ws[2] : kDefaultGiveUpTicks;
-            const uint64_t start = __builtin_amdgcn_s_memrealtime();
+            const int64_t extra = nvec * 16 / kGiveUpBytesPerTick;
+            const uint32_t limit = ws[2] ? ws[2] : kDefaultGiveUpTicks + (uint32_t)(extra < kGiveUpMaxExtra ? extra : kGiveUpMaxExtra);
+            // XCC_ID[3:0] and HW_ID.SE_ID[14:13] of this wave
+            const uint32_t xcc = __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11));
+            const uint32_t se = __builtin_amdgcn_s_getreg(4 | (13 << 6) | (1 << 11));
+            uint32_t *gcount = (uint32_t *)(lines + (size_t)((xcc * 4u + se) % kGiveUpBuckets) * (kBarLineWords / 2)) +
+                               kLineBucketWord;
+            uint64_t start = __builtin_amdgcn_s_memrealtime();
             uint64_t v;
-            for (;;) {
+            for (int timeouts = 1;; ) {
                 v = __hip_atomic_load(own, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (v != 0) break;
                 if (__builtin_amdgcn_s_memrealtime() - start > limit) {
-                    uint64_t expected = 0;
-                    v = __hip_atomic_compare_exchange_strong(own, &expected, kLineGaveUp, __ATOMIC_RELAXED,
-                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                            ? kLineGaveUp : expected;
-                    break;
+                    // give up while this bucket's share of the workgroups that have not arrived
+                    // (the header counts those of complete groups) is not yet used, or after
+                    // kGiveUpTimeouts time-outs
+                    const uint32_t h = (uint32_t)(__hip_atomic_load((uint64_t *)ws, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32);
+                    const uint32_t g = __hip_atomic_fetch_add(gcount, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (g < ((uint32_t)G - h + kGiveUpBuckets - 1) / kGiveUpBuckets || timeouts >= kGiveUpTimeouts) {
+                        uint64_t expected = 0;
+                        if (__hip_atomic_compare_exchange_strong(own, &expected, kLineGaveUp, __ATOMIC_RELAXED,
+                                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                            v = kLineGaveUp;        // stays counted in the give-up word
+                            break;
+                        }
+                        v = expected;               // released meanwhile
+                    }
+                    // not given up: the count goes back down before this workgroup goes on
+                    const uint32_t back = __hip_atomic_fetch_sub(gcount, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    asm volatile("" ::"v"(back));
+                    if (v != 0) break;
+                    ++timeouts;
+                    start = __builtin_amdgcn_s_memrealtime();
                 }
                 __builtin_amdgcn_s_sleep(1);
             }
-            if (v == kLineGaveUp) {
-                role = 2;
-            } else {
-                am = (uint32_t)v;
-                __hip_atomic_store(own, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            if (v == kLineGaveUp) role = 2;
+            else am = (uint32_t)v;                  // the line is cleared once INFO has come
         }
         sh[0] = role;
         sh[1] = am;
@@ -671,9 +715,9 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
     }
     __syncthreads();
     const uint32_t role = sh[0];
-    if (role == 2) return;                          // the last workgroup casts this one's slabs
+    if (role == 2) return;                          // the released workgroups cast this one's slabs
     m = sh[1];
-    uint64_t xres = 0;
+    uint64_t xres = kLineReleased;                  // (what no exchange returns: the line was 0 or GAVE_UP)
     if (role == 1 && t < G && t != b)               // release: one line per thread (G <= kOpThreads)
         xres = __hip_atomic_exchange(lines + (size_t)t * (kBarLineWords / 2), kLineReleased | m, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
@@ -720,19 +764,74 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
             }
         }
     }
-    for (int64_t k = KR + KL; k * G + b < nslabs; k += 8)
-        stream_slabs8<OP, BF16, FMT, true>(xv, nvec, q, sb, k, b, G, s, nvtab);
-
+    // the releaser publishes the given-up workgroups (see the barrier description above)
+    uint32_t ng = 0;
     if (role == 1) {
-        if (xres == kLineGaveUp) {                  // that workgroup exited: clear its line, cast its slabs
+        const bool tell = xres == 0u;               // released by this thread's exchange: gets INFO
+        if (xres == kLineGaveUp) {
             __hip_atomic_store(lines + (size_t)t * (kBarLineWords / 2), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             gave_up[atomicAdd(&sh[2], 1u)] = (uint16_t)t;
         }
         __syncthreads();
-        const uint32_t ng = sh[2];
-        for (uint32_t i = 0; i < ng; ++i)
-            for (int64_t k = 0; k * G + gave_up[i] < nslabs; k += 8)
-                stream_slabs8<OP, BF16, FMT, true>(xv, nvec, q, sb, k, gave_up[i], G, s, nvtab);
+        ng = sh[2];
+        if ((uint32_t)t < ng) {
+            // an exchange whose result is waited for is performed before the barrier below, so
+            // the entry is in place before any INFO that announces it
+            const uint32_t old = __hip_atomic_exchange((uint32_t *)(lines + (size_t)t * (kBarLineWords / 2)) + kLineListWord,
+                                                       (uint32_t)gave_up[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            asm volatile("" ::"v"(old));
+        }
+        __syncthreads();
+        if (tell)
+            __hip_atomic_fetch_or(lines + (size_t)t * (kBarLineWords / 2), kLineInfo | (uint64_t)ng << 48,
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    for (int64_t k = KR + KL; k * G + b < nslabs; k += 8)
+        stream_slabs8<OP, BF16, FMT, true>(xv, nvec, q, sb, k, b, G, s, nvtab);
+
+    if (role == 0) {                                // the releaser's INFO: how many gave up
+        if (t == 0) {
+            uint64_t v;
+            while (((v = __hip_atomic_load(own, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) & kLineInfo) == 0u)
+                __builtin_amdgcn_s_sleep(1);
+            __hip_atomic_store(own, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sh[2] = (uint32_t)(v >> 48);
+        }
+        __syncthreads();
+        ng = sh[2];
+    }
+    if (ng != 0u) {                                 // rare: cast the given-up slabs together
+        const int64_t most = (nslabs + G - 1) / G;                  // slabs of a workgroup at most
+        const uint32_t upw = (uint32_t)((most + 7) / 8), units = ng * upw;
+        for (;;) {
+            __syncthreads();                        // the previous unit's sh[3] has been read
+            if (t == 0) {
+                const uint32_t u = __hip_atomic_fetch_add(ws + kClaimWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sh[3] = u;
+                if (u < units)
+                    sh[0] = __hip_atomic_load((uint32_t *)(lines + (size_t)(u / upw) * (kBarLineWords / 2)) + kLineListWord,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();
+            const uint32_t u = sh[3];
+            if (u >= units) break;
+            const int j = (int)sh[0];
+            const int64_t k = (int64_t)(u % upw) * 8;
+            if (k * G + j < nslabs) stream_slabs8<OP, BF16, FMT, true>(xv, nvec, q, sb, k, j, G, s, nvtab);
+        }
+        if (t == 0 && __hip_atomic_fetch_add(ws + kDoneWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                          (uint32_t)G - ng - 1u) {  // the last one out: list and counters back to zero
+            for (uint32_t i = 0; i < ng; ++i)
+                __hip_atomic_store((uint32_t *)(lines + (size_t)i * (kBarLineWords / 2)) + kLineListWord, 0u,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(ws + kClaimWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(ws + kDoneWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int i = 0; i < kGiveUpBuckets; ++i)
+                __hip_atomic_store((uint32_t *)(lines + (size_t)i * (kBarLineWords / 2)) + kLineBucketWord, 0u,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if (role == 1) {
         if constexpr (OP == kOpFp8)          // NVFP4 sizes are whole vectors (n % 16 == 0)
             for (int64_t e = nvec * vec_elems<BF16>() + t; e < n; e += kOpThreads)
                 q[e] = (uint8_t)cast1<FMT>(__uint_as_float(elem_bits<BF16>(x, e)), s);

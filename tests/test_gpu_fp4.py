@@ -330,9 +330,9 @@ def test_nvfp4_single_pass_ragged_scale_groups():
     check_nv_big(x, ws, "1025x4112 fp32 (vectors % 16 = 4)")
 
 
-@pytest.mark.parametrize("ticks", [1, 500])
+@pytest.mark.parametrize("ticks", [1, 100])
 def test_nvfp4_single_pass_give_up(gradient_full, ticks):
-    """Waiting workgroups forced to give up at the grid barrier: the last one casts their slabs."""
+    """Waiting workgroups forced to give up at the grid barrier: the released ones cast their slabs."""
     ws = qf8.workspace(torch.empty(1, device="cuda"))
     ws.view(torch.int32)[2] = ticks
     check_nv_big(gradient_full, ws, f"give-up after {ticks} ticks")
@@ -343,8 +343,8 @@ def test_nvfp4_single_pass_give_up(gradient_full, ticks):
 @pytest.mark.parametrize("grid", [17, 300])
 def test_nvfp4_single_pass_other_grids(grid):
     """Other workgroup counts of the single-pass kernel: a ragged last barrier group (17), and
-    more workgroups than fit at once on a 256-CU device (300: the late ones find given-up
-    waiters, whose slabs the last workgroup casts)."""
+    more workgroups than fit at once on a 256-CU device (300: the late ones run once waiters have
+    given up, whose slabs the released workgroups cast)."""
     ws = qf8.workspace(torch.empty(1, device="cuda"))
     qf8.qf8_set_onepass_grid(grid)
     try:
