@@ -380,10 +380,11 @@ __global__ __launch_bounds__(kThreads) void cast_fused_kernel(const void *__rest
 //     share the given-up slabs; otherwise it waits another timeout. After kGiveUpTimeouts time-outs it gives up anyway,
 //     so that every resident workgroup leaves in the end whatever holds the CUs.
 // Given-up slabs. The releaser learns from its exchanges which workgroups gave up. After casting
-// its held slabs it clears their lines, writes their numbers to a list (word 4 of lines 0, 1, ...)
-// and ORs INFO | (count << 48) into the line of every released workgroup. Each released
-// workgroup, when its own slabs are done, polls its line for INFO (the releaser is running, so
-// the wait ends), clears the line, and if the count is not zero joins the releaser in casting the
+// kPublishAt of its held slabs it clears their lines, writes their numbers to a list (word 4 of
+// lines 0, 1, ...) and ORs INFO | (count << 48) into the line of every released workgroup. Each
+// released workgroup reads its line half-way through its held slabs and, when they are done,
+// polls again if INFO was not there yet (the releaser is running, so the wait ends), clears the
+// line, and if the count is not zero joins the releaser in casting the
 // given-up slabs: units of 8 slabs (one stream_slabs8 call) are claimed from a counter (header
 // word 3), and the last workgroup to finish (counted in header word 4) clears the list and the
 // counters. So the workspace is back to all-zero when the kernel ends, and the slabs of a
@@ -395,6 +396,10 @@ constexpr uint64_t kLineReleased = 1ull << 32;
 constexpr uint64_t kLineGaveUp = 2ull << 32;
 constexpr uint64_t kLineInfo = 4ull << 32;          // + the number of given-up workgroups << 48
 constexpr int kLineListWord = 4;                    // u32 offset of a list entry in its line
+// The releaser sends INFO after this many register slabs: by then its exchanges have returned
+// (at 8 it still waited for them, and being the last workgroup to start its casts, that cost
+// the whole call ~0.3 us at 8192x8192).
+constexpr int kPublishAt = 12;
 constexpr int kClaimWord = 3, kDoneWord = 4;        // header words of the recast counters
 // Workgroups that gave up, counted per shader engine (8 XCDs x 4 SEs; the count of bucket i is
 // word kLineBucketWord of line i): a workgroup that is not resident waits for a CU of the XCD and
@@ -733,10 +738,40 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
     // as soon as it is known (the empty asm), so that the compiler does not carry every vector's
     // inputs down to the fix-up below.
     uint32_t miss_w[2] = {0u, 0u};
+    // Given-up slabs (see the barrier description above): the releaser publishes after its first
+    // kPublishAt register slabs, when its exchanges have returned; the others read INFO after
+    // slab KR / 2, well after that, and use it only at the end, so that neither waits.
+    uint32_t ng = 0, info = 0;                      // info: the high half of the own line
+    constexpr int kInfoReadAt = KR / 2;
+    static_assert(kPublishAt + 8 <= kInfoReadAt && kInfoReadAt < KR, "INFO is read well after it is sent");
 #pragma unroll
     for (int k = 0; k < KR; ++k) {
         miss_w[k >> 5] |= (uint32_t)op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + k * vstep, R[k], s, nvtab) << (k & 31);
         if constexpr (OP == kOpNvfp4) asm volatile("" : "+v"(miss_w[k >> 5]));
+        if (k == kPublishAt && role == 1) {
+            const bool tell = xres == 0u;           // released by this thread's exchange: gets INFO
+            if (xres == kLineGaveUp) {
+                __hip_atomic_store(lines + (size_t)t * (kBarLineWords / 2), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                gave_up[atomicAdd(&sh[2], 1u)] = (uint16_t)t;
+            }
+            __syncthreads();
+            ng = sh[2];
+            if (ng != 0u) {                         // rare
+                if ((uint32_t)t < ng) {
+                    // an exchange whose result is waited for is performed before the barrier
+                    // below, so the entry is in place before any INFO that announces it
+                    const uint32_t old = __hip_atomic_exchange((uint32_t *)(lines + (size_t)t * (kBarLineWords / 2)) + kLineListWord,
+                                                               (uint32_t)gave_up[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    asm volatile("" ::"v"(old));
+                }
+                __syncthreads();
+            }
+            if (tell)
+                __hip_atomic_fetch_or(lines + (size_t)t * (kBarLineWords / 2), kLineInfo | (uint64_t)ng << 48,
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (k == kInfoReadAt && role == 0 && t == 0)   // (32 bits: no dead half to wait for)
+            info = __hip_atomic_load((uint32_t *)own + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 #pragma unroll
     for (int k = 0; k < KL; ++k) {
@@ -764,38 +799,18 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
             }
         }
     }
-    // the releaser publishes the given-up workgroups (see the barrier description above)
-    uint32_t ng = 0;
-    if (role == 1) {
-        const bool tell = xres == 0u;               // released by this thread's exchange: gets INFO
-        if (xres == kLineGaveUp) {
-            __hip_atomic_store(lines + (size_t)t * (kBarLineWords / 2), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            gave_up[atomicAdd(&sh[2], 1u)] = (uint16_t)t;
-        }
-        __syncthreads();
-        ng = sh[2];
-        if ((uint32_t)t < ng) {
-            // an exchange whose result is waited for is performed before the barrier below, so
-            // the entry is in place before any INFO that announces it
-            const uint32_t old = __hip_atomic_exchange((uint32_t *)(lines + (size_t)t * (kBarLineWords / 2)) + kLineListWord,
-                                                       (uint32_t)gave_up[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            asm volatile("" ::"v"(old));
-        }
-        __syncthreads();
-        if (tell)
-            __hip_atomic_fetch_or(lines + (size_t)t * (kBarLineWords / 2), kLineInfo | (uint64_t)ng << 48,
-                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
     for (int64_t k = KR + KL; k * G + b < nslabs; k += 8)
         stream_slabs8<OP, BF16, FMT, true>(xv, nvec, q, sb, k, b, G, s, nvtab);
 
     if (role == 0) {                                // the releaser's INFO: how many gave up
         if (t == 0) {
-            uint64_t v;
-            while (((v = __hip_atomic_load(own, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) & kLineInfo) == 0u)
+            uint32_t v = info;
+            while ((v & (uint32_t)(kLineInfo >> 32)) == 0u) {   // rare: not there yet when read above
                 __builtin_amdgcn_s_sleep(1);
+                v = __hip_atomic_load((uint32_t *)own + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
             __hip_atomic_store(own, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            sh[2] = (uint32_t)(v >> 48);
+            sh[2] = v >> 16;                        // bits 48.. of the line word
         }
         __syncthreads();
         ng = sh[2];
