@@ -46,3 +46,40 @@ def parallel_row_slabs(fn, rows, slab):
     bounds = [(r, min(r + slab, rows)) for r in range(0, rows, slab)]
     with ThreadPoolExecutor(ORACLE_THREADS) as ex:
         return list(ex.map(lambda b: fn(*b), bounds))
+
+
+def holder_lib():
+    """The CU-holding kernel of the contention tests (tests/contention/holder.hip, built by
+    __graft_entry__.build()): holder_launch(grid, lds_bytes, microseconds, sink, stream)."""
+    import ctypes
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "contention", "libholder.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    lib.holder_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.holder_launch.restype = ctypes.c_int
+    return lib
+
+
+_HOLD_STREAMS = []
+
+
+def time_beside_holders(lib, holders, call, hold_us=3000, lds=48 * 1024):
+    """Launches the holder on its own stream (holders workgroups, each with lds bytes of LDS, for
+    hold_us microseconds), then call() on another stream after a ~20 us delay that lets the
+    holder's workgroups start first. Returns call()'s time in microseconds from HIP events on its
+    stream, after a device synchronize. call() must allocate nothing: an allocation on the
+    stream between the events would be timed too."""
+    if not _HOLD_STREAMS:
+        _HOLD_STREAMS.extend([torch.cuda.Stream(), torch.cuda.Stream(), torch.zeros(1, dtype=torch.int32, device="cuda")])
+    hold, side, sink = _HOLD_STREAMS
+    torch.cuda.synchronize()
+    assert lib.holder_launch(holders, lds, hold_us, sink.data_ptr(), hold.cuda_stream) == 0
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(50000)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(side)
+        call()
+        e1.record(side)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3

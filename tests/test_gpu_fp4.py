@@ -24,7 +24,7 @@ import torch
 import mx_block_scaled_amax_amd as qf8
 import oracle as O
 from synthetic import bf16_bits, mx_gradient, small_tensor
-from qf8_test_utils import assert_bytes_equal, host, parallel_row_slabs, to_device
+from qf8_test_utils import assert_bytes_equal, holder_lib, host, parallel_row_slabs, time_beside_holders, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -338,6 +338,38 @@ def test_nvfp4_single_pass_give_up(gradient_full, ticks):
     check_nv_big(gradient_full, ws, f"give-up after {ticks} ticks")
     ws.view(torch.int32)[2] = 0
     check_nv_big(gradient_full[:2048], ws, "default timeout after a give-up run")
+
+
+def test_nvfp4_single_pass_beside_cu_holders(gradient_full):
+    """The single-pass NVFP4 kernel (16384x4096 BF16, 120 MiB held on chip) while a kernel on
+    another stream holds 48 KiB of LDS on 8 CUs for 3 ms: about as many waiters give up, per
+    shader engine, and the released workgroups cast their slabs. Same bytes as the oracle, the
+    workspace left zero, and the call ends in under 1 ms (events on its stream)."""
+    lib = holder_lib()
+    x = gradient_full
+    xd = to_device(x)
+    ws = qf8.workspace(torch.empty(1, device="cuda"))
+    a = float(O.amax(x))
+    parts = parallel_row_slabs(lambda r0, r1: O.quantize_nvfp4(x[r0:r1], amax_in=a), x.shape[0], 256)
+    wq = np.concatenate([p[0] for p in parts], axis=0)
+    wsb = np.concatenate([p[1] for p in parts], axis=0)
+    q = torch.empty(wq.shape, dtype=torch.uint8, device="cuda")
+    sb = torch.empty(wsb.shape, dtype=torch.uint8, device="cuda")
+    ts = torch.empty(1, dtype=torch.float32, device="cuda")
+    times = []
+    for rep in range(3):
+        print(f"nvfp4 single pass beside 8 CU holders, rep {rep}", flush=True)
+        q.fill_(0xA5)
+        sb.fill_(0xA5)
+        times.append(time_beside_holders(lib, 8, lambda: qf8.quantize_nvfp4(xd, q=q, s_blk=sb, tensor_scale=ts, ws=ws)))
+        assert np.float32(ts.item()) == parts[0][2], rep
+        assert_bytes_equal(host(sb), wsb, "s_blk", f" [beside 8 CU holders, rep {rep}]")
+        assert_bytes_equal(host(q), wq, "q", f" [beside 8 CU holders, rep {rep}]")
+        words = host(ws.view(torch.int32)[:qf8.BARRIER_WORDS]).copy()
+        words[2] = 0
+        assert not words.any(), "workspace not left zero"
+    print(f"call times (us): {[round(t) for t in times]}", flush=True)
+    assert max(times) < 1000.0, times
 
 
 @pytest.mark.parametrize("grid", [17, 300])

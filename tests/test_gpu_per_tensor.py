@@ -15,7 +15,8 @@ import torch
 import mx_block_scaled_amax_amd as qf8
 import oracle as O
 from synthetic import bf16_to_f32, per_tensor_activation, per_tensor_small, small_tensor
-from qf8_test_utils import assert_bytes_equal, host, parallel_row_slabs, to_device
+from qf8_test_utils import (assert_bytes_equal, holder_lib, host, parallel_row_slabs, time_beside_holders,
+                             to_device)
 
 pytestmark = pytest.mark.gpu
 FMTS = [O.E4M3, O.E5M2]
@@ -237,58 +238,40 @@ def test_onepass_other_grids(grid):
         qf8.qf8_set_onepass_grid(0)
 
 
-def holder_lib():
-    import ctypes
-    import os
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "contention", "libholder.so")
-    if not os.path.exists(path):
-        pytest.fail(f"{path} is not built: run __graft_entry__.build() first")
-    lib = ctypes.CDLL(path)
-    lib.holder_launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    lib.holder_launch.restype = ctypes.c_int
-    return lib
-
-
-@pytest.mark.parametrize("holders", [8, 64])
-def test_onepass_beside_cu_holders(activation_full, holders):
+@pytest.mark.parametrize("holders,size", [(8, "8192x8192"), (64, "8192x8192"), (8, "beyond the held capacity")])
+def test_onepass_beside_cu_holders(activation_full, holders, size):
     """A kernel on another stream holds 48 KiB of LDS on `holders` CUs for 3 ms (so one workgroup
-    of the single-pass kernel no longer fits on those CUs) while the 8192x8192 call runs: that
+    of the single-pass kernel no longer fits on those CUs) while a single-pass call runs: that
     many workgroups cannot become resident. About as many waiters give up, on every shader
-    engine, the late workgroups take their CUs, and the others share the given-up slabs. The
-    bytes, the amax and the scale are unchanged, the workspace is left zero, and the call ends
-    within the give-up timeout (~53 us here) plus a few uncontended calls: it is timed with
-    events on its stream and must end in under 1 ms, long before the holder (a design where
-    every waiter gives up after 1 ms and one workgroup casts all of their slabs took 2.8-4.5 ms)."""
+    engine, the late workgroups take their CUs, and the others share the given-up slabs (beyond
+    the held capacity those include slabs that are streamed twice). The bytes, the amax and the
+    scale are unchanged, the workspace is left zero, and the call ends within the give-up
+    timeout (~53 us at 8192x8192) plus a few uncontended calls: it is timed with events on its
+    stream and must end in under 1 ms, long before the holder (a design where every waiter gives
+    up after 1 ms and one workgroup casts all of their slabs took 2.8-4.5 ms)."""
     lib = holder_lib()
-    x = activation_full
+    if size == "8192x8192":
+        x = activation_full
+    else:
+        x = small_tensor(1, onchip_capacity_elems(2) + onchip_capacity_elems(2) // 3 + 5, seed=61)
     xd = to_device(x)
     ws = qf8.workspace(xd)
     q = torch.empty(x.shape, dtype=torch.uint8, device="cuda")
-    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
-    hold, side = torch.cuda.Stream(), torch.cuda.Stream()
-    wa = np.float32(O.amax(x))
-    wsc = np.float32(O.scale_from_amax(O.E4M3, wa))
-    want = np.concatenate(parallel_row_slabs(lambda r0, r1: O.cast(x[r0:r1], O.E4M3, wsc), x.shape[0], 512), axis=0)
+    am = torch.empty(1, dtype=torch.float32, device="cuda")
+    sc = torch.empty(1, dtype=torch.float32, device="cuda")
+    wq, wa, wsc = oracle_flat(x, O.E4M3)
     times = []
     for rep in range(3):
-        print(f"beside {holders} CU holders, rep {rep}", flush=True)
+        print(f"beside {holders} CU holders, {size}, rep {rep}", flush=True)
         q.fill_(0xA5)
-        torch.cuda.synchronize()
-        assert lib.holder_launch(holders, 48 * 1024, 3000, sink.data_ptr(), hold.cuda_stream) == 0
-        with torch.cuda.stream(side):
-            torch.cuda._sleep(50000)                 # ~20 us: the holder's workgroups start first
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(side)
-            _, am, sc = qf8.quantize_per_tensor(xd, O.E4M3, q=q, ws=ws)
-            e1.record(side)
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1) * 1e3)
+        times.append(time_beside_holders(lib, holders, lambda: qf8.quantize_per_tensor(xd, O.E4M3, q=q, amax=am, scale=sc,
+                                                                                       ws=ws)))
         assert np.float32(am.item()) == wa and np.float32(sc.item()) == wsc, rep
-        assert_bytes_equal(host(q), want, "q", f" [beside {holders} CU holders, rep {rep}]")
+        assert_bytes_equal(host(q), wq, "q", f" [beside {holders} CU holders, {size}, rep {rep}]")
         words = barrier_words(ws)
         words[2] = 0
         assert not words.any(), "barrier region not left zero"
-    print(f"call times beside {holders} CU holders (us): {[round(t) for t in times]}", flush=True)
+    print(f"call times beside {holders} CU holders, {size} (us): {[round(t) for t in times]}", flush=True)
     assert max(times) < 1000.0, times
 
 
