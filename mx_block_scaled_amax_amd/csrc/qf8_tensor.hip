@@ -43,11 +43,17 @@ constexpr int kVecs = 2;                        // 16-byte input vectors per thr
 constexpr int kAmaxThreads = 1024;              // read-only amax pass: one 16-wave workgroup per CU
 constexpr int kAmaxDepth = 8;                   //   16-byte loads per thread in flight
 constexpr int kFinalizeThreads = 256;           // single-workgroup finalize: one slot per thread
-constexpr int kOpThreads = 512;                 // single-pass kernel: 8 waves, 2 per SIMD
+constexpr int kOpThreads = 512;                 // single-pass kernel, FP8 output: 8 waves, 2 per SIMD
 constexpr int kOpRegSlabs = 48;                 //   slabs held in VGPRs (4 VGPRs each)
 constexpr int kOpLdsSlabs = 16;                 //   slabs held in LDS (8 KiB each)
-constexpr int kOpRegSlabsNv = 42;               // NVFP4 output: its block arithmetic needs more
-constexpr int kOpLdsSlabsNv = 18;               //   VGPRs, so fewer register slabs, more LDS ones
+// NVFP4 output: its write phase is VALU-bound (two code estimates per element), so it runs 16
+// waves (4 per SIMD, 128 VGPRs each) to hide the latencies of that phase, and holds 18 slabs in
+// VGPRs (the most without spills) and 9 in LDS (16 KiB each): 432 KiB per workgroup instead of
+// 480. On 16384x4096 BF16 that re-reads 20 MiB but took 52.0-52.8 µs against 54.4-54.6 µs with
+// 8 waves holding 42 + 18 slabs of 8 KiB.
+constexpr int kOpThreadsNv = 1024;
+constexpr int kOpRegSlabsNv = 18;
+constexpr int kOpLdsSlabsNv = 9;
 constexpr uint32_t kAbs16x2 = 0x7FFF7FFFu;
 
 // |x| maximum of one 16-byte vector, accumulated as bit patterns (BF16 kept packed).
@@ -346,12 +352,12 @@ __global__ __launch_bounds__(kThreads) void cast_fused_kernel(const void *__rest
 }
 
 // ---------------------------------------------------------------------------------------------
-// Single-HBM-pass current scaling. One workgroup of kOpThreads per CU (grid = CU count, at most
-// kBarMaxGroups). The tensor is cut into slabs of kOpThreads 16-byte vectors; workgroup b owns
-// slabs b, b + G, b + 2G, ... (neighbouring workgroups read neighbouring slabs, so every HBM
-// channel is busy at once). Its first kOpRegSlabs slabs stay in VGPRs and the next kOpLdsSlabs
-// in LDS (loaded by direct-to-LDS DMA, no VGPR staging), so that a tensor up to
-//   G * kOpThreads * (kOpRegSlabs + kOpLdsSlabs) * 16 bytes   (128 MiB on 256 CUs)
+// Single-HBM-pass current scaling. One workgroup of op_threads<OP>() threads per CU (grid = CU
+// count, at most kBarMaxGroups). The tensor is cut into slabs of one 16-byte vector per thread;
+// workgroup b owns slabs b, b + G, b + 2G, ... (neighbouring workgroups read neighbouring slabs,
+// so every HBM channel is busy at once). Its first KR slabs stay in VGPRs and the next KL in LDS
+// (loaded by direct-to-LDS DMA, no VGPR staging), so that a tensor up to
+//   G * threads * (KR + KL) * 16 bytes   (FP8 output: 128 MiB on 256 CUs; NVFP4: 108 MiB)
 // is read from HBM exactly once; slabs beyond that are reduced in the first pass and re-read
 // for the cast.
 //
@@ -396,10 +402,11 @@ constexpr uint64_t kLineReleased = 1ull << 32;
 constexpr uint64_t kLineGaveUp = 2ull << 32;
 constexpr uint64_t kLineInfo = 4ull << 32;          // + the number of given-up workgroups << 48
 constexpr int kLineListWord = 4;                    // u32 offset of a list entry in its line
-// The releaser sends INFO after this many register slabs: by then its exchanges have returned
-// (at 8 it still waited for them, and being the last workgroup to start its casts, that cost
-// the whole call ~0.3 us at 8192x8192).
-constexpr int kPublishAt = 12;
+// The releaser sends INFO after this many register slabs (FP8 output; NVFP4, whose slabs are twice
+// as large and slower to cast, after a third of them): by then its exchanges have returned (at 8
+// it still waited for them, and being the last workgroup to start its casts, that cost the whole
+// call ~0.3 us at 8192x8192).
+constexpr int kPublishAtFp8 = 12;
 constexpr int kClaimWord = 3, kDoneWord = 4;        // header words of the recast counters
 // Workgroups that gave up, counted per shader engine (8 XCDs x 4 SEs; the count of bucket i is
 // word kLineBucketWord of line i): a workgroup that is not resident waits for a CU of the XCD and
@@ -429,6 +436,7 @@ __device__ __forceinline__ void cast_vec_store(__amdgpu_buffer_rsrc_t w, uint32_
 // (FP32) vectors held by adjacent lanes, whose amax meets by DPP; each lane writes its 4 or 2
 // code bytes and the block's first lane the E4M3 scale byte. All lanes must be active.
 constexpr int kOpFp8 = 0, kOpNvfp4 = 1;
+template <int OP> constexpr int op_threads() { return OP == kOpFp8 ? kOpThreads : kOpThreadsNv; }
 template <int OP, bool BF16>
 constexpr uint32_t op_out_bytes() { return OP == kOpFp8 ? (BF16 ? 8u : 4u) : (BF16 ? 4u : 2u); }
 
@@ -557,10 +565,11 @@ __device__ __forceinline__ uint32_t span_bytes(int64_t first, int64_t nvec, uint
 template <int OP, bool BF16, int FMT, bool CAST>
 __device__ __forceinline__ uint32_t stream_slabs8(const uint4 *x, int64_t nvec, uint8_t *q, uint8_t *sb, int64_t k,
                                                   int j, int G, float s, const float2 *tab) {
+    constexpr int NT = op_threads<OP>();
     constexpr uint32_t kOut = op_out_bytes<OP, BF16>();
     constexpr uint32_t kVpb = BF16 ? 2u : 4u;                      // vectors per NVFP4 block
-    const uint32_t step = (uint32_t)G * kOpThreads * 16u;
-    const int64_t first = (k * G + j) * kOpThreads;
+    const uint32_t step = (uint32_t)G * NT * 16u;
+    const int64_t first = (k * G + j) * NT;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(x + first, span_bytes(first, nvec, 16u));
     uint4 v[8];
 #pragma unroll
@@ -613,27 +622,28 @@ __device__ __forceinline__ bool arrive(uint64_t *word, uint32_t m, uint32_t inc,
 }
 
 template <bool BF16, int FMT, int OP>
-__global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
+__global__ __launch_bounds__(op_threads<OP>()) void per_tensor_onepass_kernel(
         const void *__restrict__ x, int64_t n, int64_t nvec, uint8_t *__restrict__ q, uint8_t *__restrict__ sb,
         uint32_t *ws, float *amax_out, float *scale_out, int32_t *nonfinite, uint32_t *amax_bits_out) {
+    constexpr int NT = op_threads<OP>();
     constexpr int KR = OP == kOpFp8 ? kOpRegSlabs : kOpRegSlabsNv;
     constexpr int KL = OP == kOpFp8 ? kOpLdsSlabs : kOpLdsSlabsNv;
     constexpr uint32_t kOut = op_out_bytes<OP, BF16>();
     constexpr uint32_t kVpb = BF16 ? 2u : 4u;
-    __shared__ uint4 held[KL * kOpThreads];
-    __shared__ uint32_t red[kOpThreads / 64];
+    __shared__ uint4 held[KL * NT];
+    __shared__ uint32_t red[NT / 64];
     __shared__ uint32_t sh[4];
     __shared__ uint16_t gave_up[kBarMaxGroups];
     __shared__ float2 nvtab[OP == kOpNvfp4 ? 128 : 1];            // NVFP4: (r_lo, r_hi) per E4M3 code
     const uint4 *xv = (const uint4 *)x;
     const int G = gridDim.x, b = blockIdx.x, t = threadIdx.x;
-    const int64_t nslabs = (nvec + kOpThreads - 1) / kOpThreads;
-    // held slabs: offsets below (KR + KL) * G * kOpThreads * 16 < 2^32 (G <= kBarMaxGroups)
+    const int64_t nslabs = (nvec + NT - 1) / NT;
+    // held slabs: offsets below (KR + KL) * G * NT * 16 < 2^32 (G <= kBarMaxGroups)
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(xv, span_bytes(0, nvec, 16u));
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(q, span_bytes(0, nvec, kOut));
     const __amdgpu_buffer_rsrc_t rsb = make_rsrc(OP == kOpNvfp4 ? sb : q, OP == kOpNvfp4 ? span_bytes(0, nvec, 1u) / kVpb : 0u);
-    const uint32_t step = (uint32_t)G * kOpThreads * 16u;        // bytes between a workgroup's slabs
-    const uint32_t base = ((uint32_t)b * kOpThreads + t) * 16u;
+    const uint32_t step = (uint32_t)G * NT * 16u;        // bytes between a workgroup's slabs
+    const uint32_t base = ((uint32_t)b * NT + t) * 16u;
 
     // pass 1: slabs that are not held (maximum only), then the LDS-held slabs (DMA), then the
     // register-held slabs, all loads in flight together
@@ -644,7 +654,7 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
 #pragma unroll
     for (int k = 0; k < KL; ++k)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void *)&held[k * kOpThreads + wave * 64],
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void *)&held[k * NT + wave * 64],
                                                  16, base + (KR + k) * step, 0, 0, kNonTemporal);
     uint4 R[KR];
 #pragma unroll
@@ -656,11 +666,11 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
         else c0 = vec_absmax<BF16>(c0, R[k]);
     }
 #pragma unroll
-    for (int k = 0; k < KL; ++k) c1 = vec_absmax<BF16>(c1, held[k * kOpThreads + t]);
+    for (int k = 0; k < KL; ++k) c1 = vec_absmax<BF16>(c1, held[k * NT + t]);
     uint32_t m = umax(a0, umax(acc_to_f32bits<BF16>(c0), acc_to_f32bits<BF16>(c1)));
     if (b == 0)                                                    // elements after the last vector
-        for (int64_t e = nvec * vec_elems<BF16>() + t; e < n; e += kOpThreads) m = umax(m, elem_bits<BF16>(x, e) & 0x7FFFFFFFu);
-    m = block_max_bcast<kOpThreads>(m, red);
+        for (int64_t e = nvec * vec_elems<BF16>() + t; e < n; e += NT) m = umax(m, elem_bits<BF16>(x, e) & 0x7FFFFFFFu);
+    m = block_max_bcast<NT>(m, red);
 
     // grid barrier
     uint64_t *lines = (uint64_t *)(ws + kBarHeaderWords);
@@ -723,7 +733,7 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
     if (role == 2) return;                          // the released workgroups cast this one's slabs
     m = sh[1];
     uint64_t xres = kLineReleased;                  // (what no exchange returns: the line was 0 or GAVE_UP)
-    if (role == 1 && t < G && t != b)               // release: one line per thread (G <= kOpThreads)
+    if (role == 1 && t < G && t != b)               // release: one line per thread (G <= NT)
         xres = __hip_atomic_exchange(lines + (size_t)t * (kBarLineWords / 2), kLineReleased | m, __ATOMIC_RELAXED,
                                      __HIP_MEMORY_SCOPE_AGENT);
     const float s = OP == kOpFp8 ? scale_from_amax_bits<FMT>(m) : nv_tensor_scale(m);
@@ -733,16 +743,17 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
     }
 
     // pass 2: cast the held slabs, then re-read and cast the rest (vector indices: vbase + k * vstep)
-    const uint32_t vbase = (uint32_t)b * kOpThreads + t, vstep = step / 16u;
+    const uint32_t vbase = (uint32_t)b * NT + t, vstep = step / 16u;
     // NVFP4: one bit per held vector whose two estimates disagree. Each bit is pinned in a register
     // as soon as it is known (the empty asm), so that the compiler does not carry every vector's
     // inputs down to the fix-up below.
     uint32_t miss_w[2] = {0u, 0u};
     // Given-up slabs (see the barrier description above): the releaser publishes after its first
     // kPublishAt register slabs, when its exchanges have returned; the others read INFO after
-    // slab KR / 2, well after that, and use it only at the end, so that neither waits.
+    // slab kInfoReadAt, well after that, and use it only at the end, so that neither waits.
     uint32_t ng = 0, info = 0;                      // info: the high half of the own line
-    constexpr int kInfoReadAt = KR / 2;
+    constexpr int kPublishAt = OP == kOpFp8 ? kPublishAtFp8 : KR / 3;
+    constexpr int kInfoReadAt = OP == kOpFp8 ? KR / 2 : KR - 4;
     static_assert(kPublishAt + 8 <= kInfoReadAt && kInfoReadAt < KR, "INFO is read well after it is sent");
 #pragma unroll
     for (int k = 0; k < KR; ++k) {
@@ -776,7 +787,7 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
 #pragma unroll
     for (int k = 0; k < KL; ++k) {
         miss_w[(KR + k) >> 5] |= (uint32_t)op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + (KR + k) * vstep,
-                                                                       held[k * kOpThreads + t], s, nvtab)
+                                                                       held[k * NT + t], s, nvtab)
                                  << ((KR + k) & 31);
         if constexpr (OP == kOpNvfp4) asm volatile("" : "+v"(miss_w[(KR + k) >> 5]));
     }
@@ -848,7 +859,7 @@ __global__ __launch_bounds__(kOpThreads) void per_tensor_onepass_kernel(
     }
     if (role == 1) {
         if constexpr (OP == kOpFp8)          // NVFP4 sizes are whole vectors (n % 16 == 0)
-            for (int64_t e = nvec * vec_elems<BF16>() + t; e < n; e += kOpThreads)
+            for (int64_t e = nvec * vec_elems<BF16>() + t; e < n; e += NT)
                 q[e] = (uint8_t)cast1<FMT>(__uint_as_float(elem_bits<BF16>(x, e)), s);
         if (t == 0) {
             if (amax_out) *amax_out = __uint_as_float(m);
@@ -1011,10 +1022,10 @@ int launch_nvfp4_onepass(const void *x, int dtype, int64_t n, uint8_t *q, uint8_
                          float *tensor_scale, float *amax_out, int32_t *nonfinite, int grid, hipStream_t s) {
     const int64_t nvec = vec_count(n, dtype);
     if (dtype == QF8_IN_BF16)
-        hipLaunchKernelGGL((per_tensor_onepass_kernel<true, kE4M3, kOpNvfp4>), dim3(grid), dim3(kOpThreads), 0, s, x, n,
+        hipLaunchKernelGGL((per_tensor_onepass_kernel<true, kE4M3, kOpNvfp4>), dim3(grid), dim3(op_threads<kOpNvfp4>()), 0, s, x, n,
                            nvec, q, s_blk, ws, amax_out, tensor_scale, nonfinite, (uint32_t *)nullptr);
     else
-        hipLaunchKernelGGL((per_tensor_onepass_kernel<false, kE4M3, kOpNvfp4>), dim3(grid), dim3(kOpThreads), 0, s, x,
+        hipLaunchKernelGGL((per_tensor_onepass_kernel<false, kE4M3, kOpNvfp4>), dim3(grid), dim3(op_threads<kOpNvfp4>()), 0, s, x,
                            n, nvec, q, s_blk, ws, amax_out, tensor_scale, nonfinite, (uint32_t *)nullptr);
     return status_after_launch();
 }

@@ -341,7 +341,7 @@ def test_nvfp4_single_pass_give_up(gradient_full, ticks):
 
 
 def test_nvfp4_single_pass_beside_cu_holders(gradient_full):
-    """The single-pass NVFP4 kernel (16384x4096 BF16, 120 MiB held on chip) while a kernel on
+    """The single-pass NVFP4 kernel (16384x4096 BF16, 108 MiB held on chip) while a kernel on
     another stream holds 48 KiB of LDS on 8 CUs for 3 ms: about as many waiters give up, per
     shader engine, and the released workgroups cast their slabs. Same bytes as the oracle, the
     workspace left zero, and the call ends in under 1 ms (events on its stream)."""
