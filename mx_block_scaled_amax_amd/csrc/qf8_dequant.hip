@@ -22,8 +22,9 @@
 //
 // Work: a unit is 8 consecutive codes for BF16 output, 4 for FP32 output, 16 with statistics (4
 // when a group's rows are only a multiple of 4 or 8 long), always inside one row, one group and
-// one MX block, so its scale is looked up once. A thread takes 32 codes per iteration
-// (consecutive threads on consecutive units), decodes with the gfx950 fp8/bf8 -> f32 converts
+// one MX block, so its scale is looked up once. A thread takes 32 codes per iteration (16 with
+// statistics), consecutive threads on consecutive units, and loads the next iteration's codes
+// and inputs before the current one's arithmetic; decodes with the gfx950 fp8/bf8 -> f32 converts
 // (exact), de-scales (MX: ldexp; groups: IEEE division; one tensor scale: a 256-entry LDS table
 // of decode(c) / S built per workgroup) and stores each 8-code BF16 or 4-code FP32 unit as one
 // 16-byte piece, consecutive lanes on consecutive pieces. With statistics, the fp64
@@ -157,6 +158,39 @@ __device__ __forceinline__ void load_x(const void *x, uint32_t u, float *xv) {
         }
     }
 }
+// The same in two steps: the raw dwords (BF16 pairs or fp32 bits) of unit u, loaded a loop
+// iteration ahead, then their fp32 values.
+template <int XK, int W>
+constexpr int x_raw_dwords() { return XK == kBF16 ? W / 2 : W; }
+template <int XK, int W>
+__device__ __forceinline__ void load_x_raw(const void *x, uint32_t u, uint32_t *w) {
+    static_assert(W == 4 || W == 16, "statistics units");
+    constexpr int D = x_raw_dwords<XK, W>();
+    const uint32_t *p = (const uint32_t *)x + (size_t)u * D;
+    if constexpr (D % 4 == 0) {
+#pragma unroll
+        for (int k = 0; k < D / 4; ++k) {
+            const uint4 a0 = ((const uint4 *)p)[k];
+            w[4 * k] = a0.x; w[4 * k + 1] = a0.y; w[4 * k + 2] = a0.z; w[4 * k + 3] = a0.w;
+        }
+    } else {
+        const uint2 a0 = *(const uint2 *)p;
+        w[0] = a0.x; w[1] = a0.y;
+    }
+}
+template <int XK, int W>
+__device__ __forceinline__ void x_from_raw(const uint32_t *w, float *xv) {
+    if constexpr (XK == kBF16) {
+#pragma unroll
+        for (int k = 0; k < W / 2; ++k) {
+            xv[2 * k] = __uint_as_float(w[k] << 16);
+            xv[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < W; ++k) xv[k] = __uint_as_float(w[k]);
+    }
+}
 template <int XK>
 __device__ __forceinline__ float load_x1(const void *x, int64_t e) {
     if constexpr (XK == kBF16) return __uint_as_float((uint32_t)((const uint16_t *)x)[e] << 16);
@@ -281,7 +315,9 @@ template <int FMT, int MODE, int OUTK, int XK, int W>
 __global__ __launch_bounds__(kDqThreads) void dequant_kernel(DqArgs a) {
     constexpr bool STATS = XK != kNone;
     static_assert(W == 16 || W == 8 || W == 4, "16-, 8- or 4-code units");
-    constexpr int UPT = 32 / W;                 // units per thread and iteration: 32 codes
+    // units per thread and iteration: 32 codes, or 16 with the statistics (two iterations' raw
+    // inputs are held at once, below)
+    constexpr int UPT = (STATS ? 16 : 32) / W;
     constexpr int ND = W / 4;                     // dwords of codes per unit
     __shared__ float tab[MODE == kModeScaled ? 256 : 1];
     float s_tensor = 1.0f;
@@ -294,9 +330,11 @@ __global__ __launch_bounds__(kDqThreads) void dequant_kernel(DqArgs a) {
     }
     Acc acc;
     const uint32_t stride = gridDim.x * kDqThreads * UPT;
-    for (uint32_t base = blockIdx.x * kDqThreads * UPT; base < a.units; base += stride) {
-        uint32_t codes[UPT][ND];
-        float xv[UPT][W];
+    constexpr int XD = STATS ? x_raw_dwords<XK == kNone ? kBF16 : XK, W == 8 ? 16 : W>() : 1;
+    // one iteration's codes and raw x, loaded one iteration ahead of their arithmetic (two
+    // buffers, the loop unrolled by two), so that the loads of the next 32 codes per thread are in
+    // flight during the current ones' de-scaling and statistics
+    auto load_iter = [&](uint32_t base, uint32_t (&codes)[UPT][ND], uint32_t (&xr)[UPT][XD]) {
 #pragma unroll
         for (int j = 0; j < UPT; ++j) {
             const uint32_t u = base + j * kDqThreads + threadIdx.x;
@@ -312,9 +350,11 @@ __global__ __launch_bounds__(kDqThreads) void dequant_kernel(DqArgs a) {
                 } else {
                     codes[j][0] = __builtin_nontemporal_load((const uint32_t *)a.q + u);
                 }
-                if constexpr (STATS) load_x<XK, W>(a.x, u, xv[j]);
+                if constexpr (STATS) load_x_raw<XK, W>(a.x, u, xr[j]);
             }
         }
+    };
+    auto process = [&](uint32_t base, const uint32_t (&codes)[UPT][ND], const uint32_t (&xr)[UPT][XD]) {
 #pragma unroll
         for (int j = 0; j < UPT; ++j) {
             const uint32_t u = base + j * kDqThreads + threadIdx.x;
@@ -334,12 +374,25 @@ __global__ __launch_bounds__(kDqThreads) void dequant_kernel(DqArgs a) {
             }
             store_out<OUTK, W>(a.out, u, v);
             if constexpr (STATS) {
+                float xv[W];
+                x_from_raw<XK, W>(xr[j], xv);
                 bool sat[W];
 #pragma unroll
-                for (int k = 0; k < W; ++k) sat[k] = saturates<FMT, MODE>(xv[j][k], us);
-                acc_add_unit<W>(acc, xv[j], v, sat);
+                for (int k = 0; k < W; ++k) sat[k] = saturates<FMT, MODE>(xv[k], us);
+                acc_add_unit<W>(acc, xv, v, sat);
             }
         }
+    };
+    uint32_t c0[UPT][ND], c1[UPT][ND], x0[UPT][XD], x1[UPT][XD];
+    uint32_t base = blockIdx.x * kDqThreads * UPT;
+    if (base < a.units) load_iter(base, c0, x0);
+    for (; base < a.units; base += 2 * stride) {
+        const uint32_t b1 = base + stride;
+        if (b1 < a.units) load_iter(b1, c1, x1);
+        process(base, c0, x0);
+        if (b1 >= a.units) break;
+        if (b1 + stride < a.units) load_iter(b1 + stride, c0, x0);
+        process(b1, c1, x1);
     }
     if (MODE == kModeScaled && blockIdx.x == 0) {            // the last n % W elements
         const int64_t e = (int64_t)a.units * W + threadIdx.x;
