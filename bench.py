@@ -563,7 +563,7 @@ def run_suite(args):
     nvt = torch.empty(1, dtype=torch.float32, device="cuda")
     nva = torch.empty(1, dtype=torch.float32, device="cuda")
     wsn = qf8.workspace(xg)
-    res.append(_summ("nvfp4 16384x4096 bf16 (amax pass + cast)", 2 * N + N // 2 + N // 16,
+    res.append(_summ("nvfp4 16384x4096 bf16 (measured amax, single pass)", 2 * N + N // 2 + N // 16,
                      _timed(torch, stream, [PreCall(L.quantize_nvfp4, vp(xg), 0, ROWS, COLS, None, vp(f4r), vp(nvs),
                                                     vp(nvt), vp(nva), None, vp(wsn), wsn.numel(), sp)], reps, warm)))
     res.append(_summ("nvfp4 16384x4096 bf16 (caller amax, one read)", 2 * N + N // 2 + N // 16,
