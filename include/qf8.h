@@ -298,7 +298,8 @@ qf8_status quantize_nvfp4(const void *x, qf8_dtype dtype, int64_t rows, int64_t 
  * to device memory. Sums are fp64 over the finite elements of x, reduced in a fixed order (the
  * same input gives the same bits); SQNR = 10 log10(signal / noise), zero-rate = zeroed /
  * nonzero (or / count). With stats, ws (qf8_workspace_bytes) holds per-workgroup partials.
- * At least one of out and stats must be given. q, out and x are 16-byte aligned; stats 8-byte.
+ * At least one of out and stats must be given. q, out and x are 16-byte aligned; stats 8-byte;
+ * out overlaps neither q nor x.
  * Sizes: rows * cols < 2^33. */
 typedef enum qf8_out_dtype { QF8_OUT_BF16 = 0, QF8_OUT_FP32 = 1 } qf8_out_dtype;
 

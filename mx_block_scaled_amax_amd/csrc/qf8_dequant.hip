@@ -22,16 +22,21 @@
 //
 // Work: a unit is 8 consecutive codes for BF16 output, 4 for FP32 output, 16 with statistics (4
 // when a group's rows are only a multiple of 4 or 8 long), always inside one row, one group and
-// one MX block, so its scale is looked up once. A thread takes 32 codes per iteration (16 with
-// statistics), consecutive threads on consecutive units, and loads the next iteration's codes
-// and inputs before the current one's arithmetic; decodes with the gfx950 fp8/bf8 -> f32 converts
-// (exact), de-scales (MX: ldexp; groups: IEEE division; one tensor scale: a 256-entry LDS table
-// of decode(c) / S built per workgroup) and stores each 8-code BF16 or 4-code FP32 unit as one
-// 16-byte piece, consecutive lanes on consecutive pieces. With statistics, the fp64
-// terms go to 4 independent running sums per thread (short dependency chains); each
-// workgroup reduces its sums and counts in a fixed order into a 64-byte partial in the
-// workspace, and one workgroup folds the partials in a fixed order: the same input always gives
-// the same bits.
+// one MX block, so its scale is looked up once. A workgroup tile is 256 threads x 32 codes (16
+// with statistics), consecutive threads on consecutive units; a workgroup walks its tiles a grid
+// stride apart and loads the next tile's codes, inputs and scale words before the current one's
+// arithmetic, with only uniform branches and unconditional loads in that loop so that the
+// compiler's wait counts stay exact. Codes decode with the gfx950 fp8/bf8 -> f32 converts
+// (exact) and de-scale (MX: times 2^X; groups: IEEE division; one tensor scale: a 256-entry LDS
+// table of decode(c) / S built per workgroup); each 8-code BF16 or 4-code FP32 unit leaves as one
+// 16-byte store, consecutive lanes on consecutive pieces. With statistics, whole tiles sum
+// without a per-element Inf/NaN filter (a wave whose x holds one starts over with the filter),
+// the fp64 terms go to 4 independent running sums per thread, and the counts are popcounts of
+// wave ballots on the scalar unit; each workgroup reduces its sums and counts in a fixed order
+// into a 64-byte partial in the workspace, and one workgroup folds the partials in a fixed order:
+// the same input always gives the same bits.
+#include <type_traits>
+
 #include "qf8_device.h"
 #include "qf8_internal.h"
 #include "../../include/qf8.h"
@@ -42,10 +47,12 @@ namespace {
 constexpr int kDqThreads = 256;
 constexpr int kDqMaxGrid = 16384;
 constexpr int kStatsGrid = 1024;                 // workgroups (= 64-byte partials) with statistics
+static_assert(kStatsGrid % kDqThreads == 0, "whole partials per thread in the final fold");
 static_assert(kStatsGrid * 64 <= kMaxStreamGrid * 4, "partials fit the workspace partial region");
 
 enum { kModeScaled = 0, kModeBlock = 1, kModeMx = 2 };
 enum { kNone = 0, kBF16 = 1, kFP32 = 2 };
+
 
 struct StatsPart {                               // same layout as qf8_error_stats
     double signal, noise;
@@ -129,6 +136,34 @@ __device__ __forceinline__ void acc_add_unit(Acc &acc, const float *x, const flo
         acc.saturated += (fin && sat[k]) ? 1u : 0u;
     }
 }
+
+// Counts of one wave, kept as wave-uniform sums of ballot masks (on the scalar unit).
+struct WaveCounts {
+    uint32_t nonzero = 0, zeroed = 0, saturated = 0;
+};
+
+// The statistics of one unit for a whole wave in step, without the Inf/NaN filter: a non-finite
+// x makes the lane's signal sum non-finite (a finite BF16/FP32 x^2 is below 2^256, so a finite sum
+// of fewer than 2^33 of them stays finite), and a wave that finds one starts over with
+// acc_add_unit. Counts go to wave-uniform sums: only where every lane of the wave takes the same
+// path.
+template <int W>
+__device__ __forceinline__ void acc_add_unit_fast(Acc &acc, WaveCounts &wc, const float *x, const float *xh,
+                                                  const bool *sat) {
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+        const double xd = (double)x[k], d = xd - (double)xh[k];
+        acc.signal[k & 3] += xd * xd;
+        acc.noise[k & 3] += d * d;
+        const uint64_t nz = __builtin_amdgcn_ballot_w64(x[k] != 0.0f), z = __builtin_amdgcn_ballot_w64(xh[k] == 0.0f);
+        wc.nonzero += (uint32_t)__builtin_popcountll(nz);
+        wc.zeroed += (uint32_t)__builtin_popcountll(nz & z);
+        wc.saturated += (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(sat[k]));
+    }
+    acc.count += W;
+}
+
+__device__ __forceinline__ bool finite_f64(double v) { return fabs(v) <= 1.79769313486231570815e+308; }
 
 // W consecutive elements of x (W = 4 or 16: the units of the statistics) of unit u.
 template <int XK, int W>
@@ -229,11 +264,12 @@ __device__ __forceinline__ void store1(void *out, int64_t e, float v) {
     else if constexpr (OUTK == kFP32) ((float *)out)[e] = v;
 }
 
-// How one unit is de-scaled: a scale factor S (divide) or an E8M0 byte (ldexp).
+// How one unit is de-scaled: a scale factor S (divide), or for MX the multiplier 2^X (an exact
+// power of two, subnormal for X = -127; fp32 denormals are kept, so the product rounds exactly as
+// ldexp does).
 struct UnitScale {
-    float s;      // S, or F8max * 2^X for MX saturation tests
-    int xexp;     // X (MX)
-    bool nan;     // MX byte 0xFF
+    float s;      // S; MX: F8max * 2^X for the saturation test, +Inf for the byte 0xFF
+    float m;      // MX: 2^X, NaN for the byte 0xFF (every element of the block de-scales to NaN)
 };
 
 // Row of unit u (u < 2^31) without a division instruction sequence: the multiplier and shift are
@@ -242,32 +278,44 @@ __device__ __forceinline__ uint32_t unit_row(const DqArgs &a, uint32_t u) {
     return (uint32_t)(((uint64_t)u * a.upr_mul) >> a.upr_shift);
 }
 
-// Scale of unit u (W codes, all in one row and one group: cols % W == 0, W divides 32 and 128).
-template <int FMT, int MODE, int W>
-__device__ __forceinline__ UnitScale unit_scale(const DqArgs &a, uint32_t u, float s_tensor) {
-    UnitScale us{s_tensor, 0, false};
+// The raw scale word of unit u (W codes, all in one row and one group: cols % W == 0, W divides
+// 32 and 128): the fp32 bits of its group scale, or its E8M0 byte. Loaded with the unit's codes.
+template <int MODE, int W>
+__device__ __forceinline__ uint32_t load_scale_raw(const DqArgs &a, uint32_t u) {
     if constexpr (MODE == kModeBlock) {
         const uint32_t r = unit_row(a, u), c = (u - r * a.upr) * W;
-        us.s = a.scale[(size_t)(r >> a.br_shift) * a.gcols + (c >> 7)];
+        return __float_as_uint(a.scale[(size_t)(r >> a.br_shift) * a.gcols + (c >> 7)]);
     } else if constexpr (MODE == kModeMx) {
         const uint32_t r = unit_row(a, u), c = (u - r * a.upr) * W;
-        const uint32_t b = a.sb[(size_t)r * (a.upr * W / 32) + (c >> 5)];
-        us.nan = b == 0xFFu;
-        us.xexp = (int)b - 127;
-        us.s = __builtin_ldexpf(F8<FMT>::kMax, us.xexp);
+        return a.sb[(size_t)r * (a.upr * W / 32) + (c >> 5)];
+    } else {
+        return 0u;
+    }
+}
+
+template <int FMT, int MODE>
+__device__ __forceinline__ UnitScale unit_scale(uint32_t raw, float s_tensor) {
+    UnitScale us{s_tensor, 1.0f};
+    if constexpr (MODE == kModeBlock) {
+        us.s = __uint_as_float(raw);
+    } else if constexpr (MODE == kModeMx) {
+        const int xexp = (int)raw - 127;
+        const bool nan = raw == 0xFFu;
+        us.m = nan ? __uint_as_float(0x7FC00000u) : __builtin_ldexpf(1.0f, xexp);
+        us.s = nan ? __builtin_inff() : __builtin_ldexpf(F8<FMT>::kMax, xexp);
     }
     return us;
 }
 
 template <int MODE>
 __device__ __forceinline__ float descale(float v, const UnitScale &us) {
-    if constexpr (MODE == kModeMx) return us.nan ? __uint_as_float(0x7FC00000u) : __builtin_ldexpf(v, us.xexp);
+    if constexpr (MODE == kModeMx) return v * us.m;
     else return v / us.s;
 }
 
 template <int FMT, int MODE>
 __device__ __forceinline__ bool saturates(float x, const UnitScale &us) {
-    if constexpr (MODE == kModeMx) return !us.nan && fabsf(x) > us.s;
+    if constexpr (MODE == kModeMx) return fabsf(x) > us.s;
     else return fabsf(x * us.s) > F8<FMT>::kMax;
 }
 
@@ -278,13 +326,16 @@ __device__ __forceinline__ T wave_sum(T v) {
     return v;
 }
 
-// Fixed-order workgroup sum of the accumulator into one partial (thread 0 writes it).
-__device__ void block_store_partial(const Acc &acc, StatsPart *dst) {
+// Fixed-order workgroup sum of the accumulator into one partial (thread 0 writes it). The
+// wave-uniform counts of the whole-tile passes are added once per wave.
+__device__ void block_store_partial(const Acc &acc, const WaveCounts &wcnt, StatsPart *dst) {
     __shared__ double sd[2][kDqThreads / 64];
     __shared__ uint32_t sc[5][kDqThreads / 64];
     const double sg = wave_sum(acc.signal_sum()), ns = wave_sum(acc.noise_sum());
-    const uint32_t c0 = wave_sum(acc.count), c1 = wave_sum(acc.nonzero), c2 = wave_sum(acc.zeroed),
-                   c3 = wave_sum(acc.saturated), c4 = wave_sum(acc.nonfinite);
+    const uint32_t c0 = wave_sum(acc.count), c4 = wave_sum(acc.nonfinite);
+    const uint32_t c1 = wave_sum(acc.nonzero) + __builtin_amdgcn_readfirstlane(wcnt.nonzero),
+                   c2 = wave_sum(acc.zeroed) + __builtin_amdgcn_readfirstlane(wcnt.zeroed),
+                   c3 = wave_sum(acc.saturated) + __builtin_amdgcn_readfirstlane(wcnt.saturated);
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) {
         sd[0][w] = sg; sd[1][w] = ns;
@@ -302,23 +353,18 @@ __device__ void block_store_partial(const Acc &acc, StatsPart *dst) {
     }
 }
 
-// W codes per unit. De-scaling alone takes 8 or 4, so that each lane moves one 16-byte piece of the
-// output and consecutive lanes move consecutive pieces: 8 codes (an 8-byte load) make 16 bytes of
-// BF16, 4 codes 16 bytes of FP32, and whole 16-byte outputs leave as non-temporal stores (a lane
-// writing 32 bytes as two 16-byte stores leaves every store instruction half-dense over its span,
-// which measured ~10% slower for this stream). With the statistics, whose fp64 terms make the
-// kernel VALU-bound, 16-code units (one 16-byte load of codes) halve the per-unit overhead.
-// 4-code units also serve rows that are only a multiple of 4 codes long (8-byte BF16 stores,
-// cached so that L2 merges them). With one scale factor the workgroup first tabulates
-// fl32(decode(c) / S) for all 256 codes in LDS, so an element costs a table read, not a division.
+template <int P> using Pass = std::integral_constant<int, P>;
+enum { kWhole = 0, kPart = 1, kRedo = 2 };   // a whole tile, the partial last tile, a statistics re-run
+
 template <int FMT, int MODE, int OUTK, int XK, int W>
 __global__ __launch_bounds__(kDqThreads) void dequant_kernel(DqArgs a) {
     constexpr bool STATS = XK != kNone;
     static_assert(W == 16 || W == 8 || W == 4, "16-, 8- or 4-code units");
-    // units per thread and iteration: 32 codes, or 16 with the statistics (two iterations' raw
-    // inputs are held at once, below)
+    // units per thread and tile: 32 codes, or 16 with the statistics (two tiles' raw inputs are
+    // held at once, below)
     constexpr int UPT = (STATS ? 16 : 32) / W;
     constexpr int ND = W / 4;                     // dwords of codes per unit
+    constexpr uint32_t kTile = kDqThreads * UPT;  // units of one workgroup tile
     __shared__ float tab[MODE == kModeScaled ? 256 : 1];
     float s_tensor = 1.0f;
     if constexpr (MODE == kModeScaled) {
@@ -329,75 +375,139 @@ __global__ __launch_bounds__(kDqThreads) void dequant_kernel(DqArgs a) {
         __syncthreads();
     }
     Acc acc;
-    const uint32_t stride = gridDim.x * kDqThreads * UPT;
+    WaveCounts wcnt;
+    const uint32_t stride = gridDim.x * kTile;
     constexpr int XD = STATS ? x_raw_dwords<XK == kNone ? kBF16 : XK, W == 8 ? 16 : W>() : 1;
-    // one iteration's codes and raw x, loaded one iteration ahead of their arithmetic (two
-    // buffers, the loop unrolled by two), so that the loads of the next 32 codes per thread are in
-    // flight during the current ones' de-scaling and statistics
-    auto load_iter = [&](uint32_t base, uint32_t (&codes)[UPT][ND], uint32_t (&xr)[UPT][XD]) {
+    // one tile's inputs of this thread: codes, raw x and raw scale word of each of its units
+    struct In {
+        uint32_t c[UPT][ND];
+        uint32_t x[UPT][XD];
+        uint32_t s[UPT];
+    };
+    auto load = [&](auto pass, uint32_t base, In &in) {
+        constexpr int P = decltype(pass)::value;
 #pragma unroll
         for (int j = 0; j < UPT; ++j) {
             const uint32_t u = base + j * kDqThreads + threadIdx.x;
-            if (u < a.units) {
+            if (P == kWhole || u < a.units) {
                 if constexpr (W == 16) {
                     typedef unsigned int v4u __attribute__((ext_vector_type(4)));
                     const v4u c = __builtin_nontemporal_load((const v4u *)a.q + u);
-                    codes[j][0] = c.x; codes[j][1] = c.y; codes[j][2] = c.z; codes[j][3] = c.w;
+                    in.c[j][0] = c.x; in.c[j][1] = c.y; in.c[j][2] = c.z; in.c[j][3] = c.w;
                 } else if constexpr (W == 8) {
                     typedef unsigned int v2u __attribute__((ext_vector_type(2)));
                     const v2u c = __builtin_nontemporal_load((const v2u *)a.q + u);
-                    codes[j][0] = c.x; codes[j][1] = c.y;
+                    in.c[j][0] = c.x; in.c[j][1] = c.y;
                 } else {
-                    codes[j][0] = __builtin_nontemporal_load((const uint32_t *)a.q + u);
+                    in.c[j][0] = __builtin_nontemporal_load((const uint32_t *)a.q + u);
                 }
-                if constexpr (STATS) load_x_raw<XK, W>(a.x, u, xr[j]);
+                if constexpr (STATS) load_x_raw<XK, W>(a.x, u, in.x[j]);
+                in.s[j] = load_scale_raw<MODE, W>(a, u);
             }
         }
     };
-    auto process = [&](uint32_t base, const uint32_t (&codes)[UPT][ND], const uint32_t (&xr)[UPT][XD]) {
+    auto process = [&](auto pass, uint32_t base, const In &in) {
+        constexpr int P = decltype(pass)::value;
 #pragma unroll
         for (int j = 0; j < UPT; ++j) {
             const uint32_t u = base + j * kDqThreads + threadIdx.x;
-            if (u >= a.units) continue;
-            const UnitScale us = unit_scale<FMT, MODE, W>(a, u, s_tensor);
+            if (P != kWhole && u >= a.units) continue;
+            const UnitScale us = unit_scale<FMT, MODE>(in.s[j], s_tensor);
             float v[W];
 #pragma unroll
             for (int d = 0; d < ND; ++d) {
                 if constexpr (MODE == kModeScaled) {
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) v[4 * d + k] = tab[(codes[j][d] >> (8 * k)) & 0xFFu];
+                    for (int k = 0; k < 4; ++k) v[4 * d + k] = tab[(in.c[j][d] >> (8 * k)) & 0xFFu];
                 } else {
-                    decode4<FMT>(codes[j][d], v + 4 * d);
+                    decode4<FMT>(in.c[j][d], v + 4 * d);
 #pragma unroll
                     for (int k = 0; k < 4; ++k) v[4 * d + k] = descale<MODE>(v[4 * d + k], us);
                 }
             }
-            store_out<OUTK, W>(a.out, u, v);
+            if constexpr (P != kRedo) store_out<OUTK, W>(a.out, u, v);
             if constexpr (STATS) {
                 float xv[W];
-                x_from_raw<XK, W>(xr[j], xv);
+                x_from_raw<XK, W>(in.x[j], xv);
                 bool sat[W];
 #pragma unroll
                 for (int k = 0; k < W; ++k) sat[k] = saturates<FMT, MODE>(xv[k], us);
-                acc_add_unit<W>(acc, xv, v, sat);
+                if constexpr (P == kWhole) acc_add_unit_fast<W>(acc, wcnt, xv, v, sat);
+                else acc_add_unit<W>(acc, xv, v, sat);
             }
         }
     };
-    uint32_t c0[UPT][ND], c1[UPT][ND], x0[UPT][XD], x1[UPT][XD];
-    uint32_t base = blockIdx.x * kDqThreads * UPT;
-    if (base < a.units) load_iter(base, c0, x0);
-    for (; base < a.units; base += 2 * stride) {
-        const uint32_t b1 = base + stride;
-        if (b1 < a.units) load_iter(b1, c1, x1);
-        process(base, c0, x0);
-        if (b1 >= a.units) break;
-        if (b1 + stride < a.units) load_iter(b1 + stride, c0, x0);
-        process(b1, c1, x1);
+    // Whole tiles first, each tile's loads issued one tile ahead of its arithmetic (two buffers,
+    // unrolled by two). Every branch here is uniform over the workgroup and the loads and their
+    // uses are unconditional, so the compiler's wait counts stay exact: the next tile's loads
+    // remain in flight while the current one is de-scaled. Only a workgroup's last tile can be
+    // partial (the tiles of one workgroup are a grid stride apart).
+    In i0, i1;
+    uint32_t base = blockIdx.x * kTile;
+    if (base + kTile <= a.units) {
+        load(Pass<kWhole>(), base, i0);
+        if constexpr (STATS) {
+            // Several tiles per workgroup (the grid is capped). One processing site per buffer:
+            // past the workgroup's last whole tile the prefetch reads tile 0 again (an L2 hit,
+            // never used). With the exit path processing a buffer as well, the compiler hoists
+            // the arithmetic shared by both paths above the exit test and keeps twice the
+            // registers live; the empty asm keeps the loads from sinking below the arithmetic.
+            for (;;) {
+                const uint32_t b1 = base + stride;
+                const bool more1 = b1 + kTile <= a.units;
+                load(Pass<kWhole>(), more1 ? b1 : 0u, i1);
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                process(Pass<kWhole>(), base, i0);
+                base = b1;
+                if (!more1) break;
+                const uint32_t b2 = b1 + stride;
+                const bool more2 = b2 + kTile <= a.units;
+                load(Pass<kWhole>(), more2 ? b2 : 0u, i0);
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_sched_barrier(0);
+                process(Pass<kWhole>(), b1, i1);
+                base = b2;
+                if (!more2) break;
+            }
+        } else {
+            // Mostly one tile per workgroup: the exit path processes the buffer itself, so no
+            // workgroup fetches a tile it does not use.
+            for (;;) {
+                const uint32_t b1 = base + stride;
+                if (b1 + kTile > a.units) { process(Pass<kWhole>(), base, i0); base = b1; break; }
+                load(Pass<kWhole>(), b1, i1);
+                __builtin_amdgcn_sched_barrier(0);
+                process(Pass<kWhole>(), base, i0);
+                const uint32_t b2 = b1 + stride;
+                if (b2 + kTile > a.units) { process(Pass<kWhole>(), b1, i1); base = b2; break; }
+                load(Pass<kWhole>(), b2, i0);
+                __builtin_amdgcn_sched_barrier(0);
+                process(Pass<kWhole>(), b1, i1);
+                base = b2;
+            }
+        }
+    }
+    if (base < a.units) {
+        load(Pass<kPart>(), base, i0);
+        process(Pass<kPart>(), base, i0);
+    }
+    if constexpr (STATS) {
+        if (__builtin_amdgcn_ballot_w64(!finite_f64(acc.signal_sum())) != 0u) {
+            // Inf/NaN in this wave's x: the whole tiles above took them unfiltered, so the wave
+            // starts over on every tile with the per-element filter (rare; no stores)
+            acc = Acc();
+            wcnt = WaveCounts();
+            for (uint32_t b = blockIdx.x * kTile; b < a.units; b += stride) {
+                load(Pass<kRedo>(), b, i0);
+                process(Pass<kRedo>(), b, i0);
+            }
+        }
     }
     if (MODE == kModeScaled && blockIdx.x == 0) {            // the last n % W elements
         const int64_t e = (int64_t)a.units * W + threadIdx.x;
         if (e < a.n) {
-            const UnitScale us{s_tensor, 0, false};
+            const UnitScale us{s_tensor, 1.0f};
             const float xh = tab[a.q[e]];
             store1<OUTK>(a.out, e, xh);
             if constexpr (STATS) {
@@ -407,36 +517,49 @@ __global__ __launch_bounds__(kDqThreads) void dequant_kernel(DqArgs a) {
             }
         }
     }
-    if constexpr (STATS) block_store_partial(acc, a.parts + blockIdx.x);
+    if constexpr (STATS) block_store_partial(acc, wcnt, a.parts + blockIdx.x);
 }
 
+// One workgroup folds the partials in a fixed order: thread t takes partials t, t + 256, ...
+// (all loads in flight at once), then a shuffle tree in each wave and the waves in order.
 __global__ __launch_bounds__(kDqThreads) void stats_finalize_kernel(const StatsPart *parts, int nparts,
                                                                     qf8_error_stats *out) {
+    constexpr int kPer = kStatsGrid / kDqThreads;
+    StatsPart p[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        const int i = (int)threadIdx.x + r * kDqThreads;
+        p[r] = parts[i < nparts ? i : 0];               // beyond nparts: partial 0 read, not used
+    }
     double sg = 0.0, ns = 0.0;
     uint64_t c[5] = {0, 0, 0, 0, 0};
-    for (int i = threadIdx.x; i < nparts; i += kDqThreads) {
-        const StatsPart p = parts[i];
-        sg += p.signal; ns += p.noise;
-        c[0] += p.count; c[1] += p.nonzero; c[2] += p.zeroed; c[3] += p.saturated; c[4] += p.nonfinite;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {                   // + 0 for the unused ones (sums are >= 0)
+        const bool in = (int)threadIdx.x + r * kDqThreads < nparts;
+        sg += in ? p[r].signal : 0.0; ns += in ? p[r].noise : 0.0;
+        c[0] += in ? p[r].count : 0; c[1] += in ? p[r].nonzero : 0; c[2] += in ? p[r].zeroed : 0;
+        c[3] += in ? p[r].saturated : 0; c[4] += in ? p[r].nonfinite : 0;
     }
-    __shared__ double sd[2][kDqThreads];
-    __shared__ uint64_t sc[5][kDqThreads];
-    sd[0][threadIdx.x] = sg; sd[1][threadIdx.x] = ns;
-    for (int k = 0; k < 5; ++k) sc[k][threadIdx.x] = c[k];
+    sg = wave_sum(sg);
+    ns = wave_sum(ns);
+#pragma unroll
+    for (int k = 0; k < 5; ++k) c[k] = wave_sum(c[k]);
+    __shared__ double sd[2][kDqThreads / 64];
+    __shared__ uint64_t sc[5][kDqThreads / 64];
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        sd[0][w] = sg; sd[1][w] = ns;
+#pragma unroll
+        for (int k = 0; k < 5; ++k) sc[k][w] = c[k];
+    }
     __syncthreads();
-    for (int half = kDqThreads / 2; half > 0; half >>= 1) {     // fixed-order tree
-        if ((int)threadIdx.x < half) {
-            sd[0][threadIdx.x] += sd[0][threadIdx.x + half];
-            sd[1][threadIdx.x] += sd[1][threadIdx.x + half];
-            for (int k = 0; k < 5; ++k) sc[k][threadIdx.x] += sc[k][threadIdx.x + half];
-        }
-        __syncthreads();
-    }
     if (threadIdx.x == 0) {
-        qf8_error_stats r;
-        r.signal = sd[0][0]; r.noise = sd[1][0];
-        r.count = (int64_t)sc[0][0]; r.nonzero = (int64_t)sc[1][0]; r.zeroed = (int64_t)sc[2][0];
-        r.saturated = (int64_t)sc[3][0]; r.nonfinite = (int64_t)sc[4][0]; r.reserved = 0;
+        qf8_error_stats r{};
+        for (int k = 0; k < kDqThreads / 64; ++k) {
+            r.signal += sd[0][k]; r.noise += sd[1][k];
+            r.count += (int64_t)sc[0][k]; r.nonzero += (int64_t)sc[1][k]; r.zeroed += (int64_t)sc[2][k];
+            r.saturated += (int64_t)sc[3][k]; r.nonfinite += (int64_t)sc[4][k];
+        }
         *out = r;
     }
 }

@@ -9,7 +9,8 @@ CPU oracle.
     (per-tensor 8192x8192, 1x128 8192x7168, 128x128 7168x18432, MX dual 16384x4096 rowwise and
     columnwise): the de-scaled tensors are bit-exact against the oracle on every element;
   * statistics: counts exact, fp64 sums within the summation-order bound (n * 2^-52 relative),
-    the same bits on repeated calls, non-finite inputs counted and excluded, empty input.
+    the same bits on repeated calls, non-finite inputs counted and excluded (in whole tiles of
+    several workgroups and in a partial one, BF16 and FP32 x, every scaling mode), empty input.
 """
 import numpy as np
 import pytest
@@ -209,6 +210,82 @@ def test_stats_nonfinite_and_empty():
     _, st = qf8.dequantize_scaled(e, O.E4M3, s, x=torch.empty(0, dtype=BF16, device="cuda"), want_out=False)
     assert qf8.stats_to_dict(st) == {"signal": 0.0, "noise": 0.0, "count": 0, "nonzero": 0, "zeroed": 0,
                                      "saturated": 0, "nonfinite": 0}
+
+
+def check_stats_nan_aware(got, want, what):
+    """check_stats where a NaN sum (a NaN de-scaled element next to a finite x) must be NaN in both."""
+    for k in ("signal", "noise"):
+        if np.isnan(want[k]):
+            assert np.isnan(got[k]), f"{what}: {k} {got[k]!r}, want NaN"
+    check_stats({k: (0.0 if k in ("signal", "noise") and np.isnan(want[k]) else v) for k, v in got.items()},
+                {k: (0.0 if k in ("signal", "noise") and np.isnan(v) else v) for k, v in want.items()}, what)
+
+
+# 2051 x 4128 = 529,158 sixteen-code units: 2067 whole workgroup tiles of 256 units and a partial
+# one of 6 units, over a statistics grid of 1024 workgroups (so workgroups 0..18 take three tiles)
+NF_ROWS, NF_COLS = 2051, 4128
+NF_TILE = 256 * 16
+
+
+def nonfinite_inputs(xdt):
+    """The clean x and a copy with Inf/NaN in whole tiles of several workgroups (first, second and
+    third tile of a workgroup) and in the partial last tile; Inf and NaN of both signs."""
+    x = small_tensor(NF_ROWS, NF_COLS, seed=11)
+    bad = x.copy()
+    flat = bad.reshape(-1)
+    n = flat.size
+    pos = {5 * NF_TILE + 77: 0x7F80, 5 * NF_TILE + 78: 0xFF80, 1724 * NF_TILE + 4000: 0x7FC0,
+           2051 * NF_TILE + 9: 0xFFC0, n - 5: 0x7F80}
+    for p, v in pos.items():
+        flat[p] = v
+    if xdt == "f32":
+        return bf16_to_f32(x), bf16_to_f32(bad)
+    return x, bad
+
+
+@pytest.mark.parametrize("xdt", ["bf16", "f32"])
+@pytest.mark.parametrize("mode", ["scaled", "block", "mx"])
+def test_stats_nonfinite_in_whole_tiles(mode, xdt):
+    """Inf/NaN inside whole tiles, where a wave sums without the per-element filter and starts
+    over once its sum turns non-finite, beside waves and workgroups without them, plus one in
+    the partial last tile (filtered per element). MX also puts the NaN scale byte 0xFF on one
+    block of a whole tile: its elements de-scale to NaN and make the noise sum NaN."""
+    x, bad = nonfinite_inputs(xdt)
+    xd, badd = to_device(x), to_device(bad)
+    fmt = O.E4M3
+    if mode == "scaled":
+        q, _, s = qf8.quantize_per_tensor(xd, fmt)
+        o, st = qf8.dequantize_scaled(q, fmt, s, out_dtype=F32, x=badd)
+        qh, sh = host(q), np.float32(s.item())
+        want = O.stats_scaled(bad, qh, fmt, sh)
+        want_o = O.dequant_scaled(qh, fmt, sh)
+    elif mode == "block":
+        q, sc = qf8.quantize_block(xd, 1, 128, fmt)[:2]
+        o, st = qf8.dequantize_block(q, 1, 128, fmt, sc, out_dtype=F32, x=badd)
+        qh, sch = host(q), host(sc)
+        want = O.stats_block(bad, qh, 1, 128, fmt, sch)
+        want_o = O.dequant_block(qh, 1, 128, fmt, sch)
+    else:
+        q, s_row = qf8.quantize_mx_dual(xd, fmt, O.ROUND_DOWN, colwise=False)[:2]
+        c0 = 700 * NF_TILE + 100                               # a block inside workgroup 700's first tile
+        s_row[c0 // NF_COLS, (c0 % NF_COLS) // 32] = 0xFF
+        o, st = qf8.dequantize_mx(q, s_row, fmt, out_dtype=F32, x=badd)
+        qh, sh = host(q), host(s_row)
+        want = O.stats_mx(bad, qh, sh, fmt)
+        want_o = O.dequant_mx(qh, sh, fmt)
+        assert np.isnan(want["noise"])
+    got = qf8.stats_to_dict(st)
+    check_stats_nan_aware(got, want, f"{mode} {xdt} non-finite")
+    assert got["nonfinite"] == 5
+    assert_f32_equal(f32_host(o), want_o, f"{mode} {xdt} output beside non-finite x")
+    # the same tensor without the non-finite values: the clean sums, all elements counted
+    _, st2 = (qf8.dequantize_scaled(q, fmt, s, x=xd, want_out=False) if mode == "scaled" else
+              qf8.dequantize_block(q, 1, 128, fmt, sc, x=xd, want_out=False) if mode == "block" else
+              qf8.dequantize_mx(q, s_row, fmt, x=xd, want_out=False))
+    want2 = (O.stats_scaled(x, qh, fmt, sh) if mode == "scaled" else O.stats_block(x, qh, 1, 128, fmt, sch)
+             if mode == "block" else O.stats_mx(x, qh, sh, fmt))
+    check_stats_nan_aware(qf8.stats_to_dict(st2), want2, f"{mode} {xdt} clean")
+    assert qf8.stats_to_dict(st2)["count"] == x.size
 
 
 def test_delayed_spike_saturation_counted():
