@@ -5,6 +5,8 @@ CPU oracle.
     and 22.4, random), FP32 output bit for bit and BF16 output equal to the oracle's fp32
     result rounded to nearest even;
   * MX: every code under every E8M0 byte (0xFF gives NaN);
+  * random codes and scales on a tensor large enough that every workgroup walks several tiles
+    (each scaling mode, sampled row bands bit-exact);
   * round trips through the GPU quantizers on ragged shapes and on the full workloads
     (per-tensor 8192x8192, 1x128 8192x7168, 128x128 7168x18432, MX dual 16384x4096 rowwise and
     columnwise): the de-scaled tensors are bit-exact against the oracle on every element;
@@ -210,6 +212,40 @@ def test_stats_nonfinite_and_empty():
     _, st = qf8.dequantize_scaled(e, O.E4M3, s, x=torch.empty(0, dtype=BF16, device="cuda"), want_out=False)
     assert qf8.stats_to_dict(st) == {"signal": 0.0, "noise": 0.0, "count": 0, "nonzero": 0, "zeroed": 0,
                                      "saturated": 0, "nonfinite": 0}
+
+
+# 16384 x 20480 codes: 41,943,040 eight-code units in 40,960 workgroup tiles of 1024 units on the
+# de-scaling grid of 16384 workgroups, so workgroups 0..8191 walk three tiles and the others two
+# (both halves of the prefetching loop and both of its exits). Row bands checked: one of the first
+# tiles, one of the second and the last rows (third tiles).
+BIG_ROWS, BIG_COLS = 16384, 20480
+BIG_BANDS = ((0, 64), (8000, 8064), (BIG_ROWS - 64, BIG_ROWS))
+
+
+@pytest.mark.parametrize("mode", ["scaled", "block", "mx"])
+def test_dequant_several_tiles_per_workgroup(mode):
+    """Random codes of every value (NaN codes included) and random scales: de-scaling alone, BF16
+    output, on a tensor large enough for several tiles per workgroup; sampled row bands bit-exact."""
+    rng = np.random.default_rng(77)
+    q = rng.integers(0, 256, (BIG_ROWS, BIG_COLS), dtype=np.uint8)
+    qd = to_device(q)
+    fmt = O.E5M2 if mode == "block" else O.E4M3
+    if mode == "scaled":
+        s = np.float32(rng.uniform(0.01, 1000.0))
+        o, _ = qf8.dequantize_scaled(qd, fmt, dev_scale(s), out_dtype=BF16)
+        want = lambda r0, r1: O.dequant_scaled(q[r0:r1], fmt, s)
+    elif mode == "block":
+        sc = (2.0 ** rng.integers(-20, 21, (BIG_ROWS, BIG_COLS // 128))).astype(np.float32)
+        sc *= rng.choice(np.array([1.0, 1.0, 3.0, 0.7], np.float32), sc.shape)
+        o, _ = qf8.dequantize_block(qd, 1, 128, fmt, to_device(sc), out_dtype=BF16)
+        want = lambda r0, r1: O.dequant_block(q[r0:r1], 1, 128, fmt, sc[r0:r1])
+    else:
+        sb = rng.integers(0, 256, (BIG_ROWS, BIG_COLS // 32), dtype=np.uint8)
+        o, _ = qf8.dequantize_mx(qd, to_device(sb), fmt, out_dtype=BF16)
+        want = lambda r0, r1: O.dequant_mx(q[r0:r1], sb[r0:r1], fmt)
+    for r0, r1 in BIG_BANDS:
+        assert_bf16_of(bf16_host(o[r0:r1]), want(r0, r1), f"{mode} rows {r0}..{r1}")
+    del o, qd
 
 
 def check_stats_nan_aware(got, want, what):
