@@ -266,8 +266,11 @@ __device__ __forceinline__ uint32_t nv_block_code(uint32_t amax_bits, float st) 
     const float p = a * st;                       // inf when the caller's tensor amax is far too small
     constexpr float kSixthLo = (float)((1.0 / 6.0) * (1.0 - 0x1p-20));
     constexpr float kSixthHi = (float)((1.0 / 6.0) * (1.0 + 0x1p-20));
-    const uint32_t clo = e4m3_code(fminf(p * kSixthLo, 448.0f));
-    const uint32_t chi = e4m3_code(fminf(p * kSixthHi, 448.0f));
+    // both estimates in one convert (byte 0 from below, byte 1 from above); the upper half of the
+    // result comes from p's bits and is not used
+    const uint32_t c2 = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(fminf(p * kSixthLo, 448.0f),
+                                                                 fminf(p * kSixthHi, 448.0f), __float_as_int(p), false);
+    const uint32_t clo = c2 & 0xFFu, chi = (c2 >> 8) & 0xFFu;
     if (clo == chi) return clo;
     // adjacent codes: 6 * their midpoint = 3 * (sum of the two values), exact in fp32
     const float t = 3.0f * (__builtin_amdgcn_cvt_f32_fp8(clo, 0) + __builtin_amdgcn_cvt_f32_fp8(chi, 0));

@@ -429,9 +429,15 @@ __global__ __launch_bounds__(kThreads) void nvfp4_kernel(const void *__restrict_
     for (int64_t base = (int64_t)blockIdx.x * kThreads; base < nblk; base += (int64_t)gridDim.x * kThreads) {
         const int64_t blk = base + threadIdx.x;
         const bool valid = blk < nblk;
+        // loads without a branch: a thread past the last block reads the last block again and
+        // zeroes what it read (nblk > 0)
         uint4 v[NV];
+        const int64_t lb = valid ? blk : nblk - 1;
 #pragma unroll
-        for (int j = 0; j < NV; ++j) v[j] = valid ? ld_stream(xv + blk * NV + j) : make_uint4(0, 0, 0, 0);
+        for (int j = 0; j < NV; ++j) {
+            const uint4 t = ld_stream(xv + lb * NV + j);
+            v[j] = valid ? t : make_uint4(0, 0, 0, 0);
+        }
         float f[16];
         if constexpr (BF16) {
 #pragma unroll
@@ -460,7 +466,9 @@ __global__ __launch_bounds__(kThreads) void nvfp4_kernel(const void *__restrict_
 #pragma unroll
         for (int w = 0; w < 2; ++w) {
             const float *g = f + 8 * w;
-            uint32_t lo = 0u, hi = 0u;
+            // every byte of lo and hi is written by its four converts: BF16 starts them from input
+            // words that are dead once unpacked instead of zeros
+            uint32_t lo = BF16 ? v[w].x : 0u, hi = BF16 ? v[w].y : 0u;
             lo = fp4_f32<0>(lo, g[0] * r.x, g[1] * r.x, 1.0f);
             lo = fp4_f32<1>(lo, g[2] * r.x, g[3] * r.x, 1.0f);
             lo = fp4_f32<2>(lo, g[4] * r.x, g[5] * r.x, 1.0f);

@@ -445,7 +445,9 @@ constexpr uint32_t op_out_bytes() { return OP == kOpFp8 ? (BF16 ? 8u : 4u) : (BF
 // somewhere (the vector is then recomputed exactly by nv_fix_vecs4 after the caller's stores).
 template <bool BF16>
 __device__ __forceinline__ bool nv_vec_codes(uint4 v, float2 r, uint32_t &lo) {
-    uint32_t l = 0u, h = 0u;
+    // every byte of l and h is written by its four converts, so they start from input words that
+    // are dead by then instead of zeros
+    uint32_t l = v.x, h = v.y;
     if constexpr (BF16) {
         l = cvt_fp4_f32<0>(l, bf16_lo(v.x) * r.x, bf16_hi(v.x) * r.x, 1.0f);
         l = cvt_fp4_f32<1>(l, bf16_lo(v.y) * r.x, bf16_hi(v.y) * r.x, 1.0f);
