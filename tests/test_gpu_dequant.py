@@ -150,30 +150,31 @@ def test_per_tensor_full_round_trip_and_stats(fmt):
     assert 25 < sqnr < 60
 
 
-def test_block_full_round_trip_and_stats():
+@pytest.mark.parametrize("fmt", FMTS)
+def test_block_full_round_trip_and_stats(fmt):
     for make, br in ((token_activation, 1), (block_weight, 128)):
         x = make()
         xd = to_device(x)
-        q, sc = qf8.quantize_block(xd, br, 128, O.E4M3)[:2]
-        o, st = qf8.dequantize_block(q, br, 128, O.E4M3, sc, out_dtype=BF16, x=xd)
+        q, sc = qf8.quantize_block(xd, br, 128, fmt)[:2]
+        o, st = qf8.dequantize_block(q, br, 128, fmt, sc, out_dtype=BF16, x=xd)
         qh, sch = host(q), host(sc)
         ob = bf16_host(o)
         r0 = 128 * 13
-        want = O.dequant_block(qh[r0:r0 + 256], br, 128, O.E4M3, sch[r0 // br:(r0 + 256 + br - 1) // br])
+        want = O.dequant_block(qh[r0:r0 + 256], br, 128, fmt, sch[r0 // br:(r0 + 256 + br - 1) // br])
         assert_bf16_of(ob[r0:r0 + 256], want, f"block br={br}")
         gs = sch.shape[1]
         want_st = oracle_stats_slabs(
-            lambda a, b: O.stats_block(x[a:b], qh[a:b], br, 128, O.E4M3, sch[a // br:(b + br - 1) // br]),
+            lambda a, b: O.stats_block(x[a:b], qh[a:b], br, 128, fmt, sch[a // br:(b + br - 1) // br]),
             x.shape[0], 1024 if br == 128 else 512)
         check_stats(qf8.stats_to_dict(st), want_st, f"block {x.shape} br={br}")
         del xd, q, o
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("rnd", [O.ROUND_DOWN, O.ROUND_UP])
-def test_mx_dual_full_round_trip_and_stats(rnd):
+def test_mx_dual_full_round_trip_and_stats(rnd, fmt):
     x = mx_gradient()
     xd = to_device(x)
-    fmt = O.E4M3
     q_row, s_row, q_colT, s_colT = qf8.quantize_mx_dual(xd, fmt, rnd)
     o_r, st_r = qf8.dequantize_mx(q_row, s_row, fmt, out_dtype=BF16, x=xd)
     xt = xd.t().contiguous()
@@ -192,7 +193,7 @@ def test_mx_dual_full_round_trip_and_stats(rnd):
     got = qf8.stats_to_dict(st_r)
     if rnd == O.ROUND_UP:
         assert got["saturated"] == 0                  # round-up never saturates
-    else:
+    elif fmt == O.E4M3:
         assert got["saturated"] > 0
 
 
