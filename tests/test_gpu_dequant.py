@@ -249,6 +249,27 @@ def test_dequant_several_tiles_per_workgroup(mode):
     del o, qd
 
 
+def test_dequant_several_tiles_per_workgroup_4_code_units():
+    """The 4-code units on a tensor where every workgroup walks several tiles: MX to FP32 (one
+    16-byte FP32 piece per unit) and groups to BF16 on rows that are only a multiple of 4 codes
+    long (8-byte pieces); sampled row bands bit-exact."""
+    rng = np.random.default_rng(78)
+    q = rng.integers(0, 256, (BIG_ROWS, BIG_COLS), dtype=np.uint8)
+    sb = rng.integers(0, 256, (BIG_ROWS, BIG_COLS // 32), dtype=np.uint8)
+    o, _ = qf8.dequantize_mx(to_device(q), to_device(sb), O.E5M2, out_dtype=F32)
+    for r0, r1 in BIG_BANDS:
+        assert_f32_equal(f32_host(o[r0:r1]), O.dequant_mx(q[r0:r1], sb[r0:r1], O.E5M2), f"mx fp32 rows {r0}..{r1}")
+    del o
+    cols = BIG_COLS + 4                                   # cols % 8 == 4
+    q4 = rng.integers(0, 256, (BIG_ROWS, cols), dtype=np.uint8)
+    sc = (2.0 ** rng.integers(-20, 21, (BIG_ROWS, (cols + 127) // 128))).astype(np.float32)
+    o, _ = qf8.dequantize_block(to_device(q4), 1, 128, O.E4M3, to_device(sc), out_dtype=BF16)
+    for r0, r1 in BIG_BANDS:
+        assert_bf16_of(bf16_host(o[r0:r1]), O.dequant_block(q4[r0:r1], 1, 128, O.E4M3, sc[r0:r1]),
+                       f"block 4-code rows {r0}..{r1}")
+    del o
+
+
 def check_stats_nan_aware(got, want, what):
     """check_stats where a NaN sum (a NaN de-scaled element next to a finite x) must be NaN in both."""
     for k in ("signal", "noise"):
