@@ -84,6 +84,24 @@ def test_scaled_ragged_lengths(n):
         assert_f32_equal(f32_host(o), O.dequant_scaled(codes, fmt, s), f"n={n}")
 
 
+@pytest.mark.parametrize("n", [1, 17, 4097, 1000003, 5 * 1048576 + 11])
+def test_scaled_ragged_lengths_with_stats(n):
+    """Statistics on lengths that leave a partial last tile and a tail of n % 16 elements (the
+    largest also gives whole tiles to several workgroups), BF16 x with a few outliers."""
+    rng = np.random.default_rng(n + 7)
+    x = small_tensor(1, n, seed=n).reshape(-1)
+    x[rng.integers(0, n, max(1, n // 1000))] = 0x4780              # 65536: saturates below
+    codes = rng.integers(0, 256, n, dtype=np.uint64).astype(np.uint8)
+    codes[(codes & 0x7F) >= 0x7C] = 0x10            # no Inf/NaN codes, so the noise sum stays finite
+    s = np.float32(rng.uniform(0.5, 8.0))
+    for fmt in FMTS:
+        o, st = qf8.dequantize_scaled(to_device(codes), fmt, dev_scale(s), out_dtype=BF16, x=to_device(x))
+        want = O.stats_scaled(x, codes, fmt, s)
+        assert np.isfinite(want["noise"])
+        check_stats(qf8.stats_to_dict(st), want, f"n={n}")
+        assert_bf16_of(bf16_host(o), O.dequant_scaled(codes, fmt, s), f"n={n}")
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_mx_every_code_every_byte(fmt):
     q = np.tile(np.arange(256, dtype=np.uint8), (256, 1))       # row r: all 256 codes
