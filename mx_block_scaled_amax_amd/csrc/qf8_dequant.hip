@@ -165,36 +165,8 @@ __device__ __forceinline__ void acc_add_unit_fast(Acc &acc, WaveCounts &wc, cons
 
 __device__ __forceinline__ bool finite_f64(double v) { return fabs(v) <= 1.79769313486231570815e+308; }
 
-// W consecutive elements of x (W = 4 or 16: the units of the statistics) of unit u.
-template <int XK, int W>
-__device__ __forceinline__ void load_x(const void *x, uint32_t u, float *xv) {
-    static_assert(W == 4 || W == 16, "statistics units");
-    if constexpr (XK == kBF16) {
-        const uint32_t *p = (const uint32_t *)x + (size_t)u * (W / 2);
-        uint32_t w[W / 2];
-        if constexpr (W == 16) {
-            const uint4 a0 = ((const uint4 *)p)[0], a1 = ((const uint4 *)p)[1];
-            w[0] = a0.x; w[1] = a0.y; w[2] = a0.z; w[3] = a0.w; w[4] = a1.x; w[5] = a1.y; w[6] = a1.z; w[7] = a1.w;
-        } else {
-            const uint2 a0 = *(const uint2 *)p;
-            w[0] = a0.x; w[1] = a0.y;
-        }
-#pragma unroll
-        for (int k = 0; k < W / 2; ++k) {
-            xv[2 * k] = __uint_as_float(w[k] << 16);
-            xv[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-        }
-    } else {
-        const float4 *p = (const float4 *)x + (size_t)u * (W / 4);
-#pragma unroll
-        for (int k = 0; k < W / 4; ++k) {
-            const float4 f = p[k];
-            xv[4 * k] = f.x; xv[4 * k + 1] = f.y; xv[4 * k + 2] = f.z; xv[4 * k + 3] = f.w;
-        }
-    }
-}
-// The same in two steps: the raw dwords (BF16 pairs or fp32 bits) of unit u, loaded a loop
-// iteration ahead, then their fp32 values.
+// W consecutive elements of x (W = 4 or 16: the units of the statistics) of unit u in two steps:
+// the raw dwords (BF16 pairs or fp32 bits), loaded a tile ahead, then their fp32 values.
 template <int XK, int W>
 constexpr int x_raw_dwords() { return XK == kBF16 ? W / 2 : W; }
 template <int XK, int W>
@@ -356,6 +328,15 @@ __device__ void block_store_partial(const Acc &acc, const WaveCounts &wcnt, Stat
 template <int P> using Pass = std::integral_constant<int, P>;
 enum { kWhole = 0, kPart = 1, kRedo = 2 };   // a whole tile, the partial last tile, a statistics re-run
 
+// W codes per unit. De-scaling alone takes 8 or 4, so that each lane moves one 16-byte piece of the
+// output and consecutive lanes move consecutive pieces: 8 codes (an 8-byte load) make 16 bytes of
+// BF16, 4 codes 16 bytes of FP32, and whole 16-byte outputs leave as non-temporal stores (a lane
+// writing 32 bytes as two 16-byte stores leaves every store instruction half-dense over its span,
+// which measured ~10% slower for this stream). With the statistics, 16-code units (one 16-byte
+// load of codes) halve the per-unit overhead of the fp64 terms. 4-code units also serve rows that
+// are only a multiple of 4 codes long (8-byte BF16 stores, cached so that L2 merges them). With
+// one scale factor the workgroup first tabulates fl32(decode(c) / S) for all 256 codes in LDS, so
+// an element costs a table read, not a division.
 template <int FMT, int MODE, int OUTK, int XK, int W>
 __global__ __launch_bounds__(kDqThreads) void dequant_kernel(DqArgs a) {
     constexpr bool STATS = XK != kNone;
