@@ -298,16 +298,18 @@ __device__ __forceinline__ void nv_factor_table(float2 *tab, float st) {
 }
 // The exact E2M1 code of x * S_t / dec (dec > 0): the number of E2M1 midpoints (0.25, 0.75, 1.25,
 // 1.75, 2.5, 3.5, 5) the exact quotient lies above, a tie counting when the even code is the upper
-// one; saturation at 6 follows. Each midpoint times dec is exact (3 x 4 significant bits).
+// one; saturation at 6 follows. Midpoint j lies between magnitudes j and j + 1, and being above it
+// is monotone in j, so three comparisons find the count: midpoint 3, then 1 or 5, then 0, 2, 4 or
+// 6. Each comparison is the sign of fma(|x|, S_t, -midpoint * dec), the exact difference rounded
+// once (midpoint * dec is exact: 3 x 4 significant bits). A tie goes up at the odd midpoints
+// 1, 3, 5 (the upper code is the even one) and stays at the even ones. NaN x gives zeros of its sign.
 __device__ __forceinline__ uint32_t nv_elem_exact(float x, float st, float dec) {
     const float ax = __builtin_fabsf(x);
-    constexpr float kMid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
-    uint32_t c = 0;
-#pragma unroll
-    for (int j = 0; j < 7; ++j) {
-        const float s = __builtin_fmaf(ax, st, -(kMid[j] * dec));
-        c += (s > 0.0f || (s == 0.0f && (j & 1))) ? 1u : 0u;
-    }
+    const bool u4 = __builtin_fmaf(ax, st, -(1.75f * dec)) >= 0.0f;
+    const bool u2 = __builtin_fmaf(ax, st, -((u4 ? 3.5f : 0.75f) * dec)) >= 0.0f;
+    const float m = u4 ? (u2 ? 5.0f : 2.5f) : (u2 ? 1.25f : 0.25f);
+    const bool u1 = __builtin_fmaf(ax, st, -(m * dec)) > 0.0f;
+    const uint32_t c = (u4 ? 4u : 0u) + (u2 ? 2u : 0u) + (u1 ? 1u : 0u);
     return c | ((__float_as_uint(x) >> 31) << 3);
 }
 // Two fp32 values -> one byte of two E2M1 codes (first value in the low nibble) in byte SEL of

@@ -46,11 +46,12 @@ constexpr int kFinalizeThreads = 256;           // single-workgroup finalize: on
 constexpr int kOpThreads = 512;                 // single-pass kernel, FP8 output: 8 waves, 2 per SIMD
 constexpr int kOpRegSlabs = 48;                 //   slabs held in VGPRs (4 VGPRs each)
 constexpr int kOpLdsSlabs = 16;                 //   slabs held in LDS (8 KiB each)
-// NVFP4 output: its write phase is VALU-bound (two code estimates per element), so it runs 16
-// waves (4 per SIMD, 128 VGPRs each) to hide the latencies of that phase, and holds 18 slabs in
-// VGPRs (the most without spills) and 9 in LDS (16 KiB each): 432 KiB per workgroup instead of
-// 480. On 16384x4096 BF16 that re-reads 20 MiB but took 52.0-52.8 µs against 54.4-54.6 µs with
-// 8 waves holding 42 + 18 slabs of 8 KiB.
+// NVFP4 output: its write phase is VALU-bound (two code estimates per element, and the exact
+// recomputation of the elements where they differ), so it runs 16 waves (4 per SIMD, 128 VGPRs
+// each) to hide the latencies of that phase, and holds 18 slabs in VGPRs (one more, without
+// spills, gained nothing) and 9 in LDS (16 KiB each): 432 KiB per workgroup instead of 480. On
+// 16384x4096 BF16 that re-reads 20 MiB but took 52.0-52.8 µs against 54.4-54.6 µs with 8 waves
+// holding 42 + 18 slabs of 8 KiB.
 constexpr int kOpThreadsNv = 1024;
 constexpr int kOpRegSlabsNv = 18;
 constexpr int kOpLdsSlabsNv = 9;
@@ -440,11 +441,13 @@ template <int OP> constexpr int op_threads() { return OP == kOpFp8 ? kOpThreads 
 template <int OP, bool BF16>
 constexpr uint32_t op_out_bytes() { return OP == kOpFp8 ? (BF16 ? 8u : 4u) : (BF16 ? 4u : 2u); }
 
-// NVFP4 codes of one input vector from two estimates of x * S_t / decode(e_b), one below and one
-// above the exact quotient (nv_factor_table); returns them in `lo`, and whether they disagree
-// somewhere (the vector is then recomputed exactly by nv_fix_vecs4 after the caller's stores).
+// NVFP4 codes of one input vector. Two estimates of every quotient x * S_t / decode(e_b), one
+// below and one above the exact value (nv_factor_table), give codes lo and hi; where a nibble
+// differs the quotient lies next to an E2M1 midpoint, and that element alone is recomputed
+// exactly (nv_elem_exact) from the vector still in registers. The loop over the differing nibbles
+// runs in the lanes that have any (about 1% of the vectors of a BF16 gradient).
 template <bool BF16>
-__device__ __forceinline__ bool nv_vec_codes(uint4 v, float2 r, uint32_t &lo) {
+__device__ __forceinline__ uint32_t nv_vec_codes(uint4 v, float2 r, uint32_t e, float st) {
     // every byte of l and h is written by its four converts, so they start from input words that
     // are dead by then instead of zeros
     uint32_t l = v.x, h = v.y;
@@ -462,23 +465,36 @@ __device__ __forceinline__ bool nv_vec_codes(uint4 v, float2 r, uint32_t &lo) {
         l = cvt_fp4_f32<1>(l, __uint_as_float(v.z) * r.x, __uint_as_float(v.w) * r.x, 1.0f);
         h = cvt_fp4_f32<0>(h, __uint_as_float(v.x) * r.y, __uint_as_float(v.y) * r.y, 1.0f);
         h = cvt_fp4_f32<1>(h, __uint_as_float(v.z) * r.y, __uint_as_float(v.w) * r.y, 1.0f);
+        l &= 0xFFFFu;                           // the FP32 vector's 4 codes fill two bytes
+        h &= 0xFFFFu;
     }
-    lo = l;
-    return l != h;
+    uint32_t d = l ^ h;
+    if (d != 0u) {
+        const float dec = __builtin_amdgcn_cvt_f32_fp8(e, 0);
+        do {
+            const uint32_t sh = (uint32_t)__builtin_ctz(d) & ~3u;     // nibble of the lowest set bit
+            d &= ~(0xFu << sh);
+            // element sh / 4 of the vector: BF16 nibble 2k + j is half j of word k, FP32 nibble k word k
+            const uint32_t k = BF16 ? sh >> 3 : sh >> 2;
+            const uint32_t w = k == 0u ? v.x : k == 1u ? v.y : k == 2u ? v.z : v.w;
+            const float xe = BF16 ? __uint_as_float((sh & 4u) ? (w & 0xFFFF0000u) : (w << 16)) : __uint_as_float(w);
+            l = (l & ~(0xFu << sh)) | (nv_elem_exact(xe, st, dec) << sh);
+        } while (d != 0u);
+    }
+    return l;
 }
 
 // A block of 16 is 2 (BF16) or 4 (FP32) vectors held by adjacent lanes, whose amax meets by DPP;
 // each lane writes its 4 or 2 code bytes and the block's first lane the E4M3 scale byte. All lanes
-// must be active. Returns whether the vector needs nv_fix_vecs4.
+// must be active.
 template <bool BF16>
-__device__ __forceinline__ bool nv_vec_store(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t wsb, uint32_t vrel,
+__device__ __forceinline__ void nv_vec_store(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t wsb, uint32_t vrel,
                                              uint4 v, float st, const float2 *tab) {
     uint32_t a = acc_to_f32bits<BF16>(vec_absmax<BF16>(0u, v));
     if constexpr (BF16) a = umax(a, dpp_mov<0xB1>(a));         // lanes 2j, 2j+1 hold one block
     else a = max_quad(a);                                       // lanes 4j .. 4j+3
     const uint32_t e = nv_block_code(a, st);
-    uint32_t o;
-    const bool miss = nv_vec_codes<BF16>(v, tab[e], o);
+    const uint32_t o = nv_vec_codes<BF16>(v, tab[e], e, st);
     if constexpr (BF16) {
         buf_store4<kNonTemporal>(wq, vrel * 4u, 0u, o);
         if ((vrel & 1u) == 0u) buf_store1(wsb, vrel >> 1, 0u, e);
@@ -486,72 +502,13 @@ __device__ __forceinline__ bool nv_vec_store(__amdgpu_buffer_rsrc_t wq, __amdgpu
         buf_store2(wq, vrel * 2u, 0u, o);
         if ((vrel & 3u) == 0u) buf_store1(wsb, vrel >> 2, 0u, e);
     }
-    return miss;
-}
-
-// The exact codes of one vector, by one lane alone, from its block's vectors b0, b1 (BF16) or
-// b0..b3 (FP32), read again from memory by the caller, and its place sel in the block: the block
-// amax, e_b, then every
-// element through nv_elem_exact. The lane's earlier store of the same bytes was issued first, so
-// this one is the one that stays.
-template <bool BF16>
-__device__ __forceinline__ void nv_fix_one(__amdgpu_buffer_rsrc_t wq, uint32_t vrel, uint4 b0, uint4 b1, uint4 b2,
-                                           uint4 b3, int sel, bool ok, float st) {
-    uint32_t a = vec_absmax<BF16>(vec_absmax<BF16>(0u, b0), b1);
-    if constexpr (!BF16) a = vec_absmax<BF16>(vec_absmax<BF16>(a, b2), b3);
-    const uint32_t e = nv_block_code(acc_to_f32bits<BF16>(a), st);
-    const float dec = __builtin_amdgcn_cvt_f32_fp8(e, 0);
-    // the vector's own values, chosen by value (b0..b3 stay in registers)
-    const uint32_t w[4] = {sel == 0 ? b0.x : sel == 1 ? b1.x : sel == 2 ? b2.x : b3.x,
-                           sel == 0 ? b0.y : sel == 1 ? b1.y : sel == 2 ? b2.y : b3.y,
-                           sel == 0 ? b0.z : sel == 1 ? b1.z : sel == 2 ? b2.z : b3.z,
-                           sel == 0 ? b0.w : sel == 1 ? b1.w : sel == 2 ? b2.w : b3.w};
-    uint32_t o = 0u;
-    if (dec == dec && dec != 0.0f) {               // else signed zeros (or a non-finite block)
-        if constexpr (BF16) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                o |= nv_elem_exact(bf16_lo(w[k]), st, dec) << (8 * k);
-                o |= nv_elem_exact(bf16_hi(w[k]), st, dec) << (8 * k + 4);
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) o |= nv_elem_exact(__uint_as_float(w[k]), st, dec) << (4 * k);
-        }
-    }
-    if (ok) {
-        if constexpr (BF16) buf_store4<kNonTemporal>(wq, vrel * 4u, 0u, o);
-        else buf_store2(wq, vrel * 2u, 0u, o);
-    }
-}
-
-// Up to four vectors (indices vrel[j] in wq, vabs[j] in x; ok[j] false for unused places) recomputed
-// exactly: every block is read again before any is used, so the loads are in flight together.
-template <bool BF16>
-__device__ __forceinline__ void nv_fix_vecs4(const uint4 *xv, __amdgpu_buffer_rsrc_t wq, const uint32_t (&vrel)[4],
-                                             const int64_t (&vabs)[4], const bool (&ok)[4], float st) {
-    constexpr int kVpb = BF16 ? 2 : 4;
-    uint4 v[4][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t s = ok[j] ? vabs[j] - vabs[j] % kVpb : 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[j][i] = (ok[j] && i < kVpb) ? xv[s + i] : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        nv_fix_one<BF16>(wq, vrel[j], v[j][0], v[j][1], v[j][2], v[j][3], (int)(vabs[j] % kVpb), ok[j], st);
 }
 
 template <int OP, bool BF16, int FMT>
-__device__ __forceinline__ bool op_vec_store(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t wsb, uint32_t vrel,
+__device__ __forceinline__ void op_vec_store(__amdgpu_buffer_rsrc_t wq, __amdgpu_buffer_rsrc_t wsb, uint32_t vrel,
                                              uint4 v, float s, const float2 *tab) {
-    if constexpr (OP == kOpFp8) {
-        cast_vec_store<BF16, FMT>(wq, vrel * op_out_bytes<OP, BF16>(), v, s);
-        return false;
-    } else {
-        return nv_vec_store<BF16>(wq, wsb, vrel, v, s, tab);
-    }
+    if constexpr (OP == kOpFp8) cast_vec_store<BF16, FMT>(wq, vrel * op_out_bytes<OP, BF16>(), v, s);
+    else nv_vec_store<BF16>(wq, wsb, vrel, v, s, tab);
 }
 
 // Byte count of the vectors [first, nvec) clamped to one buffer descriptor's range.
@@ -581,27 +538,8 @@ __device__ __forceinline__ uint32_t stream_slabs8(const uint4 *x, int64_t nvec, 
         const __amdgpu_buffer_rsrc_t w = make_rsrc(q + first * kOut, span_bytes(first, nvec, kOut));
         const __amdgpu_buffer_rsrc_t wsb = make_rsrc(OP == kOpNvfp4 ? sb + first / kVpb : q,
                                                      OP == kOpNvfp4 ? span_bytes(first, nvec, 1u) / kVpb : 0u);
-        uint32_t miss = 0u;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            miss |= (uint32_t)op_vec_store<OP, BF16, FMT>(w, wsb, i * (step / 16u) + threadIdx.x, v[i], s, tab) << i;
-        if constexpr (OP == kOpNvfp4) {
-            if (__builtin_amdgcn_ballot_w64(miss != 0u) != 0u) {        // rare: wave-uniform branch
-                while (miss != 0u) {                // four of the lane's set bits per trip
-                    uint32_t vr[4];
-                    int64_t va[4];
-                    bool ok[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        ok[j] = miss != 0u;
-                        vr[j] = ok[j] ? (uint32_t)__builtin_ctz(miss) * (step / 16u) + threadIdx.x : 0u;
-                        va[j] = first + vr[j];
-                        miss &= miss - 1u;
-                    }
-                    nv_fix_vecs4<BF16>(x, w, vr, va, ok, s);
-                }
-            }
-        }
+        for (int i = 0; i < 8; ++i) op_vec_store<OP, BF16, FMT>(w, wsb, i * (step / 16u) + threadIdx.x, v[i], s, tab);
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) a = vec_absmax<BF16>(a, v[i]);
@@ -746,10 +684,6 @@ __global__ __launch_bounds__(op_threads<OP>()) void per_tensor_onepass_kernel(
 
     // pass 2: cast the held slabs, then re-read and cast the rest (vector indices: vbase + k * vstep)
     const uint32_t vbase = (uint32_t)b * NT + t, vstep = step / 16u;
-    // NVFP4: one bit per held vector whose two estimates disagree. Each bit is pinned in a register
-    // as soon as it is known (the empty asm), so that the compiler does not carry every vector's
-    // inputs down to the fix-up below.
-    uint32_t miss_w[2] = {0u, 0u};
     // Given-up slabs (see the barrier description above): the releaser publishes after its first
     // kPublishAt register slabs, when its exchanges have returned; the others read INFO after
     // slab kInfoReadAt, well after that, and use it only at the end, so that neither waits.
@@ -759,8 +693,7 @@ __global__ __launch_bounds__(op_threads<OP>()) void per_tensor_onepass_kernel(
     static_assert(kPublishAt + 8 <= kInfoReadAt && kInfoReadAt < KR, "INFO is read well after it is sent");
 #pragma unroll
     for (int k = 0; k < KR; ++k) {
-        miss_w[k >> 5] |= (uint32_t)op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + k * vstep, R[k], s, nvtab) << (k & 31);
-        if constexpr (OP == kOpNvfp4) asm volatile("" : "+v"(miss_w[k >> 5]));
+        op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + k * vstep, R[k], s, nvtab);
         if (k == kPublishAt && role == 1) {
             const bool tell = xres == 0u;           // released by this thread's exchange: gets INFO
             if (xres == kLineGaveUp) {
@@ -787,31 +720,7 @@ __global__ __launch_bounds__(op_threads<OP>()) void per_tensor_onepass_kernel(
             info = __hip_atomic_load((uint32_t *)own + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 #pragma unroll
-    for (int k = 0; k < KL; ++k) {
-        miss_w[(KR + k) >> 5] |= (uint32_t)op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + (KR + k) * vstep,
-                                                                       held[k * NT + t], s, nvtab)
-                                 << ((KR + k) & 31);
-        if constexpr (OP == kOpNvfp4) asm volatile("" : "+v"(miss_w[(KR + k) >> 5]));
-    }
-    uint64_t miss = (uint64_t)miss_w[0] | ((uint64_t)miss_w[1] << 32);
-    if constexpr (OP == kOpNvfp4) {
-        static_assert(KR + KL <= 64, "one miss bit per held slab");
-        if (__builtin_amdgcn_ballot_w64(miss != 0u) != 0u) {            // rare: wave-uniform branch
-            while (miss != 0u) {                    // four of the lane's set bits per trip
-                uint32_t vr[4];
-                int64_t va[4];
-                bool ok[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    ok[j] = miss != 0u;
-                    vr[j] = ok[j] ? vbase + (uint32_t)__builtin_ctzll(miss) * vstep : 0u;
-                    va[j] = vr[j];
-                    miss &= miss - 1u;
-                }
-                nv_fix_vecs4<BF16>(xv, rq, vr, va, ok, s);
-            }
-        }
-    }
+    for (int k = 0; k < KL; ++k) op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + (KR + k) * vstep, held[k * NT + t], s, nvtab);
     for (int64_t k = KR + KL; k * G + b < nslabs; k += 8)
         stream_slabs8<OP, BF16, FMT, true>(xv, nvec, q, sb, k, b, G, s, nvtab);
 
