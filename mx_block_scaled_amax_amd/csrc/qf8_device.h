@@ -227,12 +227,13 @@ __device__ __forceinline__ float scale_pow2_from_amax_bits(uint32_t abits) {
 // F8max * 2^X before the convert: identical for all finite BF16 inputs and all 255 scales.
 template <int FMT>
 __device__ __forceinline__ uint32_t mx_saturate_codes(uint32_t w) {
-    if constexpr (FMT == kE4M3) {                 // bytes whose low 7 bits are all ones
-        return w - ((((w & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u) >> 7);
-    } else {                                      // bytes whose low 7 bits are 0x7C
-        const uint32_t z = (w & 0x7F7F7F7Fu) ^ 0x7C7C7C7Cu;
-        const uint32_t nonzero = ((z + 0x7F7F7F7Fu) | z) & 0x80808080u;
-        return w - ((~nonzero & 0x80808080u) >> 7);
+    if constexpr (FMT == kE4M3) {                 // bytes whose low 7 bits are all ones: 0x7F -> 0x7E
+        return w ^ ((((w & 0x7F7F7F7Fu) + 0x01010101u) >> 7) & 0x01010101u);
+    } else {                                      // bytes whose low 7 bits are 0x7C: 0x7C -> 0x7B
+        // with bit 7 of every byte set, a byte minus one borrows from no other byte, and keeps
+        // bit 7 unless its low 7 bits were zero, i.e. the code's were 0x7C
+        const uint32_t y = (((w & 0x7F7F7F7Fu) ^ 0x7C7C7C7Cu) | 0x80808080u) - 0x01010101u;
+        return w - ((~y & 0x80808080u) >> 7);
     }
 }
 

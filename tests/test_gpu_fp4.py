@@ -433,12 +433,44 @@ def test_nvfp4_midpoint_ties_streaming(dtype, unit):
 @pytest.mark.parametrize("dtype,unit", [("fp32", False), ("bf16", True)])
 def test_nvfp4_midpoint_ties_single_pass(dtype, unit):
     """The same construction at 2^22 elements, through the single-pass kernel (the tensor held on
-    chip across its grid barrier; vectors whose two estimates disagree are recomputed exactly
-    from memory after the held slabs are written)."""
+    chip across its grid barrier; the elements whose two estimates disagree are recomputed
+    exactly from the vector still in registers or LDS, before its store)."""
     ws = qf8.workspace(torch.empty(1, device="cuda"))
     x = nv_tie_tensor(2048, 2048, seed=35 + unit, dtype=dtype, unit_scale=unit)
     check_nv_big(x, ws, f"ties {dtype} unit_scale={unit} 2048x2048")
 
+
+
+def nv_overflow_tensor(rows, cols, seed, dtype):
+    """A tensor amax A = 2^-120, so small that 2688 / A exceeds FLT_MAX: S_t is held at FLT_MAX,
+    and S_t / decode(e_b) overflows for every block code below about 1. Block amaxes A * 2^-u
+    with u uniform in [0, 12] put about half of the blocks there; each block holds its amax,
+    uniform magnitudes below it (fp32 subnormals among them), 5% zeros, and random signs."""
+    rng = np.random.default_rng(seed)
+    nb = rows * cols // 16
+    ab = 2.0 ** -120 * 2.0 ** -rng.uniform(0, 12, nb)
+    v = rng.uniform(0, 1, (nb, 16)) * ab[:, None]
+    v[:, 0] = ab
+    v[:, 1:][rng.random((nb, 15)) < 0.05] = 0.0
+    x = (v * np.where(rng.integers(0, 2, v.shape) == 1, -1.0, 1.0)).astype(np.float32).reshape(rows, cols)
+    x[0, 0] = np.float32(2.0 ** -120)
+    if dtype == "bf16":
+        return (x.view(np.uint32) >> 16).astype(np.uint16)      # truncation: 2^-120 stays the amax
+    return x
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_nvfp4_single_pass_overflowing_factors(dtype):
+    """Blocks whose element factor S_t / decode(e_b) overflows get the factors (0, Inf): their two
+    code estimates are 0 and +-6, never adjacent, so every nonzero element goes through the exact
+    search, and zeros keep their signs. Streaming kernel (96x512) and single-pass kernel (2^22
+    elements), every byte compared."""
+    check_nv(nv_overflow_tensor(96, 512, seed=40, dtype=dtype), tag=f"overflowing factors {dtype}")
+    ws = qf8.workspace(torch.empty(1, device="cuda"))
+    x = nv_overflow_tensor(2048, 2048, seed=41, dtype=dtype)
+    g = run_nv_ws(x, ws)
+    assert g[2] == np.finfo(np.float32).max, g[2]
+    check_nv_big(x, ws, f"overflowing factors {dtype} 2048x2048")
 
 # ---- FP4 de-scaling ------------------------------------------------------------------------------
 
