@@ -432,6 +432,27 @@ __device__ __forceinline__ void cast_vec_store(__amdgpu_buffer_rsrc_t w, uint32_
     }
 }
 
+// Per-tensor FP8 codes of two whole slabs, stored by lane pairs as 16-byte pieces (8 for FP32
+// input): the even lane of a pair writes its vector's codes and its partner's from slab k, the odd
+// lane both from slab k + 1, after one DPP swap of the codes each sends. v0 is the lane's vector
+// index in slab k; every lane of the wave must be active.
+template <bool BF16, int FMT>
+__device__ __forceinline__ void cast_pair_store(__amdgpu_buffer_rsrc_t w, uint32_t v0, uint32_t vstep, uint4 a, uint4 b,
+                                                float s) {
+    const bool odd = (threadIdx.x & 1u) != 0u;
+    const uint32_t v = odd ? v0 - 1u + vstep : v0;      // the pair's first vector in its slab
+    if constexpr (BF16) {
+        const uint2 A = cast8_bf16<FMT>(a, s), B = cast8_bf16<FMT>(b, s);
+        const uint32_t rx = dpp_mov<0xB1>(odd ? A.x : B.x), ry = dpp_mov<0xB1>(odd ? A.y : B.y);
+        const uint4 o = odd ? make_uint4(rx, ry, B.x, B.y) : make_uint4(A.x, A.y, rx, ry);
+        buf_store16<kNonTemporal>(w, v * 8u, 0u, o);
+    } else {
+        const uint32_t A = cast4_f32<FMT>(a, s), B = cast4_f32<FMT>(b, s);
+        const uint32_t r = dpp_mov<0xB1>(odd ? A : B);
+        buf_store8<kNonTemporal>(w, v * 4u, 0u, odd ? r : A, odd ? B : r);
+    }
+}
+
 // The single-pass kernel's outputs. kOpFp8: per-tensor FP8 cast (8 or 4 code bytes per 16-byte
 // input vector). kOpNvfp4: NVFP4 with the tensor scale S_t: a 16-element block is 2 (BF16) or 4
 // (FP32) vectors held by adjacent lanes, whose amax meets by DPP; each lane writes its 4 or 2
@@ -691,9 +712,23 @@ __global__ __launch_bounds__(op_threads<OP>()) void per_tensor_onepass_kernel(
     constexpr int kPublishAt = OP == kOpFp8 ? kPublishAtFp8 : KR / 3;
     constexpr int kInfoReadAt = OP == kOpFp8 ? KR / 2 : KR - 4;
     static_assert(kPublishAt + 8 <= kInfoReadAt && kInfoReadAt < KR, "INFO is read well after it is sent");
+    // FP8 output: slabs k, k + 1 that are both whole leave through lane pairs as 16-byte pieces
+    const auto pair_whole = [&](int k) { return ((int64_t)(k + 1) * G + b + 1) * NT <= nvec; };
+    static_assert(OP != kOpFp8 || (KR % 2 == 0 && KL % 2 == 0), "FP8 held slabs go in pairs");
 #pragma unroll
     for (int k = 0; k < KR; ++k) {
-        op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + k * vstep, R[k], s, nvtab);
+        if constexpr (OP == kOpFp8) {
+            if ((k & 1) == 0) {
+                if (pair_whole(k)) {
+                    cast_pair_store<BF16, FMT>(rq, vbase + k * vstep, vstep, R[k], R[k + 1], s);
+                } else {
+                    op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + k * vstep, R[k], s, nvtab);
+                    op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + (k + 1) * vstep, R[k + 1], s, nvtab);
+                }
+            }
+        } else {
+            op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + k * vstep, R[k], s, nvtab);
+        }
         if (k == kPublishAt && role == 1) {
             const bool tell = xres == 0u;           // released by this thread's exchange: gets INFO
             if (xres == kLineGaveUp) {
@@ -720,7 +755,20 @@ __global__ __launch_bounds__(op_threads<OP>()) void per_tensor_onepass_kernel(
             info = __hip_atomic_load((uint32_t *)own + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 #pragma unroll
-    for (int k = 0; k < KL; ++k) op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + (KR + k) * vstep, held[k * NT + t], s, nvtab);
+    for (int k = 0; k < KL; ++k) {
+        if constexpr (OP == kOpFp8) {
+            if ((k & 1) == 0) {
+                if (pair_whole(KR + k)) {
+                    cast_pair_store<BF16, FMT>(rq, vbase + (KR + k) * vstep, vstep, held[k * NT + t], held[(k + 1) * NT + t], s);
+                } else {
+                    op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + (KR + k) * vstep, held[k * NT + t], s, nvtab);
+                    op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + (KR + k + 1) * vstep, held[(k + 1) * NT + t], s, nvtab);
+                }
+            }
+        } else {
+            op_vec_store<OP, BF16, FMT>(rq, rsb, vbase + (KR + k) * vstep, held[k * NT + t], s, nvtab);
+        }
+    }
     for (int64_t k = KR + KL; k * G + b < nslabs; k += 8)
         stream_slabs8<OP, BF16, FMT, true>(xv, nvec, q, sb, k, b, G, s, nvtab);
 
