@@ -17,7 +17,8 @@
 //   owns VEC consecutive columns (column slot l % 32) of 16 rows (half l / 32 of the wave's
 //   rows), held in 16 x 16-byte registers.
 //   * A rowwise block (1 row x 32 columns) spans 32/VEC lanes (4 for BF16): its amax takes two
-//     (or three) DPP steps, and each lane writes its VEC codes of the row.
+//     (or three) DPP steps. Lane pairs write two rows' codes at once: after a DPP swap the even
+//     lane stores row 2p of both lanes' columns and the odd lane row 2p + 1 (2 * VEC bytes each).
 //   * A columnwise block (32 rows x 1 column) is split over lanes l and l ^ 32: each lane folds
 //     its 16 rows in registers and one cross-half exchange completes the amax. The lane's 16
 //     codes per column go to an LDS tile [column][128 rows]; after a barrier the workgroup
@@ -45,6 +46,7 @@ constexpr int kThreads = 256;
 constexpr int kTileRows = 128;
 constexpr int kRowsPerWave = 32;
 constexpr int kRowsPerLane = kRowsPerWave / 2;
+static_assert(kRowsPerLane % 2 == 0, "rowwise codes leave two rows at a time");
 
 template <bool BF16, int FMT, int RND>
 __device__ __forceinline__ uint32_t mx_byte(uint32_t absbits) {
@@ -113,6 +115,14 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const void *__restrict__ x
             const __amdgpu_buffer_rsrc_t qr = make_rsrc(q_row + (size_t)r0 * cols, (uint32_t)wrows * cols);
             const uint32_t qvo = active ? (uint32_t)(half * RPL) * cols + c0 : kOutOfRange;
             const uint32_t sstride = cols / 32;
+            // Rows 2p and 2p + 1 leave through lane pairs: the even lane of a pair writes row 2p of
+            // both lanes' columns, the odd lane row 2p + 1, after one DPP swap of the codes each
+            // sends (16-byte pieces for BF16, 8 for FP32: half the store instructions). A pair's
+            // lanes are both active or both idle, since cols % 32 == 0.
+            const bool odd = (slot & 1) != 0;
+            constexpr uint32_t kCodes = VEC;             // code bytes per lane and row
+            const uint32_t qpo = !active ? kOutOfRange : odd ? qvo - kCodes : qvo;
+            uint32_t p0 = 0u, p1 = 0u;                   // the codes of the pair's first row
 #pragma unroll
             for (int i = 0; i < RPL; ++i) {
                 uint32_t m[4];
@@ -140,13 +150,24 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const void *__restrict__ x
                     uint32_t o1 = cvt2_bf16_div2x<FMT, true>(v[3], sc, cvt2_bf16_div2x<FMT, false>(v[2], sc, m[2]));
                     if constexpr (RND == kRoundDown) { o0 = mx_saturate_codes<FMT>(o0); o1 = mx_saturate_codes<FMT>(o1); }
                     if (a == 0u) o0 = o1 = 0u;                          // all-zero block: 0x00, not -0
-                    buf_store8(qr, qvo, (uint32_t)i * cols, o0, o1);
+                    if ((i & 1) == 0) {
+                        p0 = o0; p1 = o1;
+                    } else {
+                        const uint32_t rx = dpp_mov<0xB1>(odd ? p0 : o0), ry = dpp_mov<0xB1>(odd ? p1 : o1);
+                        const uint4 w = odd ? make_uint4(rx, ry, o0, o1) : make_uint4(p0, p1, rx, ry);
+                        buf_store16(qr, qpo + (uint32_t)(odd ? i : i - 1) * cols, 0u, w);
+                    }
                 } else {
                     uint32_t o0 = cvt2_f32_div2x<FMT, true>(__uint_as_float(v[2]), __uint_as_float(v[3]), sc,
                                   cvt2_f32_div2x<FMT, false>(__uint_as_float(v[0]), __uint_as_float(v[1]), sc, m[0]));
                     if constexpr (RND == kRoundDown) o0 = mx_saturate_codes<FMT>(o0);
                     if (a == 0u) o0 = 0u;
-                    buf_store4(qr, qvo, (uint32_t)i * cols, o0);
+                    if ((i & 1) == 0) {
+                        p0 = o0;
+                    } else {
+                        const uint32_t r = dpp_mov<0xB1>(odd ? p0 : o0);
+                        buf_store8(qr, qpo + (uint32_t)(odd ? i : i - 1) * cols, 0u, odd ? r : p0, odd ? o0 : r);
+                    }
                 }
                 // every lane of the block writes the same byte to the same LDS slot
                 srow[(wave * kRowsPerWave + half * RPL + i) * NBLK + slot / LPB] = (uint8_t)byte;
