@@ -148,6 +148,14 @@ __global__ __launch_bounds__(2 * TR) void mxfp4_kernel(const void *__restrict__ 
             const __amdgpu_buffer_rsrc_t qr = make_rsrc(q_row + (size_t)r0 * qstride, (uint32_t)wrows * qstride);
             const uint32_t qvo = active ? (uint32_t)(half * RPL) * qstride + c0 / 2 : kOutOfRange;
             const uint32_t sstride = cols / 32;
+            // Rows 2p and 2p + 1 leave through lane pairs: the even lane of a pair writes row 2p of
+            // both lanes' columns, the odd lane row 2p + 1, after one DPP swap (8-byte pieces for
+            // BF16, 4 for FP32). A pair's lanes are both active or both idle (cols % 32 == 0).
+            static_assert(RPL % 2 == 0, "rowwise codes leave two rows at a time");
+            const bool odd = (slot & 1) != 0;
+            constexpr uint32_t kCodeBytes = VEC / 2;     // code bytes per lane and row
+            const uint32_t qpo = !active ? kOutOfRange : odd ? qvo - kCodeBytes : qvo;
+            uint32_t prev = 0u;                          // the codes of the pair's first row
 #pragma unroll
             for (int i = 0; i < RPL; ++i) {
                 uint32_t m[4];
@@ -173,12 +181,23 @@ __global__ __launch_bounds__(2 * TR) void mxfp4_kernel(const void *__restrict__ 
                     o = fp4_bf16<2>(o, d[i][2], sc);
                     o = fp4_bf16<3>(o, d[i][3], sc);
                     if (a == 0u) o = 0u;                            // all-zero block: zero codes
-                    buf_store4(qr, qvo, (uint32_t)i * qstride, o);
+                    if ((i & 1) == 0) {
+                        prev = o;
+                    } else {
+                        const uint32_t r = dpp_mov<0xB1>(odd ? prev : o);
+                        buf_store8(qr, qpo + (uint32_t)(odd ? i : i - 1) * qstride, 0u, odd ? r : prev, odd ? o : r);
+                    }
                 } else {
                     uint32_t o = fp4_f32<0>(0u, __uint_as_float(d[i][0]), __uint_as_float(d[i][1]), sc);
                     o = fp4_f32<1>(o, __uint_as_float(d[i][2]), __uint_as_float(d[i][3]), sc);
                     if (a == 0u) o = 0u;
-                    buf_store2(qr, qvo, (uint32_t)i * qstride, o);
+                    if ((i & 1) == 0) {
+                        prev = o;
+                    } else {
+                        const uint32_t r = dpp_mov<0xB1>(odd ? prev : o);
+                        buf_store4(qr, qpo + (uint32_t)(odd ? i : i - 1) * qstride, 0u,
+                                   odd ? ((r & 0xFFFFu) | (o << 16)) : ((prev & 0xFFFFu) | (r << 16)));
+                    }
                 }
                 // every lane of the block writes the same byte to the same LDS slot
                 srow[(wave * kRowsPerWave + half * RPL + i) * NBLK + slot / LPB] = (uint8_t)byte;
