@@ -125,6 +125,10 @@ def test_mxfp4_single_direction_and_ragged(rnd):
     check_mx(small_tensor(320, 288, seed=8), rnd, row=False, col=True, tag="col-two-tile-rows")
     x = (np.random.default_rng(7).standard_normal((96, 36)) * 10).astype(np.float32)
     check_mx(x, rnd, row=False, col=True, tag="col-fp32-ragged")
+    rng = np.random.default_rng(9)
+    for shape in [(37, 64), (130, 96), (1, 32)]:          # FP32 rows in pairs, the second one missing
+        x = (rng.standard_normal(shape) * np.exp(rng.uniform(-3, 3, (shape[0], 1)))).astype(np.float32)
+        check_mx(x, rnd, row=True, col=False, tag=f"row-ragged-rows-fp32 {shape}")
 
 
 def test_mxfp4_zero_blocks_and_extremes():

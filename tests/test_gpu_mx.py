@@ -120,6 +120,16 @@ def test_single_direction_and_ragged(fmt, rnd):
     check(small_tensor(96, 520, seed=6), fmt, rnd, row=False, col=True, tag="col-ragged-cols")
 
 
+@pytest.mark.parametrize("fmt,rnd", VARIANTS, ids=VID)
+def test_rowwise_ragged_rows_fp32(fmt, rnd):
+    """Rowwise codes leave two rows at a time through lane pairs; with an odd number of rows in a
+    wave the pair's second row lies outside the tensor. FP32 input (the 8-byte pieces)."""
+    rng = np.random.default_rng(9)
+    for shape in [(37, 64), (130, 96), (1, 32)]:
+        x = (rng.standard_normal(shape) * np.exp(rng.uniform(-3, 3, (shape[0], 1)))).astype(np.float32)
+        check(x, fmt, rnd, row=True, col=False, tag=f"row-ragged-rows-fp32 {shape}")
+
+
 def test_zero_blocks_and_negative_zero():
     x = np.zeros((64, 64), np.uint16)
     x[3, 5] = 0x8000                     # -0 inside an all-zero block -> 0x00
