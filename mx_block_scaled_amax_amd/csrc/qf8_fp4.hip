@@ -150,7 +150,8 @@ __global__ __launch_bounds__(2 * TR) void mxfp4_kernel(const void *__restrict__ 
             const uint32_t sstride = cols / 32;
             // Rows 2p and 2p + 1 leave through lane pairs: the even lane of a pair writes row 2p of
             // both lanes' columns, the odd lane row 2p + 1, after one DPP swap (8-byte pieces for
-            // BF16, 4 for FP32). A pair's lanes are both active or both idle (cols % 32 == 0).
+            // BF16, 4 for FP32). A pair's lanes are both active or both idle (cols % 32 == 0). The
+            // swapped value comes from the zero-block select, never straight from a convert.
             static_assert(RPL % 2 == 0, "rowwise codes leave two rows at a time");
             const bool odd = (slot & 1) != 0;
             constexpr uint32_t kCodeBytes = VEC / 2;     // code bytes per lane and row

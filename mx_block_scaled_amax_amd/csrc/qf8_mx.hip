@@ -118,7 +118,9 @@ __global__ __launch_bounds__(kThreads) void mx_kernel(const void *__restrict__ x
             // Rows 2p and 2p + 1 leave through lane pairs: the even lane of a pair writes row 2p of
             // both lanes' columns, the odd lane row 2p + 1, after one DPP swap of the codes each
             // sends (16-byte pieces for BF16, 8 for FP32: half the store instructions). A pair's
-            // lanes are both active or both idle, since cols % 32 == 0.
+            // lanes are both active or both idle, since cols % 32 == 0. The swapped value is the
+            // result of the zero-block select, written whole by one VALU instruction: a DPP move
+            // never reads a convert's partially written destination.
             const bool odd = (slot & 1) != 0;
             constexpr uint32_t kCodes = VEC;             // code bytes per lane and row
             const uint32_t qpo = !active ? kOutOfRange : odd ? qvo - kCodes : qvo;
