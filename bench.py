@@ -21,8 +21,9 @@ variant finds the previous variant's data in the 256 MB last-level cache.
                    profiles/), scaled by the same counters' reading for a plain copy of known
                    size; null when the kernel sources changed since the counters were taken.
   config.per_tensor_8192x8192 = per-tensor current scaling of the 8192x8192 BF16 activation, E4M3
-                   and E5M2, each launch's average over back-to-back launches under one event pair
-                   (algorithmic bytes 2N + N + 8 = 201,326,600), with its % of HBM peak.
+                   and E5M2, the average launch of back-to-back launches (algorithmic bytes
+                   2N + N + 8 = 201,326,600), with its % of HBM peak; the two formats are timed
+                   in alternating chunks of 40 launches after a long warm-up (time_per_tensor).
   cpu_baseline   = the CPU oracle (plain C) on the whole input, all four variants, on 1 thread and on
                    T threads over row bands (T = the usable CPUs, at most 16), with the CPU model.
 
@@ -164,9 +165,12 @@ def cpu_baseline(xb):
 
 def time_per_tensor(args, qf8, stream):
     """Per-tensor current scaling of the 8192x8192 BF16 activation (N(0,1), 0.1% entries x1000,
-    seed 2), E4M3 and E5M2: args.steps rounds over four device-resident input copies, launches back
-    to back under one HIP event pair on the launch stream; algorithmic bytes 2N read + N written +
-    the fp32 amax and scale = 201,326,600 per launch."""
+    seed 2), E4M3 and E5M2: a round is one launch on each of four device-resident input copies.
+    After at least 100 untimed rounds of each format (this leg follows the cold launches, whose
+    cache flushes leave the GPU idle between launches), args.steps rounds per format are timed in
+    chunks of up to 10 rounds, the two formats alternating chunk by chunk so that both see the same
+    conditions; each chunk's launches run back to back under one HIP event pair on the launch
+    stream. Algorithmic bytes 2N read + N written + the fp32 amax and scale = 201,326,600 per launch."""
     import torch
     from synthetic import per_tensor_activation
     xb = per_tensor_activation()
@@ -182,25 +186,36 @@ def time_per_tensor(args, qf8, stream):
     sp = vp(stream.cuda_stream)
     out = {"workload": "per_tensor_current_8192x8192", "values": "N(0,1), 0.1% entries x1000, seed 2",
            "algorithmic_bytes": nbytes}
+    runs = {}
     for fmt, name in ((qf8.E4M3, "e4m3"), (qf8.E5M2, "e5m2")):
         args_of = [(vp(x.data_ptr()), 0, xb.shape[0], xb.shape[1], fmt, vp(q.data_ptr()), vp(am.data_ptr()),
                     vp(sc.data_ptr()), None, vp(ws.data_ptr()), ws.numel(), sp) for x in xs]
 
-        def run():
+        def run(args_of=args_of):
             for a in args_of:
                 st = lib.quantize_per_tensor(*a)
                 if st != 0:
                     raise RuntimeError(f"quantize_per_tensor failed with status {st}")
-        for _ in range(args.warmup):
+        runs[name] = run
+    for _ in range(max(args.warmup, 100)):
+        for run in runs.values():
             run()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(args.steps):
-            run()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / (4 * args.steps)
+    torch.cuda.synchronize()
+    spans = {name: [] for name in runs}
+    done = 0
+    while done < args.steps:
+        rounds = min(10, args.steps - done)
+        for name, run in runs.items():
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(rounds):
+                run()
+            e1.record(stream)
+            spans[name].append((e0, e1))
+        done += rounds
+    torch.cuda.synchronize()
+    for name in runs:
+        ms = sum(e0.elapsed_time(e1) for e0, e1 in spans[name]) / (4 * args.steps)
         gbps = nbytes / (ms / 1e3) / 1e9
         out[name] = {"avg_launch_ms": round(ms, 5), "GBps": round(gbps, 1),
                      "pct_of_hbm_peak": round(100 * gbps / PEAK_GBPS, 2)}
