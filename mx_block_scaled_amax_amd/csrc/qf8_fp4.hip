@@ -412,13 +412,15 @@ void launch_mxfp4_dirs(const void *x, int rows, int cols, uint8_t *q_row, uint8_
 }
 
 // ---------------------------------------------------------------------------------------------
-// NVFP4: one thread per block of 16 consecutive elements (cols % 16 == 0, so a block never
-// crosses a row and block b of the flattened tensor is row b / (cols/16)). Every workgroup first
-// takes the tensor amax (the caller's value, or the fold of the amax pass's partials), S_t and the
-// table of element factors; a thread then loads its 32 (BF16) or 64 (FP32) bytes, takes the block
-// amax and the E4M3 block scale, converts the two bracketing estimates of every element and
-// writes 8 bytes of codes and the scale byte. The elements whose two estimates disagree (those
-// within about 2^-20 of an E2M1 midpoint) are recomputed exactly, each by its own lane.
+// NVFP4: a thread works on blocks of 16 consecutive elements (cols % 16 == 0, so a block never
+// crosses a row and block b of the flattened tensor is row b / (cols/16)), one per pass over the
+// workgroup's 256 threads, two passes per trip for BF16 input (nv_passes_per_trip). Every
+// workgroup first takes the tensor amax (the caller's value, or the fold of the amax pass's
+// partials), S_t and the table of element factors; for each block a thread loads its 32 (BF16) or
+// 64 (FP32) bytes, takes the block amax and the E4M3 block scale, converts the two bracketing
+// estimates of every element and produces 8 bytes of codes and the scale byte. The elements whose
+// two estimates disagree (those within about 2^-20 of an E2M1 midpoint) are recomputed exactly,
+// each by its own lane.
 
 
 template <bool BF16>
